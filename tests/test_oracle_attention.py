@@ -1,0 +1,63 @@
+"""Pins of oracle.attention: torch scaled-dot-product attention in float64 on the
+CPU, a pure-Python loop on tiny shapes, and PSAC full-rank exactness."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import attention, psac
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_matches_torch_sdpa_fp64(causal):
+    rng = np.random.default_rng(0)
+    q = rng.standard_normal((40, 3, 32)).astype(np.float32)
+    k = (rng.standard_normal((40, 3, 32)) * 3).astype(np.float32)
+    v = (rng.standard_normal((40, 3, 32)) * 10).astype(np.float32)
+    out = attention.attend(q, k, v, causal=causal)
+    t = lambda a: torch.from_numpy(a.astype(np.float64)).permute(1, 0, 2)
+    ref = torch.nn.functional.scaled_dot_product_attention(t(q), t(k), t(v), is_causal=causal)
+    for h in range(3):
+        assert np.allclose(out[h], ref[h].numpy(), rtol=1e-12, atol=1e-12)
+
+
+def test_python_loop_tiny_with_psac():
+    rng = np.random.default_rng(1)
+    nq, nk, d, r = 5, 7, 4, 2
+    q = rng.standard_normal((nq, d)).astype(np.float32)
+    k = rng.standard_normal((nk, d)).astype(np.float32)
+    v = rng.standard_normal((nk, d)).astype(np.float32)
+    u = np.linalg.qr(rng.standard_normal((d, r)))[0]
+    coef = rng.standard_normal((nk, r)).astype(np.float32)
+    o = attention.attend_head(q, k, v, coef, u, scale=0.3)
+    for i in range(nq):
+        s = []
+        for j in range(nk):
+            dot = sum(float(q[i, a]) * float(k[j, a]) for a in range(d))
+            qu = [sum(float(q[i, a]) * u[a, b] for a in range(d)) for b in range(r)]
+            dot += sum(qu[b] * float(coef[j, b]) for b in range(r))
+            s.append(0.3 * dot)
+        m = max(s)
+        p = [math.exp(x - m) for x in s]
+        z = sum(p)
+        for a in range(d):
+            ref = sum(p[j] / z * float(v[j, a]) for j in range(nk))
+            assert o[i, a] == pytest.approx(ref, rel=1e-12, abs=1e-14)
+
+
+def test_psac_full_rank_recovers_exact_logits():
+    rng = np.random.default_rng(2)
+    d = 16
+    qh = rng.standard_normal((300, d))
+    u, _, _ = psac.principal_subspace(psac.query_gram(qh), d)
+    k = (rng.standard_normal((50, d)) * 5).astype(np.float32)
+    k_hat = np.round(k).astype(np.float32)           # any approximation
+    e = (k.astype(np.float64) - k_hat.astype(np.float64))
+    coef = e @ u                                      # unrounded coefficients
+    q = rng.standard_normal((9, d)).astype(np.float32)
+    s_corr = attention.logits(q, k_hat, coef, u)
+    s_true = attention.logits(q, k)
+    assert np.allclose(s_corr, s_true, rtol=0, atol=1e-12)
+    # rank 0: no correction
+    assert np.array_equal(attention.logits(q, k_hat, coef[:, :0], u[:, :0]), attention.logits(q, k_hat))
