@@ -1,0 +1,115 @@
+"""Helpers of the GPU parity tests: device transfer, library calls on synthetic
+workloads, and the oracle run per (head, tensor) problem in a process pool.
+
+Only tests import this module.  Inputs come from video_model_kv_amd.synth; the
+expected values come from oracle/ alone.
+"""
+from __future__ import annotations
+
+import os
+import sys
+import time
+from concurrent.futures import ProcessPoolExecutor
+
+import numpy as np
+
+import video_model_kv_amd as qk
+from video_model_kv_amd import packed as pk
+
+
+def log(msg: str):
+    print(f"[gpu-test {time.strftime('%H:%M:%S')}] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def torch():
+    import torch as t
+    return t
+
+
+def dev():
+    t = torch()
+    if not t.cuda.is_available():
+        raise RuntimeError("GPU tests need a visible MI355X (torch.cuda.is_available() is False)")
+    qk.lib()      # fail loudly when the HIP library is missing
+    return t.device("cuda")
+
+
+def to_dev(a: np.ndarray, dtype: str = "f32"):
+    """float32 numpy values -> device tensor of the workload dtype (bf16 values are exact)."""
+    t = torch()
+    x = t.from_numpy(np.ascontiguousarray(a, dtype=np.float32))
+    if dtype == "bf16":
+        x = x.to(t.bfloat16)
+    return x.to(dev())
+
+
+def bits16(x) -> np.ndarray:
+    """int16 device/host tensor of bf16 bit patterns -> uint16 numpy."""
+    return x.cpu().numpy().view(np.uint16)
+
+
+def f32_bits_to_bf16(a: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns of bf16-exact float32 values."""
+    u = np.ascontiguousarray(a, np.float32).view(np.uint32)
+    assert not np.any(u & 0xFFFF), "value is not bf16-exact"
+    return (u >> 16).astype(np.uint16)
+
+
+def config_of(wl, tensor: str, n_heads=None, rtn=False) -> qk.Config:
+    mixed = tensor == "K" and wl.n_int4 > 0
+    return qk.Config(n_heads=n_heads or wl.n_heads, n_clusters=wl.n_clusters, bits=wl.bits, group=wl.group,
+                     n_stages=wl.n_stages, kmeans_iters=wl.kmeans_iters,
+                     n_int4_channels=wl.n_int4 if mixed else 0,
+                     psac_rank=wl.psac_rank if tensor == "K" else 0,
+                     use_qsac=1 if (wl.qsac and tensor == "K") else 0,
+                     flags=qk.QKV_FLAG_RTN if rtn else 0)
+
+
+def workspace(cfg: qk.Config, n_tokens: int, n_query: int = 0, n_chunks: int = 0):
+    t = torch()
+    nb = qk.qkv_workspace_bytes(cfg, n_tokens, n_query, n_chunks)
+    return t.empty(max(nb, 256), dtype=t.uint8, device=dev())
+
+
+def quantize(cfg: qk.Config, x_dev, w=None, perm=None, u=None, ws=None):
+    t = torch()
+    n = x_dev.shape[0]
+    lay = qk.qkv_chunk_layout(cfg, n)
+    packed = t.zeros(lay.bytes, dtype=t.uint8, device=dev())
+    ws = workspace(cfg, n) if ws is None else ws
+    qk.qkv_quantize_chunk(cfg, x_dev, packed, ws, w=w, perm=perm, U=u)
+    return packed
+
+
+def host_views(packed, cfg: qk.Config, n_tokens: int) -> dict:
+    v = pk.views(packed, cfg, n_tokens)
+    out = {}
+    for k, val in v.items():
+        if k == "layout" or val is None:
+            out[k] = val
+        else:
+            out[k] = val.cpu().numpy()
+    return out
+
+
+# ---------------------------------------------------------------- oracle pool
+def _oracle_job(args):
+    from oracle import pipeline
+    x, kw = args
+    return pipeline.quantize_problem(x, **kw)
+
+
+def oracle_problems(jobs, workers: int | None = None):
+    """Run oracle.pipeline.quantize_problem for each (x [N, d], kwargs) job."""
+    if len(jobs) == 1:
+        return [_oracle_job(jobs[0])]
+    workers = workers or min(len(jobs), max(1, min(16, len(os.sched_getaffinity(0)))))
+    with ProcessPoolExecutor(max_workers=workers) as ex:
+        return list(ex.map(_oracle_job, jobs))
+
+
+def rel_l2(a, b) -> float:
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300))

@@ -1,0 +1,157 @@
+"""The C-ABI library: it loads, exports every entry point the header declares,
+reports the documented layout, and rejects invalid arguments on the host before
+touching a device (no GPU needed)."""
+import ctypes as ct
+import os
+import re
+
+import numpy as np
+import pytest
+
+from video_model_kv_amd import _binding as B
+from oracle import quant
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 0x100000            # an aligned address that validation never dereferences
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "qkv.h")).read()
+    return sorted(set(re.findall(r"^(?:int|const char\*)\s+(qkv_[a-z_0-9]+)\s*\(", src, re.M)))
+
+
+def test_exports_every_declared_symbol():
+    lib = B.lib()
+    names = _declared()
+    assert len(names) >= 11
+    for n in names:
+        assert hasattr(lib, n), n
+    assert sorted(names) == sorted(B.EXPORTED)
+    assert B.qkv_version() == 1
+
+
+@pytest.mark.parametrize("bits,group,n4", [(2, 32, 0), (2, 64, 0), (4, 32, 0), (2, 16, 0), (2, 32, 26), (2, 128, 0)])
+def test_layout_matches_independent_format(bits, group, n4):
+    cfg = B.Config(n_heads=3, n_clusters=64, bits=bits, group=group, n_int4_channels=n4, n_stages=2, psac_rank=8)
+    n = 1000
+    L = B.qkv_chunk_layout(cfg, n)
+    perm = np.arange(128)
+    ref = quant.channel_layout(128, bits, group, n4, perm)
+    assert L.words_per_token == ref.words
+    assert L.groups_per_token == len(ref.groups)
+    if n4:
+        assert L.int4_words == ref.class_word0[1]
+    al = lambda x: (x + 255) // 256 * 256
+    assert L.stage_bytes_codes == al(3 * n * ref.words * 4)
+    assert L.stage_bytes_scales == al(3 * n * len(ref.groups) * 2)
+    assert L.stage_bytes_labels == al(3 * n)
+    assert L.stage_bytes_centroids == al(3 * 64 * 128 * 2)
+    offs = [L.off_codes, L.off_scales, L.off_labels, L.off_centroids, L.off_perm, L.off_psac]
+    assert offs == sorted(offs) and all(o % 256 == 0 for o in offs)
+    assert L.off_scales == L.off_codes + 2 * L.stage_bytes_codes
+    assert L.bytes == L.off_psac + al(3 * n * 8 * 2)
+
+
+def _cfg(**kw):
+    base = dict(n_heads=2, n_clusters=16)
+    base.update(kw)
+    return B.Config(**base)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(head_dim=64), B.QKV_EUNSUPPORTED),
+    (dict(n_clusters=0), B.QKV_EINVAL),
+    (dict(n_clusters=257), B.QKV_EINVAL),
+    (dict(bits=3), B.QKV_EINVAL),
+    (dict(group=24), B.QKV_EINVAL),
+    (dict(group=8), B.QKV_EINVAL),
+    (dict(n_stages=0), B.QKV_EINVAL),
+    (dict(n_stages=5), B.QKV_EINVAL),
+    (dict(psac_rank=9), B.QKV_EINVAL),
+    (dict(n_int4_channels=128), B.QKV_EINVAL),
+    (dict(n_int4_channels=10, bits=4), B.QKV_EINVAL),
+    (dict(kmeans_iters=0), B.QKV_EINVAL),
+    (dict(flags=4), B.QKV_EINVAL),
+])
+def test_invalid_configs(kw, status):
+    with pytest.raises(B.QkvError) as e:
+        B.qkv_chunk_layout(_cfg(**kw), 100)
+    assert e.value.status == status
+    assert len(B.qkv_last_error()) > 0
+
+
+def test_too_few_tokens():
+    with pytest.raises(B.QkvError) as e:
+        B.qkv_chunk_layout(_cfg(), 15)
+    assert e.value.status == B.QKV_EINVAL
+
+
+def _tensor(n=100, dtype=B.QKV_BF16, ptr=FAKE, st=256, sh=128):
+    return B.qkv_tensor(ptr, dtype, 0, n, st, sh)
+
+
+def _quantize(cfg, x, side=None, packed=FAKE, ws=FAKE, ws_bytes=1 << 40):
+    lib = B.lib()
+    side = side or B.qkv_side(None, None, None)
+    return lib.qkv_quantize_chunk(ct.byref(cfg.c()), ct.byref(x), ct.byref(side), packed, ws, ws_bytes, None)
+
+
+def test_quantize_validation_paths():
+    cfg = _cfg()
+    assert _quantize(cfg, _tensor(ptr=0)) == B.QKV_EINVAL                  # NULL data
+    assert _quantize(cfg, _tensor(ptr=FAKE + 4)) == B.QKV_EINVAL           # misaligned
+    assert _quantize(cfg, _tensor(dtype=7)) == B.QKV_EINVAL
+    assert _quantize(cfg, _tensor(st=100)) == B.QKV_EINVAL                 # stride not a multiple of 8
+    assert _quantize(cfg, _tensor(sh=64)) == B.QKV_EINVAL                  # heads overlap
+    assert _quantize(cfg, _tensor(n=10)) == B.QKV_EINVAL                   # N < C
+    assert _quantize(cfg, _tensor(), packed=None) == B.QKV_EINVAL
+    assert _quantize(cfg, _tensor(), ws=None) == B.QKV_EWORKSPACE
+    assert _quantize(cfg, _tensor(), ws_bytes=1000) == B.QKV_EWORKSPACE
+    assert _quantize(_cfg(use_qsac=1), _tensor()) == B.QKV_EINVAL          # missing w
+    assert _quantize(_cfg(n_int4_channels=26), _tensor()) == B.QKV_EINVAL  # missing perm
+    assert _quantize(_cfg(psac_rank=8), _tensor()) == B.QKV_EINVAL         # missing U
+    assert "U" in B.qkv_last_error()
+
+
+def test_workspace_sizes_grow_with_work():
+    cfg = _cfg(n_heads=32, n_clusters=256)
+    a = B.qkv_workspace_bytes(cfg, 6240)
+    b = B.qkv_workspace_bytes(_cfg(n_heads=32, n_clusters=256, n_stages=3), 6240)
+    c = B.qkv_workspace_bytes(cfg, 6240, 1560, 6)
+    assert 0 < a < b and a <= c
+    # centroids f32 + planes + norms at minimum
+    assert a >= 32 * 256 * 128 * 4 + 32 * 2 * 256 * 128 * 2
+
+
+def test_attend_validation_paths():
+    lib = B.lib()
+    cfg = _cfg()
+    q = _tensor(n=64)
+    out = B.qkv_tensor(FAKE, B.QKV_F32, 0, 64, 256, 128)
+    chunks = (ct.c_void_p * 1)(FAKE)
+    ntok = (ct.c_int64 * 1)(100)
+
+    def call(k_cfg=cfg, v_cfg=cfg, q=q, out=out, n=1, ntok=ntok, U=None, causal=0, scale=0.0, ws_bytes=1 << 40):
+        return lib.qkv_attend(ct.byref(k_cfg.c()), ct.byref(v_cfg.c()), ct.byref(q), chunks, chunks, ntok, n,
+                              U, causal, scale, ct.byref(out), None, FAKE, ws_bytes, None)
+
+    assert call(n=0) == B.QKV_EINVAL
+    assert call(n=2000) == B.QKV_EINVAL
+    assert call(k_cfg=_cfg(n_heads=3)) == B.QKV_EINVAL
+    assert call(k_cfg=_cfg(psac_rank=8)) == B.QKV_EINVAL                  # no U
+    assert call(v_cfg=_cfg(psac_rank=8)) == B.QKV_EINVAL                  # PSAC on V
+    assert call(out=B.qkv_tensor(FAKE, B.QKV_BF16, 0, 64, 256, 128)) == B.QKV_EINVAL
+    assert call(ntok=(ct.c_int64 * 1)(5)) == B.QKV_EINVAL                 # chunk smaller than C
+    assert call(causal=1) == B.QKV_EINVAL                                 # Nq != Nk
+    assert call(scale=-1.0) == B.QKV_EINVAL
+    assert call(ws_bytes=16) == B.QKV_EWORKSPACE
+
+
+def test_psac_fit_validation_paths():
+    lib = B.lib()
+    q = _tensor(n=4096)
+    f = ct.c_float * 2
+    assert lib.qkv_psac_fit(ct.byref(q), 2, 9, 0, FAKE, None, None, f(), FAKE, 1 << 40, None) == B.QKV_EINVAL
+    assert lib.qkv_psac_fit(ct.byref(q), 2, 8, 0, None, None, None, f(), FAKE, 1 << 40, None) == B.QKV_EINVAL
+    assert lib.qkv_psac_fit(ct.byref(q), 0, 8, 0, FAKE, None, None, f(), FAKE, 1 << 40, None) == B.QKV_EINVAL
+    assert lib.qkv_psac_fit(ct.byref(q), 2, 8, 0, FAKE, None, None, f(), FAKE, 64, None) == B.QKV_EWORKSPACE

@@ -1,0 +1,127 @@
+"""GPU parity of the attention over the packed cache against the oracle
+(attention in float64 over the oracle's own dequantized cache, with the PSAC
+term).  Bar: logits within 1e-3 and outputs within 5e-3 relative L2."""
+import numpy as np
+import pytest
+
+import video_model_kv_amd as qk
+from video_model_kv_amd import synth
+from oracle import attention as oa
+from oracle import psac as ops
+
+import gpu_helpers as G
+
+pytestmark = pytest.mark.gpu
+
+LOGIT_TOL = 1e-3
+OUT_TOL = 5e-3
+
+
+def _run(name, wl, chunk_bounds, nq, heads_checked, causal=False, logit_queries=64):
+    t = G.torch()
+    H = wl.n_heads
+    kcfg, vcfg = G.config_of(wl, "K"), G.config_of(wl, "V")
+    w = u = perm = None
+    if wl.qsac or wl.psac_rank or wl.n_int4:
+        hist = synth.history_queries(wl)
+        wlist = [ops.qsac_weights(hist[:, h]) for h in range(H)]
+        if wl.qsac:
+            w = np.stack(wlist)
+        if wl.psac_rank:
+            u = np.stack([ops.principal_subspace(ops.query_gram(hist[:, h]), wl.psac_rank)[0]
+                          for h in range(H)]).astype(np.float32)
+        if wl.n_int4:
+            perm = np.stack([ops.sensitivity_perm(x, wl.n_int4) for x in wlist])
+    wd = None if w is None else G.to_dev(w)
+    ud = None if u is None else G.to_dev(u)
+    pd = None if perm is None else t.from_numpy(perm.astype(np.uint8)).to(G.dev())
+    kch, vch, ntok, xk, xv = [], [], [], [], []
+    maxn = max(b - a for a, b in chunk_bounds)
+    ws = G.workspace(kcfg, maxn, nq, len(chunk_bounds))
+    wsv = G.workspace(vcfg, maxn)
+    for a, b in chunk_bounds:
+        k = synth.kv_tokens(wl, "K", a, b)
+        v = synth.kv_tokens(wl, "V", a, b)
+        xk.append(k)
+        xv.append(v)
+        kch.append(G.quantize(kcfg, G.to_dev(k, wl.dtype), w=wd, perm=pd, u=ud, ws=ws))
+        vch.append(G.quantize(vcfg, G.to_dev(v, wl.dtype), ws=wsv))
+        ntok.append(b - a)
+    q = synth.queries(wl, n=nq)
+    qd = G.to_dev(q, wl.dtype)
+    out = t.empty((nq, H, 128), dtype=t.float32, device=G.dev())
+    G.log(f"attend {name}: H={H} chunks={len(ntok)} Nk={sum(ntok)} Nq={nq} causal={causal} psac={kcfg.psac_rank}")
+    qk.qkv_attend(kcfg, vcfg, qd, kch, vch, ntok, out, ws, U=ud, causal=causal)
+    nk = sum(ntok)
+    nlq = min(logit_queries, nq)
+    logits = t.empty((H, nq, nk), dtype=t.float32, device=G.dev())
+    out2 = t.empty_like(out)
+    qk.qkv_attend(kcfg, vcfg, qd, kch, vch, ntok, out2, ws, U=ud, causal=causal, logits=logits)
+    o = out.cpu().numpy()
+    assert np.array_equal(o, out2.cpu().numpy()), "the logits debug path changed the output"
+    # oracle: quantize the checked heads itself, then attend in float64
+    jobs = []
+    for ci in range(len(chunk_bounds)):
+        for h in heads_checked:
+            for tensor, xs, cfg in (("K", xk, kcfg), ("V", xv, vcfg)):
+                jobs.append((xs[ci][:, h], dict(
+                    n_clusters=wl.n_clusters, bits=wl.bits, group=wl.group, n_stages=wl.n_stages,
+                    iters=wl.kmeans_iters, w=None if (w is None or tensor == "V") else w[h],
+                    n_int4=cfg.n_int4_channels, perm=None if (perm is None or tensor == "V") else perm[h],
+                    u=None if (u is None or tensor == "V") else u[h].astype(np.float64))))
+    res = G.oracle_problems(jobs)
+    lg = logits[:, :nlq].cpu().numpy()
+    for hi, h in enumerate(heads_checked):
+        k_hat = np.concatenate([res[(ci * len(heads_checked) + hi) * 2].x_hat for ci in range(len(chunk_bounds))])
+        v_hat = np.concatenate([res[(ci * len(heads_checked) + hi) * 2 + 1].x_hat for ci in range(len(chunk_bounds))])
+        coef = None
+        if u is not None:
+            coef = np.concatenate([res[(ci * len(heads_checked) + hi) * 2].coef for ci in range(len(chunk_bounds))])
+        ref = oa.attend_head(q[:, h], k_hat, v_hat, coef, None if u is None else u[h].astype(np.float64),
+                             causal=causal)
+        e_out = G.rel_l2(o[:, h], ref)
+        s_ref = oa.logits(q[:nlq, h], k_hat, coef, None if u is None else u[h].astype(np.float64), causal=causal)
+        fin = np.isfinite(s_ref)
+        assert np.array_equal(fin, np.isfinite(lg[h])), f"{name} h{h}: mask differs"
+        e_log = G.rel_l2(lg[h][fin], s_ref[fin])
+        # the unquantized cache, for the quality diagnostic only
+        kx = np.concatenate([x[:, h] for x in xk])
+        vx = np.concatenate([x[:, h] for x in xv])
+        e_q = G.rel_l2(ref, oa.attend_head(q[:, h], kx, vx, causal=causal))
+        G.log(f"attend {name} h{h}: rel-L2 logits {e_log:.3g} (tol {LOGIT_TOL}), out {e_out:.3g} (tol {OUT_TOL}); "
+              f"quantized-vs-bf16-cache out {e_q:.3g}")
+        assert e_log <= LOGIT_TOL, f"{name} h{h}: logits rel-L2 {e_log}"
+        assert e_out <= OUT_TOL, f"{name} h{h}: output rel-L2 {e_out}"
+
+
+def test_tiny_causal_fp32_queries():
+    wl = synth.workload(1)
+    _run("tiny", wl, [(0, 1560)], 1560, [0], causal=True, logit_queries=1560)
+
+
+def test_field_ragged_multi_chunk():
+    wl = synth.workload(2, n_heads=2, n_clusters=64)
+    _run("field-ragged", wl, [(0, 1000), (1000, 2100), (2100, 2300)], 300, [0, 1])
+
+
+def test_progressive_three_stages():
+    wl = synth.workload(3, n_heads=2, n_clusters=64)
+    _run("progressive", wl, [(0, 900), (900, 1700)], 200, [1])
+
+
+def test_quantwm_psac():
+    wl = synth.workload(4, n_heads=2, n_clusters=64)
+    _run("quantwm", wl, [(0, 1200), (1200, 2400)], 260, [0, 1])
+
+
+def test_mixed_precision_keys():
+    wl = synth.workload(5, n_heads=2, n_clusters=64)
+    _run("mixed", wl, [(0, 1100), (1100, 2000)], 150, [0])
+
+
+def test_bench_shape_sampled_head():
+    """The bench workload: 32 heads, 6 chunks of 6,240 tokens, 1,560 queries,
+    in the bench's launch configuration; oracle on one sampled head."""
+    wl = synth.workload(2)
+    bounds = [wl.chunk_range(c) for c in range(wl.n_chunks)]
+    _run("bench-shape", wl, bounds, wl.n_query, [11], logit_queries=64)

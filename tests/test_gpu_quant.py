@@ -1,0 +1,253 @@
+"""GPU parity of the KV write path (k-means assign/update, quant-pack, the whole
+chunk quantizer, dequantization and the query statistics) against the CPU
+oracle on seeded synthetic inputs.
+
+Bar: cluster ids, codes, scales, stored centroids and dequantized values are
+bit-exact.  The fixed k-means protocol lets assignments whose float64 distance
+gap is below 1e-5 relative be excluded; their count is reported (the library
+re-decides such close calls in float64, so they are expected to match too).
+"""
+import numpy as np
+import pytest
+
+import video_model_kv_amd as qk
+from video_model_kv_amd import synth
+from oracle import kmeans as km
+from oracle import psac as ops
+from oracle import quant as oq
+from oracle.numerics import bf16_rne
+
+import gpu_helpers as G
+
+pytestmark = pytest.mark.gpu
+
+NEAR_TIE = 1e-5
+
+# (case id, workload id, overrides, tensor, n_tokens or None for a full chunk)
+SMALL = [
+    ("tiny-K", 1, {}, "K", None),
+    ("tiny-V", 1, {}, "V", None),
+    ("field-K-ragged", 2, dict(n_heads=2, n_clusters=64), "K", 1500),
+    ("field-V-ragged", 2, dict(n_heads=2, n_clusters=64), "V", 1500),
+    ("qsac-K", 4, dict(n_heads=2, n_clusters=64), "K", 1300),
+]
+
+
+def _inputs(cid, over, tensor, n):
+    wl = synth.workload(cid, **over)
+    n = n or wl.chunk_tokens
+    x = synth.kv_tokens(wl, tensor, 0, n)
+    w = None
+    if wl.qsac and tensor == "K":
+        hist = synth.history_queries(wl)
+        w = np.stack([ops.qsac_weights(hist[:, h]) for h in range(wl.n_heads)])
+    return wl, x, w
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[c[0] for c in SMALL])
+def test_assign_and_update_lockstep(case):
+    name, cid, over, tensor, n = case
+    wl, x, w = _inputs(cid, over, tensor, n)
+    H, N, C = wl.n_heads, x.shape[0], wl.n_clusters
+    G.log(f"lockstep {name}: H={H} N={N} C={C} dtype={wl.dtype}")
+    traces = [km.kmeans(x[:, h], C, wl.kmeans_iters, None if w is None else w[h], track_objective=False)
+              for h in range(H)]
+    t = G.torch()
+    cfg = G.config_of(wl, tensor)
+    xd = G.to_dev(x, wl.dtype)
+    ws = G.workspace(cfg, N)
+    wd = None if w is None else G.to_dev(w)
+    labels = t.empty(H * N, dtype=t.uint8, device=G.dev())
+    counts = t.empty(H * C, dtype=t.int32, device=G.dev())
+    near_total = mism_near = 0
+    for it in range(wl.kmeans_iters):
+        cin = np.stack([tr.centroids_in[it] for tr in traces])
+        qk.qkv_kmeans_assign(cfg, xd, G.to_dev(cin), labels, ws, w=wd)
+        got = labels.cpu().numpy().reshape(H, N)
+        for h, tr in enumerate(traces):
+            near = tr.gaps_iter[it] < NEAR_TIE
+            mism = got[h] != tr.labels_iter[it]
+            assert not np.any(mism & ~near), f"{name} iter {it} head {h}: {int((mism & ~near).sum())} label mismatches"
+            near_total += int(near.sum())
+            mism_near += int((mism & near).sum())
+        # update from the oracle's labels of this iteration
+        lab = np.stack([tr.labels_iter[it] for tr in traces]).astype(np.uint8)
+        cd = G.to_dev(cin)
+        qk.qkv_kmeans_update(cfg, xd, t.from_numpy(lab.reshape(-1)).to(G.dev()), cd, counts)
+        exp = np.stack([tr.centroids_in[it + 1] if it + 1 < wl.kmeans_iters else tr.centroids for tr in traces])
+        got_c = cd.cpu().numpy()
+        assert np.array_equal(got_c.view(np.uint32), exp.view(np.uint32)), \
+            f"{name} iter {it}: {int((got_c != exp).sum())} centroid values differ"
+        exp_counts = np.stack([np.bincount(lab[h], minlength=C) for h in range(H)])
+        assert np.array_equal(counts.cpu().numpy().reshape(H, C), exp_counts)
+    G.log(f"lockstep {name}: near-ties {near_total}, of which mismatched {mism_near}")
+
+
+@pytest.mark.parametrize("case", SMALL + [("mixed-K", 5, dict(n_heads=2, n_clusters=64, frames=1), "K", 1560)],
+                         ids=[c[0] for c in SMALL] + ["mixed-K"])
+def test_quant_pack_lockstep(case):
+    name, cid, over, tensor, n = case
+    wl, x, w = _inputs(cid, over, tensor, n)
+    H, N, C = wl.n_heads, x.shape[0], wl.n_clusters
+    G.log(f"quant_pack {name}: H={H} N={N}")
+    rng = np.random.default_rng(7)
+    perm = None
+    if tensor == "K" and wl.n_int4:
+        perm = np.stack([rng.permutation(128) for _ in range(H)])
+    # oracle labels/centroids (a few iterations are enough for this step)
+    traces = [km.kmeans(x[:, h], C, 3, None if w is None else w[h], track_objective=False) for h in range(H)]
+    cfg = G.config_of(wl, tensor)
+    t = G.torch()
+    lay = qk.qkv_chunk_layout(cfg, N)
+    packed = t.zeros(lay.bytes, dtype=t.uint8, device=G.dev())
+    lab = np.stack([tr.labels for tr in traces]).astype(np.uint8)
+    cent = np.stack([tr.centroids for tr in traces])
+    ynext = t.empty((H, N, 128), dtype=t.float32, device=G.dev())
+    permd = None if perm is None else t.from_numpy(perm.astype(np.uint8)).to(G.dev())
+    qk.qkv_quant_pack(cfg, G.to_dev(x, wl.dtype), t.from_numpy(lab.reshape(-1)).to(G.dev()), G.to_dev(cent),
+                      packed, 0, perm=permd, y_next=ynext)
+    v = G.host_views(packed, cfg, N)
+    yn = ynext.cpu().numpy()
+    for h in range(H):
+        layout = oq.channel_layout(128, wl.bits, wl.group, cfg.n_int4_channels, None if perm is None else perm[h])
+        cbf = bf16_rne(cent[h])
+        rows = cbf[lab[h].astype(np.int64)]
+        r = (x[:, h] - rows).astype(np.float32)
+        q, s = oq.quantize_groups(r, layout)
+        assert np.array_equal(v["codes"][0, h].view(np.uint32), oq.pack_codes(q, layout)), f"{name} head {h}: codes"
+        assert np.array_equal(v["scales"][0, h].view(np.uint16), G.f32_bits_to_bf16(s)), f"{name} head {h}: scales"
+        assert np.array_equal(v["centroids"][0, h].view(np.uint16), G.f32_bits_to_bf16(cbf))
+        assert np.array_equal(v["labels"][0, h], lab[h])
+        yhat = oq.dequantize(q, s, rows, layout)
+        assert np.array_equal(yn[h].view(np.uint32), (x[:, h] - yhat).astype(np.float32).view(np.uint32))
+        if perm is not None:
+            assert np.array_equal(v["perm"][h], perm[h].astype(np.uint8))
+
+
+FREE = [
+    ("tiny-K", 1, {}, "K", None, False),
+    ("tiny-V-rtn", 1, {}, "V", None, True),
+    ("field-V", 2, dict(n_heads=2, n_clusters=64), "V", 1500, False),
+    ("progressive-K", 3, dict(n_heads=2, n_clusters=64), "K", 1500, False),
+    ("quantwm-K", 4, dict(n_heads=2, n_clusters=64), "K", 1300, False),
+    ("mixed-K", 5, dict(n_heads=2, n_clusters=64), "K", 1500, False),
+]
+
+
+def _side(wl, tensor):
+    """Oracle-computed side inputs (QSAC weights, PSAC basis, channel order)."""
+    w = u = perm = None
+    if tensor == "K" and (wl.qsac or wl.psac_rank or wl.n_int4):
+        hist = synth.history_queries(wl)
+        ws_ = [ops.qsac_weights(hist[:, h]) for h in range(wl.n_heads)]
+        if wl.qsac:
+            w = np.stack(ws_)
+        if wl.psac_rank:
+            u = np.stack([ops.principal_subspace(ops.query_gram(hist[:, h]), wl.psac_rank)[0]
+                          for h in range(wl.n_heads)]).astype(np.float32)
+        if wl.n_int4:
+            perm = np.stack([ops.sensitivity_perm(x, wl.n_int4) for x in ws_])
+    return w, u, perm
+
+
+def compare_chunk(name, wl, tensor, x, packed, cfg, res_by_head, heads):
+    v = G.host_views(packed, cfg, x.shape[0])
+    near = 0
+    for h in heads:
+        res = res_by_head[h]
+        for l, st in enumerate(res.stages):
+            if st.trace is not None:
+                near += int(sum((g < NEAR_TIE).sum() for g in st.trace.gaps_iter))
+            assert np.array_equal(v["labels"][l, h], st.labels.astype(np.uint8)), f"{name} h{h} stage {l}: labels"
+            assert np.array_equal(v["centroids"][l, h].view(np.uint16), G.f32_bits_to_bf16(st.centroids_bf16)), \
+                f"{name} h{h} stage {l}: centroids"
+            assert np.array_equal(v["codes"][l, h].view(np.uint32), oq.pack_codes(st.q, res.layout)), \
+                f"{name} h{h} stage {l}: codes"
+            assert np.array_equal(v["scales"][l, h].view(np.uint16), G.f32_bits_to_bf16(st.scales)), \
+                f"{name} h{h} stage {l}: scales"
+        if res.coef is not None:
+            got = v["psac"][h].view(np.uint16)
+            exp = G.f32_bits_to_bf16(res.coef)
+            diff = np.abs(got.astype(np.int32) - exp.astype(np.int32))
+            assert diff.max() <= 1 and (diff > 0).mean() < 1e-3, f"{name} h{h}: psac coefficients"
+    return near
+
+
+@pytest.mark.parametrize("case", FREE, ids=[c[0] for c in FREE])
+def test_quantize_chunk_free_running(case):
+    name, cid, over, tensor, n, rtn = case
+    wl = synth.workload(cid, **over)
+    n = n or wl.chunk_tokens
+    x = synth.kv_tokens(wl, tensor, 0, n)
+    w, u, perm = _side(wl, tensor)
+    cfg = G.config_of(wl, tensor, rtn=rtn)
+    G.log(f"free-running {name}: H={wl.n_heads} N={n} stages={cfg.n_stages} qsac={cfg.use_qsac} "
+          f"psac={cfg.psac_rank} int4={cfg.n_int4_channels}")
+    t = G.torch()
+    packed = G.quantize(cfg, G.to_dev(x, wl.dtype),
+                        w=None if w is None else G.to_dev(w),
+                        perm=None if perm is None else t.from_numpy(perm.astype(np.uint8)).to(G.dev()),
+                        u=None if u is None else G.to_dev(u))
+    jobs = [(x[:, h], dict(n_clusters=wl.n_clusters, bits=wl.bits, group=wl.group, n_stages=wl.n_stages,
+                           iters=wl.kmeans_iters, w=None if w is None else w[h], n_int4=cfg.n_int4_channels,
+                           perm=None if perm is None else perm[h],
+                           u=None if u is None else u[h].astype(np.float64), rtn=rtn))
+            for h in range(wl.n_heads)]
+    res = dict(enumerate(G.oracle_problems(jobs)))
+    near = compare_chunk(name, wl, tensor, x, packed, cfg, res, range(wl.n_heads))
+    # dequantization, f32 and bf16 outputs
+    out = t.empty((n, wl.n_heads, 128), dtype=t.float32, device=G.dev())
+    qk.qkv_dequantize(cfg, n, packed, out)
+    outb = t.empty((n, wl.n_heads, 128), dtype=t.bfloat16, device=G.dev())
+    qk.qkv_dequantize(cfg, n, packed, outb)
+    o = out.cpu().numpy()
+    ob = outb.view(t.int16).cpu().numpy().view(np.uint16)
+    for h in range(wl.n_heads):
+        assert np.array_equal(o[:, h].view(np.uint32), res[h].x_hat.view(np.uint32)), f"{name} h{h}: x_hat"
+        assert np.array_equal(ob[:, h], G.f32_bits_to_bf16(bf16_rne(res[h].x_hat)))
+    err = G.rel_l2(o, x)
+    G.log(f"free-running {name}: bit-exact; near-ties in oracle trace {near}; rel-L2(x_hat, x) = {err:.4g}")
+
+
+def test_full_chunk_bench_shape_sampled_heads():
+    """The bench workload's chunk (32 heads x 6,240 tokens, C = 256, INT2, g = 32)
+    in the bench's launch configuration; the oracle recomputes sampled heads."""
+    wl = synth.workload(2)
+    t = G.torch()
+    for tensor, heads in (("K", [0, 17, 31]), ("V", [5, 31])):
+        x = synth.kv_chunk(wl, tensor, 0)
+        cfg = G.config_of(wl, tensor)
+        G.log(f"bench-shape chunk {tensor}: N={x.shape[0]} H={wl.n_heads}; oracle heads {heads}")
+        packed = G.quantize(cfg, G.to_dev(x, "bf16"))
+        t.cuda.synchronize()
+        jobs = [(x[:, h], dict(n_clusters=wl.n_clusters, bits=2, group=32, iters=10)) for h in heads]
+        res = dict(zip(heads, G.oracle_problems(jobs)))
+        near = compare_chunk(f"bench-{tensor}", wl, tensor, x, packed, cfg, res, heads)
+        G.log(f"bench-shape chunk {tensor}: bit-exact on heads {heads}; near-ties {near}")
+
+
+def test_psac_fit_matches_oracle():
+    wl = synth.workload(4)
+    hist = synth.history_queries(wl)
+    H = wl.n_heads
+    G.log(f"psac_fit: n={hist.shape[0]} H={H}")
+    t = G.torch()
+    cfg = G.config_of(wl, "K")
+    ws = G.workspace(cfg, 0, hist.shape[0], 0)
+    U = t.empty((H, 128, 8), dtype=t.float32, device=G.dev())
+    w = t.empty((H, 128), dtype=t.float32, device=G.dev())
+    perm = t.empty((H, 128), dtype=t.uint8, device=G.dev())
+    energy = qk.qkv_psac_fit(G.to_dev(hist, "bf16"), H, 8, 26, ws, U_out=U, w_out=w, perm_out=perm)
+    Ug, wg, pg = U.cpu().numpy(), w.cpu().numpy(), perm.cpu().numpy()
+    worst = 0.0
+    for h in range(H):
+        m = ops.query_gram(hist[:, h])
+        uo, lam, eo = ops.principal_subspace(m, 8)
+        wo = ops.qsac_weights(hist[:, h])
+        assert np.array_equal(wg[h].view(np.uint32), wo.view(np.uint32)), f"head {h}: weights"
+        assert np.array_equal(pg[h], ops.sensitivity_perm(wo, 26).astype(np.uint8)), f"head {h}: perm"
+        assert abs(energy[h] - eo) < 1e-6
+        dp = np.linalg.norm(Ug[h].astype(np.float64) @ Ug[h].T.astype(np.float64) - uo @ uo.T)
+        worst = max(worst, dp)
+        assert dp < 1e-4, f"head {h}: projector differs by {dp}"
+    G.log(f"psac_fit: weights/perm exact, worst projector difference {worst:.3g}, energy[0] {energy[0]:.4f}")

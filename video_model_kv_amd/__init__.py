@@ -1,0 +1,13 @@
+"""libqkv for MI355X: KV-chunk quantization (k-means smoothing, per-group INT2/INT4,
+progressive residual stages, QSAC/PSAC) and attention over the packed cache.
+
+The compute lives in the HIP library ``libqkv.so`` (C-ABI: include/qkv.h); this
+package is its thin ctypes binding (``_binding``), helpers that slice a packed
+chunk into typed views (``packed``), and the seeded synthetic inputs
+(``synth``).
+"""
+from ._binding import (  # noqa: F401
+    Config, QkvError, qkv_attend, qkv_chunk_layout, qkv_dequantize, qkv_kmeans_assign,
+    qkv_kmeans_update, qkv_last_error, qkv_psac_fit, qkv_quant_pack, qkv_quantize_chunk,
+    qkv_version, qkv_workspace_bytes, lib, tensor_desc, QKV_FLAG_RTN,
+)

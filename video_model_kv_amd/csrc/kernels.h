@@ -1,0 +1,107 @@
+// Internal launch interface between the host API (qkv_host.cpp) and the HIP
+// kernels.  Every launcher enqueues on `stream` and returns the launch status.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "layout.h"
+
+namespace qkv {
+
+// A strided [n_tokens][n_heads][128] tensor (f32 or bf16; dtype 0 = f32, 1 = bf16).
+struct TensorView {
+  const void* ptr;
+  int dtype;
+  int64_t n_tokens, stride_token, stride_head;
+};
+
+// Channel decode of one head: for original channel k, where its code lives.
+//   word index (within the token's words), bit shift, code bits, group index.
+struct ChannelCode {
+  uint8_t word, shift, bits, group;
+};
+
+// ---- k-means (kmeans.hip) ----
+// Centroids c: f32 [H][C][128].  planes: bf16 bits [H][2][C][128], the split
+// hi/lo of fp32(w * c) used as the MFMA operand of the distance GEMM.
+// cn: f32 [H][C], sum_k w_k c_k^2 (rounded from float64).
+hipError_t launch_kmeans_init(const TensorView& y, int H, int C, float* c, hipStream_t s);
+hipError_t launch_centroid_prep(int H, int C, const float* c, const float* w, uint16_t* planes,
+                                float* cn, hipStream_t s);
+hipError_t launch_kmeans_assign(const TensorView& y, int H, int C, const uint16_t* planes,
+                                const float* cn, const float* c, const float* w, uint8_t* labels,
+                                hipStream_t s);
+hipError_t launch_kmeans_update(const TensorView& y, int H, int C, const uint8_t* labels, float* c,
+                                int32_t* counts, hipStream_t s);
+hipError_t launch_centroid_bf16(int H, int C, const float* c, uint16_t* out, hipStream_t s);
+hipError_t launch_fill_zero_u32(void* p, size_t n_words, hipStream_t s);
+
+// ---- quantize / dequantize (quant.hip) ----
+struct PackArgs {
+  TensorView y;          // stage input
+  int H, C, N;
+  const uint8_t* labels;       // [H][N]
+  const uint16_t* centroids;   // bf16 [H][C][128]
+  const uint8_t* perm;         // [H][128] or null (identity)
+  int bits, group, n_int4, int4_words;
+  uint32_t* codes;             // [H][N][words]
+  uint16_t* scales;            // bf16 [H][N][groups]
+  int words, groups;
+  float* y_next;               // f32 [H][N][128] or null
+};
+hipError_t launch_quant_pack(const PackArgs& a, hipStream_t s);
+
+hipError_t launch_dequantize(const ChunkDecode& d, void* out, int out_dtype, int64_t stride_token,
+                             int64_t stride_head, hipStream_t s);
+hipError_t launch_psac_encode(const ChunkDecode& d, const TensorView& x, const float* U,
+                              uint16_t* coef_out, hipStream_t s);
+hipError_t launch_copy_perm(const uint8_t* perm, uint8_t* dst, int H, hipStream_t s);
+
+// ---- history-query statistics (gram.hip) ----
+hipError_t launch_gram(const TensorView& q, int H, double* partial, int n_split, double* m,
+                       hipStream_t s);
+
+// ---- attention (attend.hip) ----
+constexpr int kMaxChunks = 1024;
+constexpr int kChunkBatch = 96;      // chunk records per upload launch (fits the kernel-argument limit)
+
+// Per-chunk record of the concatenated cache (device array in the workspace).
+struct ChunkRec {
+  const uint8_t* kbase;
+  const uint8_t* vbase;
+  int64_t token_start;   // global index of the chunk's first token
+  int32_t n;             // tokens in the chunk
+  int32_t tile_start;    // global index of the chunk's first 64-key tile
+};
+
+struct ChunkBatch {
+  int32_t first, count;
+  ChunkRec rec[kChunkBatch];
+};
+hipError_t launch_upload_chunks(const ChunkBatch& b, ChunkRec* dst, hipStream_t s);
+
+struct AttendArgs {
+  TensorView q;
+  int H, Nq;
+  int64_t Nk;
+  int n_chunks, n_tiles;
+  LayoutParams kp, vp;           // layouts of the K and V chunks
+  const ChunkRec* chunks;        // device [n_chunks]
+  const float* U;                // [H][128][r] or null
+  int psac_rank;
+  float* qu;                     // workspace [H][Nq][8] f32
+  int causal;
+  float scale;
+  int n_split;                   // split s covers tiles [n_tiles*s/n_split, n_tiles*(s+1)/n_split)
+  float* part_o;                 // [n_split][H][Nq][128]
+  float* part_ml;                // [n_split][H][Nq][2]
+  float* out;                    // [Nq][H][128] via strides
+  int64_t out_stride_token, out_stride_head;
+  float* logits;                 // [H][Nq][Nk] or null
+  bool k_uniform_int2_1stage;    // fast-path selectors: one uniform INT2 stage,
+  bool v_uniform_int2_1stage;    // groups of a multiple of 32 channels
+};
+hipError_t launch_attend(const AttendArgs& a, hipStream_t s);
+
+}  // namespace qkv

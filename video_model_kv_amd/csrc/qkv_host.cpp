@@ -1,0 +1,574 @@
+// libqkv host side: argument validation, packed-chunk layout, workspace
+// planning and launch sequencing of the C-ABI declared in include/qkv.h.
+//
+// Everything here runs before any work is enqueued, so each error path is
+// reachable without a GPU.  The library holds no device state: all device
+// memory is caller-owned (packed chunks, workspace, outputs).
+#include "qkv.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <thread>
+#include <vector>
+
+#include "kernels.h"
+
+namespace qkv {
+void jacobi_eigh(int n, double* a, double* evals, double* evecs);
+}
+
+using namespace qkv;
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int status, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return status;
+}
+
+int ok() {
+  g_err.clear();
+  return QKV_OK;
+}
+
+#define QKV_HIP(expr)                                                                 \
+  do {                                                                                \
+    hipError_t e_ = (expr);                                                           \
+    if (e_ != hipSuccess) return fail(QKV_EDEVICE, "%s: %s", #expr, hipGetErrorString(e_)); \
+  } while (0)
+
+#define QKV_TRY(expr)           \
+  do {                          \
+    int st_ = (expr);           \
+    if (st_ != QKV_OK) return st_; \
+  } while (0)
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+int check_config(const qkv_config* c, const char* what) {
+  if (!c) return fail(QKV_EINVAL, "%s: config is NULL", what);
+  if (c->head_dim != kHeadDim)
+    return fail(QKV_EUNSUPPORTED, "%s: head_dim %d (this build supports 128)", what, c->head_dim);
+  if (c->n_heads < 1 || c->n_heads > 1024) return fail(QKV_EINVAL, "%s: n_heads %d not in [1, 1024]", what, c->n_heads);
+  if (c->n_clusters < 1 || c->n_clusters > kMaxClusters)
+    return fail(QKV_EINVAL, "%s: n_clusters %d not in [1, 256]", what, c->n_clusters);
+  if (c->kmeans_iters < 1 || c->kmeans_iters > 1000)
+    return fail(QKV_EINVAL, "%s: kmeans_iters %d not in [1, 1000]", what, c->kmeans_iters);
+  if (c->n_stages < 1 || c->n_stages > kMaxStages)
+    return fail(QKV_EINVAL, "%s: n_stages %d not in [1, %d]", what, c->n_stages, kMaxStages);
+  if (c->bits != 2 && c->bits != 4) return fail(QKV_EINVAL, "%s: bits %d (2 or 4)", what, c->bits);
+  if (c->group != 16 && c->group != 32 && c->group != 64 && c->group != 128)
+    return fail(QKV_EINVAL, "%s: group %d must be a multiple of 16 dividing 128", what, c->group);
+  if (c->n_int4_channels < 0 || c->n_int4_channels >= kHeadDim)
+    return fail(QKV_EINVAL, "%s: n_int4_channels %d not in [0, 127]", what, c->n_int4_channels);
+  if (c->n_int4_channels > 0 && c->bits != 2)
+    return fail(QKV_EINVAL, "%s: the mixed layout needs bits == 2 for the base class", what);
+  if (c->psac_rank < 0 || c->psac_rank > kMaxRank)
+    return fail(QKV_EINVAL, "%s: psac_rank %d not in [0, 8]", what, c->psac_rank);
+  if (c->use_qsac != 0 && c->use_qsac != 1) return fail(QKV_EINVAL, "%s: use_qsac must be 0 or 1", what);
+  if (c->flags & ~QKV_FLAG_RTN) return fail(QKV_EINVAL, "%s: unknown flags 0x%x", what, c->flags);
+  return QKV_OK;
+}
+
+LayoutParams params_of(const qkv_config* c) {
+  LayoutParams p;
+  p.H = c->n_heads;
+  p.C = c->n_clusters;
+  p.n_stages = c->n_stages;
+  p.bits = c->bits;
+  p.group = c->group;
+  p.n_int4 = c->n_int4_channels;
+  p.psac_rank = c->psac_rank;
+  return p;
+}
+
+ChunkDecode decode_of(const qkv_config* c, int64_t n, const void* base) {
+  return make_decode(params_of(c), n, base);
+}
+
+void layout_of(const qkv_config* c, int64_t n, qkv_layout* L) {
+  const ChunkDecode d = decode_of(c, n, nullptr);
+  std::memset(L, 0, sizeof *L);
+  L->bytes = d.bytes;
+  L->off_codes = d.off_codes;
+  L->stage_bytes_codes = d.stage_codes;
+  L->off_scales = d.off_scales;
+  L->stage_bytes_scales = d.stage_scales;
+  L->off_labels = d.off_labels;
+  L->stage_bytes_labels = d.stage_labels;
+  L->off_centroids = d.off_centroids;
+  L->stage_bytes_centroids = d.stage_centroids;
+  L->off_perm = d.off_perm;
+  L->off_psac = d.off_psac;
+  L->words_per_token = d.words;
+  L->groups_per_token = d.groups;
+  L->int4_words = d.int4_words;
+  L->n_tokens = n;
+}
+
+int check_tensor(const qkv_tensor* t, int n_heads, const char* what, bool allow_f32 = true) {
+  if (!t) return fail(QKV_EINVAL, "%s: tensor is NULL", what);
+  if (!t->ptr) return fail(QKV_EINVAL, "%s: data pointer is NULL", what);
+  if (!aligned16(t->ptr)) return fail(QKV_EINVAL, "%s: data pointer not 16-byte aligned", what);
+  if (t->dtype != QKV_F32 && t->dtype != QKV_BF16) return fail(QKV_EINVAL, "%s: dtype %d", what, t->dtype);
+  if (!allow_f32 && t->dtype == QKV_F32) return fail(QKV_EUNSUPPORTED, "%s: f32 not supported here", what);
+  if (t->n_tokens < 1 || t->n_tokens > (int64_t)1 << 24) return fail(QKV_EINVAL, "%s: n_tokens %lld", what, (long long)t->n_tokens);
+  if (t->stride_token < 0 || t->stride_head < 0 || t->stride_token % 8 || t->stride_head % 8)
+    return fail(QKV_EINVAL, "%s: strides must be non-negative multiples of 8 elements", what);
+  if (n_heads > 1 && t->stride_head < kHeadDim)
+    return fail(QKV_EINVAL, "%s: head stride %lld overlaps the channel dimension", what, (long long)t->stride_head);
+  if (t->n_tokens > 1 && t->stride_token < kHeadDim)
+    return fail(QKV_EINVAL, "%s: token stride %lld overlaps the channel dimension", what, (long long)t->stride_token);
+  return QKV_OK;
+}
+
+TensorView view_of(const qkv_tensor* t) {
+  TensorView v;
+  v.ptr = t->ptr;
+  v.dtype = t->dtype == QKV_F32 ? 0 : 1;
+  v.n_tokens = t->n_tokens;
+  v.stride_token = t->stride_token;
+  v.stride_head = t->stride_head;
+  return v;
+}
+
+// ---- workspace plans ----
+struct QuantWs {
+  uint64_t c, planes, cn, ybuf0, ybuf1, bytes;
+};
+
+QuantWs quant_ws(const qkv_config* c, int64_t n) {
+  const uint64_t H = c->n_heads, C = c->n_clusters;
+  QuantWs w;
+  uint64_t off = 0;
+  w.c = off;       off += align256(H * C * kHeadDim * 4);
+  w.planes = off;  off += align256(H * 2 * C * kHeadDim * 2);
+  w.cn = off;      off += align256(H * C * 4);
+  w.ybuf0 = off;   if (c->n_stages > 1) off += align256(H * (uint64_t)n * kHeadDim * 4);
+  w.ybuf1 = off;   if (c->n_stages > 2) off += align256(H * (uint64_t)n * kHeadDim * 4);
+  w.bytes = off;
+  return w;
+}
+
+constexpr int kTileKeys = 64;
+
+struct AttendWs {
+  uint64_t chunks, qu, part_o, part_ml, bytes;
+};
+
+AttendWs attend_ws(int H, int64_t nq, int n_chunks, int n_split) {
+  AttendWs w;
+  uint64_t off = 0;
+  w.chunks = off;  off += align256((uint64_t)n_chunks * sizeof(ChunkRec));
+  w.qu = off;      off += align256((uint64_t)H * nq * kMaxRank * 4);
+  w.part_o = off;  if (n_split > 1) off += align256((uint64_t)n_split * H * nq * kHeadDim * 4);
+  w.part_ml = off; if (n_split > 1) off += align256((uint64_t)n_split * H * nq * 2 * 4);
+  w.bytes = off;
+  return w;
+}
+
+// Key splits: enough workgroups to fill the chip several times over.
+int choose_splits(int H, int64_t nq, int64_t n_tiles) {
+  const int64_t q_tiles = (nq + 127) / 128;
+  const int64_t base = q_tiles * H;
+  int64_t want = (4096 + base - 1) / base;                       // >= 4096 workgroups
+  want = std::max<int64_t>(1, std::min<int64_t>(want, n_tiles));
+  want = std::min<int64_t>(want, 256);
+  return (int)want;
+}
+
+int64_t max_tiles(int64_t max_chunk_tokens, int n_chunks) {
+  return (int64_t)n_chunks * ((max_chunk_tokens + kTileKeys - 1) / kTileKeys);
+}
+
+constexpr int kGramSplit = 16;
+
+uint64_t psac_ws(int H) {
+  return align256((uint64_t)kGramSplit * H * kHeadDim * kHeadDim * 8) + align256((uint64_t)H * kHeadDim * kHeadDim * 8);
+}
+
+int check_ws(const void* ws, size_t have, uint64_t need, const char* what) {
+  if (need == 0) return QKV_OK;
+  if (!ws) return fail(QKV_EWORKSPACE, "%s: workspace is NULL (%llu bytes needed)", what, (unsigned long long)need);
+  if (!aligned16(ws)) return fail(QKV_EINVAL, "%s: workspace not 16-byte aligned", what);
+  if (have < need)
+    return fail(QKV_EWORKSPACE, "%s: workspace has %zu bytes, %llu needed", what, have, (unsigned long long)need);
+  return QKV_OK;
+}
+
+uint8_t* at(void* base, uint64_t off) { return reinterpret_cast<uint8_t*>(base) + off; }
+
+// Run the k-means protocol of one stage on `y`; labels go to `labels`.
+int run_kmeans(const qkv_config* cfg, const TensorView& y, const float* w, uint8_t* labels, float* c,
+               uint16_t* planes, float* cn, hipStream_t s) {
+  const int H = cfg->n_heads, C = cfg->n_clusters;
+  QKV_HIP(launch_kmeans_init(y, H, C, c, s));
+  for (int it = 0; it < cfg->kmeans_iters; ++it) {
+    QKV_HIP(launch_centroid_prep(H, C, c, w, planes, cn, s));
+    QKV_HIP(launch_kmeans_assign(y, H, C, planes, cn, c, w, labels, s));
+    QKV_HIP(launch_kmeans_update(y, H, C, labels, c, nullptr, s));
+  }
+  return QKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int qkv_version(void) { return QKV_VERSION; }
+
+const char* qkv_last_error(void) { return g_err.c_str(); }
+
+int qkv_chunk_layout(const qkv_config* cfg, int64_t n_tokens, qkv_layout* out) {
+  QKV_TRY(check_config(cfg, "qkv_chunk_layout"));
+  if (!out) return fail(QKV_EINVAL, "qkv_chunk_layout: out is NULL");
+  if (n_tokens < cfg->n_clusters || n_tokens > ((int64_t)1 << 24))
+    return fail(QKV_EINVAL, "qkv_chunk_layout: n_tokens %lld must be in [n_clusters, 2^24]", (long long)n_tokens);
+  layout_of(cfg, n_tokens, out);
+  return ok();
+}
+
+int qkv_workspace_bytes(const qkv_config* cfg, int64_t max_chunk_tokens, int64_t n_query, int32_t n_chunks,
+                        size_t* out) {
+  QKV_TRY(check_config(cfg, "qkv_workspace_bytes"));
+  if (!out) return fail(QKV_EINVAL, "qkv_workspace_bytes: out is NULL");
+  if (max_chunk_tokens < 0 || n_query < 0 || n_chunks < 0 || n_chunks > kMaxChunks)
+    return fail(QKV_EINVAL, "qkv_workspace_bytes: negative size or n_chunks > %d", kMaxChunks);
+  uint64_t need = 0;
+  if (max_chunk_tokens > 0) need = std::max(need, quant_ws(cfg, max_chunk_tokens).bytes);
+  if (n_query > 0 && n_chunks > 0) {
+    const int64_t nt = max_tiles(std::max<int64_t>(max_chunk_tokens, 1), n_chunks);
+    const int ns = choose_splits(cfg->n_heads, n_query, nt);
+    need = std::max(need, attend_ws(cfg->n_heads, n_query, n_chunks, ns).bytes);
+  }
+  if (n_query > 0) need = std::max(need, psac_ws(cfg->n_heads));
+  *out = (size_t)need;
+  return ok();
+}
+
+int qkv_quantize_chunk(const qkv_config* cfg, const qkv_tensor* x, const qkv_side* side, void* packed,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+  const char* fn = "qkv_quantize_chunk";
+  QKV_TRY(check_config(cfg, fn));
+  QKV_TRY(check_tensor(x, cfg->n_heads, fn));
+  const int64_t N = x->n_tokens;
+  if (N < cfg->n_clusters) return fail(QKV_EINVAL, "%s: n_tokens %lld < n_clusters %d", fn, (long long)N, cfg->n_clusters);
+  if (!packed || !aligned16(packed)) return fail(QKV_EINVAL, "%s: packed is NULL or not 16-byte aligned", fn);
+  const float* w = side ? side->w : nullptr;
+  const uint8_t* perm = side ? side->perm : nullptr;
+  const float* U = side ? side->U : nullptr;
+  if (cfg->use_qsac && !w) return fail(QKV_EINVAL, "%s: use_qsac needs side->w", fn);
+  if (cfg->n_int4_channels > 0 && !perm) return fail(QKV_EINVAL, "%s: the mixed layout needs side->perm", fn);
+  if (cfg->psac_rank > 0 && !U) return fail(QKV_EINVAL, "%s: psac_rank > 0 needs side->U", fn);
+  const QuantWs ws = quant_ws(cfg, N);
+  QKV_TRY(check_ws(workspace, workspace_bytes, ws.bytes, fn));
+
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const int H = cfg->n_heads, C = cfg->n_clusters;
+  qkv_layout L;
+  layout_of(cfg, N, &L);
+  const ChunkDecode g = decode_of(cfg, N, nullptr);
+  uint8_t* base = reinterpret_cast<uint8_t*>(packed);
+  float* c = reinterpret_cast<float*>(at(workspace, ws.c));
+  uint16_t* planes = reinterpret_cast<uint16_t*>(at(workspace, ws.planes));
+  float* cn = reinterpret_cast<float*>(at(workspace, ws.cn));
+  const float* wk = cfg->use_qsac ? w : nullptr;
+  const uint8_t* pm = cfg->n_int4_channels > 0 ? perm : nullptr;
+  if (pm) QKV_HIP(launch_copy_perm(pm, base + L.off_perm, H, s));
+
+  TensorView y = view_of(x);
+  for (int l = 0; l < cfg->n_stages; ++l) {
+    uint8_t* labels = base + L.off_labels + (uint64_t)l * L.stage_bytes_labels;
+    uint16_t* cent = reinterpret_cast<uint16_t*>(base + L.off_centroids + (uint64_t)l * L.stage_bytes_centroids);
+    if (cfg->flags & QKV_FLAG_RTN) {
+      QKV_HIP(launch_fill_zero_u32(labels, L.stage_bytes_labels / 4, s));
+      QKV_HIP(launch_fill_zero_u32(cent, L.stage_bytes_centroids / 4, s));
+    } else {
+      QKV_TRY(run_kmeans(cfg, y, wk, labels, c, planes, cn, s));
+      QKV_HIP(launch_centroid_bf16(H, C, c, cent, s));
+    }
+    PackArgs pa;
+    pa.y = y;
+    pa.H = H;
+    pa.C = C;
+    pa.N = (int)N;
+    pa.labels = labels;
+    pa.centroids = cent;
+    pa.perm = pm;
+    pa.bits = cfg->bits;
+    pa.group = cfg->group;
+    pa.n_int4 = cfg->n_int4_channels;
+    pa.int4_words = g.int4_words;
+    pa.codes = reinterpret_cast<uint32_t*>(base + L.off_codes + (uint64_t)l * L.stage_bytes_codes);
+    pa.scales = reinterpret_cast<uint16_t*>(base + L.off_scales + (uint64_t)l * L.stage_bytes_scales);
+    pa.words = g.words;
+    pa.groups = g.groups;
+    const bool more = l + 1 < cfg->n_stages;
+    float* ynext = more ? reinterpret_cast<float*>(at(workspace, (l % 2 == 0) ? ws.ybuf0 : ws.ybuf1)) : nullptr;
+    pa.y_next = ynext;
+    QKV_HIP(launch_quant_pack(pa, s));
+    if (more) {
+      y.ptr = ynext;
+      y.dtype = 0;
+      y.stride_token = kHeadDim;
+      y.stride_head = N * kHeadDim;
+      // y_next is laid out [H][N][128]: token stride 128, head stride N*128
+    }
+  }
+  if (cfg->psac_rank > 0) {
+    const ChunkDecode d = decode_of(cfg, N, packed);
+    QKV_HIP(launch_psac_encode(d, view_of(x), U, reinterpret_cast<uint16_t*>(base + L.off_psac), s));
+  }
+  return ok();
+}
+
+int qkv_dequantize(const qkv_config* cfg, int64_t n_tokens, const void* packed, const qkv_tensor* out, void* stream) {
+  const char* fn = "qkv_dequantize";
+  QKV_TRY(check_config(cfg, fn));
+  if (n_tokens < cfg->n_clusters || n_tokens > ((int64_t)1 << 24))
+    return fail(QKV_EINVAL, "%s: n_tokens %lld out of range", fn, (long long)n_tokens);
+  if (!packed || !aligned16(packed)) return fail(QKV_EINVAL, "%s: packed is NULL or misaligned", fn);
+  QKV_TRY(check_tensor(out, cfg->n_heads, fn));
+  if (out->n_tokens != n_tokens) return fail(QKV_EINVAL, "%s: out has %lld tokens, chunk has %lld", fn,
+                                             (long long)out->n_tokens, (long long)n_tokens);
+  const ChunkDecode d = decode_of(cfg, n_tokens, packed);
+  QKV_HIP(launch_dequantize(d, out->ptr, out->dtype == QKV_F32 ? 0 : 1, out->stride_token, out->stride_head,
+                            reinterpret_cast<hipStream_t>(stream)));
+  return ok();
+}
+
+int qkv_attend(const qkv_config* k_cfg, const qkv_config* v_cfg, const qkv_tensor* q, const void* const* k_chunks,
+               const void* const* v_chunks, const int64_t* chunk_tokens, int32_t n_chunks, const float* U,
+               int32_t causal, float softmax_scale, const qkv_tensor* out, float* logits_debug, void* workspace,
+               size_t workspace_bytes, void* stream) {
+  const char* fn = "qkv_attend";
+  QKV_TRY(check_config(k_cfg, "qkv_attend (k_cfg)"));
+  QKV_TRY(check_config(v_cfg, "qkv_attend (v_cfg)"));
+  if (k_cfg->n_heads != v_cfg->n_heads) return fail(QKV_EINVAL, "%s: K and V head counts differ", fn);
+  if (v_cfg->psac_rank != 0) return fail(QKV_EINVAL, "%s: PSAC applies to keys only (v_cfg->psac_rank != 0)", fn);
+  const int H = k_cfg->n_heads;
+  QKV_TRY(check_tensor(q, H, "qkv_attend (q)"));
+  QKV_TRY(check_tensor(out, H, "qkv_attend (out)"));
+  if (out->dtype != QKV_F32) return fail(QKV_EINVAL, "%s: out must be f32", fn);
+  if (out->n_tokens != q->n_tokens) return fail(QKV_EINVAL, "%s: out and q token counts differ", fn);
+  if (n_chunks < 1 || n_chunks > kMaxChunks) return fail(QKV_EINVAL, "%s: n_chunks %d not in [1, %d]", fn, n_chunks, kMaxChunks);
+  if (!k_chunks || !v_chunks || !chunk_tokens) return fail(QKV_EINVAL, "%s: chunk arrays are NULL", fn);
+  if (k_cfg->psac_rank > 0 && !U) return fail(QKV_EINVAL, "%s: k_cfg->psac_rank > 0 needs U", fn);
+  if (!std::isfinite(softmax_scale) || softmax_scale < 0.0f) return fail(QKV_EINVAL, "%s: softmax_scale must be >= 0", fn);
+  const int64_t Nq = q->n_tokens;
+  std::vector<ChunkRec> recs(n_chunks);
+  int64_t Nk = 0, n_tiles = 0, max_n = 0;
+  for (int i = 0; i < n_chunks; ++i) {
+    const int64_t n = chunk_tokens[i];
+    if (n < std::max(k_cfg->n_clusters, v_cfg->n_clusters) || n > ((int64_t)1 << 24))
+      return fail(QKV_EINVAL, "%s: chunk %d has %lld tokens", fn, i, (long long)n);
+    if (!k_chunks[i] || !v_chunks[i] || !aligned16(k_chunks[i]) || !aligned16(v_chunks[i]))
+      return fail(QKV_EINVAL, "%s: chunk %d pointer NULL or misaligned", fn, i);
+    recs[i].kbase = reinterpret_cast<const uint8_t*>(k_chunks[i]);
+    recs[i].vbase = reinterpret_cast<const uint8_t*>(v_chunks[i]);
+    recs[i].token_start = Nk;
+    recs[i].n = (int32_t)n;
+    recs[i].tile_start = (int32_t)n_tiles;
+    Nk += n;
+    n_tiles += (n + kTileKeys - 1) / kTileKeys;
+    max_n = std::max(max_n, n);
+  }
+  if (Nk > ((int64_t)1 << 31) - 1) return fail(QKV_EINVAL, "%s: the cache holds more than 2^31 tokens", fn);
+  if (causal && Nk != Nq) return fail(QKV_EINVAL, "%s: causal attention needs as many queries as cached keys", fn);
+  // Splits are planned from (max chunk size, n_chunks) so that a workspace sized
+  // by qkv_workspace_bytes with those bounds always suffices.
+  const int ns_plan = choose_splits(H, Nq, max_tiles(max_n, n_chunks));
+  const int ns = choose_splits(H, Nq, n_tiles);
+  const AttendWs ws = attend_ws(H, Nq, n_chunks, std::max(ns, ns_plan));
+  QKV_TRY(check_ws(workspace, workspace_bytes, ws.bytes, fn));
+
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  ChunkRec* drecs = reinterpret_cast<ChunkRec*>(at(workspace, ws.chunks));
+  for (int first = 0; first < n_chunks; first += kChunkBatch) {
+    ChunkBatch b;
+    std::memset(&b, 0, sizeof b);
+    b.first = first;
+    b.count = std::min(kChunkBatch, n_chunks - first);
+    for (int i = 0; i < b.count; ++i) b.rec[i] = recs[first + i];
+    QKV_HIP(launch_upload_chunks(b, drecs, s));
+  }
+
+  AttendArgs a;
+  a.q = view_of(q);
+  a.H = H;
+  a.Nq = (int)Nq;
+  a.Nk = Nk;
+  a.n_chunks = n_chunks;
+  a.n_tiles = (int)n_tiles;
+  a.kp = params_of(k_cfg);
+  a.vp = params_of(v_cfg);
+  a.chunks = drecs;
+  a.U = U;
+  a.psac_rank = k_cfg->psac_rank;
+  a.qu = reinterpret_cast<float*>(at(workspace, ws.qu));
+  a.causal = causal ? 1 : 0;
+  a.scale = softmax_scale > 0.0f ? softmax_scale : 1.0f / std::sqrt((float)kHeadDim);
+  a.n_split = ns;
+  a.part_o = reinterpret_cast<float*>(at(workspace, ws.part_o));
+  a.part_ml = reinterpret_cast<float*>(at(workspace, ws.part_ml));
+  a.out = reinterpret_cast<float*>(out->ptr);
+  a.out_stride_token = out->stride_token;
+  a.out_stride_head = out->stride_head;
+  a.logits = logits_debug;
+  auto fast = [](const qkv_config* c) {
+    return c->n_stages == 1 && c->n_int4_channels == 0 && c->bits == 2 && c->group % 32 == 0;
+  };
+  a.k_uniform_int2_1stage = fast(k_cfg);
+  a.v_uniform_int2_1stage = fast(v_cfg);
+  QKV_HIP(launch_attend(a, s));
+  return ok();
+}
+
+int qkv_psac_fit(const qkv_tensor* q_hist, int32_t n_heads, int32_t rank, int32_t n_int4, float* U_out, float* w_out, uint8_t* perm_out,
+                 float* energy_out, void* workspace, size_t workspace_bytes, void* stream) {
+  const char* fn = "qkv_psac_fit";
+  if (!q_hist) return fail(QKV_EINVAL, "%s: q_hist is NULL", fn);
+  if (rank < 0 || rank > kMaxRank) return fail(QKV_EINVAL, "%s: rank %d not in [0, 8]", fn, rank);
+  if (n_int4 < 0 || n_int4 >= kHeadDim) return fail(QKV_EINVAL, "%s: n_int4 %d not in [0, 127]", fn, n_int4);
+  if (rank > 0 && !U_out) return fail(QKV_EINVAL, "%s: rank > 0 needs U_out", fn);
+  const int H = n_heads;
+  if (H < 1 || H > 1024) return fail(QKV_EINVAL, "%s: n_heads %d not in [1, 1024]", fn, H);
+  QKV_TRY(check_tensor(q_hist, H, fn));
+  QKV_TRY(check_ws(workspace, workspace_bytes, psac_ws(H), fn));
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  double* partial = reinterpret_cast<double*>(workspace);
+  double* m = reinterpret_cast<double*>(at(workspace, align256((uint64_t)kGramSplit * H * kHeadDim * kHeadDim * 8)));
+  QKV_HIP(launch_gram(view_of(q_hist), H, partial, kGramSplit, m, s));
+  std::vector<double> hm((size_t)H * kHeadDim * kHeadDim);
+  QKV_HIP(hipMemcpyAsync(hm.data(), m, hm.size() * 8, hipMemcpyDeviceToHost, s));
+  QKV_HIP(hipStreamSynchronize(s));
+
+  const double n = (double)q_hist->n_tokens;
+  std::vector<float> hw((size_t)H * kHeadDim), hU((size_t)H * kHeadDim * std::max(rank, 1));
+  std::vector<uint8_t> hperm((size_t)H * kHeadDim);
+  std::vector<float> energy(H);
+  for (int h = 0; h < H; ++h)
+    for (int k = 0; k < kHeadDim; ++k) hw[(size_t)h * kHeadDim + k] = (float)(hm[((size_t)h * kHeadDim + k) * kHeadDim + k] / n);
+  if (rank > 0 || energy_out) {
+    const unsigned nt = std::max(1u, std::min(16u, std::thread::hardware_concurrency()));
+    std::vector<std::thread> pool;
+    for (unsigned t = 0; t < nt; ++t) {
+      pool.emplace_back([&, t]() {
+        std::vector<double> a((size_t)kHeadDim * kHeadDim), ev(kHeadDim), vec((size_t)kHeadDim * kHeadDim);
+        for (int h = (int)t; h < H; h += (int)nt) {
+          std::memcpy(a.data(), hm.data() + (size_t)h * kHeadDim * kHeadDim, a.size() * 8);
+          jacobi_eigh(kHeadDim, a.data(), ev.data(), vec.data());
+          double tot = 0.0, top = 0.0;
+          for (int i = 0; i < kHeadDim; ++i) tot += ev[i];
+          for (int i = 0; i < rank; ++i) top += ev[i];
+          energy[h] = tot > 0.0 ? (float)(top / tot) : 0.0f;
+          for (int k = 0; k < kHeadDim; ++k)
+            for (int b = 0; b < rank; ++b)
+              hU[((size_t)h * kHeadDim + k) * rank + b] = (float)vec[(size_t)k * kHeadDim + b];
+        }
+      });
+    }
+    for (auto& th : pool) th.join();
+  }
+  for (int h = 0; h < H; ++h) {
+    std::vector<int> order(kHeadDim);
+    for (int k = 0; k < kHeadDim; ++k) order[k] = k;
+    const float* wh = hw.data() + (size_t)h * kHeadDim;
+    std::stable_sort(order.begin(), order.end(), [&](int x, int y) { return wh[x] > wh[y]; });
+    std::vector<int> top(order.begin(), order.begin() + n_int4), rest(order.begin() + n_int4, order.end());
+    std::sort(top.begin(), top.end());
+    std::sort(rest.begin(), rest.end());
+    int p = 0;
+    for (int k : top) hperm[(size_t)h * kHeadDim + p++] = (uint8_t)k;
+    for (int k : rest) hperm[(size_t)h * kHeadDim + p++] = (uint8_t)k;
+  }
+  if (w_out) QKV_HIP(hipMemcpy(w_out, hw.data(), hw.size() * 4, hipMemcpyHostToDevice));
+  if (rank > 0) QKV_HIP(hipMemcpy(U_out, hU.data(), (size_t)H * kHeadDim * rank * 4, hipMemcpyHostToDevice));
+  if (perm_out && n_int4 > 0) QKV_HIP(hipMemcpy(perm_out, hperm.data(), hperm.size(), hipMemcpyHostToDevice));
+  if (energy_out) std::memcpy(energy_out, energy.data(), H * sizeof(float));
+  return ok();
+}
+
+int qkv_kmeans_assign(const qkv_config* cfg, const qkv_tensor* y, const float* centroids, const float* w,
+                      uint8_t* labels, void* workspace, size_t workspace_bytes, void* stream) {
+  const char* fn = "qkv_kmeans_assign";
+  QKV_TRY(check_config(cfg, fn));
+  QKV_TRY(check_tensor(y, cfg->n_heads, fn));
+  if (!centroids || !labels) return fail(QKV_EINVAL, "%s: centroids/labels NULL", fn);
+  const QuantWs ws = quant_ws(cfg, y->n_tokens);
+  QKV_TRY(check_ws(workspace, workspace_bytes, ws.cn + align256((uint64_t)cfg->n_heads * cfg->n_clusters * 4), fn));
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  uint16_t* planes = reinterpret_cast<uint16_t*>(at(workspace, ws.planes));
+  float* cn = reinterpret_cast<float*>(at(workspace, ws.cn));
+  QKV_HIP(launch_centroid_prep(cfg->n_heads, cfg->n_clusters, centroids, w, planes, cn, s));
+  QKV_HIP(launch_kmeans_assign(view_of(y), cfg->n_heads, cfg->n_clusters, planes, cn, centroids, w, labels, s));
+  return ok();
+}
+
+int qkv_kmeans_update(const qkv_config* cfg, const qkv_tensor* y, const uint8_t* labels, float* centroids,
+                      int32_t* counts, void* stream) {
+  const char* fn = "qkv_kmeans_update";
+  QKV_TRY(check_config(cfg, fn));
+  QKV_TRY(check_tensor(y, cfg->n_heads, fn));
+  if (!centroids || !labels) return fail(QKV_EINVAL, "%s: centroids/labels NULL", fn);
+  QKV_HIP(launch_kmeans_update(view_of(y), cfg->n_heads, cfg->n_clusters, labels, centroids, counts,
+                               reinterpret_cast<hipStream_t>(stream)));
+  return ok();
+}
+
+int qkv_quant_pack(const qkv_config* cfg, const qkv_tensor* y, const uint8_t* labels, const float* centroids,
+                   const uint8_t* perm, void* packed, int32_t stage, float* y_next, void* stream) {
+  const char* fn = "qkv_quant_pack";
+  QKV_TRY(check_config(cfg, fn));
+  QKV_TRY(check_tensor(y, cfg->n_heads, fn));
+  if (!labels || !centroids || !packed || !aligned16(packed)) return fail(QKV_EINVAL, "%s: NULL or misaligned pointer", fn);
+  if (stage < 0 || stage >= cfg->n_stages) return fail(QKV_EINVAL, "%s: stage %d not in [0, n_stages)", fn, stage);
+  if (cfg->n_int4_channels > 0 && !perm) return fail(QKV_EINVAL, "%s: the mixed layout needs perm", fn);
+  const int64_t N = y->n_tokens;
+  if (N < cfg->n_clusters) return fail(QKV_EINVAL, "%s: n_tokens < n_clusters", fn);
+  qkv_layout L;
+  layout_of(cfg, N, &L);
+  const ChunkDecode g = decode_of(cfg, N, nullptr);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  uint8_t* base = reinterpret_cast<uint8_t*>(packed);
+  uint8_t* lab_dst = base + L.off_labels + (uint64_t)stage * L.stage_bytes_labels;
+  if (lab_dst != labels) QKV_HIP(hipMemcpyAsync(lab_dst, labels, (size_t)cfg->n_heads * N, hipMemcpyDeviceToDevice, s));
+  uint16_t* cent = reinterpret_cast<uint16_t*>(base + L.off_centroids + (uint64_t)stage * L.stage_bytes_centroids);
+  QKV_HIP(launch_centroid_bf16(cfg->n_heads, cfg->n_clusters, centroids, cent, s));
+  const uint8_t* pm = cfg->n_int4_channels > 0 ? perm : nullptr;
+  if (pm) QKV_HIP(launch_copy_perm(pm, base + L.off_perm, cfg->n_heads, s));
+  PackArgs pa;
+  pa.y = view_of(y);
+  pa.H = cfg->n_heads;
+  pa.C = cfg->n_clusters;
+  pa.N = (int)N;
+  pa.labels = lab_dst;
+  pa.centroids = cent;
+  pa.perm = pm;
+  pa.bits = cfg->bits;
+  pa.group = cfg->group;
+  pa.n_int4 = cfg->n_int4_channels;
+  pa.int4_words = g.int4_words;
+  pa.codes = reinterpret_cast<uint32_t*>(base + L.off_codes + (uint64_t)stage * L.stage_bytes_codes);
+  pa.scales = reinterpret_cast<uint16_t*>(base + L.off_scales + (uint64_t)stage * L.stage_bytes_scales);
+  pa.words = g.words;
+  pa.groups = g.groups;
+  pa.y_next = y_next;
+  QKV_HIP(launch_quant_pack(pa, s));
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,290 @@
+// Residual, per-group scale, rounding and bit packing of one stage; and the
+// inverse (dequantization), and the PSAC coefficient encoder.
+//
+// Method: Quant VideoGen notes, "Research background / core tension" (symmetric
+// per-group quantization, S = max|X| / (2^(b-1) - 1), X_INT = round(X / S)) and
+// "Method / Overall framework" (residual against the token's centroid, BF16
+// centroids, dequantization S * X_INT + C_i); mixed 4/2-bit classes from the
+// 2-bit trap explainer (section five, advice one) and the practitioner blog
+// (section 3.2); PSAC coefficients from the QuantWM summary ("QuantWM", second
+// technique).
+//
+// Arithmetic (matches the documented format bit for bit):
+//   r = fp32(y - C_bf16[label]);  S = bf16_rne(fp32(max|r| / qmax));
+//   q = S == 0 ? 0 : clamp(rint_even(fp32(r / S)), -2^(b-1), 2^(b-1) - 1);
+//   y_hat = fp32(S * q + C) (S * q is exact);  y_next = fp32(y - y_hat).
+#include "common.h"
+#include "kernels.h"
+
+namespace qkv {
+
+namespace {
+
+struct GroupInfo {
+  int start;      // first storage position (index into the perm order)
+  int len;        // channels in the group
+  int bits;
+  int pos0;       // position of the first channel within its class
+  int word0;      // first word of the class
+};
+
+// Group g (storage order) of the uniform or mixed layout.
+__device__ __forceinline__ GroupInfo group_info(int g, int bits, int group, int n_int4, int int4_words) {
+  GroupInfo gi;
+  if (n_int4 > 0) {
+    const int g4 = (n_int4 + group - 1) / group;
+    if (g < g4) {
+      gi.pos0 = g * group;
+      gi.len = min(group, n_int4 - gi.pos0);
+      gi.bits = 4;
+      gi.word0 = 0;
+      gi.start = gi.pos0;
+    } else {
+      gi.pos0 = (g - g4) * group;
+      gi.len = min(group, kHeadDim - n_int4 - gi.pos0);
+      gi.bits = bits;
+      gi.word0 = int4_words;
+      gi.start = n_int4 + gi.pos0;
+    }
+  } else {
+    gi.pos0 = g * group;
+    gi.len = group;
+    gi.bits = bits;
+    gi.word0 = 0;
+    gi.start = gi.pos0;
+  }
+  return gi;
+}
+
+// Decode entry of the channel at storage position p.
+__device__ __forceinline__ ChannelCode code_of(int p, int bits, int group, int n_int4, int int4_words) {
+  ChannelCode cc;
+  int pos, b, w0, gidx;
+  if (n_int4 > 0 && p < n_int4) {
+    pos = p; b = 4; w0 = 0; gidx = p / group;
+  } else if (n_int4 > 0) {
+    pos = p - n_int4; b = bits; w0 = int4_words;
+    gidx = (n_int4 + group - 1) / group + pos / group;
+  } else {
+    pos = p; b = bits; w0 = 0; gidx = p / group;
+  }
+  const int per = 32 / b;
+  cc.word = (uint8_t)(w0 + pos / per);
+  cc.shift = (uint8_t)(b * (pos % per));
+  cc.bits = (uint8_t)b;
+  cc.group = (uint8_t)gidx;
+  return cc;
+}
+
+template <bool F32>
+__device__ __forceinline__ float load_y(const TensorView& y, int64_t tok, int h, int k) {
+  const int64_t off = tok * y.stride_token + (int64_t)h * y.stride_head + k;
+  if constexpr (F32) return reinterpret_cast<const float*>(y.ptr)[off];
+  return bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(y.ptr)[off]);
+}
+
+// One thread per (head, token, group).
+template <int G, bool F32>
+__global__ __launch_bounds__(256) void k_quant_pack(PackArgs a) {
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t total = (int64_t)a.H * a.N * a.groups;
+  if (gid >= total) return;
+  const int g = (int)(gid % a.groups);
+  const int64_t t = gid / a.groups;
+  const int i = (int)(t % a.N);
+  const int h = (int)(t / a.N);
+  const GroupInfo gi = group_info(g, a.bits, a.group, a.n_int4, a.int4_words);
+  const int lab = min((int)a.labels[(int64_t)h * a.N + i], a.C - 1);   // labels < C (memory safety)
+  const uint16_t* crow = a.centroids + ((int64_t)h * a.C + lab) * kHeadDim;
+  const uint8_t* perm = a.perm ? a.perm + h * kHeadDim : nullptr;
+
+  float r[G];
+  float amax = 0.0f;
+#pragma unroll
+  for (int e = 0; e < G; ++e) {
+    r[e] = 0.0f;
+    if (e < gi.len) {
+      const int p = gi.start + e;
+      const int k = perm ? (perm[p] & (kHeadDim - 1)) : p;
+      const float yv = load_y<F32>(a.y, i, h, k);
+      const float cv = bf16_bits_to_f32(crow[k]);
+      r[e] = yv - cv;
+      amax = fmaxf(amax, fabsf(r[e]));
+    }
+  }
+  const int b = gi.bits;
+  const float qmax = (float)((1 << (b - 1)) - 1);
+  const uint32_t sbits = f32_to_bf16_bits(amax / qmax);
+  const float S = bf16_bits_to_f32(sbits);
+  const float qlo = -(float)(1 << (b - 1)), qhi = qmax;
+  const int per = 32 / b;
+  const uint32_t off = 1u << (b - 1);
+  uint32_t words[G / 8];
+#pragma unroll
+  for (int w = 0; w < G / 8; ++w) words[w] = 0u;
+  const int64_t ynext_base = ((int64_t)h * a.N + i) * kHeadDim;
+#pragma unroll
+  for (int e = 0; e < G; ++e) {
+    if (e < gi.len) {
+      float q = 0.0f;
+      if (S != 0.0f) q = fminf(fmaxf(rintf(r[e] / S), qlo), qhi);
+      const uint32_t u = (uint32_t)((int)q + (int)off);
+      const int pc = gi.pos0 + e;            // position in class
+      const int wl = e / per;                // word within the group (pos0 is word aligned)
+      words[wl] |= u << (b * (pc % per));
+      if (a.y_next) {
+        const int p = gi.start + e;
+        const int k = perm ? (perm[p] & (kHeadDim - 1)) : p;
+        const float yv = load_y<F32>(a.y, i, h, k);
+        const float cv = bf16_bits_to_f32(crow[k]);
+        const float yhat = __fadd_rn(S * q, cv);
+        a.y_next[ynext_base + k] = __fsub_rn(yv, yhat);
+      }
+    }
+  }
+  const int nw = (gi.len + per - 1) / per;
+  uint32_t* wout = a.codes + ((int64_t)h * a.N + i) * a.words + gi.word0 + gi.pos0 / per;
+#pragma unroll
+  for (int w = 0; w < G / 8; ++w)
+    if (w < nw) wout[w] = words[w];
+  a.scales[((int64_t)h * a.N + i) * a.groups + g] = (uint16_t)sbits;
+}
+
+__device__ __forceinline__ const uint8_t* stage_ptr(const ChunkDecode& d, uint64_t off, uint64_t stride, int l) {
+  return d.base + off + stride * (uint64_t)l;
+}
+
+// Build the decode table of head h into tab[128] (block-cooperative).  A perm
+// that is not a permutation decodes wrongly but stays inside every buffer.
+__device__ __forceinline__ void build_table(const ChunkDecode& d, int h, ChannelCode* tab) {
+  for (int p = threadIdx.x; p < kHeadDim; p += blockDim.x) tab[p] = ChannelCode{0, 0, (uint8_t)d.bits, 0};
+  __syncthreads();
+  for (int p = threadIdx.x; p < kHeadDim; p += blockDim.x) {
+    const int k = d.n_int4 > 0 ? ((int)(d.base + d.off_perm)[h * kHeadDim + p] & (kHeadDim - 1)) : p;
+    tab[k] = code_of(p, d.bits, d.group, d.n_int4, d.int4_words);
+  }
+}
+
+// x_hat for channels [k0, k0 + n) of token i, head h (fp32 sum over stages in order).
+template <int NCH>
+__device__ __forceinline__ void dequant_row(const ChunkDecode& d, const ChannelCode* tab, int h, int64_t i,
+                                            int k0, float* out) {
+#pragma unroll
+  for (int e = 0; e < NCH; ++e) out[e] = 0.0f;
+  for (int l = 0; l < d.n_stages; ++l) {
+    const uint32_t* codes = reinterpret_cast<const uint32_t*>(stage_ptr(d, d.off_codes, d.stage_codes, l)) +
+                            ((int64_t)h * d.N + i) * d.words;
+    const uint16_t* scales = reinterpret_cast<const uint16_t*>(stage_ptr(d, d.off_scales, d.stage_scales, l)) +
+                             ((int64_t)h * d.N + i) * d.groups;
+    const int lab = min((int)stage_ptr(d, d.off_labels, d.stage_labels, l)[(int64_t)h * d.N + i], d.C - 1);
+    const uint16_t* crow = reinterpret_cast<const uint16_t*>(stage_ptr(d, d.off_centroids, d.stage_centroids, l)) +
+                           ((int64_t)h * d.C + lab) * kHeadDim;
+#pragma unroll
+    for (int e = 0; e < NCH; ++e) {
+      const ChannelCode cc = tab[k0 + e];
+      const uint32_t u = (codes[cc.word] >> cc.shift) & ((1u << cc.bits) - 1u);
+      const float q = (float)((int)u - (1 << (cc.bits - 1)));
+      const float S = bf16_bits_to_f32(scales[cc.group]);
+      const float yhat = __fadd_rn(S * q, bf16_bits_to_f32(crow[k0 + e]));
+      out[e] = l == 0 ? yhat : __fadd_rn(out[e], yhat);
+    }
+  }
+}
+
+// Block: one head, 32 tokens; thread: one token, 16 channels.
+__global__ __launch_bounds__(256) void k_dequant(ChunkDecode d, void* out, int out_dtype, int64_t st, int64_t sh) {
+  __shared__ ChannelCode tab[kHeadDim];
+  const int h = blockIdx.y;
+  build_table(d, h, tab);
+  __syncthreads();
+  const int64_t i = (int64_t)blockIdx.x * 32 + threadIdx.x / 8;
+  if (i >= d.N) return;
+  const int k0 = (threadIdx.x % 8) * 16;
+  float v[16];
+  dequant_row<16>(d, tab, h, i, k0, v);
+  const int64_t o = i * st + (int64_t)h * sh + k0;
+  if (out_dtype == 0) {
+    float* op = reinterpret_cast<float*>(out) + o;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) op[e] = v[e];
+  } else {
+    uint16_t* op = reinterpret_cast<uint16_t*>(out) + o;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) op[e] = (uint16_t)f32_to_bf16_bits(v[e]);
+  }
+}
+
+// PSAC encode: e = fp32(x - x_hat) after all stages, coef = bf16(U^T e) from
+// float64 dot products.  Block: one head, 256 tokens; thread: one token.
+template <bool F32>
+__global__ __launch_bounds__(256) void k_psac_encode(ChunkDecode d, TensorView x, const float* __restrict__ U,
+                                                     uint16_t* __restrict__ coef) {
+  __shared__ ChannelCode tab[kHeadDim];
+  __shared__ float sU[kHeadDim * kMaxRank];
+  const int h = blockIdx.y;
+  const int r = d.psac_rank;
+  build_table(d, h, tab);
+  for (int idx = threadIdx.x; idx < kHeadDim * r; idx += blockDim.x) sU[idx] = U[(int64_t)h * kHeadDim * r + idx];
+  __syncthreads();
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= d.N) return;
+  double acc[kMaxRank];
+#pragma unroll
+  for (int b = 0; b < kMaxRank; ++b) acc[b] = 0.0;
+  for (int k0 = 0; k0 < kHeadDim; k0 += 16) {
+    float v[16];
+    dequant_row<16>(d, tab, h, i, k0, v);
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const float err = __fsub_rn(load_y<F32>(x, i, h, k0 + e), v[e]);
+#pragma unroll
+      for (int b = 0; b < kMaxRank; ++b)
+        if (b < r) acc[b] += (double)sU[(k0 + e) * r + b] * (double)err;
+    }
+  }
+  uint16_t* cp = coef + ((int64_t)h * d.N + i) * r;
+#pragma unroll
+  for (int b = 0; b < kMaxRank; ++b)
+    if (b < r) cp[b] = (uint16_t)f64_to_bf16_bits(acc[b]);
+}
+
+}  // namespace
+
+hipError_t launch_quant_pack(const PackArgs& a, hipStream_t s) {
+  const int64_t total = (int64_t)a.H * a.N * a.groups;
+  const dim3 grid((unsigned)((total + 255) / 256)), block(256);
+  const bool f32 = a.y.dtype == 0;
+#define QKV_QP(GV)                                                              \
+  if (a.group == GV) {                                                          \
+    if (f32) hipLaunchKernelGGL((k_quant_pack<GV, true>), grid, block, 0, s, a); \
+    else hipLaunchKernelGGL((k_quant_pack<GV, false>), grid, block, 0, s, a);    \
+    return hipGetLastError();                                                   \
+  }
+  QKV_QP(16)
+  QKV_QP(32)
+  QKV_QP(64)
+  QKV_QP(128)
+#undef QKV_QP
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_dequantize(const ChunkDecode& d, void* out, int out_dtype, int64_t stride_token,
+                             int64_t stride_head, hipStream_t s) {
+  const dim3 grid((unsigned)((d.N + 31) / 32), (unsigned)d.H);
+  hipLaunchKernelGGL(k_dequant, grid, dim3(256), 0, s, d, out, out_dtype, stride_token, stride_head);
+  return hipGetLastError();
+}
+
+hipError_t launch_psac_encode(const ChunkDecode& d, const TensorView& x, const float* U, uint16_t* coef_out,
+                              hipStream_t s) {
+  const dim3 grid((unsigned)((d.N + 255) / 256), (unsigned)d.H);
+  if (x.dtype == 0) hipLaunchKernelGGL(k_psac_encode<true>, grid, dim3(256), 0, s, d, x, U, coef_out);
+  else hipLaunchKernelGGL(k_psac_encode<false>, grid, dim3(256), 0, s, d, x, U, coef_out);
+  return hipGetLastError();
+}
+
+hipError_t launch_copy_perm(const uint8_t* perm, uint8_t* dst, int H, hipStream_t s) {
+  return hipMemcpyAsync(dst, perm, (size_t)H * kHeadDim, hipMemcpyDeviceToDevice, s);
+}
+
+}  // namespace qkv
