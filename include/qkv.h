@@ -240,9 +240,11 @@ int qkv_kmeans_assign(const qkv_config* cfg, const qkv_tensor* y, const float* c
 
 /* One k-means update step: centroids[h][j] = fp32(exact sum / count) of the
    tokens labelled j; an empty cluster keeps its value (in/out).
-   counts int32 [H][C] device or NULL. */
+   counts int32 [H][C] device or NULL.  workspace: qkv_workspace_bytes(cfg, N,
+   0, 0, ...) bytes. */
 int qkv_kmeans_update(const qkv_config* cfg, const qkv_tensor* y, const uint8_t* labels,
-                      float* centroids, int32_t* counts, void* stream);
+                      float* centroids, int32_t* counts, void* workspace, size_t workspace_bytes,
+                      void* stream);
 
 /* Quantize stage `stage` of a packed chunk from given labels and float
    centroids (rounded to bf16 and stored in the chunk): residual, group scale,

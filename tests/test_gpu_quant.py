@@ -73,7 +73,7 @@ def test_assign_and_update_lockstep(case):
         # update from the oracle's labels of this iteration
         lab = np.stack([tr.labels_iter[it] for tr in traces]).astype(np.uint8)
         cd = G.to_dev(cin)
-        qk.qkv_kmeans_update(cfg, xd, t.from_numpy(lab.reshape(-1)).to(G.dev()), cd, counts)
+        qk.qkv_kmeans_update(cfg, xd, t.from_numpy(lab.reshape(-1)).to(G.dev()), cd, ws, counts)
         exp = np.stack([tr.centroids_in[it + 1] if it + 1 < wl.kmeans_iters else tr.centroids for tr in traces])
         got_c = cd.cpu().numpy()
         assert np.array_equal(got_c.view(np.uint32), exp.view(np.uint32)), \

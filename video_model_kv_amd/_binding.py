@@ -101,7 +101,7 @@ def lib():
                                  vp, i32, ct.c_float, P(qkv_tensor), vp, vp, sz, vp]
         L.qkv_psac_fit.argtypes = [P(qkv_tensor), i32, i32, i32, vp, vp, vp, P(ct.c_float), vp, sz, vp]
         L.qkv_kmeans_assign.argtypes = [P(qkv_config), P(qkv_tensor), vp, vp, vp, vp, sz, vp]
-        L.qkv_kmeans_update.argtypes = [P(qkv_config), P(qkv_tensor), vp, vp, vp, vp]
+        L.qkv_kmeans_update.argtypes = [P(qkv_config), P(qkv_tensor), vp, vp, vp, vp, sz, vp]
         L.qkv_quant_pack.argtypes = [P(qkv_config), P(qkv_tensor), vp, vp, vp, vp, i32, vp, vp]
         for name in EXPORTED[2:]:
             getattr(L, name).restype = ct.c_int
@@ -198,9 +198,10 @@ def qkv_kmeans_assign(cfg: Config, y, centroids, labels, workspace, w=None, stre
                                    _stream(stream)))
 
 
-def qkv_kmeans_update(cfg: Config, y, labels, centroids, counts=None, stream=None):
+def qkv_kmeans_update(cfg: Config, y, labels, centroids, workspace, counts=None, stream=None):
     _check(lib().qkv_kmeans_update(ct.byref(cfg.c()), ct.byref(tensor_desc(y)), _ptr(labels), _ptr(centroids),
-                                   _ptr(counts), _stream(stream)))
+                                   _ptr(counts), _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                   _stream(stream)))
 
 
 def qkv_quant_pack(cfg: Config, y, labels, centroids, packed, stage: int = 0, perm=None, y_next=None,

@@ -34,12 +34,16 @@ __device__ __forceinline__ float load1(const TensorView& y, int64_t tok, int h, 
   return bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(y.ptr)[off]);
 }
 
+// Block (head, 8 centroids): c_j = y[j * floor(N / C)] as float32.
 template <bool F32>
 __global__ __launch_bounds__(256) void k_init(TensorView y, int C, float* __restrict__ c) {
-  const int h = blockIdx.x;
+  const int h = blockIdx.y;
+  const int j = blockIdx.x * 8 + (threadIdx.x >> 5);
+  if (j >= C) return;
   const int64_t step = y.n_tokens / C;
-  for (int idx = threadIdx.x; idx < C * kHeadDim; idx += blockDim.x) {
-    const int j = idx / kHeadDim, k = idx % kHeadDim;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int k = (threadIdx.x & 31) * 4 + e;
     c[((int64_t)h * C + j) * kHeadDim + k] = load1<F32>(y, (int64_t)j * step, h, k);
   }
 }
@@ -47,9 +51,11 @@ __global__ __launch_bounds__(256) void k_init(TensorView y, int C, float* __rest
 // One wave per centroid: hi/lo planes of fp32(w*c) and the weighted norm.
 __global__ __launch_bounds__(64) void k_prep(int C, const float* __restrict__ c,
                                              const float* __restrict__ w,
-                                             uint16_t* __restrict__ planes, float* __restrict__ cn) {
+                                             uint16_t* __restrict__ planes, float* __restrict__ cn,
+                                             int* __restrict__ amb_count) {
   const int h = blockIdx.x / C, j = blockIdx.x % C;
   const int lane = threadIdx.x;
+  if (blockIdx.x == 0 && lane == 0 && amb_count) *amb_count = 0;
   const float* cr = c + ((int64_t)h * C + j) * kHeadDim;
   double nrm = 0.0;
   uint16_t* ph = planes + ((int64_t)h * 2 * C + j) * kHeadDim;
@@ -75,21 +81,23 @@ template <bool F32>
 __global__ __launch_bounds__(256) void k_assign(TensorView y, int C, int tiles_per_head, int n_heads,
                                                 const uint16_t* __restrict__ planes,
                                                 const float* __restrict__ cn,
-                                                const float* __restrict__ cent,
                                                 const float* __restrict__ w,
-                                                uint8_t* __restrict__ labels) {
-  __shared__ __attribute__((aligned(16))) uint16_t sA[2][32][kPitch];
-  __shared__ float sCn[32];
+                                                uint8_t* __restrict__ labels, int* __restrict__ amb_count,
+                                                int64_t* __restrict__ amb_list) {
+  __shared__ __attribute__((aligned(16))) uint16_t sA[2][2][32][kPitch];
+  __shared__ float sCn[2][32];
+  __shared__ __attribute__((aligned(16))) float sW[kHeadDim];
   const uint32_t logical = xcd_remap(blockIdx.x, (uint32_t)(tiles_per_head * n_heads));
   const int h = logical / tiles_per_head, tile = logical % tiles_per_head;
   const int N = (int)y.n_tokens;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int col = lane & 31, half = lane >> 5;
-  const float* wh = w ? w + h * kHeadDim : nullptr;
+  if (threadIdx.x < kHeadDim) sW[threadIdx.x] = w ? w[h * kHeadDim + threadIdx.x] : 1.0f;
+  __syncthreads();
 
   // B operand (tokens): lane holds token `col` of sub-block t, channels s*16 + half*8 + [0, 8).
-  // ynorm[t] accumulates sum_k w_k y_k^2 over the lane's channels (fp32, for the
-  // screening threshold only).
+  // ynorm[t] accumulates sum_k w_k y_k^2 over the lane's channels (fp32; it only
+  // sets the screening threshold).
   bf16x8 yh[2][8];
   bf16x8 yl[2][F32 ? 8 : 1];
   float ynorm[2] = {0.0f, 0.0f};
@@ -124,34 +132,57 @@ __global__ __launch_bounds__(256) void k_assign(TensorView y, int C, int tiles_p
 #pragma unroll
         for (int e = 0; e < 8; ++e) v[e] = bf16_bits_to_f32((r4[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
       }
+      const float4 w0 = *reinterpret_cast<const float4*>(&sW[ch]);
+      const float4 w1 = *reinterpret_cast<const float4*>(&sW[ch + 4]);
+      const float wv[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
 #pragma unroll
-      for (int e = 0; e < 8; ++e) ynorm[t] += (wh ? wh[ch + e] : 1.0f) * (v[e] * v[e]);
+      for (int e = 0; e < 8; ++e) ynorm[t] += wv[e] * (v[e] * v[e]);
     }
   }
 
+  // top-2 of the screened values, branch-free; rows beyond C carry +inf.
+  // Centroid planes stream through double-buffered LDS: the next block's
+  // global loads are issued before the current block's MFMAs.
   float b1[2] = {INFINITY, INFINITY}, b2[2] = {INFINITY, INFINITY};
   int bidx[2] = {0, 0};
   const uint16_t* ph = planes + (int64_t)h * 2 * C * kHeadDim;
   const int nblk = (C + 31) / 32;
-  for (int cb = 0; cb < nblk; ++cb) {
-    __syncthreads();
-    for (int v = threadIdx.x; v < 1024; v += 256) {
+  uint4 pf[4];
+  float cnpf = INFINITY;
+  auto fetch = [&](int cb) {
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      const int v = threadIdx.x + x * 256;
       const int p = v >> 9, r = (v >> 4) & 31, c16 = v & 15;
       const int j = cb * 32 + r;
-      uint4 val = make_uint4(0, 0, 0, 0);
-      if (j < C) val = *reinterpret_cast<const uint4*>(ph + ((int64_t)p * C + j) * kHeadDim + c16 * 8);
-      *reinterpret_cast<uint4*>(&sA[p][r][c16 * 8]) = val;
+      pf[x] = make_uint4(0, 0, 0, 0);
+      if (j < C) pf[x] = *reinterpret_cast<const uint4*>(ph + ((int64_t)p * C + j) * kHeadDim + c16 * 8);
     }
     if (threadIdx.x < 32) {
       const int j = cb * 32 + threadIdx.x;
-      sCn[threadIdx.x] = j < C ? cn[h * C + j] : INFINITY;
+      cnpf = j < C ? cn[h * C + j] : INFINITY;
     }
-    __syncthreads();
+  };
+  auto stash = [&](int buf) {
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      const int v = threadIdx.x + x * 256;
+      const int p = v >> 9, r = (v >> 4) & 31, c16 = v & 15;
+      *reinterpret_cast<uint4*>(&sA[buf][p][r][c16 * 8]) = pf[x];
+    }
+    if (threadIdx.x < 32) sCn[buf][threadIdx.x] = cnpf;
+  };
+  fetch(0);
+  stash(0);
+  __syncthreads();
+  for (int cb = 0; cb < nblk; ++cb) {
+    const int buf = cb & 1;
+    if (cb + 1 < nblk) fetch(cb + 1);
     f32x16 acc0 = {}, acc1 = {};
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
-      const bf16x8 ahi = as_bf16x8(*reinterpret_cast<const uint4*>(&sA[0][col][s * 16 + half * 8]));
-      const bf16x8 alo = as_bf16x8(*reinterpret_cast<const uint4*>(&sA[1][col][s * 16 + half * 8]));
+      const bf16x8 ahi = as_bf16x8(*reinterpret_cast<const uint4*>(&sA[buf][0][col][s * 16 + half * 8]));
+      const bf16x8 alo = as_bf16x8(*reinterpret_cast<const uint4*>(&sA[buf][1][col][s * 16 + half * 8]));
       acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahi, yh[0][s], acc0, 0, 0, 0);
       acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahi, yh[1][s], acc1, 0, 0, 0);
       acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(alo, yh[0][s], acc0, 0, 0, 0);
@@ -167,14 +198,19 @@ __global__ __launch_bounds__(256) void k_assign(TensorView y, int C, int tiles_p
     for (int r = 0; r < 16; ++r) {
       const int jr = (r >> 2) * 8 + half * 4 + (r & 3);
       const int j = cb * 32 + jr;
-      const float cnv = sCn[jr];
+      const float cnv = sCn[buf][jr];
       const float v0 = cnv - 2.0f * acc0[r];
       const float v1 = cnv - 2.0f * acc1[r];
-      if (j < C) {
-        if (v0 < b1[0]) { b2[0] = b1[0]; b1[0] = v0; bidx[0] = j; } else if (v0 < b2[0]) { b2[0] = v0; }
-        if (v1 < b1[1]) { b2[1] = b1[1]; b1[1] = v1; bidx[1] = j; } else if (v1 < b2[1]) { b2[1] = v1; }
-      }
+      const bool l0 = v0 < b1[0], l1 = v1 < b1[1];
+      b2[0] = l0 ? b1[0] : fminf(b2[0], v0);
+      b2[1] = l1 ? b1[1] : fminf(b2[1], v1);
+      bidx[0] = l0 ? j : bidx[0];
+      bidx[1] = l1 ? j : bidx[1];
+      b1[0] = l0 ? v0 : b1[0];
+      b1[1] = l1 ? v1 : b1[1];
     }
+    if (cb + 1 < nblk) stash(buf ^ 1);
+    __syncthreads();
   }
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
@@ -186,117 +222,172 @@ __global__ __launch_bounds__(256) void k_assign(TensorView y, int C, int tiles_p
     ynorm[t] += __shfl_xor(ynorm[t], 32);
   }
 
-  // Exact re-check of close calls: when the two best screened values are within
-  // the screening error bound (generously 2e-5 of ||y||_w^2 + ||c||_w^2), the
-  // label is decided from float64 distances sum_k w_k (y_k - c_k)^2 accumulated
-  // in channel order, the lowest index winning ties.
+  // Close calls -- the two best screened values within the screening error
+  // bound (generously 2e-5 of ||y||_w^2 + ||c||_w^2) -- are queued for k_refine,
+  // which re-decides them from float64 distances.
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
     const int tok = tile * kAssignTokens + wave * 64 + t * 32 + col;
-    const float thr = 2e-5f * (ynorm[t] + cn[h * C + bidx[t]]);
-    uint64_t amb = __ballot(half == 0 && tok < N && !(b2[t] - b1[t] > thr));
-    while (amb) {
-      const int src = __ffsll((unsigned long long)amb) - 1;
-      amb &= amb - 1;
-      const int tk = __shfl(tok, src);
-      const int64_t ybase = (int64_t)tk * y.stride_token + (int64_t)h * y.stride_head;
-      double dist[kMaxClusters / 64];
-#pragma unroll
-      for (int m = 0; m < kMaxClusters / 64; ++m) dist[m] = 0.0;
-      for (int k = 0; k < kHeadDim; ++k) {
-        double yk;
-        if constexpr (F32) yk = (double)reinterpret_cast<const float*>(y.ptr)[ybase + k];
-        else yk = (double)bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(y.ptr)[ybase + k]);
-        const double wk = wh ? (double)wh[k] : 1.0;
-#pragma unroll
-        for (int m = 0; m < kMaxClusters / 64; ++m) {
-          const int j = lane + 64 * m;
-          if (j < C) {
-            const double diff = yk - (double)cent[((int64_t)h * C + j) * kHeadDim + k];
-            dist[m] = dist[m] + wk * (diff * diff);
-          }
-        }
+    if (half == 0 && tok < N) {
+      labels[(int64_t)h * N + tok] = (uint8_t)bidx[t];
+      const float thr = 2e-5f * (ynorm[t] + cn[h * C + bidx[t]]);
+      if (!(b2[t] - b1[t] > thr)) {
+        const int slot = atomicAdd(amb_count, 1);
+        amb_list[slot] = (int64_t)h * N + tok;
       }
-      double bv = INFINITY;
-      int bj = 0;
-#pragma unroll
-      for (int m = 0; m < kMaxClusters / 64; ++m) {
-        const int j = lane + 64 * m;
-        if (j < C && dist[m] < bv) { bv = dist[m]; bj = j; }
-      }
-#pragma unroll
-      for (int off = 32; off > 0; off >>= 1) {
-        const double ov = __shfl_xor(bv, off);
-        const int oj = __shfl_xor(bj, off);
-        if (ov < bv || (ov == bv && oj < bj)) { bv = ov; bj = oj; }
-      }
-      if (lane == src) bidx[t] = bj;
     }
-    if (half == 0 && tok < N) labels[(int64_t)h * N + tok] = (uint8_t)bidx[t];
   }
 }
 
-// One block per (head, cluster): 4 waves scan a quarter of the tokens each,
-// accumulate the members' rows in double-double (each lane two channels), then
-// combine the waves in a fixed order.  The double-double value is the exact
-// sum up to ~2^-104 relative, so its float64 rounding equals the correctly
-// rounded sum whatever the order of additions.
+// Float64 re-decision of queued close calls: one block per entry (grid-stride
+// over the device-side count).  Thread j computes sum_k w_k (y_k - c_jk)^2 in
+// channel order; the lowest index wins ties.
 template <bool F32>
-__global__ __launch_bounds__(256) void k_update(TensorView y, int C, int n_heads,
-                                                const uint8_t* __restrict__ labels,
-                                                float* __restrict__ c, int32_t* __restrict__ counts) {
+__global__ __launch_bounds__(256) void k_refine(TensorView y, int C, const float* __restrict__ cent,
+                                                const float* __restrict__ w, const int* __restrict__ amb_count,
+                                                const int64_t* __restrict__ amb_list, uint8_t* __restrict__ labels) {
+  __shared__ float sY[kHeadDim];
+  __shared__ float sW[kHeadDim];
+  __shared__ double s_bv[4];
+  __shared__ int s_bj[4];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int N = (int)y.n_tokens;
+  const int count = *amb_count;
+  for (int e = blockIdx.x; e < count; e += gridDim.x) {
+    const int64_t ht = amb_list[e];
+    const int h = (int)(ht / N), tok = (int)(ht % N);
+    __syncthreads();
+    if (threadIdx.x < kHeadDim) {
+      const int64_t off = (int64_t)tok * y.stride_token + (int64_t)h * y.stride_head + threadIdx.x;
+      if constexpr (F32) sY[threadIdx.x] = reinterpret_cast<const float*>(y.ptr)[off];
+      else sY[threadIdx.x] = bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(y.ptr)[off]);
+      sW[threadIdx.x] = w ? w[h * kHeadDim + threadIdx.x] : 1.0f;
+    }
+    __syncthreads();
+    const int j = threadIdx.x;
+    double dist = INFINITY;
+    if (j < C) {
+      dist = 0.0;
+      const float4* crow = reinterpret_cast<const float4*>(cent + ((int64_t)h * C + j) * kHeadDim);
+      for (int kb = 0; kb < kHeadDim / 32; ++kb) {
+        float4 cv[8];
+#pragma unroll
+        for (int x = 0; x < 8; ++x) cv[x] = crow[kb * 8 + x];
+#pragma unroll
+        for (int x = 0; x < 8; ++x) {
+          const float c4[4] = {cv[x].x, cv[x].y, cv[x].z, cv[x].w};
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int k = kb * 32 + x * 4 + q;
+            const double diff = (double)sY[k] - (double)c4[q];
+            dist = dist + (double)sW[k] * (diff * diff);
+          }
+        }
+      }
+    }
+    double bv = dist;
+    int bj = j;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+      const double ov = __shfl_xor(bv, off);
+      const int oj = __shfl_xor(bj, off);
+      if (ov < bv || (ov == bv && oj < bj)) { bv = ov; bj = oj; }
+    }
+    if (lane == 0) { s_bv[wave] = bv; s_bj[wave] = bj; }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      double v = s_bv[0];
+      int jj = s_bj[0];
+      for (int x = 1; x < 4; ++x)
+        if (s_bv[x] < v || (s_bv[x] == v && s_bj[x] < jj)) { v = s_bv[x]; jj = s_bj[x]; }
+      labels[ht] = (uint8_t)jj;
+    }
+  }
+}
+
+// Counting sort of one head's tokens by label: counts, exclusive offsets and
+// the member list (the order inside a cluster is immaterial: the sums below
+// are exact up to ~2^-104).  One block of 1024 threads per head.
+__global__ __launch_bounds__(1024) void k_sort(int N, int C, const uint8_t* __restrict__ labels,
+                                               int32_t* __restrict__ start, int32_t* __restrict__ order,
+                                               int32_t* __restrict__ counts, int* __restrict__ amb_count) {
+  __shared__ int cnt[kMaxClusters];
+  __shared__ int cur[kMaxClusters];
+  const int h = blockIdx.x;
+  if (h == 0 && threadIdx.x == 0 && amb_count) *amb_count = 0;   // the close-call queue of the next assign
+  const uint8_t* lab = labels + (int64_t)h * N;
+  for (int j = threadIdx.x; j < C; j += blockDim.x) cnt[j] = 0;
+  __syncthreads();
+  for (int i = threadIdx.x; i < N; i += blockDim.x) atomicAdd(&cnt[min((int)lab[i], C - 1)], 1);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int acc = 0;
+    for (int j = 0; j < C; ++j) {
+      cur[j] = acc;
+      start[h * (C + 1) + j] = acc;
+      acc += cnt[j];
+    }
+    start[h * (C + 1) + C] = acc;
+  }
+  __syncthreads();
+  if (counts)
+    for (int j = threadIdx.x; j < C; j += blockDim.x) counts[h * C + j] = cnt[j];
+  for (int i = threadIdx.x; i < N; i += blockDim.x) {
+    const int pos = atomicAdd(&cur[min((int)lab[i], C - 1)], 1);
+    order[(int64_t)h * N + pos] = i;
+  }
+}
+
+// One block per (head, cluster): the 4 waves take a quarter of the members
+// each, accumulate rows in double-double (each lane two channels, up to 8 rows
+// in flight), then combine in a fixed order.  The double-double value is the
+// exact sum up to ~2^-104 relative, so its float64 rounding is the correctly
+// rounded sum whatever the order; the mean is rounded once more to float32.
+template <bool F32>
+__global__ __launch_bounds__(256) void k_sum(TensorView y, int C, int n_heads, const int32_t* __restrict__ start,
+                                             const int32_t* __restrict__ order, float* __restrict__ c,
+                                             const float* __restrict__ w, uint16_t* __restrict__ planes,
+                                             float* __restrict__ cn) {
   __shared__ double sd[4][64][4];
-  __shared__ int scnt[4];
   const uint32_t logical = xcd_remap(blockIdx.x, (uint32_t)(n_heads * C));
   const int h = logical / C, j = logical % C;
   const int N = (int)y.n_tokens;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int per = (N + 3) / 4;
-  const int i0 = wave * per, i1 = min(N, i0 + per);
+  const int s0 = start[h * (C + 1) + j], s1 = start[h * (C + 1) + j + 1];
+  const int n = s1 - s0;
+  if (n == 0) return;                      // empty cluster: the centroid keeps its value
+  const int per = (n + 3) / 4;
+  const int m0 = s0 + wave * per, m1 = min(s1, m0 + per);
+  const int32_t* ord = order + (int64_t)h * N;
   DD a0{0.0, 0.0}, a1{0.0, 0.0};
-  int cnt = 0;
-  const uint8_t* lab = labels + (int64_t)h * N;
   const int64_t hoff = (int64_t)h * y.stride_head + lane * 2;
-  for (int base = i0; base < i1; base += 64) {
-    const int i = base + lane;
-    const bool m = (i < i1) && (lab[i] == j);
-    uint64_t mask = __ballot(m);
-    cnt += __popcll(mask);
-    while (mask) {
-      int idx[8];
+  int my_idx = 0;
+  for (int m = m0; m < m1; m += 8) {
+    if (((m - m0) & 63) == 0) my_idx = (m + lane < m1) ? ord[m + lane] : 0;   // 64 member ids per load
+    float vx[8], vy[8];
 #pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        if (mask) {
-          idx[q] = base + (__ffsll((unsigned long long)mask) - 1);
-          mask &= mask - 1;
+    for (int q = 0; q < 8; ++q) {
+      vx[q] = 0.f;
+      vy[q] = 0.f;
+      const int idq = __shfl(my_idx, ((m - m0) & 63) + q);
+      if (m + q < m1) {
+        const int64_t off = (int64_t)idq * y.stride_token + hoff;
+        if constexpr (F32) {
+          const float2 v = *reinterpret_cast<const float2*>(reinterpret_cast<const float*>(y.ptr) + off);
+          vx[q] = v.x;
+          vy[q] = v.y;
         } else {
-          idx[q] = -1;
+          const uint32_t v = *reinterpret_cast<const uint32_t*>(reinterpret_cast<const uint16_t*>(y.ptr) + off);
+          vx[q] = bf16_bits_to_f32(v & 0xFFFFu);
+          vy[q] = bf16_bits_to_f32(v >> 16);
         }
       }
-      float vx[8], vy[8];
+    }
 #pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        vx[q] = 0.f;
-        vy[q] = 0.f;
-        if (idx[q] >= 0) {
-          const int64_t off = (int64_t)idx[q] * y.stride_token + hoff;
-          if constexpr (F32) {
-            const float2 v = *reinterpret_cast<const float2*>(reinterpret_cast<const float*>(y.ptr) + off);
-            vx[q] = v.x;
-            vy[q] = v.y;
-          } else {
-            const uint32_t v = *reinterpret_cast<const uint32_t*>(reinterpret_cast<const uint16_t*>(y.ptr) + off);
-            vx[q] = bf16_bits_to_f32(v & 0xFFFFu);
-            vy[q] = bf16_bits_to_f32(v >> 16);
-          }
-        }
-      }
-#pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        if (idx[q] >= 0) {
-          a0.add((double)vx[q]);
-          a1.add((double)vy[q]);
-        }
+    for (int q = 0; q < 8; ++q) {
+      if (m + q < m1) {
+        a0.add((double)vx[q]);
+        a1.add((double)vy[q]);
       }
     }
   }
@@ -304,23 +395,37 @@ __global__ __launch_bounds__(256) void k_update(TensorView y, int C, int n_heads
   sd[wave][lane][1] = a0.lo;
   sd[wave][lane][2] = a1.hi;
   sd[wave][lane][3] = a1.lo;
-  if (lane == 0) scnt[wave] = cnt;
   __syncthreads();
   if (wave == 0) {
     DD t0{sd[0][lane][0], sd[0][lane][1]}, t1{sd[0][lane][2], sd[0][lane][3]};
-    int n = scnt[0];
 #pragma unroll
     for (int w = 1; w < 4; ++w) {
       t0.add(DD{sd[w][lane][0], sd[w][lane][1]});
       t1.add(DD{sd[w][lane][2], sd[w][lane][3]});
-      n += scnt[w];
     }
-    if (n > 0) {
-      float* cr = c + ((int64_t)h * C + j) * kHeadDim + lane * 2;
-      cr[0] = (float)(t0.hi / (double)n);
-      cr[1] = (float)(t1.hi / (double)n);
+    float* cr = c + ((int64_t)h * C + j) * kHeadDim + lane * 2;
+    const float c0 = (float)(t0.hi / (double)n);
+    const float c1 = (float)(t1.hi / (double)n);
+    cr[0] = c0;
+    cr[1] = c1;
+    if (planes) {   // operand planes and weighted norm for the next assign
+      double nrm = 0.0;
+      uint16_t* ph = planes + ((int64_t)h * 2 * C + j) * kHeadDim + lane * 2;
+      uint16_t* pl = planes + ((int64_t)h * 2 * C + C + j) * kHeadDim + lane * 2;
+      const float cv[2] = {c0, c1};
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const float wv = w ? w[h * kHeadDim + lane * 2 + e] : 1.0f;
+        const float b = wv * cv[e];
+        const uint32_t hi = f32_to_bf16_bits(b);
+        ph[e] = (uint16_t)hi;
+        pl[e] = (uint16_t)f32_to_bf16_bits(b - bf16_bits_to_f32(hi));
+        nrm += (double)wv * ((double)cv[e] * (double)cv[e]);
+      }
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) nrm += __shfl_xor(nrm, off);
+      if (lane == 0) cn[h * C + j] = (float)nrm;
     }
-    if (lane == 0 && counts) counts[h * C + j] = n;
   }
 }
 
@@ -337,36 +442,48 @@ __global__ void k_fill_zero(uint32_t* __restrict__ p, int64_t n) {
 }  // namespace
 
 hipError_t launch_kmeans_init(const TensorView& y, int H, int C, float* c, hipStream_t s) {
-  if (y.dtype == 0) hipLaunchKernelGGL(k_init<true>, dim3(H), dim3(256), 0, s, y, C, c);
-  else hipLaunchKernelGGL(k_init<false>, dim3(H), dim3(256), 0, s, y, C, c);
+  const dim3 grid((C + 7) / 8, H);
+  if (y.dtype == 0) hipLaunchKernelGGL(k_init<true>, grid, dim3(256), 0, s, y, C, c);
+  else hipLaunchKernelGGL(k_init<false>, grid, dim3(256), 0, s, y, C, c);
   return hipGetLastError();
 }
 
 hipError_t launch_centroid_prep(int H, int C, const float* c, const float* w, uint16_t* planes,
-                                float* cn, hipStream_t s) {
-  hipLaunchKernelGGL(k_prep, dim3(H * C), dim3(64), 0, s, C, c, w, planes, cn);
+                                float* cn, int* amb_count, hipStream_t s) {
+  hipLaunchKernelGGL(k_prep, dim3(H * C), dim3(64), 0, s, C, c, w, planes, cn, amb_count);
   return hipGetLastError();
 }
 
 hipError_t launch_kmeans_assign(const TensorView& y, int H, int C, const uint16_t* planes,
                                 const float* cn, const float* c, const float* w, uint8_t* labels,
-                                hipStream_t s) {
+                                int* amb_count, int64_t* amb_list, hipStream_t s) {
   const int tiles = (int)((y.n_tokens + kAssignTokens - 1) / kAssignTokens);
   const dim3 grid(tiles * H);
   if (y.dtype == 0)
-    hipLaunchKernelGGL(k_assign<true>, grid, dim3(256), 0, s, y, C, tiles, H, planes, cn, c, w, labels);
+    hipLaunchKernelGGL(k_assign<true>, grid, dim3(256), 0, s, y, C, tiles, H, planes, cn, w, labels, amb_count,
+                       amb_list);
   else
-    hipLaunchKernelGGL(k_assign<false>, grid, dim3(256), 0, s, y, C, tiles, H, planes, cn, c, w, labels);
+    hipLaunchKernelGGL(k_assign<false>, grid, dim3(256), 0, s, y, C, tiles, H, planes, cn, w, labels, amb_count,
+                       amb_list);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const dim3 rgrid(256);
+  if (y.dtype == 0)
+    hipLaunchKernelGGL(k_refine<true>, rgrid, dim3(256), 0, s, y, C, c, w, amb_count, amb_list, labels);
+  else
+    hipLaunchKernelGGL(k_refine<false>, rgrid, dim3(256), 0, s, y, C, c, w, amb_count, amb_list, labels);
   return hipGetLastError();
 }
 
 hipError_t launch_kmeans_update(const TensorView& y, int H, int C, const uint8_t* labels, float* c,
-                                int32_t* counts, hipStream_t s) {
+                                int32_t* counts, int32_t* start, int32_t* order, const float* w,
+                                uint16_t* planes, float* cn, int* amb_count, hipStream_t s) {
+  hipLaunchKernelGGL(k_sort, dim3(H), dim3(1024), 0, s, (int)y.n_tokens, C, labels, start, order, counts, amb_count);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
   const dim3 grid(H * C);
-  if (y.dtype == 0)
-    hipLaunchKernelGGL(k_update<true>, grid, dim3(256), 0, s, y, C, H, labels, c, counts);
-  else
-    hipLaunchKernelGGL(k_update<false>, grid, dim3(256), 0, s, y, C, H, labels, c, counts);
+  if (y.dtype == 0) hipLaunchKernelGGL(k_sum<true>, grid, dim3(256), 0, s, y, C, H, start, order, c, w, planes, cn);
+  else hipLaunchKernelGGL(k_sum<false>, grid, dim3(256), 0, s, y, C, H, start, order, c, w, planes, cn);
   return hipGetLastError();
 }
 

@@ -147,7 +147,7 @@ TensorView view_of(const qkv_tensor* t) {
 
 // ---- workspace plans ----
 struct QuantWs {
-  uint64_t c, planes, cn, ybuf0, ybuf1, bytes;
+  uint64_t c, planes, cn, start, order, amb_count, amb_list, ybuf0, ybuf1, bytes;
 };
 
 QuantWs quant_ws(const qkv_config* c, int64_t n) {
@@ -157,6 +157,10 @@ QuantWs quant_ws(const qkv_config* c, int64_t n) {
   w.c = off;       off += align256(H * C * kHeadDim * 4);
   w.planes = off;  off += align256(H * 2 * C * kHeadDim * 2);
   w.cn = off;      off += align256(H * C * 4);
+  w.start = off;   off += align256(H * (C + 1) * 4);
+  w.order = off;   off += align256(H * (uint64_t)n * 4);
+  w.amb_count = off; off += 256;
+  w.amb_list = off; off += align256(H * (uint64_t)n * 8);
   w.ybuf0 = off;   if (c->n_stages > 1) off += align256(H * (uint64_t)n * kHeadDim * 4);
   w.ybuf1 = off;   if (c->n_stages > 2) off += align256(H * (uint64_t)n * kHeadDim * 4);
   w.bytes = off;
@@ -212,14 +216,22 @@ int check_ws(const void* ws, size_t have, uint64_t need, const char* what) {
 uint8_t* at(void* base, uint64_t off) { return reinterpret_cast<uint8_t*>(base) + off; }
 
 // Run the k-means protocol of one stage on `y`; labels go to `labels`.
-int run_kmeans(const qkv_config* cfg, const TensorView& y, const float* w, uint8_t* labels, float* c,
-               uint16_t* planes, float* cn, hipStream_t s) {
+int run_kmeans(const qkv_config* cfg, const TensorView& y, const float* w, uint8_t* labels, void* workspace,
+               const QuantWs& ws, hipStream_t s) {
   const int H = cfg->n_heads, C = cfg->n_clusters;
+  float* c = reinterpret_cast<float*>(at(workspace, ws.c));
+  uint16_t* planes = reinterpret_cast<uint16_t*>(at(workspace, ws.planes));
+  float* cn = reinterpret_cast<float*>(at(workspace, ws.cn));
+  int32_t* start = reinterpret_cast<int32_t*>(at(workspace, ws.start));
+  int32_t* order = reinterpret_cast<int32_t*>(at(workspace, ws.order));
+  int* amb = reinterpret_cast<int*>(at(workspace, ws.amb_count));
+  int64_t* amb_list = reinterpret_cast<int64_t*>(at(workspace, ws.amb_list));
   QKV_HIP(launch_kmeans_init(y, H, C, c, s));
+  QKV_HIP(launch_centroid_prep(H, C, c, w, planes, cn, amb, s));
   for (int it = 0; it < cfg->kmeans_iters; ++it) {
-    QKV_HIP(launch_centroid_prep(H, C, c, w, planes, cn, s));
-    QKV_HIP(launch_kmeans_assign(y, H, C, planes, cn, c, w, labels, s));
-    QKV_HIP(launch_kmeans_update(y, H, C, labels, c, nullptr, s));
+    const bool last = it + 1 == cfg->kmeans_iters;
+    QKV_HIP(launch_kmeans_assign(y, H, C, planes, cn, c, w, labels, amb, amb_list, s));
+    QKV_HIP(launch_kmeans_update(y, H, C, labels, c, nullptr, start, order, w, last ? nullptr : planes, cn, amb, s));
   }
   return QKV_OK;
 }
@@ -283,8 +295,6 @@ int qkv_quantize_chunk(const qkv_config* cfg, const qkv_tensor* x, const qkv_sid
   const ChunkDecode g = decode_of(cfg, N, nullptr);
   uint8_t* base = reinterpret_cast<uint8_t*>(packed);
   float* c = reinterpret_cast<float*>(at(workspace, ws.c));
-  uint16_t* planes = reinterpret_cast<uint16_t*>(at(workspace, ws.planes));
-  float* cn = reinterpret_cast<float*>(at(workspace, ws.cn));
   const float* wk = cfg->use_qsac ? w : nullptr;
   const uint8_t* pm = cfg->n_int4_channels > 0 ? perm : nullptr;
   if (pm) QKV_HIP(launch_copy_perm(pm, base + L.off_perm, H, s));
@@ -297,7 +307,7 @@ int qkv_quantize_chunk(const qkv_config* cfg, const qkv_tensor* x, const qkv_sid
       QKV_HIP(launch_fill_zero_u32(labels, L.stage_bytes_labels / 4, s));
       QKV_HIP(launch_fill_zero_u32(cent, L.stage_bytes_centroids / 4, s));
     } else {
-      QKV_TRY(run_kmeans(cfg, y, wk, labels, c, planes, cn, s));
+      QKV_TRY(run_kmeans(cfg, y, wk, labels, workspace, ws, s));
       QKV_HIP(launch_centroid_bf16(H, C, c, cent, s));
     }
     PackArgs pa;
@@ -509,23 +519,30 @@ int qkv_kmeans_assign(const qkv_config* cfg, const qkv_tensor* y, const float* c
   QKV_TRY(check_tensor(y, cfg->n_heads, fn));
   if (!centroids || !labels) return fail(QKV_EINVAL, "%s: centroids/labels NULL", fn);
   const QuantWs ws = quant_ws(cfg, y->n_tokens);
-  QKV_TRY(check_ws(workspace, workspace_bytes, ws.cn + align256((uint64_t)cfg->n_heads * cfg->n_clusters * 4), fn));
+  QKV_TRY(check_ws(workspace, workspace_bytes, ws.ybuf0, fn));
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   uint16_t* planes = reinterpret_cast<uint16_t*>(at(workspace, ws.planes));
   float* cn = reinterpret_cast<float*>(at(workspace, ws.cn));
-  QKV_HIP(launch_centroid_prep(cfg->n_heads, cfg->n_clusters, centroids, w, planes, cn, s));
-  QKV_HIP(launch_kmeans_assign(view_of(y), cfg->n_heads, cfg->n_clusters, planes, cn, centroids, w, labels, s));
+  int* amb = reinterpret_cast<int*>(at(workspace, ws.amb_count));
+  int64_t* amb_list = reinterpret_cast<int64_t*>(at(workspace, ws.amb_list));
+  QKV_HIP(launch_centroid_prep(cfg->n_heads, cfg->n_clusters, centroids, w, planes, cn, amb, s));
+  QKV_HIP(launch_kmeans_assign(view_of(y), cfg->n_heads, cfg->n_clusters, planes, cn, centroids, w, labels, amb,
+                               amb_list, s));
   return ok();
 }
 
 int qkv_kmeans_update(const qkv_config* cfg, const qkv_tensor* y, const uint8_t* labels, float* centroids,
-                      int32_t* counts, void* stream) {
+                      int32_t* counts, void* workspace, size_t workspace_bytes, void* stream) {
   const char* fn = "qkv_kmeans_update";
   QKV_TRY(check_config(cfg, fn));
   QKV_TRY(check_tensor(y, cfg->n_heads, fn));
   if (!centroids || !labels) return fail(QKV_EINVAL, "%s: centroids/labels NULL", fn);
+  const QuantWs ws = quant_ws(cfg, y->n_tokens);
+  QKV_TRY(check_ws(workspace, workspace_bytes, ws.ybuf0, fn));
   QKV_HIP(launch_kmeans_update(view_of(y), cfg->n_heads, cfg->n_clusters, labels, centroids, counts,
-                               reinterpret_cast<hipStream_t>(stream)));
+                               reinterpret_cast<int32_t*>(at(workspace, ws.start)),
+                               reinterpret_cast<int32_t*>(at(workspace, ws.order)), nullptr, nullptr, nullptr,
+                               reinterpret_cast<int*>(at(workspace, ws.amb_count)), reinterpret_cast<hipStream_t>(stream)));
   return ok();
 }
 

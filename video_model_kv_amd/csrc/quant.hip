@@ -150,6 +150,78 @@ __global__ __launch_bounds__(256) void k_quant_pack(PackArgs a) {
   a.scales[((int64_t)h * a.N + i) * a.groups + g] = (uint16_t)sbits;
 }
 
+// Uniform layout without a channel permutation: one thread per 8 consecutive
+// channels of a (head, token) row, so a wave covers 4 rows with 16-byte loads;
+// a group of G channels spans G/8 aligned lanes and takes its max through xor
+// shuffles; two lanes' INT2 codes form one word.  Same arithmetic as
+// k_quant_pack.
+template <int G, int BITS, bool F32>
+__global__ __launch_bounds__(256) void k_quant_pack_fast(PackArgs a) {
+  constexpr int L = G / 8;                       // lanes per group
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t total = (int64_t)a.H * a.N * 16;
+  const bool valid = gid < total;                 // invalid lanes still join the shuffles
+  const int64_t g2 = valid ? gid : total - 1;
+  const int part = (int)(g2 & 15);
+  const int64_t row = g2 >> 4;                    // (h, i) in [H][N] order
+  const int i = (int)(row % a.N), h = (int)(row / a.N);
+  const int k0 = part * 8;
+  float yv[8], cv[8], r[8];
+  const int64_t yoff = (int64_t)i * a.y.stride_token + (int64_t)h * a.y.stride_head + k0;
+  if constexpr (F32) {
+    const float4 p0 = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(a.y.ptr) + yoff);
+    const float4 p1 = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(a.y.ptr) + yoff + 4);
+    yv[0] = p0.x; yv[1] = p0.y; yv[2] = p0.z; yv[3] = p0.w; yv[4] = p1.x; yv[5] = p1.y; yv[6] = p1.z; yv[7] = p1.w;
+  } else {
+    const uint4 p = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(a.y.ptr) + yoff);
+    const uint32_t w4[4] = {p.x, p.y, p.z, p.w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) yv[e] = bf16_bits_to_f32((w4[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
+  }
+  const int lab = min((int)a.labels[row], a.C - 1);
+  {
+    const uint4 p = *reinterpret_cast<const uint4*>(a.centroids + ((int64_t)h * a.C + lab) * kHeadDim + k0);
+    const uint32_t w4[4] = {p.x, p.y, p.z, p.w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) cv[e] = bf16_bits_to_f32((w4[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
+  }
+  float amax = 0.0f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    r[e] = yv[e] - cv[e];
+    amax = fmaxf(amax, fabsf(r[e]));
+  }
+#pragma unroll
+  for (int off = 1; off < L; off <<= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+  constexpr float qmax = (float)((1 << (BITS - 1)) - 1);
+  const uint32_t sbits = f32_to_bf16_bits(amax / qmax);
+  const float S = bf16_bits_to_f32(sbits);
+  uint32_t bitsw = 0;
+  float q[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    q[e] = 0.0f;
+    if (S != 0.0f) q[e] = fminf(fmaxf(rintf(r[e] / S), -(float)(1 << (BITS - 1))), qmax);
+    bitsw |= (uint32_t)((int)q[e] + (1 << (BITS - 1))) << (BITS * e);
+  }
+  uint32_t* wrow = a.codes + row * a.words;
+  if constexpr (BITS == 2) {
+    const uint32_t other = __shfl_xor(bitsw, 1);
+    if (valid && (part & 1) == 0) wrow[part >> 1] = bitsw | (other << 16);
+  } else {
+    if (valid) wrow[part] = bitsw;
+  }
+  if (valid && part % L == 0) a.scales[row * a.groups + part / L] = (uint16_t)sbits;
+  if (valid && a.y_next) {
+    float o[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = __fsub_rn(yv[e], __fadd_rn(S * q[e], cv[e]));
+    float* yp = a.y_next + row * kHeadDim + k0;
+    *reinterpret_cast<float4*>(yp) = make_float4(o[0], o[1], o[2], o[3]);
+    *reinterpret_cast<float4*>(yp + 4) = make_float4(o[4], o[5], o[6], o[7]);
+  }
+}
+
 __device__ __forceinline__ const uint8_t* stage_ptr(const ChunkDecode& d, uint64_t off, uint64_t stride, int l) {
   return d.base + off + stride * (uint64_t)l;
 }
@@ -251,9 +323,23 @@ __global__ __launch_bounds__(256) void k_psac_encode(ChunkDecode d, TensorView x
 }  // namespace
 
 hipError_t launch_quant_pack(const PackArgs& a, hipStream_t s) {
+  const bool f32 = a.y.dtype == 0;
+  if (!a.perm && a.n_int4 == 0) {
+    const int64_t total = (int64_t)a.H * a.N * 16;
+    const dim3 grid((unsigned)((total + 255) / 256)), block(256);
+#define QKV_QF(GV, BV)                                                                        \
+    if (a.group == GV && a.bits == BV) {                                                      \
+      if (f32) hipLaunchKernelGGL((k_quant_pack_fast<GV, BV, true>), grid, block, 0, s, a);    \
+      else hipLaunchKernelGGL((k_quant_pack_fast<GV, BV, false>), grid, block, 0, s, a);       \
+      return hipGetLastError();                                                               \
+    }
+    QKV_QF(16, 2) QKV_QF(32, 2) QKV_QF(64, 2) QKV_QF(128, 2)
+    QKV_QF(16, 4) QKV_QF(32, 4) QKV_QF(64, 4) QKV_QF(128, 4)
+#undef QKV_QF
+    return hipErrorInvalidValue;
+  }
   const int64_t total = (int64_t)a.H * a.N * a.groups;
   const dim3 grid((unsigned)((total + 255) / 256)), block(256);
-  const bool f32 = a.y.dtype == 0;
 #define QKV_QP(GV)                                                              \
   if (a.group == GV) {                                                          \
     if (f32) hipLaunchKernelGGL((k_quant_pack<GV, true>), grid, block, 0, s, a); \
