@@ -27,7 +27,6 @@ namespace qkv {
 
 namespace {
 
-constexpr int kQTile = 128;     // queries per workgroup (4 waves x 32)
 constexpr int kKTile = 64;      // keys per tile
 constexpr int kKPitch = 136;    // bf16 pitch of the K_hat rows in LDS
 constexpr int kVPitch = 68;     // bf16 pitch of the V_hat^T rows in LDS (34 dwords)
@@ -91,274 +90,539 @@ __device__ __forceinline__ void decode_generic(const ChunkDecode& d, const Chann
   }
 }
 
-// Fast decode for one uniform INT2 stage with groups of >= 32 channels:
-// channels k0..k0+NCH-1 (NCH <= 32, k0 % NCH == 0 and inside one group).
-template <int NCH>
-__device__ __forceinline__ void decode_int2(const ChunkDecode& d, int h, int j, int k0, float* v) {
-  const int64_t row = (int64_t)h * d.N + j;
-  const uint32_t* codes = reinterpret_cast<const uint32_t*>(d.base + d.off_codes) + row * d.words + k0 / 16;
-  const float S = bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(d.base + d.off_scales)[row * d.groups + k0 / d.group]);
-  const int lab = min((int)(d.base + d.off_labels)[row], d.C - 1);
-  const uint16_t* crow = reinterpret_cast<const uint16_t*>(d.base + d.off_centroids) + ((int64_t)h * d.C + lab) * kHeadDim + k0;
-  uint32_t w[(NCH + 15) / 16];
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWaves = 8;                 // two waves per SIMD
+constexpr int kBM = kWaves * 32;          // queries per workgroup, 32 per wave
+constexpr int kThreads = kWaves * 64;
+constexpr int kItems = 1024 / kThreads;   // K (and V) decode items per thread per tile
+constexpr int kRing = 3;                  // raw-tile slots in LDS
+constexpr int kVCentPitch = 136;          // u16 pitch of a gathered V centroid row (272 bytes)
+constexpr float kF16Max = 65504.0f;
+static_assert(kBM == kAttendQueries, "queries per workgroup");
+
+// two fp32 values -> packed fp16 (round to nearest even), saturated to the fp16 range
+__device__ __forceinline__ uint32_t pack_f16x2(float x0, float x1) {
+  f16x2 r;
+  r[0] = (_Float16)__builtin_amdgcn_fmed3f(x0, -kF16Max, kF16Max);
+  r[1] = (_Float16)__builtin_amdgcn_fmed3f(x1, -kF16Max, kF16Max);
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+// Two 2-bit codes (already spread to bits [0,1] and [16,17] of x) -> fp16 pair
+// (u0 - 2, u1 - 2): 0x6400 | u is the fp16 number 1024 + u.
+__device__ __forceinline__ f16x2 codes_to_f16x2(uint32_t x) {
+  const f16x2 biased = __builtin_bit_cast(f16x2, x | 0x64006400u);
+  const f16x2 off = {(_Float16)1026.0f, (_Float16)1026.0f};
+  return biased - off;
+}
+// bf16 pair (lo, hi halves of w) -> fp16 pair (round to nearest even; beyond
+// the fp16 range -> +-inf, clamped by the caller)
+__device__ __forceinline__ f16x2 bf16x2_to_f16x2(uint32_t w) {
+  f16x2 r;
+  r[0] = (_Float16)__uint_as_float(w << 16);
+  r[1] = (_Float16)__uint_as_float(w & 0xFFFF0000u);
+  return r;
+}
+__device__ __forceinline__ uint32_t f16x2_sat(f16x2 v) {
+  const f16x2 lim = {(_Float16)65504.0f, (_Float16)65504.0f};
+  v = __builtin_elementwise_min(v, lim);
+  v = __builtin_elementwise_max(v, -lim);
+  return __builtin_bit_cast(uint32_t, v);
+}
+// S * q + c as saturated fp16 pairs for NP consecutive channel pairs: code
+// pair j of `t` sits at bits [4j, 4j+1] and [4j+16, 4j+17] (t = codes | codes << 14).
+template <int NP>
+__device__ __forceinline__ void decode_pairs_f16(uint32_t t, float S, const uint32_t* cw, uint32_t* out) {
+  const _Float16 sh = (_Float16)__builtin_amdgcn_fmed3f(S, -kF16Max, kF16Max);
+  const f16x2 s2 = {sh, sh};
 #pragma unroll
-  for (int x = 0; x < (NCH + 15) / 16; ++x) w[x] = codes[x];
-  uint4 cw[NCH / 8];
-#pragma unroll
-  for (int x = 0; x < NCH / 8; ++x) cw[x] = reinterpret_cast<const uint4*>(crow)[x];
-  const uint32_t* cu = reinterpret_cast<const uint32_t*>(cw);
-#pragma unroll
-  for (int e = 0; e < NCH; ++e) {
-    const uint32_t u = (w[e / 16] >> (2 * (e % 16))) & 3u;
-    const float q = (float)((int)u - 2);
-    const uint32_t cb = (cu[e / 2] >> (16 * (e & 1))) & 0xFFFFu;
-    v[e] = __fadd_rn(S * q, bf16_bits_to_f32(cb));
+  for (int j = 0; j < NP; ++j) {
+    const f16x2 q = codes_to_f16x2((t >> (4 * j)) & 0x00030003u);
+    out[j] = f16x2_sat(__builtin_elementwise_fma(s2, q, bf16x2_to_f16x2(cw[j])));
   }
 }
 
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo_elem, float hi_elem) {
-  return f32_to_bf16_bits(lo_elem) | (f32_to_bf16_bits(hi_elem) << 16);
+typedef __attribute__((address_space(3))) void* lds_ptr;
+typedef __attribute__((address_space(1))) void* glb_ptr;
+
+// Asynchronous global -> LDS copy: every active lane moves BYTES bytes from its
+// own address to dst + lane * BYTES (dst is wave-uniform).  Tracked by vmcnt.
+template <int BYTES>
+__device__ __forceinline__ void dma(const void* src, void* dst) {
+  const glb_ptr g = (glb_ptr)const_cast<void*>(src);
+  if constexpr (BYTES == 16) __builtin_amdgcn_global_load_lds(g, (lds_ptr)dst, 16, 0, 0);
+  else if constexpr (BYTES == 4) __builtin_amdgcn_global_load_lds(g, (lds_ptr)dst, 4, 0, 0);
+  else if constexpr (BYTES == 2) __builtin_amdgcn_global_load_lds(g, (lds_ptr)dst, 2, 0, 0);
+  else __builtin_amdgcn_global_load_lds(g, (lds_ptr)dst, 1, 0, 0);
+  static_assert(BYTES == 16 || BYTES == 4 || BYTES == 2 || BYTES == 1, "copy size");
 }
+__device__ __forceinline__ void wait_dma() { __builtin_amdgcn_s_waitcnt(0x0F70); }   // vmcnt(0)
 
-template <bool QF32, bool KFAST, bool VFAST>
-__global__ __launch_bounds__(256) void k_attend(AttendArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t sKh[kKTile][kKPitch];
-  __shared__ __attribute__((aligned(16))) uint16_t sKl[kKTile][kKPitch];
-  __shared__ __attribute__((aligned(16))) uint16_t sKp[kKTile][16];
-  __shared__ __attribute__((aligned(16))) uint16_t sVt[kHeadDim][kVPitch];
-  __shared__ ChannelCode tabK[kHeadDim], tabV[kHeadDim];
+typedef const __attribute__((address_space(4))) ChunkRec* crec_ptr;
+typedef const __attribute__((address_space(4))) TileInfo* ctile_ptr;
+typedef const __attribute__((address_space(4))) AttendArgs* cargs_ptr;
 
-  const int q_tiles = (a.Nq + kQTile - 1) / kQTile;
+struct __attribute__((aligned(16))) AttendSmem {
+  uint16_t K[2][kKTile][kKPitch];              // fp16 K_hat rows
+  uint16_t Vt[2][kHeadDim][kVPitch];           // fp16 V_hat^T rows
+  uint16_t Kp[2][kKTile][16];                  // fp16 [coef | coef]
+  uint16_t centK[2][kKTile * kHeadDim];        // gathered K centroid rows (bf16)
+  uint16_t centV[2][kKTile * kVCentPitch];     // gathered V centroid rows (bf16, padded)
+  uint32_t rc[kRing][2][kKTile * 8];           // [slot][K/V] code words
+  uint16_t rs[kRing][2][kKTile * 4];           // [slot][K/V] scales
+  uint8_t rl[kRing][2][kKTile];                // [slot][K/V] labels
+  ChannelCode tabK[kHeadDim], tabV[kHeadDim];  // generic decode tables
+};
+
+template <bool QF32, bool KFAST, bool VFAST, bool LOGITS>
+__global__ __launch_bounds__(kThreads) void k_attend(AttendArgs a) {
+  __shared__ AttendSmem sm;
+
+  const int q_tiles = (a.Nq + kBM - 1) / kBM;
   const uint32_t total = (uint32_t)(q_tiles * a.n_split * a.H);
   const uint32_t logical = xcd_remap(blockIdx.x, total);
   const int qt = logical % q_tiles;
   const int split = (logical / q_tiles) % a.n_split;
   const int h = logical / (q_tiles * a.n_split);
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave >> 2;                   // the two waves of a SIMD sit in different groups
   const int col = lane & 31, half = lane >> 5;
-  const int qrow = qt * kQTile + wave * 32 + col;     // this lane's query
+  const int q_last = min(a.Nq, (qt + 1) * kBM) - 1;
+  const int wq_first = qt * kBM + wave * 32;   // this wave's queries
+  const int wq_last = min(a.Nq, wq_first + 32) - 1;
+  const bool wave_active = wq_first < a.Nq;
+  const bool psac = a.psac_rank > 0;
+  const int qrow = wq_first + col;             // this lane's query
   const bool qok = qrow < a.Nq;
-  const int q_last = min(a.Nq, (qt + 1) * kQTile) - 1;
 
-  // ---- Q fragments (B operand: column = query, k = channel) ----
-  bf16x8 qh[8];
-  bf16x8 ql[QF32 ? 8 : 1];
+  // ---- Q fragments in fp16 (B operand: column = query, k = channel) ----
+  f16x8 qh[8];
+  f16x8 ql[QF32 ? 8 : 1];
+  f16x8 qpsac;
   {
     const int64_t base = (int64_t)(qok ? qrow : 0) * a.q.stride_token + (int64_t)h * a.q.stride_head;
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
       const int ch = s * 16 + half * 8;
+      float v[8];
       if constexpr (QF32) {
         const float* p = reinterpret_cast<const float*>(a.q.ptr) + base + ch;
-        float4 x0 = qok ? *reinterpret_cast<const float4*>(p) : make_float4(0, 0, 0, 0);
-        float4 x1 = qok ? *reinterpret_cast<const float4*>(p + 4) : make_float4(0, 0, 0, 0);
-        float v[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-        u16x8 hi, lo;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const uint32_t hb = f32_to_bf16_bits(v[e]);
-          hi[e] = (uint16_t)hb;
-          lo[e] = (uint16_t)f32_to_bf16_bits(v[e] - bf16_bits_to_f32(hb));
-        }
-        qh[s] = __builtin_bit_cast(bf16x8, hi);
-        ql[QF32 ? s : 0] = __builtin_bit_cast(bf16x8, lo);
+        const float4 x0 = qok ? *reinterpret_cast<const float4*>(p) : make_float4(0, 0, 0, 0);
+        const float4 x1 = qok ? *reinterpret_cast<const float4*>(p + 4) : make_float4(0, 0, 0, 0);
+        v[0] = x0.x; v[1] = x0.y; v[2] = x0.z; v[3] = x0.w; v[4] = x1.x; v[5] = x1.y; v[6] = x1.z; v[7] = x1.w;
       } else {
         const uint16_t* p = reinterpret_cast<const uint16_t*>(a.q.ptr) + base + ch;
-        qh[s] = as_bf16x8(qok ? *reinterpret_cast<const uint4*>(p) : make_uint4(0, 0, 0, 0));
+        const uint4 r = qok ? *reinterpret_cast<const uint4*>(p) : make_uint4(0, 0, 0, 0);
+        const uint32_t r4[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = bf16_bits_to_f32((r4[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
+      }
+      f16x8 hi;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        v[e] = __builtin_amdgcn_fmed3f(v[e], -kF16Max, kF16Max);
+        hi[e] = (_Float16)v[e];
+      }
+      qh[s] = hi;
+      if constexpr (QF32) {
+        f16x8 lo;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) lo[e] = (_Float16)(v[e] - (float)hi[e]);
+        ql[QF32 ? s : 0] = lo;
       }
     }
-  }
-  bf16x8 qpsac;
-  {
-    u16x8 t;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       float v = 0.0f;
-      if (a.psac_rank > 0 && qok && e < a.psac_rank) v = a.qu[((int64_t)h * a.Nq + qrow) * kMaxRank + e];
-      const uint32_t hb = f32_to_bf16_bits(v);
-      t[e] = (uint16_t)(half == 0 ? hb : f32_to_bf16_bits(v - bf16_bits_to_f32(hb)));
+      if (psac && qok && e < a.psac_rank)
+        v = __builtin_amdgcn_fmed3f(a.qu[((int64_t)h * a.Nq + qrow) * kMaxRank + e], -kF16Max, kF16Max);
+      const _Float16 hv = (_Float16)v;
+      qpsac[e] = half == 0 ? hv : (_Float16)(v - (float)hv);
     }
-    qpsac = __builtin_bit_cast(bf16x8, t);
   }
 
   f32x16 o[4];
 #pragma unroll
   for (int db = 0; db < 4; ++db) o[db] = f32x16{};
-  float m_run = -INFINITY, l_run = 0.0f;
+  float m_run = -INFINITY, l_run = 0.0f;       // m_run: running max in the scaled (log2) domain
   const float c2 = a.scale * kLog2e;
 
   const int t_begin = (int)(((int64_t)a.n_tiles * split) / a.n_split);
-  const int t_end = (int)(((int64_t)a.n_tiles * (split + 1)) / a.n_split);
-  // chunk holding tile t_begin (binary search over the tile starts)
-  int c = 0;
-  {
-    int lo = 0, hi = a.n_chunks - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (a.chunks[mid].tile_start <= t_begin) lo = mid; else hi = mid - 1;
-    }
-    c = lo;
+  int t_end = (int)(((int64_t)a.n_tiles * (split + 1)) / a.n_split);
+
+  // Tile and chunk records are read-only here: scalar loads through the
+  // constant address space keep them out of the vector-memory counter, which
+  // the asynchronous copies below are waited on with.
+  // The arguments themselves are re-read through the kernel-argument segment at
+  // every pipeline step (A is made opaque there): holding them all in scalar
+  // registers across the loop would spill them.
+  cargs_ptr A = (cargs_ptr)__builtin_amdgcn_kernarg_segment_ptr();
+  crec_ptr recs = (crec_ptr)A->chunks;
+  ctile_ptr tiles = (ctile_ptr)A->tiles;
+  struct TileRef {
+    int chunk, token0, nvalid, kstart, n;
+  };
+  auto tile_ref = [&](int j) __attribute__((always_inline)) -> TileRef {
+    TileRef t;
+    t.chunk = tiles[j].chunk;
+    t.token0 = tiles[j].token0;
+    t.n = recs[t.chunk].n;
+    t.nvalid = min(kKTile, t.n - t.token0);
+    t.kstart = (int)recs[t.chunk].token_start + t.token0;
+    return t;
+  };
+
+  // causal: drop trailing tiles wholly above the diagonal (unless debug logits are requested)
+  if (a.causal && !LOGITS) {
+    while (t_end > t_begin && tile_ref(t_end - 1).kstart > q_last) --t_end;
   }
-  int cur_chunk = -1;
-  ChunkDecode dk, dv;
-  for (int ti = t_begin; ti < t_end; ++ti) {
-    while (c + 1 < a.n_chunks && a.chunks[c + 1].tile_start <= ti) ++c;
-    const ChunkRec rec = a.chunks[c];
-    const int token0 = (ti - rec.tile_start) * kKTile;
-    const int64_t kstart = rec.token_start + token0;                     // global index of key 0
-    // a tile wholly above the diagonal holds no visible key (visited anyway when
-    // debug logits are requested, so that every masked entry is written)
-    if (a.causal && kstart > q_last && !a.logits) continue;
-    const int nvalid = min(kKTile, rec.n - token0);
-    __syncthreads();   // previous tile fully consumed
-    if (c != cur_chunk) {
-      dk = make_decode(a.kp, rec.n, rec.kbase);
-      dv = make_decode(a.vp, rec.n, rec.vbase);
-      if constexpr (!KFAST) build_tab(dk, h, tabK);
-      if constexpr (!VFAST) build_tab(dv, h, tabV);
-      cur_chunk = c;
-      __syncthreads();
+  if (t_begin >= t_end) {
+    // nothing visible in this split: write an empty partial
+    if (qok && a.n_split > 1) {
+      if (half == 0) {
+        float* ml = a.part_ml + (((int64_t)split * a.H + h) * a.Nq + qrow) * 2;
+        ml[0] = -INFINITY;
+        ml[1] = 0.0f;
+      }
+      float* prow = a.part_o + (((int64_t)split * a.H + h) * a.Nq + qrow) * kHeadDim;
+      for (int d0 = half * 4; d0 < kHeadDim; d0 += 8)
+        *reinterpret_cast<float4*>(prow + d0) = make_float4(0, 0, 0, 0);
     }
-    // ---- decode K_hat (hi/lo) : thread = (key, 32-channel quarter) ----
-    {
-      const int key = threadIdx.x >> 2, k0 = (threadIdx.x & 3) * 32;
-      float v[32];
-      if (key < nvalid) {
-        if constexpr (KFAST) decode_int2<32>(dk, h, token0 + key, k0, v);
-        else decode_generic<32>(dk, tabK, h, token0 + key, k0, v);
+    return;
+  }
+
+  // ---- tile pipeline ----
+  // Four stages, one tile each, one barrier per step:
+  //   (1) raw copy: code words, scales and labels -> LDS ring (asynchronous);
+  //   (2) centroid gather: the labelled centroid rows -> LDS staging (asynchronous);
+  //   (3) decode: K_hat rows and V_hat^T rows in fp16 -> LDS buffer;
+  //   (4) compute: S^T = K_hat Q^T, online softmax, O^T += V_hat^T P^T.
+  // At step i the workgroup runs (1) on tile i+3, (2) on i+2, (3) on i+1 and (4)
+  // on i.  Waves 0-3 compute before they decode, waves 4-7 decode before they
+  // compute, so the two waves sharing a SIMD overlap MFMA and VALU work.
+  //
+  // Per-thread indexes used inside the steps come from xtid, which is made
+  // opaque at every step so that the addresses derived from it are recomputed
+  // there instead of being held in registers across the whole loop.
+  int xtid = tid;
+  auto geom = [&](int cc, bool v) __attribute__((always_inline)) -> ChunkDecode {
+    LayoutParams p;
+    p.H = v ? A->vp.H : A->kp.H;
+    p.C = v ? A->vp.C : A->kp.C;
+    p.n_stages = v ? A->vp.n_stages : A->kp.n_stages;
+    p.bits = v ? A->vp.bits : A->kp.bits;
+    p.group = v ? A->vp.group : A->kp.group;
+    p.n_int4 = v ? A->vp.n_int4 : A->kp.n_int4;
+    p.psac_rank = v ? A->vp.psac_rank : A->kp.psac_rank;
+    return make_decode(p, recs[cc].n, v ? recs[cc].vbase : recs[cc].kbase);
+  };
+  const int kG = kHeadDim / A->kp.group, vG = kHeadDim / A->vp.group;   // scale groups per token (fast paths)
+
+  // (1) raw copy of tile j into ring slot r: waves 0-3 copy K, waves 4-7 V.
+  // Code words and 4-byte scale runs go by asynchronous copy; labels (and
+  // 2-byte scales, one group per token) by plain loads into `held`, written to
+  // the ring by raw_finish at the end of the step.
+  uint32_t held = 0;
+  auto raw_copy = [&](int j, int r) __attribute__((always_inline)) {
+    const int lane = xtid & 63;
+    const int v = wave >> 2, part = wave & 3;
+    if ((v == 0 && !KFAST) || (v == 1 && !VFAST)) return;
+    const TileRef t = tile_ref(j);
+    const int64_t row0 = (int64_t)h * t.n + t.token0;
+    if (part < 2) {                              // code words: 32 bytes per key
+      const int key = part * 32 + (lane >> 1);
+      const uint8_t* src = v ? recs[t.chunk].vcodes : recs[t.chunk].kcodes;
+      if (key < t.nvalid) dma<16>(src + (row0 * 32 + part * 1024 + lane * 16), &sm.rc[r][v][part * 256]);
+    } else if (part == 2) {                      // scales: 2 * G bytes per key
+      const int G = v ? vG : kG;
+      const uint8_t* src = (v ? recs[t.chunk].vscales : recs[t.chunk].kscales) + row0 * G * 2;
+      if (G == 1) {
+        held = lane < t.nvalid ? reinterpret_cast<const uint16_t*>(src)[lane] : 0u;
+      } else {                                   // row0 * 2G is a multiple of 4
+        const int per = 2 * G;
+#pragma unroll
+        for (int x = 0; x < 2; ++x) {
+          const int off = x * 256 + lane * 4;
+          if (x * 256 < kKTile * per && off / per < t.nvalid) dma<4>(src + off, &sm.rs[r][v][x * 128]);
+        }
+      }
+    } else {                                     // labels: 1 byte per key
+      const uint8_t* src = v ? recs[t.chunk].vlabels : recs[t.chunk].klabels;
+      held = lane < t.nvalid ? (uint32_t)src[row0 + lane] : 0u;
+    }
+  };
+  auto raw_finish = [&](int r) __attribute__((always_inline)) {
+    const int lane = xtid & 63;
+    const int v = wave >> 2, part = wave & 3;
+    if ((v == 0 && !KFAST) || (v == 1 && !VFAST)) return;
+    if (part == 3) sm.rl[r][v][lane] = (uint8_t)held;
+    else if (part == 2 && (v ? vG : kG) == 1) sm.rs[r][v][lane] = (uint16_t)held;
+  };
+  // (2) centroid gather of tile j (labels in ring slot r) into staging slot g
+  auto cent_gather = [&](int j, int r, int g) __attribute__((always_inline)) {
+    const int lane = xtid & 63;
+    const TileRef t = tile_ref(j);
+    if constexpr (KFAST) {                       // 16 copies of 4 rows; two per wave
+      const uint16_t* cent = reinterpret_cast<const uint16_t*>(recs[t.chunk].kcent) + (int64_t)h * A->kp.C * kHeadDim;
+#pragma unroll
+      for (int x = 0; x < 2; ++x) {
+        const int n = wave * 2 + x;
+        const int key = n * 4 + (lane >> 4);
+        const int lab = min((int)sm.rl[r][0][key], A->kp.C - 1);
+        if (key < t.nvalid) dma<16>(cent + lab * kHeadDim + (lane & 15) * 8, &sm.centK[g][n * 4 * kHeadDim]);
+      }
+    }
+    if constexpr (VFAST) {                       // 64 copies of one row; eight per wave
+      const uint16_t* cent = reinterpret_cast<const uint16_t*>(recs[t.chunk].vcent) + (int64_t)h * A->vp.C * kHeadDim;
+#pragma unroll
+      for (int x = 0; x < 8; ++x) {
+        const int key = wave * 8 + x;
+        const int lab = min((int)sm.rl[r][1][key], A->vp.C - 1);
+        if (key < t.nvalid && lane < 16) dma<16>(cent + lab * kHeadDim + lane * 8, &sm.centV[g][key * kVCentPitch]);
+      }
+    }
+  };
+  // (3) decode tile j (ring slot r, staging slot g) into LDS buffer b
+  auto decode_tile = [&](int j, int r, int g, int b) __attribute__((always_inline)) {
+    const int tid = xtid;
+    const TileRef t = tile_ref(j);
+#pragma unroll
+    for (int x = 0; x < kItems; ++x) {          // K: (key, 8 channels) per item
+      const int item = tid + x * kThreads;
+      const int key = item >> 4, k0 = (item & 15) * 8;
+      const bool ok = key < t.nvalid;
+      uint32_t o4[4];
+      if constexpr (KFAST) {
+        const uint32_t w = sm.rc[r][0][key * 8 + (k0 >> 4)];
+        const uint32_t sb = sm.rs[r][0][key * kG + k0 * kG / kHeadDim];
+        const uint4 cr = *reinterpret_cast<const uint4*>(&sm.centK[g][key * kHeadDim + k0]);
+        const uint32_t code16 = ok ? (w >> (16 * ((k0 >> 3) & 1))) & 0xFFFFu : 0xAAAAu;   // code 2 -> 0
+        const float S = ok ? bf16_bits_to_f32(sb) : 0.0f;
+        const uint32_t cw[4] = {ok ? cr.x : 0u, ok ? cr.y : 0u, ok ? cr.z : 0u, ok ? cr.w : 0u};
+        decode_pairs_f16<4>(code16 | (code16 << 14), S, cw, o4);
       } else {
+        float v[8];
+        if (ok) decode_generic<8>(geom(t.chunk, false), sm.tabK, h, t.token0 + key, k0, v);
+        else {
 #pragma unroll
-        for (int e = 0; e < 32; ++e) v[e] = 0.0f;
-      }
-      uint32_t hw[16], lw[16];
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const uint32_t h0 = f32_to_bf16_bits(v[2 * e]), h1 = f32_to_bf16_bits(v[2 * e + 1]);
-        hw[e] = h0 | (h1 << 16);
-        lw[e] = f32_to_bf16_bits(v[2 * e] - bf16_bits_to_f32(h0)) |
-                (f32_to_bf16_bits(v[2 * e + 1] - bf16_bits_to_f32(h1)) << 16);
-      }
-#pragma unroll
-      for (int x = 0; x < 4; ++x) {
-        *reinterpret_cast<uint4*>(&sKh[key][k0 + 8 * x]) = make_uint4(hw[4 * x], hw[4 * x + 1], hw[4 * x + 2], hw[4 * x + 3]);
-        *reinterpret_cast<uint4*>(&sKl[key][k0 + 8 * x]) = make_uint4(lw[4 * x], lw[4 * x + 1], lw[4 * x + 2], lw[4 * x + 3]);
-      }
-      if (a.psac_rank > 0 && threadIdx.x < kKTile) {
-        const int kk = threadIdx.x;
-        uint16_t cf[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) cf[e] = 0;
-        if (kk < nvalid) {
-          const uint16_t* cp = reinterpret_cast<const uint16_t*>(dk.base + dk.off_psac) +
-                               ((int64_t)h * dk.N + token0 + kk) * dk.psac_rank;
-          for (int e = 0; e < dk.psac_rank; ++e) cf[e] = cp[e];
+          for (int e = 0; e < 8; ++e) v[e] = 0.0f;
         }
 #pragma unroll
-        for (int e = 0; e < 8; ++e) { sKp[kk][e] = cf[e]; sKp[kk][8 + e] = cf[e]; }
+        for (int e = 0; e < 4; ++e) o4[e] = pack_f16x2(v[2 * e], v[2 * e + 1]);
+      }
+      *reinterpret_cast<uint4*>(&sm.K[b][key][k0]) = make_uint4(o4[0], o4[1], o4[2], o4[3]);
+    }
+#pragma unroll
+    for (int x = 0; x < kItems; ++x) {          // V: (2 keys, 4 channels) per item
+      const int item = tid + x * kThreads;
+      const int kp = item & 31, k0 = (item >> 5) * 4;
+      uint32_t pr[2][2];                         // [key][channel pair] fp16 pairs
+#pragma unroll
+      for (int y = 0; y < 2; ++y) {
+        const int key = 2 * kp + y;
+        const bool ok = key < t.nvalid;
+        if constexpr (VFAST) {
+          const uint32_t w = sm.rc[r][1][key * 8 + (k0 >> 4)];
+          const uint32_t sb = sm.rs[r][1][key * vG + k0 * vG / kHeadDim];
+          const uint2 cr = *reinterpret_cast<const uint2*>(&sm.centV[g][key * kVCentPitch + k0]);
+          const uint32_t code8 = ok ? (w >> (2 * (k0 & 15))) & 0xFFu : 0xAAu;
+          const float S = ok ? bf16_bits_to_f32(sb) : 0.0f;
+          const uint32_t cw[2] = {ok ? cr.x : 0u, ok ? cr.y : 0u};
+          decode_pairs_f16<2>(code8 | (code8 << 14), S, cw, pr[y]);
+        } else {
+          float v[4];
+          if (ok) decode_generic<4>(geom(t.chunk, true), sm.tabV, h, t.token0 + key, k0, v);
+          else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] = 0.0f;
+          }
+          pr[y][0] = pack_f16x2(v[0], v[1]);
+          pr[y][1] = pack_f16x2(v[2], v[3]);
+        }
+      }
+      // channel k0 + e gets (key 2kp, key 2kp + 1)
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj) {
+        *reinterpret_cast<uint32_t*>(&sm.Vt[b][k0 + 2 * jj][2 * kp]) = __builtin_amdgcn_perm(pr[1][jj], pr[0][jj], 0x05040100u);
+        *reinterpret_cast<uint32_t*>(&sm.Vt[b][k0 + 2 * jj + 1][2 * kp]) = __builtin_amdgcn_perm(pr[1][jj], pr[0][jj], 0x07060302u);
       }
     }
-    // ---- decode V_hat^T (bf16) : thread = (key pair, 16-channel block) ----
-    {
-      const int kp = threadIdx.x & 31, k0 = (threadIdx.x >> 5) * 16;
-      float v0[16], v1[16];
-      const int j0 = 2 * kp, j1 = 2 * kp + 1;
-      if (j0 < nvalid) {
-        if constexpr (VFAST) decode_int2<16>(dv, h, token0 + j0, k0, v0);
-        else decode_generic<16>(dv, tabV, h, token0 + j0, k0, v0);
-      } else {
+    if (psac && tid < kKTile) {
+      uint32_t f16w[4] = {0u, 0u, 0u, 0u};
+      if (tid < t.nvalid) {
+        const int rank = A->psac_rank;
+        const uint16_t* cpp = reinterpret_cast<const uint16_t*>(recs[t.chunk].kpsac) + ((int64_t)h * t.n + t.token0 + tid) * rank;
+        float f[8];
 #pragma unroll
-        for (int e = 0; e < 16; ++e) v0[e] = 0.0f;
+        for (int e = 0; e < 8; ++e) f[e] = e < rank ? bf16_bits_to_f32(cpp[e]) : 0.0f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) f16w[e] = pack_f16x2(f[2 * e], f[2 * e + 1]);
       }
-      if (j1 < nvalid) {
-        if constexpr (VFAST) decode_int2<16>(dv, h, token0 + j1, k0, v1);
-        else decode_generic<16>(dv, tabV, h, token0 + j1, k0, v1);
-      } else {
-#pragma unroll
-        for (int e = 0; e < 16; ++e) v1[e] = 0.0f;
-      }
-#pragma unroll
-      for (int e = 0; e < 16; ++e)
-        *reinterpret_cast<uint32_t*>(&sVt[k0 + e][2 * kp]) = pack_bf16x2(v0[e], v1[e]);
+      *reinterpret_cast<uint4*>(&sm.Kp[b][tid][0]) = make_uint4(f16w[0], f16w[1], f16w[2], f16w[3]);
+      *reinterpret_cast<uint4*>(&sm.Kp[b][tid][8]) = make_uint4(f16w[0], f16w[1], f16w[2], f16w[3]);
     }
-    __syncthreads();
-
-    // ---- S^T = K_hat Q^T for the two 32-key blocks ----
-    f32x16 sacc[2];
+  };
+  // (4) this wave's 32 queries against tile j in LDS buffer b
+  auto compute_tile = [&](int j, int b) __attribute__((always_inline)) {
+    const int lane = xtid & 63, col = lane & 31, half = lane >> 5;
+    if (!wave_active) return;
+    const TileRef t = tile_ref(j);
+    if (A->causal && !LOGITS && t.kstart > wq_last) return;      // wholly above the diagonal
+    const bool need_mask = t.nvalid < kKTile || (A->causal && t.kstart + kKTile - 1 > wq_first);
+    // S^T = K_hat Q^T, both 32-key halves interleaved (fp16 operands, fp32 accumulation)
+    f32x16 acc[2] = {f32x16{}, f32x16{}};
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      f32x16 acc = {};
-      const int krow = kb * 32 + col;
+    for (int s = 0; s < 8; ++s) {
+      f16x8 kf[2];
 #pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        const bf16x8 kh = as_bf16x8(*reinterpret_cast<const uint4*>(&sKh[krow][s * 16 + half * 8]));
-        const bf16x8 kl = as_bf16x8(*reinterpret_cast<const uint4*>(&sKl[krow][s * 16 + half * 8]));
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kh, qh[s], acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kl, qh[s], acc, 0, 0, 0);
-        if constexpr (QF32) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kh, ql[QF32 ? s : 0], acc, 0, 0, 0);
-      }
-      if (a.psac_rank > 0) {
-        const bf16x8 kp = as_bf16x8(*reinterpret_cast<const uint4*>(&sKp[krow][half * 8]));
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kp, qpsac, acc, 0, 0, 0);
-      }
-      sacc[kb] = acc;
-    }
-
-    // ---- masks, debug logits, online softmax (exp2 domain) ----
-    float x[2][16];
-    float mloc = -INFINITY;
+      for (int kb = 0; kb < 2; ++kb)
+        kf[kb] = __builtin_bit_cast(f16x8, *reinterpret_cast<const uint4*>(&sm.K[b][kb * 32 + col][s * 16 + half * 8]));
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int kl = kb * 32 + (r >> 2) * 8 + half * 4 + (r & 3);   // key within tile
-        const int64_t kg = kstart + kl;
-        bool valid = kl < nvalid;
-        if (a.causal) valid = valid && (kg <= qrow);
-        if (a.logits && qok && kl < nvalid)
-          a.logits[((int64_t)h * a.Nq + qrow) * a.Nk + kg] = valid ? sacc[kb][r] * a.scale : -INFINITY;
-        const float xv = valid ? sacc[kb][r] * c2 : -INFINITY;
-        x[kb][r] = xv;
-        mloc = fmaxf(mloc, xv);
+      for (int kb = 0; kb < 2; ++kb) {
+        acc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf[kb], qh[s], acc[kb], 0, 0, 0);
+        if constexpr (QF32) acc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf[kb], ql[QF32 ? s : 0], acc[kb], 0, 0, 0);
       }
     }
+    if (psac) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const f16x8 kpf = __builtin_bit_cast(f16x8, *reinterpret_cast<const uint4*>(&sm.Kp[b][kb * 32 + col][half * 8]));
+        acc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kpf, qpsac, acc[kb], 0, 0, 0);
+      }
+    }
+    float sv[32];                                // key kb*32 + (r/4)*8 + half*4 + r%4 for sv[kb*16 + r]
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sv[kb * 16 + r] = acc[kb][r];
+    if (need_mask || LOGITS) {
+      // key kl of element i is kc(i) + half*4; it is visible iff kl < nvalid and
+      // (causal) kstart + kl <= qrow, i.e. iff kc(i) < lim.  The select is done
+      // with integer bit operations, not per-element compare masks.
+      int lim = t.nvalid;
+      if (A->causal) lim = min(lim, qrow - t.kstart + 1);
+      lim -= half * 4;
+#pragma unroll
+      for (int i = 0; i < 32; ++i) {
+        const int kc = (i >> 4) * 32 + ((i & 15) >> 2) * 8 + (i & 3);
+        const uint32_t masked = (uint32_t)((lim - 1 - kc) >> 31);   // all ones when hidden
+        if (LOGITS) {
+          const int kl = kc + half * 4;
+          if (qok && kl < t.nvalid)
+            A->logits[((int64_t)h * A->Nq + qrow) * A->Nk + (int64_t)(t.kstart + kl)] = masked ? -INFINITY : sv[i] * A->scale;
+        }
+        sv[i] = __uint_as_float((__float_as_uint(sv[i]) & ~masked) | (0xFF800000u & masked));
+      }
+    }
+    float mloc = sv[0];
+#pragma unroll
+    for (int i = 1; i < 32; ++i) mloc = fmaxf(mloc, sv[i]);
     mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
-    const float m_new = fmaxf(m_run, mloc);
+    const float m_cand = mloc * c2;                             // c2 > 0
+    // lazy rescaling: keep the running max unless it grows by more than 8 (p <= 2^8)
+    const bool grow = m_cand > m_run + 8.0f;
     float alpha = 1.0f;
-    if (m_new != -INFINITY) alpha = exp2f(m_run - m_new);   // m_run = -inf gives 0
+    if (__any(grow)) {
+      const float m_new = fmaxf(m_run, m_cand);
+      alpha = (m_run == -INFINITY) ? 0.0f : exp2f(m_run - m_new);
+      m_run = m_new;
+#pragma unroll
+      for (int db = 0; db < 4; ++db) o[db] *= alpha;
+    }
+    const float mneg = m_run == -INFINITY ? 0.0f : -m_run;
+    // hardware exp2 (v_exp_f32): arguments are <= 8 here; results below the
+    // fp32 normal range flush to zero, which a probability can afford.  The sum
+    // runs over the fp16-rounded probabilities that enter P V.
+    uint32_t pw[4][4];                           // [16-key step][pair]
     float psum = 0.0f;
-    u16x8 pb[2][2];
+    const f16x2 ones = {(_Float16)1.0f, (_Float16)1.0f};
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = (m_new == -INFINITY) ? 0.0f : exp2f(x[kb][r] - m_new);
-        psum += p;
-        pb[kb][r >> 3][r & 7] = (uint16_t)f32_to_bf16_bits(p);
-      }
+    for (int i = 0; i < 32; i += 2) {
+      f16x2 pp;
+      pp[0] = (_Float16)__builtin_amdgcn_exp2f(__builtin_fmaf(sv[i], c2, mneg));
+      pp[1] = (_Float16)__builtin_amdgcn_exp2f(__builtin_fmaf(sv[i + 1], c2, mneg));
+      psum = __builtin_amdgcn_fdot2(pp, ones, psum, false);
+      pw[i >> 3][(i & 7) >> 1] = __builtin_bit_cast(uint32_t, pp);
     }
     l_run = l_run * alpha + psum;
-    m_run = m_new;
+    // O^T += V_hat^T P^T: A = V_hat^T (row = channel, k = key slot), B = P^T
 #pragma unroll
-    for (int db = 0; db < 4; ++db) o[db] *= alpha;
-
-    // ---- O^T += V_hat^T P^T ----
+    for (int st = 0; st < 4; ++st) {
+      const int kbase = st * 16 + half * 4;
+      f16x8 vf[4];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+      for (int db = 0; db < 4; ++db) {
+        const int drow = db * 32 + col;
+        const uint2 v0 = *reinterpret_cast<const uint2*>(&sm.Vt[b][drow][kbase]);
+        const uint2 v1 = *reinterpret_cast<const uint2*>(&sm.Vt[b][drow][kbase + 8]);
+        vf[db] = __builtin_bit_cast(f16x8, make_uint4(v0.x, v0.y, v1.x, v1.y));
+      }
+      const f16x8 pfrag = __builtin_bit_cast(f16x8, make_uint4(pw[st][0], pw[st][1], pw[st][2], pw[st][3]));
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const bf16x8 pfrag = __builtin_bit_cast(bf16x8, pb[kb][t]);
-        const int kbase = kb * 32 + t * 16 + half * 4;
-#pragma unroll
-        for (int db = 0; db < 4; ++db) {
-          const int drow = db * 32 + col;
-          const uint2 v0 = *reinterpret_cast<const uint2*>(&sVt[drow][kbase]);
-          const uint2 v1 = *reinterpret_cast<const uint2*>(&sVt[drow][kbase + 8]);
-          const bf16x8 vfrag = as_bf16x8(make_uint4(v0.x, v0.y, v1.x, v1.y));
-          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vfrag, pfrag, o[db], 0, 0, 0);
-        }
+      for (int db = 0; db < 4; ++db) o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf[db], pfrag, o[db], 0, 0, 0);
+    }
+  };
+  // generic decode tables follow the chunk of the tile being decoded
+  int gen_chunk = -1;
+  auto tables_for = [&](int j) __attribute__((always_inline)) {
+    if constexpr (!KFAST || !VFAST) {
+      const int chunk = tiles[j].chunk;
+      if (chunk != gen_chunk) {
+        __syncthreads();
+        if constexpr (!KFAST) build_tab(geom(chunk, false), h, sm.tabK);
+        if constexpr (!VFAST) build_tab(geom(chunk, true), h, sm.tabV);
+        __syncthreads();
+        gen_chunk = chunk;
       }
     }
+  };
+
+  // ---- prologue: tiles t_begin .. t_begin+2 raw, t_begin .. t_begin+1 gathered, t_begin decoded ----
+  const int r0 = t_begin % kRing;
+#pragma unroll 1
+  for (int k = 0; k < 3 && t_begin + k < t_end; ++k) {
+    raw_copy(t_begin + k, (r0 + k) % kRing);
+    raw_finish((r0 + k) % kRing);
+  }
+  wait_dma();
+  __syncthreads();
+  cent_gather(t_begin, r0, t_begin & 1);
+  if (t_begin + 1 < t_end) cent_gather(t_begin + 1, (r0 + 1) % kRing, (t_begin + 1) & 1);
+  wait_dma();
+  __syncthreads();
+  tables_for(t_begin);
+  decode_tile(t_begin, r0, t_begin & 1, t_begin & 1);
+  __syncthreads();
+
+  int ring = r0;                                 // ring slot of tile ti
+#pragma unroll 1
+  for (int ti = t_begin; ti < t_end; ++ti) {
+    xtid = tid;
+    asm volatile("" : "+v"(xtid));
+    asm volatile("" : "+s"(A));
+    recs = (crec_ptr)A->chunks;
+    tiles = (ctile_ptr)A->tiles;
+    const int r3 = ring;                         // (ti + 3) % 3
+    const int r1 = ring + 1 == kRing ? 0 : ring + 1;
+    const int r2 = r1 + 1 == kRing ? 0 : r1 + 1;
+    const bool has1 = ti + 1 < t_end, has2 = ti + 2 < t_end, has3 = ti + 3 < t_end;
+    if (has3) raw_copy(ti + 3, r3);              // (1) tile i+3
+    if (has2) cent_gather(ti + 2, r2, ti & 1);   // (2) tile i+2
+    if (has1) tables_for(ti + 1);
+#pragma unroll 1
+    for (int ph = 0; ph < 2; ++ph) {
+      if (ph == grp) compute_tile(ti, ti & 1);                              // (4) tile i
+      else if (has1) decode_tile(ti + 1, r1, (ti + 1) & 1, (ti + 1) & 1);   // (3) tile i+1
+    }
+    if (has3) raw_finish(r3);
+    wait_dma();
+    __syncthreads();
+    ring = r1;
   }
 
   // ---- epilogue ----
@@ -444,6 +708,19 @@ __global__ __launch_bounds__(256) void k_qu(TensorView q, int H, int Nq, int r, 
   for (int b = 0; b < kMaxRank; ++b) qu[gid * kMaxRank + b] = b < r ? (float)acc[b] : 0.0f;
 }
 
+// TileInfo of every tile: the chunk holding it (last chunk whose first tile is <= j).
+__global__ __launch_bounds__(256) void k_tile_table(const ChunkRec* __restrict__ recs, int n_chunks, int n_tiles,
+                                                    TileInfo* __restrict__ tiles) {
+  const int j = blockIdx.x * blockDim.x + threadIdx.x;
+  if (j >= n_tiles) return;
+  int lo = 0, hi = n_chunks - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (recs[mid].tile_start <= j) lo = mid; else hi = mid - 1;
+  }
+  tiles[j] = TileInfo{lo, (j - recs[lo].tile_start) * kKTile};
+}
+
 __global__ void k_upload(ChunkBatch b, ChunkRec* __restrict__ dst) {
   const int i = threadIdx.x;
   if (i < b.count) dst[b.first + i] = b.rec[i];
@@ -453,6 +730,12 @@ __global__ void k_upload(ChunkBatch b, ChunkRec* __restrict__ dst) {
 
 hipError_t launch_upload_chunks(const ChunkBatch& b, ChunkRec* dst, hipStream_t s) {
   hipLaunchKernelGGL(k_upload, dim3(1), dim3(kChunkBatch), 0, s, b, dst);
+  return hipGetLastError();
+}
+
+hipError_t launch_tile_table(const ChunkRec* recs, int n_chunks, int n_tiles, TileInfo* tiles, hipStream_t s) {
+  if (n_tiles <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_tile_table, dim3((unsigned)((n_tiles + 255) / 256)), dim3(256), 0, s, recs, n_chunks, n_tiles, tiles);
   return hipGetLastError();
 }
 
@@ -466,11 +749,15 @@ hipError_t launch_attend(const AttendArgs& a, hipStream_t s) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  const int q_tiles = (a.Nq + kQTile - 1) / kQTile;
+  const int q_tiles = (a.Nq + kBM - 1) / kBM;
   const dim3 grid((unsigned)(q_tiles * a.n_split * a.H));
   const bool kf = a.k_uniform_int2_1stage;
   const bool vf = a.v_uniform_int2_1stage;
-#define QKV_AT(QF, KF, VF) hipLaunchKernelGGL((k_attend<QF, KF, VF>), grid, dim3(256), 0, s, a)
+#define QKV_AT(QF, KF, VF)                                                                        \
+  do {                                                                                            \
+    if (a.logits) hipLaunchKernelGGL((k_attend<QF, KF, VF, true>), grid, dim3(kThreads), 0, s, a);  \
+    else hipLaunchKernelGGL((k_attend<QF, KF, VF, false>), grid, dim3(kThreads), 0, s, a);          \
+  } while (0)
   if (a.q.dtype == 0) {
     if (kf && vf) QKV_AT(true, true, true);
     else if (!kf && vf) QKV_AT(true, false, true);

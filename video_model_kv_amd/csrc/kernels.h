@@ -70,15 +70,32 @@ hipError_t launch_gram(const TensorView& q, int H, double* partial, int n_split,
 
 // ---- attention (attend.hip) ----
 constexpr int kMaxChunks = 1024;
-constexpr int kChunkBatch = 96;      // chunk records per upload launch (fits the kernel-argument limit)
+constexpr int kChunkBatch = 32;      // chunk records per upload launch (fits the kernel-argument limit)
+constexpr int kAttendQueries = 256;  // queries per attention workgroup (8 waves of 32)
 
 // Per-chunk record of the concatenated cache (device array in the workspace).
+// The section pointers are those of stage 0, head 0; head h adds h * N times
+// the per-token size (h * C rows for the centroids).
 struct ChunkRec {
   const uint8_t* kbase;
   const uint8_t* vbase;
+  const uint8_t* kcodes;
+  const uint8_t* kscales;
+  const uint8_t* klabels;
+  const uint8_t* kcent;
+  const uint8_t* kpsac;
+  const uint8_t* vcodes;
+  const uint8_t* vscales;
+  const uint8_t* vlabels;
+  const uint8_t* vcent;
   int64_t token_start;   // global index of the chunk's first token
   int32_t n;             // tokens in the chunk
   int32_t tile_start;    // global index of the chunk's first 64-key tile
+};
+
+// Per 64-key tile of the concatenated cache: its chunk and first token there.
+struct TileInfo {
+  int32_t chunk, token0;
 };
 
 struct ChunkBatch {
@@ -86,6 +103,8 @@ struct ChunkBatch {
   ChunkRec rec[kChunkBatch];
 };
 hipError_t launch_upload_chunks(const ChunkBatch& b, ChunkRec* dst, hipStream_t s);
+// TileInfo of every tile from the uploaded chunk records.
+hipError_t launch_tile_table(const ChunkRec* recs, int n_chunks, int n_tiles, TileInfo* tiles, hipStream_t s);
 
 struct AttendArgs {
   TensorView q;
@@ -94,6 +113,7 @@ struct AttendArgs {
   int n_chunks, n_tiles;
   LayoutParams kp, vp;           // layouts of the K and V chunks
   const ChunkRec* chunks;        // device [n_chunks]
+  const TileInfo* tiles;         // device [n_tiles]
   const float* U;                // [H][128][r] or null
   int psac_rank;
   float* qu;                     // workspace [H][Nq][8] f32

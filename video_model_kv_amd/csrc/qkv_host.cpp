@@ -170,32 +170,66 @@ QuantWs quant_ws(const qkv_config* c, int64_t n) {
 constexpr int kTileKeys = 64;
 
 struct AttendWs {
-  uint64_t chunks, qu, part_o, part_ml, bytes;
+  uint64_t chunks, tiles, qu, part_o, part_ml, bytes;
 };
 
-AttendWs attend_ws(int H, int64_t nq, int n_chunks, int n_split) {
+// rows = n_split * nq: one partial (o, m, l) row per split and query (none when n_split == 1)
+AttendWs attend_ws(int H, int64_t nq, int n_chunks, int64_t n_tiles, int64_t split_rows) {
   AttendWs w;
   uint64_t off = 0;
   w.chunks = off;  off += align256((uint64_t)n_chunks * sizeof(ChunkRec));
+  w.tiles = off;   off += align256((uint64_t)n_tiles * sizeof(TileInfo));
   w.qu = off;      off += align256((uint64_t)H * nq * kMaxRank * 4);
-  w.part_o = off;  if (n_split > 1) off += align256((uint64_t)n_split * H * nq * kHeadDim * 4);
-  w.part_ml = off; if (n_split > 1) off += align256((uint64_t)n_split * H * nq * 2 * 4);
+  w.part_o = off;  off += align256((uint64_t)split_rows * H * kHeadDim * 4);
+  w.part_ml = off; off += align256((uint64_t)split_rows * H * 2 * 4);
   w.bytes = off;
   return w;
 }
 
-// Key splits: enough workgroups to fill the chip several times over.
-int choose_splits(int H, int64_t nq, int64_t n_tiles) {
-  const int64_t q_tiles = (nq + 127) / 128;
-  const int64_t base = q_tiles * H;
-  int64_t want = (4096 + base - 1) / base;                       // >= 4096 workgroups
-  want = std::max<int64_t>(1, std::min<int64_t>(want, n_tiles));
-  want = std::min<int64_t>(want, 256);
-  return (int)want;
+// Key splits.  One attention workgroup fills a compute unit (its LDS use), so
+// the grid runs in rounds of kComputeUnits workgroups.  The split count is at
+// most split_cap (about eight rounds of workgroups; the workspace is sized for
+// it) and minimises rounds x (tiles per split + ~3 tiles of fixed per-split
+// cost: pipeline fill and the partial write).
+constexpr int kComputeUnits = 256;
+
+int split_cap(int H, int64_t nq) {
+  const int64_t base = (nq + kAttendQueries - 1) / kAttendQueries * H;
+  return (int)std::max<int64_t>(1, std::min<int64_t>(64, (8 * kComputeUnits + base - 1) / base));
 }
 
+int choose_splits(int H, int64_t nq, int64_t n_tiles) {
+  const int64_t base = (nq + kAttendQueries - 1) / kAttendQueries * H;
+  const int64_t hi = std::max<int64_t>(1, std::min<int64_t>(n_tiles, split_cap(H, nq)));
+  int64_t best = 1;
+  double best_cost = 0.0;
+  for (int64_t s = 1; s <= hi; ++s) {
+    const int64_t rounds = (base * s + kComputeUnits - 1) / kComputeUnits;
+    const double cost = (double)rounds * ((double)n_tiles / (double)s + 3.0);
+    if (s == 1 || cost < best_cost) {
+      best = s;
+      best_cost = cost;
+    }
+  }
+  return (int)best;
+}
+
+// The largest n_split * nq over every query count nq <= n_query (split counts
+// never exceed split_cap(H, nq), which only changes with the number of query tiles).
 int64_t max_tiles(int64_t max_chunk_tokens, int n_chunks) {
   return (int64_t)n_chunks * ((max_chunk_tokens + kTileKeys - 1) / kTileKeys);
+}
+
+int64_t max_split_rows(int H, int64_t n_query) {
+  int64_t best = 0;
+  const int64_t tiles = (n_query + kAttendQueries - 1) / kAttendQueries;
+  for (int64_t k = 1; k <= tiles; ++k) {
+    const int64_t nq = std::min<int64_t>(n_query, k * kAttendQueries);
+    const int cap = split_cap(H, nq);
+    best = std::max<int64_t>(best, cap > 1 ? cap * nq : 0);
+    if (cap == 1) break;                     // from here on no splits at all
+  }
+  return best;
 }
 
 constexpr int kGramSplit = 16;
@@ -262,9 +296,8 @@ int qkv_workspace_bytes(const qkv_config* cfg, int64_t max_chunk_tokens, int64_t
   uint64_t need = 0;
   if (max_chunk_tokens > 0) need = std::max(need, quant_ws(cfg, max_chunk_tokens).bytes);
   if (n_query > 0 && n_chunks > 0) {
-    const int64_t nt = max_tiles(std::max<int64_t>(max_chunk_tokens, 1), n_chunks);
-    const int ns = choose_splits(cfg->n_heads, n_query, nt);
-    need = std::max(need, attend_ws(cfg->n_heads, n_query, n_chunks, ns).bytes);
+    need = std::max(need, attend_ws(cfg->n_heads, n_query, n_chunks, max_tiles(std::max<int64_t>(max_chunk_tokens, 1), n_chunks),
+                                    max_split_rows(cfg->n_heads, n_query)).bytes);
   }
   if (n_query > 0) need = std::max(need, psac_ws(cfg->n_heads));
   *out = (size_t)need;
@@ -380,29 +413,38 @@ int qkv_attend(const qkv_config* k_cfg, const qkv_config* v_cfg, const qkv_tenso
   if (!std::isfinite(softmax_scale) || softmax_scale < 0.0f) return fail(QKV_EINVAL, "%s: softmax_scale must be >= 0", fn);
   const int64_t Nq = q->n_tokens;
   std::vector<ChunkRec> recs(n_chunks);
-  int64_t Nk = 0, n_tiles = 0, max_n = 0;
+  int64_t Nk = 0, n_tiles = 0;
   for (int i = 0; i < n_chunks; ++i) {
     const int64_t n = chunk_tokens[i];
     if (n < std::max(k_cfg->n_clusters, v_cfg->n_clusters) || n > ((int64_t)1 << 24))
       return fail(QKV_EINVAL, "%s: chunk %d has %lld tokens", fn, i, (long long)n);
     if (!k_chunks[i] || !v_chunks[i] || !aligned16(k_chunks[i]) || !aligned16(v_chunks[i]))
       return fail(QKV_EINVAL, "%s: chunk %d pointer NULL or misaligned", fn, i);
-    recs[i].kbase = reinterpret_cast<const uint8_t*>(k_chunks[i]);
-    recs[i].vbase = reinterpret_cast<const uint8_t*>(v_chunks[i]);
+    const ChunkDecode dk = make_decode(params_of(k_cfg), n, k_chunks[i]);
+    const ChunkDecode dv = make_decode(params_of(v_cfg), n, v_chunks[i]);
+    recs[i].kbase = dk.base;
+    recs[i].vbase = dv.base;
+    recs[i].kcodes = dk.base + dk.off_codes;
+    recs[i].kscales = dk.base + dk.off_scales;
+    recs[i].klabels = dk.base + dk.off_labels;
+    recs[i].kcent = dk.base + dk.off_centroids;
+    recs[i].kpsac = dk.base + dk.off_psac;
+    recs[i].vcodes = dv.base + dv.off_codes;
+    recs[i].vscales = dv.base + dv.off_scales;
+    recs[i].vlabels = dv.base + dv.off_labels;
+    recs[i].vcent = dv.base + dv.off_centroids;
     recs[i].token_start = Nk;
     recs[i].n = (int32_t)n;
     recs[i].tile_start = (int32_t)n_tiles;
     Nk += n;
     n_tiles += (n + kTileKeys - 1) / kTileKeys;
-    max_n = std::max(max_n, n);
   }
   if (Nk > ((int64_t)1 << 31) - 1) return fail(QKV_EINVAL, "%s: the cache holds more than 2^31 tokens", fn);
   if (causal && Nk != Nq) return fail(QKV_EINVAL, "%s: causal attention needs as many queries as cached keys", fn);
-  // Splits are planned from (max chunk size, n_chunks) so that a workspace sized
-  // by qkv_workspace_bytes with those bounds always suffices.
-  const int ns_plan = choose_splits(H, Nq, max_tiles(max_n, n_chunks));
+  // A workspace sized by qkv_workspace_bytes for at least these queries and
+  // chunks always suffices: ns <= split_cap(H, Nq).
   const int ns = choose_splits(H, Nq, n_tiles);
-  const AttendWs ws = attend_ws(H, Nq, n_chunks, std::max(ns, ns_plan));
+  const AttendWs ws = attend_ws(H, Nq, n_chunks, n_tiles, ns > 1 ? (int64_t)ns * Nq : 0);
   QKV_TRY(check_ws(workspace, workspace_bytes, ws.bytes, fn));
 
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
@@ -415,6 +457,8 @@ int qkv_attend(const qkv_config* k_cfg, const qkv_config* v_cfg, const qkv_tenso
     for (int i = 0; i < b.count; ++i) b.rec[i] = recs[first + i];
     QKV_HIP(launch_upload_chunks(b, drecs, s));
   }
+  TileInfo* dtiles = reinterpret_cast<TileInfo*>(at(workspace, ws.tiles));
+  QKV_HIP(launch_tile_table(drecs, n_chunks, (int)n_tiles, dtiles, s));
 
   AttendArgs a;
   a.q = view_of(q);
@@ -426,6 +470,7 @@ int qkv_attend(const qkv_config* k_cfg, const qkv_config* v_cfg, const qkv_tenso
   a.kp = params_of(k_cfg);
   a.vp = params_of(v_cfg);
   a.chunks = drecs;
+  a.tiles = dtiles;
   a.U = U;
   a.psac_rank = k_cfg->psac_rank;
   a.qu = reinterpret_cast<float*>(at(workspace, ws.qu));
