@@ -20,6 +20,9 @@
 // V_hat and the probabilities enter P V in bf16 with fp32 accumulation.  The
 // PSAC term rides one extra MFMA k-step: [coef | coef] against
 // [hi(qU) | lo(qU)].  Splits are merged with the usual log-sum-exp rescaling.
+#include <cstddef>
+#include <utility>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -29,7 +32,7 @@ namespace {
 
 constexpr int kKTile = 64;      // keys per tile
 constexpr int kKPitch = 136;    // bf16 pitch of the K_hat rows in LDS
-constexpr int kVPitch = 68;     // bf16 pitch of the V_hat^T rows in LDS (34 dwords)
+constexpr int kVPitch = 66;     // fp16 pitch of the V_hat^T rows in LDS (33 dwords: odd, for conflict-free writes)
 constexpr float kLog2e = 1.4426950408889634f;
 
 __device__ __forceinline__ const uint8_t* sp(const ChunkDecode& d, uint64_t off, uint64_t stride, int l) {
@@ -98,7 +101,7 @@ constexpr int kBM = kWaves * 32;          // queries per workgroup, 32 per wave
 constexpr int kThreads = kWaves * 64;
 constexpr int kItems = 1024 / kThreads;   // K (and V) decode items per thread per tile
 constexpr int kRing = 3;                  // raw-tile slots in LDS
-constexpr int kVCentPitch = 136;          // u16 pitch of a gathered V centroid row (272 bytes)
+constexpr int kMetaSlots = 6;             // tile-record slots in LDS
 constexpr float kF16Max = 65504.0f;
 static_assert(kBM == kAttendQueries, "queries per workgroup");
 
@@ -161,24 +164,26 @@ __device__ __forceinline__ void dma(const void* src, void* dst) {
 __device__ __forceinline__ void wait_dma() { __builtin_amdgcn_s_waitcnt(0x0F70); }   // vmcnt(0)
 
 typedef const __attribute__((address_space(4))) ChunkRec* crec_ptr;
-typedef const __attribute__((address_space(4))) TileInfo* ctile_ptr;
+typedef const __attribute__((address_space(4))) TileRec* ctile_ptr;
 typedef const __attribute__((address_space(4))) AttendArgs* cargs_ptr;
 
-struct __attribute__((aligned(16))) AttendSmem {
-  uint16_t K[2][kKTile][kKPitch];              // fp16 K_hat rows
-  uint16_t Vt[2][kHeadDim][kVPitch];           // fp16 V_hat^T rows
-  uint16_t Kp[2][kKTile][16];                  // fp16 [coef | coef]
-  uint16_t centK[2][kKTile * kHeadDim];        // gathered K centroid rows (bf16)
-  uint16_t centV[2][kKTile * kVCentPitch];     // gathered V centroid rows (bf16, padded)
-  uint32_t rc[kRing][2][kKTile * 8];           // [slot][K/V] code words
-  uint16_t rs[kRing][2][kKTile * 4];           // [slot][K/V] scales
-  uint8_t rl[kRing][2][kKTile];                // [slot][K/V] labels
-  ChannelCode tabK[kHeadDim], tabV[kHeadDim];  // generic decode tables
-};
 
-template <bool QF32, bool KFAST, bool VFAST, bool LOGITS>
+template <bool QF32, bool KFAST, bool VFAST, bool LOGITS, bool PSAC>
 __global__ __launch_bounds__(kThreads) void k_attend(AttendArgs a) {
-  __shared__ AttendSmem sm;
+  // Separate LDS objects: the compiler waits for outstanding asynchronous
+  // copies before an LDS read only when the read may touch a copy target, so
+  // the MFMA operands (K, Vt, Kp) live apart from the copy targets (ring and
+  // centroid staging), and the labels (written by plain stores) apart again.
+  __shared__ __attribute__((aligned(16))) uint16_t sK[2][kKTile][kKPitch];         // fp16 K_hat rows
+  __shared__ __attribute__((aligned(16))) uint16_t sVt[2][kHeadDim][kVPitch];      // fp16 V_hat^T rows
+  __shared__ __attribute__((aligned(16))) uint16_t sKp[2][kKTile][16];             // fp16 [coef | coef]
+  __shared__ __attribute__((aligned(16))) uint16_t sCentK[2][kKTile * kHeadDim];   // gathered K centroid rows
+  __shared__ __attribute__((aligned(16))) uint16_t sCentV[2][kKTile * kHeadDim];   // gathered V centroid rows
+  __shared__ __attribute__((aligned(16))) uint32_t sRc[kRing][2][kKTile * 8];      // [slot][K/V] code words
+  __shared__ __attribute__((aligned(16))) uint16_t sRs[kRing][2][kKTile * 4 + 8];  // [slot][K/V] scales (+ lead)
+  __shared__ __attribute__((aligned(16))) uint8_t sRl[kRing][2][kKTile + 16];      // [slot][K/V] labels (+ lead)
+  __shared__ ChannelCode sTabK[kHeadDim], sTabV[kHeadDim];                         // generic decode tables
+  __shared__ __attribute__((aligned(16))) uint32_t sMeta[kMetaSlots][sizeof(TileRec) / 4];   // tile records
 
   const int q_tiles = (a.Nq + kBM - 1) / kBM;
   const uint32_t total = (uint32_t)(q_tiles * a.n_split * a.H);
@@ -196,7 +201,6 @@ __global__ __launch_bounds__(kThreads) void k_attend(AttendArgs a) {
   const int wq_first = qt * kBM + wave * 32;   // this wave's queries
   const int wq_last = min(a.Nq, wq_first + 32) - 1;
   const bool wave_active = wq_first < a.Nq;
-  const bool psac = a.psac_rank > 0;
   const int qrow = wq_first + col;             // this lane's query
   const bool qok = qrow < a.Nq;
 
@@ -239,7 +243,7 @@ __global__ __launch_bounds__(kThreads) void k_attend(AttendArgs a) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       float v = 0.0f;
-      if (psac && qok && e < a.psac_rank)
+      if (PSAC && qok && e < a.psac_rank)
         v = __builtin_amdgcn_fmed3f(a.qu[((int64_t)h * a.Nq + qrow) * kMaxRank + e], -kF16Max, kF16Max);
       const _Float16 hv = (_Float16)v;
       qpsac[e] = half == 0 ? hv : (_Float16)(v - (float)hv);
@@ -258,28 +262,12 @@ __global__ __launch_bounds__(kThreads) void k_attend(AttendArgs a) {
   // Tile and chunk records are read-only here: scalar loads through the
   // constant address space keep them out of the vector-memory counter, which
   // the asynchronous copies below are waited on with.
-  // The arguments themselves are re-read through the kernel-argument segment at
-  // every pipeline step (A is made opaque there): holding them all in scalar
-  // registers across the loop would spill them.
-  cargs_ptr A = (cargs_ptr)__builtin_amdgcn_kernarg_segment_ptr();
-  crec_ptr recs = (crec_ptr)A->chunks;
-  ctile_ptr tiles = (ctile_ptr)A->tiles;
-  struct TileRef {
-    int chunk, token0, nvalid, kstart, n;
-  };
-  auto tile_ref = [&](int j) __attribute__((always_inline)) -> TileRef {
-    TileRef t;
-    t.chunk = tiles[j].chunk;
-    t.token0 = tiles[j].token0;
-    t.n = recs[t.chunk].n;
-    t.nvalid = min(kKTile, t.n - t.token0);
-    t.kstart = (int)recs[t.chunk].token_start + t.token0;
-    return t;
-  };
+  const crec_ptr recs = (crec_ptr)a.chunks;
+  const ctile_ptr tiles = (ctile_ptr)a.tiles;
 
   // causal: drop trailing tiles wholly above the diagonal (unless debug logits are requested)
   if (a.causal && !LOGITS) {
-    while (t_end > t_begin && tile_ref(t_end - 1).kstart > q_last) --t_end;
+    while (t_end > t_begin && tiles[t_end - 1].kstart > q_last) --t_end;
   }
   if (t_begin >= t_end) {
     // nothing visible in this split: write an empty partial
@@ -306,108 +294,164 @@ __global__ __launch_bounds__(kThreads) void k_attend(AttendArgs a) {
   // on i.  Waves 0-3 compute before they decode, waves 4-7 decode before they
   // compute, so the two waves sharing a SIMD overlap MFMA and VALU work.
   //
-  // Per-thread indexes used inside the steps come from xtid, which is made
-  // opaque at every step so that the addresses derived from it are recomputed
-  // there instead of being held in registers across the whole loop.
-  int xtid = tid;
+  // Per-thread and per-wave indexes used inside the steps come from xtid and
+  // xwave, which are made opaque at every step so that the addresses derived
+  // from them are recomputed there instead of being held in registers across
+  // the whole loop.
+  int xtid = tid, xwave = wave;
   auto geom = [&](int cc, bool v) __attribute__((always_inline)) -> ChunkDecode {
-    LayoutParams p;
-    p.H = v ? A->vp.H : A->kp.H;
-    p.C = v ? A->vp.C : A->kp.C;
-    p.n_stages = v ? A->vp.n_stages : A->kp.n_stages;
-    p.bits = v ? A->vp.bits : A->kp.bits;
-    p.group = v ? A->vp.group : A->kp.group;
-    p.n_int4 = v ? A->vp.n_int4 : A->kp.n_int4;
-    p.psac_rank = v ? A->vp.psac_rank : A->kp.psac_rank;
-    return make_decode(p, recs[cc].n, v ? recs[cc].vbase : recs[cc].kbase);
+    return make_decode(v ? a.vp : a.kp, recs[cc].n, v ? recs[cc].vbase : recs[cc].kbase);
   };
-  const int kG = kHeadDim / A->kp.group, vG = kHeadDim / A->vp.group;   // scale groups per token (fast paths)
+  const int kG = kHeadDim / a.kp.group, vG = kHeadDim / a.vp.group;   // scale groups per token (fast paths)
+  const int kGs = __builtin_ctz(kG), vGs = __builtin_ctz(vG);
+  const int kC = a.kp.C, vC = a.vp.C;
 
-  // (1) raw copy of tile j into ring slot r: waves 0-3 copy K, waves 4-7 V.
-  // Code words and 4-byte scale runs go by asynchronous copy; labels (and
-  // 2-byte scales, one group per token) by plain loads into `held`, written to
-  // the ring by raw_finish at the end of the step.
-  uint32_t held = 0;
-  auto raw_copy = [&](int j, int r) __attribute__((always_inline)) {
+  // Tile records travel into an LDS ring (sMeta, kMetaSlots tiles) by
+  // asynchronous copy five tiles ahead of their first use, so that a step
+  // reads them from LDS instead of taking scalar-cache misses.  A step reads
+  // the fields it needs at its start into small views; the view of a tile past
+  // the end of the split has nvalid = 0.  Scale and label runs of a head need
+  // not start on a 4-byte boundary: they are copied from the boundary below
+  // and sit `lead` bytes into their LDS slot.
+  constexpr int kRecWords = (int)(sizeof(TileRec) / 4);
+  constexpr int kFSrc = 0, kFCent = 12, kFPsac = 16, kFN = 18, kFNvalid = 19, kFKstart = 20;
+  static_assert(offsetof(TileRec, cent) == 4 * kFCent && offsetof(TileRec, kpsac) == 4 * kFPsac &&
+                offsetof(TileRec, n) == 4 * kFN && offsetof(TileRec, nvalid) == 4 * kFNvalid &&
+                offsetof(TileRec, kstart) == 4 * kFKstart, "TileRec field offsets");
+  auto meta_copy = [&](int j) __attribute__((always_inline)) {   // wave 0 only
     const int lane = xtid & 63;
-    const int v = wave >> 2, part = wave & 3;
-    if ((v == 0 && !KFAST) || (v == 1 && !VFAST)) return;
-    const TileRef t = tile_ref(j);
-    const int64_t row0 = (int64_t)h * t.n + t.token0;
-    if (part < 2) {                              // code words: 32 bytes per key
-      const int key = part * 32 + (lane >> 1);
-      const uint8_t* src = v ? recs[t.chunk].vcodes : recs[t.chunk].kcodes;
-      if (key < t.nvalid) dma<16>(src + (row0 * 32 + part * 1024 + lane * 16), &sm.rc[r][v][part * 256]);
-    } else if (part == 2) {                      // scales: 2 * G bytes per key
-      const int G = v ? vG : kG;
-      const uint8_t* src = (v ? recs[t.chunk].vscales : recs[t.chunk].kscales) + row0 * G * 2;
-      if (G == 1) {
-        held = lane < t.nvalid ? reinterpret_cast<const uint16_t*>(src)[lane] : 0u;
-      } else {                                   // row0 * 2G is a multiple of 4
-        const int per = 2 * G;
+    if (lane < kRecWords)
+      dma<4>(reinterpret_cast<const uint8_t*>(a.tiles + j) + lane * 4, &sMeta[j % kMetaSlots][0]);
+  };
+  auto m32 = [&](int j, int k) __attribute__((always_inline)) -> uint32_t {
+    return (uint32_t)__builtin_amdgcn_readfirstlane((int)sMeta[j % kMetaSlots][k]);
+  };
+  auto m64 = [&](int j, int k) __attribute__((always_inline)) -> const uint8_t* {
+    return reinterpret_cast<const uint8_t*>(((uint64_t)m32(j, k + 1) << 32) | m32(j, k));
+  };
+  auto lead_of = [](uint32_t addr_lo) __attribute__((always_inline)) -> int { return (int)(addr_lo & 3); };
+  // raw copy role of this wave: tensor rv, part rpart (code words by parts
+  // 0 and 1, scales by part 2, labels by part 3); rshift = log2 bytes per token
+  struct RawRole {
+    int rv, rpart, rsel, rshift;
+  };
+  auto raw_role = [&]() __attribute__((always_inline)) -> RawRole {
+    RawRole q;
+    q.rv = xwave >> 2;
+    q.rpart = xwave & 3;
+    q.rsel = q.rpart < 2 ? 0 : q.rpart - 1;
+    q.rshift = q.rsel == 0 ? 5 : q.rsel == 1 ? (q.rv ? vGs : kGs) + 1 : 0;
+    return q;
+  };
+  struct RawView {                               // tile i+3: this wave's run
+    const uint8_t* src;
+    int nvalid;
+  };
+  struct GatherView {                            // tile i+2
+    const uint8_t* cent[2];
+    int lead[2], nvalid;
+  };
+  struct DecodeView {                            // tile i+1
+    int lead[2], nvalid;                         // lead in scales (2 bytes)
+  };
+  auto raw_view = [&](int j, bool live) __attribute__((always_inline)) -> RawView {
+    const RawRole q = raw_role();
+    RawView w;
+    const int64_t hrow = (int64_t)h * (int)m32(j, kFN);
+    w.src = m64(j, kFSrc + (q.rv * 3 + q.rsel) * 2) + (hrow << q.rshift) + (q.rpart == 1 ? 1024 : 0);
+    w.nvalid = live ? (int)m32(j, kFNvalid) : 0;
+    return w;
+  };
+  auto gather_view = [&](int j, bool live) __attribute__((always_inline)) -> GatherView {
+    GatherView w;
+    const uint32_t hrow = (uint32_t)h * m32(j, kFN);
+    w.cent[0] = m64(j, kFCent) + (int64_t)h * kC * kHeadDim * 2;
+    w.cent[1] = m64(j, kFCent + 2) + (int64_t)h * vC * kHeadDim * 2;
+    w.lead[0] = lead_of(m32(j, kFSrc + 4) + hrow);         // src[0][2]: K labels
+    w.lead[1] = lead_of(m32(j, kFSrc + 10) + hrow);        // src[1][2]: V labels
+    w.nvalid = live ? (int)m32(j, kFNvalid) : 0;
+    return w;
+  };
+  auto decode_view = [&](int j, bool live) __attribute__((always_inline)) -> DecodeView {
+    DecodeView w;
+    const uint32_t hrow = (uint32_t)h * m32(j, kFN);
+    w.lead[0] = lead_of(m32(j, kFSrc + 2) + (hrow << (kGs + 1))) >> 1;   // src[0][1]: K scales
+    w.lead[1] = lead_of(m32(j, kFSrc + 8) + (hrow << (vGs + 1))) >> 1;   // src[1][1]: V scales
+    w.nvalid = live ? (int)m32(j, kFNvalid) : 0;
+    return w;
+  };
+
+  // (1) raw copy into ring slot r: waves 0-3 copy K, waves 4-7 V (code words
+  // by two waves, scales and labels by one each), all by asynchronous 16- or
+  // 4-byte copies.
+  auto raw_copy = [&](const RawView& R, int r) __attribute__((always_inline)) {
+    const int lane = xtid & 63;
+    const RawRole q = raw_role();
+    const int rv = q.rv, rpart = q.rpart, rsel = q.rsel, rshift = q.rshift;
+    if ((rv == 0 && !KFAST) || (rv == 1 && !VFAST)) return;
+    if (rsel == 0) {                             // code words: 32 bytes per key
+      const int key = rpart * 32 + (lane >> 1);
+      if (key < R.nvalid) dma<16>(R.src + lane * 16, &sRc[r][rv][rpart * 256]);
+    } else {                                     // scales (2G bytes per key) or labels (1 byte per key)
+      const int lead = lead_of((uint32_t)reinterpret_cast<uintptr_t>(R.src));
+      const uint8_t* base = R.src - lead;
+      const int words = (lead + (R.nvalid << rshift) + 3) >> 2;
 #pragma unroll
-        for (int x = 0; x < 2; ++x) {
-          const int off = x * 256 + lane * 4;
-          if (x * 256 < kKTile * per && off / per < t.nvalid) dma<4>(src + off, &sm.rs[r][v][x * 128]);
+      for (int x = 0; x < 3; ++x) {              // at most 3 + 512 bytes: 129 words
+        const int wd = x * 64 + lane;
+        if (x * 64 < words && wd < words) {
+          if (rsel == 1) dma<4>(base + wd * 4, &sRs[r][rv][x * 128]);
+          else dma<4>(base + wd * 4, &sRl[r][rv][x * 256]);
         }
       }
-    } else {                                     // labels: 1 byte per key
-      const uint8_t* src = v ? recs[t.chunk].vlabels : recs[t.chunk].klabels;
-      held = lane < t.nvalid ? (uint32_t)src[row0 + lane] : 0u;
     }
   };
-  auto raw_finish = [&](int r) __attribute__((always_inline)) {
+  // (2) centroid gather (labels in ring slot r) into staging slot g: per
+  // tensor 16 copies of 4 rows, two per wave; the labels are read first.
+  auto cent_gather = [&](const GatherView& G, int r, int g) __attribute__((always_inline)) {
     const int lane = xtid & 63;
-    const int v = wave >> 2, part = wave & 3;
-    if ((v == 0 && !KFAST) || (v == 1 && !VFAST)) return;
-    if (part == 3) sm.rl[r][v][lane] = (uint8_t)held;
-    else if (part == 2 && (v ? vG : kG) == 1) sm.rs[r][v][lane] = (uint16_t)held;
-  };
-  // (2) centroid gather of tile j (labels in ring slot r) into staging slot g
-  auto cent_gather = [&](int j, int r, int g) __attribute__((always_inline)) {
-    const int lane = xtid & 63;
-    const TileRef t = tile_ref(j);
-    if constexpr (KFAST) {                       // 16 copies of 4 rows; two per wave
-      const uint16_t* cent = reinterpret_cast<const uint16_t*>(recs[t.chunk].kcent) + (int64_t)h * A->kp.C * kHeadDim;
+    int lab[2][2];
+#pragma unroll
+    for (int v = 0; v < 2; ++v)
+#pragma unroll
+      for (int x = 0; x < 2; ++x) lab[v][x] = sRl[r][v][G.lead[v] + (xwave * 2 + x) * 4 + (lane >> 4)];
+#pragma unroll
+    for (int v = 0; v < 2; ++v) {
+      if ((v == 0 && !KFAST) || (v == 1 && !VFAST)) continue;
+      const uint16_t* cent = reinterpret_cast<const uint16_t*>(G.cent[v]);
+      const int C = v ? vC : kC;
 #pragma unroll
       for (int x = 0; x < 2; ++x) {
-        const int n = wave * 2 + x;
-        const int key = n * 4 + (lane >> 4);
-        const int lab = min((int)sm.rl[r][0][key], A->kp.C - 1);
-        if (key < t.nvalid) dma<16>(cent + lab * kHeadDim + (lane & 15) * 8, &sm.centK[g][n * 4 * kHeadDim]);
-      }
-    }
-    if constexpr (VFAST) {                       // 64 copies of one row; eight per wave
-      const uint16_t* cent = reinterpret_cast<const uint16_t*>(recs[t.chunk].vcent) + (int64_t)h * A->vp.C * kHeadDim;
-#pragma unroll
-      for (int x = 0; x < 8; ++x) {
-        const int key = wave * 8 + x;
-        const int lab = min((int)sm.rl[r][1][key], A->vp.C - 1);
-        if (key < t.nvalid && lane < 16) dma<16>(cent + lab * kHeadDim + lane * 8, &sm.centV[g][key * kVCentPitch]);
+        const int n = xwave * 2 + x;
+        if (n * 4 + (lane >> 4) < G.nvalid)
+          dma<16>(cent + min(lab[v][x], C - 1) * kHeadDim + (lane & 15) * 8,
+                  v ? &sCentV[g][n * 4 * kHeadDim] : &sCentK[g][n * 4 * kHeadDim]);
       }
     }
   };
   // (3) decode tile j (ring slot r, staging slot g) into LDS buffer b
-  auto decode_tile = [&](int j, int r, int g, int b) __attribute__((always_inline)) {
+  auto decode_tile = [&](const DecodeView& D, int j, int r, int g, int b) __attribute__((always_inline)) {
     const int tid = xtid;
-    const TileRef t = tile_ref(j);
+    const int nvalid = D.nvalid;
+    const int klead = D.lead[0], vlead = D.lead[1];
 #pragma unroll
     for (int x = 0; x < kItems; ++x) {          // K: (key, 8 channels) per item
       const int item = tid + x * kThreads;
       const int key = item >> 4, k0 = (item & 15) * 8;
-      const bool ok = key < t.nvalid;
+      const bool ok = key < nvalid;
       uint32_t o4[4];
       if constexpr (KFAST) {
-        const uint32_t w = sm.rc[r][0][key * 8 + (k0 >> 4)];
-        const uint32_t sb = sm.rs[r][0][key * kG + k0 * kG / kHeadDim];
-        const uint4 cr = *reinterpret_cast<const uint4*>(&sm.centK[g][key * kHeadDim + k0]);
-        const uint32_t code16 = ok ? (w >> (16 * ((k0 >> 3) & 1))) & 0xFFFFu : 0xAAAAu;   // code 2 -> 0
-        const float S = ok ? bf16_bits_to_f32(sb) : 0.0f;
-        const uint32_t cw[4] = {ok ? cr.x : 0u, ok ? cr.y : 0u, ok ? cr.z : 0u, ok ? cr.w : 0u};
-        decode_pairs_f16<4>(code16 | (code16 << 14), S, cw, o4);
+        const uint32_t w = sRc[r][0][key * 8 + (k0 >> 4)];
+        const uint32_t sb = sRs[r][0][klead + key * kG + k0 * kG / kHeadDim];
+        const uint4 cr = *reinterpret_cast<const uint4*>(&sCentK[g][key * kHeadDim + k0]);
+        // keys past nvalid decode stale LDS contents: the saturation keeps
+        // them finite, and their scores are masked (probability 0)
+        const uint32_t code16 = (w >> (16 * ((k0 >> 3) & 1))) & 0xFFFFu;
+        const uint32_t cw[4] = {cr.x, cr.y, cr.z, cr.w};
+        decode_pairs_f16<4>(code16 | (code16 << 14), bf16_bits_to_f32(sb), cw, o4);
       } else {
         float v[8];
-        if (ok) decode_generic<8>(geom(t.chunk, false), sm.tabK, h, t.token0 + key, k0, v);
+        if (ok) decode_generic<8>(geom(tiles[j].chunk, false), sTabK, h, tiles[j].token0 + key, k0, v);
         else {
 #pragma unroll
           for (int e = 0; e < 8; ++e) v[e] = 0.0f;
@@ -415,28 +459,27 @@ __global__ __launch_bounds__(kThreads) void k_attend(AttendArgs a) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) o4[e] = pack_f16x2(v[2 * e], v[2 * e + 1]);
       }
-      *reinterpret_cast<uint4*>(&sm.K[b][key][k0]) = make_uint4(o4[0], o4[1], o4[2], o4[3]);
+      *reinterpret_cast<uint4*>(&sK[b][key][k0]) = make_uint4(o4[0], o4[1], o4[2], o4[3]);
     }
 #pragma unroll
-    for (int x = 0; x < kItems; ++x) {          // V: (2 keys, 4 channels) per item
+    for (int x = 0; x < kItems; ++x) {          // V: (2 keys, 4 channels) per item, channels fastest
       const int item = tid + x * kThreads;
-      const int kp = item & 31, k0 = (item >> 5) * 4;
+      const int k0 = (item & 31) * 4, kp = item >> 5;
       uint32_t pr[2][2];                         // [key][channel pair] fp16 pairs
 #pragma unroll
       for (int y = 0; y < 2; ++y) {
         const int key = 2 * kp + y;
-        const bool ok = key < t.nvalid;
+        const bool ok = key < nvalid;
         if constexpr (VFAST) {
-          const uint32_t w = sm.rc[r][1][key * 8 + (k0 >> 4)];
-          const uint32_t sb = sm.rs[r][1][key * vG + k0 * vG / kHeadDim];
-          const uint2 cr = *reinterpret_cast<const uint2*>(&sm.centV[g][key * kVCentPitch + k0]);
-          const uint32_t code8 = ok ? (w >> (2 * (k0 & 15))) & 0xFFu : 0xAAu;
-          const float S = ok ? bf16_bits_to_f32(sb) : 0.0f;
-          const uint32_t cw[2] = {ok ? cr.x : 0u, ok ? cr.y : 0u};
-          decode_pairs_f16<2>(code8 | (code8 << 14), S, cw, pr[y]);
+          const uint32_t w = sRc[r][1][key * 8 + (k0 >> 4)];
+          const uint32_t sb = sRs[r][1][vlead + key * vG + k0 * vG / kHeadDim];
+          const uint2 cr = *reinterpret_cast<const uint2*>(&sCentV[g][key * kHeadDim + k0]);
+          const uint32_t code8 = (w >> (2 * (k0 & 15))) & 0xFFu;   // keys past nvalid: finite, weight 0
+          const uint32_t cw[2] = {cr.x, cr.y};
+          decode_pairs_f16<2>(code8 | (code8 << 14), bf16_bits_to_f32(sb), cw, pr[y]);
         } else {
           float v[4];
-          if (ok) decode_generic<4>(geom(t.chunk, true), sm.tabV, h, t.token0 + key, k0, v);
+          if (ok) decode_generic<4>(geom(tiles[j].chunk, true), sTabV, h, tiles[j].token0 + key, k0, v);
           else {
 #pragma unroll
             for (int e = 0; e < 4; ++e) v[e] = 0.0f;
@@ -448,32 +491,31 @@ __global__ __launch_bounds__(kThreads) void k_attend(AttendArgs a) {
       // channel k0 + e gets (key 2kp, key 2kp + 1)
 #pragma unroll
       for (int jj = 0; jj < 2; ++jj) {
-        *reinterpret_cast<uint32_t*>(&sm.Vt[b][k0 + 2 * jj][2 * kp]) = __builtin_amdgcn_perm(pr[1][jj], pr[0][jj], 0x05040100u);
-        *reinterpret_cast<uint32_t*>(&sm.Vt[b][k0 + 2 * jj + 1][2 * kp]) = __builtin_amdgcn_perm(pr[1][jj], pr[0][jj], 0x07060302u);
+        *reinterpret_cast<uint32_t*>(&sVt[b][k0 + 2 * jj][2 * kp]) = __builtin_amdgcn_perm(pr[1][jj], pr[0][jj], 0x05040100u);
+        *reinterpret_cast<uint32_t*>(&sVt[b][k0 + 2 * jj + 1][2 * kp]) = __builtin_amdgcn_perm(pr[1][jj], pr[0][jj], 0x07060302u);
       }
     }
-    if (psac && tid < kKTile) {
+    if (PSAC && tid < kKTile) {
       uint32_t f16w[4] = {0u, 0u, 0u, 0u};
-      if (tid < t.nvalid) {
-        const int rank = A->psac_rank;
-        const uint16_t* cpp = reinterpret_cast<const uint16_t*>(recs[t.chunk].kpsac) + ((int64_t)h * t.n + t.token0 + tid) * rank;
+      if (tid < nvalid) {
+        const int rank = a.psac_rank;
+        const uint16_t* cpp = reinterpret_cast<const uint16_t*>(m64(j, kFPsac)) + ((int64_t)h * (int)m32(j, kFN) + tid) * rank;
         float f[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) f[e] = e < rank ? bf16_bits_to_f32(cpp[e]) : 0.0f;
 #pragma unroll
         for (int e = 0; e < 4; ++e) f16w[e] = pack_f16x2(f[2 * e], f[2 * e + 1]);
       }
-      *reinterpret_cast<uint4*>(&sm.Kp[b][tid][0]) = make_uint4(f16w[0], f16w[1], f16w[2], f16w[3]);
-      *reinterpret_cast<uint4*>(&sm.Kp[b][tid][8]) = make_uint4(f16w[0], f16w[1], f16w[2], f16w[3]);
+      *reinterpret_cast<uint4*>(&sKp[b][tid][0]) = make_uint4(f16w[0], f16w[1], f16w[2], f16w[3]);
+      *reinterpret_cast<uint4*>(&sKp[b][tid][8]) = make_uint4(f16w[0], f16w[1], f16w[2], f16w[3]);
     }
   };
   // (4) this wave's 32 queries against tile j in LDS buffer b
-  auto compute_tile = [&](int j, int b) __attribute__((always_inline)) {
+  auto compute_tile = [&](int nvalid, int kstart, int b) __attribute__((always_inline)) {
     const int lane = xtid & 63, col = lane & 31, half = lane >> 5;
     if (!wave_active) return;
-    const TileRef t = tile_ref(j);
-    if (A->causal && !LOGITS && t.kstart > wq_last) return;      // wholly above the diagonal
-    const bool need_mask = t.nvalid < kKTile || (A->causal && t.kstart + kKTile - 1 > wq_first);
+    if (a.causal && !LOGITS && kstart > wq_last) return;        // wholly above the diagonal
+    const bool need_mask = nvalid < kKTile || (a.causal && kstart + kKTile - 1 > wq_first);
     // S^T = K_hat Q^T, both 32-key halves interleaved (fp16 operands, fp32 accumulation)
     f32x16 acc[2] = {f32x16{}, f32x16{}};
 #pragma unroll
@@ -481,17 +523,17 @@ __global__ __launch_bounds__(kThreads) void k_attend(AttendArgs a) {
       f16x8 kf[2];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
-        kf[kb] = __builtin_bit_cast(f16x8, *reinterpret_cast<const uint4*>(&sm.K[b][kb * 32 + col][s * 16 + half * 8]));
+        kf[kb] = __builtin_bit_cast(f16x8, *reinterpret_cast<const uint4*>(&sK[b][kb * 32 + col][s * 16 + half * 8]));
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         acc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf[kb], qh[s], acc[kb], 0, 0, 0);
         if constexpr (QF32) acc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf[kb], ql[QF32 ? s : 0], acc[kb], 0, 0, 0);
       }
     }
-    if (psac) {
+    if constexpr (PSAC) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        const f16x8 kpf = __builtin_bit_cast(f16x8, *reinterpret_cast<const uint4*>(&sm.Kp[b][kb * 32 + col][half * 8]));
+        const f16x8 kpf = __builtin_bit_cast(f16x8, *reinterpret_cast<const uint4*>(&sKp[b][kb * 32 + col][half * 8]));
         acc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kpf, qpsac, acc[kb], 0, 0, 0);
       }
     }
@@ -504,17 +546,18 @@ __global__ __launch_bounds__(kThreads) void k_attend(AttendArgs a) {
       // key kl of element i is kc(i) + half*4; it is visible iff kl < nvalid and
       // (causal) kstart + kl <= qrow, i.e. iff kc(i) < lim.  The select is done
       // with integer bit operations, not per-element compare masks.
-      int lim = t.nvalid;
-      if (A->causal) lim = min(lim, qrow - t.kstart + 1);
+      int lim = nvalid;
+      if (a.causal) lim = min(lim, qrow - kstart + 1);
       lim -= half * 4;
 #pragma unroll
       for (int i = 0; i < 32; ++i) {
         const int kc = (i >> 4) * 32 + ((i & 15) >> 2) * 8 + (i & 3);
-        const uint32_t masked = (uint32_t)((lim - 1 - kc) >> 31);   // all ones when hidden
+        uint32_t masked;                                          // all ones when hidden
+        asm("v_ashrrev_i32 %0, 31, %1" : "=v"(masked) : "v"(lim - 1 - kc));   // kept arithmetic (no compare mask)
         if (LOGITS) {
           const int kl = kc + half * 4;
-          if (qok && kl < t.nvalid)
-            A->logits[((int64_t)h * A->Nq + qrow) * A->Nk + (int64_t)(t.kstart + kl)] = masked ? -INFINITY : sv[i] * A->scale;
+          if (qok && kl < nvalid)
+            a.logits[((int64_t)h * a.Nq + qrow) * a.Nk + (int64_t)(kstart + kl)] = masked ? -INFINITY : sv[i] * a.scale;
         }
         sv[i] = __uint_as_float((__float_as_uint(sv[i]) & ~masked) | (0xFF800000u & masked));
       }
@@ -558,9 +601,8 @@ __global__ __launch_bounds__(kThreads) void k_attend(AttendArgs a) {
 #pragma unroll
       for (int db = 0; db < 4; ++db) {
         const int drow = db * 32 + col;
-        const uint2 v0 = *reinterpret_cast<const uint2*>(&sm.Vt[b][drow][kbase]);
-        const uint2 v1 = *reinterpret_cast<const uint2*>(&sm.Vt[b][drow][kbase + 8]);
-        vf[db] = __builtin_bit_cast(f16x8, make_uint4(v0.x, v0.y, v1.x, v1.y));
+        const uint32_t* vrow = reinterpret_cast<const uint32_t*>(&sVt[b][drow][kbase]);   // 4-byte aligned
+        vf[db] = __builtin_bit_cast(f16x8, make_uint4(vrow[0], vrow[1], vrow[4], vrow[5]));
       }
       const f16x8 pfrag = __builtin_bit_cast(f16x8, make_uint4(pw[st][0], pw[st][1], pw[st][2], pw[st][3]));
 #pragma unroll
@@ -574,8 +616,8 @@ __global__ __launch_bounds__(kThreads) void k_attend(AttendArgs a) {
       const int chunk = tiles[j].chunk;
       if (chunk != gen_chunk) {
         __syncthreads();
-        if constexpr (!KFAST) build_tab(geom(chunk, false), h, sm.tabK);
-        if constexpr (!VFAST) build_tab(geom(chunk, true), h, sm.tabV);
+        if constexpr (!KFAST) build_tab(geom(chunk, false), h, sTabK);
+        if constexpr (!VFAST) build_tab(geom(chunk, true), h, sTabV);
         __syncthreads();
         gen_chunk = chunk;
       }
@@ -584,53 +626,108 @@ __global__ __launch_bounds__(kThreads) void k_attend(AttendArgs a) {
 
   // ---- prologue: tiles t_begin .. t_begin+2 raw, t_begin .. t_begin+1 gathered, t_begin decoded ----
   const int r0 = t_begin % kRing;
+  if (xwave == 0) {
 #pragma unroll 1
-  for (int k = 0; k < 3 && t_begin + k < t_end; ++k) {
-    raw_copy(t_begin + k, (r0 + k) % kRing);
-    raw_finish((r0 + k) % kRing);
+    for (int k = 0; k < 5 && t_begin + k < t_end; ++k) meta_copy(t_begin + k);
   }
   wait_dma();
   __syncthreads();
-  cent_gather(t_begin, r0, t_begin & 1);
-  if (t_begin + 1 < t_end) cent_gather(t_begin + 1, (r0 + 1) % kRing, (t_begin + 1) & 1);
+#pragma unroll 1
+  for (int k = 0; k < 3 && t_begin + k < t_end; ++k) raw_copy(raw_view(t_begin + k, true), (r0 + k) % kRing);
+  wait_dma();
+  __syncthreads();
+  cent_gather(gather_view(t_begin, true), r0, t_begin & 1);
+  if (t_begin + 1 < t_end) cent_gather(gather_view(t_begin + 1, true), (r0 + 1) % kRing, (t_begin + 1) & 1);
   wait_dma();
   __syncthreads();
   tables_for(t_begin);
-  decode_tile(t_begin, r0, t_begin & 1, t_begin & 1);
+  decode_tile(decode_view(t_begin, true), t_begin, r0, t_begin & 1, t_begin & 1);
   __syncthreads();
 
   int ring = r0;                                 // ring slot of tile ti
 #pragma unroll 1
   for (int ti = t_begin; ti < t_end; ++ti) {
     xtid = tid;
-    asm volatile("" : "+v"(xtid));
-    asm volatile("" : "+s"(A));
-    recs = (crec_ptr)A->chunks;
-    tiles = (ctile_ptr)A->tiles;
+    xwave = wave;
+    asm volatile("" : "+v"(xtid), "+s"(xwave));
     const int r3 = ring;                         // (ti + 3) % 3
     const int r1 = ring + 1 == kRing ? 0 : ring + 1;
     const int r2 = r1 + 1 == kRing ? 0 : r1 + 1;
     const bool has1 = ti + 1 < t_end, has2 = ti + 2 < t_end, has3 = ti + 3 < t_end;
-    if (has3) raw_copy(ti + 3, r3);              // (1) tile i+3
-    if (has2) cent_gather(ti + 2, r2, ti & 1);   // (2) tile i+2
-    if (has1) tables_for(ti + 1);
+    // this step's tile-record fields, loaded up front (indexes clamped to
+    // real tiles; the view of a missing tile has nvalid = 0 and is not used)
+    const int j1 = has1 ? ti + 1 : ti, j2 = has2 ? ti + 2 : ti, j3 = has3 ? ti + 3 : ti;
+    // all metadata words of this step, read from LDS as one batch
+    const RawRole q = raw_role();
+    const uint32_t* M0 = sMeta[ti % kMetaSlots];
+    const uint32_t* M1 = sMeta[j1 % kMetaSlots];
+    const uint32_t* M2 = sMeta[j2 % kMetaSlots];
+    const uint32_t* M3 = sMeta[j3 % kMetaSlots];
+    const int fs = kFSrc + (q.rv * 3 + q.rsel) * 2;
+    uint32_t w[18] = {M0[kFNvalid], M0[kFKstart],
+                      M1[kFNvalid], M1[kFN], M1[kFSrc + 2], M1[kFSrc + 8],
+                      M2[kFNvalid], M2[kFN], M2[kFCent], M2[kFCent + 1], M2[kFCent + 2], M2[kFCent + 3],
+                      M2[kFSrc + 4], M2[kFSrc + 10],
+                      M3[kFNvalid], M3[kFN], M3[fs], M3[fs + 1]};
+#pragma unroll
+    for (int k = 0; k < 18; ++k) w[k] = (uint32_t)__builtin_amdgcn_readfirstlane((int)w[k]);
+    const int nv0 = (int)w[0], ks0 = (int)w[1];
+    DecodeView DV;
+    {
+      const uint32_t hrow = (uint32_t)h * w[3];
+      DV.lead[0] = lead_of(w[4] + (hrow << (kGs + 1))) >> 1;     // K scales
+      DV.lead[1] = lead_of(w[5] + (hrow << (vGs + 1))) >> 1;     // V scales
+      DV.nvalid = has1 ? (int)w[2] : 0;
+    }
+    GatherView GV;
+    {
+      const uint32_t hrow = (uint32_t)h * w[7];
+      GV.cent[0] = reinterpret_cast<const uint8_t*>(((uint64_t)w[9] << 32) | w[8]) + (int64_t)h * kC * kHeadDim * 2;
+      GV.cent[1] = reinterpret_cast<const uint8_t*>(((uint64_t)w[11] << 32) | w[10]) + (int64_t)h * vC * kHeadDim * 2;
+      GV.lead[0] = lead_of(w[12] + hrow);                         // K labels
+      GV.lead[1] = lead_of(w[13] + hrow);                         // V labels
+      GV.nvalid = has2 ? (int)w[6] : 0;
+    }
+    RawView RV;
+    {
+      const int64_t hrow = (int64_t)h * (int)w[15];
+      RV.src = reinterpret_cast<const uint8_t*>(((uint64_t)w[17] << 32) | w[16]) + (hrow << q.rshift) + (q.rpart == 1 ? 1024 : 0);
+      RV.nvalid = has3 ? (int)w[14] : 0;
+    }
+    if (has1) tables_for(j1);
+    // (1) raw copy of tile i+3 and (2) centroid gather of tile i+2 are issued
+    // after this wave's decode (its reads of the copy targets would otherwise
+    // wait for them) and before its compute, which reads other LDS objects.
+    auto issue = [&]() __attribute__((always_inline)) {
+      if (has2) cent_gather(GV, r2, ti & 1);
+      if (has3) raw_copy(RV, r3);
+      if (xwave == 0 && ti + 5 < t_end) meta_copy(ti + 5);   // slot of tile i+5: read from step i+2 on
+    };
 #pragma unroll 1
     for (int ph = 0; ph < 2; ++ph) {
-      if (ph == grp) compute_tile(ti, ti & 1);                              // (4) tile i
-      else if (has1) decode_tile(ti + 1, r1, (ti + 1) & 1, (ti + 1) & 1);   // (3) tile i+1
+      if (ph == grp) {
+        if (grp == 0) issue();
+        compute_tile(nv0, ks0, ti & 1);                                     // (4) tile i
+      } else {
+        if (has1) decode_tile(DV, j1, r1, (ti + 1) & 1, (ti + 1) & 1);      // (3) tile i+1
+        if (grp == 1) issue();
+      }
     }
-    if (has3) raw_finish(r3);
     wait_dma();
     __syncthreads();
     ring = r1;
   }
 
   // ---- epilogue ----
+  // The output arguments are read here, through an opaque pointer to the
+  // kernel arguments, so that they are not held in registers during the loop.
+  cargs_ptr E = (cargs_ptr)__builtin_amdgcn_kernarg_segment_ptr();
+  asm volatile("" : "+s"(E));
   const float l_tot = l_run + __shfl_xor(l_run, 32);
   if (!qok) return;
-  if (a.n_split == 1) {
+  if (E->n_split == 1) {
     const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
-    float* orow = a.out + (int64_t)qrow * a.out_stride_token + (int64_t)h * a.out_stride_head;
+    float* orow = E->out + (int64_t)qrow * E->out_stride_token + (int64_t)h * E->out_stride_head;
 #pragma unroll
     for (int db = 0; db < 4; ++db)
 #pragma unroll
@@ -640,7 +737,7 @@ __global__ __launch_bounds__(kThreads) void k_attend(AttendArgs a) {
             make_float4(o[db][4 * g] * inv, o[db][4 * g + 1] * inv, o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv);
       }
   } else {
-    float* prow = a.part_o + (((int64_t)split * a.H + h) * a.Nq + qrow) * kHeadDim;
+    float* prow = E->part_o + (((int64_t)split * E->H + h) * E->Nq + qrow) * kHeadDim;
 #pragma unroll
     for (int db = 0; db < 4; ++db)
 #pragma unroll
@@ -649,7 +746,7 @@ __global__ __launch_bounds__(kThreads) void k_attend(AttendArgs a) {
         *reinterpret_cast<float4*>(prow + d0) = make_float4(o[db][4 * g], o[db][4 * g + 1], o[db][4 * g + 2], o[db][4 * g + 3]);
       }
     if (half == 0) {
-      float* ml = a.part_ml + (((int64_t)split * a.H + h) * a.Nq + qrow) * 2;
+      float* ml = E->part_ml + (((int64_t)split * E->H + h) * E->Nq + qrow) * 2;
       ml[0] = m_run;
       ml[1] = l_tot;
     }
@@ -708,9 +805,9 @@ __global__ __launch_bounds__(256) void k_qu(TensorView q, int H, int Nq, int r, 
   for (int b = 0; b < kMaxRank; ++b) qu[gid * kMaxRank + b] = b < r ? (float)acc[b] : 0.0f;
 }
 
-// TileInfo of every tile: the chunk holding it (last chunk whose first tile is <= j).
+// TileRec of every tile: the chunk holding it is the last one whose first tile is <= j.
 __global__ __launch_bounds__(256) void k_tile_table(const ChunkRec* __restrict__ recs, int n_chunks, int n_tiles,
-                                                    TileInfo* __restrict__ tiles) {
+                                                    TokenBytes tb, TileRec* __restrict__ tiles) {
   const int j = blockIdx.x * blockDim.x + threadIdx.x;
   if (j >= n_tiles) return;
   int lo = 0, hi = n_chunks - 1;
@@ -718,7 +815,25 @@ __global__ __launch_bounds__(256) void k_tile_table(const ChunkRec* __restrict__
     const int mid = (lo + hi + 1) >> 1;
     if (recs[mid].tile_start <= j) lo = mid; else hi = mid - 1;
   }
-  tiles[j] = TileInfo{lo, (j - recs[lo].tile_start) * kKTile};
+  const ChunkRec& c = recs[lo];
+  const int token0 = (j - c.tile_start) * kKTile;
+  TileRec t;
+  t.src[0][0] = c.kcodes + (int64_t)token0 * tb.kcodes;
+  t.src[1][0] = c.vcodes + (int64_t)token0 * tb.vcodes;
+  t.src[0][1] = c.kscales + (int64_t)token0 * tb.kscales;
+  t.src[1][1] = c.vscales + (int64_t)token0 * tb.vscales;
+  t.src[0][2] = c.klabels + token0;
+  t.src[1][2] = c.vlabels + token0;
+  t.cent[0] = c.kcent;
+  t.cent[1] = c.vcent;
+  t.kpsac = c.kpsac + (int64_t)token0 * tb.kpsac;
+  t.n = c.n;
+  t.nvalid = min(kKTile, c.n - token0);
+  t.kstart = (int)c.token_start + token0;
+  t.token0 = token0;
+  t.chunk = lo;
+  t.pad = 0;
+  tiles[j] = t;
 }
 
 __global__ void k_upload(ChunkBatch b, ChunkRec* __restrict__ dst) {
@@ -733,10 +848,23 @@ hipError_t launch_upload_chunks(const ChunkBatch& b, ChunkRec* dst, hipStream_t 
   return hipGetLastError();
 }
 
-hipError_t launch_tile_table(const ChunkRec* recs, int n_chunks, int n_tiles, TileInfo* tiles, hipStream_t s) {
+hipError_t launch_tile_table(const ChunkRec* recs, int n_chunks, int n_tiles, TokenBytes tb, TileRec* tiles,
+                             hipStream_t s) {
   if (n_tiles <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k_tile_table, dim3((unsigned)((n_tiles + 255) / 256)), dim3(256), 0, s, recs, n_chunks, n_tiles, tiles);
+  hipLaunchKernelGGL(k_tile_table, dim3((unsigned)((n_tiles + 255) / 256)), dim3(256), 0, s, recs, n_chunks, n_tiles, tb,
+                     tiles);
   return hipGetLastError();
+}
+
+template <int F>
+void launch_attend_flags(const AttendArgs& a, dim3 grid, hipStream_t s) {
+  hipLaunchKernelGGL((k_attend<(F & 1) != 0, (F & 2) != 0, (F & 4) != 0, (F & 8) != 0, (F & 16) != 0>), grid,
+                     dim3(kThreads), 0, s, a);
+}
+// flags: 1 fp32 queries, 2 K fast path, 4 V fast path, 8 debug logits, 16 PSAC
+template <int... F>
+void launch_attend_variant(int flags, const AttendArgs& a, dim3 grid, hipStream_t s, std::integer_sequence<int, F...>) {
+  ((flags == F ? launch_attend_flags<F>(a, grid, s) : void()), ...);
 }
 
 hipError_t launch_attend(const AttendArgs& a, hipStream_t s) {
@@ -751,25 +879,9 @@ hipError_t launch_attend(const AttendArgs& a, hipStream_t s) {
   }
   const int q_tiles = (a.Nq + kBM - 1) / kBM;
   const dim3 grid((unsigned)(q_tiles * a.n_split * a.H));
-  const bool kf = a.k_uniform_int2_1stage;
-  const bool vf = a.v_uniform_int2_1stage;
-#define QKV_AT(QF, KF, VF)                                                                        \
-  do {                                                                                            \
-    if (a.logits) hipLaunchKernelGGL((k_attend<QF, KF, VF, true>), grid, dim3(kThreads), 0, s, a);  \
-    else hipLaunchKernelGGL((k_attend<QF, KF, VF, false>), grid, dim3(kThreads), 0, s, a);          \
-  } while (0)
-  if (a.q.dtype == 0) {
-    if (kf && vf) QKV_AT(true, true, true);
-    else if (!kf && vf) QKV_AT(true, false, true);
-    else if (kf && !vf) QKV_AT(true, true, false);
-    else QKV_AT(true, false, false);
-  } else {
-    if (kf && vf) QKV_AT(false, true, true);
-    else if (!kf && vf) QKV_AT(false, false, true);
-    else if (kf && !vf) QKV_AT(false, true, false);
-    else QKV_AT(false, false, false);
-  }
-#undef QKV_AT
+  const int flags = (a.q.dtype == 0 ? 1 : 0) | (a.k_uniform_int2_1stage ? 2 : 0) | (a.v_uniform_int2_1stage ? 4 : 0) |
+                    (a.logits ? 8 : 0) | (a.psac_rank > 0 ? 16 : 0);
+  launch_attend_variant(flags, a, grid, s, std::make_integer_sequence<int, 32>{});
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.n_split == 1) return e;
   const int64_t total = (int64_t)a.H * a.Nq * (kHeadDim / 4);

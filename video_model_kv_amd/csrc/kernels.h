@@ -93,9 +93,25 @@ struct ChunkRec {
   int32_t tile_start;    // global index of the chunk's first 64-key tile
 };
 
-// Per 64-key tile of the concatenated cache: its chunk and first token there.
-struct TileInfo {
-  int32_t chunk, token0;
+// Per 64-key tile of the concatenated cache: the stage-0 section pointers of
+// head 0 advanced to the tile's first token (head h adds h * n tokens; the
+// centroid pointers are the chunk's tables), and the tile geometry.
+struct TileRec {
+  const uint8_t* src[2][3];   // [K, V][code words, scales, labels]
+  const uint8_t* cent[2];     // [K, V] centroid tables of the chunk
+  const uint8_t* kpsac;
+  int32_t n;        // tokens in the chunk (head stride in tokens)
+  int32_t nvalid;   // keys in the tile (<= 64)
+  int32_t kstart;   // global index of the tile's first key
+  int32_t token0;   // index of the tile's first key within the chunk
+  int32_t chunk;
+  int32_t pad;
+};
+static_assert(sizeof(TileRec) == 96, "TileRec layout");
+
+// Bytes per token of each section (stage 0), for the tile records.
+struct TokenBytes {
+  int32_t kcodes, vcodes, kscales, vscales, kpsac;
 };
 
 struct ChunkBatch {
@@ -103,8 +119,9 @@ struct ChunkBatch {
   ChunkRec rec[kChunkBatch];
 };
 hipError_t launch_upload_chunks(const ChunkBatch& b, ChunkRec* dst, hipStream_t s);
-// TileInfo of every tile from the uploaded chunk records.
-hipError_t launch_tile_table(const ChunkRec* recs, int n_chunks, int n_tiles, TileInfo* tiles, hipStream_t s);
+// TileRec of every tile from the uploaded chunk records.
+hipError_t launch_tile_table(const ChunkRec* recs, int n_chunks, int n_tiles, TokenBytes tb, TileRec* tiles,
+                             hipStream_t s);
 
 struct AttendArgs {
   TensorView q;
@@ -113,7 +130,7 @@ struct AttendArgs {
   int n_chunks, n_tiles;
   LayoutParams kp, vp;           // layouts of the K and V chunks
   const ChunkRec* chunks;        // device [n_chunks]
-  const TileInfo* tiles;         // device [n_tiles]
+  const TileRec* tiles;          // device [n_tiles]
   const float* U;                // [H][128][r] or null
   int psac_rank;
   float* qu;                     // workspace [H][Nq][8] f32

@@ -178,7 +178,7 @@ AttendWs attend_ws(int H, int64_t nq, int n_chunks, int64_t n_tiles, int64_t spl
   AttendWs w;
   uint64_t off = 0;
   w.chunks = off;  off += align256((uint64_t)n_chunks * sizeof(ChunkRec));
-  w.tiles = off;   off += align256((uint64_t)n_tiles * sizeof(TileInfo));
+  w.tiles = off;   off += align256((uint64_t)n_tiles * sizeof(TileRec));
   w.qu = off;      off += align256((uint64_t)H * nq * kMaxRank * 4);
   w.part_o = off;  off += align256((uint64_t)split_rows * H * kHeadDim * 4);
   w.part_ml = off; off += align256((uint64_t)split_rows * H * 2 * 4);
@@ -457,8 +457,12 @@ int qkv_attend(const qkv_config* k_cfg, const qkv_config* v_cfg, const qkv_tenso
     for (int i = 0; i < b.count; ++i) b.rec[i] = recs[first + i];
     QKV_HIP(launch_upload_chunks(b, drecs, s));
   }
-  TileInfo* dtiles = reinterpret_cast<TileInfo*>(at(workspace, ws.tiles));
-  QKV_HIP(launch_tile_table(drecs, n_chunks, (int)n_tiles, dtiles, s));
+  TileRec* dtiles = reinterpret_cast<TileRec*>(at(workspace, ws.tiles));
+  {
+    const ChunkDecode dk = make_decode(params_of(k_cfg), 1, nullptr), dv = make_decode(params_of(v_cfg), 1, nullptr);
+    const TokenBytes tb{dk.words * 4, dv.words * 4, dk.groups * 2, dv.groups * 2, k_cfg->psac_rank * 2};
+    QKV_HIP(launch_tile_table(drecs, n_chunks, (int)n_tiles, tb, dtiles, s));
+  }
 
   AttendArgs a;
   a.q = view_of(q);
