@@ -25,6 +25,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "KV tokens quantized/s + fused INT2 attention TFLOP/s, GB/s vs MI355X peak"
 HBM_PEAK_GBS = 8000.0
+N_STREAMS = 4          # concurrent chunk quantizations (hardware queues per process on this part)
 BF16_PEAK_TFLOPS = 2500.0
 
 
@@ -133,16 +134,32 @@ def main():
         side_k = dict(w=w if wl.qsac else None, perm=perm if wl.n_int4 else None, U=U if wl.psac_rank else None)
     log(f"inputs ready in {time.time() - t0:.1f} s")
     maxn = max(ntok)
-    ws = torch.empty(max(qk.qkv_workspace_bytes(kcfg, maxn, wl.n_query, wl.n_chunks),
-                         qk.qkv_workspace_bytes(vcfg, maxn)), dtype=torch.uint8, device=dev)
+    ws_bytes = max(qk.qkv_workspace_bytes(kcfg, maxn, wl.n_query, wl.n_chunks), qk.qkv_workspace_bytes(vcfg, maxn))
+    # The chunk quantizations of a step are independent: they run on N_STREAMS
+    # streams (default priority), each with its own workspace, joined by events
+    # before the attention.
+    streams = [torch.cuda.Stream() for _ in range(N_STREAMS)]
+    wss = [torch.empty(ws_bytes, dtype=torch.uint8, device=dev) for _ in range(N_STREAMS)]
+    ws = wss[0]
     kp = [torch.empty(qk.qkv_chunk_layout(kcfg, n).bytes, dtype=torch.uint8, device=dev) for n in ntok]
     vp = [torch.empty(qk.qkv_chunk_layout(vcfg, n).bytes, dtype=torch.uint8, device=dev) for n in ntok]
     out = torch.empty((wl.n_query, H, d), dtype=torch.float32, device=dev)
+    problems = [(kcfg, xk[c], kp[c], side_k) for c in range(wl.n_chunks)] + \
+               [(vcfg, xv[c], vp[c], {}) for c in range(wl.n_chunks)]
 
     def quantize_all():
-        for c in range(wl.n_chunks):
-            qk.qkv_quantize_chunk(kcfg, xk[c], kp[c], ws, **side_k)
-            qk.qkv_quantize_chunk(vcfg, xv[c], vp[c], ws)
+        main = torch.cuda.current_stream()
+        start = torch.cuda.Event()
+        start.record(main)
+        for i, (cfg, x, packed, side) in enumerate(problems):
+            st = streams[i % N_STREAMS]
+            if i < N_STREAMS:
+                st.wait_event(start)
+            qk.qkv_quantize_chunk(cfg, x, packed, wss[i % N_STREAMS], stream=st.cuda_stream, **side)
+        for st in streams:
+            done = torch.cuda.Event()
+            done.record(st)
+            main.wait_event(done)
 
     def attend():
         qk.qkv_attend(kcfg, vcfg, q, kp, vp, ntok, out, ws, U=side_k.get("U"))

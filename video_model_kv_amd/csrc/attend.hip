@@ -216,12 +216,14 @@ __global__ __launch_bounds__(kThreads) void k_attend(AttendArgs a) {
       float v[8];
       if constexpr (QF32) {
         const float* p = reinterpret_cast<const float*>(a.q.ptr) + base + ch;
-        const float4 x0 = qok ? *reinterpret_cast<const float4*>(p) : make_float4(0, 0, 0, 0);
-        const float4 x1 = qok ? *reinterpret_cast<const float4*>(p + 4) : make_float4(0, 0, 0, 0);
+        float4 x0 = *reinterpret_cast<const float4*>(p);   // p is in range (query 0 when !qok)
+        float4 x1 = *reinterpret_cast<const float4*>(p + 4);
+        if (!qok) x0 = x1 = make_float4(0, 0, 0, 0);
         v[0] = x0.x; v[1] = x0.y; v[2] = x0.z; v[3] = x0.w; v[4] = x1.x; v[5] = x1.y; v[6] = x1.z; v[7] = x1.w;
       } else {
         const uint16_t* p = reinterpret_cast<const uint16_t*>(a.q.ptr) + base + ch;
-        const uint4 r = qok ? *reinterpret_cast<const uint4*>(p) : make_uint4(0, 0, 0, 0);
+        uint4 r = *reinterpret_cast<const uint4*>(p);      // p is in range (query 0 when !qok)
+        if (!qok) r = make_uint4(0, 0, 0, 0);
         const uint32_t r4[4] = {r.x, r.y, r.z, r.w};
 #pragma unroll
         for (int e = 0; e < 8; ++e) v[e] = bf16_bits_to_f32((r4[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);

@@ -34,12 +34,12 @@ hipError_t launch_centroid_prep(int H, int C, const float* c, const float* w, ui
 hipError_t launch_kmeans_assign(const TensorView& y, int H, int C, const uint16_t* planes,
                                 const float* cn, const float* c, const float* w, uint8_t* labels,
                                 int* amb_count, int64_t* amb_list, hipStream_t s);
-// Update = counting sort of the labels (start [H][C+1], order [H][N] int32
-// workspace) + exact per-cluster sums; when planes != null it also refreshes
-// the operand planes / norms for the next assign.  Zeroes amb_count.
+// Update = grouping of the tokens by label (in LDS) + exact per-cluster sums;
+// when planes != null it also refreshes the operand planes / norms for the
+// next assign.  Zeroes amb_count.
 hipError_t launch_kmeans_update(const TensorView& y, int H, int C, const uint8_t* labels, float* c,
-                                int32_t* counts, int32_t* start, int32_t* order, const float* w,
-                                uint16_t* planes, float* cn, int* amb_count, hipStream_t s);
+                                int32_t* counts, const float* w, uint16_t* planes, float* cn, int* amb_count,
+                                hipStream_t s);
 hipError_t launch_centroid_bf16(int H, int C, const float* c, uint16_t* out, hipStream_t s);
 hipError_t launch_fill_zero_u32(void* p, size_t n_words, hipStream_t s);
 

@@ -7,10 +7,11 @@
 // query-activity weights w in the distance).
 //
 // Assign computes, for every token y and centroid c,
-//     D'(y, c) = sum_k w_k c_k^2 - 2 sum_k y_k (w_k c_k)
+//     D'(y, c) = sum_k w_k c_k^2 + sum_k y_k (-2 w_k c_k)
 // which differs from the weighted squared distance by sum_k w_k y_k^2, a
 // per-token constant that does not move the argmin.  The dot products run on
-// MFMA (v_mfma_f32_32x32x16_bf16): fp32(w*c) is split into bf16 hi + lo (16
+// MFMA (v_mfma_f32_32x32x16_bf16), the accumulators starting from the norms:
+// fp32(-2*w*c) is split into bf16 hi + lo (16
 // significant bits), bf16 tokens are exact operands, fp32 tokens are split
 // into hi + lo too (three products: hh, lh, hl); products are exact and the
 // sums are fp32.  The error of D' stays below ~1e-6 of ||y||_w^2 + ||c||_w^2;
@@ -65,7 +66,7 @@ __global__ __launch_bounds__(64) void k_prep(int C, const float* __restrict__ c,
     const int k = lane * 2 + e;
     const float cv = cr[k];
     const float wv = w ? w[h * kHeadDim + k] : 1.0f;
-    const float b = wv * cv;
+    const float b = -2.0f * (wv * cv);           // exact doubling: the planes carry -2 w c
     const uint32_t hi = f32_to_bf16_bits(b);
     const uint32_t lo = f32_to_bf16_bits(b - bf16_bits_to_f32(hi));
     ph[k] = (uint16_t)hi;
@@ -78,12 +79,10 @@ __global__ __launch_bounds__(64) void k_prep(int C, const float* __restrict__ c,
 }
 
 template <bool F32>
-__global__ __launch_bounds__(256) void k_assign(TensorView y, int C, int tiles_per_head, int n_heads,
-                                                const uint16_t* __restrict__ planes,
-                                                const float* __restrict__ cn,
-                                                const float* __restrict__ w,
-                                                uint8_t* __restrict__ labels, int* __restrict__ amb_count,
-                                                int64_t* __restrict__ amb_list) {
+__device__ __forceinline__ void assign_body(TensorView y, int C, int tiles_per_head, int n_heads,
+                                            const uint16_t* __restrict__ planes, const float* __restrict__ cn,
+                                            const float* __restrict__ w, uint8_t* __restrict__ labels,
+                                            int* __restrict__ amb_count, int64_t* __restrict__ amb_list) {
   __shared__ __attribute__((aligned(16))) uint16_t sA[2][2][32][kPitch];
   __shared__ float sCn[2][32];
   __shared__ __attribute__((aligned(16))) float sW[kHeadDim];
@@ -101,42 +100,57 @@ __global__ __launch_bounds__(256) void k_assign(TensorView y, int C, int tiles_p
   bf16x8 yh[2][8];
   bf16x8 yl[2][F32 ? 8 : 1];
   float ynorm[2] = {0.0f, 0.0f};
+  if constexpr (F32) {
 #pragma unroll
-  for (int t = 0; t < 2; ++t) {
-    const int tok = tile * kAssignTokens + wave * 64 + t * 32 + col;
-    const bool ok = tok < N;
-    const int64_t base = (int64_t)(ok ? tok : 0) * y.stride_token + (int64_t)h * y.stride_head;
+    for (int t = 0; t < 2; ++t) {
+      const int tok = tile * kAssignTokens + wave * 64 + t * 32 + col;
+      const bool ok = tok < N;
+      const int64_t base = (int64_t)(ok ? tok : 0) * y.stride_token + (int64_t)h * y.stride_head;
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      const int ch = s * 16 + half * 8;
-      float v[8];
-      if constexpr (F32) {
+      for (int s = 0; s < 8; ++s) {
+        const int ch = s * 16 + half * 8;
         const float* p = reinterpret_cast<const float*>(y.ptr) + base + ch;
-        float4 a = ok ? *reinterpret_cast<const float4*>(p) : make_float4(0, 0, 0, 0);
-        float4 b = ok ? *reinterpret_cast<const float4*>(p + 4) : make_float4(0, 0, 0, 0);
-        v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+        float4 a = *reinterpret_cast<const float4*>(p);       // p is in range (token 0 when !ok)
+        float4 b = *reinterpret_cast<const float4*>(p + 4);
+        if (!ok) a = b = make_float4(0, 0, 0, 0);
+        const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
         u16x8 hi, lo;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const uint32_t hb = f32_to_bf16_bits(v[e]);
           hi[e] = (uint16_t)hb;
           lo[e] = (uint16_t)f32_to_bf16_bits(v[e] - bf16_bits_to_f32(hb));
+          ynorm[t] += sW[ch + e] * (v[e] * v[e]);
         }
         yh[t][s] = __builtin_bit_cast(bf16x8, hi);
         yl[t][F32 ? s : 0] = __builtin_bit_cast(bf16x8, lo);
-      } else {
-        const uint16_t* p = reinterpret_cast<const uint16_t*>(y.ptr) + base + ch;
-        uint4 raw = ok ? *reinterpret_cast<const uint4*>(p) : make_uint4(0, 0, 0, 0);
-        yh[t][s] = as_bf16x8(raw);
-        const uint32_t r4[4] = {raw.x, raw.y, raw.z, raw.w};
-#pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = bf16_bits_to_f32((r4[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
       }
-      const float4 w0 = *reinterpret_cast<const float4*>(&sW[ch]);
-      const float4 w1 = *reinterpret_cast<const float4*>(&sW[ch + 4]);
-      const float wv[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+    }
+  } else {
+    uint4 raw[2][8];                             // all 16 loads in flight before any use
 #pragma unroll
-      for (int e = 0; e < 8; ++e) ynorm[t] += wv[e] * (v[e] * v[e]);
+    for (int t = 0; t < 2; ++t) {
+      const int tok = tile * kAssignTokens + wave * 64 + t * 32 + col;
+      const int64_t base = (int64_t)min(tok, N - 1) * y.stride_token + (int64_t)h * y.stride_head;
+#pragma unroll
+      for (int s = 0; s < 8; ++s)
+        raw[t][s] = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(y.ptr) + base + s * 16 + half * 8);
+    }
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const bool ok = tile * kAssignTokens + wave * 64 + t * 32 + col < N;
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        if (!ok) raw[t][s] = make_uint4(0, 0, 0, 0);
+        yh[t][s] = as_bf16x8(raw[t][s]);
+        const uint32_t r4[4] = {raw[t][s].x, raw[t][s].y, raw[t][s].z, raw[t][s].w};
+        const int ch = s * 16 + half * 8;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float v = bf16_bits_to_f32((r4[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
+          ynorm[t] += sW[ch + e] * (v * v);
+        }
+      }
     }
   }
 
@@ -147,38 +161,58 @@ __global__ __launch_bounds__(256) void k_assign(TensorView y, int C, int tiles_p
   int bidx[2] = {0, 0};
   const uint16_t* ph = planes + (int64_t)h * 2 * C * kHeadDim;
   const int nblk = (C + 31) / 32;
-  uint4 pf[4];
-  float cnpf = INFINITY;
-  auto fetch = [&](int cb) {
+  // one centroid block (rows cb*32 .. +31 of both planes, and their norms),
+  // fetched into registers one block ahead
+  struct Block {
+    uint4 v0, v1, v2, v3;
+    float cn;
+  };
+  auto fetch = [&](int cb) __attribute__((always_inline)) -> Block {
+    Block B;
+    uint4* dst[4] = {&B.v0, &B.v1, &B.v2, &B.v3};
 #pragma unroll
     for (int x = 0; x < 4; ++x) {
       const int v = threadIdx.x + x * 256;
       const int p = v >> 9, r = (v >> 4) & 31, c16 = v & 15;
-      const int j = cb * 32 + r;
-      pf[x] = make_uint4(0, 0, 0, 0);
-      if (j < C) pf[x] = *reinterpret_cast<const uint4*>(ph + ((int64_t)p * C + j) * kHeadDim + c16 * 8);
+      const int j = min(cb * 32 + r, C - 1);   // rows past C: a copy of row C-1, never chosen (norm +inf)
+      *dst[x] = *reinterpret_cast<const uint4*>(ph + ((int64_t)p * C + j) * kHeadDim + c16 * 8);
     }
-    if (threadIdx.x < 32) {
-      const int j = cb * 32 + threadIdx.x;
-      cnpf = j < C ? cn[h * C + j] : INFINITY;
-    }
+    const int j = cb * 32 + (threadIdx.x & 31);
+    const float v = cn[h * C + min(j, C - 1)];
+    B.cn = j < C ? v : INFINITY;
+    return B;
   };
-  auto stash = [&](int buf) {
+  auto stash = [&](const Block& B, int buf) __attribute__((always_inline)) {
+    const uint4 src[4] = {B.v0, B.v1, B.v2, B.v3};
 #pragma unroll
     for (int x = 0; x < 4; ++x) {
       const int v = threadIdx.x + x * 256;
       const int p = v >> 9, r = (v >> 4) & 31, c16 = v & 15;
-      *reinterpret_cast<uint4*>(&sA[buf][p][r][c16 * 8]) = pf[x];
+      *reinterpret_cast<uint4*>(&sA[buf][p][r][c16 * 8]) = src[x];
     }
-    if (threadIdx.x < 32) sCn[buf][threadIdx.x] = cnpf;
+    if (threadIdx.x < 32) sCn[buf][threadIdx.x] = B.cn;
   };
-  fetch(0);
-  stash(0);
+  stash(fetch(0), 0);
   __syncthreads();
   for (int cb = 0; cb < nblk; ++cb) {
     const int buf = cb & 1;
-    if (cb + 1 < nblk) fetch(cb + 1);
-    f32x16 acc0 = {}, acc1 = {};
+    const Block nxt = fetch(min(cb + 1, nblk - 1));   // the last block is fetched twice, stashed once
+    // the accumulators start from ||c_j||_w^2 of their centroid rows: row
+    // (r/4)*8 + half*4 + r%4 of the block for element r
+    f32x16 acc0, acc1;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const float4 c4 = *reinterpret_cast<const float4*>(&sCn[buf][g * 8 + half * 4]);
+      const float4 d4 = *reinterpret_cast<const float4*>(&sCn[buf][g * 8 + half * 4]);
+      acc0[4 * g] = c4.x;
+      acc0[4 * g + 1] = c4.y;
+      acc0[4 * g + 2] = c4.z;
+      acc0[4 * g + 3] = c4.w;
+      acc1[4 * g] = d4.x;
+      acc1[4 * g + 1] = d4.y;
+      acc1[4 * g + 2] = d4.z;
+      acc1[4 * g + 3] = d4.w;
+    }
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
       const bf16x8 ahi = as_bf16x8(*reinterpret_cast<const uint4*>(&sA[buf][0][col][s * 16 + half * 8]));
@@ -194,22 +228,20 @@ __global__ __launch_bounds__(256) void k_assign(TensorView y, int C, int tiles_p
     }
     // Output layout: lane holds token `col`, centroid rows (r/4)*8 + half*4 + r%4
     // (increasing in r), so strict '<' keeps the lowest index among equal values.
+    // Running best b1 and second best b2 (b1 <= b2): new b2 = med3(b1, b2, v).
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int jr = (r >> 2) * 8 + half * 4 + (r & 3);
-      const int j = cb * 32 + jr;
-      const float cnv = sCn[buf][jr];
-      const float v0 = cnv - 2.0f * acc0[r];
-      const float v1 = cnv - 2.0f * acc1[r];
+      const int j = cb * 32 + (r >> 2) * 8 + half * 4 + (r & 3);
+      const float v0 = acc0[r], v1 = acc1[r];
       const bool l0 = v0 < b1[0], l1 = v1 < b1[1];
-      b2[0] = l0 ? b1[0] : fminf(b2[0], v0);
-      b2[1] = l1 ? b1[1] : fminf(b2[1], v1);
+      b2[0] = __builtin_amdgcn_fmed3f(b1[0], b2[0], v0);
+      b2[1] = __builtin_amdgcn_fmed3f(b1[1], b2[1], v1);
+      b1[0] = fminf(b1[0], v0);
+      b1[1] = fminf(b1[1], v1);
       bidx[0] = l0 ? j : bidx[0];
       bidx[1] = l1 ? j : bidx[1];
-      b1[0] = l0 ? v0 : b1[0];
-      b1[1] = l1 ? v1 : b1[1];
     }
-    if (cb + 1 < nblk) stash(buf ^ 1);
+    if (cb + 1 < nblk) stash(nxt, buf ^ 1);
     __syncthreads();
   }
 #pragma unroll
@@ -237,6 +269,20 @@ __global__ __launch_bounds__(256) void k_assign(TensorView y, int C, int tiles_p
       }
     }
   }
+}
+
+// bf16 tokens: two waves per SIMD; fp32 tokens (a second operand plane) one.
+__global__ __launch_bounds__(256, 2) void k_assign_bf16(TensorView y, int C, int tiles_per_head, int n_heads,
+                                                     const uint16_t* __restrict__ planes, const float* __restrict__ cn,
+                                                     const float* __restrict__ w, uint8_t* __restrict__ labels,
+                                                     int* __restrict__ amb_count, int64_t* __restrict__ amb_list) {
+  assign_body<false>(y, C, tiles_per_head, n_heads, planes, cn, w, labels, amb_count, amb_list);
+}
+__global__ __launch_bounds__(256) void k_assign_f32(TensorView y, int C, int tiles_per_head, int n_heads,
+                                                 const uint16_t* __restrict__ planes, const float* __restrict__ cn,
+                                                 const float* __restrict__ w, uint8_t* __restrict__ labels,
+                                                 int* __restrict__ amb_count, int64_t* __restrict__ amb_list) {
+  assign_body<true>(y, C, tiles_per_head, n_heads, planes, cn, w, labels, amb_count, amb_list);
 }
 
 // Float64 re-decision of queued close calls: one block per entry (grid-stride
@@ -305,123 +351,197 @@ __global__ __launch_bounds__(256) void k_refine(TensorView y, int C, const float
   }
 }
 
-// Counting sort of one head's tokens by label: counts, exclusive offsets and
-// the member list (the order inside a cluster is immaterial: the sums below
-// are exact up to ~2^-104).  One block of 1024 threads per head.
-__global__ __launch_bounds__(1024) void k_sort(int N, int C, const uint8_t* __restrict__ labels,
-                                               int32_t* __restrict__ start, int32_t* __restrict__ order,
-                                               int32_t* __restrict__ counts, int* __restrict__ amb_count) {
-  __shared__ int cnt[kMaxClusters];
-  __shared__ int cur[kMaxClusters];
-  const int h = blockIdx.x;
-  if (h == 0 && threadIdx.x == 0 && amb_count) *amb_count = 0;   // the close-call queue of the next assign
-  const uint8_t* lab = labels + (int64_t)h * N;
-  for (int j = threadIdx.x; j < C; j += blockDim.x) cnt[j] = 0;
-  __syncthreads();
-  for (int i = threadIdx.x; i < N; i += blockDim.x) atomicAdd(&cnt[min((int)lab[i], C - 1)], 1);
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    int acc = 0;
-    for (int j = 0; j < C; ++j) {
-      cur[j] = acc;
-      start[h * (C + 1) + j] = acc;
-      acc += cnt[j];
-    }
-    start[h * (C + 1) + C] = acc;
-  }
-  __syncthreads();
-  if (counts)
-    for (int j = threadIdx.x; j < C; j += blockDim.x) counts[h * C + j] = cnt[j];
-  for (int i = threadIdx.x; i < N; i += blockDim.x) {
-    const int pos = atomicAdd(&cur[min((int)lab[i], C - 1)], 1);
-    order[(int64_t)h * N + pos] = i;
-  }
-}
+// Centroid update fused with the grouping of tokens by label.  One workgroup
+// per (head, 8 consecutive clusters); wave w owns clusters 2w and 2w + 1 of
+// the group.  The head's labels are scanned in windows of kUpdWindow tokens:
+// the members of the group's clusters in the window are listed in LDS
+// (counting sort), then each wave adds its clusters' member rows (each lane
+// two channels).  The sums must be exact (their float64 rounding is then the
+// correctly rounded sum whatever the order; the mean is rounded once more to
+// float32):
+//  - bf16 tokens in one window: plain float64 sums, with a certificate: every
+//    partial sum of n values of 8-bit significands is an integer multiple of
+//    the smallest significand unit, below n * 2^(emax+1), so it is exact when
+//    emax - emin + ceil(log2 n) <= 44 (biased exponents of the largest and the
+//    smallest nonzero magnitude, tracked with packed 16-bit min/max); a
+//    channel that fails it is summed again in double-double;
+//  - otherwise double-double throughout (exact up to ~2^-104 relative).
+// An empty cluster keeps its centroid (and its operand planes and norm).
+constexpr int kUpdClusters = 8;
+constexpr int kUpdWindow = 8192;          // token index << 3 fits 16 bits
 
-// One block per (head, cluster): the 4 waves take a quarter of the members
-// each, accumulate rows in double-double (each lane two channels, up to 8 rows
-// in flight), then combine in a fixed order.  The double-double value is the
-// exact sum up to ~2^-104 relative, so its float64 rounding is the correctly
-// rounded sum whatever the order; the mean is rounded once more to float32.
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
 template <bool F32>
-__global__ __launch_bounds__(256) void k_sum(TensorView y, int C, int n_heads, const int32_t* __restrict__ start,
-                                             const int32_t* __restrict__ order, float* __restrict__ c,
-                                             const float* __restrict__ w, uint16_t* __restrict__ planes,
-                                             float* __restrict__ cn) {
-  __shared__ double sd[4][64][4];
-  const uint32_t logical = xcd_remap(blockIdx.x, (uint32_t)(n_heads * C));
-  const int h = logical / C, j = logical % C;
+__global__ __launch_bounds__(256) void k_update(TensorView y, int C, int n_heads, const uint8_t* __restrict__ labels,
+                                                float* __restrict__ c, const float* __restrict__ w,
+                                                uint16_t* __restrict__ planes, float* __restrict__ cn,
+                                                int32_t* __restrict__ counts, int* __restrict__ amb_count) {
+  __shared__ int s_cnt[kUpdClusters], s_off[kUpdClusters + 1], s_cur[kUpdClusters];
+  __shared__ uint16_t s_mem[kUpdWindow], s_tmp[kUpdWindow];
+  __shared__ int s_wtot[4];
+  const int groups = (C + kUpdClusters - 1) / kUpdClusters;
+  const uint32_t logical = xcd_remap(blockIdx.x, (uint32_t)(n_heads * groups));
+  const int h = logical / groups, c0 = (logical % groups) * kUpdClusters;
   const int N = (int)y.n_tokens;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int s0 = start[h * (C + 1) + j], s1 = start[h * (C + 1) + j + 1];
-  const int n = s1 - s0;
-  if (n == 0) return;                      // empty cluster: the centroid keeps its value
-  const int per = (n + 3) / 4;
-  const int m0 = s0 + wave * per, m1 = min(s1, m0 + per);
-  const int32_t* ord = order + (int64_t)h * N;
-  DD a0{0.0, 0.0}, a1{0.0, 0.0};
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (blockIdx.x == 0 && tid == 0 && amb_count) *amb_count = 0;   // the close-call queue of the next assign
+  const uint8_t* lab = labels + (int64_t)h * N;
   const int64_t hoff = (int64_t)h * y.stride_head + lane * 2;
-  int my_idx = 0;
-  for (int m = m0; m < m1; m += 8) {
-    if (((m - m0) & 63) == 0) my_idx = (m + lane < m1) ? ord[m + lane] : 0;   // 64 member ids per load
-    float vx[8], vy[8];
+  const bool plain = !F32 && N <= kUpdWindow;   // certified float64 sums
+  DD acc[2][2] = {{{0.0, 0.0}, {0.0, 0.0}}, {{0.0, 0.0}, {0.0, 0.0}}};
+  int total[2] = {0, 0};
+
+  // member rows [m0, m1) of the window list: value pairs (channels lane*2, +1)
+  auto row_pair = [&](int t0, int mm, float& x0, float& x1) __attribute__((always_inline)) -> uint32_t {
+    const int64_t off = (int64_t)(t0 + s_mem[mm]) * y.stride_token + hoff;
+    if constexpr (F32) {
+      const float2 v = *reinterpret_cast<const float2*>(reinterpret_cast<const float*>(y.ptr) + off);
+      x0 = v.x;
+      x1 = v.y;
+      return 0u;
+    } else {
+      const uint32_t v = *reinterpret_cast<const uint32_t*>(reinterpret_cast<const uint16_t*>(y.ptr) + off);
+      x0 = bf16_bits_to_f32(v & 0xFFFFu);
+      x1 = bf16_bits_to_f32(v >> 16);
+      return v;
+    }
+  };
+  auto dd_rows = [&](int t0, int m0, int m1, DD& a0, DD& a1) __attribute__((always_inline)) {
+    for (int m = m0; m < m1; m += 16) {
+      float vx[16], vy[16];
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      vx[q] = 0.f;
-      vy[q] = 0.f;
-      const int idq = __shfl(my_idx, ((m - m0) & 63) + q);
-      if (m + q < m1) {
-        const int64_t off = (int64_t)idq * y.stride_token + hoff;
-        if constexpr (F32) {
-          const float2 v = *reinterpret_cast<const float2*>(reinterpret_cast<const float*>(y.ptr) + off);
-          vx[q] = v.x;
-          vy[q] = v.y;
-        } else {
-          const uint32_t v = *reinterpret_cast<const uint32_t*>(reinterpret_cast<const uint16_t*>(y.ptr) + off);
-          vx[q] = bf16_bits_to_f32(v & 0xFFFFu);
-          vy[q] = bf16_bits_to_f32(v >> 16);
+      for (int q = 0; q < 16; ++q) row_pair(t0, min(m + q, m1 - 1), vx[q], vy[q]);   // past the end: loaded, not added
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        if (m + q < m1) {
+          a0.add((double)vx[q]);
+          a1.add((double)vy[q]);
         }
       }
     }
+  };
+
+  for (int t0 = 0; t0 < N; t0 += kUpdWindow) {
+    // this thread's labels of the window (tokens t0 + tid + 256 x), one batch
+    // of loads, kept in registers for both counting passes
+    uint32_t kk[kUpdWindow / 256];
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      if (m + q < m1) {
-        a0.add((double)vx[q]);
-        a1.add((double)vy[q]);
+    for (int x = 0; x < kUpdWindow / 256; ++x) {
+      const int i = t0 + tid + 256 * x;
+      const uint32_t l = lab[min(i, N - 1)];                          // unconditional: one batch of loads
+      kk[x] = i < N ? l - (uint32_t)c0 : 0xFFFFFFFFu;                 // unsigned: in the group iff < 8
+    }
+    // (1) compact the window's members of the group into s_tmp (token << 3 |
+    // cluster): per wave one ballot per label slot, the wave's range from the
+    // wave totals (no atomics);  (2) counting sort of s_tmp by cluster into s_mem.
+    int wtot = 0;
+#pragma unroll
+    for (int x = 0; x < kUpdWindow / 256; ++x) wtot += __popcll(__ballot(kk[x] < (uint32_t)kUpdClusters));
+    if (lane == 0) s_wtot[wave] = wtot;
+    if (tid < kUpdClusters) s_cnt[tid] = 0;
+    __syncthreads();
+    int run = 0;
+    for (int v = 0; v < wave; ++v) run += s_wtot[v];
+    const int n_mem = s_wtot[0] + s_wtot[1] + s_wtot[2] + s_wtot[3];
+#pragma unroll
+    for (int x = 0; x < kUpdWindow / 256; ++x) {
+      const bool in = kk[x] < (uint32_t)kUpdClusters;
+      const uint64_t m = __ballot(in);
+      if (in) {
+        const int pos = run + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+        s_tmp[pos] = (uint16_t)(((tid + 256 * x) << 3) | kk[x]);
+      }
+      run += __popcll(m);
+    }
+    __syncthreads();
+    for (int e = tid; e < n_mem; e += 256) atomicAdd(&s_cnt[s_tmp[e] & 7], 1);
+    __syncthreads();
+    if (tid == 0) {
+      int a = 0;
+      for (int k = 0; k < kUpdClusters; ++k) {
+        s_off[k] = a;
+        s_cur[k] = a;
+        a += s_cnt[k];
+      }
+      s_off[kUpdClusters] = a;
+    }
+    __syncthreads();
+    for (int e = tid; e < n_mem; e += 256) {
+      const uint32_t v = s_tmp[e];
+      s_mem[atomicAdd(&s_cur[v & 7], 1)] = (uint16_t)(v >> 3);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int cc = 0; cc < 2; ++cc) {
+      const int k = wave * 2 + cc;
+      const int m0 = s_off[k], m1 = s_off[k + 1];
+      total[cc] += m1 - m0;
+      if (plain) {
+        double s0 = 0.0, s1 = 0.0;
+        u16x2 mx = {0, 0}, mn = {0xFFFF, 0xFFFF};          // magnitudes: max, and min nonzero - 1
+        for (int m = m0; m < m1; m += 16) {
+          float vx[16], vy[16];
+          uint32_t raw[16];
+#pragma unroll
+          for (int q = 0; q < 16; ++q) raw[q] = row_pair(t0, min(m + q, m1 - 1), vx[q], vy[q]);
+#pragma unroll
+          for (int q = 0; q < 16; ++q) {
+            if (m + q < m1) {
+              s0 += (double)vx[q];
+              s1 += (double)vy[q];
+              const u16x2 mag = __builtin_bit_cast(u16x2, raw[q] & 0x7FFF7FFFu);
+              const u16x2 one = {1, 1};
+              mx = __builtin_elementwise_max(mx, mag);
+              mn = __builtin_elementwise_min(mn, mag - one);    // a zero wraps to 0xFFFF: ignored
+            }
+          }
+        }
+        const int lg = 32 - __builtin_clz((unsigned)max(m1 - m0, 1));   // >= ceil(log2 n)
+        bool exact[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const int emax = (int)(mx[e] >> 7), nz = (int)mn[e] + 1;      // nz: smallest nonzero magnitude
+          const int emin = max((nz >> 7) & 0xFF, 1);                     // subnormals share exponent 1's unit
+          exact[e] = mn[e] == 0xFFFF || (emax < 0xFF && emax - emin + lg <= 44);
+        }
+        acc[cc][0] = DD{s0, 0.0};
+        acc[cc][1] = DD{s1, 0.0};
+        if (__any(!exact[0] || !exact[1])) {              // rare: redo this cluster exactly
+          DD a0{0.0, 0.0}, a1{0.0, 0.0};
+          dd_rows(t0, m0, m1, a0, a1);
+          if (!exact[0]) acc[cc][0] = a0;
+          if (!exact[1]) acc[cc][1] = a1;
+        }
+      } else {
+        dd_rows(t0, m0, m1, acc[cc][0], acc[cc][1]);
       }
     }
+    __syncthreads();                           // the lists are rebuilt for the next window
   }
-  sd[wave][lane][0] = a0.hi;
-  sd[wave][lane][1] = a0.lo;
-  sd[wave][lane][2] = a1.hi;
-  sd[wave][lane][3] = a1.lo;
-  __syncthreads();
-  if (wave == 0) {
-    DD t0{sd[0][lane][0], sd[0][lane][1]}, t1{sd[0][lane][2], sd[0][lane][3]};
 #pragma unroll
-    for (int w = 1; w < 4; ++w) {
-      t0.add(DD{sd[w][lane][0], sd[w][lane][1]});
-      t1.add(DD{sd[w][lane][2], sd[w][lane][3]});
-    }
-    float* cr = c + ((int64_t)h * C + j) * kHeadDim + lane * 2;
-    const float c0 = (float)(t0.hi / (double)n);
-    const float c1 = (float)(t1.hi / (double)n);
-    cr[0] = c0;
-    cr[1] = c1;
-    if (planes) {   // operand planes and weighted norm for the next assign
+  for (int cc = 0; cc < 2; ++cc) {
+    const int j = c0 + wave * 2 + cc;
+    if (j >= C) continue;
+    const int n = total[cc];
+    if (counts && lane == 0) counts[h * C + j] = n;
+    if (n == 0) continue;
+    const float cv[2] = {(float)(acc[cc][0].hi / (double)n), (float)(acc[cc][1].hi / (double)n)};
+    *reinterpret_cast<float2*>(c + ((int64_t)h * C + j) * kHeadDim + lane * 2) = make_float2(cv[0], cv[1]);
+    if (planes) {   // operand planes (-2 w c) and weighted norm for the next assign
       double nrm = 0.0;
-      uint16_t* ph = planes + ((int64_t)h * 2 * C + j) * kHeadDim + lane * 2;
-      uint16_t* pl = planes + ((int64_t)h * 2 * C + C + j) * kHeadDim + lane * 2;
-      const float cv[2] = {c0, c1};
+      uint32_t hw = 0, lw = 0;
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
         const float wv = w ? w[h * kHeadDim + lane * 2 + e] : 1.0f;
-        const float b = wv * cv[e];
+        const float b = -2.0f * (wv * cv[e]);
         const uint32_t hi = f32_to_bf16_bits(b);
-        ph[e] = (uint16_t)hi;
-        pl[e] = (uint16_t)f32_to_bf16_bits(b - bf16_bits_to_f32(hi));
+        hw |= hi << (16 * e);
+        lw |= f32_to_bf16_bits(b - bf16_bits_to_f32(hi)) << (16 * e);
         nrm += (double)wv * ((double)cv[e] * (double)cv[e]);
       }
+      *reinterpret_cast<uint32_t*>(planes + ((int64_t)h * 2 * C + j) * kHeadDim + lane * 2) = hw;
+      *reinterpret_cast<uint32_t*>(planes + ((int64_t)h * 2 * C + C + j) * kHeadDim + lane * 2) = lw;
 #pragma unroll
       for (int off = 32; off > 0; off >>= 1) nrm += __shfl_xor(nrm, off);
       if (lane == 0) cn[h * C + j] = (float)nrm;
@@ -460,10 +580,10 @@ hipError_t launch_kmeans_assign(const TensorView& y, int H, int C, const uint16_
   const int tiles = (int)((y.n_tokens + kAssignTokens - 1) / kAssignTokens);
   const dim3 grid(tiles * H);
   if (y.dtype == 0)
-    hipLaunchKernelGGL(k_assign<true>, grid, dim3(256), 0, s, y, C, tiles, H, planes, cn, w, labels, amb_count,
+    hipLaunchKernelGGL(k_assign_f32, grid, dim3(256), 0, s, y, C, tiles, H, planes, cn, w, labels, amb_count,
                        amb_list);
   else
-    hipLaunchKernelGGL(k_assign<false>, grid, dim3(256), 0, s, y, C, tiles, H, planes, cn, w, labels, amb_count,
+    hipLaunchKernelGGL(k_assign_bf16, grid, dim3(256), 0, s, y, C, tiles, H, planes, cn, w, labels, amb_count,
                        amb_list);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -476,14 +596,13 @@ hipError_t launch_kmeans_assign(const TensorView& y, int H, int C, const uint16_
 }
 
 hipError_t launch_kmeans_update(const TensorView& y, int H, int C, const uint8_t* labels, float* c,
-                                int32_t* counts, int32_t* start, int32_t* order, const float* w,
-                                uint16_t* planes, float* cn, int* amb_count, hipStream_t s) {
-  hipLaunchKernelGGL(k_sort, dim3(H), dim3(1024), 0, s, (int)y.n_tokens, C, labels, start, order, counts, amb_count);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const dim3 grid(H * C);
-  if (y.dtype == 0) hipLaunchKernelGGL(k_sum<true>, grid, dim3(256), 0, s, y, C, H, start, order, c, w, planes, cn);
-  else hipLaunchKernelGGL(k_sum<false>, grid, dim3(256), 0, s, y, C, H, start, order, c, w, planes, cn);
+                                int32_t* counts, const float* w, uint16_t* planes, float* cn, int* amb_count,
+                                hipStream_t s) {
+  const dim3 grid((unsigned)(H * ((C + kUpdClusters - 1) / kUpdClusters)));
+  if (y.dtype == 0)
+    hipLaunchKernelGGL(k_update<true>, grid, dim3(256), 0, s, y, C, H, labels, c, w, planes, cn, counts, amb_count);
+  else
+    hipLaunchKernelGGL(k_update<false>, grid, dim3(256), 0, s, y, C, H, labels, c, w, planes, cn, counts, amb_count);
   return hipGetLastError();
 }
 

@@ -147,7 +147,7 @@ TensorView view_of(const qkv_tensor* t) {
 
 // ---- workspace plans ----
 struct QuantWs {
-  uint64_t c, planes, cn, start, order, amb_count, amb_list, ybuf0, ybuf1, bytes;
+  uint64_t c, planes, cn, amb_count, amb_list, ybuf0, ybuf1, bytes;
 };
 
 QuantWs quant_ws(const qkv_config* c, int64_t n) {
@@ -157,8 +157,6 @@ QuantWs quant_ws(const qkv_config* c, int64_t n) {
   w.c = off;       off += align256(H * C * kHeadDim * 4);
   w.planes = off;  off += align256(H * 2 * C * kHeadDim * 2);
   w.cn = off;      off += align256(H * C * 4);
-  w.start = off;   off += align256(H * (C + 1) * 4);
-  w.order = off;   off += align256(H * (uint64_t)n * 4);
   w.amb_count = off; off += 256;
   w.amb_list = off; off += align256(H * (uint64_t)n * 8);
   w.ybuf0 = off;   if (c->n_stages > 1) off += align256(H * (uint64_t)n * kHeadDim * 4);
@@ -256,8 +254,6 @@ int run_kmeans(const qkv_config* cfg, const TensorView& y, const float* w, uint8
   float* c = reinterpret_cast<float*>(at(workspace, ws.c));
   uint16_t* planes = reinterpret_cast<uint16_t*>(at(workspace, ws.planes));
   float* cn = reinterpret_cast<float*>(at(workspace, ws.cn));
-  int32_t* start = reinterpret_cast<int32_t*>(at(workspace, ws.start));
-  int32_t* order = reinterpret_cast<int32_t*>(at(workspace, ws.order));
   int* amb = reinterpret_cast<int*>(at(workspace, ws.amb_count));
   int64_t* amb_list = reinterpret_cast<int64_t*>(at(workspace, ws.amb_list));
   QKV_HIP(launch_kmeans_init(y, H, C, c, s));
@@ -265,7 +261,7 @@ int run_kmeans(const qkv_config* cfg, const TensorView& y, const float* w, uint8
   for (int it = 0; it < cfg->kmeans_iters; ++it) {
     const bool last = it + 1 == cfg->kmeans_iters;
     QKV_HIP(launch_kmeans_assign(y, H, C, planes, cn, c, w, labels, amb, amb_list, s));
-    QKV_HIP(launch_kmeans_update(y, H, C, labels, c, nullptr, start, order, w, last ? nullptr : planes, cn, amb, s));
+    QKV_HIP(launch_kmeans_update(y, H, C, labels, c, nullptr, w, last ? nullptr : planes, cn, amb, s));
   }
   return QKV_OK;
 }
@@ -588,10 +584,9 @@ int qkv_kmeans_update(const qkv_config* cfg, const qkv_tensor* y, const uint8_t*
   if (!centroids || !labels) return fail(QKV_EINVAL, "%s: centroids/labels NULL", fn);
   const QuantWs ws = quant_ws(cfg, y->n_tokens);
   QKV_TRY(check_ws(workspace, workspace_bytes, ws.ybuf0, fn));
-  QKV_HIP(launch_kmeans_update(view_of(y), cfg->n_heads, cfg->n_clusters, labels, centroids, counts,
-                               reinterpret_cast<int32_t*>(at(workspace, ws.start)),
-                               reinterpret_cast<int32_t*>(at(workspace, ws.order)), nullptr, nullptr, nullptr,
-                               reinterpret_cast<int*>(at(workspace, ws.amb_count)), reinterpret_cast<hipStream_t>(stream)));
+  QKV_HIP(launch_kmeans_update(view_of(y), cfg->n_heads, cfg->n_clusters, labels, centroids, counts, nullptr,
+                               nullptr, nullptr, reinterpret_cast<int*>(at(workspace, ws.amb_count)),
+                               reinterpret_cast<hipStream_t>(stream)));
   return ok();
 }
 
