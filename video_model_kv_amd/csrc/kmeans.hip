@@ -145,10 +145,18 @@ __device__ __forceinline__ void assign_body(TensorView y, int C, int tiles_per_h
         yh[t][s] = as_bf16x8(raw[t][s]);
         const uint32_t r4[4] = {raw[t][s].x, raw[t][s].y, raw[t][s].z, raw[t][s].w};
         const int ch = s * 16 + half * 8;
+        if (w == nullptr) {                      // sum of squares by packed bf16 dot products
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float v = bf16_bits_to_f32((r4[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
-          ynorm[t] += sW[ch + e] * (v * v);
+          for (int e = 0; e < 4; ++e) {
+            const bf16x2 p = __builtin_bit_cast(bf16x2, r4[e]);
+            ynorm[t] = __builtin_amdgcn_fdot2_f32_bf16(p, p, ynorm[t], false);
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float v = bf16_bits_to_f32((r4[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
+            ynorm[t] += sW[ch + e] * (v * v);
+          }
         }
       }
     }
@@ -315,19 +323,17 @@ __global__ __launch_bounds__(256) void k_refine(TensorView y, int C, const float
     if (j < C) {
       dist = 0.0;
       const float4* crow = reinterpret_cast<const float4*>(cent + ((int64_t)h * C + j) * kHeadDim);
-      for (int kb = 0; kb < kHeadDim / 32; ++kb) {
-        float4 cv[8];
+      float4 cv[kHeadDim / 4];                   // the whole row in flight at once
 #pragma unroll
-        for (int x = 0; x < 8; ++x) cv[x] = crow[kb * 8 + x];
+      for (int x = 0; x < kHeadDim / 4; ++x) cv[x] = crow[x];
 #pragma unroll
-        for (int x = 0; x < 8; ++x) {
-          const float c4[4] = {cv[x].x, cv[x].y, cv[x].z, cv[x].w};
+      for (int x = 0; x < kHeadDim / 4; ++x) {
+        const float c4[4] = {cv[x].x, cv[x].y, cv[x].z, cv[x].w};
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int k = kb * 32 + x * 4 + q;
-            const double diff = (double)sY[k] - (double)c4[q];
-            dist = dist + (double)sW[k] * (diff * diff);
-          }
+        for (int q = 0; q < 4; ++q) {
+          const int k = x * 4 + q;
+          const double diff = (double)sY[k] - (double)c4[q];
+          dist = dist + (double)sW[k] * (diff * diff);
         }
       }
     }
@@ -481,15 +487,17 @@ __global__ __launch_bounds__(256) void k_update(TensorView y, int C, int n_heads
         double s0 = 0.0, s1 = 0.0;
         u16x2 mx = {0, 0}, mn = {0xFFFF, 0xFFFF};          // magnitudes: max, and min nonzero - 1
         for (int m = m0; m < m1; m += 16) {
-          float vx[16], vy[16];
-          uint32_t raw[16];
+          uint32_t raw[16];                                 // bf16 pairs (channels lane*2, +1)
 #pragma unroll
-          for (int q = 0; q < 16; ++q) raw[q] = row_pair(t0, min(m + q, m1 - 1), vx[q], vy[q]);
+          for (int q = 0; q < 16; ++q) {
+            const int64_t off = (int64_t)(t0 + s_mem[min(m + q, m1 - 1)]) * y.stride_token + hoff;
+            raw[q] = *reinterpret_cast<const uint32_t*>(reinterpret_cast<const uint16_t*>(y.ptr) + off);
+          }
 #pragma unroll
           for (int q = 0; q < 16; ++q) {
             if (m + q < m1) {
-              s0 += (double)vx[q];
-              s1 += (double)vy[q];
+              s0 += (double)bf16_bits_to_f32(raw[q] & 0xFFFFu);
+              s1 += (double)bf16_bits_to_f32(raw[q] >> 16);
               const u16x2 mag = __builtin_bit_cast(u16x2, raw[q] & 0x7FFF7FFFu);
               const u16x2 one = {1, 1};
               mx = __builtin_elementwise_max(mx, mag);
