@@ -147,9 +147,6 @@ __device__ __forceinline__ void decode_pairs_f16(uint32_t t, float S, const uint
   }
 }
 
-typedef __attribute__((address_space(3))) void* lds_ptr;
-typedef __attribute__((address_space(1))) void* glb_ptr;
-
 // Asynchronous global -> LDS copy: every active lane moves BYTES bytes from its
 // own address to dst + lane * BYTES (dst is wave-uniform).  Tracked by vmcnt.
 template <int BYTES>

@@ -80,4 +80,22 @@ __device__ __forceinline__ uint32_t xcd_remap(uint32_t linear, uint32_t total) {
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
 
+// s_waitcnt immediates (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt
+// 6:4, lgkmcnt 11:8): wait for vmcnt <= n only, or for lgkmcnt == 0 only
+constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0F70; }
+constexpr int kWaitLgkm0 = 0xC07F;
+
+typedef __attribute__((address_space(3))) void* lds_ptr;
+typedef __attribute__((address_space(1))) void* glb_ptr;
+
+// Asynchronous global -> LDS copy of 16 bytes per lane: lane i's bytes land at
+// dst + 16 i (dst wave-uniform).  Tracked by vmcnt; a workgroup barrier after
+// the wait makes them visible to the other waves.
+__device__ __forceinline__ void dma16(const void* src, void* dst) {
+  __builtin_amdgcn_global_load_lds((glb_ptr)const_cast<void*>(src), (lds_ptr)dst, 16, 0, 0);
+}
+__device__ __forceinline__ void dma4(const void* src, void* dst) {   // 4 bytes per lane at dst + 4 i
+  __builtin_amdgcn_global_load_lds((glb_ptr)const_cast<void*>(src), (lds_ptr)dst, 4, 0, 0);
+}
+
 }  // namespace qkv

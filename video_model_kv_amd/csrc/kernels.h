@@ -29,11 +29,12 @@ struct ChannelCode {
 hipError_t launch_kmeans_init(const TensorView& y, int H, int C, float* c, hipStream_t s);
 hipError_t launch_centroid_prep(int H, int C, const float* c, const float* w, uint16_t* planes,
                                 float* cn, int* amb_count, hipStream_t s);
-// Assign = MFMA screening (labels) + float64 re-decision of queued close calls.
-// amb_count (zeroed by the preceding prep or sort) and amb_list [H*N] are workspace.
+// Assign = MFMA screening (labels) + float64 re-decision of the close calls,
+// in one kernel.  amb_count (zeroed by the preceding prep or update; may be
+// null) receives the number of close calls.
 hipError_t launch_kmeans_assign(const TensorView& y, int H, int C, const uint16_t* planes,
                                 const float* cn, const float* c, const float* w, uint8_t* labels,
-                                int* amb_count, int64_t* amb_list, hipStream_t s);
+                                int* amb_count, hipStream_t s);
 // Update = grouping of the tokens by label (in LDS) + exact per-cluster sums;
 // when planes != null it also refreshes the operand planes / norms for the
 // next assign.  Zeroes amb_count.

@@ -18,6 +18,9 @@
 // every token whose two best screened values are closer than 2e-5 of that
 // scale is re-decided from float64 distances accumulated in channel order, so
 // the labels are those of the float64 definition (ties to the lowest index).
+#include <algorithm>
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -25,7 +28,6 @@ namespace qkv {
 
 namespace {
 
-constexpr int kAssignTokens = 256;   // 4 waves x 64 tokens
 constexpr int kPitch = 136;          // LDS row pitch (bf16): 128 + 8 keeps ds_read_b128 conflict-free
 
 template <bool F32>
@@ -78,281 +80,341 @@ __global__ __launch_bounds__(64) void k_prep(int C, const float* __restrict__ c,
   if (lane == 0) cn[h * C + j] = (float)nrm;
 }
 
-template <bool F32>
-__device__ __forceinline__ void assign_body(TensorView y, int C, int tiles_per_head, int n_heads,
-                                            const uint16_t* __restrict__ planes, const float* __restrict__ cn,
-                                            const float* __restrict__ w, uint8_t* __restrict__ labels,
-                                            int* __restrict__ amb_count, int64_t* __restrict__ amb_list) {
-  __shared__ __attribute__((aligned(16))) uint16_t sA[2][2][32][kPitch];
-  __shared__ float sCn[2][32];
-  __shared__ __attribute__((aligned(16))) float sW[kHeadDim];
-  const uint32_t logical = xcd_remap(blockIdx.x, (uint32_t)(tiles_per_head * n_heads));
-  const int h = logical / tiles_per_head, tile = logical % tiles_per_head;
-  const int N = (int)y.n_tokens;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int col = lane & 31, half = lane >> 5;
-  if (threadIdx.x < kHeadDim) sW[threadIdx.x] = w ? w[h * kHeadDim + threadIdx.x] : 1.0f;
-  __syncthreads();
+// Assign: one workgroup per (head, range of 32-token sub-blocks), eight waves.
+// The head's operand planes (2 x C rows of 128 bf16, ~136 KB padded) are
+// loaded into LDS once and stay resident; each wave then sweeps all centroid
+// blocks for 64 tokens at a time (32 for an odd last sub-block), with the next
+// tokens' loads in flight.  Close calls go to an LDS list, flushed to the
+// global queue with one atomic per workgroup.
+constexpr int kAsgWaves = 8;
+constexpr int kAsgThreads = kAsgWaves * 64;
+constexpr int kAsgMaxC = 256;
+constexpr int kAsgMaxSub = 32;        // sub-blocks per workgroup at most (LDS close-call list)
+constexpr int kAsgCUs = 256;
 
-  // B operand (tokens): lane holds token `col` of sub-block t, channels s*16 + half*8 + [0, 8).
-  // ynorm[t] accumulates sum_k w_k y_k^2 over the lane's channels (fp32; it only
-  // sets the screening threshold).
-  bf16x8 yh[2][8];
-  bf16x8 yl[2][F32 ? 8 : 1];
-  float ynorm[2] = {0.0f, 0.0f};
-  if constexpr (F32) {
+template <bool F32>
+__global__ __launch_bounds__(kAsgThreads) void k_assign(TensorView y, int C, int G, int n_heads,
+                                                      const uint16_t* __restrict__ planes,
+                                                      const float* __restrict__ cn, const float* __restrict__ w,
+                                                      const float* __restrict__ cent, uint8_t* __restrict__ labels,
+                                                      int* __restrict__ amb_count) {
+  __shared__ __attribute__((aligned(16))) uint16_t sP[2][kAsgMaxC][kPitch];
+  __shared__ __attribute__((aligned(16))) float sCn[kAsgMaxC];
+  __shared__ __attribute__((aligned(16))) float sW[kHeadDim];
+  __shared__ int sAmb[kAsgMaxSub * 32];
+  __shared__ int sAmbN;
+  __shared__ __attribute__((aligned(16))) float sYr[4][kHeadDim];
+  __shared__ double sRv[kAsgWaves][4];
+  __shared__ int sRj[kAsgWaves][4];
+  const uint32_t logical = xcd_remap(blockIdx.x, (uint32_t)(G * n_heads));
+  const int h = logical / G, g = logical % G;
+  const int N = (int)y.n_tokens;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int col = lane & 31, half = lane >> 5;
+  const int S = (N + 31) >> 5;
+  const int sb0 = (int)((int64_t)S * g / G), sb1 = (int)((int64_t)S * (g + 1) / G);
+  // each wave takes an even share of the sub-blocks, in items of two (fp32
+  // tokens: one), an odd last one alone
+  constexpr int kPer = F32 ? 1 : 2;
+  const int nsb = sb1 - sb0;
+  const int wsb0 = sb0 + nsb * wave / kAsgWaves, wsb1 = sb0 + nsb * (wave + 1) / kAsgWaves;
+  const int Cp = (C + 31) & ~31;                 // whole 32-row blocks; rows past C never win (norm +inf)
+  const uint16_t* y16 = reinterpret_cast<const uint16_t*>(y.ptr);
+  const int64_t hoff = (int64_t)h * y.stride_head + half * 8;
+
+  // bf16 tokens of one item (nt sub-blocks; clamped rows past N are masked later)
+  uint4 raw[2][8];
+  auto load_tokens = [&](int sb, int nt) __attribute__((always_inline)) {
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-      const int tok = tile * kAssignTokens + wave * 64 + t * 32 + col;
-      const bool ok = tok < N;
-      const int64_t base = (int64_t)(ok ? tok : 0) * y.stride_token + (int64_t)h * y.stride_head;
+      if (t < nt) {                              // wave-uniform
+        const int64_t base = (int64_t)min(sb * 32 + t * 32 + col, N - 1) * y.stride_token + hoff;
 #pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        const int ch = s * 16 + half * 8;
-        const float* p = reinterpret_cast<const float*>(y.ptr) + base + ch;
-        float4 a = *reinterpret_cast<const float4*>(p);       // p is in range (token 0 when !ok)
-        float4 b = *reinterpret_cast<const float4*>(p + 4);
-        if (!ok) a = b = make_float4(0, 0, 0, 0);
-        const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-        u16x8 hi, lo;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const uint32_t hb = f32_to_bf16_bits(v[e]);
-          hi[e] = (uint16_t)hb;
-          lo[e] = (uint16_t)f32_to_bf16_bits(v[e] - bf16_bits_to_f32(hb));
-          ynorm[t] += sW[ch + e] * (v[e] * v[e]);
-        }
-        yh[t][s] = __builtin_bit_cast(bf16x8, hi);
-        yl[t][F32 ? s : 0] = __builtin_bit_cast(bf16x8, lo);
+        for (int s = 0; s < 8; ++s) raw[t][s] = *reinterpret_cast<const uint4*>(y16 + base + s * 16);
       }
     }
-  } else {
-    uint4 raw[2][8];                             // all 16 loads in flight before any use
+  };
+
+  {
+    // Everything reaches LDS by asynchronous copies (norms, weights, the
+    // planes), then the first item's tokens are requested (always 16 loads);
+    // the barrier waits for all but those 16, so no wave waits for another
+    // wave's tokens.
+    if (wave == 0) {
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const int tok = tile * kAssignTokens + wave * 64 + t * 32 + col;
-      const int64_t base = (int64_t)min(tok, N - 1) * y.stride_token + (int64_t)h * y.stride_head;
-#pragma unroll
-      for (int s = 0; s < 8; ++s)
-        raw[t][s] = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(y.ptr) + base + s * 16 + half * 8);
+      for (int q = 0; q < kAsgMaxC / 64; ++q) {
+        const int j = q * 64 + lane;
+        if (j < C) dma4(cn + h * C + j, &sCn[q * 64]);   // lane i lands at sCn[q*64 + i]
+        else if (j < Cp) sCn[j] = INFINITY;
+      }
+    } else if (wave == 1) {
+      if (w) {
+        dma4(w + h * kHeadDim + lane, &sW[0]);        // lane i lands at sW[i]
+        dma4(w + h * kHeadDim + 64 + lane, &sW[64]);
+      } else {
+        sW[lane] = 1.0f;
+        sW[64 + lane] = 1.0f;
+      }
+    } else if (wave == 2 && lane == 0) {
+      sAmbN = 0;
     }
+    // planes: 1 KB of the padded image per wave instruction; pad pieces and
+    // rows in [C, Cp) take copies of valid pieces
+    const uint16_t* ph = planes + (int64_t)h * 2 * C * kHeadDim;
+    constexpr int kPlaneBytes = kAsgMaxC * kPitch * 2;
+    const int nch = (Cp * kPitch * 2 + 1023) >> 10;          // 1 KB chunks per plane
+    for (int k = wave; k < 2 * nch; k += kAsgWaves) {
+      const int p = k >= nch ? 1 : 0;
+      const int a = (k - p * nch) * 1024 + lane * 16;        // byte offset in the plane image
+      const int row = min(a / (kPitch * 2), C - 1), piece = min((a % (kPitch * 2)) >> 4, 15);
+      dma16(ph + ((int64_t)(p * C + row) * kHeadDim + piece * 8),
+            reinterpret_cast<char*>(&sP[0][0][0]) + p * kPlaneBytes + (k - p * nch) * 1024);
+    }
+    asm volatile("" ::: "memory");
+    if constexpr (!F32) load_tokens(wsb0, 2);   // past the wave's range: clamped, unused
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(F32 ? 0 : 16));   // vmcnt counts in issue order
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  }
+
+  for (int sb = wsb0; sb < wsb1; sb += kPer) {
+    const int nt = min(kPer, wsb1 - sb);
+    const int tok0 = sb * 32;
+    // B operand (tokens): lane holds token tok0 + t*32 + col, channels s*16 + half*8 + [0, 8).
+    // ynorm[t] = sum_k w_k y_k^2 over the lane's channels (fp32; it only sets
+    // the screening threshold).
+    bf16x8 yh[2][8];
+    bf16x8 yl[2][F32 ? 8 : 1];
+    float ynorm[2] = {0.0f, 0.0f};
+    if constexpr (F32) {
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const bool ok = tile * kAssignTokens + wave * 64 + t * 32 + col < N;
+      for (int t = 0; t < kPer; ++t) {
+        const int tok = tok0 + t * 32 + col;
+        const bool ok = tok < N;
+        const float* p = reinterpret_cast<const float*>(y.ptr) + (int64_t)min(tok, N - 1) * y.stride_token + hoff;
 #pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        if (!ok) raw[t][s] = make_uint4(0, 0, 0, 0);
-        yh[t][s] = as_bf16x8(raw[t][s]);
-        const uint32_t r4[4] = {raw[t][s].x, raw[t][s].y, raw[t][s].z, raw[t][s].w};
-        const int ch = s * 16 + half * 8;
-        if (w == nullptr) {                      // sum of squares by packed bf16 dot products
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const bf16x2 p = __builtin_bit_cast(bf16x2, r4[e]);
-            ynorm[t] = __builtin_amdgcn_fdot2_f32_bf16(p, p, ynorm[t], false);
-          }
-        } else {
+        for (int s = 0; s < 8; ++s) {
+          const int ch = s * 16 + half * 8;
+          float4 a = *reinterpret_cast<const float4*>(p + s * 16);
+          float4 b = *reinterpret_cast<const float4*>(p + s * 16 + 4);
+          if (!ok) a = b = make_float4(0, 0, 0, 0);
+          const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+          u16x8 hi, lo;
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
-            const float v = bf16_bits_to_f32((r4[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
-            ynorm[t] += sW[ch + e] * (v * v);
+            const uint32_t hb = f32_to_bf16_bits(v[e]);
+            hi[e] = (uint16_t)hb;
+            lo[e] = (uint16_t)f32_to_bf16_bits(v[e] - bf16_bits_to_f32(hb));
+            ynorm[t] += sW[ch + e] * (v[e] * v[e]);
+          }
+          yh[t][s] = __builtin_bit_cast(bf16x8, hi);
+          yl[t][F32 ? s : 0] = __builtin_bit_cast(bf16x8, lo);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const bool ok = tok0 + t * 32 + col < N;
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+          const uint4 r = ok ? raw[t][s] : make_uint4(0, 0, 0, 0);
+          yh[t][s] = as_bf16x8(r);
+          const uint32_t r4[4] = {r.x, r.y, r.z, r.w};
+          const int ch = s * 16 + half * 8;
+          if (w == nullptr) {                    // sum of squares by packed bf16 dot products
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const bf16x2 q = __builtin_bit_cast(bf16x2, r4[e]);
+              ynorm[t] = __builtin_amdgcn_fdot2_f32_bf16(q, q, ynorm[t], false);
+            }
+          } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const float v = bf16_bits_to_f32((r4[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
+              ynorm[t] += sW[ch + e] * (v * v);
+            }
           }
         }
       }
+      if (sb + kPer < wsb1) load_tokens(sb + kPer, min(kPer, wsb1 - sb - kPer));
     }
-  }
 
-  // top-2 of the screened values, branch-free; rows beyond C carry +inf.
-  // Centroid planes stream through double-buffered LDS: the next block's
-  // global loads are issued before the current block's MFMAs.
-  float b1[2] = {INFINITY, INFINITY}, b2[2] = {INFINITY, INFINITY};
-  int bidx[2] = {0, 0};
-  const uint16_t* ph = planes + (int64_t)h * 2 * C * kHeadDim;
-  const int nblk = (C + 31) / 32;
-  // one centroid block (rows cb*32 .. +31 of both planes, and their norms),
-  // fetched into registers one block ahead
-  struct Block {
-    uint4 v0, v1, v2, v3;
-    float cn;
-  };
-  auto fetch = [&](int cb) __attribute__((always_inline)) -> Block {
-    Block B;
-    uint4* dst[4] = {&B.v0, &B.v1, &B.v2, &B.v3};
+    // Sweep of the centroid blocks for NT sub-blocks: running best b1 and
+    // second best b2 of the screened values (b1 <= b2; new b2 = med3(b1, b2, v),
+    // new b1 = min(b1, v)).  rel is the best row relative
+    // to the current block's first row, so each element selects a small
+    // immediate; the lane's row offset half*4 is added at the end.
+    auto sweep = [&](auto nt) __attribute__((always_inline)) {
+      constexpr int NT = decltype(nt)::value;
+      float b1[NT], b2[NT];
+      int rel[NT];
 #pragma unroll
-    for (int x = 0; x < 4; ++x) {
-      const int v = threadIdx.x + x * 256;
-      const int p = v >> 9, r = (v >> 4) & 31, c16 = v & 15;
-      const int j = min(cb * 32 + r, C - 1);   // rows past C: a copy of row C-1, never chosen (norm +inf)
-      *dst[x] = *reinterpret_cast<const uint4*>(ph + ((int64_t)p * C + j) * kHeadDim + c16 * 8);
-    }
-    const int j = cb * 32 + (threadIdx.x & 31);
-    const float v = cn[h * C + min(j, C - 1)];
-    B.cn = j < C ? v : INFINITY;
-    return B;
-  };
-  auto stash = [&](const Block& B, int buf) __attribute__((always_inline)) {
-    const uint4 src[4] = {B.v0, B.v1, B.v2, B.v3};
-#pragma unroll
-    for (int x = 0; x < 4; ++x) {
-      const int v = threadIdx.x + x * 256;
-      const int p = v >> 9, r = (v >> 4) & 31, c16 = v & 15;
-      *reinterpret_cast<uint4*>(&sA[buf][p][r][c16 * 8]) = src[x];
-    }
-    if (threadIdx.x < 32) sCn[buf][threadIdx.x] = B.cn;
-  };
-  stash(fetch(0), 0);
-  __syncthreads();
-  for (int cb = 0; cb < nblk; ++cb) {
-    const int buf = cb & 1;
-    const Block nxt = fetch(min(cb + 1, nblk - 1));   // the last block is fetched twice, stashed once
-    // the accumulators start from ||c_j||_w^2 of their centroid rows: row
-    // (r/4)*8 + half*4 + r%4 of the block for element r
-    f32x16 acc0, acc1;
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const float4 c4 = *reinterpret_cast<const float4*>(&sCn[buf][g * 8 + half * 4]);
-      const float4 d4 = *reinterpret_cast<const float4*>(&sCn[buf][g * 8 + half * 4]);
-      acc0[4 * g] = c4.x;
-      acc0[4 * g + 1] = c4.y;
-      acc0[4 * g + 2] = c4.z;
-      acc0[4 * g + 3] = c4.w;
-      acc1[4 * g] = d4.x;
-      acc1[4 * g + 1] = d4.y;
-      acc1[4 * g + 2] = d4.z;
-      acc1[4 * g + 3] = d4.w;
-    }
-#pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      const bf16x8 ahi = as_bf16x8(*reinterpret_cast<const uint4*>(&sA[buf][0][col][s * 16 + half * 8]));
-      const bf16x8 alo = as_bf16x8(*reinterpret_cast<const uint4*>(&sA[buf][1][col][s * 16 + half * 8]));
-      acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahi, yh[0][s], acc0, 0, 0, 0);
-      acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahi, yh[1][s], acc1, 0, 0, 0);
-      acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(alo, yh[0][s], acc0, 0, 0, 0);
-      acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(alo, yh[1][s], acc1, 0, 0, 0);
-      if constexpr (F32) {
-        acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahi, yl[0][F32 ? s : 0], acc0, 0, 0, 0);
-        acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahi, yl[1][F32 ? s : 0], acc1, 0, 0, 0);
+      for (int t = 0; t < NT; ++t) {
+        b1[t] = INFINITY;
+        b2[t] = INFINITY;
+        rel[t] = 32;
       }
-    }
-    // Output layout: lane holds token `col`, centroid rows (r/4)*8 + half*4 + r%4
-    // (increasing in r), so strict '<' keeps the lowest index among equal values.
-    // Running best b1 and second best b2 (b1 <= b2): new b2 = med3(b1, b2, v).
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int j = cb * 32 + (r >> 2) * 8 + half * 4 + (r & 3);
-      const float v0 = acc0[r], v1 = acc1[r];
-      const bool l0 = v0 < b1[0], l1 = v1 < b1[1];
-      b2[0] = __builtin_amdgcn_fmed3f(b1[0], b2[0], v0);
-      b2[1] = __builtin_amdgcn_fmed3f(b1[1], b2[1], v1);
-      b1[0] = fminf(b1[0], v0);
-      b1[1] = fminf(b1[1], v1);
-      bidx[0] = l0 ? j : bidx[0];
-      bidx[1] = l1 ? j : bidx[1];
-    }
-    if (cb + 1 < nblk) stash(nxt, buf ^ 1);
-    __syncthreads();
-  }
-#pragma unroll
-  for (int t = 0; t < 2; ++t) {
-    const float o1 = __shfl_xor(b1[t], 32), o2 = __shfl_xor(b2[t], 32);
-    const int oi = __shfl_xor(bidx[t], 32);
-    const float second = fminf(fmaxf(b1[t], o1), fminf(b2[t], o2));
-    if (o1 < b1[t] || (o1 == b1[t] && oi < bidx[t])) { b1[t] = o1; bidx[t] = oi; }
-    b2[t] = second;
-    ynorm[t] += __shfl_xor(ynorm[t], 32);
-  }
-
-  // Close calls -- the two best screened values within the screening error
-  // bound (generously 2e-5 of ||y||_w^2 + ||c||_w^2) -- are queued for k_refine,
-  // which re-decides them from float64 distances.
-#pragma unroll
-  for (int t = 0; t < 2; ++t) {
-    const int tok = tile * kAssignTokens + wave * 64 + t * 32 + col;
-    if (half == 0 && tok < N) {
-      labels[(int64_t)h * N + tok] = (uint8_t)bidx[t];
-      const float thr = 2e-5f * (ynorm[t] + cn[h * C + bidx[t]]);
-      if (!(b2[t] - b1[t] > thr)) {
-        const int slot = atomicAdd(amb_count, 1);
-        amb_list[slot] = (int64_t)h * N + tok;
-      }
-    }
-  }
-}
-
-// bf16 tokens: two waves per SIMD; fp32 tokens (a second operand plane) one.
-__global__ __launch_bounds__(256, 2) void k_assign_bf16(TensorView y, int C, int tiles_per_head, int n_heads,
-                                                     const uint16_t* __restrict__ planes, const float* __restrict__ cn,
-                                                     const float* __restrict__ w, uint8_t* __restrict__ labels,
-                                                     int* __restrict__ amb_count, int64_t* __restrict__ amb_list) {
-  assign_body<false>(y, C, tiles_per_head, n_heads, planes, cn, w, labels, amb_count, amb_list);
-}
-__global__ __launch_bounds__(256) void k_assign_f32(TensorView y, int C, int tiles_per_head, int n_heads,
-                                                 const uint16_t* __restrict__ planes, const float* __restrict__ cn,
-                                                 const float* __restrict__ w, uint8_t* __restrict__ labels,
-                                                 int* __restrict__ amb_count, int64_t* __restrict__ amb_list) {
-  assign_body<true>(y, C, tiles_per_head, n_heads, planes, cn, w, labels, amb_count, amb_list);
-}
-
-// Float64 re-decision of queued close calls: one block per entry (grid-stride
-// over the device-side count).  Thread j computes sum_k w_k (y_k - c_jk)^2 in
-// channel order; the lowest index wins ties.
-template <bool F32>
-__global__ __launch_bounds__(256) void k_refine(TensorView y, int C, const float* __restrict__ cent,
-                                                const float* __restrict__ w, const int* __restrict__ amb_count,
-                                                const int64_t* __restrict__ amb_list, uint8_t* __restrict__ labels) {
-  __shared__ float sY[kHeadDim];
-  __shared__ float sW[kHeadDim];
-  __shared__ double s_bv[4];
-  __shared__ int s_bj[4];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int N = (int)y.n_tokens;
-  const int count = *amb_count;
-  for (int e = blockIdx.x; e < count; e += gridDim.x) {
-    const int64_t ht = amb_list[e];
-    const int h = (int)(ht / N), tok = (int)(ht % N);
-    __syncthreads();
-    if (threadIdx.x < kHeadDim) {
-      const int64_t off = (int64_t)tok * y.stride_token + (int64_t)h * y.stride_head + threadIdx.x;
-      if constexpr (F32) sY[threadIdx.x] = reinterpret_cast<const float*>(y.ptr)[off];
-      else sY[threadIdx.x] = bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(y.ptr)[off]);
-      sW[threadIdx.x] = w ? w[h * kHeadDim + threadIdx.x] : 1.0f;
-    }
-    __syncthreads();
-    const int j = threadIdx.x;
-    double dist = INFINITY;
-    if (j < C) {
-      dist = 0.0;
-      const float4* crow = reinterpret_cast<const float4*>(cent + ((int64_t)h * C + j) * kHeadDim);
-      float4 cv[kHeadDim / 4];                   // the whole row in flight at once
-#pragma unroll
-      for (int x = 0; x < kHeadDim / 4; ++x) cv[x] = crow[x];
-#pragma unroll
-      for (int x = 0; x < kHeadDim / 4; ++x) {
-        const float c4[4] = {cv[x].x, cv[x].y, cv[x].z, cv[x].w};
+      // MFMAs of block cb; the accumulators start from ||c_j||_w^2 of their
+      // centroid rows: row (r/4)*8 + half*4 + r%4 of the block for element r
+      auto mma = [&](f32x16 (&acc)[NT], int cb) __attribute__((always_inline)) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const int k = x * 4 + q;
-          const double diff = (double)sY[k] - (double)c4[q];
-          dist = dist + (double)sW[k] * (diff * diff);
+          const float4 c4 = *reinterpret_cast<const float4*>(&sCn[cb + q * 8 + half * 4]);
+#pragma unroll
+          for (int t = 0; t < NT; ++t) {
+            acc[t][4 * q] = c4.x;
+            acc[t][4 * q + 1] = c4.y;
+            acc[t][4 * q + 2] = c4.z;
+            acc[t][4 * q + 3] = c4.w;
+          }
+        }
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+          const bf16x8 ahi = as_bf16x8(*reinterpret_cast<const uint4*>(&sP[0][cb + col][s * 16 + half * 8]));
+          const bf16x8 alo = as_bf16x8(*reinterpret_cast<const uint4*>(&sP[1][cb + col][s * 16 + half * 8]));
+#pragma unroll
+          for (int t = 0; t < NT; ++t) acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahi, yh[t][s], acc[t], 0, 0, 0);
+#pragma unroll
+          for (int t = 0; t < NT; ++t) acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(alo, yh[t][s], acc[t], 0, 0, 0);
+          if constexpr (F32) {
+#pragma unroll
+            for (int t = 0; t < NT; ++t)
+              acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahi, yl[t][F32 ? s : 0], acc[t], 0, 0, 0);
+          }
+        }
+      };
+      // rows increase with r within the lane, so strict '<' keeps the lowest
+      // index among equal values
+      auto top2 = [&](const f32x16 (&acc)[NT]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int t = 0; t < NT; ++t) rel[t] -= 32;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int j = (r >> 2) * 8 + (r & 3);
+#pragma unroll
+          for (int t = 0; t < NT; ++t) {
+            const float v = acc[t][r];
+            const bool l = v < b1[t];
+            b2[t] = __builtin_amdgcn_fmed3f(b1[t], b2[t], v);
+            b1[t] = l ? v : b1[t];               // a select: min() would first quiet v
+            rel[t] = l ? j : rel[t];
+          }
+        }
+      };
+      for (int cb = 0; cb < Cp; cb += 32) {
+        f32x16 acc[NT];
+        mma(acc, cb);
+        top2(acc);
+      }
+      int bidx[NT];
+#pragma unroll
+      for (int t = 0; t < NT; ++t) bidx[t] = rel[t] + Cp - 32 + half * 4;
+      // Close calls -- the two best screened values within the screening
+      // error bound (generously 2e-5 of ||y||_w^2 + ||c||_w^2) -- are listed
+      // for the float64 re-decision at the end.
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const float o1 = __shfl_xor(b1[t], 32), o2 = __shfl_xor(b2[t], 32);
+        const int oi = __shfl_xor(bidx[t], 32);
+        const float second = fminf(fmaxf(b1[t], o1), fminf(b2[t], o2));
+        if (o1 < b1[t] || (o1 == b1[t] && oi < bidx[t])) {
+          b1[t] = o1;
+          bidx[t] = oi;
+        }
+        const float yn = ynorm[t] + __shfl_xor(ynorm[t], 32);
+        const int tok = tok0 + t * 32 + col;
+        if (half == 0 && tok < N) {
+          labels[(int64_t)h * N + tok] = (uint8_t)bidx[t];
+          const float thr = 2e-5f * (yn + sCn[bidx[t]]);
+          if (!(second - b1[t] > thr)) {
+            const int slot = atomicAdd(&sAmbN, 1);
+            if (slot < kAsgMaxSub * 32) sAmb[slot] = tok;
+          }
         }
       }
+    };
+    if constexpr (F32) {
+      sweep(std::integral_constant<int, 1>{});
+    } else {
+      if (nt == 2) sweep(std::integral_constant<int, 2>{});
+      else sweep(std::integral_constant<int, 1>{});
     }
-    double bv = dist;
-    int bj = j;
+  }
+
+  // Close calls re-decided from float64 distances sum_k w_k (y_k - c_jk)^2,
+  // four tokens at a time: thread t holds half (t & 1) of centroid row t >> 1
+  // (fp32) and accumulates its 64 channels for each token; the
+  // halves are joined, then the lowest distance wins, ties to the lowest index.
+  __syncthreads();
+  const int n_amb = min(sAmbN, kAsgMaxSub * 32);
+  if (n_amb > 0) {
+    if (tid == 0 && amb_count) atomicAdd(amb_count, n_amb);   // statistics only
+    const int j = tid >> 1, hk = (tid & 1) * 64;
+    const float* cr = cent + ((int64_t)h * C + min(j, C - 1)) * kHeadDim + hk;
+    for (int e0 = 0; e0 < n_amb; e0 += 4) {
+      {
+        const int q = tid >> 7, k = tid & 127;                // 4 tokens x 128 channels
+        const int tok = sAmb[min(e0 + q, n_amb - 1)];
+        const int64_t off = (int64_t)tok * y.stride_token + (int64_t)h * y.stride_head + k;
+        sYr[q][k] = F32 ? reinterpret_cast<const float*>(y.ptr)[off] : bf16_bits_to_f32(y16[off]);
+      }
+      __syncthreads();
+      double d[4] = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll 1
+      for (int x0 = 0; x0 < 64; x0 += 16) {          // 16 channels of the row half per step
+        float4 c4[4];
 #pragma unroll
-    for (int off = 32; off > 0; off >>= 1) {
-      const double ov = __shfl_xor(bv, off);
-      const int oj = __shfl_xor(bj, off);
-      if (ov < bv || (ov == bv && oj < bj)) { bv = ov; bj = oj; }
-    }
-    if (lane == 0) { s_bv[wave] = bv; s_bj[wave] = bj; }
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      double v = s_bv[0];
-      int jj = s_bj[0];
-      for (int x = 1; x < 4; ++x)
-        if (s_bv[x] < v || (s_bv[x] == v && s_bj[x] < jj)) { v = s_bv[x]; jj = s_bj[x]; }
-      labels[ht] = (uint8_t)jj;
+        for (int x = 0; x < 4; ++x) c4[x] = *reinterpret_cast<const float4*>(cr + x0 + 4 * x);
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+          const float cv[4] = {c4[x].x, c4[x].y, c4[x].z, c4[x].w};
+          const float4 w4 = *reinterpret_cast<const float4*>(&sW[hk + x0 + 4 * x]);
+          const float wv4[4] = {w4.x, w4.y, w4.z, w4.w};
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const float4 y4 = *reinterpret_cast<const float4*>(&sYr[q][hk + x0 + 4 * x]);
+            const float yv4[4] = {y4.x, y4.y, y4.z, y4.w};
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+              const double diff = (double)yv4[u] - (double)cv[u];
+              d[q] += (double)wv4[u] * (diff * diff);
+            }
+          }
+        }
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        double v = d[q] + __shfl_xor(d[q], 1);
+        int bj = j;
+        if (j >= C) v = INFINITY;
+#pragma unroll
+        for (int off = 2; off < 64; off <<= 1) {
+          const double ov = __shfl_xor(v, off);
+          const int oj = __shfl_xor(bj, off);
+          if (ov < v || (ov == v && oj < bj)) {
+            v = ov;
+            bj = oj;
+          }
+        }
+        if (lane == 0) {
+          sRv[wave][q] = v;
+          sRj[wave][q] = bj;
+        }
+      }
+      __syncthreads();
+      if (tid < 4 && e0 + tid < n_amb) {
+        double v = sRv[0][tid];
+        int bj = sRj[0][tid];
+        for (int x = 1; x < kAsgWaves; ++x)
+          if (sRv[x][tid] < v || (sRv[x][tid] == v && sRj[x][tid] < bj)) {
+            v = sRv[x][tid];
+            bj = sRj[x][tid];
+          }
+        labels[(int64_t)h * N + sAmb[e0 + tid]] = (uint8_t)bj;
+      }
+      __syncthreads();
     }
   }
 }
@@ -584,22 +646,20 @@ hipError_t launch_centroid_prep(int H, int C, const float* c, const float* w, ui
 
 hipError_t launch_kmeans_assign(const TensorView& y, int H, int C, const uint16_t* planes,
                                 const float* cn, const float* c, const float* w, uint8_t* labels,
-                                int* amb_count, int64_t* amb_list, hipStream_t s) {
-  const int tiles = (int)((y.n_tokens + kAssignTokens - 1) / kAssignTokens);
-  const dim3 grid(tiles * H);
+                                int* amb_count, hipStream_t s) {
+  if (C > kAsgMaxC) return hipErrorInvalidValue;
+  // workgroups per head: about one per compute unit overall, at least 16
+  // sub-blocks each where the head has them, at most kAsgMaxSub
+  const int S = (int)((y.n_tokens + 31) / 32);
+  int G = std::min((S + 15) / 16, std::max(1, kAsgCUs / H));
+  G = std::max(G, (S + kAsgMaxSub - 1) / kAsgMaxSub);
+  const dim3 grid((unsigned)(G * H));
   if (y.dtype == 0)
-    hipLaunchKernelGGL(k_assign_f32, grid, dim3(256), 0, s, y, C, tiles, H, planes, cn, w, labels, amb_count,
-                       amb_list);
+    hipLaunchKernelGGL(k_assign<true>, grid, dim3(kAsgThreads), 0, s, y, C, G, H, planes, cn, w, c, labels,
+                       amb_count);
   else
-    hipLaunchKernelGGL(k_assign_bf16, grid, dim3(256), 0, s, y, C, tiles, H, planes, cn, w, labels, amb_count,
-                       amb_list);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const dim3 rgrid(256);
-  if (y.dtype == 0)
-    hipLaunchKernelGGL(k_refine<true>, rgrid, dim3(256), 0, s, y, C, c, w, amb_count, amb_list, labels);
-  else
-    hipLaunchKernelGGL(k_refine<false>, rgrid, dim3(256), 0, s, y, C, c, w, amb_count, amb_list, labels);
+    hipLaunchKernelGGL(k_assign<false>, grid, dim3(kAsgThreads), 0, s, y, C, G, H, planes, cn, w, c, labels,
+                       amb_count);
   return hipGetLastError();
 }
 

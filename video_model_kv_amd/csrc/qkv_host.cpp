@@ -147,7 +147,7 @@ TensorView view_of(const qkv_tensor* t) {
 
 // ---- workspace plans ----
 struct QuantWs {
-  uint64_t c, planes, cn, amb_count, amb_list, ybuf0, ybuf1, bytes;
+  uint64_t c, planes, cn, amb_count, ybuf0, ybuf1, bytes;
 };
 
 QuantWs quant_ws(const qkv_config* c, int64_t n) {
@@ -158,7 +158,6 @@ QuantWs quant_ws(const qkv_config* c, int64_t n) {
   w.planes = off;  off += align256(H * 2 * C * kHeadDim * 2);
   w.cn = off;      off += align256(H * C * 4);
   w.amb_count = off; off += 256;
-  w.amb_list = off; off += align256(H * (uint64_t)n * 8);
   w.ybuf0 = off;   if (c->n_stages > 1) off += align256(H * (uint64_t)n * kHeadDim * 4);
   w.ybuf1 = off;   if (c->n_stages > 2) off += align256(H * (uint64_t)n * kHeadDim * 4);
   w.bytes = off;
@@ -255,12 +254,11 @@ int run_kmeans(const qkv_config* cfg, const TensorView& y, const float* w, uint8
   uint16_t* planes = reinterpret_cast<uint16_t*>(at(workspace, ws.planes));
   float* cn = reinterpret_cast<float*>(at(workspace, ws.cn));
   int* amb = reinterpret_cast<int*>(at(workspace, ws.amb_count));
-  int64_t* amb_list = reinterpret_cast<int64_t*>(at(workspace, ws.amb_list));
   QKV_HIP(launch_kmeans_init(y, H, C, c, s));
   QKV_HIP(launch_centroid_prep(H, C, c, w, planes, cn, amb, s));
   for (int it = 0; it < cfg->kmeans_iters; ++it) {
     const bool last = it + 1 == cfg->kmeans_iters;
-    QKV_HIP(launch_kmeans_assign(y, H, C, planes, cn, c, w, labels, amb, amb_list, s));
+    QKV_HIP(launch_kmeans_assign(y, H, C, planes, cn, c, w, labels, amb, s));
     QKV_HIP(launch_kmeans_update(y, H, C, labels, c, nullptr, w, last ? nullptr : planes, cn, amb, s));
   }
   return QKV_OK;
@@ -569,10 +567,8 @@ int qkv_kmeans_assign(const qkv_config* cfg, const qkv_tensor* y, const float* c
   uint16_t* planes = reinterpret_cast<uint16_t*>(at(workspace, ws.planes));
   float* cn = reinterpret_cast<float*>(at(workspace, ws.cn));
   int* amb = reinterpret_cast<int*>(at(workspace, ws.amb_count));
-  int64_t* amb_list = reinterpret_cast<int64_t*>(at(workspace, ws.amb_list));
   QKV_HIP(launch_centroid_prep(cfg->n_heads, cfg->n_clusters, centroids, w, planes, cn, amb, s));
-  QKV_HIP(launch_kmeans_assign(view_of(y), cfg->n_heads, cfg->n_clusters, planes, cn, centroids, w, labels, amb,
-                               amb_list, s));
+  QKV_HIP(launch_kmeans_assign(view_of(y), cfg->n_heads, cfg->n_clusters, planes, cn, centroids, w, labels, amb, s));
   return ok();
 }
 
