@@ -1,8 +1,9 @@
 """Throughput of the KV-cache compression hot path on one MI355X.
 
 One step = the whole path over one batch of synthetic input: every chunk of the
-cache is quantized (K and V: k-means smoothing, per-group INT2 codes, packing),
-then one query chunk attends over the full packed cache.  Default workload: 32
+cache is quantized (K and V: k-means smoothing, per-group INT2 codes, packing;
+the 12 independent problems go through one batched call), then one query chunk
+attends over the full packed cache.  Default workload: 32
 heads, d = 128, bf16, 6 chunks of 6,240 tokens (37,440 tokens), C = 256,
 INT2 with groups of 32, 1,560 queries.
 
@@ -26,7 +27,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "KV tokens quantized/s + fused INT2 attention TFLOP/s, GB/s vs MI355X peak"
 HBM_PEAK_GBS = 8000.0
-N_STREAMS = 4          # concurrent chunk quantizations (hardware queues per process on this part)
+MAX_BATCH = 16         # problems per qkv_quantize_chunks call
 BF16_PEAK_TFLOPS = 2500.0
 
 
@@ -136,31 +137,30 @@ def main():
     log(f"inputs ready in {time.time() - t0:.1f} s")
     maxn = max(ntok)
     ws_bytes = max(qk.qkv_workspace_bytes(kcfg, maxn, wl.n_query, wl.n_chunks), qk.qkv_workspace_bytes(vcfg, maxn))
-    # The chunk quantizations of a step are independent: they run on N_STREAMS
-    # streams (default priority), each with its own workspace, joined by events
-    # before the attention.
-    streams = [torch.cuda.Stream() for _ in range(N_STREAMS)]
-    wss = [torch.empty(ws_bytes, dtype=torch.uint8, device=dev) for _ in range(N_STREAMS)]
-    ws = wss[0]
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     kp = [torch.empty(qk.qkv_chunk_layout(kcfg, n).bytes, dtype=torch.uint8, device=dev) for n in ntok]
     vp = [torch.empty(qk.qkv_chunk_layout(vcfg, n).bytes, dtype=torch.uint8, device=dev) for n in ntok]
     out = torch.empty((wl.n_query, H, d), dtype=torch.float32, device=dev)
-    problems = [(kcfg, xk[c], kp[c], side_k) for c in range(wl.n_chunks)] + \
-               [(vcfg, xv[c], vp[c], {}) for c in range(wl.n_chunks)]
+    # The chunk quantizations of a step are independent: K and V of every chunk
+    # go through qkv_quantize_chunks in batches of up to MAX_BATCH problems of
+    # equal token count, one workspace slice each.
+    ks = (side_k.get("w"), side_k.get("perm"), side_k.get("U")) if side_k else None
+    problems = [(kcfg, xk[c], kp[c], ks) for c in range(wl.n_chunks)] + \
+               [(vcfg, xv[c], vp[c], None) for c in range(wl.n_chunks)]
+    batches = []
+    for n in sorted(set(ntok)):
+        same = [p for p in problems if p[1].shape[0] == n]
+        batches += [same[i:i + MAX_BATCH] for i in range(0, len(same), MAX_BATCH)]
+    qws = torch.empty(max(qk.qkv_quantize_chunks_workspace_bytes(kcfg, b[0][1].shape[0], len(b)) for b in batches),
+                      dtype=torch.uint8, device=dev)
 
     def quantize_all():
-        main = torch.cuda.current_stream()
-        start = torch.cuda.Event()
-        start.record(main)
-        for i, (cfg, x, packed, side) in enumerate(problems):
-            st = streams[i % N_STREAMS]
-            if i < N_STREAMS:
-                st.wait_event(start)
-            qk.qkv_quantize_chunk(cfg, x, packed, wss[i % N_STREAMS], stream=st.cuda_stream, **side)
-        for st in streams:
-            done = torch.cuda.Event()
-            done.record(st)
-            main.wait_event(done)
+        for b in batches:
+            qk.qkv_quantize_chunks([p[0] for p in b], [p[1] for p in b], [p[2] for p in b], qws,
+                                   sides=[p[3] for p in b])
+
+    def quantize_one_chunk():        # streaming use: K and V of one new chunk in one call
+        qk.qkv_quantize_chunks([kcfg, vcfg], [xk[0], xv[0]], [kp[0], vp[0]], qws, sides=[ks, None])
 
     def attend():
         qk.qkv_attend(kcfg, vcfg, q, kp, vp, ntok, out, ws, U=side_k.get("U"))
@@ -199,6 +199,7 @@ def main():
 
     reps = a.kernel_reps
     t_quant = timed(quantize_all, max(1, reps // 2))
+    t_chunk = timed(quantize_one_chunk, max(1, reps // 2))
     t_att = timed(attend, reps)
     # the dominant kernels of the quantizer: one k-means assign (all heads, one
     # tensor) and one quant-pack, through their step-level entry points
@@ -224,11 +225,13 @@ def main():
         "kmeans_assign_launches_per_step": n_assign,
         "quant_pack_ms": t_pack, "quant_pack_gbps": pack_bytes / (t_pack * 1e-3) / 1e9,
         "kv_tokens_quantized_per_s": nk / (t_quant * 1e-3),
+        "quantize_batches_per_step": len(batches),
+        "one_chunk_kv_ms": t_chunk, "one_chunk_kv_tokens_per_s": ntok[0] / (t_chunk * 1e-3),
     }
     # Roofline of the fused attention (the metric's headline kernel, MFMA-bound), timed at call level:
     # the qkv_attend call is k_attend plus three small helpers (chunk upload, tile table, split merge,
     # ~3 % of the call; the rocprofv3 summary in profiles/ lists each).  The k-means assign step is
-    # reported beside it (its call is k_prep + k_assign + k_refine).
+    # reported beside it (its call is k_prep + k_assign).
     achieved = att_flops / (t_att * 1e-3) / 1e12
     roof = {"kernel": "k_attend (qkv_attend call)", "bound": "mfma", "achieved": achieved,
             "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": achieved / BF16_PEAK_TFLOPS,

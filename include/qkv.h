@@ -185,6 +185,28 @@ int qkv_workspace_bytes(const qkv_config* cfg, int64_t max_chunk_tokens, int64_t
 int qkv_quantize_chunk(const qkv_config* cfg, const qkv_tensor* x, const qkv_side* side,
                        void* packed, void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * The write path of qkv_quantize_chunk ([QVG] "Method / Overall framework")
+ * for n independent problems (1 <= n <= 16) in one set of launches, e.g. K
+ * and V of a chunk, or several chunks: problem p reads
+ * xs[p] and writes packed[p] exactly as qkv_quantize_chunk(cfgs[p], xs[p],
+ * sides[p], packed[p], ...) would (sides may be NULL, as may each sides[p]).
+ * The problems must share n_heads, n_clusters, kmeans_iters, n_stages and
+ * flags of their configs, and n_tokens and dtype of their tensors; bits,
+ * group, the mixed layout, QSAC and PSAC may differ.  workspace: at least
+ * qkv_quantize_chunks_workspace_bytes(cfgs[0], N, n) bytes, split into one
+ * slice per problem.  Errors: QKV_EINVAL for a mismatch or a bad pointer (no
+ * work is queued), as qkv_quantize_chunk otherwise.
+ */
+int qkv_quantize_chunks(int32_t n, const qkv_config* const* cfgs, const qkv_tensor* const* xs,
+                        const qkv_side* const* sides, void* const* packed, void* workspace,
+                        size_t workspace_bytes, void* stream);
+
+/* Host only: workspace bytes of qkv_quantize_chunks for n problems of
+   n_tokens tokens under cfg. */
+int qkv_quantize_chunks_workspace_bytes(const qkv_config* cfg, int64_t n_tokens, int32_t n,
+                                        size_t* out);
+
 /* Dequantize a packed chunk: out [N][H][d], f32 or bf16 (bf16 = nearest-even
    rounding of the f32 sum).  ([QVG] "Method / Overall framework".) */
 int qkv_dequantize(const qkv_config* cfg, int64_t n_tokens, const void* packed,

@@ -113,6 +113,39 @@ def test_quantize_validation_paths():
     assert "U" in B.qkv_last_error()
 
 
+def _quantize_batch(cfgs, xs, sides=None, packs=None, ws=FAKE, ws_bytes=1 << 40, n=None):
+    lib = B.lib()
+    n = len(xs) if n is None else n
+    m = max(len(xs), 1)
+    cc = [c.c() for c in cfgs]
+    cp = (ct.POINTER(B.qkv_config) * m)(*[ct.pointer(c) for c in cc])
+    tp = (ct.POINTER(B.qkv_tensor) * m)(*[ct.pointer(x) for x in xs])
+    sides = sides or [B.qkv_side(None, None, None)] * m
+    sp = (ct.POINTER(B.qkv_side) * m)(*[ct.pointer(s) for s in sides])
+    pk = (ct.c_void_p * m)(*(packs or [FAKE] * m))
+    return lib.qkv_quantize_chunks(n, cp, tp, sp, pk, ws, ws_bytes, None)
+
+
+def test_quantize_batch_validation_paths():
+    k, v = _cfg(), _cfg(bits=4)                       # bits may differ within a batch
+    assert _quantize_batch([k, v], [_tensor(), _tensor()], ws_bytes=1000) == B.QKV_EWORKSPACE
+    assert _quantize_batch([k], [_tensor()], n=0) == B.QKV_EINVAL
+    assert _quantize_batch([k] * 17, [_tensor()] * 17) == B.QKV_EINVAL          # more than 16 problems
+    assert _quantize_batch([k, _cfg(n_clusters=32)], [_tensor(), _tensor()]) == B.QKV_EINVAL
+    assert _quantize_batch([k, _cfg(kmeans_iters=3)], [_tensor(), _tensor()]) == B.QKV_EINVAL
+    assert _quantize_batch([k, _cfg(n_stages=2)], [_tensor(), _tensor()]) == B.QKV_EINVAL
+    assert _quantize_batch([k, v], [_tensor(), _tensor(n=120)]) == B.QKV_EINVAL   # token counts differ
+    assert _quantize_batch([k, v], [_tensor(), _tensor(dtype=B.QKV_F32)]) == B.QKV_EINVAL
+    assert _quantize_batch([k, v], [_tensor(), _tensor()], packs=[FAKE, None]) == B.QKV_EINVAL
+    assert _quantize_batch([k, _cfg(use_qsac=1)], [_tensor(), _tensor()]) == B.QKV_EINVAL   # missing w
+    assert "problem 1" in B.qkv_last_error()
+    one = B.qkv_quantize_chunks_workspace_bytes(k, 6240, 1)
+    assert B.qkv_quantize_chunks_workspace_bytes(k, 6240, 12) == 12 * one
+    assert one >= B.qkv_workspace_bytes(k, 6240) - 256
+    with pytest.raises(B.QkvError):
+        B.qkv_quantize_chunks_workspace_bytes(k, 6240, 17)
+
+
 def test_workspace_sizes_grow_with_work():
     cfg = _cfg(n_heads=32, n_clusters=256)
     a = B.qkv_workspace_bytes(cfg, 6240)

@@ -251,3 +251,77 @@ def test_psac_fit_matches_oracle():
         worst = max(worst, dp)
         assert dp < 1e-4, f"head {h}: projector differs by {dp}"
     G.log(f"psac_fit: weights/perm exact, worst projector difference {worst:.3g}, energy[0] {energy[0]:.4f}")
+
+
+def _batch_vs_single(problems):
+    """problems: list of (cfg, x_dev, (w, perm, u) device tensors or None).
+    The batched write path must reproduce every single-problem call byte for byte."""
+    t = G.torch()
+    n = problems[0][1].shape[0]
+    packs = [t.zeros(qk.qkv_chunk_layout(cfg, n).bytes, dtype=t.uint8, device=G.dev()) for cfg, _, _ in problems]
+    wsb = qk.qkv_quantize_chunks_workspace_bytes(problems[0][0], n, len(problems))
+    ws = t.empty(wsb, dtype=t.uint8, device=G.dev())
+    qk.qkv_quantize_chunks([p[0] for p in problems], [p[1] for p in problems], packs, ws,
+                           sides=[p[2] for p in problems])
+    for i, (cfg, x, side) in enumerate(problems):
+        w, perm, u = side if side is not None else (None, None, None)
+        single = G.quantize(cfg, x, w=w, perm=perm, u=u)
+        t.cuda.synchronize()
+        assert t.equal(packs[i], single), f"problem {i}: batched bytes differ from the single call"
+
+
+def test_quantize_batch_mixed_configs_matches_single():
+    """K with QSAC + PSAC, V plain, and K with the mixed INT4 layout in one batch
+    (configs differ in everything a batch allows), ragged N."""
+    t = G.torch()
+    n = 1300
+    probs = []
+    for cid, tensor in ((4, "K"), (4, "V"), (5, "K")):
+        wl = synth.workload(cid, n_heads=2, n_clusters=64)
+        x = synth.kv_tokens(wl, tensor, 0, n)
+        w, u, perm = _side(wl, tensor)
+        side = (None if w is None else G.to_dev(w),
+                None if perm is None else t.from_numpy(perm.astype(np.uint8)).to(G.dev()),
+                None if u is None else G.to_dev(u))
+        probs.append((G.config_of(wl, tensor), G.to_dev(x, wl.dtype), side))
+    G.log("batch of 3 mixed configs, N=1300, H=2, C=64")
+    _batch_vs_single(probs)
+
+
+def test_quantize_batch_bench_shape_matches_single():
+    """The bench's batch: K and V of all six chunks of the 5 s cache (12 problems,
+    32 heads x 6,240 tokens, C = 256) in one call, against single calls (whose
+    parity with the oracle the sampled-head test above establishes)."""
+    wl = synth.workload(2)
+    probs = []
+    for c in range(wl.n_chunks):
+        for tensor in ("K", "V"):
+            probs.append((G.config_of(wl, tensor), G.to_dev(synth.kv_chunk(wl, tensor, c), "bf16"), None))
+    G.log(f"bench batch: {len(probs)} problems of N={wl.chunk_tokens}, H={wl.n_heads}")
+    _batch_vs_single(probs)
+
+
+def test_quantize_batch_all_ties_overflow_list():
+    """Every token of a problem identical: all centroids tie, every token is a
+    close call (more than the workgroup's LDS list holds, so the per-wave
+    re-decision runs too).  Ties go to the lowest index, so every label is 0,
+    the centroid is the token and the residual is zero: the dequantized chunk
+    equals the input exactly."""
+    t = G.torch()
+    n_prob, H, N = 16, 16, 4096
+    cfg = qk.Config(n_heads=H, n_clusters=64, bits=2, group=32, kmeans_iters=2)
+    rng = np.random.default_rng(7)
+    xs = []
+    for p in range(n_prob):
+        row = bf16_rne(rng.standard_normal((1, H, 128)) * 3.0).astype(np.float32)
+        xs.append(G.to_dev(np.repeat(row, N, axis=0), "bf16"))
+    packs = [t.zeros(qk.qkv_chunk_layout(cfg, N).bytes, dtype=t.uint8, device=G.dev()) for _ in range(n_prob)]
+    ws = t.empty(qk.qkv_quantize_chunks_workspace_bytes(cfg, N, n_prob), dtype=t.uint8, device=G.dev())
+    G.log(f"all-ties batch: {n_prob} problems, H={H}, N={N}, C=64")
+    qk.qkv_quantize_chunks([cfg] * n_prob, xs, packs, ws)
+    for p in range(n_prob):
+        v = G.host_views(packs[p], cfg, N)
+        assert not np.any(v["labels"]), f"problem {p}: a tie did not go to index 0"
+        out = t.empty((N, H, 128), dtype=t.bfloat16, device=G.dev())
+        qk.qkv_dequantize(cfg, N, packs[p], out)
+        assert t.equal(out, xs[p]), f"problem {p}: dequantized chunk differs from the input"

@@ -23,6 +23,7 @@ EXPORTED = [
     "qkv_version", "qkv_last_error", "qkv_chunk_layout", "qkv_workspace_bytes",
     "qkv_quantize_chunk", "qkv_dequantize", "qkv_attend", "qkv_psac_fit",
     "qkv_kmeans_assign", "qkv_kmeans_update", "qkv_quant_pack",
+    "qkv_quantize_chunks", "qkv_quantize_chunks_workspace_bytes",
 ]
 
 
@@ -103,6 +104,8 @@ def lib():
         L.qkv_kmeans_assign.argtypes = [P(qkv_config), P(qkv_tensor), vp, vp, vp, vp, sz, vp]
         L.qkv_kmeans_update.argtypes = [P(qkv_config), P(qkv_tensor), vp, vp, vp, vp, sz, vp]
         L.qkv_quant_pack.argtypes = [P(qkv_config), P(qkv_tensor), vp, vp, vp, vp, i32, vp, vp]
+        L.qkv_quantize_chunks.argtypes = [i32, P(P(qkv_config)), P(P(qkv_tensor)), P(P(qkv_side)), P(vp), vp, sz, vp]
+        L.qkv_quantize_chunks_workspace_bytes.argtypes = [P(qkv_config), i64, i32, P(sz)]
         for name in EXPORTED[2:]:
             getattr(L, name).restype = ct.c_int
         _lib = L
@@ -190,6 +193,27 @@ def qkv_psac_fit(q_hist, n_heads: int, rank: int, n_int4: int, workspace, U_out=
                               _ptr(perm_out), energy, _ptr(workspace),
                               workspace.numel() * workspace.element_size(), _stream(stream)))
     return list(energy)
+
+
+def qkv_quantize_chunks_workspace_bytes(cfg: Config, n_tokens: int, n: int) -> int:
+    out = ct.c_size_t()
+    _check(lib().qkv_quantize_chunks_workspace_bytes(ct.byref(cfg.c()), n_tokens, n, ct.byref(out)))
+    return out.value
+
+
+def qkv_quantize_chunks(cfgs, xs, packs, workspace, sides=None, stream=None):
+    """Batch of write paths in one set of launches; sides: list of (w, perm, U) or None."""
+    n = len(xs)
+    cc = [c.c() for c in cfgs]
+    tt = [tensor_desc(x) for x in xs]
+    ss = [qkv_side(_ptr(s[0]), _ptr(s[1]), _ptr(s[2])) if s is not None else qkv_side(None, None, None)
+          for s in (sides or [None] * n)]
+    cp = (ct.POINTER(qkv_config) * n)(*[ct.pointer(c) for c in cc])
+    tp = (ct.POINTER(qkv_tensor) * n)(*[ct.pointer(t) for t in tt])
+    sp = (ct.POINTER(qkv_side) * n)(*[ct.pointer(s) for s in ss])
+    pk = (ct.c_void_p * n)(*[p.data_ptr() for p in packs])
+    _check(lib().qkv_quantize_chunks(n, cp, tp, sp, pk, _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                     _stream(stream)))
 
 
 def qkv_kmeans_assign(cfg: Config, y, centroids, labels, workspace, w=None, stream=None):

@@ -24,24 +24,39 @@ struct ChannelCode {
 
 // ---- k-means (kmeans.hip) ----
 // Centroids c: f32 [H][C][128].  planes: bf16 bits [H][2][C][128], the split
-// hi/lo of fp32(w * c) used as the MFMA operand of the distance GEMM.
+// hi/lo of fp32(-2 w c) used as the MFMA operand of the distance GEMM.
 // cn: f32 [H][C], sum_k w_k c_k^2 (rounded from float64).
-hipError_t launch_kmeans_init(const TensorView& y, int H, int C, float* c, hipStream_t s);
-hipError_t launch_centroid_prep(int H, int C, const float* c, const float* w, uint16_t* planes,
-                                float* cn, int* amb_count, hipStream_t s);
+// Every launch covers a batch of independent problems (one per grid slice);
+// the problems of a batch share dtype, n_tokens, n_heads and n_clusters.
+struct KmItem {
+  const void* y;                 // tokens [N][H][128] (strided)
+  int64_t stride_token, stride_head;
+  const float* w;                // QSAC weights [H][128], or null (all ones)
+  float* c;
+  uint16_t* planes;
+  float* cn;
+  uint8_t* labels;               // [H][N]
+  int* amb_count;                // close calls of the last assign (statistics), or null
+  int32_t* counts;               // member counts [H][C] from the update, or null
+  uint16_t* cent_bf16;           // bf16 centroids written by launch_centroid_bf16
+};
+constexpr int kKmMaxBatch = 16;
+struct KmBatch {
+  int n, dtype, H, C;
+  int64_t N;
+  KmItem it[kKmMaxBatch];
+};
+hipError_t launch_kmeans_init(const KmBatch& b, hipStream_t s);
+// planes + cn from c (and w); zeroes amb_count.
+hipError_t launch_centroid_prep(const KmBatch& b, hipStream_t s);
 // Assign = MFMA screening (labels) + float64 re-decision of the close calls,
-// in one kernel.  amb_count (zeroed by the preceding prep or update; may be
-// null) receives the number of close calls.
-hipError_t launch_kmeans_assign(const TensorView& y, int H, int C, const uint16_t* planes,
-                                const float* cn, const float* c, const float* w, uint8_t* labels,
-                                int* amb_count, hipStream_t s);
+// in one kernel; adds the number of close calls to amb_count.
+hipError_t launch_kmeans_assign(const KmBatch& b, hipStream_t s);
 // Update = grouping of the tokens by label (in LDS) + exact per-cluster sums;
-// when planes != null it also refreshes the operand planes / norms for the
-// next assign.  Zeroes amb_count.
-hipError_t launch_kmeans_update(const TensorView& y, int H, int C, const uint8_t* labels, float* c,
-                                int32_t* counts, const float* w, uint16_t* planes, float* cn, int* amb_count,
-                                hipStream_t s);
-hipError_t launch_centroid_bf16(int H, int C, const float* c, uint16_t* out, hipStream_t s);
+// with refresh it also rewrites the operand planes / norms for the next
+// assign.  Zeroes amb_count.
+hipError_t launch_kmeans_update(const KmBatch& b, bool refresh, hipStream_t s);
+hipError_t launch_centroid_bf16(const KmBatch& b, hipStream_t s);
 hipError_t launch_fill_zero_u32(void* p, size_t n_words, hipStream_t s);
 
 // ---- quantize / dequantize (quant.hip) ----

@@ -28,6 +28,10 @@ namespace qkv {
 
 namespace {
 
+__device__ __forceinline__ TensorView item_view(const KmBatch& b, const KmItem& it) {
+  return TensorView{it.y, b.dtype, b.N, it.stride_token, it.stride_head};
+}
+
 constexpr int kPitch = 136;          // LDS row pitch (bf16): 128 + 8 keeps ds_read_b128 conflict-free
 
 template <bool F32>
@@ -39,7 +43,11 @@ __device__ __forceinline__ float load1(const TensorView& y, int64_t tok, int h, 
 
 // Block (head, 8 centroids): c_j = y[j * floor(N / C)] as float32.
 template <bool F32>
-__global__ __launch_bounds__(256) void k_init(TensorView y, int C, float* __restrict__ c) {
+__global__ __launch_bounds__(256) void k_init(KmBatch b) {
+  const KmItem& it = b.it[blockIdx.z];
+  const TensorView y = item_view(b, it);
+  const int C = b.C;
+  float* __restrict__ c = it.c;
   const int h = blockIdx.y;
   const int j = blockIdx.x * 8 + (threadIdx.x >> 5);
   if (j >= C) return;
@@ -52,10 +60,14 @@ __global__ __launch_bounds__(256) void k_init(TensorView y, int C, float* __rest
 }
 
 // One wave per centroid: hi/lo planes of fp32(w*c) and the weighted norm.
-__global__ __launch_bounds__(64) void k_prep(int C, const float* __restrict__ c,
-                                             const float* __restrict__ w,
-                                             uint16_t* __restrict__ planes, float* __restrict__ cn,
-                                             int* __restrict__ amb_count) {
+__global__ __launch_bounds__(64) void k_prep(KmBatch b) {
+  const KmItem& it = b.it[blockIdx.y];
+  const int C = b.C;
+  const float* __restrict__ c = it.c;
+  const float* __restrict__ w = it.w;
+  uint16_t* __restrict__ planes = it.planes;
+  float* __restrict__ cn = it.cn;
+  int* __restrict__ amb_count = it.amb_count;
   const int h = blockIdx.x / C, j = blockIdx.x % C;
   const int lane = threadIdx.x;
   if (blockIdx.x == 0 && lane == 0 && amb_count) *amb_count = 0;
@@ -89,21 +101,27 @@ __global__ __launch_bounds__(64) void k_prep(int C, const float* __restrict__ c,
 constexpr int kAsgWaves = 8;
 constexpr int kAsgThreads = kAsgWaves * 64;
 constexpr int kAsgMaxC = 256;
-constexpr int kAsgMaxSub = 32;        // sub-blocks per workgroup at most (LDS close-call list)
+constexpr int kAsgList = 1024;        // LDS close-call list; beyond it a wave re-decides on the spot
 constexpr int kAsgCUs = 256;
+constexpr int kAsgUnitCost = 25;
 
 template <bool F32>
-__global__ __launch_bounds__(kAsgThreads) void k_assign(TensorView y, int C, int G, int n_heads,
-                                                      const uint16_t* __restrict__ planes,
-                                                      const float* __restrict__ cn, const float* __restrict__ w,
-                                                      const float* __restrict__ cent, uint8_t* __restrict__ labels,
-                                                      int* __restrict__ amb_count) {
+__global__ __launch_bounds__(kAsgThreads) void k_assign(KmBatch b, int G) {
+  const KmItem& it = b.it[blockIdx.y];
+  const TensorView y = item_view(b, it);
+  const int C = b.C, n_heads = b.H;
+  const uint16_t* __restrict__ planes = it.planes;
+  const float* __restrict__ cn = it.cn;
+  const float* __restrict__ w = it.w;
+  const float* __restrict__ cent = it.c;
+  uint8_t* __restrict__ labels = it.labels;
+  int* __restrict__ amb_count = it.amb_count;
   __shared__ __attribute__((aligned(16))) uint16_t sP[2][kAsgMaxC][kPitch];
   __shared__ __attribute__((aligned(16))) float sCn[kAsgMaxC];
   __shared__ __attribute__((aligned(16))) float sW[kHeadDim];
-  __shared__ int sAmb[kAsgMaxSub * 32];
-  __shared__ int sAmbN;
-  __shared__ __attribute__((aligned(16))) float sYr[4][kHeadDim];
+  __shared__ int sAmb[kAsgList];
+  __shared__ int sAmbN, sNext;
+  __shared__ double sWY[4][kHeadDim];
   __shared__ double sRv[kAsgWaves][4];
   __shared__ int sRj[kAsgWaves][4];
   const uint32_t logical = xcd_remap(blockIdx.x, (uint32_t)(G * n_heads));
@@ -113,11 +131,12 @@ __global__ __launch_bounds__(kAsgThreads) void k_assign(TensorView y, int C, int
   const int col = lane & 31, half = lane >> 5;
   const int S = (N + 31) >> 5;
   const int sb0 = (int)((int64_t)S * g / G), sb1 = (int)((int64_t)S * (g + 1) / G);
-  // each wave takes an even share of the sub-blocks, in items of two (fp32
-  // tokens: one), an odd last one alone
+  // items: pairs of sub-blocks (fp32 tokens: single ones), an odd last one
+  // alone; wave w starts with item w, then takes the next one from an LDS
+  // counter, so the waves finish together
   constexpr int kPer = F32 ? 1 : 2;
   const int nsb = sb1 - sb0;
-  const int wsb0 = sb0 + nsb * wave / kAsgWaves, wsb1 = sb0 + nsb * (wave + 1) / kAsgWaves;
+  const int npair = F32 ? 0 : nsb >> 1, nitems = F32 ? nsb : npair + (nsb & 1);
   const int Cp = (C + 31) & ~31;                 // whole 32-row blocks; rows past C never win (norm +inf)
   const uint16_t* y16 = reinterpret_cast<const uint16_t*>(y.ptr);
   const int64_t hoff = (int64_t)h * y.stride_head + half * 8;
@@ -157,6 +176,7 @@ __global__ __launch_bounds__(kAsgThreads) void k_assign(TensorView y, int C, int
       }
     } else if (wave == 2 && lane == 0) {
       sAmbN = 0;
+      sNext = kAsgWaves;
     }
     // planes: 1 KB of the padded image per wave instruction; pad pieces and
     // rows in [C, Cp) take copies of valid pieces
@@ -171,7 +191,7 @@ __global__ __launch_bounds__(kAsgThreads) void k_assign(TensorView y, int C, int
             reinterpret_cast<char*>(&sP[0][0][0]) + p * kPlaneBytes + (k - p * nch) * 1024);
     }
     asm volatile("" ::: "memory");
-    if constexpr (!F32) load_tokens(wsb0, 2);   // past the wave's range: clamped, unused
+    if constexpr (!F32) load_tokens(sb0 + kPer * wave, 2);   // past the range: clamped, unused
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(F32 ? 0 : 16));   // vmcnt counts in issue order
     __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
     asm volatile("" ::: "memory");
@@ -179,9 +199,12 @@ __global__ __launch_bounds__(kAsgThreads) void k_assign(TensorView y, int C, int
     asm volatile("" ::: "memory");
   }
 
-  for (int sb = wsb0; sb < wsb1; sb += kPer) {
-    const int nt = min(kPer, wsb1 - sb);
+  for (int it = wave; it < nitems;) {
+    const int sb = sb0 + kPer * it, nt = it < npair ? 2 : 1;
     const int tok0 = sb * 32;
+    int next = 0;
+    if (lane == 0) next = atomicAdd(&sNext, 1);
+    next = __builtin_amdgcn_readfirstlane(next);
     // B operand (tokens): lane holds token tok0 + t*32 + col, channels s*16 + half*8 + [0, 8).
     // ynorm[t] = sum_k w_k y_k^2 over the lane's channels (fp32; it only sets
     // the screening threshold).
@@ -214,33 +237,51 @@ __global__ __launch_bounds__(kAsgThreads) void k_assign(TensorView y, int C, int
         }
       }
     } else {
+      if (tok0 + 64 > N) {                       // the head's last item: rows past N are zero
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const bool ok = tok0 + t * 32 + col < N;
+        for (int t = 0; t < 2; ++t) {
+          const bool ok = tok0 + t * 32 + col < N;
 #pragma unroll
-        for (int s = 0; s < 8; ++s) {
-          const uint4 r = ok ? raw[t][s] : make_uint4(0, 0, 0, 0);
-          yh[t][s] = as_bf16x8(r);
-          const uint32_t r4[4] = {r.x, r.y, r.z, r.w};
-          const int ch = s * 16 + half * 8;
-          if (w == nullptr) {                    // sum of squares by packed bf16 dot products
+          for (int s = 0; s < 8; ++s) raw[t][s] = ok ? raw[t][s] : make_uint4(0, 0, 0, 0);
+        }
+      }
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int s = 0; s < 8; ++s) yh[t][s] = as_bf16x8(raw[t][s]);
+      if (w == nullptr) {                        // sum of squares by packed bf16 dot products
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          float part[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+          for (int s = 0; s < 8; ++s) {
+            const uint32_t r4[4] = {raw[t][s].x, raw[t][s].y, raw[t][s].z, raw[t][s].w};
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
               const bf16x2 q = __builtin_bit_cast(bf16x2, r4[e]);
-              ynorm[t] = __builtin_amdgcn_fdot2_f32_bf16(q, q, ynorm[t], false);
+              part[e] = __builtin_amdgcn_fdot2_f32_bf16(q, q, part[e], false);
             }
-          } else {
+          }
+          ynorm[t] = (part[0] + part[1]) + (part[2] + part[3]);
+        }
+      } else {
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int s = 0; s < 8; ++s) {
+            const uint32_t r4[4] = {raw[t][s].x, raw[t][s].y, raw[t][s].z, raw[t][s].w};
+            const int ch = s * 16 + half * 8;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
               const float v = bf16_bits_to_f32((r4[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
               ynorm[t] += sW[ch + e] * (v * v);
             }
           }
-        }
       }
-      if (sb + kPer < wsb1) load_tokens(sb + kPer, min(kPer, wsb1 - sb - kPer));
+      if (next < nitems) load_tokens(sb0 + kPer * next, next < npair ? 2 : 1);
     }
 
+    int spill = 0;                               // 1 + token of a close call past the list
     // Sweep of the centroid blocks for NT sub-blocks: running best b1 and
     // second best b2 of the screened values (b1 <= b2; new b2 = med3(b1, b2, v),
     // new b1 = min(b1, v)).  rel is the best row relative
@@ -330,7 +371,8 @@ __global__ __launch_bounds__(kAsgThreads) void k_assign(TensorView y, int C, int
           const float thr = 2e-5f * (yn + sCn[bidx[t]]);
           if (!(second - b1[t] > thr)) {
             const int slot = atomicAdd(&sAmbN, 1);
-            if (slot < kAsgMaxSub * 32) sAmb[slot] = tok;
+            if (slot < kAsgList) sAmb[slot] = tok;
+            else spill = tok + 1;
           }
         }
       }
@@ -341,52 +383,108 @@ __global__ __launch_bounds__(kAsgThreads) void k_assign(TensorView y, int C, int
       if (nt == 2) sweep(std::integral_constant<int, 2>{});
       else sweep(std::integral_constant<int, 1>{});
     }
+    // the list is full (a pathological input): this wave re-decides its
+    // overflowing close calls one at a time, lanes over centroids
+    for (uint64_t m = __ballot(spill != 0); m; m &= m - 1) {
+      const int src = __builtin_ctzll(m);
+      const int tok = __builtin_amdgcn_readlane(spill, src) - 1;
+      const int64_t off = (int64_t)tok * y.stride_token + (int64_t)h * y.stride_head + lane * 2;
+      float ya, yb;
+      if constexpr (F32) {
+        const float2 v = *reinterpret_cast<const float2*>(reinterpret_cast<const float*>(y.ptr) + off);
+        ya = v.x;
+        yb = v.y;
+      } else {
+        const uint32_t v = *reinterpret_cast<const uint32_t*>(y16 + off);
+        ya = bf16_bits_to_f32(v & 0xFFFFu);
+        yb = bf16_bits_to_f32(v >> 16);
+      }
+      double best = INFINITY;
+      int bj = 0;
+      for (int q = 0; q < kAsgMaxC / 64; ++q) {
+        const int j = q * 64 + lane;
+        const float* cr = cent + ((int64_t)h * C + min(j, C - 1)) * kHeadDim;
+        double dist = 0.0;
+#pragma unroll 8
+        for (int k = 0; k < kHeadDim; k += 2) {
+          const float yk0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, ya), k >> 1));
+          const float yk1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, yb), k >> 1));
+          const float2 cv = *reinterpret_cast<const float2*>(cr + k);
+          const double d0 = (double)yk0 - (double)cv.x, d1 = (double)yk1 - (double)cv.y;
+          dist += (double)sW[k] * (d0 * d0);
+          dist += (double)sW[k + 1] * (d1 * d1);
+        }
+        if (j < C && dist < best) {
+          best = dist;
+          bj = j;
+        }
+      }
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const double ov = __shfl_xor(best, o);
+        const int oj = __shfl_xor(bj, o);
+        if (ov < best || (ov == best && oj < bj)) {
+          best = ov;
+          bj = oj;
+        }
+      }
+      if (lane == 0) labels[(int64_t)h * N + tok] = (uint8_t)bj;
+    }
+    it = next;
   }
 
-  // Close calls re-decided from float64 distances sum_k w_k (y_k - c_jk)^2,
-  // four tokens at a time: thread t holds half (t & 1) of centroid row t >> 1
-  // (fp32) and accumulates its 64 channels for each token; the
-  // halves are joined, then the lowest distance wins, ties to the lowest index.
+  // Close calls re-decided in float64, four tokens at a time: the distances
+  // differ from sum_j w_k c_jk^2 - 2 sum_k (w_k y_k) c_jk by the token's own
+  // norm, which does not move the argmin.  Thread t holds half (t & 1) of
+  // centroid row t >> 1 (fp32) and accumulates its 64 channels of both sums
+  // (products of fp32 values are exact in float64); the halves are joined,
+  // then the lowest value wins, ties to the lowest index.
   __syncthreads();
-  const int n_amb = min(sAmbN, kAsgMaxSub * 32);
+  const int n_amb = min(sAmbN, kAsgList);
   if (n_amb > 0) {
     if (tid == 0 && amb_count) atomicAdd(amb_count, n_amb);   // statistics only
     const int j = tid >> 1, hk = (tid & 1) * 64;
     const float* cr = cent + ((int64_t)h * C + min(j, C - 1)) * kHeadDim + hk;
     for (int e0 = 0; e0 < n_amb; e0 += 4) {
       {
-        const int q = tid >> 7, k = tid & 127;                // 4 tokens x 128 channels
+        const int q = tid >> 7, k = tid & 127;                // 4 tokens x 128 channels: w_k y_k
         const int tok = sAmb[min(e0 + q, n_amb - 1)];
         const int64_t off = (int64_t)tok * y.stride_token + (int64_t)h * y.stride_head + k;
-        sYr[q][k] = F32 ? reinterpret_cast<const float*>(y.ptr)[off] : bf16_bits_to_f32(y16[off]);
+        const float yv = F32 ? reinterpret_cast<const float*>(y.ptr)[off] : bf16_bits_to_f32(y16[off]);
+        sWY[q][k] = (double)sW[k] * (double)yv;
       }
       __syncthreads();
-      double d[4] = {0.0, 0.0, 0.0, 0.0};
-#pragma unroll 1
-      for (int x0 = 0; x0 < 64; x0 += 16) {          // 16 channels of the row half per step
-        float4 c4[4];
+      // the row half streams in four groups of 16 channels, the next group's
+      // loads in flight during the current group's arithmetic
+      double d[4] = {0.0, 0.0, 0.0, 0.0}, cc = 0.0;
+      float4 cur[4], nxt[4];
 #pragma unroll
-        for (int x = 0; x < 4; ++x) c4[x] = *reinterpret_cast<const float4*>(cr + x0 + 4 * x);
+      for (int x = 0; x < 4; ++x) cur[x] = *reinterpret_cast<const float4*>(cr + 4 * x);
+#pragma unroll 1
+      for (int g = 0; g < 4; ++g) {
+        if (g < 3) {
+#pragma unroll
+          for (int x = 0; x < 4; ++x) nxt[x] = *reinterpret_cast<const float4*>(cr + 16 * (g + 1) + 4 * x);
+        }
 #pragma unroll
         for (int x = 0; x < 4; ++x) {
-          const float cv[4] = {c4[x].x, c4[x].y, c4[x].z, c4[x].w};
-          const float4 w4 = *reinterpret_cast<const float4*>(&sW[hk + x0 + 4 * x]);
-          const float wv4[4] = {w4.x, w4.y, w4.z, w4.w};
+          const float cv[4] = {cur[x].x, cur[x].y, cur[x].z, cur[x].w};
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const float4 y4 = *reinterpret_cast<const float4*>(&sYr[q][hk + x0 + 4 * x]);
-            const float yv4[4] = {y4.x, y4.y, y4.z, y4.w};
+          for (int u = 0; u < 4; ++u) {
+            const int k = hk + 16 * g + 4 * x + u;
+            const double c64 = (double)cv[u];
+            cc = __builtin_fma((double)sW[k], c64 * c64, cc);
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-              const double diff = (double)yv4[u] - (double)cv[u];
-              d[q] += (double)wv4[u] * (diff * diff);
-            }
+            for (int q = 0; q < 4; ++q) d[q] = __builtin_fma(sWY[q][k], c64, d[q]);
           }
         }
+#pragma unroll
+        for (int x = 0; x < 4; ++x) cur[x] = nxt[x];
       }
+      cc += __shfl_xor(cc, 1);
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        double v = d[q] + __shfl_xor(d[q], 1);
+        double v = cc - 2.0 * (d[q] + __shfl_xor(d[q], 1));
         int bj = j;
         if (j >= C) v = INFINITY;
 #pragma unroll
@@ -441,10 +539,17 @@ constexpr int kUpdWindow = 8192;          // token index << 3 fits 16 bits
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
 template <bool F32>
-__global__ __launch_bounds__(256) void k_update(TensorView y, int C, int n_heads, const uint8_t* __restrict__ labels,
-                                                float* __restrict__ c, const float* __restrict__ w,
-                                                uint16_t* __restrict__ planes, float* __restrict__ cn,
-                                                int32_t* __restrict__ counts, int* __restrict__ amb_count) {
+__global__ __launch_bounds__(256) void k_update(KmBatch b, int refresh) {
+  const KmItem& it = b.it[blockIdx.y];
+  const TensorView y = item_view(b, it);
+  const int C = b.C, n_heads = b.H;
+  const uint8_t* __restrict__ labels = it.labels;
+  float* __restrict__ c = it.c;
+  const float* __restrict__ w = it.w;
+  uint16_t* __restrict__ planes = refresh ? it.planes : nullptr;
+  float* __restrict__ cn = it.cn;
+  int32_t* __restrict__ counts = it.counts;
+  int* __restrict__ amb_count = it.amb_count;
   __shared__ int s_cnt[kUpdClusters], s_off[kUpdClusters + 1], s_cur[kUpdClusters];
   __shared__ uint16_t s_mem[kUpdWindow], s_tmp[kUpdWindow];
   __shared__ int s_wtot[4];
@@ -453,7 +558,7 @@ __global__ __launch_bounds__(256) void k_update(TensorView y, int C, int n_heads
   const int h = logical / groups, c0 = (logical % groups) * kUpdClusters;
   const int N = (int)y.n_tokens;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  if (blockIdx.x == 0 && tid == 0 && amb_count) *amb_count = 0;   // the close-call queue of the next assign
+  if (blockIdx.x == 0 && tid == 0 && amb_count) *amb_count = 0;   // the close-call count of the next assign
   const uint8_t* lab = labels + (int64_t)h * N;
   const int64_t hoff = (int64_t)h * y.stride_head + lane * 2;
   const bool plain = !F32 && N <= kUpdWindow;   // certified float64 sums
@@ -619,9 +724,11 @@ __global__ __launch_bounds__(256) void k_update(TensorView y, int C, int n_heads
   }
 }
 
-__global__ void k_centroid_bf16(int64_t n, const float* __restrict__ c, uint16_t* __restrict__ out) {
+__global__ void k_centroid_bf16(KmBatch b) {
+  const KmItem& it = b.it[blockIdx.y];
+  const int64_t n = (int64_t)b.H * b.C * kHeadDim;
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) out[i] = (uint16_t)f32_to_bf16_bits(c[i]);
+  if (i < n) it.cent_bf16[i] = (uint16_t)f32_to_bf16_bits(it.c[i]);
 }
 
 __global__ void k_fill_zero(uint32_t* __restrict__ p, int64_t n) {
@@ -631,52 +738,51 @@ __global__ void k_fill_zero(uint32_t* __restrict__ p, int64_t n) {
 
 }  // namespace
 
-hipError_t launch_kmeans_init(const TensorView& y, int H, int C, float* c, hipStream_t s) {
-  const dim3 grid((C + 7) / 8, H);
-  if (y.dtype == 0) hipLaunchKernelGGL(k_init<true>, grid, dim3(256), 0, s, y, C, c);
-  else hipLaunchKernelGGL(k_init<false>, grid, dim3(256), 0, s, y, C, c);
+hipError_t launch_kmeans_init(const KmBatch& b, hipStream_t s) {
+  const dim3 grid((b.C + 7) / 8, b.H, b.n);
+  if (b.dtype == 0) hipLaunchKernelGGL(k_init<true>, grid, dim3(256), 0, s, b);
+  else hipLaunchKernelGGL(k_init<false>, grid, dim3(256), 0, s, b);
   return hipGetLastError();
 }
 
-hipError_t launch_centroid_prep(int H, int C, const float* c, const float* w, uint16_t* planes,
-                                float* cn, int* amb_count, hipStream_t s) {
-  hipLaunchKernelGGL(k_prep, dim3(H * C), dim3(64), 0, s, C, c, w, planes, cn, amb_count);
+hipError_t launch_centroid_prep(const KmBatch& b, hipStream_t s) {
+  hipLaunchKernelGGL(k_prep, dim3(b.H * b.C, b.n), dim3(64), 0, s, b);
   return hipGetLastError();
 }
 
-hipError_t launch_kmeans_assign(const TensorView& y, int H, int C, const uint16_t* planes,
-                                const float* cn, const float* c, const float* w, uint8_t* labels,
-                                int* amb_count, hipStream_t s) {
-  if (C > kAsgMaxC) return hipErrorInvalidValue;
-  // workgroups per head: about one per compute unit overall, at least 16
-  // sub-blocks each where the head has them, at most kAsgMaxSub
-  const int S = (int)((y.n_tokens + 31) / 32);
-  int G = std::min((S + 15) / 16, std::max(1, kAsgCUs / H));
-  G = std::max(G, (S + kAsgMaxSub - 1) / kAsgMaxSub);
-  const dim3 grid((unsigned)(G * H));
-  if (y.dtype == 0)
-    hipLaunchKernelGGL(k_assign<true>, grid, dim3(kAsgThreads), 0, s, y, C, G, H, planes, cn, w, c, labels,
-                       amb_count);
-  else
-    hipLaunchKernelGGL(k_assign<false>, grid, dim3(kAsgThreads), 0, s, y, C, G, H, planes, cn, w, c, labels,
-                       amb_count);
+hipError_t launch_kmeans_assign(const KmBatch& b, hipStream_t s) {
+  if (b.C > kAsgMaxC) return hipErrorInvalidValue;
+  // Workgroups per head G: each workgroup pays a fixed cost (plane load,
+  // first tokens, close calls; about kAsgUnitCost sub-blocks' worth) and the
+  // launch runs in rounds of one workgroup per compute unit, so G minimizes
+  // rounds x (sub-blocks per workgroup + fixed cost).
+  const int S = (int)((b.N + 31) / 32);
+  int G = 1;
+  double best = 1e300;
+  for (int g = 1; g <= std::min(S, 64); ++g) {
+    const int64_t rounds = ((int64_t)b.n * b.H * g + kAsgCUs - 1) / kAsgCUs;
+    const double cost = (double)rounds * ((S + g - 1) / g + kAsgUnitCost);
+    if (cost < best) {
+      best = cost;
+      G = g;
+    }
+  }
+  const dim3 grid((unsigned)(G * b.H), b.n);
+  if (b.dtype == 0) hipLaunchKernelGGL(k_assign<true>, grid, dim3(kAsgThreads), 0, s, b, G);
+  else hipLaunchKernelGGL(k_assign<false>, grid, dim3(kAsgThreads), 0, s, b, G);
   return hipGetLastError();
 }
 
-hipError_t launch_kmeans_update(const TensorView& y, int H, int C, const uint8_t* labels, float* c,
-                                int32_t* counts, const float* w, uint16_t* planes, float* cn, int* amb_count,
-                                hipStream_t s) {
-  const dim3 grid((unsigned)(H * ((C + kUpdClusters - 1) / kUpdClusters)));
-  if (y.dtype == 0)
-    hipLaunchKernelGGL(k_update<true>, grid, dim3(256), 0, s, y, C, H, labels, c, w, planes, cn, counts, amb_count);
-  else
-    hipLaunchKernelGGL(k_update<false>, grid, dim3(256), 0, s, y, C, H, labels, c, w, planes, cn, counts, amb_count);
+hipError_t launch_kmeans_update(const KmBatch& b, bool refresh, hipStream_t s) {
+  const dim3 grid((unsigned)(b.H * ((b.C + kUpdClusters - 1) / kUpdClusters)), b.n);
+  if (b.dtype == 0) hipLaunchKernelGGL(k_update<true>, grid, dim3(256), 0, s, b, refresh ? 1 : 0);
+  else hipLaunchKernelGGL(k_update<false>, grid, dim3(256), 0, s, b, refresh ? 1 : 0);
   return hipGetLastError();
 }
 
-hipError_t launch_centroid_bf16(int H, int C, const float* c, uint16_t* out, hipStream_t s) {
-  const int64_t n = (int64_t)H * C * kHeadDim;
-  hipLaunchKernelGGL(k_centroid_bf16, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, n, c, out);
+hipError_t launch_centroid_bf16(const KmBatch& b, hipStream_t s) {
+  const int64_t n = (int64_t)b.H * b.C * kHeadDim;
+  hipLaunchKernelGGL(k_centroid_bf16, dim3((unsigned)((n + 255) / 256), b.n), dim3(256), 0, s, b);
   return hipGetLastError();
 }
 

@@ -246,22 +246,139 @@ int check_ws(const void* ws, size_t have, uint64_t need, const char* what) {
 
 uint8_t* at(void* base, uint64_t off) { return reinterpret_cast<uint8_t*>(base) + off; }
 
-// Run the k-means protocol of one stage on `y`; labels go to `labels`.
-int run_kmeans(const qkv_config* cfg, const TensorView& y, const float* w, uint8_t* labels, void* workspace,
-               const QuantWs& ws, hipStream_t s) {
-  const int H = cfg->n_heads, C = cfg->n_clusters;
-  float* c = reinterpret_cast<float*>(at(workspace, ws.c));
-  uint16_t* planes = reinterpret_cast<uint16_t*>(at(workspace, ws.planes));
-  float* cn = reinterpret_cast<float*>(at(workspace, ws.cn));
-  int* amb = reinterpret_cast<int*>(at(workspace, ws.amb_count));
-  QKV_HIP(launch_kmeans_init(y, H, C, c, s));
-  QKV_HIP(launch_centroid_prep(H, C, c, w, planes, cn, amb, s));
+// Run the k-means protocol of one stage on every problem of the batch.
+int run_kmeans(const qkv_config* cfg, const KmBatch& b, hipStream_t s) {
+  QKV_HIP(launch_kmeans_init(b, s));
+  QKV_HIP(launch_centroid_prep(b, s));
   for (int it = 0; it < cfg->kmeans_iters; ++it) {
-    const bool last = it + 1 == cfg->kmeans_iters;
-    QKV_HIP(launch_kmeans_assign(y, H, C, planes, cn, c, w, labels, amb, s));
-    QKV_HIP(launch_kmeans_update(y, H, C, labels, c, nullptr, w, last ? nullptr : planes, cn, amb, s));
+    QKV_HIP(launch_kmeans_assign(b, s));
+    QKV_HIP(launch_kmeans_update(b, it + 1 < cfg->kmeans_iters, s));
   }
   return QKV_OK;
+}
+
+// The write path of qkv_quantize_chunk(s): problems share n_heads,
+// n_clusters, kmeans_iters, n_stages, flags, n_tokens and dtype; each has its
+// own slice of the workspace.
+int quantize_batch(int32_t n, const qkv_config* const* cfgs, const qkv_tensor* const* xs,
+                   const qkv_side* const* sides, void* const* packed, void* workspace, size_t workspace_bytes,
+                   void* stream, const char* fn) {
+  if (n < 1 || n > kKmMaxBatch) return fail(QKV_EINVAL, "%s: %d problems (1 to %d)", fn, n, kKmMaxBatch);
+  if (!cfgs || !xs || !packed) return fail(QKV_EINVAL, "%s: NULL array", fn);
+  const qkv_config* c0 = cfgs[0];
+  QKV_TRY(check_config(c0, fn));
+  QKV_TRY(check_tensor(xs[0], c0->n_heads, fn));
+  const int64_t N = xs[0]->n_tokens;
+  if (N < c0->n_clusters) return fail(QKV_EINVAL, "%s: n_tokens %lld < n_clusters %d", fn, (long long)N, c0->n_clusters);
+  for (int p = 0; p < n; ++p) {
+    const qkv_config* cfg = cfgs[p];
+    QKV_TRY(check_config(cfg, fn));
+    QKV_TRY(check_tensor(xs[p], c0->n_heads, fn));
+    if (cfg->n_heads != c0->n_heads || cfg->n_clusters != c0->n_clusters || cfg->kmeans_iters != c0->kmeans_iters ||
+        cfg->n_stages != c0->n_stages || cfg->flags != c0->flags)
+      return fail(QKV_EINVAL, "%s: problem %d: configs of a batch must share n_heads, n_clusters, kmeans_iters, "
+                  "n_stages and flags", fn, p);
+    if (xs[p]->n_tokens != N || xs[p]->dtype != xs[0]->dtype)
+      return fail(QKV_EINVAL, "%s: problem %d: tensors of a batch must share n_tokens and dtype", fn, p);
+    if (!packed[p] || !aligned16(packed[p])) return fail(QKV_EINVAL, "%s: packed[%d] is NULL or not 16-byte aligned", fn, p);
+    const qkv_side* side = sides ? sides[p] : nullptr;
+    if (cfg->use_qsac && !(side && side->w)) return fail(QKV_EINVAL, "%s: problem %d: use_qsac needs side->w", fn, p);
+    if (cfg->n_int4_channels > 0 && !(side && side->perm))
+      return fail(QKV_EINVAL, "%s: problem %d: the mixed layout needs side->perm", fn, p);
+    if (cfg->psac_rank > 0 && !(side && side->U)) return fail(QKV_EINVAL, "%s: problem %d: psac_rank > 0 needs side->U", fn, p);
+  }
+  const QuantWs ws = quant_ws(c0, N);
+  const uint64_t per = align256(ws.bytes);
+  QKV_TRY(check_ws(workspace, workspace_bytes, per * n, fn));
+
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const int H = c0->n_heads;
+  std::vector<qkv_layout> L(n);
+  std::vector<ChunkDecode> g(n);
+  std::vector<TensorView> y(n);
+  KmBatch b{};
+  b.n = n;
+  b.dtype = xs[0]->dtype == QKV_F32 ? 0 : 1;
+  b.H = H;
+  b.C = c0->n_clusters;
+  b.N = N;
+  for (int p = 0; p < n; ++p) {
+    layout_of(cfgs[p], N, &L[p]);
+    g[p] = decode_of(cfgs[p], N, nullptr);
+    y[p] = view_of(xs[p]);
+    uint8_t* wsp = at(workspace, per * p);
+    const qkv_side* side = sides ? sides[p] : nullptr;
+    KmItem& it = b.it[p];
+    it.w = cfgs[p]->use_qsac ? side->w : nullptr;
+    it.c = reinterpret_cast<float*>(wsp + ws.c);
+    it.planes = reinterpret_cast<uint16_t*>(wsp + ws.planes);
+    it.cn = reinterpret_cast<float*>(wsp + ws.cn);
+    it.amb_count = reinterpret_cast<int*>(wsp + ws.amb_count);
+    it.counts = nullptr;
+    if (cfgs[p]->n_int4_channels > 0)
+      QKV_HIP(launch_copy_perm(side->perm, reinterpret_cast<uint8_t*>(packed[p]) + L[p].off_perm, H, s));
+  }
+  for (int l = 0; l < c0->n_stages; ++l) {
+    for (int p = 0; p < n; ++p) {
+      uint8_t* base = reinterpret_cast<uint8_t*>(packed[p]);
+      KmItem& it = b.it[p];
+      it.y = y[p].ptr;
+      it.stride_token = y[p].stride_token;
+      it.stride_head = y[p].stride_head;
+      it.labels = base + L[p].off_labels + (uint64_t)l * L[p].stage_bytes_labels;
+      it.cent_bf16 = reinterpret_cast<uint16_t*>(base + L[p].off_centroids + (uint64_t)l * L[p].stage_bytes_centroids);
+    }
+    b.dtype = y[0].dtype;
+    if (c0->flags & QKV_FLAG_RTN) {
+      for (int p = 0; p < n; ++p) {
+        QKV_HIP(launch_fill_zero_u32(b.it[p].labels, L[p].stage_bytes_labels / 4, s));
+        QKV_HIP(launch_fill_zero_u32(b.it[p].cent_bf16, L[p].stage_bytes_centroids / 4, s));
+      }
+    } else {
+      QKV_TRY(run_kmeans(c0, b, s));
+      QKV_HIP(launch_centroid_bf16(b, s));
+    }
+    const bool more = l + 1 < c0->n_stages;
+    for (int p = 0; p < n; ++p) {
+      const qkv_config* cfg = cfgs[p];
+      uint8_t* base = reinterpret_cast<uint8_t*>(packed[p]);
+      uint8_t* wsp = at(workspace, per * p);
+      PackArgs pa;
+      pa.y = y[p];
+      pa.H = H;
+      pa.C = c0->n_clusters;
+      pa.N = (int)N;
+      pa.labels = b.it[p].labels;
+      pa.centroids = b.it[p].cent_bf16;
+      pa.perm = cfg->n_int4_channels > 0 ? sides[p]->perm : nullptr;
+      pa.bits = cfg->bits;
+      pa.group = cfg->group;
+      pa.n_int4 = cfg->n_int4_channels;
+      pa.int4_words = g[p].int4_words;
+      pa.codes = reinterpret_cast<uint32_t*>(base + L[p].off_codes + (uint64_t)l * L[p].stage_bytes_codes);
+      pa.scales = reinterpret_cast<uint16_t*>(base + L[p].off_scales + (uint64_t)l * L[p].stage_bytes_scales);
+      pa.words = g[p].words;
+      pa.groups = g[p].groups;
+      float* ynext = more ? reinterpret_cast<float*>(wsp + ((l % 2 == 0) ? ws.ybuf0 : ws.ybuf1)) : nullptr;
+      pa.y_next = ynext;
+      QKV_HIP(launch_quant_pack(pa, s));
+      if (more) {
+        // y_next is laid out [H][N][128]: token stride 128, head stride N*128
+        y[p].ptr = ynext;
+        y[p].dtype = 0;
+        y[p].stride_token = kHeadDim;
+        y[p].stride_head = N * kHeadDim;
+      }
+    }
+  }
+  for (int p = 0; p < n; ++p) {
+    if (cfgs[p]->psac_rank > 0) {
+      const ChunkDecode d = decode_of(cfgs[p], N, packed[p]);
+      QKV_HIP(launch_psac_encode(d, view_of(xs[p]), sides[p]->U,
+                                 reinterpret_cast<uint16_t*>(reinterpret_cast<uint8_t*>(packed[p]) + L[p].off_psac), s));
+    }
+  }
+  return ok();
 }
 
 }  // namespace
@@ -300,75 +417,22 @@ int qkv_workspace_bytes(const qkv_config* cfg, int64_t max_chunk_tokens, int64_t
 
 int qkv_quantize_chunk(const qkv_config* cfg, const qkv_tensor* x, const qkv_side* side, void* packed,
                        void* workspace, size_t workspace_bytes, void* stream) {
-  const char* fn = "qkv_quantize_chunk";
-  QKV_TRY(check_config(cfg, fn));
-  QKV_TRY(check_tensor(x, cfg->n_heads, fn));
-  const int64_t N = x->n_tokens;
-  if (N < cfg->n_clusters) return fail(QKV_EINVAL, "%s: n_tokens %lld < n_clusters %d", fn, (long long)N, cfg->n_clusters);
-  if (!packed || !aligned16(packed)) return fail(QKV_EINVAL, "%s: packed is NULL or not 16-byte aligned", fn);
-  const float* w = side ? side->w : nullptr;
-  const uint8_t* perm = side ? side->perm : nullptr;
-  const float* U = side ? side->U : nullptr;
-  if (cfg->use_qsac && !w) return fail(QKV_EINVAL, "%s: use_qsac needs side->w", fn);
-  if (cfg->n_int4_channels > 0 && !perm) return fail(QKV_EINVAL, "%s: the mixed layout needs side->perm", fn);
-  if (cfg->psac_rank > 0 && !U) return fail(QKV_EINVAL, "%s: psac_rank > 0 needs side->U", fn);
-  const QuantWs ws = quant_ws(cfg, N);
-  QKV_TRY(check_ws(workspace, workspace_bytes, ws.bytes, fn));
+  return quantize_batch(1, &cfg, &x, &side, &packed, workspace, workspace_bytes, stream, "qkv_quantize_chunk");
+}
 
-  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  const int H = cfg->n_heads, C = cfg->n_clusters;
-  qkv_layout L;
-  layout_of(cfg, N, &L);
-  const ChunkDecode g = decode_of(cfg, N, nullptr);
-  uint8_t* base = reinterpret_cast<uint8_t*>(packed);
-  float* c = reinterpret_cast<float*>(at(workspace, ws.c));
-  const float* wk = cfg->use_qsac ? w : nullptr;
-  const uint8_t* pm = cfg->n_int4_channels > 0 ? perm : nullptr;
-  if (pm) QKV_HIP(launch_copy_perm(pm, base + L.off_perm, H, s));
+int qkv_quantize_chunks(int32_t n, const qkv_config* const* cfgs, const qkv_tensor* const* xs,
+                        const qkv_side* const* sides, void* const* packed, void* workspace, size_t workspace_bytes,
+                        void* stream) {
+  return quantize_batch(n, cfgs, xs, sides, packed, workspace, workspace_bytes, stream, "qkv_quantize_chunks");
+}
 
-  TensorView y = view_of(x);
-  for (int l = 0; l < cfg->n_stages; ++l) {
-    uint8_t* labels = base + L.off_labels + (uint64_t)l * L.stage_bytes_labels;
-    uint16_t* cent = reinterpret_cast<uint16_t*>(base + L.off_centroids + (uint64_t)l * L.stage_bytes_centroids);
-    if (cfg->flags & QKV_FLAG_RTN) {
-      QKV_HIP(launch_fill_zero_u32(labels, L.stage_bytes_labels / 4, s));
-      QKV_HIP(launch_fill_zero_u32(cent, L.stage_bytes_centroids / 4, s));
-    } else {
-      QKV_TRY(run_kmeans(cfg, y, wk, labels, workspace, ws, s));
-      QKV_HIP(launch_centroid_bf16(H, C, c, cent, s));
-    }
-    PackArgs pa;
-    pa.y = y;
-    pa.H = H;
-    pa.C = C;
-    pa.N = (int)N;
-    pa.labels = labels;
-    pa.centroids = cent;
-    pa.perm = pm;
-    pa.bits = cfg->bits;
-    pa.group = cfg->group;
-    pa.n_int4 = cfg->n_int4_channels;
-    pa.int4_words = g.int4_words;
-    pa.codes = reinterpret_cast<uint32_t*>(base + L.off_codes + (uint64_t)l * L.stage_bytes_codes);
-    pa.scales = reinterpret_cast<uint16_t*>(base + L.off_scales + (uint64_t)l * L.stage_bytes_scales);
-    pa.words = g.words;
-    pa.groups = g.groups;
-    const bool more = l + 1 < cfg->n_stages;
-    float* ynext = more ? reinterpret_cast<float*>(at(workspace, (l % 2 == 0) ? ws.ybuf0 : ws.ybuf1)) : nullptr;
-    pa.y_next = ynext;
-    QKV_HIP(launch_quant_pack(pa, s));
-    if (more) {
-      y.ptr = ynext;
-      y.dtype = 0;
-      y.stride_token = kHeadDim;
-      y.stride_head = N * kHeadDim;
-      // y_next is laid out [H][N][128]: token stride 128, head stride N*128
-    }
-  }
-  if (cfg->psac_rank > 0) {
-    const ChunkDecode d = decode_of(cfg, N, packed);
-    QKV_HIP(launch_psac_encode(d, view_of(x), U, reinterpret_cast<uint16_t*>(base + L.off_psac), s));
-  }
+int qkv_quantize_chunks_workspace_bytes(const qkv_config* cfg, int64_t n_tokens, int32_t n, size_t* out) {
+  QKV_TRY(check_config(cfg, "qkv_quantize_chunks_workspace_bytes"));
+  if (!out) return fail(QKV_EINVAL, "qkv_quantize_chunks_workspace_bytes: out is NULL");
+  if (n < 1 || n > kKmMaxBatch || n_tokens < cfg->n_clusters || n_tokens > ((int64_t)1 << 24))
+    return fail(QKV_EINVAL, "qkv_quantize_chunks_workspace_bytes: n %d not in [1, %d] or n_tokens %lld out of range",
+                n, kKmMaxBatch, (long long)n_tokens);
+  *out = (size_t)(align256(quant_ws(cfg, n_tokens).bytes) * (uint64_t)n);
   return ok();
 }
 
@@ -555,20 +619,45 @@ int qkv_psac_fit(const qkv_tensor* q_hist, int32_t n_heads, int32_t rank, int32_
   return ok();
 }
 
+// A one-problem k-means batch over caller buffers (step-level entry points).
+KmBatch single_batch(const qkv_config* cfg, const qkv_tensor* y, const float* w, float* centroids, uint8_t* labels,
+                     int32_t* counts, void* workspace, const QuantWs& ws) {
+  KmBatch b{};
+  b.n = 1;
+  b.dtype = y->dtype == QKV_F32 ? 0 : 1;
+  b.H = cfg->n_heads;
+  b.C = cfg->n_clusters;
+  b.N = y->n_tokens;
+  const TensorView v = view_of(y);
+  KmItem& it = b.it[0];
+  it.y = v.ptr;
+  it.stride_token = v.stride_token;
+  it.stride_head = v.stride_head;
+  it.w = w;
+  it.c = centroids;
+  it.planes = reinterpret_cast<uint16_t*>(at(workspace, ws.planes));
+  it.cn = reinterpret_cast<float*>(at(workspace, ws.cn));
+  it.labels = labels;
+  it.amb_count = reinterpret_cast<int*>(at(workspace, ws.amb_count));
+  it.counts = counts;
+  it.cent_bf16 = nullptr;
+  return b;
+}
+
 int qkv_kmeans_assign(const qkv_config* cfg, const qkv_tensor* y, const float* centroids, const float* w,
                       uint8_t* labels, void* workspace, size_t workspace_bytes, void* stream) {
   const char* fn = "qkv_kmeans_assign";
   QKV_TRY(check_config(cfg, fn));
   QKV_TRY(check_tensor(y, cfg->n_heads, fn));
   if (!centroids || !labels) return fail(QKV_EINVAL, "%s: centroids/labels NULL", fn);
+  if (y->n_tokens < cfg->n_clusters) return fail(QKV_EINVAL, "%s: n_tokens < n_clusters", fn);
   const QuantWs ws = quant_ws(cfg, y->n_tokens);
   QKV_TRY(check_ws(workspace, workspace_bytes, ws.ybuf0, fn));
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  uint16_t* planes = reinterpret_cast<uint16_t*>(at(workspace, ws.planes));
-  float* cn = reinterpret_cast<float*>(at(workspace, ws.cn));
-  int* amb = reinterpret_cast<int*>(at(workspace, ws.amb_count));
-  QKV_HIP(launch_centroid_prep(cfg->n_heads, cfg->n_clusters, centroids, w, planes, cn, amb, s));
-  QKV_HIP(launch_kmeans_assign(view_of(y), cfg->n_heads, cfg->n_clusters, planes, cn, centroids, w, labels, amb, s));
+  // the kernels only read the centroids here
+  const KmBatch b = single_batch(cfg, y, w, const_cast<float*>(centroids), labels, nullptr, workspace, ws);
+  QKV_HIP(launch_centroid_prep(b, s));
+  QKV_HIP(launch_kmeans_assign(b, s));
   return ok();
 }
 
@@ -580,9 +669,8 @@ int qkv_kmeans_update(const qkv_config* cfg, const qkv_tensor* y, const uint8_t*
   if (!centroids || !labels) return fail(QKV_EINVAL, "%s: centroids/labels NULL", fn);
   const QuantWs ws = quant_ws(cfg, y->n_tokens);
   QKV_TRY(check_ws(workspace, workspace_bytes, ws.ybuf0, fn));
-  QKV_HIP(launch_kmeans_update(view_of(y), cfg->n_heads, cfg->n_clusters, labels, centroids, counts, nullptr,
-                               nullptr, nullptr, reinterpret_cast<int*>(at(workspace, ws.amb_count)),
-                               reinterpret_cast<hipStream_t>(stream)));
+  const KmBatch b = single_batch(cfg, y, nullptr, centroids, const_cast<uint8_t*>(labels), counts, workspace, ws);
+  QKV_HIP(launch_kmeans_update(b, false, reinterpret_cast<hipStream_t>(stream)));
   return ok();
 }
 
@@ -604,7 +692,15 @@ int qkv_quant_pack(const qkv_config* cfg, const qkv_tensor* y, const uint8_t* la
   uint8_t* lab_dst = base + L.off_labels + (uint64_t)stage * L.stage_bytes_labels;
   if (lab_dst != labels) QKV_HIP(hipMemcpyAsync(lab_dst, labels, (size_t)cfg->n_heads * N, hipMemcpyDeviceToDevice, s));
   uint16_t* cent = reinterpret_cast<uint16_t*>(base + L.off_centroids + (uint64_t)stage * L.stage_bytes_centroids);
-  QKV_HIP(launch_centroid_bf16(cfg->n_heads, cfg->n_clusters, centroids, cent, s));
+  {
+    KmBatch b{};
+    b.n = 1;
+    b.H = cfg->n_heads;
+    b.C = cfg->n_clusters;
+    b.it[0].c = const_cast<float*>(centroids);   // read only
+    b.it[0].cent_bf16 = cent;
+    QKV_HIP(launch_centroid_bf16(b, s));
+  }
   const uint8_t* pm = cfg->n_int4_channels > 0 ? perm : nullptr;
   if (pm) QKV_HIP(launch_copy_perm(pm, base + L.off_perm, cfg->n_heads, s));
   PackArgs pa;
