@@ -598,12 +598,26 @@ __global__ __launch_bounds__(256) void k_update(KmBatch b, int refresh) {
   for (int t0 = 0; t0 < N; t0 += kUpdWindow) {
     // this thread's labels of the window (tokens t0 + tid + 256 x), one batch
     // of loads, kept in registers for both counting passes
+    // thread tid holds the labels of window tokens tid*32 .. tid*32 + 31,
+    // fetched as dwords when the head's labels are 4-byte aligned (N % 4 == 0)
     uint32_t kk[kUpdWindow / 256];
+    {
+      const int i0 = t0 + tid * 32;
+      if ((N & 3) == 0 && i0 + 32 <= N) {
+        uint32_t wv[8];
+        const uint32_t* l4 = reinterpret_cast<const uint32_t*>(lab + i0);
 #pragma unroll
-    for (int x = 0; x < kUpdWindow / 256; ++x) {
-      const int i = t0 + tid + 256 * x;
-      const uint32_t l = lab[min(i, N - 1)];                          // unconditional: one batch of loads
-      kk[x] = i < N ? l - (uint32_t)c0 : 0xFFFFFFFFu;                 // unsigned: in the group iff < 8
+        for (int q = 0; q < 8; ++q) wv[q] = l4[q];
+#pragma unroll
+        for (int x = 0; x < 32; ++x) kk[x] = ((wv[x >> 2] >> (8 * (x & 3))) & 0xFFu) - (uint32_t)c0;
+      } else {
+#pragma unroll
+        for (int x = 0; x < 32; ++x) {
+          const int i = i0 + x;
+          const uint32_t l = lab[min(i, N - 1)];                      // unconditional: one batch of loads
+          kk[x] = i < N ? l - (uint32_t)c0 : 0xFFFFFFFFu;             // unsigned: in the group iff < 8
+        }
+      }
     }
     // (1) compact the window's members of the group into s_tmp (token << 3 |
     // cluster): per wave one ballot per label slot, the wave's range from the
@@ -623,7 +637,7 @@ __global__ __launch_bounds__(256) void k_update(KmBatch b, int refresh) {
       const uint64_t m = __ballot(in);
       if (in) {
         const int pos = run + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-        s_tmp[pos] = (uint16_t)(((tid + 256 * x) << 3) | kk[x]);
+        s_tmp[pos] = (uint16_t)(((tid * 32 + x) << 3) | kk[x]);
       }
       run += __popcll(m);
     }
