@@ -535,6 +535,7 @@ __global__ __launch_bounds__(kAsgThreads) void k_assign(KmBatch b, int G) {
 // An empty cluster keeps its centroid (and its operand planes and norm).
 constexpr int kUpdClusters = 8;
 constexpr int kUpdWindow = 8192;          // token index << 3 fits 16 bits
+constexpr int kUpdRows = 12;            // row loads (2 rows each) in flight per wave
 
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
@@ -564,6 +565,7 @@ __global__ __launch_bounds__(256) void k_update(KmBatch b, int refresh) {
   const bool plain = !F32 && N <= kUpdWindow;   // certified float64 sums
   DD acc[2][2] = {{{0.0, 0.0}, {0.0, 0.0}}, {{0.0, 0.0}, {0.0, 0.0}}};
   int total[2] = {0, 0};
+  bool old_fin[2] = {true, true};               // finished after the window loop (2 channels per lane)
 
   // member rows [m0, m1) of the window list: value pairs (channels lane*2, +1)
   auto row_pair = [&](int t0, int mm, float& x0, float& x1) __attribute__((always_inline)) -> uint32_t {
@@ -659,52 +661,133 @@ __global__ __launch_bounds__(256) void k_update(KmBatch b, int refresh) {
       s_mem[atomicAdd(&s_cur[v & 7], 1)] = (uint16_t)(v >> 3);
     }
     __syncthreads();
+    // wave w: clusters 2w and 2w + 1, member rows [ma, mb) and [mb, mc) of the list
+    const int ma = s_off[wave * 2], mb = s_off[wave * 2 + 1], mc = s_off[wave * 2 + 2];
+    total[0] += mb - ma;
+    total[1] += mc - mb;
+    if (plain) {
+      // Both clusters at once, 8 bytes per lane: lane group g = lane / 32 takes rows
+      // ma + g, ma + g + 2, ...; lane channels c4 .. c4 + 3.  Float64 partial sums per
+      // group, joined across the two groups (exact under the certificate, so any
+      // grouping gives the same sum).
+      const int g = lane >> 5, c4 = (lane & 31) * 4;
+      const int64_t hoff4 = (int64_t)h * y.stride_head + c4;
+      double sa[4], sb[4];
+      u16x2 mxa[2], mna[2], mxb[2], mnb[2];      // magnitudes: max, and min nonzero - 1
 #pragma unroll
-    for (int cc = 0; cc < 2; ++cc) {
-      const int k = wave * 2 + cc;
-      const int m0 = s_off[k], m1 = s_off[k + 1];
-      total[cc] += m1 - m0;
-      if (plain) {
-        double s0 = 0.0, s1 = 0.0;
-        u16x2 mx = {0, 0}, mn = {0xFFFF, 0xFFFF};          // magnitudes: max, and min nonzero - 1
-        for (int m = m0; m < m1; m += 16) {
-          uint32_t raw[16];                                 // bf16 pairs (channels lane*2, +1)
+      for (int e = 0; e < 4; ++e) sa[e] = sb[e] = 0.0;
 #pragma unroll
-          for (int q = 0; q < 16; ++q) {
-            const int64_t off = (int64_t)(t0 + s_mem[min(m + q, m1 - 1)]) * y.stride_token + hoff;
-            raw[q] = *reinterpret_cast<const uint32_t*>(reinterpret_cast<const uint16_t*>(y.ptr) + off);
-          }
+      for (int p = 0; p < 2; ++p) {
+        mxa[p] = mxb[p] = u16x2{0, 0};
+        mna[p] = mnb[p] = u16x2{0xFFFF, 0xFFFF};
+      }
+      for (int m = ma; m < mc; m += 2 * kUpdRows) {
+        uint2 raw[kUpdRows];
 #pragma unroll
-          for (int q = 0; q < 16; ++q) {
-            if (m + q < m1) {
-              s0 += (double)bf16_bits_to_f32(raw[q] & 0xFFFFu);
-              s1 += (double)bf16_bits_to_f32(raw[q] >> 16);
-              const u16x2 mag = __builtin_bit_cast(u16x2, raw[q] & 0x7FFF7FFFu);
-              const u16x2 one = {1, 1};
-              mx = __builtin_elementwise_max(mx, mag);
-              mn = __builtin_elementwise_min(mn, mag - one);    // a zero wraps to 0xFFFF: ignored
+        for (int q = 0; q < kUpdRows; ++q) {
+          const int r = min(m + 2 * q + g, mc - 1);
+          raw[q] = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(y.ptr) +
+                                                   (int64_t)(t0 + s_mem[r]) * y.stride_token + hoff4);
+        }
+#pragma unroll
+        for (int q = 0; q < kUpdRows; ++q) {
+          const int r = m + 2 * q + g;
+          if (r < mc) {
+            const bool inA = r < mb;
+            const uint32_t w2[2] = {raw[q].x, raw[q].y};
+#pragma unroll
+            for (int p = 0; p < 2; ++p) {
+              const double v0 = (double)bf16_bits_to_f32(w2[p] & 0xFFFFu), v1 = (double)bf16_bits_to_f32(w2[p] >> 16);
+              sa[2 * p] += inA ? v0 : 0.0;
+              sa[2 * p + 1] += inA ? v1 : 0.0;
+              sb[2 * p] += inA ? 0.0 : v0;
+              sb[2 * p + 1] += inA ? 0.0 : v1;
+              const u16x2 mag = __builtin_bit_cast(u16x2, w2[p] & 0x7FFF7FFFu);
+              const u16x2 m1 = mag - u16x2{1, 1};           // a zero wraps to 0xFFFF: ignored by min
+              if (inA) {
+                mxa[p] = __builtin_elementwise_max(mxa[p], mag);
+                mna[p] = __builtin_elementwise_min(mna[p], m1);
+              } else {
+                mxb[p] = __builtin_elementwise_max(mxb[p], mag);
+                mnb[p] = __builtin_elementwise_min(mnb[p], m1);
+              }
             }
           }
         }
-        const int lg = 32 - __builtin_clz((unsigned)max(m1 - m0, 1));   // >= ceil(log2 n)
-        bool exact[2];
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          const int emax = (int)(mx[e] >> 7), nz = (int)mn[e] + 1;      // nz: smallest nonzero magnitude
-          const int emin = max((nz >> 7) & 0xFF, 1);                     // subnormals share exponent 1's unit
-          exact[e] = mn[e] == 0xFFFF || (emax < 0xFF && emax - emin + lg <= 44);
-        }
-        acc[cc][0] = DD{s0, 0.0};
-        acc[cc][1] = DD{s1, 0.0};
-        if (__any(!exact[0] || !exact[1])) {              // rare: redo this cluster exactly
-          DD a0{0.0, 0.0}, a1{0.0, 0.0};
-          dd_rows(t0, m0, m1, a0, a1);
-          if (!exact[0]) acc[cc][0] = a0;
-          if (!exact[1]) acc[cc][1] = a1;
-        }
-      } else {
-        dd_rows(t0, m0, m1, acc[cc][0], acc[cc][1]);
       }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        sa[e] += __shfl_xor(sa[e], 32);
+        sb[e] += __shfl_xor(sb[e], 32);
+      }
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        mxa[p] = __builtin_elementwise_max(mxa[p], __builtin_bit_cast(u16x2, __shfl_xor(__builtin_bit_cast(int, mxa[p]), 32)));
+        mna[p] = __builtin_elementwise_min(mna[p], __builtin_bit_cast(u16x2, __shfl_xor(__builtin_bit_cast(int, mna[p]), 32)));
+        mxb[p] = __builtin_elementwise_max(mxb[p], __builtin_bit_cast(u16x2, __shfl_xor(__builtin_bit_cast(int, mxb[p]), 32)));
+        mnb[p] = __builtin_elementwise_min(mnb[p], __builtin_bit_cast(u16x2, __shfl_xor(__builtin_bit_cast(int, mnb[p]), 32)));
+      }
+      // certificate per cluster over this lane's 4 channels, then over the wave
+      auto certified = [&](const u16x2 (&mx)[2], const u16x2 (&mn)[2], int n) __attribute__((always_inline)) {
+        const int lg = 32 - __builtin_clz((unsigned)max(n, 1));   // >= ceil(log2 n)
+        bool ok = true;
+#pragma unroll
+        for (int p = 0; p < 2; ++p)
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            const int emax = (int)(mx[p][e] >> 7), nz = (int)mn[p][e] + 1;      // nz: smallest nonzero magnitude
+            const int emin = max((nz >> 7) & 0xFF, 1);                           // subnormals share exponent 1's unit
+            ok = ok && (mn[p][e] == 0xFFFF || (emax < 0xFF && emax - emin + lg <= 44));
+          }
+        return __all(ok) != 0;
+      };
+      const bool okc[2] = {certified(mxa, mna, mb - ma), certified(mxb, mnb, mc - mb)};
+      // certified clusters: lane group 0 finishes the first, group 1 the second
+      {
+        const int cc = g;
+        const int n = cc == 0 ? mb - ma : mc - mb;
+        const int j = c0 + wave * 2 + cc;
+        if (okc[cc] && n > 0 && j < C) {
+          float cv[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) cv[e] = (float)((cc == 0 ? sa[e] : sb[e]) / (double)n);
+          *reinterpret_cast<float4*>(c + ((int64_t)h * C + j) * kHeadDim + c4) = make_float4(cv[0], cv[1], cv[2], cv[3]);
+          if (planes) {   // operand planes (-2 w c) and weighted norm for the next assign
+            double nrm = 0.0;
+            uint32_t hw[2], lw[2];
+#pragma unroll
+            for (int p = 0; p < 2; ++p) {
+              hw[p] = lw[p] = 0u;
+#pragma unroll
+              for (int e = 0; e < 2; ++e) {
+                const int k = c4 + 2 * p + e;
+                const float wv = w ? w[h * kHeadDim + k] : 1.0f;
+                const float bb = -2.0f * (wv * cv[2 * p + e]);
+                const uint32_t hi = f32_to_bf16_bits(bb);
+                hw[p] |= hi << (16 * e);
+                lw[p] |= f32_to_bf16_bits(bb - bf16_bits_to_f32(hi)) << (16 * e);
+                nrm += (double)wv * ((double)cv[2 * p + e] * (double)cv[2 * p + e]);
+              }
+            }
+            *reinterpret_cast<uint2*>(planes + ((int64_t)h * 2 * C + j) * kHeadDim + c4) = make_uint2(hw[0], hw[1]);
+            *reinterpret_cast<uint2*>(planes + ((int64_t)h * 2 * C + C + j) * kHeadDim + c4) = make_uint2(lw[0], lw[1]);
+#pragma unroll
+            for (int off = 1; off < 32; off <<= 1) nrm += __shfl_xor(nrm, off);   // within the lane group
+            if ((lane & 31) == 0) cn[h * C + j] = (float)nrm;
+          }
+        }
+      }
+#pragma unroll
+      for (int cc = 0; cc < 2; ++cc) {
+        old_fin[cc] = !okc[cc];
+        if (!okc[cc]) {                             // rare: this cluster again in double-double
+          const int m0 = cc == 0 ? ma : mb, m1 = cc == 0 ? mb : mc;
+          dd_rows(t0, m0, m1, acc[cc][0], acc[cc][1]);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int cc = 0; cc < 2; ++cc) dd_rows(t0, cc == 0 ? ma : mb, cc == 0 ? mb : mc, acc[cc][0], acc[cc][1]);
     }
     __syncthreads();                           // the lists are rebuilt for the next window
   }
@@ -714,7 +797,7 @@ __global__ __launch_bounds__(256) void k_update(KmBatch b, int refresh) {
     if (j >= C) continue;
     const int n = total[cc];
     if (counts && lane == 0) counts[h * C + j] = n;
-    if (n == 0) continue;
+    if (n == 0 || !old_fin[cc]) continue;
     const float cv[2] = {(float)(acc[cc][0].hi / (double)n), (float)(acc[cc][1].hi / (double)n)};
     *reinterpret_cast<float2*>(c + ((int64_t)h * C + j) * kHeadDim + lane * 2) = make_float2(cv[0], cv[1]);
     if (planes) {   // operand planes (-2 w c) and weighted norm for the next assign
