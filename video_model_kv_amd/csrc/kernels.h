@@ -39,6 +39,8 @@ struct KmItem {
   int* amb_count;                // close calls of the last assign (statistics), or null
   int32_t* counts;               // member counts [H][C] from the update, or null
   uint16_t* cent_bf16;           // bf16 centroids written by launch_centroid_bf16
+  int* grp_off;                  // [H][C + 1] cluster offsets from launch_kmeans_group, or null
+  uint16_t* grp_list;            // [H][N] tokens ordered by cluster (same producer)
 };
 constexpr int kKmMaxBatch = 16;
 struct KmBatch {
@@ -56,6 +58,10 @@ hipError_t launch_kmeans_assign(const KmBatch& b, hipStream_t s);
 // with refresh it also rewrites the operand planes / norms for the next
 // assign.  Zeroes amb_count.
 hipError_t launch_kmeans_update(const KmBatch& b, bool refresh, hipStream_t s);
+// Counting sort of each head's tokens by label into grp_off / grp_list (heads of
+// at most kGroupMaxTokens tokens); the update then reads its clusters' members from there.
+constexpr int kGroupMaxTokens = 8192;
+hipError_t launch_kmeans_group(const KmBatch& b, hipStream_t s);
 hipError_t launch_centroid_bf16(const KmBatch& b, hipStream_t s);
 hipError_t launch_fill_zero_u32(void* p, size_t n_words, hipStream_t s);
 

@@ -535,12 +535,81 @@ __global__ __launch_bounds__(kAsgThreads) void k_assign(KmBatch b, int G) {
 // An empty cluster keeps its centroid (and its operand planes and norm).
 constexpr int kUpdClusters = 8;
 constexpr int kUpdWindow = 8192;          // token index << 3 fits 16 bits
+static_assert(kUpdWindow == kGroupMaxTokens, "grouped heads fit one update window");
 constexpr int kUpdRows = 12;            // row loads (2 rows each) in flight per wave
 
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
-template <bool F32>
-__global__ __launch_bounds__(256) void k_update(KmBatch b, int refresh) {
+// Grouping of a head's tokens by label for the update (counting sort): one
+// workgroup per (problem, head of at most kUpdWindow tokens) writes the cluster
+// offsets [C + 1] and the token list ordered by cluster, so that the update's
+// workgroups (32 per head) read their clusters' members instead of each
+// scanning all labels.
+__global__ __launch_bounds__(256) void k_group(KmBatch b) {
+  const KmItem& it = b.it[blockIdx.y];
+  const int C = b.C, N = (int)b.N, h = blockIdx.x;
+  __shared__ int s_c[256], s_o[257];
+  __shared__ uint16_t s_l[kUpdWindow];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const uint8_t* lab = it.labels + (int64_t)h * N;
+  uint32_t kk[kUpdWindow / 256];                 // labels of tokens tid*32 .. tid*32 + 31
+  {
+    const int i0 = tid * 32;
+    if ((N & 3) == 0 && i0 + 32 <= N) {
+      uint32_t wv[8];
+      const uint32_t* l4 = reinterpret_cast<const uint32_t*>(lab + i0);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) wv[q] = l4[q];
+#pragma unroll
+      for (int x = 0; x < 32; ++x) kk[x] = (wv[x >> 2] >> (8 * (x & 3))) & 0xFFu;
+    } else {
+#pragma unroll
+      for (int x = 0; x < 32; ++x) {
+        const int i = i0 + x;
+        const uint32_t l = lab[min(i, N - 1)];
+        kk[x] = i < N ? l : 0xFFFFFFFFu;
+      }
+    }
+  }
+  s_c[tid] = 0;
+  __syncthreads();
+#pragma unroll
+  for (int x = 0; x < 32; ++x)
+    if (kk[x] < (uint32_t)C) atomicAdd(&s_c[kk[x]], 1);
+  __syncthreads();
+  if (wave == 0) {                               // exclusive prefix over the clusters, four per lane
+    int a[4], sum = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      a[e] = s_c[lane * 4 + e];
+      sum += a[e];
+    }
+    int incl = sum;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int t = __shfl_up(incl, o);
+      if (lane >= o) incl += t;
+    }
+    int ex = incl - sum;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      s_o[lane * 4 + e] = ex;
+      s_c[lane * 4 + e] = ex;                    // the cursor of the scatter
+      ex += a[e];
+    }
+    if (lane == 63) s_o[256] = incl;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int x = 0; x < 32; ++x)
+    if (kk[x] < (uint32_t)C) s_l[atomicAdd(&s_c[kk[x]], 1)] = (uint16_t)(tid * 32 + x);
+  __syncthreads();
+  for (int k = tid; k <= C; k += 256) it.grp_off[(int64_t)h * (C + 1) + k] = k < C ? s_o[k] : s_o[256];
+  for (int e = tid; e < N; e += 256) it.grp_list[(int64_t)h * N + e] = s_l[e];
+}
+
+template <bool F32, bool GROUPED>
+__global__ __launch_bounds__(256, 4) void k_update(KmBatch b, int refresh) {
   const KmItem& it = b.it[blockIdx.y];
   const TensorView y = item_view(b, it);
   const int C = b.C, n_heads = b.H;
@@ -552,7 +621,7 @@ __global__ __launch_bounds__(256) void k_update(KmBatch b, int refresh) {
   int32_t* __restrict__ counts = it.counts;
   int* __restrict__ amb_count = it.amb_count;
   __shared__ int s_cnt[kUpdClusters], s_off[kUpdClusters + 1], s_cur[kUpdClusters];
-  __shared__ uint16_t s_mem[kUpdWindow], s_tmp[kUpdWindow];
+  __shared__ uint16_t s_mem[kUpdWindow];
   __shared__ int s_wtot[4];
   const int groups = (C + kUpdClusters - 1) / kUpdClusters;
   const uint32_t logical = xcd_remap(blockIdx.x, (uint32_t)(n_heads * groups));
@@ -598,69 +667,77 @@ __global__ __launch_bounds__(256) void k_update(KmBatch b, int refresh) {
   };
 
   for (int t0 = 0; t0 < N; t0 += kUpdWindow) {
-    // this thread's labels of the window (tokens t0 + tid + 256 x), one batch
-    // of loads, kept in registers for both counting passes
-    // thread tid holds the labels of window tokens tid*32 .. tid*32 + 31,
-    // fetched as dwords when the head's labels are 4-byte aligned (N % 4 == 0)
-    uint32_t kk[kUpdWindow / 256];
-    {
-      const int i0 = t0 + tid * 32;
-      if ((N & 3) == 0 && i0 + 32 <= N) {
-        uint32_t wv[8];
-        const uint32_t* l4 = reinterpret_cast<const uint32_t*>(lab + i0);
-#pragma unroll
-        for (int q = 0; q < 8; ++q) wv[q] = l4[q];
-#pragma unroll
-        for (int x = 0; x < 32; ++x) kk[x] = ((wv[x >> 2] >> (8 * (x & 3))) & 0xFFu) - (uint32_t)c0;
-      } else {
-#pragma unroll
-        for (int x = 0; x < 32; ++x) {
-          const int i = i0 + x;
-          const uint32_t l = lab[min(i, N - 1)];                      // unconditional: one batch of loads
-          kk[x] = i < N ? l - (uint32_t)c0 : 0xFFFFFFFFu;             // unsigned: in the group iff < 8
+    if constexpr (GROUPED) {                     // the head's tokens already ordered by cluster (k_group)
+      const int* go = it.grp_off + (int64_t)h * (C + 1);
+      const int base = go[c0];
+      const int M = go[min(c0 + kUpdClusters, C)] - base;
+      if (tid <= kUpdClusters) s_off[tid] = go[min(c0 + tid, C)] - base;
+      for (int e = tid; e < M; e += 256) s_mem[e] = it.grp_list[(int64_t)h * N + base + e];
+      __syncthreads();
+    } else {
+      __shared__ uint16_t s_tmp[kUpdWindow];
+      // thread tid holds the labels of window tokens tid*32 .. tid*32 + 31,
+      // fetched as dwords when the head's labels are 4-byte aligned (N % 4 == 0)
+      uint32_t kk[kUpdWindow / 256];
+      {
+        const int i0 = t0 + tid * 32;
+        if ((N & 3) == 0 && i0 + 32 <= N) {
+          uint32_t wv[8];
+          const uint32_t* l4 = reinterpret_cast<const uint32_t*>(lab + i0);
+  #pragma unroll
+          for (int q = 0; q < 8; ++q) wv[q] = l4[q];
+  #pragma unroll
+          for (int x = 0; x < 32; ++x) kk[x] = ((wv[x >> 2] >> (8 * (x & 3))) & 0xFFu) - (uint32_t)c0;
+        } else {
+  #pragma unroll
+          for (int x = 0; x < 32; ++x) {
+            const int i = i0 + x;
+            const uint32_t l = lab[min(i, N - 1)];                      // unconditional: one batch of loads
+            kk[x] = i < N ? l - (uint32_t)c0 : 0xFFFFFFFFu;             // unsigned: in the group iff < 8
+          }
         }
       }
-    }
-    // (1) compact the window's members of the group into s_tmp (token << 3 |
-    // cluster): per wave one ballot per label slot, the wave's range from the
-    // wave totals (no atomics);  (2) counting sort of s_tmp by cluster into s_mem.
-    int wtot = 0;
-#pragma unroll
-    for (int x = 0; x < kUpdWindow / 256; ++x) wtot += __popcll(__ballot(kk[x] < (uint32_t)kUpdClusters));
-    if (lane == 0) s_wtot[wave] = wtot;
-    if (tid < kUpdClusters) s_cnt[tid] = 0;
-    __syncthreads();
-    int run = 0;
-    for (int v = 0; v < wave; ++v) run += s_wtot[v];
-    const int n_mem = s_wtot[0] + s_wtot[1] + s_wtot[2] + s_wtot[3];
-#pragma unroll
-    for (int x = 0; x < kUpdWindow / 256; ++x) {
-      const bool in = kk[x] < (uint32_t)kUpdClusters;
-      const uint64_t m = __ballot(in);
-      if (in) {
-        const int pos = run + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-        s_tmp[pos] = (uint16_t)(((tid * 32 + x) << 3) | kk[x]);
+      // (1) compact the window's members of the group into s_tmp (token << 3 |
+      // cluster): per wave one ballot per label slot, the wave's range from the
+      // wave totals (no atomics);  (2) counting sort of s_tmp by cluster into s_mem.
+      int wtot = 0;
+  #pragma unroll
+      for (int x = 0; x < kUpdWindow / 256; ++x) wtot += __popcll(__ballot(kk[x] < (uint32_t)kUpdClusters));
+      if (lane == 0) s_wtot[wave] = wtot;
+      if (tid < kUpdClusters) s_cnt[tid] = 0;
+      __syncthreads();
+      int run = 0;
+      for (int v = 0; v < wave; ++v) run += s_wtot[v];
+      const int n_mem = s_wtot[0] + s_wtot[1] + s_wtot[2] + s_wtot[3];
+  #pragma unroll
+      for (int x = 0; x < kUpdWindow / 256; ++x) {
+        const bool in = kk[x] < (uint32_t)kUpdClusters;
+        const uint64_t m = __ballot(in);
+        if (in) {
+          const int pos = run + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+          s_tmp[pos] = (uint16_t)(((tid * 32 + x) << 3) | kk[x]);
+        }
+        run += __popcll(m);
       }
-      run += __popcll(m);
-    }
-    __syncthreads();
-    for (int e = tid; e < n_mem; e += 256) atomicAdd(&s_cnt[s_tmp[e] & 7], 1);
-    __syncthreads();
-    if (tid == 0) {
-      int a = 0;
-      for (int k = 0; k < kUpdClusters; ++k) {
-        s_off[k] = a;
-        s_cur[k] = a;
-        a += s_cnt[k];
+      __syncthreads();
+      for (int e = tid; e < n_mem; e += 256) atomicAdd(&s_cnt[s_tmp[e] & 7], 1);
+      __syncthreads();
+      if (tid == 0) {
+        int a = 0;
+        for (int k = 0; k < kUpdClusters; ++k) {
+          s_off[k] = a;
+          s_cur[k] = a;
+          a += s_cnt[k];
+        }
+        s_off[kUpdClusters] = a;
       }
-      s_off[kUpdClusters] = a;
+      __syncthreads();
+      for (int e = tid; e < n_mem; e += 256) {
+        const uint32_t v = s_tmp[e];
+        s_mem[atomicAdd(&s_cur[v & 7], 1)] = (uint16_t)(v >> 3);
+      }
+      __syncthreads();
     }
-    __syncthreads();
-    for (int e = tid; e < n_mem; e += 256) {
-      const uint32_t v = s_tmp[e];
-      s_mem[atomicAdd(&s_cur[v & 7], 1)] = (uint16_t)(v >> 3);
-    }
-    __syncthreads();
     // wave w: clusters 2w and 2w + 1, member rows [ma, mb) and [mb, mc) of the list
     const int ma = s_off[wave * 2], mb = s_off[wave * 2 + 1], mc = s_off[wave * 2 + 2];
     total[0] += mb - ma;
@@ -872,8 +949,20 @@ hipError_t launch_kmeans_assign(const KmBatch& b, hipStream_t s) {
 
 hipError_t launch_kmeans_update(const KmBatch& b, bool refresh, hipStream_t s) {
   const dim3 grid((unsigned)(b.H * ((b.C + kUpdClusters - 1) / kUpdClusters)), b.n);
-  if (b.dtype == 0) hipLaunchKernelGGL(k_update<true>, grid, dim3(256), 0, s, b, refresh ? 1 : 0);
-  else hipLaunchKernelGGL(k_update<false>, grid, dim3(256), 0, s, b, refresh ? 1 : 0);
+  const bool grouped = b.it[0].grp_off != nullptr && b.N <= kUpdWindow;   // set for all problems or none
+  if (grouped) {
+    if (b.dtype == 0) hipLaunchKernelGGL((k_update<true, true>), grid, dim3(256), 0, s, b, refresh ? 1 : 0);
+    else hipLaunchKernelGGL((k_update<false, true>), grid, dim3(256), 0, s, b, refresh ? 1 : 0);
+  } else {
+    if (b.dtype == 0) hipLaunchKernelGGL((k_update<true, false>), grid, dim3(256), 0, s, b, refresh ? 1 : 0);
+    else hipLaunchKernelGGL((k_update<false, false>), grid, dim3(256), 0, s, b, refresh ? 1 : 0);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_kmeans_group(const KmBatch& b, hipStream_t s) {
+  if (b.N > kUpdWindow || b.C > 256) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_group, dim3(b.H, b.n), dim3(256), 0, s, b);
   return hipGetLastError();
 }
 

@@ -147,7 +147,7 @@ TensorView view_of(const qkv_tensor* t) {
 
 // ---- workspace plans ----
 struct QuantWs {
-  uint64_t c, planes, cn, amb_count, ybuf0, ybuf1, bytes;
+  uint64_t c, planes, cn, amb_count, grp_off, grp_list, ybuf0, ybuf1, bytes;
 };
 
 QuantWs quant_ws(const qkv_config* c, int64_t n) {
@@ -158,6 +158,8 @@ QuantWs quant_ws(const qkv_config* c, int64_t n) {
   w.planes = off;  off += align256(H * 2 * C * kHeadDim * 2);
   w.cn = off;      off += align256(H * C * 4);
   w.amb_count = off; off += 256;
+  w.grp_off = off; off += align256(H * (C + 1) * 4);
+  w.grp_list = off; off += align256(H * (uint64_t)n * 2);
   w.ybuf0 = off;   if (c->n_stages > 1) off += align256(H * (uint64_t)n * kHeadDim * 4);
   w.ybuf1 = off;   if (c->n_stages > 2) off += align256(H * (uint64_t)n * kHeadDim * 4);
   w.bytes = off;
@@ -248,10 +250,12 @@ uint8_t* at(void* base, uint64_t off) { return reinterpret_cast<uint8_t*>(base) 
 
 // Run the k-means protocol of one stage on every problem of the batch.
 int run_kmeans(const qkv_config* cfg, const KmBatch& b, hipStream_t s) {
+  const bool grouped = b.it[0].grp_off != nullptr;
   QKV_HIP(launch_kmeans_init(b, s));
   QKV_HIP(launch_centroid_prep(b, s));
   for (int it = 0; it < cfg->kmeans_iters; ++it) {
     QKV_HIP(launch_kmeans_assign(b, s));
+    if (grouped) QKV_HIP(launch_kmeans_group(b, s));
     QKV_HIP(launch_kmeans_update(b, it + 1 < cfg->kmeans_iters, s));
   }
   return QKV_OK;
@@ -315,6 +319,9 @@ int quantize_batch(int32_t n, const qkv_config* const* cfgs, const qkv_tensor* c
     it.cn = reinterpret_cast<float*>(wsp + ws.cn);
     it.amb_count = reinterpret_cast<int*>(wsp + ws.amb_count);
     it.counts = nullptr;
+    const bool grouped = N <= kGroupMaxTokens;   // the update reads the tokens grouped by cluster
+    it.grp_off = grouped ? reinterpret_cast<int*>(wsp + ws.grp_off) : nullptr;
+    it.grp_list = grouped ? reinterpret_cast<uint16_t*>(wsp + ws.grp_list) : nullptr;
     if (cfgs[p]->n_int4_channels > 0)
       QKV_HIP(launch_copy_perm(side->perm, reinterpret_cast<uint8_t*>(packed[p]) + L[p].off_perm, H, s));
   }
@@ -641,6 +648,8 @@ KmBatch single_batch(const qkv_config* cfg, const qkv_tensor* y, const float* w,
   it.amb_count = reinterpret_cast<int*>(at(workspace, ws.amb_count));
   it.counts = counts;
   it.cent_bf16 = nullptr;
+  it.grp_off = nullptr;
+  it.grp_list = nullptr;
   return b;
 }
 
