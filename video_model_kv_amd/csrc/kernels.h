@@ -79,6 +79,14 @@ struct PackArgs {
   float* y_next;               // f32 [H][N][128] or null
 };
 hipError_t launch_quant_pack(const PackArgs& a, hipStream_t s);
+// Several problems of the fast layout (no channel permutation) that share group,
+// bits, dtype, H and N, in one launch (grid slice per problem).
+struct PackBatch {
+  int n;
+  PackArgs a[kKmMaxBatch];
+};
+bool quant_pack_batchable(const PackArgs& a, const PackArgs& b0);
+hipError_t launch_quant_pack_batch(const PackBatch& b, hipStream_t s);
 
 hipError_t launch_dequantize(const ChunkDecode& d, void* out, int out_dtype, int64_t stride_token,
                              int64_t stride_head, hipStream_t s);

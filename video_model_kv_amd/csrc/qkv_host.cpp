@@ -346,6 +346,8 @@ int quantize_batch(int32_t n, const qkv_config* const* cfgs, const qkv_tensor* c
       QKV_HIP(launch_centroid_bf16(b, s));
     }
     const bool more = l + 1 < c0->n_stages;
+    PackBatch pb;
+    pb.n = 0;
     for (int p = 0; p < n; ++p) {
       const qkv_config* cfg = cfgs[p];
       uint8_t* base = reinterpret_cast<uint8_t*>(packed[p]);
@@ -368,7 +370,9 @@ int quantize_batch(int32_t n, const qkv_config* const* cfgs, const qkv_tensor* c
       pa.groups = g[p].groups;
       float* ynext = more ? reinterpret_cast<float*>(wsp + ((l % 2 == 0) ? ws.ybuf0 : ws.ybuf1)) : nullptr;
       pa.y_next = ynext;
-      QKV_HIP(launch_quant_pack(pa, s));
+      if (pb.n > 0 && quant_pack_batchable(pa, pb.a[0])) pb.a[pb.n++] = pa;   // joins the batched launch
+      else if (pb.n == 0 && quant_pack_batchable(pa, pa)) pb.a[pb.n++] = pa;
+      else QKV_HIP(launch_quant_pack(pa, s));
       if (more) {
         // y_next is laid out [H][N][128]: token stride 128, head stride N*128
         y[p].ptr = ynext;
@@ -377,6 +381,7 @@ int quantize_batch(int32_t n, const qkv_config* const* cfgs, const qkv_tensor* c
         y[p].stride_head = N * kHeadDim;
       }
     }
+    if (pb.n > 0) QKV_HIP(launch_quant_pack_batch(pb, s));
   }
   for (int p = 0; p < n; ++p) {
     if (cfgs[p]->psac_rank > 0) {

@@ -156,7 +156,8 @@ __global__ __launch_bounds__(256) void k_quant_pack(PackArgs a) {
 // shuffles; two lanes' INT2 codes form one word.  Same arithmetic as
 // k_quant_pack.
 template <int G, int BITS, bool F32>
-__global__ __launch_bounds__(256) void k_quant_pack_fast(PackArgs a) {
+__global__ __launch_bounds__(256) void k_quant_pack_fast(PackBatch pb) {
+  const PackArgs& a = pb.a[blockIdx.y];
   constexpr int L = G / 8;                       // lanes per group
   const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t total = (int64_t)a.H * a.N * 16;
@@ -325,18 +326,10 @@ __global__ __launch_bounds__(256) void k_psac_encode(ChunkDecode d, TensorView x
 hipError_t launch_quant_pack(const PackArgs& a, hipStream_t s) {
   const bool f32 = a.y.dtype == 0;
   if (!a.perm && a.n_int4 == 0) {
-    const int64_t total = (int64_t)a.H * a.N * 16;
-    const dim3 grid((unsigned)((total + 255) / 256)), block(256);
-#define QKV_QF(GV, BV)                                                                        \
-    if (a.group == GV && a.bits == BV) {                                                      \
-      if (f32) hipLaunchKernelGGL((k_quant_pack_fast<GV, BV, true>), grid, block, 0, s, a);    \
-      else hipLaunchKernelGGL((k_quant_pack_fast<GV, BV, false>), grid, block, 0, s, a);       \
-      return hipGetLastError();                                                               \
-    }
-    QKV_QF(16, 2) QKV_QF(32, 2) QKV_QF(64, 2) QKV_QF(128, 2)
-    QKV_QF(16, 4) QKV_QF(32, 4) QKV_QF(64, 4) QKV_QF(128, 4)
-#undef QKV_QF
-    return hipErrorInvalidValue;
+    PackBatch pb;
+    pb.n = 1;
+    pb.a[0] = a;
+    return launch_quant_pack_batch(pb, s);
   }
   const int64_t total = (int64_t)a.H * a.N * a.groups;
   const dim3 grid((unsigned)((total + 255) / 256)), block(256);
@@ -351,6 +344,30 @@ hipError_t launch_quant_pack(const PackArgs& a, hipStream_t s) {
   QKV_QP(64)
   QKV_QP(128)
 #undef QKV_QP
+  return hipErrorInvalidValue;
+}
+
+bool quant_pack_batchable(const PackArgs& a, const PackArgs& b0) {
+  return !a.perm && a.n_int4 == 0 && a.group == b0.group && a.bits == b0.bits && a.y.dtype == b0.y.dtype &&
+         a.H == b0.H && a.N == b0.N;
+}
+
+hipError_t launch_quant_pack_batch(const PackBatch& b, hipStream_t s) {
+  const PackArgs& a = b.a[0];
+  for (int p = 0; p < b.n; ++p)
+    if (!quant_pack_batchable(b.a[p], a)) return hipErrorInvalidValue;
+  const bool f32 = a.y.dtype == 0;
+  const int64_t total = (int64_t)a.H * a.N * 16;
+  const dim3 grid((unsigned)((total + 255) / 256), (unsigned)b.n), block(256);
+#define QKV_QF(GV, BV)                                                                        \
+  if (a.group == GV && a.bits == BV) {                                                        \
+    if (f32) hipLaunchKernelGGL((k_quant_pack_fast<GV, BV, true>), grid, block, 0, s, b);      \
+    else hipLaunchKernelGGL((k_quant_pack_fast<GV, BV, false>), grid, block, 0, s, b);         \
+    return hipGetLastError();                                                                 \
+  }
+  QKV_QF(16, 2) QKV_QF(32, 2) QKV_QF(64, 2) QKV_QF(128, 2)
+  QKV_QF(16, 4) QKV_QF(32, 4) QKV_QF(64, 4) QKV_QF(128, 4)
+#undef QKV_QF
   return hipErrorInvalidValue;
 }
 
