@@ -124,6 +124,62 @@ def test_quant_pack_lockstep(case):
             assert np.array_equal(v["perm"][h], perm[h].astype(np.uint8))
 
 
+def _half_integer_residuals(bits, n, H, rng):
+    """float32 rows whose residuals (centroids all zero) divided by their group
+    scale land exactly on half-integers, within 2^-21 of them, or elsewhere:
+    each group of 32 has an element of magnitude qmax * S with S a power of
+    two, so the stored scale is exactly S.  About 5 % of the groups are all
+    zero (S = 0) and 5 % have S = 2^-110 (far below the usual range)."""
+    qmax = (1 << (bits - 1)) - 1
+    halves = np.arange(-qmax, qmax) + 0.5                      # ..., -0.5, 0.5, ..., qmax - 0.5
+    y = np.zeros((n, H, 128), np.float64)
+    for g in range(4):
+        S = 2.0 ** rng.integers(-3, 4, size=(n, H, 1))
+        pick = rng.uniform(size=(n, H, 1))
+        S = np.where(pick < 0.05, 0.0, np.where(pick < 0.10, 2.0 ** -110, S))
+        kind = rng.integers(0, 4, size=(n, H, 32))
+        base = rng.choice(halves, size=(n, H, 32))
+        nudge = rng.choice([-1.0, 1.0], size=(n, H, 32)) * 2.0 ** -21
+        free = rng.uniform(-qmax, qmax, size=(n, H, 32))
+        v = np.where(kind == 0, base, np.where(kind == 1, base + nudge, np.where(kind == 2, base - nudge, free)))
+        v[:, :, 0] = qmax * rng.choice([-1.0, 1.0], size=(n, H))
+        y[:, :, g * 32:(g + 1) * 32] = v * S
+    return y.astype(np.float32)
+
+
+@pytest.mark.parametrize("bits", [2, 4])
+def test_quant_pack_half_integer_quotients(bits):
+    """Quotients r / S exactly on or within 2^-21 of a half-integer: codes follow
+    the correctly rounded quotient with ties to even (the oracle's definition)."""
+    H, N, C = 2, 300, 4
+    rng = np.random.default_rng(11 + bits)
+    x = _half_integer_residuals(bits, N, H, rng)
+    lab = rng.integers(0, C, size=(H, N)).astype(np.uint8)
+    cent = np.zeros((H, C, 128), np.float32)
+    cfg = qk.Config(n_heads=H, n_clusters=C, bits=bits, group=32)
+    t = G.torch()
+    G.log(f"quant_pack half-integer quotients: bits={bits} H={H} N={N}")
+    packed = t.zeros(qk.qkv_chunk_layout(cfg, N).bytes, dtype=t.uint8, device=G.dev())
+    ynext = t.empty((H, N, 128), dtype=t.float32, device=G.dev())
+    qk.qkv_quant_pack(cfg, G.to_dev(x), t.from_numpy(lab.reshape(-1)).to(G.dev()), G.to_dev(cent),
+                      packed, 0, y_next=ynext)
+    v = G.host_views(packed, cfg, N)
+    yn = ynext.cpu().numpy()
+    ties = 0
+    for h in range(H):
+        layout = oq.channel_layout(128, bits, 32, 0, None)
+        r = x[:, h].astype(np.float32)
+        q, s = oq.quantize_groups(r, layout)
+        with np.errstate(invalid="ignore", divide="ignore"):
+            ties += int(np.sum(np.abs(r / np.repeat(s, 32, axis=1)) % 1.0 == 0.5))
+        assert np.any(s == 0) and np.any((s > 0) & (s < 2.0 ** -96)), "zero and tiny scales present"
+        assert np.array_equal(v["codes"][0, h].view(np.uint32), oq.pack_codes(q, layout)), f"bits {bits} head {h}: codes"
+        assert np.array_equal(v["scales"][0, h].view(np.uint16), G.f32_bits_to_bf16(s)), f"bits {bits} head {h}: scales"
+        yhat = oq.dequantize(q, s, np.zeros_like(r), layout)
+        assert np.array_equal(yn[h].view(np.uint32), (r - yhat).astype(np.float32).view(np.uint32))
+    assert ties > 1000, "the input should hold many exact half-integer quotients"
+
+
 FREE = [
     ("tiny-K", 1, {}, "K", None, False),
     ("tiny-V-rtn", 1, {}, "V", None, True),

@@ -83,6 +83,82 @@ __device__ __forceinline__ float load_y(const TensorView& y, int64_t tok, int h,
   return bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(y.ptr)[off]);
 }
 
+// Codes of NE residuals of one group: q_e = clamp(rint(fp32(r_e / S))), with
+// one division per group.  The quotient starts as r * rS, rS = fp32(1 / S),
+// and takes two refinement steps q <- q + fp32(r - q S) * rS, the remainder
+// formed exactly by a fused multiply-add.  After the first step q is within
+// one ulp of r / S, so the second gives the correctly rounded quotient
+// (Markstein's theorem for division with a reciprocal rounded to nearest).
+// Scales outside [2^-96, 2^96], where an intermediate could leave the normal
+// range, use the division itself; S == 0 gives q = 0.
+template <int NE>
+__device__ __forceinline__ void group_codes(const float* r, float S, float qlo, float qhi, float* q) {
+  const float rS = 1.0f / S;
+  if (S >= 0x1p-96f && S <= 0x1p96f) {
+#pragma unroll
+    for (int e = 0; e < NE; ++e) {
+      float x = r[e] * rS;
+      x = __builtin_fmaf(__builtin_fmaf(-x, S, r[e]), rS, x);
+      x = __builtin_fmaf(__builtin_fmaf(-x, S, r[e]), rS, x);
+      q[e] = rintf(x);
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < NE; ++e) q[e] = rintf(r[e] / S);
+  }
+#pragma unroll
+  for (int e = 0; e < NE; ++e) q[e] = S != 0.0f ? __builtin_amdgcn_fmed3f(q[e], qlo, qhi) : 0.0f;
+}
+
+// DPP lane exchanges inside a row of 16 lanes (all lanes active): quad_perm
+// swaps for xor 1 and xor 2, then half-row and row mirrors, which pair every
+// lane of one aligned half with a lane of the other half.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+template <int LANES>   // max over aligned groups of LANES lanes (1, 2, 4, 8 or 16)
+__device__ __forceinline__ float group_max_dpp(float v) {
+  if constexpr (LANES >= 2) v = fmaxf(v, __uint_as_float(dpp_u32<0xB1>(__float_as_uint(v))));   // [1,0,3,2]
+  if constexpr (LANES >= 4) v = fmaxf(v, __uint_as_float(dpp_u32<0x4E>(__float_as_uint(v))));   // [2,3,0,1]
+  if constexpr (LANES >= 8) v = fmaxf(v, __uint_as_float(dpp_u32<0x141>(__float_as_uint(v))));  // half mirror
+  if constexpr (LANES >= 16) v = fmaxf(v, __uint_as_float(dpp_u32<0x140>(__float_as_uint(v))));  // mirror
+  return v;
+}
+
+// Stored codes u = q + 2^(b-1) of 8 residuals sharing the scale S (bits
+// S_bits), packed b bits per channel; the arithmetic of group_codes with
+// three shortcuts that do not change a result: fp32(1 / S) is read from a
+// table of fp32(1 / m) over the 128 bf16 significands m, scaled by the
+// exponent (exact for normal S); rint and the offset come from one addition
+// of 1.5 * 2^23 + 2^(b-1) (round to nearest even at unit spacing); and the
+// clamp is dropped, since |r| <= max|r| <= qmax * S * (1 + 2^-8.9) keeps
+// |q| <= qmax.  Scales outside [2^-96, 2^96] (and S == 0) take group_codes.
+template <int BITS>
+__device__ __forceinline__ uint32_t pack8_codes(const float* r, float S, uint32_t S_bits, const float* rtab) {
+  constexpr float qmax = (float)((1 << (BITS - 1)) - 1);
+  const uint32_t E = (S_bits >> 7) & 0xFFu;
+  uint32_t w = 0;
+  if (__builtin_expect(E >= 31u && E <= 223u, 1)) {            // S in [2^-96, 2^96)
+    const float rS = __builtin_amdgcn_ldexpf(rtab[S_bits & 0x7Fu], 127 - (int)E);
+    constexpr float kBias = 12582912.0f + (float)(1 << (BITS - 1));
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float x = r[e] * rS;
+      x = __builtin_fmaf(__builtin_fmaf(-x, S, r[e]), rS, x);
+      x = __builtin_fmaf(__builtin_fmaf(-x, S, r[e]), rS, x);
+      const uint32_t z = __float_as_uint(x + kBias);           // 0x4B400000 + u
+      w |= (z & ((1u << BITS) - 1u)) << (BITS * e);
+    }
+  } else {
+    float q[8];
+    group_codes<8>(r, S, -(float)(1 << (BITS - 1)), qmax, q);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) w |= (uint32_t)((int)q[e] + (1 << (BITS - 1))) << (BITS * e);
+  }
+  return w;
+}
+
 // One thread per (head, token, group).
 template <int G, bool F32>
 __global__ __launch_bounds__(256) void k_quant_pack(PackArgs a) {
@@ -150,76 +226,164 @@ __global__ __launch_bounds__(256) void k_quant_pack(PackArgs a) {
   a.scales[((int64_t)h * a.N + i) * a.groups + g] = (uint16_t)sbits;
 }
 
-// Uniform layout without a channel permutation: one thread per 8 consecutive
-// channels of a (head, token) row, so a wave covers 4 rows with 16-byte loads;
-// a group of G channels spans G/8 aligned lanes and takes its max through xor
-// shuffles; two lanes' INT2 codes form one word.  Same arithmetic as
+// Uniform layout without a channel permutation.  A workgroup owns a tile of
+// T tokens x HB heads (T * HB <= 128 rows, HB = min(H, 128)) taken in
+// token-major order, so with the usual [N][H][128] input it reads one
+// contiguous run of memory (32 KB for 32 bf16 heads) and HBM pages stream in
+// order.  A thread handles 8 consecutive channels of a row (one 16-byte load);
+// a wave covers 4 rows per item; a group of G channels spans G/8 aligned lanes
+// and takes its max through xor shuffles.  Codes and scales are staged in LDS
+// and written per head as contiguous runs of T rows.  Same arithmetic as
 // k_quant_pack.
+constexpr int kTileRows = 128;
+struct TileGeom {
+  int HB, T, nhb, tiles;    // heads per tile, tokens per tile, head blocks, tiles per problem
+};
+__host__ __device__ inline TileGeom tile_geom(int H, int N) {
+  TileGeom g;
+  g.HB = H < kTileRows ? H : kTileRows;
+  g.T = kTileRows / g.HB;
+  g.nhb = (H + g.HB - 1) / g.HB;
+  g.tiles = ((N + g.T - 1) / g.T) * g.nhb;
+  return g;
+}
+
 template <int G, int BITS, bool F32>
-__global__ __launch_bounds__(256) void k_quant_pack_fast(PackBatch pb) {
-  const PackArgs& a = pb.a[blockIdx.y];
-  constexpr int L = G / 8;                       // lanes per group
-  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int64_t total = (int64_t)a.H * a.N * 16;
-  const bool valid = gid < total;                 // invalid lanes still join the shuffles
-  const int64_t g2 = valid ? gid : total - 1;
-  const int part = (int)(g2 & 15);
-  const int64_t row = g2 >> 4;                    // (h, i) in [H][N] order
-  const int i = (int)(row % a.N), h = (int)(row / a.N);
-  const int k0 = part * 8;
-  float yv[8], cv[8], r[8];
-  const int64_t yoff = (int64_t)i * a.y.stride_token + (int64_t)h * a.y.stride_head + k0;
-  if constexpr (F32) {
-    const float4 p0 = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(a.y.ptr) + yoff);
-    const float4 p1 = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(a.y.ptr) + yoff + 4);
-    yv[0] = p0.x; yv[1] = p0.y; yv[2] = p0.z; yv[3] = p0.w; yv[4] = p1.x; yv[5] = p1.y; yv[6] = p1.z; yv[7] = p1.w;
-  } else {
-    const uint4 p = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(a.y.ptr) + yoff);
-    const uint32_t w4[4] = {p.x, p.y, p.z, p.w};
+__global__ __launch_bounds__(256) void k_quant_pack_tile(PackBatch pb, int tiles) {
+  constexpr int L = G / 8;                        // lanes per group
+  constexpr int W = kHeadDim * BITS / 32;         // code words per row
+  constexpr int NG = kHeadDim / G;                // groups per row
+  constexpr int kIt = kTileRows * 16 / 256;       // items per thread
+  __shared__ __attribute__((aligned(16))) uint32_t s_codes[kTileRows * W];
+  __shared__ uint16_t s_scales[kTileRows * NG];
+  __shared__ float s_rtab[128];                   // fp32(1 / (1 + k / 128))
+  if (threadIdx.x < 128) s_rtab[threadIdx.x] = 1.0f / (1.0f + (float)threadIdx.x * 0.0078125f);
+  __syncthreads();
+  const uint32_t logical = xcd_remap(blockIdx.x, gridDim.x);   // neighbouring tiles share an XCD (L2)
+  const PackArgs& a = pb.a[logical / tiles];
+  const int tile = (int)(logical % tiles);
+  const TileGeom tg = tile_geom(a.H, a.N);
+  const int hb = tile % tg.nhb;
+  const int i0 = (tile / tg.nhb) * tg.T, h0 = hb * tg.HB;
+  const int rows = tg.T * tg.HB;                  // <= kTileRows
+  const int tid = threadIdx.x;
+  const int part = tid & 15, k0 = part * 8;
+  // local row lr = x * 16 + tid / 16 of item x splits as lr = t * HB + hh;
+  // t = (lr * inv) >> 16 is exact for lr < 128, HB <= 128
+  const uint32_t inv = 65536u / (uint32_t)tg.HB + 1u;
+  auto split = [&](int x, int& t, int& hh) __attribute__((always_inline)) {
+    const int lr = x * 16 + (tid >> 4);
+    t = (int)(((uint32_t)lr * inv) >> 16);
+    hh = lr - t * tg.HB;
+  };
+  auto row_ok = [&](int x) __attribute__((always_inline)) -> bool {
+    int t, hh;
+    split(x, t, hh);
+    return x * 16 + (tid >> 4) < rows && h0 + hh < a.H && i0 + t < a.N;   // uniform over a row's 16 lanes
+  };
+
+  // Every load is unconditional (rows outside the tile read a clamped, valid
+  // row and are never stored), so no branch separates them and all of a
+  // thread's requests are in flight together: labels, then the input rows,
+  // then the labelled centroid rows (the memory counter drains in order, so
+  // the centroid requests wait on the labels only).
+  uint32_t lab[kIt];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) yv[e] = bf16_bits_to_f32((w4[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
+  for (int x = 0; x < kIt; ++x) {
+    int t, hh;
+    split(x, t, hh);
+    const int h = min(h0 + hh, a.H - 1), i = min(i0 + t, a.N - 1);
+    lab[x] = a.labels[(int64_t)h * a.N + i];
   }
-  const int lab = min((int)a.labels[row], a.C - 1);
-  {
-    const uint4 p = *reinterpret_cast<const uint4*>(a.centroids + ((int64_t)h * a.C + lab) * kHeadDim + k0);
-    const uint32_t w4[4] = {p.x, p.y, p.z, p.w};
+  uint32_t yw[kIt][F32 ? 8 : 4];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) cv[e] = bf16_bits_to_f32((w4[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
+  for (int x = 0; x < kIt; ++x) {
+    int t, hh;
+    split(x, t, hh);
+    const int h = min(h0 + hh, a.H - 1), i = min(i0 + t, a.N - 1);
+    const int64_t yoff = (int64_t)i * a.y.stride_token + (int64_t)h * a.y.stride_head + k0;
+    if constexpr (F32) {
+      const uint4 p0 = *reinterpret_cast<const uint4*>(reinterpret_cast<const float*>(a.y.ptr) + yoff);
+      const uint4 p1 = *reinterpret_cast<const uint4*>(reinterpret_cast<const float*>(a.y.ptr) + yoff + 4);
+      yw[x][0] = p0.x; yw[x][1] = p0.y; yw[x][2] = p0.z; yw[x][3] = p0.w;
+      yw[x][4] = p1.x; yw[x][5] = p1.y; yw[x][6] = p1.z; yw[x][7] = p1.w;
+    } else {
+      const uint4 p = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(a.y.ptr) + yoff);
+      yw[x][0] = p.x; yw[x][1] = p.y; yw[x][2] = p.z; yw[x][3] = p.w;
+    }
   }
-  float amax = 0.0f;
+  uint4 cw[kIt];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    r[e] = yv[e] - cv[e];
-    amax = fmaxf(amax, fabsf(r[e]));
+  for (int x = 0; x < kIt; ++x) {
+    int t, hh;
+    split(x, t, hh);
+    const int h = min(h0 + hh, a.H - 1);
+    cw[x] = *reinterpret_cast<const uint4*>(a.centroids +
+                                            ((int64_t)h * a.C + min((int)lab[x], a.C - 1)) * kHeadDim + k0);
   }
 #pragma unroll
-  for (int off = 1; off < L; off <<= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
-  constexpr float qmax = (float)((1 << (BITS - 1)) - 1);
-  const uint32_t sbits = f32_to_bf16_bits(amax / qmax);
-  const float S = bf16_bits_to_f32(sbits);
-  uint32_t bitsw = 0;
-  float q[8];
+  for (int x = 0; x < kIt; ++x) {
+    const int lr = x * 16 + (tid >> 4);
+    int t, hh;
+    split(x, t, hh);
+    const int h = h0 + hh, i = i0 + t;
+    const bool ok = row_ok(x);
+    float yv[8], cv[8], r[8];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    q[e] = 0.0f;
-    if (S != 0.0f) q[e] = fminf(fmaxf(rintf(r[e] / S), -(float)(1 << (BITS - 1))), qmax);
-    bitsw |= (uint32_t)((int)q[e] + (1 << (BITS - 1))) << (BITS * e);
-  }
-  uint32_t* wrow = a.codes + row * a.words;
-  if constexpr (BITS == 2) {
-    const uint32_t other = __shfl_xor(bitsw, 1);
-    if (valid && (part & 1) == 0) wrow[part >> 1] = bitsw | (other << 16);
-  } else {
-    if (valid) wrow[part] = bitsw;
-  }
-  if (valid && part % L == 0) a.scales[row * a.groups + part / L] = (uint16_t)sbits;
-  if (valid && a.y_next) {
-    float o[8];
+    for (int e = 0; e < 8; ++e) {
+      if constexpr (F32) yv[e] = __uint_as_float(yw[x][e]);
+      else yv[e] = bf16_bits_to_f32((yw[x][e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
+    }
+    const uint32_t c4[4] = {cw[x].x, cw[x].y, cw[x].z, cw[x].w};
 #pragma unroll
-    for (int e = 0; e < 8; ++e) o[e] = __fsub_rn(yv[e], __fadd_rn(S * q[e], cv[e]));
-    float* yp = a.y_next + row * kHeadDim + k0;
-    *reinterpret_cast<float4*>(yp) = make_float4(o[0], o[1], o[2], o[3]);
-    *reinterpret_cast<float4*>(yp + 4) = make_float4(o[4], o[5], o[6], o[7]);
+    for (int e = 0; e < 8; ++e) cv[e] = bf16_bits_to_f32((c4[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
+    float amax = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      r[e] = yv[e] - cv[e];
+      amax = fmaxf(amax, fabsf(r[e]));
+    }
+    amax = group_max_dpp<L>(amax);
+    constexpr float qmax = (float)((1 << (BITS - 1)) - 1);
+    const uint32_t sbits = f32_to_bf16_bits(amax / qmax);
+    const float S = bf16_bits_to_f32(sbits);
+    const uint32_t bitsw = pack8_codes<BITS>(r, S, sbits, s_rtab);
+    if constexpr (BITS == 2) {
+      const uint32_t other = dpp_u32<0xB1>(bitsw);
+      if ((part & 1) == 0 && lr < kTileRows) s_codes[lr * W + (part >> 1)] = bitsw | (other << 16);
+    } else {
+      if (lr < kTileRows) s_codes[lr * W + part] = bitsw;
+    }
+    if (part % L == 0 && lr < kTileRows) s_scales[lr * NG + part / L] = (uint16_t)sbits;
+    if (ok && a.y_next) {
+      float o[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float q = (float)((int)((bitsw >> (BITS * e)) & ((1u << BITS) - 1u)) - (1 << (BITS - 1)));
+        o[e] = __fsub_rn(yv[e], __fadd_rn(S * q, cv[e]));
+      }
+      float* yp = a.y_next + ((int64_t)h * a.N + i) * kHeadDim + k0;
+      *reinterpret_cast<float4*>(yp) = make_float4(o[0], o[1], o[2], o[3]);
+      *reinterpret_cast<float4*>(yp + 4) = make_float4(o[4], o[5], o[6], o[7]);
+    }
+  }
+  __syncthreads();
+  // write-out: per head, the tile's T rows are contiguous in [H][N] order
+  const int tv = min(tg.T, a.N - i0);             // valid tokens of the tile
+  constexpr int W4 = W / 4;
+  for (int idx = tid; idx < tg.HB * tg.T * W4; idx += 256) {
+    const int hh = idx / (tg.T * W4), rem = idx % (tg.T * W4);
+    const int t = rem / W4, w4 = rem % W4;
+    const int h = h0 + hh;
+    if (h < a.H && t < tv)
+      *reinterpret_cast<uint4*>(a.codes + ((int64_t)h * a.N + i0 + t) * W + w4 * 4) =
+          *reinterpret_cast<const uint4*>(&s_codes[(t * tg.HB + hh) * W + w4 * 4]);
+  }
+  for (int idx = tid; idx < tg.HB * tg.T * NG; idx += 256) {
+    const int hh = idx / (tg.T * NG), rem = idx % (tg.T * NG);
+    const int t = rem / NG, g = rem % NG;
+    const int h = h0 + hh;
+    if (h < a.H && t < tv) a.scales[((int64_t)h * a.N + i0 + t) * NG + g] = s_scales[(t * tg.HB + hh) * NG + g];
   }
 }
 
@@ -356,14 +520,15 @@ hipError_t launch_quant_pack_batch(const PackBatch& b, hipStream_t s) {
   const PackArgs& a = b.a[0];
   for (int p = 0; p < b.n; ++p)
     if (!quant_pack_batchable(b.a[p], a)) return hipErrorInvalidValue;
+  if (a.words != kHeadDim * a.bits / 32 || a.groups != kHeadDim / a.group) return hipErrorInvalidValue;
   const bool f32 = a.y.dtype == 0;
-  const int64_t total = (int64_t)a.H * a.N * 16;
-  const dim3 grid((unsigned)((total + 255) / 256), (unsigned)b.n), block(256);
-#define QKV_QF(GV, BV)                                                                        \
-  if (a.group == GV && a.bits == BV) {                                                        \
-    if (f32) hipLaunchKernelGGL((k_quant_pack_fast<GV, BV, true>), grid, block, 0, s, b);      \
-    else hipLaunchKernelGGL((k_quant_pack_fast<GV, BV, false>), grid, block, 0, s, b);         \
-    return hipGetLastError();                                                                 \
+  const int tiles = tile_geom(a.H, a.N).tiles;
+  const dim3 grid((unsigned)(tiles * b.n)), block(256);
+#define QKV_QF(GV, BV)                                                                              \
+  if (a.group == GV && a.bits == BV) {                                                              \
+    if (f32) hipLaunchKernelGGL((k_quant_pack_tile<GV, BV, true>), grid, block, 0, s, b, tiles);     \
+    else hipLaunchKernelGGL((k_quant_pack_tile<GV, BV, false>), grid, block, 0, s, b, tiles);        \
+    return hipGetLastError();                                                                       \
   }
   QKV_QF(16, 2) QKV_QF(32, 2) QKV_QF(64, 2) QKV_QF(128, 2)
   QKV_QF(16, 4) QKV_QF(32, 4) QKV_QF(64, 4) QKV_QF(128, 4)
