@@ -95,18 +95,61 @@ def host_views(packed, cfg: qk.Config, n_tokens: int) -> dict:
 
 # ---------------------------------------------------------------- oracle pool
 def _oracle_job(args):
+    from threadpoolctl import threadpool_limits
     from oracle import pipeline
     x, kw = args
-    return pipeline.quantize_problem(x, **kw)
+    with threadpool_limits(limits=1):     # one BLAS thread per worker process
+        return pipeline.quantize_problem(x, **kw)
+
+
+def _spawn_pool(workers: int) -> ProcessPoolExecutor:
+    """Worker processes started fresh (no state inherited from a process that
+    holds GPU and thread-pool handles)."""
+    import multiprocessing as mp
+    return ProcessPoolExecutor(max_workers=workers, mp_context=mp.get_context("spawn"))
+
+
+def pool_workers(n_jobs: int) -> int:
+    return min(n_jobs, max(1, min(16, len(os.sched_getaffinity(0)))))
 
 
 def oracle_problems(jobs, workers: int | None = None):
-    """Run oracle.pipeline.quantize_problem for each (x [N, d], kwargs) job."""
+    """Run oracle.pipeline.quantize_problem for each (x [N, d], kwargs) job;
+    long batches print a progress line every 16 problems."""
     if len(jobs) == 1:
         return [_oracle_job(jobs[0])]
-    workers = workers or min(len(jobs), max(1, min(16, len(os.sched_getaffinity(0)))))
-    with ProcessPoolExecutor(max_workers=workers) as ex:
-        return list(ex.map(_oracle_job, jobs))
+    out = []
+    with _spawn_pool(workers or pool_workers(len(jobs))) as ex:
+        for r in ex.map(_oracle_job, jobs):
+            out.append(r)
+            if len(jobs) > 16 and len(out) % 16 == 0:
+                log(f"oracle: {len(out)} / {len(jobs)} problems")
+    return out
+
+
+def gen_chunk_bits(args):
+    """Chunk c of workload cid (all heads) as bf16 bit patterns [N, H, d] uint16
+    for K and V, plus float32 rows of the kept heads (bf16-exact)."""
+    from threadpoolctl import threadpool_limits
+    from video_model_kv_amd import synth
+    cid, c, keep = args
+    with threadpool_limits(limits=1):
+        wl = synth.workload(cid)
+        out = {}
+        for tensor in ("K", "V"):
+            x = synth.kv_chunk(wl, tensor, c)
+            out[tensor] = ((x.view(np.uint32) >> 16).astype(np.uint16), x[:, keep].copy())
+    return c, out
+
+
+def generated_chunks(cid: int, n_chunks: int, keep):
+    """Yields (c, {tensor: (bf16 bits, kept heads)}) in chunk order, generated in
+    a process pool, with a progress line every 8 chunks."""
+    with _spawn_pool(pool_workers(n_chunks)) as ex:
+        for c, out in ex.map(gen_chunk_bits, [(cid, c, keep) for c in range(n_chunks)]):
+            if (c + 1) % 8 == 0:
+                log(f"generated {c + 1} / {n_chunks} chunks")
+            yield c, out
 
 
 def rel_l2(a, b) -> float:

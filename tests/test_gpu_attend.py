@@ -125,3 +125,77 @@ def test_bench_shape_sampled_head():
     wl = synth.workload(2)
     bounds = [wl.chunk_range(c) for c in range(wl.n_chunks)]
     _run("bench-shape", wl, bounds, wl.n_query, [11], logit_queries=64)
+
+
+def test_progressive_full_cache_sampled_head():
+    """Three progressive stages at full shape: 32 heads, 6 chunks of 6,240 tokens,
+    C = 256, INT2 g = 32 per stage, 1,560 queries over the whole cache; the oracle
+    quantizes one sampled head of every chunk (three stages each) and attends."""
+    wl = synth.workload(3)
+    bounds = [wl.chunk_range(c) for c in range(wl.n_chunks)]
+    _run("progressive-full", wl, bounds, wl.n_query, [9], logit_queries=64)
+
+
+def test_quantwm_full_cache_sampled_head():
+    """QSAC-weighted k-means and rank-8 PSAC on the keys at full shape (32 heads,
+    6 chunks of 6,240 tokens, C = 256); oracle on one sampled head."""
+    wl = synth.workload(4)
+    bounds = [wl.chunk_range(c) for c in range(wl.n_chunks)]
+    _run("quantwm-full", wl, bounds, wl.n_query, [13], logit_queries=64)
+
+
+def test_long_horizon_full_cache_sampled_queries():
+    """The one-minute cache at full size: 72 chunks of 6,240 tokens (449,280 keys),
+    32 heads, keys mixed INT4 on the 26 most query-sensitive channels / INT2 on the
+    rest, values INT2, C = 256; 1,560 queries attend over the whole packed cache.
+    The oracle quantizes head 0 of every chunk itself and attends 65 sampled
+    queries (every 24th) in float64; logits of the first 64 queries are checked
+    through the debug path."""
+    wl = synth.workload(5)
+    H, h, n = wl.n_heads, 0, wl.n_chunks
+    t = G.torch()
+    kcfg, vcfg = G.config_of(wl, "K"), G.config_of(wl, "V")
+    hist = synth.history_queries(wl)
+    perm = np.stack([ops.sensitivity_perm(ops.qsac_weights(hist[:, j]), wl.n_int4) for j in range(H)])
+    pd = t.from_numpy(perm.astype(np.uint8)).to(G.dev())
+    ntok = [b - a for a, b in (wl.chunk_range(c) for c in range(n))]
+    ws = G.workspace(kcfg, max(ntok), wl.n_query, n)
+    wsv = G.workspace(vcfg, max(ntok))
+    kch, vch, xk0, xv0 = [None] * n, [None] * n, [None] * n, [None] * n
+    G.log(f"long-horizon: generating and quantizing {n} chunks x 2 tensors")
+    for c, out in G.generated_chunks(5, n, [h]):
+        (kb, xk0[c]), (vb, xv0[c]) = out["K"], out["V"]
+        kd = t.from_numpy(kb.view(np.int16)).to(G.dev()).view(t.bfloat16)
+        vd = t.from_numpy(vb.view(np.int16)).to(G.dev()).view(t.bfloat16)
+        kch[c] = G.quantize(kcfg, kd, perm=pd, ws=ws)
+        vch[c] = G.quantize(vcfg, vd, ws=wsv)
+        del kd, vd
+    q = synth.queries(wl)
+    qd = G.to_dev(q, wl.dtype)
+    out = t.empty((wl.n_query, H, 128), dtype=t.float32, device=G.dev())
+    G.log(f"long-horizon: attend Nq={wl.n_query} over Nk={sum(ntok)}")
+    qk.qkv_attend(kcfg, vcfg, qd, kch, vch, ntok, out, ws)
+    nl = 64
+    logits = t.empty((H, nl, sum(ntok)), dtype=t.float32, device=G.dev())
+    out_l = t.empty((nl, H, 128), dtype=t.float32, device=G.dev())
+    qk.qkv_attend(kcfg, vcfg, qd[:nl].contiguous(), kch, vch, ntok, out_l, ws, logits=logits)
+    o = out.cpu().numpy()[:, h]
+    lg = logits[h].cpu().numpy()
+    del logits
+    G.log(f"long-horizon: oracle on head {h} ({2 * n} problems)")
+    jobs = []
+    for c in range(n):
+        jobs.append((xk0[c][:, 0], dict(n_clusters=wl.n_clusters, bits=wl.bits, group=wl.group, iters=wl.kmeans_iters,
+                                        n_int4=kcfg.n_int4_channels, perm=perm[h])))
+        jobs.append((xv0[c][:, 0], dict(n_clusters=wl.n_clusters, bits=wl.bits, group=wl.group, iters=wl.kmeans_iters)))
+    res = G.oracle_problems(jobs)
+    k_hat = np.concatenate([res[2 * c].x_hat for c in range(n)])
+    v_hat = np.concatenate([res[2 * c + 1].x_hat for c in range(n)])
+    sample = np.arange(0, wl.n_query, 24)
+    ref = oa.attend_head(q[sample, h], k_hat, v_hat)
+    e_out = G.rel_l2(o[sample], ref)
+    e_log = G.rel_l2(lg, oa.logits(q[:nl, h], k_hat))
+    G.log(f"long-horizon h{h}: rel-L2 logits {e_log:.3g} (tol {LOGIT_TOL}), out {e_out:.3g} (tol {OUT_TOL}) "
+          f"on {len(sample)} sampled queries over {k_hat.shape[0]} keys")
+    assert e_log <= LOGIT_TOL, f"long-horizon: logits rel-L2 {e_log}"
+    assert e_out <= OUT_TOL, f"long-horizon: output rel-L2 {e_out}"
