@@ -83,31 +83,13 @@ __device__ __forceinline__ float load_y(const TensorView& y, int64_t tok, int h,
   return bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(y.ptr)[off]);
 }
 
-// Codes of NE residuals of one group: q_e = clamp(rint(fp32(r_e / S))), with
-// one division per group.  The quotient starts as r * rS, rS = fp32(1 / S),
-// and takes two refinement steps q <- q + fp32(r - q S) * rS, the remainder
-// formed exactly by a fused multiply-add.  After the first step q is within
-// one ulp of r / S, so the second gives the correctly rounded quotient
-// (Markstein's theorem for division with a reciprocal rounded to nearest).
-// Scales outside [2^-96, 2^96], where an intermediate could leave the normal
-// range, use the division itself; S == 0 gives q = 0.
+// Codes of NE residuals of one group by the definition: q_e =
+// clamp(rint(fp32(r_e / S))) with the correctly rounded division; S == 0
+// gives q = 0.
 template <int NE>
 __device__ __forceinline__ void group_codes(const float* r, float S, float qlo, float qhi, float* q) {
-  const float rS = 1.0f / S;
-  if (S >= 0x1p-96f && S <= 0x1p96f) {
 #pragma unroll
-    for (int e = 0; e < NE; ++e) {
-      float x = r[e] * rS;
-      x = __builtin_fmaf(__builtin_fmaf(-x, S, r[e]), rS, x);
-      x = __builtin_fmaf(__builtin_fmaf(-x, S, r[e]), rS, x);
-      q[e] = rintf(x);
-    }
-  } else {
-#pragma unroll
-    for (int e = 0; e < NE; ++e) q[e] = rintf(r[e] / S);
-  }
-#pragma unroll
-  for (int e = 0; e < NE; ++e) q[e] = S != 0.0f ? __builtin_amdgcn_fmed3f(q[e], qlo, qhi) : 0.0f;
+  for (int e = 0; e < NE; ++e) q[e] = S != 0.0f ? __builtin_amdgcn_fmed3f(rintf(r[e] / S), qlo, qhi) : 0.0f;
 }
 
 // DPP lane exchanges inside a row of 16 lanes (all lanes active): quad_perm
@@ -128,12 +110,19 @@ __device__ __forceinline__ float group_max_dpp(float v) {
 
 // Stored codes u = q + 2^(b-1) of 8 residuals sharing the scale S (bits
 // S_bits), packed b bits per channel; the arithmetic of group_codes with
-// three shortcuts that do not change a result: fp32(1 / S) is read from a
-// table of fp32(1 / m) over the 128 bf16 significands m, scaled by the
-// exponent (exact for normal S); rint and the offset come from one addition
-// of 1.5 * 2^23 + 2^(b-1) (round to nearest even at unit spacing); and the
-// clamp is dropped, since |r| <= max|r| <= qmax * S * (1 + 2^-8.9) keeps
-// |q| <= qmax.  Scales outside [2^-96, 2^96] (and S == 0) take group_codes.
+// shortcuts that do not change a result:
+//  * fp32(1 / S) is read from a table of fp32(1 / m) over the 128 bf16
+//    significands m, scaled by the exponent (exact for normal S);
+//  * one refinement step suffices: with x = r / S, q0 = fp32(r * rS) is within
+//    1.5 ulp(x), the remainder e = r - q0 S is exact, and the fused step
+//    fp32(q0 + e * rS) = fp32(x + eta) with |eta| < 1.5 * 2^-24 ulp(x).  As S
+//    has an 8-bit significand, x is never a rounding midpoint and lies at
+//    least ulp(x) / 512 away from every midpoint, so the step rounds like x;
+//  * rint and the offset come from one addition of 1.5 * 2^23 + 2^(b-1)
+//    (round to nearest even at unit spacing);
+//  * the clamp is dropped, since |r| <= max|r| <= qmax * S * (1 + 2^-8.9)
+//    keeps |q| <= qmax.
+// Scales outside [2^-96, 2^96] (and S == 0) take group_codes.
 template <int BITS>
 __device__ __forceinline__ uint32_t pack8_codes(const float* r, float S, uint32_t S_bits, const float* rtab) {
   constexpr float qmax = (float)((1 << (BITS - 1)) - 1);
@@ -145,7 +134,6 @@ __device__ __forceinline__ uint32_t pack8_codes(const float* r, float S, uint32_
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       float x = r[e] * rS;
-      x = __builtin_fmaf(__builtin_fmaf(-x, S, r[e]), rS, x);
       x = __builtin_fmaf(__builtin_fmaf(-x, S, r[e]), rS, x);
       const uint32_t z = __float_as_uint(x + kBias);           // 0x4B400000 + u
       w |= (z & ((1u << BITS) - 1u)) << (BITS * e);
@@ -273,14 +261,18 @@ __global__ __launch_bounds__(256) void k_quant_pack_tile(PackBatch pb, int tiles
   const uint32_t inv = 65536u / (uint32_t)tg.HB + 1u;
   auto split = [&](int x, int& t, int& hh) __attribute__((always_inline)) {
     const int lr = x * 16 + (tid >> 4);
-    t = (int)(((uint32_t)lr * inv) >> 16);
-    hh = lr - t * tg.HB;
+    t = (int)(__umul24((uint32_t)lr, inv) >> 16);
+    hh = lr - (int)__umul24((uint32_t)t, (uint32_t)tg.HB);
   };
-  auto row_ok = [&](int x) __attribute__((always_inline)) -> bool {
-    int t, hh;
-    split(x, t, hh);
-    return x * 16 + (tid >> 4) < rows && h0 + hh < a.H && i0 + t < a.N;   // uniform over a row's 16 lanes
-  };
+  // Addresses: 64-bit tile bases (wave-uniform) plus 32-bit in-tile offsets
+  // formed with 24-bit multiplies (the launcher routes strides or token
+  // counts of 2^23 or more to k_quant_pack).  Rows outside the tile are
+  // clamped to the last valid token and head.
+  const int tmax = a.N - 1 - i0, hmax = a.H - 1 - h0;
+  const uint32_t ST = (uint32_t)a.y.stride_token, SH = (uint32_t)a.y.stride_head, NN = (uint32_t)a.N;
+  const uint8_t* lab_base = a.labels + (int64_t)h0 * a.N + i0;
+  const uint16_t* cent_base = a.centroids + (int64_t)h0 * a.C * kHeadDim + k0;
+  const int64_t y_base = (int64_t)i0 * a.y.stride_token + (int64_t)h0 * a.y.stride_head + k0;
 
   // Every load is unconditional (rows outside the tile read a clamped, valid
   // row and are never stored), so no branch separates them and all of a
@@ -292,23 +284,22 @@ __global__ __launch_bounds__(256) void k_quant_pack_tile(PackBatch pb, int tiles
   for (int x = 0; x < kIt; ++x) {
     int t, hh;
     split(x, t, hh);
-    const int h = min(h0 + hh, a.H - 1), i = min(i0 + t, a.N - 1);
-    lab[x] = a.labels[(int64_t)h * a.N + i];
+    lab[x] = lab_base[__umul24((uint32_t)min(hh, hmax), NN) + (uint32_t)min(t, tmax)];
   }
   uint32_t yw[kIt][F32 ? 8 : 4];
 #pragma unroll
   for (int x = 0; x < kIt; ++x) {
     int t, hh;
     split(x, t, hh);
-    const int h = min(h0 + hh, a.H - 1), i = min(i0 + t, a.N - 1);
-    const int64_t yoff = (int64_t)i * a.y.stride_token + (int64_t)h * a.y.stride_head + k0;
+    const uint32_t yo = __umul24((uint32_t)min(t, tmax), ST) + __umul24((uint32_t)min(hh, hmax), SH);
     if constexpr (F32) {
-      const uint4 p0 = *reinterpret_cast<const uint4*>(reinterpret_cast<const float*>(a.y.ptr) + yoff);
-      const uint4 p1 = *reinterpret_cast<const uint4*>(reinterpret_cast<const float*>(a.y.ptr) + yoff + 4);
+      const float* p = reinterpret_cast<const float*>(a.y.ptr) + y_base + yo;
+      const uint4 p0 = *reinterpret_cast<const uint4*>(p);
+      const uint4 p1 = *reinterpret_cast<const uint4*>(p + 4);
       yw[x][0] = p0.x; yw[x][1] = p0.y; yw[x][2] = p0.z; yw[x][3] = p0.w;
       yw[x][4] = p1.x; yw[x][5] = p1.y; yw[x][6] = p1.z; yw[x][7] = p1.w;
     } else {
-      const uint4 p = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(a.y.ptr) + yoff);
+      const uint4 p = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(a.y.ptr) + y_base + yo);
       yw[x][0] = p.x; yw[x][1] = p.y; yw[x][2] = p.z; yw[x][3] = p.w;
     }
   }
@@ -317,17 +308,15 @@ __global__ __launch_bounds__(256) void k_quant_pack_tile(PackBatch pb, int tiles
   for (int x = 0; x < kIt; ++x) {
     int t, hh;
     split(x, t, hh);
-    const int h = min(h0 + hh, a.H - 1);
-    cw[x] = *reinterpret_cast<const uint4*>(a.centroids +
-                                            ((int64_t)h * a.C + min((int)lab[x], a.C - 1)) * kHeadDim + k0);
+    const uint32_t row = __umul24((uint32_t)min(hh, hmax), (uint32_t)a.C) + (uint32_t)min((int)lab[x], a.C - 1);
+    cw[x] = *reinterpret_cast<const uint4*>(cent_base + row * kHeadDim);
   }
 #pragma unroll
   for (int x = 0; x < kIt; ++x) {
     const int lr = x * 16 + (tid >> 4);
     int t, hh;
     split(x, t, hh);
-    const int h = h0 + hh, i = i0 + t;
-    const bool ok = row_ok(x);
+    const bool ok = lr < rows && hh <= hmax && t <= tmax;   // uniform over a row's 16 lanes
     float yv[8], cv[8], r[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
@@ -350,11 +339,11 @@ __global__ __launch_bounds__(256) void k_quant_pack_tile(PackBatch pb, int tiles
     const uint32_t bitsw = pack8_codes<BITS>(r, S, sbits, s_rtab);
     if constexpr (BITS == 2) {
       const uint32_t other = dpp_u32<0xB1>(bitsw);
-      if ((part & 1) == 0 && lr < kTileRows) s_codes[lr * W + (part >> 1)] = bitsw | (other << 16);
+      if ((part & 1) == 0) s_codes[lr * W + (part >> 1)] = bitsw | (other << 16);
     } else {
-      if (lr < kTileRows) s_codes[lr * W + part] = bitsw;
+      s_codes[lr * W + part] = bitsw;
     }
-    if (part % L == 0 && lr < kTileRows) s_scales[lr * NG + part / L] = (uint16_t)sbits;
+    if (part % L == 0) s_scales[lr * NG + part / L] = (uint16_t)sbits;
     if (ok && a.y_next) {
       float o[8];
 #pragma unroll
@@ -362,28 +351,36 @@ __global__ __launch_bounds__(256) void k_quant_pack_tile(PackBatch pb, int tiles
         const float q = (float)((int)((bitsw >> (BITS * e)) & ((1u << BITS) - 1u)) - (1 << (BITS - 1)));
         o[e] = __fsub_rn(yv[e], __fadd_rn(S * q, cv[e]));
       }
-      float* yp = a.y_next + ((int64_t)h * a.N + i) * kHeadDim + k0;
+      float* yp = a.y_next + ((int64_t)(h0 + hh) * a.N + i0 + t) * kHeadDim + k0;
       *reinterpret_cast<float4*>(yp) = make_float4(o[0], o[1], o[2], o[3]);
       *reinterpret_cast<float4*>(yp + 4) = make_float4(o[4], o[5], o[6], o[7]);
     }
   }
   __syncthreads();
-  // write-out: per head, the tile's T rows are contiguous in [H][N] order
+  // write-out: per head, the tile's T rows are contiguous in [H][N] order;
+  // n / d for n, d <= 1024 as (n * (2^20 / d + 1)) >> 20 (exact there)
   const int tv = min(tg.T, a.N - i0);             // valid tokens of the tile
   constexpr int W4 = W / 4;
-  for (int idx = tid; idx < tg.HB * tg.T * W4; idx += 256) {
-    const int hh = idx / (tg.T * W4), rem = idx % (tg.T * W4);
-    const int t = rem / W4, w4 = rem % W4;
-    const int h = h0 + hh;
-    if (h < a.H && t < tv)
-      *reinterpret_cast<uint4*>(a.codes + ((int64_t)h * a.N + i0 + t) * W + w4 * 4) =
-          *reinterpret_cast<const uint4*>(&s_codes[(t * tg.HB + hh) * W + w4 * 4]);
+  {
+    const uint32_t d = (uint32_t)tg.T * W4, dinv = (1u << 20) / d + 1u;
+    uint32_t* cbase = a.codes + ((int64_t)h0 * a.N + i0) * W;
+    for (int idx = tid; idx < tg.HB * tg.T * W4; idx += 256) {
+      const int hh = (int)(((uint64_t)idx * dinv) >> 20), rem = idx - hh * (int)d;
+      const int t = rem / W4, w4 = rem % W4;
+      if (hh <= hmax && t < tv)
+        *reinterpret_cast<uint4*>(cbase + (uint64_t)(__umul24((uint32_t)hh, NN) + (uint32_t)t) * W + w4 * 4) =
+            *reinterpret_cast<const uint4*>(&s_codes[(t * tg.HB + hh) * W + w4 * 4]);
+    }
   }
-  for (int idx = tid; idx < tg.HB * tg.T * NG; idx += 256) {
-    const int hh = idx / (tg.T * NG), rem = idx % (tg.T * NG);
-    const int t = rem / NG, g = rem % NG;
-    const int h = h0 + hh;
-    if (h < a.H && t < tv) a.scales[((int64_t)h * a.N + i0 + t) * NG + g] = s_scales[(t * tg.HB + hh) * NG + g];
+  {
+    const uint32_t d = (uint32_t)tg.T * NG, dinv = (1u << 20) / d + 1u;
+    uint16_t* sbase = a.scales + ((int64_t)h0 * a.N + i0) * NG;
+    for (int idx = tid; idx < tg.HB * tg.T * NG; idx += 256) {
+      const int hh = (int)(((uint64_t)idx * dinv) >> 20), rem = idx - hh * (int)d;
+      const int t = rem / NG, g = rem % NG;
+      if (hh <= hmax && t < tv)
+        sbase[(uint64_t)(__umul24((uint32_t)hh, NN) + (uint32_t)t) * NG + g] = s_scales[(t * tg.HB + hh) * NG + g];
+    }
   }
 }
 
@@ -487,14 +484,8 @@ __global__ __launch_bounds__(256) void k_psac_encode(ChunkDecode d, TensorView x
 
 }  // namespace
 
-hipError_t launch_quant_pack(const PackArgs& a, hipStream_t s) {
+hipError_t launch_quant_pack_generic(const PackArgs& a, hipStream_t s) {
   const bool f32 = a.y.dtype == 0;
-  if (!a.perm && a.n_int4 == 0) {
-    PackBatch pb;
-    pb.n = 1;
-    pb.a[0] = a;
-    return launch_quant_pack_batch(pb, s);
-  }
   const int64_t total = (int64_t)a.H * a.N * a.groups;
   const dim3 grid((unsigned)((total + 255) / 256)), block(256);
 #define QKV_QP(GV)                                                              \
@@ -511,6 +502,16 @@ hipError_t launch_quant_pack(const PackArgs& a, hipStream_t s) {
   return hipErrorInvalidValue;
 }
 
+hipError_t launch_quant_pack(const PackArgs& a, hipStream_t s) {
+  if (!a.perm && a.n_int4 == 0) {
+    PackBatch pb;
+    pb.n = 1;
+    pb.a[0] = a;
+    return launch_quant_pack_batch(pb, s);
+  }
+  return launch_quant_pack_generic(a, s);
+}
+
 bool quant_pack_batchable(const PackArgs& a, const PackArgs& b0) {
   return !a.perm && a.n_int4 == 0 && a.group == b0.group && a.bits == b0.bits && a.y.dtype == b0.y.dtype &&
          a.H == b0.H && a.N == b0.N;
@@ -521,6 +522,17 @@ hipError_t launch_quant_pack_batch(const PackBatch& b, hipStream_t s) {
   for (int p = 0; p < b.n; ++p)
     if (!quant_pack_batchable(b.a[p], a)) return hipErrorInvalidValue;
   if (a.words != kHeadDim * a.bits / 32 || a.groups != kHeadDim / a.group) return hipErrorInvalidValue;
+  // the tile kernel forms in-tile offsets with 24-bit multiplies
+  bool small = true;
+  for (int p = 0; p < b.n; ++p)
+    small = small && b.a[p].y.stride_token < (1 << 23) && b.a[p].y.stride_head < (1 << 23) && b.a[p].N < (1 << 23);
+  if (!small) {
+    for (int p = 0; p < b.n; ++p) {
+      hipError_t e = launch_quant_pack_generic(b.a[p], s);
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+  }
   const bool f32 = a.y.dtype == 0;
   const int tiles = tile_geom(a.H, a.N).tiles;
   const dim3 grid((unsigned)(tiles * b.n)), block(256);
