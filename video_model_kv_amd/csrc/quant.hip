@@ -215,15 +215,16 @@ __global__ __launch_bounds__(256) void k_quant_pack(PackArgs a) {
 }
 
 // Uniform layout without a channel permutation.  A workgroup owns a tile of
-// T tokens x HB heads (T * HB <= 128 rows, HB = min(H, 128)) taken in
+// T tokens x HB heads (T * HB <= 64 rows, HB = min(H, 64)) taken in
 // token-major order, so with the usual [N][H][128] input it reads one
-// contiguous run of memory (32 KB for 32 bf16 heads) and HBM pages stream in
-// order.  A thread handles 8 consecutive channels of a row (one 16-byte load);
-// a wave covers 4 rows per item; a group of G channels spans G/8 aligned lanes
-// and takes its max through xor shuffles.  Codes and scales are staged in LDS
-// and written per head as contiguous runs of T rows.  Same arithmetic as
-// k_quant_pack.
-constexpr int kTileRows = 128;
+// contiguous run of memory (16 KB for 32 bf16 heads) and HBM pages stream in
+// order; neighbouring tiles run on one XCD, whose L2 joins their partial
+// lines of codes and scales.  A thread handles 8 consecutive channels of a
+// row (one 16-byte load) in each of 4 items; a wave covers 4 rows per item; a
+// group of G channels spans G/8 aligned lanes and takes its max through DPP
+// lane exchanges.  Codes and scales are staged in LDS and written per head as
+// contiguous runs of T rows.  Same results as k_quant_pack.
+constexpr int kTileRows = 64;
 struct TileGeom {
   int HB, T, nhb, tiles;    // heads per tile, tokens per tile, head blocks, tiles per problem
 };
@@ -257,7 +258,7 @@ __global__ __launch_bounds__(256) void k_quant_pack_tile(PackBatch pb, int tiles
   const int tid = threadIdx.x;
   const int part = tid & 15, k0 = part * 8;
   // local row lr = x * 16 + tid / 16 of item x splits as lr = t * HB + hh;
-  // t = (lr * inv) >> 16 is exact for lr < 128, HB <= 128
+  // t = (lr * inv) >> 16 is exact for lr < 128, HB <= 128 (here lr < 64)
   const uint32_t inv = 65536u / (uint32_t)tg.HB + 1u;
   auto split = [&](int x, int& t, int& hh) __attribute__((always_inline)) {
     const int lr = x * 16 + (tid >> 4);
