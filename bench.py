@@ -234,7 +234,10 @@ def main():
     cent = torch.empty((H, wl.n_clusters, d), dtype=torch.float32, device=dev)
     stride = ntok[0] // wl.n_clusters
     cent.copy_(xk[0][0:wl.n_clusters * stride:stride].float().transpose(0, 1))   # strided init rows
-    labels = torch.empty(H * ntok[0], dtype=torch.uint8, device=dev)
+    # the labels live in the packed chunk's own label section, so the
+    # quant-pack call copies none (its launches: centroid rounding + pack)
+    lay0 = qk.qkv_chunk_layout(kcfg, ntok[0])
+    labels = kp[0][lay0.off_labels:lay0.off_labels + H * ntok[0]]
     t_assign = timed(lambda: qk.qkv_kmeans_assign(kcfg, xk[0], cent, labels, ws), reps)
     t_pack = timed(lambda: qk.qkv_quant_pack(kcfg, xk[0], labels, cent, kp[0], 0,
                                              perm=side_k.get("perm")), reps)
@@ -273,8 +276,12 @@ def main():
     assign_roof = {"kernel": "k_assign (qkv_kmeans_assign call)", "bound": "mfma", "achieved": achieved_a,
                    "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": achieved_a / BF16_PEAK_TFLOPS,
                    "traffic": None, "algorithmic_per_launch": assign_flops}
-    pack_roof = {"kernel": "k_quant_pack", "bound": "hbm", "achieved": comp["quant_pack_gbps"], "peak": HBM_PEAK_GBS,
-                 "unit": "GB/s", "frac": comp["quant_pack_gbps"] / HBM_PEAK_GBS, "traffic": None,
+    trq = stored_traffic("k_quant_pack_tile", ["video_model_kv_amd/csrc/quant.hip", "video_model_kv_amd/csrc/common.h",
+                                               "video_model_kv_amd/csrc/kernels.h", "video_model_kv_amd/csrc/layout.h"])
+    pack_roof = {"kernel": "k_quant_pack_tile (qkv_quant_pack call: k_centroid_bf16 + k_quant_pack_tile)",
+                 "bound": "hbm", "achieved": comp["quant_pack_gbps"], "peak": HBM_PEAK_GBS,
+                 "unit": "GB/s", "frac": comp["quant_pack_gbps"] / HBM_PEAK_GBS,
+                 "traffic": None if trq is None else trq["read"] + trq["write"],
                  "algorithmic_per_launch": pack_bytes}
     cpu = None
     if not a.no_cpu_baseline:
