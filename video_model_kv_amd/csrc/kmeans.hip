@@ -743,71 +743,53 @@ __global__ __launch_bounds__(256, 4) void k_update(KmBatch b, int refresh) {
     total[0] += mb - ma;
     total[1] += mc - mb;
     if (plain) {
-      // Both clusters at once, 8 bytes per lane: lane group g = lane / 32 takes rows
-      // ma + g, ma + g + 2, ...; lane channels c4 .. c4 + 3.  Float64 partial sums per
-      // group, joined across the two groups (exact under the certificate, so any
-      // grouping gives the same sum).
+      // Lane group g = lane / 32 sums cluster 2w + g alone, 8 bytes per lane
+      // (channels c4 .. c4 + 3), kUpdRows of its member rows in flight: no
+      // per-row selects and no join across the groups.  Float64 sums, exact
+      // under the certificate.  A group whose cluster has fewer rows reads
+      // clamped list entries (inside this window's list, which holds at least
+      // one row whenever the loop runs) and adds nothing.
       const int g = lane >> 5, c4 = (lane & 31) * 4;
       const int64_t hoff4 = (int64_t)h * y.stride_head + c4;
-      double sa[4], sb[4];
-      u16x2 mxa[2], mna[2], mxb[2], mnb[2];      // magnitudes: max, and min nonzero - 1
+      const int mg0 = g == 0 ? ma : mb, ng = g == 0 ? mb - ma : mc - mb;
+      const int nmax = max(mb - ma, mc - mb);
+      double sv[4];
+      u16x2 mx[2], mn[2];                        // magnitudes: max, and min nonzero - 1
 #pragma unroll
-      for (int e = 0; e < 4; ++e) sa[e] = sb[e] = 0.0;
+      for (int e = 0; e < 4; ++e) sv[e] = 0.0;
 #pragma unroll
       for (int p = 0; p < 2; ++p) {
-        mxa[p] = mxb[p] = u16x2{0, 0};
-        mna[p] = mnb[p] = u16x2{0xFFFF, 0xFFFF};
+        mx[p] = u16x2{0, 0};
+        mn[p] = u16x2{0xFFFF, 0xFFFF};
       }
-      for (int m = ma; m < mc; m += 2 * kUpdRows) {
+      for (int m = 0; m < nmax; m += kUpdRows) {
         uint2 raw[kUpdRows];
 #pragma unroll
         for (int q = 0; q < kUpdRows; ++q) {
-          const int r = min(m + 2 * q + g, mc - 1);
+          const int r = max(mg0 + min(m + q, ng - 1), 0);
           raw[q] = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(y.ptr) +
                                                    (int64_t)(t0 + s_mem[r]) * y.stride_token + hoff4);
         }
 #pragma unroll
         for (int q = 0; q < kUpdRows; ++q) {
-          const int r = m + 2 * q + g;
-          if (r < mc) {
-            const bool inA = r < mb;
+          if (m + q < ng) {
             const uint32_t w2[2] = {raw[q].x, raw[q].y};
 #pragma unroll
             for (int p = 0; p < 2; ++p) {
-              const double v0 = (double)bf16_bits_to_f32(w2[p] & 0xFFFFu), v1 = (double)bf16_bits_to_f32(w2[p] >> 16);
-              sa[2 * p] += inA ? v0 : 0.0;
-              sa[2 * p + 1] += inA ? v1 : 0.0;
-              sb[2 * p] += inA ? 0.0 : v0;
-              sb[2 * p + 1] += inA ? 0.0 : v1;
+              sv[2 * p] += (double)bf16_bits_to_f32(w2[p] & 0xFFFFu);
+              sv[2 * p + 1] += (double)bf16_bits_to_f32(w2[p] >> 16);
               const u16x2 mag = __builtin_bit_cast(u16x2, w2[p] & 0x7FFF7FFFu);
-              const u16x2 m1 = mag - u16x2{1, 1};           // a zero wraps to 0xFFFF: ignored by min
-              if (inA) {
-                mxa[p] = __builtin_elementwise_max(mxa[p], mag);
-                mna[p] = __builtin_elementwise_min(mna[p], m1);
-              } else {
-                mxb[p] = __builtin_elementwise_max(mxb[p], mag);
-                mnb[p] = __builtin_elementwise_min(mnb[p], m1);
-              }
+              mx[p] = __builtin_elementwise_max(mx[p], mag);
+              mn[p] = __builtin_elementwise_min(mn[p], mag - u16x2{1, 1});   // a zero wraps to 0xFFFF
             }
           }
         }
       }
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        sa[e] += __shfl_xor(sa[e], 32);
-        sb[e] += __shfl_xor(sb[e], 32);
-      }
-#pragma unroll
-      for (int p = 0; p < 2; ++p) {
-        mxa[p] = __builtin_elementwise_max(mxa[p], __builtin_bit_cast(u16x2, __shfl_xor(__builtin_bit_cast(int, mxa[p]), 32)));
-        mna[p] = __builtin_elementwise_min(mna[p], __builtin_bit_cast(u16x2, __shfl_xor(__builtin_bit_cast(int, mna[p]), 32)));
-        mxb[p] = __builtin_elementwise_max(mxb[p], __builtin_bit_cast(u16x2, __shfl_xor(__builtin_bit_cast(int, mxb[p]), 32)));
-        mnb[p] = __builtin_elementwise_min(mnb[p], __builtin_bit_cast(u16x2, __shfl_xor(__builtin_bit_cast(int, mnb[p]), 32)));
-      }
-      // certificate per cluster over this lane's 4 channels, then over the wave
-      auto certified = [&](const u16x2 (&mx)[2], const u16x2 (&mn)[2], int n) __attribute__((always_inline)) {
-        const int lg = 32 - __builtin_clz((unsigned)max(n, 1));   // >= ceil(log2 n)
-        bool ok = true;
+      // certificate of each group's cluster over its 32 lanes' channels
+      bool ok;
+      {
+        const int lg = 32 - __builtin_clz((unsigned)max(ng, 1));   // >= ceil(log2 n)
+        ok = true;
 #pragma unroll
         for (int p = 0; p < 2; ++p)
 #pragma unroll
@@ -816,9 +798,9 @@ __global__ __launch_bounds__(256, 4) void k_update(KmBatch b, int refresh) {
             const int emin = max((nz >> 7) & 0xFF, 1);                           // subnormals share exponent 1's unit
             ok = ok && (mn[p][e] == 0xFFFF || (emax < 0xFF && emax - emin + lg <= 44));
           }
-        return __all(ok) != 0;
-      };
-      const bool okc[2] = {certified(mxa, mna, mb - ma), certified(mxb, mnb, mc - mb)};
+      }
+      const uint64_t bad = __ballot(!ok);
+      const bool okc[2] = {(uint32_t)bad == 0u, (uint32_t)(bad >> 32) == 0u};
       // certified clusters: lane group 0 finishes the first, group 1 the second
       {
         const int cc = g;
@@ -827,7 +809,7 @@ __global__ __launch_bounds__(256, 4) void k_update(KmBatch b, int refresh) {
         if (okc[cc] && n > 0 && j < C) {
           float cv[4];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) cv[e] = (float)((cc == 0 ? sa[e] : sb[e]) / (double)n);
+          for (int e = 0; e < 4; ++e) cv[e] = (float)(sv[e] / (double)n);
           *reinterpret_cast<float4*>(c + ((int64_t)h * C + j) * kHeadDim + c4) = make_float4(cv[0], cv[1], cv[2], cv[3]);
           if (planes) {   // operand planes (-2 w c) and weighted norm for the next assign
             double nrm = 0.0;
