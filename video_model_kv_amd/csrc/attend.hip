@@ -20,6 +20,7 @@
 // V_hat and the probabilities enter P V in bf16 with fp32 accumulation.  The
 // PSAC term rides one extra MFMA k-step: [coef | coef] against
 // [hi(qU) | lo(qU)].  Splits are merged with the usual log-sum-exp rescaling.
+#include <algorithm>
 #include <cstddef>
 #include <utility>
 
@@ -135,7 +136,9 @@ __device__ __forceinline__ uint32_t f16x2_sat(f16x2 v) {
   return __builtin_bit_cast(uint32_t, v);
 }
 // S * q + c as saturated fp16 pairs for NP consecutive channel pairs: code
-// pair j of `t` sits at bits [4j, 4j+1] and [4j+16, 4j+17] (t = codes | codes << 14).
+// pair j of `t` sits at bits [4j, 4j+1] and [4j+16, 4j+17] (t = codes | codes << 14);
+// cw holds the centroid pairs already in fp16 (the per-call fp16 copy of the
+// chunk's bf16 table).
 template <int NP>
 __device__ __forceinline__ void decode_pairs_f16(uint32_t t, float S, const uint32_t* cw, uint32_t* out) {
   const _Float16 sh = (_Float16)__builtin_amdgcn_fmed3f(S, -kF16Max, kF16Max);
@@ -143,7 +146,7 @@ __device__ __forceinline__ void decode_pairs_f16(uint32_t t, float S, const uint
 #pragma unroll
   for (int j = 0; j < NP; ++j) {
     const f16x2 q = codes_to_f16x2((t >> (4 * j)) & 0x00030003u);
-    out[j] = f16x2_sat(__builtin_elementwise_fma(s2, q, bf16x2_to_f16x2(cw[j])));
+    out[j] = f16x2_sat(__builtin_elementwise_fma(s2, q, __builtin_bit_cast(f16x2, cw[j])));
   }
 }
 
@@ -806,7 +809,8 @@ __global__ __launch_bounds__(256) void k_qu(TensorView q, int H, int Nq, int r, 
 
 // TileRec of every tile: the chunk holding it is the last one whose first tile is <= j.
 __global__ __launch_bounds__(256) void k_tile_table(const ChunkRec* __restrict__ recs, int n_chunks, int n_tiles,
-                                                    TokenBytes tb, TileRec* __restrict__ tiles) {
+                                                    TokenBytes tb, int H, int kC, int vC, const uint16_t* k16,
+                                                    const uint16_t* v16, TileRec* __restrict__ tiles) {
   const int j = blockIdx.x * blockDim.x + threadIdx.x;
   if (j >= n_tiles) return;
   int lo = 0, hi = n_chunks - 1;
@@ -823,8 +827,8 @@ __global__ __launch_bounds__(256) void k_tile_table(const ChunkRec* __restrict__
   t.src[1][1] = c.vscales + (int64_t)token0 * tb.vscales;
   t.src[0][2] = c.klabels + token0;
   t.src[1][2] = c.vlabels + token0;
-  t.cent[0] = c.kcent;
-  t.cent[1] = c.vcent;
+  t.cent[0] = k16 ? reinterpret_cast<const uint8_t*>(k16 + (int64_t)lo * H * kC * kHeadDim) : c.kcent;
+  t.cent[1] = v16 ? reinterpret_cast<const uint8_t*>(v16 + (int64_t)lo * H * vC * kHeadDim) : c.vcent;
   t.kpsac = c.kpsac + (int64_t)token0 * tb.kpsac;
   t.n = c.n;
   t.nvalid = min(kKTile, c.n - token0);
@@ -833,6 +837,27 @@ __global__ __launch_bounds__(256) void k_tile_table(const ChunkRec* __restrict__
   t.chunk = lo;
   t.pad = 0;
   tiles[j] = t;
+}
+
+// Thread: 8 channels of one centroid row; blockIdx.y: 0 keys, 1 values.
+__global__ __launch_bounds__(256) void k_centroids_f16(const ChunkRec* __restrict__ recs, int n_chunks, int H, int kC,
+                                                       int vC, uint16_t* __restrict__ k16, uint16_t* __restrict__ v16) {
+  const bool v = blockIdx.y == 1;
+  uint16_t* dst = v ? v16 : k16;
+  const int C = v ? vC : kC;
+  if (!dst) return;
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t per_chunk = (int64_t)H * C * (kHeadDim / 8);
+  if (gid >= per_chunk * n_chunks) return;
+  const int chunk = (int)(gid / per_chunk);
+  const int64_t e = (gid % per_chunk) * 8;      // element within the chunk's [H][C][128] table
+  const uint16_t* src = reinterpret_cast<const uint16_t*>(v ? recs[chunk].vcent : recs[chunk].kcent);
+  const uint4 w = *reinterpret_cast<const uint4*>(src + e);
+  const uint32_t w4[4] = {w.x, w.y, w.z, w.w};
+  uint32_t o4[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) o4[k] = __builtin_bit_cast(uint32_t, bf16x2_to_f16x2(w4[k]));
+  *reinterpret_cast<uint4*>(dst + chunk * per_chunk * 8 + e) = make_uint4(o4[0], o4[1], o4[2], o4[3]);
 }
 
 __global__ void k_upload(ChunkBatch b, ChunkRec* __restrict__ dst) {
@@ -847,11 +872,20 @@ hipError_t launch_upload_chunks(const ChunkBatch& b, ChunkRec* dst, hipStream_t 
   return hipGetLastError();
 }
 
-hipError_t launch_tile_table(const ChunkRec* recs, int n_chunks, int n_tiles, TokenBytes tb, TileRec* tiles,
-                             hipStream_t s) {
+hipError_t launch_centroids_f16(const ChunkRec* recs, int n_chunks, int H, int kC, int vC, uint16_t* k16,
+                                uint16_t* v16, hipStream_t s) {
+  if (!k16 && !v16) return hipSuccess;
+  const int64_t per = (int64_t)H * std::max(k16 ? kC : 0, v16 ? vC : 0) * (kHeadDim / 8) * n_chunks;
+  hipLaunchKernelGGL(k_centroids_f16, dim3((unsigned)((per + 255) / 256), 2), dim3(256), 0, s, recs, n_chunks, H, kC, vC,
+                     k16, v16);
+  return hipGetLastError();
+}
+
+hipError_t launch_tile_table(const ChunkRec* recs, int n_chunks, int n_tiles, TokenBytes tb, int H, int kC, int vC,
+                             const uint16_t* k16, const uint16_t* v16, TileRec* tiles, hipStream_t s) {
   if (n_tiles <= 0) return hipSuccess;
   hipLaunchKernelGGL(k_tile_table, dim3((unsigned)((n_tiles + 255) / 256)), dim3(256), 0, s, recs, n_chunks, n_tiles, tb,
-                     tiles);
+                     H, kC, vC, k16, v16, tiles);
   return hipGetLastError();
 }
 

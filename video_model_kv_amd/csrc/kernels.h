@@ -150,8 +150,14 @@ struct ChunkBatch {
 };
 hipError_t launch_upload_chunks(const ChunkBatch& b, ChunkRec* dst, hipStream_t s);
 // TileRec of every tile from the uploaded chunk records.
-hipError_t launch_tile_table(const ChunkRec* recs, int n_chunks, int n_tiles, TokenBytes tb, TileRec* tiles,
-                             hipStream_t s);
+// fp16 copies of the chunks' bf16 centroid tables ([chunk][H][C][128], round to
+// nearest even, beyond the fp16 range -> +-inf) for the tensors decoded by the
+// attention fast path; k16 / v16 may be NULL (tensor not on the fast path).
+hipError_t launch_centroids_f16(const ChunkRec* recs, int n_chunks, int H, int kC, int vC, uint16_t* k16,
+                                uint16_t* v16, hipStream_t s);
+// Tile records; the fast-path centroid pointers go to k16 / v16 when given.
+hipError_t launch_tile_table(const ChunkRec* recs, int n_chunks, int n_tiles, TokenBytes tb, int H, int kC, int vC,
+                             const uint16_t* k16, const uint16_t* v16, TileRec* tiles, hipStream_t s);
 
 struct AttendArgs {
   TensorView q;

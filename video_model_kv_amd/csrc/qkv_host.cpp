@@ -169,11 +169,12 @@ QuantWs quant_ws(const qkv_config* c, int64_t n) {
 constexpr int kTileKeys = 64;
 
 struct AttendWs {
-  uint64_t chunks, tiles, qu, part_o, part_ml, bytes;
+  uint64_t chunks, tiles, qu, part_o, part_ml, k16, v16, bytes;
 };
 
-// rows = n_split * nq: one partial (o, m, l) row per split and query (none when n_split == 1)
-AttendWs attend_ws(int H, int64_t nq, int n_chunks, int64_t n_tiles, int64_t split_rows) {
+// rows = n_split * nq: one partial (o, m, l) row per split and query (none when n_split == 1);
+// kC16 / vC16: clusters of the key / value tables copied to fp16 for the fast decode (0: none)
+AttendWs attend_ws(int H, int64_t nq, int n_chunks, int64_t n_tiles, int64_t split_rows, int kC16, int vC16) {
   AttendWs w;
   uint64_t off = 0;
   w.chunks = off;  off += align256((uint64_t)n_chunks * sizeof(ChunkRec));
@@ -181,6 +182,8 @@ AttendWs attend_ws(int H, int64_t nq, int n_chunks, int64_t n_tiles, int64_t spl
   w.qu = off;      off += align256((uint64_t)H * nq * kMaxRank * 4);
   w.part_o = off;  off += align256((uint64_t)split_rows * H * kHeadDim * 4);
   w.part_ml = off; off += align256((uint64_t)split_rows * H * 2 * 4);
+  w.k16 = off;     off += align256((uint64_t)n_chunks * H * kC16 * kHeadDim * 2);
+  w.v16 = off;     off += align256((uint64_t)n_chunks * H * vC16 * kHeadDim * 2);
   w.bytes = off;
   return w;
 }
@@ -420,7 +423,7 @@ int qkv_workspace_bytes(const qkv_config* cfg, int64_t max_chunk_tokens, int64_t
   if (max_chunk_tokens > 0) need = std::max(need, quant_ws(cfg, max_chunk_tokens).bytes);
   if (n_query > 0 && n_chunks > 0) {
     need = std::max(need, attend_ws(cfg->n_heads, n_query, n_chunks, max_tiles(std::max<int64_t>(max_chunk_tokens, 1), n_chunks),
-                                    max_split_rows(cfg->n_heads, n_query)).bytes);
+                                    max_split_rows(cfg->n_heads, n_query), kMaxClusters, kMaxClusters).bytes);
   }
   if (n_query > 0) need = std::max(need, psac_ws(cfg->n_heads));
   *out = (size_t)need;
@@ -514,7 +517,12 @@ int qkv_attend(const qkv_config* k_cfg, const qkv_config* v_cfg, const qkv_tenso
   // A workspace sized by qkv_workspace_bytes for at least these queries and
   // chunks always suffices: ns <= split_cap(H, Nq).
   const int ns = choose_splits(H, Nq, n_tiles);
-  const AttendWs ws = attend_ws(H, Nq, n_chunks, n_tiles, ns > 1 ? (int64_t)ns * Nq : 0);
+  auto fast = [](const qkv_config* c) {
+    return c->n_stages == 1 && c->n_int4_channels == 0 && c->bits == 2 && c->group % 32 == 0;
+  };
+  const bool kfast = fast(k_cfg), vfast = fast(v_cfg);
+  const int kC16 = kfast ? k_cfg->n_clusters : 0, vC16 = vfast ? v_cfg->n_clusters : 0;
+  const AttendWs ws = attend_ws(H, Nq, n_chunks, n_tiles, ns > 1 ? (int64_t)ns * Nq : 0, kC16, vC16);
   QKV_TRY(check_ws(workspace, workspace_bytes, ws.bytes, fn));
 
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
@@ -528,10 +536,14 @@ int qkv_attend(const qkv_config* k_cfg, const qkv_config* v_cfg, const qkv_tenso
     QKV_HIP(launch_upload_chunks(b, drecs, s));
   }
   TileRec* dtiles = reinterpret_cast<TileRec*>(at(workspace, ws.tiles));
+  uint16_t* k16 = kfast ? reinterpret_cast<uint16_t*>(at(workspace, ws.k16)) : nullptr;
+  uint16_t* v16 = vfast ? reinterpret_cast<uint16_t*>(at(workspace, ws.v16)) : nullptr;
+  QKV_HIP(launch_centroids_f16(drecs, n_chunks, H, k_cfg->n_clusters, v_cfg->n_clusters, k16, v16, s));
   {
     const ChunkDecode dk = make_decode(params_of(k_cfg), 1, nullptr), dv = make_decode(params_of(v_cfg), 1, nullptr);
     const TokenBytes tb{dk.words * 4, dv.words * 4, dk.groups * 2, dv.groups * 2, k_cfg->psac_rank * 2};
-    QKV_HIP(launch_tile_table(drecs, n_chunks, (int)n_tiles, tb, dtiles, s));
+    QKV_HIP(launch_tile_table(drecs, n_chunks, (int)n_tiles, tb, H, k_cfg->n_clusters, v_cfg->n_clusters, k16, v16,
+                              dtiles, s));
   }
 
   AttendArgs a;
@@ -557,11 +569,8 @@ int qkv_attend(const qkv_config* k_cfg, const qkv_config* v_cfg, const qkv_tenso
   a.out_stride_token = out->stride_token;
   a.out_stride_head = out->stride_head;
   a.logits = logits_debug;
-  auto fast = [](const qkv_config* c) {
-    return c->n_stages == 1 && c->n_int4_channels == 0 && c->bits == 2 && c->group % 32 == 0;
-  };
-  a.k_uniform_int2_1stage = fast(k_cfg);
-  a.v_uniform_int2_1stage = fast(v_cfg);
+  a.k_uniform_int2_1stage = kfast;
+  a.v_uniform_int2_1stage = vfast;
   QKV_HIP(launch_attend(a, s));
   return ok();
 }
