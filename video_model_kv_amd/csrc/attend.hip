@@ -35,6 +35,7 @@ constexpr int kKTile = 64;      // keys per tile
 constexpr int kKPitch = 136;    // bf16 pitch of the K_hat rows in LDS
 constexpr int kVPitch = 66;     // fp16 pitch of the V_hat^T rows in LDS (33 dwords: odd, for conflict-free writes)
 constexpr float kLog2e = 1.4426950408889634f;
+static_assert(kHeadDim == 128, "scale indexes below divide by the head size with a shift by 7");
 
 __device__ __forceinline__ const uint8_t* sp(const ChunkDecode& d, uint64_t off, uint64_t stride, int l) {
   return d.base + off + stride * (uint64_t)l;
@@ -444,7 +445,7 @@ __global__ __launch_bounds__(kThreads) void k_attend(AttendArgs a) {
       uint32_t o4[4];
       if constexpr (KFAST) {
         const uint32_t w = sRc[r][0][key * 8 + (k0 >> 4)];
-        const uint32_t sb = sRs[r][0][klead + key * kG + k0 * kG / kHeadDim];
+        const uint32_t sb = sRs[r][0][klead + (key << kGs) + ((k0 << kGs) >> 7)];   // groups: powers of two
         const uint4 cr = *reinterpret_cast<const uint4*>(&sCentK[g][key * kHeadDim + k0]);
         // keys past nvalid decode stale LDS contents: the saturation keeps
         // them finite, and their scores are masked (probability 0)
@@ -474,7 +475,7 @@ __global__ __launch_bounds__(kThreads) void k_attend(AttendArgs a) {
         const bool ok = key < nvalid;
         if constexpr (VFAST) {
           const uint32_t w = sRc[r][1][key * 8 + (k0 >> 4)];
-          const uint32_t sb = sRs[r][1][vlead + key * vG + k0 * vG / kHeadDim];
+          const uint32_t sb = sRs[r][1][vlead + (key << vGs) + ((k0 << vGs) >> 7)];
           const uint2 cr = *reinterpret_cast<const uint2*>(&sCentV[g][key * kHeadDim + k0]);
           const uint32_t code8 = (w >> (2 * (k0 & 15))) & 0xFFu;   // keys past nvalid: finite, weight 0
           const uint32_t cw[2] = {cr.x, cr.y};
