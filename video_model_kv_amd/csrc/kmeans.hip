@@ -536,7 +536,7 @@ __global__ __launch_bounds__(kAsgThreads) void k_assign(KmBatch b, int G) {
 constexpr int kUpdClusters = 8;
 constexpr int kUpdWindow = 8192;          // token index << 3 fits 16 bits
 static_assert(kUpdWindow == kGroupMaxTokens, "grouped heads fit one update window");
-constexpr int kUpdRows = 12;            // row loads (2 rows each) in flight per wave
+constexpr int kUpdRows = 12;            // member-row loads in flight per lane group
 
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 

@@ -135,9 +135,13 @@ __device__ __forceinline__ uint32_t pack8_codes(const float* r, float S, uint32_
     for (int e = 0; e < 8; ++e) {
       float x = r[e] * rS;
       x = __builtin_fmaf(__builtin_fmaf(-x, S, r[e]), rS, x);
-      const uint32_t z = __float_as_uint(x + kBias);           // 0x4B400000 + u
-      w |= (z & ((1u << BITS) - 1u)) << (BITS * e);
+      const uint32_t z = __float_as_uint(x + kBias);           // 0x4B400000 + u, u < 2^BITS
+      // INT2: bits 2..21 of z are zero, so z << 2e carries u at bits [2e, 2e + 2)
+      // and nothing else below bit 22; the word is cut to 16 bits at the end
+      if constexpr (BITS == 2) w |= z << (BITS * e);
+      else w |= (z & ((1u << BITS) - 1u)) << (BITS * e);
     }
+    if constexpr (BITS == 2) w &= 0xFFFFu;
   } else {
     float q[8];
     group_codes<8>(r, S, -(float)(1 << (BITS - 1)), qmax, q);
@@ -215,22 +219,24 @@ __global__ __launch_bounds__(256) void k_quant_pack(PackArgs a) {
 }
 
 // Uniform layout without a channel permutation.  A workgroup owns a tile of
-// T tokens x HB heads (T * HB <= 64 rows, HB = min(H, 64)) taken in
-// token-major order, so with the usual [N][H][128] input it reads one
-// contiguous run of memory (16 KB for 32 bf16 heads) and HBM pages stream in
-// order; neighbouring tiles run on one XCD, whose L2 joins their partial
-// lines of codes and scales.  A thread handles 8 consecutive channels of a
-// row (one 16-byte load) in each of 4 items; a wave covers 4 rows per item; a
+// T tokens x HB heads (HB = min(H, 4), T * HB <= 64 rows) taken in
+// token-major order: with the usual [N][H][128] input that is T runs of 1 KB
+// (4 bf16 heads).  Tiles run head block by head block, so the workgroups an
+// XCD holds at a time share a few heads' centroid tables in its L2 and read
+// neighbouring token rows.  A thread handles 8 consecutive channels of a row
+// (one 16-byte load) in each of 4 items; a wave covers 4 rows per item; a
 // group of G channels spans G/8 aligned lanes and takes its max through DPP
 // lane exchanges.  Codes and scales are staged in LDS and written per head as
-// contiguous runs of T rows.  Same results as k_quant_pack.
+// contiguous runs of T rows (512 B of INT2 codes).  Same results as
+// k_quant_pack.
 constexpr int kTileRows = 64;
 struct TileGeom {
   int HB, T, nhb, tiles;    // heads per tile, tokens per tile, head blocks, tiles per problem
 };
+constexpr int kTileHeads = 4;
 __host__ __device__ inline TileGeom tile_geom(int H, int N) {
   TileGeom g;
-  g.HB = H < kTileRows ? H : kTileRows;
+  g.HB = H < kTileHeads ? H : kTileHeads;
   g.T = kTileRows / g.HB;
   g.nhb = (H + g.HB - 1) / g.HB;
   g.tiles = ((N + g.T - 1) / g.T) * g.nhb;
@@ -248,12 +254,13 @@ __global__ __launch_bounds__(256) void k_quant_pack_tile(PackBatch pb, int tiles
   __shared__ float s_rtab[128];                   // fp32(1 / (1 + k / 128))
   if (threadIdx.x < 128) s_rtab[threadIdx.x] = 1.0f / (1.0f + (float)threadIdx.x * 0.0078125f);
   __syncthreads();
-  const uint32_t logical = xcd_remap(blockIdx.x, gridDim.x);   // neighbouring tiles share an XCD (L2)
+  const uint32_t logical = xcd_remap(blockIdx.x, gridDim.x);   // consecutive tiles share an XCD (L2)
   const PackArgs& a = pb.a[logical / tiles];
   const int tile = (int)(logical % tiles);
   const TileGeom tg = tile_geom(a.H, a.N);
-  const int hb = tile % tg.nhb;
-  const int i0 = (tile / tg.nhb) * tg.T, h0 = hb * tg.HB;
+  const int ntb = (a.N + tg.T - 1) / tg.T;         // token blocks; tiles run head block by head block
+  const int hb = tile / ntb;
+  const int i0 = (tile % ntb) * tg.T, h0 = hb * tg.HB;
   const int rows = tg.T * tg.HB;                  // <= kTileRows
   const int tid = threadIdx.x;
   const int part = tid & 15, k0 = part * 8;
