@@ -180,6 +180,39 @@ def test_quant_pack_half_integer_quotients(bits):
     assert ties > 1000, "the input should hold many exact half-integer quotients"
 
 
+def test_quant_pack_large_token_stride():
+    """A token stride of 2^23 + 256 elements (beyond the tile kernel's 24-bit
+    in-tile offsets) routes to the per-group kernel; codes, scales and
+    residuals still match the oracle bit for bit."""
+    t = G.torch()
+    H, N, C = 2, 300, 16
+    ST = (1 << 23) + 256
+    rng = np.random.default_rng(23)
+    x = bf16_rne(rng.normal(0.0, 1.0, size=(N, H, 128)) * rng.choice([1.0, 40.0], size=(N, H, 1)))
+    lab = rng.integers(0, C, size=(H, N)).astype(np.uint8)
+    cent = rng.normal(0.0, 1.0, size=(H, C, 128)).astype(np.float32)
+    cfg = qk.Config(n_heads=H, n_clusters=C, bits=2, group=32)
+    G.log(f"quant_pack large token stride: stride {ST} elements, N={N}, H={H}")
+    buf = t.empty((N - 1) * ST + H * 128, dtype=t.bfloat16, device=G.dev())
+    y = t.as_strided(buf, (N, H, 128), (ST, 128, 1))
+    y.copy_(t.from_numpy(np.ascontiguousarray(x, np.float32)).to(t.bfloat16).to(G.dev()))
+    packed = t.zeros(qk.qkv_chunk_layout(cfg, N).bytes, dtype=t.uint8, device=G.dev())
+    ynext = t.empty((H, N, 128), dtype=t.float32, device=G.dev())
+    qk.qkv_quant_pack(cfg, y, t.from_numpy(lab.reshape(-1)).to(G.dev()), G.to_dev(cent), packed, 0, y_next=ynext)
+    v = G.host_views(packed, cfg, N)
+    yn = ynext.cpu().numpy()
+    del buf, y
+    for h in range(H):
+        layout = oq.channel_layout(128, 2, 32, 0, None)
+        rows = bf16_rne(cent[h])[lab[h].astype(np.int64)]
+        r = (x[:, h] - rows).astype(np.float32)
+        q, s = oq.quantize_groups(r, layout)
+        assert np.array_equal(v["codes"][0, h].view(np.uint32), oq.pack_codes(q, layout)), f"head {h}: codes"
+        assert np.array_equal(v["scales"][0, h].view(np.uint16), G.f32_bits_to_bf16(s)), f"head {h}: scales"
+        yhat = oq.dequantize(q, s, rows, layout)
+        assert np.array_equal(yn[h].view(np.uint32), (x[:, h] - yhat).astype(np.float32).view(np.uint32))
+
+
 FREE = [
     ("tiny-K", 1, {}, "K", None, False),
     ("tiny-V-rtn", 1, {}, "V", None, True),
