@@ -95,6 +95,54 @@ __device__ __forceinline__ void decode_generic(const ChunkDecode& d, const Chann
   }
 }
 
+// Uniform layout (no channel permutation): the same x_hat as decode_generic
+// for channels k0 .. k0 + NCH - 1 (k0 a multiple of NCH, so they share one
+// code word and one scale group in every stage).  The stage loop runs to
+// kMaxStages with clamped stage indexes so that every load is issued before
+// any value is used -- the labels of all stages, then the code words, scales
+// and centroid pieces they select -- instead of two dependent round trips per
+// stage; stages past n_stages are loaded again from the last one and not added.
+template <int NCH>
+__device__ __forceinline__ void decode_uniform(const ChunkDecode& d, int h, int j, int k0, float* v) {
+  static_assert(NCH == 8 || NCH == 4, "channels per item");
+  const int64_t row = (int64_t)h * d.N + j;
+  const int per = 32 / d.bits;
+  int lab[kMaxStages];
+#pragma unroll
+  for (int l = 0; l < kMaxStages; ++l) lab[l] = sp(d, d.off_labels, d.stage_labels, min(l, d.n_stages - 1))[row];
+  uint32_t word[kMaxStages], sc[kMaxStages], cw[kMaxStages][NCH / 2];
+#pragma unroll
+  for (int l = 0; l < kMaxStages; ++l) {
+    const int ls = min(l, d.n_stages - 1);
+    word[l] = reinterpret_cast<const uint32_t*>(sp(d, d.off_codes, d.stage_codes, ls))[row * d.words + k0 / per];
+    sc[l] = reinterpret_cast<const uint16_t*>(sp(d, d.off_scales, d.stage_scales, ls))[row * d.groups + k0 / d.group];
+    const uint16_t* crow = reinterpret_cast<const uint16_t*>(sp(d, d.off_centroids, d.stage_centroids, ls)) +
+                           ((int64_t)h * d.C + min(lab[l], d.C - 1)) * kHeadDim + k0;
+    if constexpr (NCH == 8) {
+      const uint4 c = *reinterpret_cast<const uint4*>(crow);
+      cw[l][0] = c.x; cw[l][1] = c.y; cw[l][2] = c.z; cw[l][3] = c.w;
+    } else {
+      const uint2 c = *reinterpret_cast<const uint2*>(crow);
+      cw[l][0] = c.x; cw[l][1] = c.y;
+    }
+  }
+  const int sh0 = d.bits * (k0 % per);
+  const uint32_t mask = (1u << d.bits) - 1u;
+  const int off = 1 << (d.bits - 1);
+#pragma unroll
+  for (int l = 0; l < kMaxStages; ++l) {
+    if (l < d.n_stages) {
+      const float S = bf16_bits_to_f32(sc[l]);
+#pragma unroll
+      for (int e = 0; e < NCH; ++e) {
+        const float q = (float)((int)((word[l] >> (sh0 + d.bits * e)) & mask) - off);
+        const float yhat = __fadd_rn(S * q, bf16_bits_to_f32((cw[l][e >> 1] >> (16 * (e & 1))) & 0xFFFFu));
+        v[e] = l == 0 ? yhat : __fadd_rn(v[e], yhat);
+      }
+    }
+  }
+}
+
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
@@ -454,7 +502,8 @@ __global__ __launch_bounds__(kThreads) void k_attend(AttendArgs a) {
         decode_pairs_f16<4>(code16 | (code16 << 14), bf16_bits_to_f32(sb), cw, o4);
       } else {
         float v[8];
-        if (ok) decode_generic<8>(geom(tiles[j].chunk, false), sTabK, h, tiles[j].token0 + key, k0, v);
+        if (ok && a.kp.n_int4 == 0) decode_uniform<8>(geom(tiles[j].chunk, false), h, tiles[j].token0 + key, k0, v);
+        else if (ok) decode_generic<8>(geom(tiles[j].chunk, false), sTabK, h, tiles[j].token0 + key, k0, v);
         else {
 #pragma unroll
           for (int e = 0; e < 8; ++e) v[e] = 0.0f;
@@ -482,7 +531,8 @@ __global__ __launch_bounds__(kThreads) void k_attend(AttendArgs a) {
           decode_pairs_f16<2>(code8 | (code8 << 14), bf16_bits_to_f32(sb), cw, pr[y]);
         } else {
           float v[4];
-          if (ok) decode_generic<4>(geom(tiles[j].chunk, true), sTabV, h, tiles[j].token0 + key, k0, v);
+          if (ok && a.vp.n_int4 == 0) decode_uniform<4>(geom(tiles[j].chunk, true), h, tiles[j].token0 + key, k0, v);
+          else if (ok) decode_generic<4>(geom(tiles[j].chunk, true), sTabV, h, tiles[j].token0 + key, k0, v);
           else {
 #pragma unroll
             for (int e = 0; e < 4; ++e) v[e] = 0.0f;
