@@ -78,7 +78,10 @@ def objective(dist: np.ndarray, labels: np.ndarray) -> float:
 
 
 def relative_gap(dist: np.ndarray, labels: np.ndarray, y, c, w=None) -> np.ndarray:
-    """(second-smallest D - smallest D) / (||y_i||^2_w + ||c_label||^2_w), float64."""
+    """(second-smallest D - smallest D) / (||y_i||^2_w + ||c_label||^2_w), float64.
+    With a single centroid there is no second candidate: the gap is +inf."""
+    if dist.shape[1] < 2:
+        return np.full(dist.shape[0], np.inf)
     y64 = np.asarray(y, dtype=np.float32).astype(np.float64)
     c64 = np.asarray(c, dtype=np.float32).astype(np.float64)
     w64 = np.ones(y64.shape[1]) if w is None else np.asarray(w, np.float32).astype(np.float64)

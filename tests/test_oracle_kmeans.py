@@ -113,3 +113,16 @@ def test_relative_gap_definition():
     gap = km.relative_gap(dist, labels, y, c)
     # (4 - 1) / (||y||^2 + ||c_0||^2) = 3 / (25 + 18)
     assert gap[0] == pytest.approx(3.0 / 43.0, rel=1e-15)
+
+
+def test_single_cluster_is_the_exact_mean():
+    """C = 1: every token joins the one cluster, no near-tie exists (gap +inf), and
+    the centroid is the exactly rounded mean of all tokens (math.fsum per channel)."""
+    import math
+    rng = np.random.default_rng(4)
+    y = (rng.normal(size=(37, 6)) * rng.choice([1.0, 1e3], size=(37, 1))).astype(np.float32)
+    tr = km.kmeans(y, 1, 10)
+    assert np.all(tr.labels == 0)
+    assert all(np.all(np.isinf(g)) for g in tr.gaps_iter)
+    mean = np.array([math.fsum(float(v) for v in y[:, k]) / 37 for k in range(6)], np.float64).astype(np.float32)
+    assert np.array_equal(tr.centroids[0].view(np.uint32), mean.view(np.uint32))
