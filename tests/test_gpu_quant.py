@@ -298,6 +298,43 @@ def test_quantize_chunk_free_running(case):
     G.log(f"free-running {name}: bit-exact; near-ties in oracle trace {near}; rel-L2(x_hat, x) = {err:.4g}")
 
 
+# (case id, tokens, clusters, bits, group, dtype, stages, input kind)
+DEGENERATE = [
+    ("all-zero", 300, 16, 2, 32, "bf16", 1, "zero"),
+    ("one-cluster", 300, 1, 2, 32, "bf16", 1, "normal"),
+    ("tokens-equal-clusters", 64, 64, 2, 32, "bf16", 1, "normal"),
+    ("identical-rows-f32-int4-2-stages", 200, 8, 4, 16, "f32", 2, "constant"),
+]
+
+
+@pytest.mark.parametrize("case", DEGENERATE, ids=[c[0] for c in DEGENERATE])
+def test_quantize_degenerate_chunks(case):
+    """Degenerate chunks: all-zero data (every scale 0, every distance tied),
+    a single cluster, as many tokens as clusters, and identical rows through two
+    stages; the packed chunk and its dequantization match the oracle bit for bit."""
+    name, n, C, bits, group, dtype, stages, kind = case
+    H = 2
+    rng = np.random.default_rng(31)
+    if kind == "zero":
+        x = np.zeros((n, H, 128), np.float32)
+    elif kind == "constant":
+        x = np.ascontiguousarray(np.broadcast_to(bf16_rne(rng.normal(size=(1, H, 128))), (n, H, 128)), np.float32)
+    else:
+        x = bf16_rne(rng.normal(size=(n, H, 128)) * rng.choice([1.0, 30.0], size=(n, H, 1)))
+    cfg = qk.Config(n_heads=H, n_clusters=C, bits=bits, group=group, n_stages=stages, kmeans_iters=10)
+    G.log(f"degenerate {name}: N={n} C={C} bits={bits} group={group} {dtype} stages={stages}")
+    t = G.torch()
+    packed = G.quantize(cfg, G.to_dev(x, dtype))
+    jobs = [(x[:, h], dict(n_clusters=C, bits=bits, group=group, n_stages=stages, iters=10)) for h in range(H)]
+    res = dict(enumerate(G.oracle_problems(jobs)))
+    compare_chunk(name, None, "K", x, packed, cfg, res, range(H))
+    out = t.empty((n, H, 128), dtype=t.float32, device=G.dev())
+    qk.qkv_dequantize(cfg, n, packed, out)
+    o = out.cpu().numpy()
+    for h in range(H):
+        assert np.array_equal(o[:, h].view(np.uint32), res[h].x_hat.view(np.uint32)), f"{name} h{h}: x_hat"
+
+
 def test_full_chunk_bench_shape_sampled_heads():
     """The bench workload's chunk (32 heads x 6,240 tokens, C = 256, INT2, g = 32)
     in the bench's launch configuration; the oracle recomputes sampled heads."""
