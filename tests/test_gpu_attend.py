@@ -17,7 +17,7 @@ LOGIT_TOL = 1e-3
 OUT_TOL = 5e-3
 
 
-def _run(name, wl, chunk_bounds, nq, heads_checked, causal=False, logit_queries=64):
+def _run(name, wl, chunk_bounds, nq, heads_checked, causal=False, logit_queries=64, q_scale=1.0):
     t = G.torch()
     H = wl.n_heads
     kcfg, vcfg = G.config_of(wl, "K"), G.config_of(wl, "V")
@@ -47,7 +47,7 @@ def _run(name, wl, chunk_bounds, nq, heads_checked, causal=False, logit_queries=
         kch.append(G.quantize(kcfg, G.to_dev(k, wl.dtype), w=wd, perm=pd, u=ud, ws=ws))
         vch.append(G.quantize(vcfg, G.to_dev(v, wl.dtype), ws=wsv))
         ntok.append(b - a)
-    q = synth.queries(wl, n=nq)
+    q = synth.queries(wl, n=nq) * np.float32(q_scale)     # a power of two keeps bf16 queries exact
     qd = G.to_dev(q, wl.dtype)
     out = t.empty((nq, H, 128), dtype=t.float32, device=G.dev())
     G.log(f"attend {name}: H={H} chunks={len(ntok)} Nk={sum(ntok)} Nq={nq} causal={causal} psac={kcfg.psac_rank}")
@@ -117,6 +117,24 @@ def test_quantwm_psac():
 def test_mixed_precision_keys():
     wl = synth.workload(5, n_heads=2, n_clusters=64)
     _run("mixed", wl, [(0, 1100), (1100, 2000)], 150, [0])
+
+
+def test_single_query():
+    wl = synth.workload(2, n_heads=2, n_clusters=16)
+    _run("single-query", wl, [(0, 300), (300, 364)], 1, [0, 1], logit_queries=1)
+
+
+def test_partial_wave_one_tile_cache():
+    """33 queries (one full wave of 32 and one query more) over a cache of exactly one 64-key tile."""
+    wl = synth.workload(2, n_heads=2, n_clusters=16)
+    _run("partial-wave", wl, [(0, 64)], 33, [1], logit_queries=33)
+
+
+def test_large_logits_rescaling():
+    """Queries scaled by 32: logits in the thousands, near one-hot softmax rows, so the
+    running maximum keeps growing across tiles (the online rescaling path)."""
+    wl = synth.workload(2, n_heads=2, n_clusters=32)
+    _run("large-logits", wl, [(0, 700), (700, 1500)], 100, [0, 1], q_scale=32.0)
 
 
 def test_bench_shape_sampled_head():
