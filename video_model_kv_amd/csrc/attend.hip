@@ -199,6 +199,14 @@ __device__ __forceinline__ void decode_pairs_f16(uint32_t t, float S, const uint
   }
 }
 
+// max(x, x of lane ^ 32): v_permlane32_swap exchanges the two 32-lane halves
+// of its operands in registers (no LDS round trip); whichever of its two
+// results holds the other half's value, the three-way max takes it.
+__device__ __forceinline__ float max_with_other_half(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(x, fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1])));
+}
+
 // Asynchronous global -> LDS copy: every active lane moves BYTES bytes from its
 // own address to dst + lane * BYTES (dst is wave-uniform).  Tracked by vmcnt.
 template <int BYTES>
@@ -571,17 +579,31 @@ __global__ __launch_bounds__(kThreads) void k_attend(AttendArgs a) {
     const bool need_mask = nvalid < kKTile || (a.causal && kstart + kKTile - 1 > wq_first);
     // S^T = K_hat Q^T, both 32-key halves interleaved (fp16 operands, fp32 accumulation)
     f32x16 acc[2] = {f32x16{}, f32x16{}};
+    // K fragments of step s + 1 are read from LDS while step s multiplies
+    auto kfrag = [&](int s, int kb) __attribute__((always_inline)) {
+      return __builtin_bit_cast(f16x8, *reinterpret_cast<const uint4*>(&sK[b][kb * 32 + col][s * 16 + half * 8]));
+    };
+    f16x8 knext[2] = {kfrag(0, 0), kfrag(0, 1)};
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
-      f16x8 kf[2];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-        kf[kb] = __builtin_bit_cast(f16x8, *reinterpret_cast<const uint4*>(&sK[b][kb * 32 + col][s * 16 + half * 8]));
+      const f16x8 kf[2] = {knext[0], knext[1]};
+      if (s + 1 < 8) {
+        knext[0] = kfrag(s + 1, 0);
+        knext[1] = kfrag(s + 1, 1);
+      }
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         acc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf[kb], qh[s], acc[kb], 0, 0, 0);
         if constexpr (QF32) acc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf[kb], ql[QF32 ? s : 0], acc[kb], 0, 0, 0);
       }
+    }
+    // instruction order of the loop above: the first step's two LDS reads, then
+    // per step the next step's two reads ahead of this step's MFMAs
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      if (s + 1 < 8) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, QF32 ? 4 : 2, 0);
     }
     if constexpr (PSAC) {
 #pragma unroll
@@ -618,7 +640,7 @@ __global__ __launch_bounds__(kThreads) void k_attend(AttendArgs a) {
     float mloc = sv[0];
 #pragma unroll
     for (int i = 1; i < 32; ++i) mloc = fmaxf(mloc, sv[i]);
-    mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
+    mloc = max_with_other_half(mloc);
     const float m_cand = mloc * c2;                             // c2 > 0
     // lazy rescaling: keep the running max unless it grows by more than 8 (p <= 2^8)
     const bool grow = m_cand > m_run + 8.0f;
