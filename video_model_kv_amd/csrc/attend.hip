@@ -7,19 +7,21 @@
 // the key error on the query principal subspace U are added back to the logits,
 // s += (q U) . coef).
 //
-// Work decomposition: one workgroup (4 waves, 256 threads) per (head, key
-// split, 128-query tile).  A key split is a contiguous run of 64-key tiles of
+// Work decomposition: one workgroup (8 waves, 512 threads) per (head, key
+// split, 256-query tile).  A key split is a contiguous run of 64-key tiles of
 // the concatenated chunks (a tile never straddles two chunks).  Per key tile the
-// workgroup decodes K_hat and V_hat into LDS once for its 128 queries, then each
-// wave (32 queries) computes S^T = K_hat Q^T and O^T += V_hat^T P^T on MFMA
-// (v_mfma_f32_32x32x16_bf16) with an online softmax in the exp2 domain.
+// workgroup decodes K_hat and V_hat^T into LDS once for its 256 queries, then
+// each wave (32 queries) computes S^T = K_hat Q^T and O^T += V_hat^T P^T on
+// MFMA (v_mfma_f32_32x32x16_f16) with an online softmax in the exp2 domain.
 //
-// Numerics: K_hat is formed in fp32 (exactly S q + C summed over stages in
-// order) and split into bf16 hi + lo, both multiplied against the bf16 queries
-// (fp32 queries are split too), so logits carry ~2^-17 relative operand error;
-// V_hat and the probabilities enter P V in bf16 with fp32 accumulation.  The
-// PSAC term rides one extra MFMA k-step: [coef | coef] against
-// [hi(qU) | lo(qU)].  Splits are merged with the usual log-sum-exp rescaling.
+// Numerics: K_hat and V_hat enter the MFMAs as fp16 (S q + C evaluated by
+// packed fp16 FMA on the fast paths, in fp32 and rounded once on the generic
+// ones; saturated to +-65504).  bf16 queries convert to fp16 exactly between
+// 2^-14 and 65504 in magnitude (rounded below); fp32 queries are split into fp16 hi + lo (two MFMA passes).
+// Probabilities are rounded to fp16 for P V (fp32 accumulation) and the row
+// sums use the same rounded values.  The PSAC term rides one extra MFMA
+// k-step: [coef | coef] against [hi(qU) | lo(qU)].  Splits are merged with the
+// usual log-sum-exp rescaling.
 #include <algorithm>
 #include <cstddef>
 #include <utility>
