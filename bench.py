@@ -113,7 +113,7 @@ print(json.dumps(dict(tq=tq / 2, ta=ta, n=x.shape[0])))
 def main():
     a = parse()
     if a.gpus != 1:
-        print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus {a.gpus}).",
+        print(f"bench.py measures one GPU only: the library has no multi-GPU path (asked for --gpus {a.gpus}).",
               file=sys.stderr)
         sys.exit(2)
     import numpy as np

@@ -58,7 +58,7 @@ typedef enum { QKV_F32 = 0, QKV_BF16 = 1 } qkv_dtype;
 
 /*
  * Quantizer configuration of one tensor (K or V) of one layer.
- *   head_dim         d; must be 128 in this build.
+ *   head_dim         d; must be 128 (the only head size supported).
  *   n_heads          H >= 1.
  *   n_clusters       C in [1, 256]: k-means groups per (chunk, head, stage)
  *                    ([QVG] "Semantic-Aware Smoothing").  Needs n_tokens >= C.

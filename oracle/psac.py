@@ -8,7 +8,7 @@ channel-sensitivity ranking (oracle; test infrastructure only).
   queries' second-moment matrix M = sum_n q_n q_n^T, keep the r eigenvectors of
   the largest eigenvalues as U (d x r); energy = sum of those r eigenvalues over
   the trace.  The key residual error e is projected onto U and the r
-  coefficients are stored (bf16 in this build; the page says only that they are
+  coefficients are stored (bf16 here; the page says only that they are
   stored quantized); attention adds (q U) . coef back to the logit.
 * Sensitivity ranking for mixed precision (2-bit trap explainer, section five;
   practitioner blog, section 3.2): the channels with the largest query energy

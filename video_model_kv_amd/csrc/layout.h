@@ -8,7 +8,7 @@
 
 namespace qkv {
 
-constexpr int kHeadDim = 128;      // the only head size this build supports
+constexpr int kHeadDim = 128;      // the only head size the library supports
 constexpr int kMaxClusters = 256;
 constexpr int kMaxStages = 4;
 constexpr int kMaxRank = 8;

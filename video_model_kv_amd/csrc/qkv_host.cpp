@@ -61,7 +61,7 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 int check_config(const qkv_config* c, const char* what) {
   if (!c) return fail(QKV_EINVAL, "%s: config is NULL", what);
   if (c->head_dim != kHeadDim)
-    return fail(QKV_EUNSUPPORTED, "%s: head_dim %d (this build supports 128)", what, c->head_dim);
+    return fail(QKV_EUNSUPPORTED, "%s: head_dim %d (the library supports 128)", what, c->head_dim);
   if (c->n_heads < 1 || c->n_heads > 1024) return fail(QKV_EINVAL, "%s: n_heads %d not in [1, 1024]", what, c->n_heads);
   if (c->n_clusters < 1 || c->n_clusters > kMaxClusters)
     return fail(QKV_EINVAL, "%s: n_clusters %d not in [1, 256]", what, c->n_clusters);
