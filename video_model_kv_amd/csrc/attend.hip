@@ -14,9 +14,9 @@
 // each wave (32 queries) computes S^T = K_hat Q^T and O^T += V_hat^T P^T on
 // MFMA (v_mfma_f32_32x32x16_f16) with an online softmax in the exp2 domain.
 //
-// Numerics: K_hat and V_hat enter the MFMAs as fp16 (S q + C evaluated by
-// packed fp16 FMA on the fast paths, in fp32 and rounded once on the generic
-// ones; saturated to +-65504).  bf16 queries convert to fp16 exactly between
+// Numerics: K_hat and V_hat enter the MFMAs as fp16 (S q + C evaluated by one
+// packed fp16 FMA on the fast paths, on operands bounded so that it stays
+// finite; in fp32, rounded once and saturated to +-65504 on the generic ones).  bf16 queries convert to fp16 exactly between
 // 2^-14 and 65504 in magnitude (rounded below); fp32 queries are split into fp16 hi + lo (two MFMA passes).
 // Probabilities are rounded to fp16 for P V (fp32 accumulation) and the row
 // sums use the same rounded values.  The PSAC term rides one extra MFMA
@@ -155,6 +155,10 @@ constexpr int kItems = 1024 / kThreads;   // K (and V) decode items per thread p
 constexpr int kRing = 3;                  // raw-tile slots in LDS
 constexpr int kMetaSlots = 6;             // tile-record slots in LDS
 constexpr float kF16Max = 65504.0f;
+// bounds of the fast decode's operands: 2 * kScaleF16Max + kCentF16Max = 65456,
+// so S q + c (|q| <= 2) is finite and exact up to one fp16 rounding
+constexpr float kScaleF16Max = 16352.0f;
+constexpr float kCentF16Max = 32752.0f;
 static_assert(kBM == kAttendQueries, "queries per workgroup");
 
 // two fp32 values -> packed fp16 (round to nearest even), saturated to the fp16 range
@@ -172,32 +176,19 @@ __device__ __forceinline__ f16x2 codes_to_f16x2(uint32_t x) {
   const f16x2 off = {(_Float16)1026.0f, (_Float16)1026.0f};
   return biased - off;
 }
-// bf16 pair (lo, hi halves of w) -> fp16 pair (round to nearest even; beyond
-// the fp16 range -> +-inf, clamped by the caller)
-__device__ __forceinline__ f16x2 bf16x2_to_f16x2(uint32_t w) {
-  f16x2 r;
-  r[0] = (_Float16)__uint_as_float(w << 16);
-  r[1] = (_Float16)__uint_as_float(w & 0xFFFF0000u);
-  return r;
-}
-__device__ __forceinline__ uint32_t f16x2_sat(f16x2 v) {
-  const f16x2 lim = {(_Float16)65504.0f, (_Float16)65504.0f};
-  v = __builtin_elementwise_min(v, lim);
-  v = __builtin_elementwise_max(v, -lim);
-  return __builtin_bit_cast(uint32_t, v);
-}
-// S * q + c as saturated fp16 pairs for NP consecutive channel pairs: code
-// pair j of `t` sits at bits [4j, 4j+1] and [4j+16, 4j+17] (t = codes | codes << 14);
-// cw holds the centroid pairs already in fp16 (the per-call fp16 copy of the
-// chunk's bf16 table).
+// S * q + c as fp16 pairs for NP consecutive channel pairs: code pair j of `t`
+// sits at bits [4j, 4j+1] and [4j+16, 4j+17] (t = codes | codes << 14); cw holds
+// the centroid pairs already in fp16 (the per-call fp16 copy of the chunk's
+// bf16 table, bounded by kCentF16Max).  With |q| <= 2 and S bounded by
+// kScaleF16Max, |S q + c| <= 65456 needs no clamp per element.
 template <int NP>
 __device__ __forceinline__ void decode_pairs_f16(uint32_t t, float S, const uint32_t* cw, uint32_t* out) {
-  const _Float16 sh = (_Float16)__builtin_amdgcn_fmed3f(S, -kF16Max, kF16Max);
+  const _Float16 sh = (_Float16)__builtin_amdgcn_fmed3f(S, -kScaleF16Max, kScaleF16Max);
   const f16x2 s2 = {sh, sh};
 #pragma unroll
   for (int j = 0; j < NP; ++j) {
     const f16x2 q = codes_to_f16x2((t >> (4 * j)) & 0x00030003u);
-    out[j] = f16x2_sat(__builtin_elementwise_fma(s2, q, __builtin_bit_cast(f16x2, cw[j])));
+    out[j] = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(s2, q, __builtin_bit_cast(f16x2, cw[j])));
   }
 }
 
@@ -505,8 +496,9 @@ __global__ __launch_bounds__(kThreads) void k_attend(AttendArgs a) {
         const uint32_t w = sRc[r][0][key * 8 + (k0 >> 4)];
         const uint32_t sb = sRs[r][0][klead + (key << kGs) + ((k0 << kGs) >> 7)];   // groups: powers of two
         const uint4 cr = *reinterpret_cast<const uint4*>(&sCentK[g][key * kHeadDim + k0]);
-        // keys past nvalid decode stale LDS contents: the saturation keeps
-        // them finite, and their scores are masked (probability 0)
+        // keys past nvalid decode stale LDS contents (zero at the start,
+        // then earlier tiles' values): finite, and their scores are masked
+        // (probability 0)
         const uint32_t code16 = (w >> (16 * ((k0 >> 3) & 1))) & 0xFFFFu;
         const uint32_t cw[4] = {cr.x, cr.y, cr.z, cr.w};
         decode_pairs_f16<4>(code16 | (code16 << 14), bf16_bits_to_f32(sb), cw, o4);
@@ -702,6 +694,20 @@ __global__ __launch_bounds__(kThreads) void k_attend(AttendArgs a) {
   };
 
   // ---- prologue: tiles t_begin .. t_begin+2 raw, t_begin .. t_begin+1 gathered, t_begin decoded ----
+  if constexpr (KFAST || VFAST) {
+    // The fast decode reads the staging slots for every key of a tile, also
+    // past its end, where no copy lands: zeroed here, they only ever hold
+    // finite values (zeros or earlier tiles' scales and centroid rows), and
+    // the barrier below orders these writes before the first copies.
+    uint4* ck = reinterpret_cast<uint4*>(&sCentK[0][0]);
+    uint4* cv = reinterpret_cast<uint4*>(&sCentV[0][0]);
+    for (int i = tid; i < (int)(sizeof(sCentK) / 16); i += kThreads) {
+      ck[i] = make_uint4(0u, 0u, 0u, 0u);
+      cv[i] = make_uint4(0u, 0u, 0u, 0u);
+    }
+    uint32_t* rs = reinterpret_cast<uint32_t*>(&sRs[0][0][0]);
+    for (int i = tid; i < (int)(sizeof(sRs) / 4); i += kThreads) rs[i] = 0u;
+  }
   const int r0 = t_begin % kRing;
   if (xwave == 0) {
 #pragma unroll 1
@@ -931,7 +937,12 @@ __global__ __launch_bounds__(256) void k_centroids_f16(const ChunkRec* __restric
   const uint32_t w4[4] = {w.x, w.y, w.z, w.w};
   uint32_t o4[4];
 #pragma unroll
-  for (int k = 0; k < 4; ++k) o4[k] = __builtin_bit_cast(uint32_t, bf16x2_to_f16x2(w4[k]));
+  for (int k = 0; k < 4; ++k) {
+    f16x2 r;
+    r[0] = (_Float16)__builtin_amdgcn_fmed3f(__uint_as_float(w4[k] << 16), -kCentF16Max, kCentF16Max);
+    r[1] = (_Float16)__builtin_amdgcn_fmed3f(__uint_as_float(w4[k] & 0xFFFF0000u), -kCentF16Max, kCentF16Max);
+    o4[k] = __builtin_bit_cast(uint32_t, r);
+  }
   *reinterpret_cast<uint4*>(dst + chunk * per_chunk * 8 + e) = make_uint4(o4[0], o4[1], o4[2], o4[3]);
 }
 
