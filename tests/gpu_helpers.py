@@ -15,6 +15,10 @@ import numpy as np
 
 import video_model_kv_amd as qk
 from video_model_kv_amd import packed as pk
+from oracle import quant as oq
+
+
+NEAR_TIE = 1e-5
 
 
 def log(msg: str):
@@ -150,6 +154,34 @@ def generated_chunks(cid: int, n_chunks: int, keep):
             if (c + 1) % 8 == 0:
                 log(f"generated {c + 1} / {n_chunks} chunks")
             yield c, out
+
+
+def compare_chunk(name, wl, tensor, x, packed, cfg, res_by_head, heads):
+    """Packed chunk on the device against the oracle's results, bit for bit:
+    labels, bf16 centroids, codes and scales of every stage for each listed
+    head; PSAC coefficients within one bf16 ulp on fewer than 0.1 % of them
+    (the float64 dot products of the two sides differ in summation order).
+    Returns the number of near-ties (gap < 1e-5) in the oracle's traces."""
+    v = host_views(packed, cfg, x.shape[0])
+    near = 0
+    for h in heads:
+        res = res_by_head[h]
+        for l, st in enumerate(res.stages):
+            if st.trace is not None:
+                near += int(sum((g < NEAR_TIE).sum() for g in st.trace.gaps_iter))
+            assert np.array_equal(v["labels"][l, h], st.labels.astype(np.uint8)), f"{name} h{h} stage {l}: labels"
+            assert np.array_equal(v["centroids"][l, h].view(np.uint16), f32_bits_to_bf16(st.centroids_bf16)), \
+                f"{name} h{h} stage {l}: centroids"
+            assert np.array_equal(v["codes"][l, h].view(np.uint32), oq.pack_codes(st.q, res.layout)), \
+                f"{name} h{h} stage {l}: codes"
+            assert np.array_equal(v["scales"][l, h].view(np.uint16), f32_bits_to_bf16(st.scales)), \
+                f"{name} h{h} stage {l}: scales"
+        if res.coef is not None:
+            got = v["psac"][h].view(np.uint16)
+            exp = f32_bits_to_bf16(res.coef)
+            diff = np.abs(got.astype(np.int32) - exp.astype(np.int32))
+            assert diff.max() <= 1 and (diff > 0).mean() < 1e-3, f"{name} h{h}: psac coefficients"
+    return near
 
 
 def rel_l2(a, b) -> float:

@@ -70,6 +70,15 @@ def _run(name, wl, chunk_bounds, nq, heads_checked, causal=False, logit_queries=
                     n_int4=cfg.n_int4_channels, perm=None if (perm is None or tensor == "V") else perm[h],
                     u=None if (u is None or tensor == "V") else u[h].astype(np.float64))))
     res = G.oracle_problems(jobs)
+    # the packed caches themselves, bit for bit (labels, centroids, codes, scales, PSAC coefficients)
+    near = 0
+    for ci in range(len(chunk_bounds)):
+        for ti, (tensor, chunks, xs, cfg) in enumerate((("K", kch, xk, kcfg), ("V", vch, xv, vcfg))):
+            by_head = {h: res[(ci * len(heads_checked) + hi) * 2 + ti] for hi, h in enumerate(heads_checked)}
+            near += G.compare_chunk(f"{name} chunk {ci} {tensor}", wl, tensor, xs[ci], chunks[ci], cfg, by_head,
+                                    heads_checked)
+    G.log(f"attend {name}: packed K/V bit-exact on heads {list(heads_checked)} of {len(chunk_bounds)} chunks "
+          f"(near-ties in the oracle's traces: {near})")
     lg = logits[:, :nlq].cpu().numpy()
     for hi, h in enumerate(heads_checked):
         k_hat = np.concatenate([res[(ci * len(heads_checked) + hi) * 2].x_hat for ci in range(len(chunk_bounds))])
@@ -119,6 +128,19 @@ def test_mixed_precision_keys():
     _run("mixed", wl, [(0, 1100), (1100, 2000)], 150, [0])
 
 
+def test_int4_uniform_cache():
+    """Uniform INT4 keys and values (one stage, groups of 32), two ragged chunks."""
+    wl = synth.workload(2, n_heads=2, n_clusters=64, bits=4)
+    _run("int4", wl, [(0, 1000), (1000, 1800)], 200, [0, 1])
+
+
+def test_int4_two_stage_cache():
+    """Uniform INT4 keys and values with two progressive stages (the multi-stage
+    INT4 variant of the QVG notes' main table)."""
+    wl = synth.workload(3, n_heads=2, n_clusters=32, bits=4, n_stages=2)
+    _run("int4-2stage", wl, [(0, 900), (900, 1500)], 130, [1])
+
+
 def test_single_query():
     wl = synth.workload(2, n_heads=2, n_clusters=16)
     _run("single-query", wl, [(0, 300), (300, 364)], 1, [0, 1], logit_queries=1)
@@ -138,39 +160,42 @@ def test_large_logits_rescaling():
 
 
 def test_bench_shape_sampled_head():
-    """The bench workload: 32 heads, 6 chunks of 6,240 tokens, 1,560 queries,
-    in the bench's launch configuration; oracle on one sampled head."""
+    """The 5 s cache: 32 heads, 6 chunks of 6,240 tokens, 1,560 queries; the
+    oracle quantizes two sampled heads of every chunk (packed bytes compared bit
+    for bit) and attends over them."""
     wl = synth.workload(2)
     bounds = [wl.chunk_range(c) for c in range(wl.n_chunks)]
-    _run("bench-shape", wl, bounds, wl.n_query, [11], logit_queries=64)
+    _run("bench-shape", wl, bounds, wl.n_query, [11, 27], logit_queries=64)
 
 
 def test_progressive_full_cache_sampled_head():
     """Three progressive stages at full shape: 32 heads, 6 chunks of 6,240 tokens,
     C = 256, INT2 g = 32 per stage, 1,560 queries over the whole cache; the oracle
-    quantizes one sampled head of every chunk (three stages each) and attends."""
+    quantizes two sampled heads of every chunk (three stages each; packed bytes of
+    every stage compared bit for bit) and attends."""
     wl = synth.workload(3)
     bounds = [wl.chunk_range(c) for c in range(wl.n_chunks)]
-    _run("progressive-full", wl, bounds, wl.n_query, [9], logit_queries=64)
+    _run("progressive-full", wl, bounds, wl.n_query, [9, 22], logit_queries=64)
 
 
 def test_quantwm_full_cache_sampled_head():
     """QSAC-weighted k-means and rank-8 PSAC on the keys at full shape (32 heads,
-    6 chunks of 6,240 tokens, C = 256); oracle on one sampled head."""
+    6 chunks of 6,240 tokens, C = 256); the oracle quantizes two sampled heads
+    (packed bytes and PSAC coefficients compared) and attends."""
     wl = synth.workload(4)
     bounds = [wl.chunk_range(c) for c in range(wl.n_chunks)]
-    _run("quantwm-full", wl, bounds, wl.n_query, [13], logit_queries=64)
+    _run("quantwm-full", wl, bounds, wl.n_query, [13, 29], logit_queries=64)
 
 
 def test_long_horizon_full_cache_sampled_queries():
     """The one-minute cache at full size: 72 chunks of 6,240 tokens (449,280 keys),
     32 heads, keys mixed INT4 on the 26 most query-sensitive channels / INT2 on the
     rest, values INT2, C = 256; 1,560 queries attend over the whole packed cache.
-    The oracle quantizes head 0 of every chunk itself and attends 65 sampled
-    queries (every 24th) in float64; logits of the first 64 queries are checked
-    through the debug path."""
+    The oracle quantizes heads 0 and 23 of every chunk itself (the packed bytes of
+    both are compared bit for bit) and attends 65 sampled queries (every 24th) in
+    float64; logits of the first 64 queries are checked through the debug path."""
     wl = synth.workload(5)
-    H, h, n = wl.n_heads, 0, wl.n_chunks
+    H, heads, n = wl.n_heads, [0, 23], wl.n_chunks
     t = G.torch()
     kcfg, vcfg = G.config_of(wl, "K"), G.config_of(wl, "V")
     hist = synth.history_queries(wl)
@@ -181,7 +206,7 @@ def test_long_horizon_full_cache_sampled_queries():
     wsv = G.workspace(vcfg, max(ntok))
     kch, vch, xk0, xv0 = [None] * n, [None] * n, [None] * n, [None] * n
     G.log(f"long-horizon: generating and quantizing {n} chunks x 2 tensors")
-    for c, out in G.generated_chunks(5, n, [h]):
+    for c, out in G.generated_chunks(5, n, heads):
         (kb, xk0[c]), (vb, xv0[c]) = out["K"], out["V"]
         kd = t.from_numpy(kb.view(np.int16)).to(G.dev()).view(t.bfloat16)
         vd = t.from_numpy(vb.view(np.int16)).to(G.dev()).view(t.bfloat16)
@@ -197,23 +222,36 @@ def test_long_horizon_full_cache_sampled_queries():
     logits = t.empty((H, nl, sum(ntok)), dtype=t.float32, device=G.dev())
     out_l = t.empty((nl, H, 128), dtype=t.float32, device=G.dev())
     qk.qkv_attend(kcfg, vcfg, qd[:nl].contiguous(), kch, vch, ntok, out_l, ws, logits=logits)
-    o = out.cpu().numpy()[:, h]
-    lg = logits[h].cpu().numpy()
+    o_all = out.cpu().numpy()
+    lg_all = {h: logits[h].cpu().numpy() for h in heads}
     del logits
-    G.log(f"long-horizon: oracle on head {h} ({2 * n} problems)")
+    G.log(f"long-horizon: oracle on heads {heads} ({2 * n * len(heads)} problems)")
     jobs = []
     for c in range(n):
-        jobs.append((xk0[c][:, 0], dict(n_clusters=wl.n_clusters, bits=wl.bits, group=wl.group, iters=wl.kmeans_iters,
-                                        n_int4=kcfg.n_int4_channels, perm=perm[h])))
-        jobs.append((xv0[c][:, 0], dict(n_clusters=wl.n_clusters, bits=wl.bits, group=wl.group, iters=wl.kmeans_iters)))
+        for hi, h in enumerate(heads):
+            jobs.append((xk0[c][:, hi], dict(n_clusters=wl.n_clusters, bits=wl.bits, group=wl.group,
+                                             iters=wl.kmeans_iters, n_int4=kcfg.n_int4_channels, perm=perm[h])))
+            jobs.append((xv0[c][:, hi], dict(n_clusters=wl.n_clusters, bits=wl.bits, group=wl.group,
+                                             iters=wl.kmeans_iters)))
     res = G.oracle_problems(jobs)
-    k_hat = np.concatenate([res[2 * c].x_hat for c in range(n)])
-    v_hat = np.concatenate([res[2 * c + 1].x_hat for c in range(n)])
+
+    def job(c, hi, ti):
+        return res[(c * len(heads) + hi) * 2 + ti]
+
+    near = 0
+    for c in range(n):
+        for ti, (tensor, chunks, cfg) in enumerate((("K", kch, kcfg), ("V", vch, vcfg))):
+            near += G.compare_chunk(f"long-horizon chunk {c} {tensor}", wl, tensor, xk0[c], chunks[c], cfg,
+                                    {h: job(c, hi, ti) for hi, h in enumerate(heads)}, heads)
+    G.log(f"long-horizon: packed K/V bit-exact on heads {heads} of all {n} chunks (near-ties {near})")
     sample = np.arange(0, wl.n_query, 24)
-    ref = oa.attend_head(q[sample, h], k_hat, v_hat)
-    e_out = G.rel_l2(o[sample], ref)
-    e_log = G.rel_l2(lg, oa.logits(q[:nl, h], k_hat))
-    G.log(f"long-horizon h{h}: rel-L2 logits {e_log:.3g} (tol {LOGIT_TOL}), out {e_out:.3g} (tol {OUT_TOL}) "
-          f"on {len(sample)} sampled queries over {k_hat.shape[0]} keys")
-    assert e_log <= LOGIT_TOL, f"long-horizon: logits rel-L2 {e_log}"
-    assert e_out <= OUT_TOL, f"long-horizon: output rel-L2 {e_out}"
+    for hi, h in enumerate(heads):
+        k_hat = np.concatenate([job(c, hi, 0).x_hat for c in range(n)])
+        v_hat = np.concatenate([job(c, hi, 1).x_hat for c in range(n)])
+        ref = oa.attend_head(q[sample, h], k_hat, v_hat)
+        e_out = G.rel_l2(o_all[sample, h], ref)
+        e_log = G.rel_l2(lg_all[h], oa.logits(q[:nl, h], k_hat))
+        G.log(f"long-horizon h{h}: rel-L2 logits {e_log:.3g} (tol {LOGIT_TOL}), out {e_out:.3g} (tol {OUT_TOL}) "
+              f"on {len(sample)} sampled queries over {k_hat.shape[0]} keys")
+        assert e_log <= LOGIT_TOL, f"long-horizon h{h}: logits rel-L2 {e_log}"
+        assert e_out <= OUT_TOL, f"long-horizon h{h}: output rel-L2 {e_out}"

@@ -239,29 +239,6 @@ def _side(wl, tensor):
     return w, u, perm
 
 
-def compare_chunk(name, wl, tensor, x, packed, cfg, res_by_head, heads):
-    v = G.host_views(packed, cfg, x.shape[0])
-    near = 0
-    for h in heads:
-        res = res_by_head[h]
-        for l, st in enumerate(res.stages):
-            if st.trace is not None:
-                near += int(sum((g < NEAR_TIE).sum() for g in st.trace.gaps_iter))
-            assert np.array_equal(v["labels"][l, h], st.labels.astype(np.uint8)), f"{name} h{h} stage {l}: labels"
-            assert np.array_equal(v["centroids"][l, h].view(np.uint16), G.f32_bits_to_bf16(st.centroids_bf16)), \
-                f"{name} h{h} stage {l}: centroids"
-            assert np.array_equal(v["codes"][l, h].view(np.uint32), oq.pack_codes(st.q, res.layout)), \
-                f"{name} h{h} stage {l}: codes"
-            assert np.array_equal(v["scales"][l, h].view(np.uint16), G.f32_bits_to_bf16(st.scales)), \
-                f"{name} h{h} stage {l}: scales"
-        if res.coef is not None:
-            got = v["psac"][h].view(np.uint16)
-            exp = G.f32_bits_to_bf16(res.coef)
-            diff = np.abs(got.astype(np.int32) - exp.astype(np.int32))
-            assert diff.max() <= 1 and (diff > 0).mean() < 1e-3, f"{name} h{h}: psac coefficients"
-    return near
-
-
 @pytest.mark.parametrize("case", FREE, ids=[c[0] for c in FREE])
 def test_quantize_chunk_free_running(case):
     name, cid, over, tensor, n, rtn = case
@@ -283,7 +260,7 @@ def test_quantize_chunk_free_running(case):
                            u=None if u is None else u[h].astype(np.float64), rtn=rtn))
             for h in range(wl.n_heads)]
     res = dict(enumerate(G.oracle_problems(jobs)))
-    near = compare_chunk(name, wl, tensor, x, packed, cfg, res, range(wl.n_heads))
+    near = G.compare_chunk(name, wl, tensor, x, packed, cfg, res, range(wl.n_heads))
     # dequantization, f32 and bf16 outputs
     out = t.empty((n, wl.n_heads, 128), dtype=t.float32, device=G.dev())
     qk.qkv_dequantize(cfg, n, packed, out)
@@ -327,7 +304,7 @@ def test_quantize_degenerate_chunks(case):
     packed = G.quantize(cfg, G.to_dev(x, dtype))
     jobs = [(x[:, h], dict(n_clusters=C, bits=bits, group=group, n_stages=stages, iters=10)) for h in range(H)]
     res = dict(enumerate(G.oracle_problems(jobs)))
-    compare_chunk(name, None, "K", x, packed, cfg, res, range(H))
+    G.compare_chunk(name, None, "K", x, packed, cfg, res, range(H))
     out = t.empty((n, H, 128), dtype=t.float32, device=G.dev())
     qk.qkv_dequantize(cfg, n, packed, out)
     o = out.cpu().numpy()
@@ -348,7 +325,7 @@ def test_full_chunk_bench_shape_sampled_heads():
         t.cuda.synchronize()
         jobs = [(x[:, h], dict(n_clusters=wl.n_clusters, bits=2, group=32, iters=10)) for h in heads]
         res = dict(zip(heads, G.oracle_problems(jobs)))
-        near = compare_chunk(f"bench-{tensor}", wl, tensor, x, packed, cfg, res, heads)
+        near = G.compare_chunk(f"bench-{tensor}", wl, tensor, x, packed, cfg, res, heads)
         G.log(f"bench-shape chunk {tensor}: bit-exact on heads {heads}; near-ties {near}")
 
 
@@ -394,6 +371,8 @@ def _batch_vs_single(problems):
         single = G.quantize(cfg, x, w=w, perm=perm, u=u)
         t.cuda.synchronize()
         assert t.equal(packs[i], single), f"problem {i}: batched bytes differ from the single call"
+        del single
+    return packs
 
 
 def test_quantize_batch_mixed_configs_matches_single():
@@ -451,3 +430,29 @@ def test_quantize_batch_all_ties_overflow_list():
         out = t.empty((N, H, 128), dtype=t.bfloat16, device=G.dev())
         qk.qkv_dequantize(cfg, N, packs[p], out)
         assert t.equal(out, xs[p]), f"problem {p}: dequantized chunk differs from the input"
+
+
+def test_quantize_batch_progressive_fp32_stages():
+    """Six problems of the progressive cache (K and V of chunks 0-2: 32 heads x
+    6,240 tokens, C = 256, three stages) in one call: stages 2 and 3 run on the
+    fp32 residuals with the wide update (32 clusters per workgroup, chosen for
+    launches of at least six 32-head problems).  Every batched chunk must equal
+    the single call (narrow update) byte for byte, and two sampled heads match
+    the oracle bit for bit in every stage."""
+    wl = synth.workload(3)
+    probs, xs = [], []
+    for c in range(3):
+        for tensor in ("K", "V"):
+            x = synth.kv_chunk(wl, tensor, c)
+            xs.append((tensor, x))
+            probs.append((G.config_of(wl, tensor), G.to_dev(x, "bf16"), None))
+    G.log(f"progressive batch: {len(probs)} problems of N={wl.chunk_tokens}, H={wl.n_heads}, 3 stages")
+    packs = _batch_vs_single(probs)
+    checks = [(0, 20), (5, 3)]          # (problem, head)
+    jobs = [(xs[p][1][:, h], dict(n_clusters=wl.n_clusters, bits=2, group=32, n_stages=3, iters=10))
+            for p, h in checks]
+    res = G.oracle_problems(jobs)
+    for (p, h), r in zip(checks, res):
+        tensor, x = xs[p]
+        near = G.compare_chunk(f"progressive-batch p{p}", wl, tensor, x, packs[p], probs[p][0], {h: r}, [h])
+        G.log(f"progressive batch: problem {p} ({tensor}) head {h} bit-exact in all 3 stages; near-ties {near}")

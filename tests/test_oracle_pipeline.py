@@ -81,3 +81,56 @@ def test_mixed_precision_groups():
     # int4 channels reconstruct better than int2 channels
     err = np.abs(x - res.x_hat)
     assert err[:, 50:76].mean() < err[:, other].mean()
+
+
+@pytest.fixture(scope="module")
+def two_stage_keys():
+    wl = synth.workload(2, n_heads=1)
+    x = synth.kv_tokens(wl, "K", 0, 700)[:, 0]
+    return x
+
+
+def test_psac_encode_uses_the_residual_after_all_stages(two_stage_keys):
+    """PSAC encode (QuantWM summary, "QuantWM", second technique: the key error
+    left after key quantization is projected on U).  With U = the first r unit
+    vectors, coef[:, b] must be the bf16 rounding of x_b - x_hat_b, x_hat the
+    sum of BOTH stages rebuilt from the stored fields.  The error of stage 1
+    alone, the last stage's input, or the opposite sign all give other values,
+    which the last asserts confirm on this input."""
+    x = two_stage_keys
+    r = 8
+    u = np.eye(128)[:, :r]
+    res = pipeline.quantize_problem(x, 16, 2, 32, n_stages=2, iters=4, u=u)
+    x_hat = pipeline.dequantize_stages(res.stages, res.layout)
+    e = x.astype(np.float64) - x_hat.astype(np.float64)     # exact: both bf16/fp32 grids fit fp64
+    expect = bf16_rne(e[:, :r].astype(np.float32))          # e is fp32-exact here (one fp32 subtraction)
+    assert np.array_equal(e[:, :r], (x - x_hat).astype(np.float32)[:, :r].astype(np.float64))
+    assert res.coef.shape == (x.shape[0], r)
+    assert np.array_equal(res.coef, expect)
+    # the plausible mistakes are distinguishable on this input
+    e1 = (x - res.stages[0].y_hat).astype(np.float32)[:, :r]
+    y2 = res.stages[1].y_in[:, :r]
+    assert not np.array_equal(bf16_rne(e1), expect)
+    assert not np.array_equal(bf16_rne(y2), expect)
+    assert not np.array_equal(bf16_rne(-e[:, :r].astype(np.float32)), expect)
+
+
+def test_psac_full_rank_restores_exact_logits(two_stage_keys):
+    """Full rank (U orthogonal, d x d): the corrected logits q.x_hat + (qU).coef
+    equal q.x up to the bf16 rounding of the coefficients alone, i.e. within
+    sum_b |(qU)_b| * 2^-8 |coef_b| (bf16's unit roundoff) per logit."""
+    from oracle import attention
+    x = two_stage_keys[:300]
+    rng = np.random.default_rng(5)
+    u, rm = np.linalg.qr(rng.standard_normal((128, 128)))
+    u = u * np.sign(np.diag(rm))[None, :]
+    res = pipeline.quantize_problem(x, 16, 2, 32, n_stages=2, iters=3, u=u)
+    q = rng.standard_normal((40, 128)).astype(np.float32)
+    s_corr = attention.logits(q, res.x_hat, res.coef, u, scale=1.0)
+    s_true = q.astype(np.float64) @ x.astype(np.float64).T
+    qu = q.astype(np.float64) @ u
+    bound = np.abs(qu) @ np.abs(res.coef.astype(np.float64)).T * 2.0 ** -8 + 1e-9 * np.abs(s_true).max()
+    assert np.all(np.abs(s_corr - s_true) <= bound)
+    # without the correction the logits are far off (the bound is not vacuous)
+    s_plain = attention.logits(q, res.x_hat, scale=1.0)
+    assert np.max(np.abs(s_plain - s_true)) > 20 * np.max(bound)
