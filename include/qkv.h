@@ -225,6 +225,14 @@ int qkv_dequantize(const qkv_config* cfg, int64_t n_tokens, const void* packed,
  * softmax_scale: 0 selects 1/sqrt(d).
  * logits_debug: NULL, or float [H][Nq][Nk] device receiving s_ij (-inf where
  * masked); for tests.  n_chunks in [1, 1024].
+ * Precision and range: decoded keys and values, queries and the PSAC operands
+ * enter the matrix cores as fp16 with fp32 accumulation.  A pre-pass reads the
+ * largest stored scale, centroid and PSAC coefficient of the call and the
+ * largest query, and scales each operand class by a power of two (exact) so
+ * that every fp16 operand stays finite; results are scaled back.  There is no
+ * bound on the cache's magnitude beyond finite inputs whose logits and outputs
+ * fit float32 (operands below the fp16 normal range, 2^-14 after scaling, lose
+ * precision gradually).
  */
 int qkv_attend(const qkv_config* k_cfg, const qkv_config* v_cfg, const qkv_tensor* q,
                const void* const* k_chunks, const void* const* v_chunks,

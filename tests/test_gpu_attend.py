@@ -17,7 +17,8 @@ LOGIT_TOL = 1e-3
 OUT_TOL = 5e-3
 
 
-def _run(name, wl, chunk_bounds, nq, heads_checked, causal=False, logit_queries=64, q_scale=1.0):
+def _run(name, wl, chunk_bounds, nq, heads_checked, causal=False, logit_queries=64, q_scale=1.0,
+         kv_scale=(1.0, 1.0), softmax_scale=0.0):
     t = G.torch()
     H = wl.n_heads
     kcfg, vcfg = G.config_of(wl, "K"), G.config_of(wl, "V")
@@ -40,8 +41,8 @@ def _run(name, wl, chunk_bounds, nq, heads_checked, causal=False, logit_queries=
     ws = G.workspace(kcfg, maxn, nq, len(chunk_bounds))
     wsv = G.workspace(vcfg, maxn)
     for a, b in chunk_bounds:
-        k = synth.kv_tokens(wl, "K", a, b)
-        v = synth.kv_tokens(wl, "V", a, b)
+        k = synth.kv_tokens(wl, "K", a, b) * np.float32(kv_scale[0])      # powers of two: still bf16-exact
+        v = synth.kv_tokens(wl, "V", a, b) * np.float32(kv_scale[1])
         xk.append(k)
         xv.append(v)
         kch.append(G.quantize(kcfg, G.to_dev(k, wl.dtype), w=wd, perm=pd, u=ud, ws=ws))
@@ -51,12 +52,13 @@ def _run(name, wl, chunk_bounds, nq, heads_checked, causal=False, logit_queries=
     qd = G.to_dev(q, wl.dtype)
     out = t.empty((nq, H, 128), dtype=t.float32, device=G.dev())
     G.log(f"attend {name}: H={H} chunks={len(ntok)} Nk={sum(ntok)} Nq={nq} causal={causal} psac={kcfg.psac_rank}")
-    qk.qkv_attend(kcfg, vcfg, qd, kch, vch, ntok, out, ws, U=ud, causal=causal)
+    qk.qkv_attend(kcfg, vcfg, qd, kch, vch, ntok, out, ws, U=ud, causal=causal, softmax_scale=softmax_scale)
     nk = sum(ntok)
     nlq = min(logit_queries, nq)
     logits = t.empty((H, nq, nk), dtype=t.float32, device=G.dev())
     out2 = t.empty_like(out)
-    qk.qkv_attend(kcfg, vcfg, qd, kch, vch, ntok, out2, ws, U=ud, causal=causal, logits=logits)
+    qk.qkv_attend(kcfg, vcfg, qd, kch, vch, ntok, out2, ws, U=ud, causal=causal, softmax_scale=softmax_scale,
+                  logits=logits)
     o = out.cpu().numpy()
     assert np.array_equal(o, out2.cpu().numpy()), "the logits debug path changed the output"
     # oracle: quantize the checked heads itself, then attend in float64
@@ -86,17 +88,19 @@ def _run(name, wl, chunk_bounds, nq, heads_checked, causal=False, logit_queries=
         coef = None
         if u is not None:
             coef = np.concatenate([res[(ci * len(heads_checked) + hi) * 2].coef for ci in range(len(chunk_bounds))])
+        sc = softmax_scale or None
         ref = oa.attend_head(q[:, h], k_hat, v_hat, coef, None if u is None else u[h].astype(np.float64),
-                             causal=causal)
+                             scale=sc, causal=causal)
         e_out = G.rel_l2(o[:, h], ref)
-        s_ref = oa.logits(q[:nlq, h], k_hat, coef, None if u is None else u[h].astype(np.float64), causal=causal)
+        s_ref = oa.logits(q[:nlq, h], k_hat, coef, None if u is None else u[h].astype(np.float64), scale=sc,
+                          causal=causal)
         fin = np.isfinite(s_ref)
         assert np.array_equal(fin, np.isfinite(lg[h])), f"{name} h{h}: mask differs"
         e_log = G.rel_l2(lg[h][fin], s_ref[fin])
         # the unquantized cache, for the quality diagnostic only
         kx = np.concatenate([x[:, h] for x in xk])
         vx = np.concatenate([x[:, h] for x in xv])
-        e_q = G.rel_l2(ref, oa.attend_head(q[:, h], kx, vx, causal=causal))
+        e_q = G.rel_l2(ref, oa.attend_head(q[:, h], kx, vx, scale=sc, causal=causal))
         G.log(f"attend {name} h{h}: rel-L2 logits {e_log:.3g} (tol {LOGIT_TOL}), out {e_out:.3g} (tol {OUT_TOL}); "
               f"quantized-vs-bf16-cache out {e_q:.3g}")
         assert e_log <= LOGIT_TOL, f"{name} h{h}: logits rel-L2 {e_log}"
@@ -157,6 +161,30 @@ def test_large_logits_rescaling():
     running maximum keeps growing across tiles (the online rescaling path)."""
     wl = synth.workload(2, n_heads=2, n_clusters=32)
     _run("large-logits", wl, [(0, 700), (700, 1500)], 100, [0, 1], q_scale=32.0)
+
+
+# Beyond the fp16 range: keys x 2^8 (scales up to ~2.5e4, decoded keys past 6.5e4),
+# values x 2^8 (~2.5e5), queries x 2^14 (~8e4); the softmax scale takes the logits
+# back to their usual size.  The power-of-two operand scaling must keep every
+# result within the usual bars.
+BIG = dict(q_scale=2.0 ** 14, kv_scale=(2.0 ** 8, 2.0 ** 8), softmax_scale=2.0 ** -22 / np.sqrt(128.0))
+
+
+def test_beyond_fp16_range_fast_path():
+    wl = synth.workload(2, n_heads=2, n_clusters=32)
+    _run("beyond-fp16", wl, [(0, 800), (800, 1300)], 120, [0, 1], **BIG)
+
+
+def test_beyond_fp16_range_psac():
+    """The same with QSAC + PSAC keys: the PSAC coefficients and qU scale with them."""
+    wl = synth.workload(4, n_heads=2, n_clusters=32)
+    _run("beyond-fp16-psac", wl, [(0, 700), (700, 1400)], 100, [0, 1], **BIG)
+
+
+def test_beyond_fp16_range_generic_path():
+    """Mixed INT4/INT2 keys and two progressive stages (the generic decode)."""
+    wl = synth.workload(5, n_heads=2, n_clusters=32, n_stages=2)
+    _run("beyond-fp16-generic", wl, [(0, 700), (700, 1300)], 100, [1], **BIG)
 
 
 def test_bench_shape_sampled_head():

@@ -15,8 +15,12 @@
 // MFMA (v_mfma_f32_32x32x16_f16) with an online softmax in the exp2 domain.
 //
 // Numerics: K_hat and V_hat enter the MFMAs as fp16 (S q + C evaluated by one
-// packed fp16 FMA on the fast paths, on operands bounded so that it stays
-// finite; in fp32, rounded once and saturated to +-65504 on the generic ones).  bf16 queries convert to fp16 exactly between
+// packed fp16 FMA on the fast paths; in fp32 and rounded once on the generic
+// ones).  A range pre-pass finds the largest stored scale, centroid, PSAC
+// coefficient and query of the call, and each operand class is scaled by a
+// power of two 2^-e (e >= 0, exact) that keeps every fp16 operand and decoded
+// value finite; the logits and outputs are scaled back (e = 0, no change, for
+// caches within the fp16 range).  bf16 queries convert to fp16 exactly between
 // 2^-14 and 65504 in magnitude (rounded below); fp32 queries are split into fp16 hi + lo (two MFMA passes).
 // Probabilities are rounded to fp16 for P V (fp32 accumulation) and the row
 // sums use the same rounded values.  The PSAC term rides one extra MFMA
@@ -155,11 +159,47 @@ constexpr int kItems = 1024 / kThreads;   // K (and V) decode items per thread p
 constexpr int kRing = 3;                  // raw-tile slots in LDS
 constexpr int kMetaSlots = 6;             // tile-record slots in LDS
 constexpr float kF16Max = 65504.0f;
-// bounds of the fast decode's operands: 2 * kScaleF16Max + kCentF16Max = 65456,
-// so S q + c (|q| <= 2) is finite and exact up to one fp16 rounding
-constexpr float kScaleF16Max = 16352.0f;
-constexpr float kCentF16Max = 32752.0f;
 static_assert(kBM == kAttendQueries, "queries per workgroup");
+
+// ---- operand range ----
+// Every decoded key or value is a sum over stages of S q + C with |q| <= 2^(b-1),
+// so n_stages * (2^(b-1) max|S| + max|C|) bounds it.  The exponent of a tensor
+// is the smallest e >= 0 that brings its bounds under kRangeLimit, which sits
+// below the fp16 maximum by more than the fp16 roundings of S and C can add.
+constexpr float kRangeLimit = 65024.0f;
+
+__device__ __forceinline__ int range_exp(float x) {
+  if (!(x > kRangeLimit)) return 0;
+  if (!(x < 3.0e38f)) return 120;
+  int k;
+  const float m = frexpf(x / kRangeLimit, &k);      // ratio = m 2^k, m in [0.5, 1)
+  return m == 0.5f ? k - 1 : k;
+}
+
+struct RangeExps {
+  int ek, ev, eq;
+};
+
+__device__ __forceinline__ float code_bound(const LayoutParams& p, float smax, float cmax) {
+  const float qmax = (p.n_int4 > 0 || p.bits == 4) ? 8.0f : 2.0f;
+  return (float)p.n_stages * (qmax * smax + cmax);
+}
+
+// rg: the call's range record (see RangeSlot); psac: the key PSAC term is on.
+template <typename P>
+__device__ __forceinline__ RangeExps range_exps(P rg, const LayoutParams& kp, const LayoutParams& vp, bool psac) {
+  RangeExps e;
+  e.ek = range_exp(code_bound(kp, __uint_as_float(rg[kRgKScale]), __uint_as_float(rg[kRgKCent])));
+  e.ev = range_exp(code_bound(vp, __uint_as_float(rg[kRgVScale]), __uint_as_float(rg[kRgVCent])));
+  e.eq = range_exp(__uint_as_float(rg[kRgQ]));
+  if (psac) {
+    e.ek = max(e.ek, range_exp(__uint_as_float(rg[kRgCoef])));
+    e.eq = max(e.eq, range_exp(__uint_as_float(rg[kRgQU])));
+  }
+  return e;
+}
+
+__device__ __forceinline__ float pow2(int e) { return __builtin_ldexpf(1.0f, e); }
 
 // two fp32 values -> packed fp16 (round to nearest even), saturated to the fp16 range
 __device__ __forceinline__ uint32_t pack_f16x2(float x0, float x1) {
@@ -179,11 +219,11 @@ __device__ __forceinline__ f16x2 codes_to_f16x2(uint32_t x) {
 // S * q + c as fp16 pairs for NP consecutive channel pairs: code pair j of `t`
 // sits at bits [4j, 4j+1] and [4j+16, 4j+17] (t = codes | codes << 14); cw holds
 // the centroid pairs already in fp16 (the per-call fp16 copy of the chunk's
-// bf16 table, bounded by kCentF16Max).  With |q| <= 2 and S bounded by
-// kScaleF16Max, |S q + c| <= 65456 needs no clamp per element.
+// bf16 table).  S and the centroids arrive scaled by the keys' or values' range
+// exponent, so |S q + c| stays below the fp16 maximum without a clamp.
 template <int NP>
 __device__ __forceinline__ void decode_pairs_f16(uint32_t t, float S, const uint32_t* cw, uint32_t* out) {
-  const _Float16 sh = (_Float16)__builtin_amdgcn_fmed3f(S, -kScaleF16Max, kScaleF16Max);
+  const _Float16 sh = (_Float16)S;
   const f16x2 s2 = {sh, sh};
 #pragma unroll
   for (int j = 0; j < NP; ++j) {
@@ -216,6 +256,7 @@ __device__ __forceinline__ void wait_dma() { __builtin_amdgcn_s_waitcnt(0x0F70);
 typedef const __attribute__((address_space(4))) ChunkRec* crec_ptr;
 typedef const __attribute__((address_space(4))) TileRec* ctile_ptr;
 typedef const __attribute__((address_space(4))) AttendArgs* cargs_ptr;
+typedef const __attribute__((address_space(4))) uint32_t* crange_ptr;
 
 
 template <bool QF32, bool KFAST, bool VFAST, bool LOGITS, bool PSAC>
@@ -254,6 +295,10 @@ __global__ __launch_bounds__(kThreads) void k_attend(AttendArgs a) {
   const int qrow = wq_first + col;             // this lane's query
   const bool qok = qrow < a.Nq;
 
+  // operand scaling of this call (scalar loads of the range record)
+  const RangeExps rx = range_exps((crange_ptr)a.range, a.kp, a.vp, PSAC);
+  const float qsc = pow2(-rx.eq), ksc = pow2(-rx.ek), vsc = pow2(-rx.ev);
+
   // ---- Q fragments in fp16 (B operand: column = query, k = channel) ----
   f16x8 qh[8];
   f16x8 ql[QF32 ? 8 : 1];
@@ -281,7 +326,7 @@ __global__ __launch_bounds__(kThreads) void k_attend(AttendArgs a) {
       f16x8 hi;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        v[e] = __builtin_amdgcn_fmed3f(v[e], -kF16Max, kF16Max);
+        v[e] = __builtin_amdgcn_fmed3f(v[e] * qsc, -kF16Max, kF16Max);
         hi[e] = (_Float16)v[e];
       }
       qh[s] = hi;
@@ -296,7 +341,7 @@ __global__ __launch_bounds__(kThreads) void k_attend(AttendArgs a) {
     for (int e = 0; e < 8; ++e) {
       float v = 0.0f;
       if (PSAC && qok && e < a.psac_rank)
-        v = __builtin_amdgcn_fmed3f(a.qu[((int64_t)h * a.Nq + qrow) * kMaxRank + e], -kF16Max, kF16Max);
+        v = __builtin_amdgcn_fmed3f(a.qu[((int64_t)h * a.Nq + qrow) * kMaxRank + e] * qsc, -kF16Max, kF16Max);
       const _Float16 hv = (_Float16)v;
       qpsac[e] = half == 0 ? hv : (_Float16)(v - (float)hv);
     }
@@ -306,7 +351,8 @@ __global__ __launch_bounds__(kThreads) void k_attend(AttendArgs a) {
 #pragma unroll
   for (int db = 0; db < 4; ++db) o[db] = f32x16{};
   float m_run = -INFINITY, l_run = 0.0f;       // m_run: running max in the scaled (log2) domain
-  const float c2 = a.scale * kLog2e;
+  const float sfull = a.scale * pow2(rx.eq + rx.ek);   // logit = sfull * accumulator
+  const float c2 = sfull * kLog2e;
 
   const int t_begin = (int)(((int64_t)a.n_tiles * split) / a.n_split);
   int t_end = (int)(((int64_t)a.n_tiles * (split + 1)) / a.n_split);
@@ -501,7 +547,7 @@ __global__ __launch_bounds__(kThreads) void k_attend(AttendArgs a) {
         // (probability 0)
         const uint32_t code16 = (w >> (16 * ((k0 >> 3) & 1))) & 0xFFFFu;
         const uint32_t cw[4] = {cr.x, cr.y, cr.z, cr.w};
-        decode_pairs_f16<4>(code16 | (code16 << 14), bf16_bits_to_f32(sb), cw, o4);
+        decode_pairs_f16<4>(code16 | (code16 << 14), bf16_bits_to_f32(sb) * ksc, cw, o4);
       } else {
         float v[8];
         if (ok && a.kp.n_int4 == 0) decode_uniform<8>(geom(tiles[j].chunk, false), h, tiles[j].token0 + key, k0, v);
@@ -511,7 +557,7 @@ __global__ __launch_bounds__(kThreads) void k_attend(AttendArgs a) {
           for (int e = 0; e < 8; ++e) v[e] = 0.0f;
         }
 #pragma unroll
-        for (int e = 0; e < 4; ++e) o4[e] = pack_f16x2(v[2 * e], v[2 * e + 1]);
+        for (int e = 0; e < 4; ++e) o4[e] = pack_f16x2(v[2 * e] * ksc, v[2 * e + 1] * ksc);
       }
       *reinterpret_cast<uint4*>(&sK[b][key][k0]) = make_uint4(o4[0], o4[1], o4[2], o4[3]);
     }
@@ -530,7 +576,7 @@ __global__ __launch_bounds__(kThreads) void k_attend(AttendArgs a) {
           const uint2 cr = *reinterpret_cast<const uint2*>(&sCentV[g][key * kHeadDim + k0]);
           const uint32_t code8 = (w >> (2 * (k0 & 15))) & 0xFFu;   // keys past nvalid: finite, weight 0
           const uint32_t cw[2] = {cr.x, cr.y};
-          decode_pairs_f16<2>(code8 | (code8 << 14), bf16_bits_to_f32(sb), cw, pr[y]);
+          decode_pairs_f16<2>(code8 | (code8 << 14), bf16_bits_to_f32(sb) * vsc, cw, pr[y]);
         } else {
           float v[4];
           if (ok && a.vp.n_int4 == 0) decode_uniform<4>(geom(tiles[j].chunk, true), h, tiles[j].token0 + key, k0, v);
@@ -539,8 +585,8 @@ __global__ __launch_bounds__(kThreads) void k_attend(AttendArgs a) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) v[e] = 0.0f;
           }
-          pr[y][0] = pack_f16x2(v[0], v[1]);
-          pr[y][1] = pack_f16x2(v[2], v[3]);
+          pr[y][0] = pack_f16x2(v[0] * vsc, v[1] * vsc);
+          pr[y][1] = pack_f16x2(v[2] * vsc, v[3] * vsc);
         }
       }
       // channel k0 + e gets (key 2kp, key 2kp + 1)
@@ -557,7 +603,7 @@ __global__ __launch_bounds__(kThreads) void k_attend(AttendArgs a) {
         const uint16_t* cpp = reinterpret_cast<const uint16_t*>(m64(j, kFPsac)) + ((int64_t)h * (int)m32(j, kFN) + tid) * rank;
         float f[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) f[e] = e < rank ? bf16_bits_to_f32(cpp[e]) : 0.0f;
+        for (int e = 0; e < 8; ++e) f[e] = e < rank ? bf16_bits_to_f32(cpp[e]) * ksc : 0.0f;
 #pragma unroll
         for (int e = 0; e < 4; ++e) f16w[e] = pack_f16x2(f[2 * e], f[2 * e + 1]);
       }
@@ -626,7 +672,7 @@ __global__ __launch_bounds__(kThreads) void k_attend(AttendArgs a) {
         if (LOGITS) {
           const int kl = kc + half * 4;
           if (qok && kl < nvalid)
-            a.logits[((int64_t)h * a.Nq + qrow) * a.Nk + (int64_t)(kstart + kl)] = masked ? -INFINITY : sv[i] * a.scale;
+            a.logits[((int64_t)h * a.Nq + qrow) * a.Nk + (int64_t)(kstart + kl)] = masked ? -INFINITY : sv[i] * sfull;
         }
         sv[i] = __uint_as_float((__float_as_uint(sv[i]) & ~masked) | (0xFF800000u & masked));
       }
@@ -809,7 +855,7 @@ __global__ __launch_bounds__(kThreads) void k_attend(AttendArgs a) {
   const float l_tot = l_run + __shfl_xor(l_run, 32);
   if (!qok) return;
   if (E->n_split == 1) {
-    const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+    const float inv = l_tot > 0.0f ? pow2(rx.ev) / l_tot : 0.0f;
     float* orow = E->out + (int64_t)qrow * E->out_stride_token + (int64_t)h * E->out_stride_head;
 #pragma unroll
     for (int db = 0; db < 4; ++db)
@@ -860,32 +906,43 @@ __global__ __launch_bounds__(256) void k_merge(AttendArgs a) {
       acc.x += wgt * v.x; acc.y += wgt * v.y; acc.z += wgt * v.z; acc.w += wgt * v.w;
     }
   }
-  const float inv = lsum > 0.0f ? 1.0f / lsum : 0.0f;
+  const int ev = range_exps(a.range, a.kp, a.vp, a.psac_rank > 0).ev;
+  const float inv = lsum > 0.0f ? pow2(ev) / lsum : 0.0f;
   float* orow = a.out + (int64_t)qrow * a.out_stride_token + (int64_t)h * a.out_stride_head + d0;
   *reinterpret_cast<float4*>(orow) = make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
 }
 
-// qU[h][i][b] = sum_k q_ik U[h][k][b] (float64 accumulation, rounded to fp32).
+// qU[h][i][b] = sum_k q_ik U[h][k][b] (float64 accumulation, rounded to fp32);
+// the largest |qU| of the call goes to the range record.
 template <bool QF32>
 __global__ __launch_bounds__(256) void k_qu(TensorView q, int H, int Nq, int r, const float* __restrict__ U,
-                                            float* __restrict__ qu) {
+                                            float* __restrict__ qu, uint32_t* __restrict__ range) {
   const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (gid >= (int64_t)H * Nq) return;
-  const int i = (int)(gid % Nq), h = (int)(gid / Nq);
-  double acc[kMaxRank];
+  float mx = 0.0f;
+  if (gid < (int64_t)H * Nq) {
+    const int i = (int)(gid % Nq), h = (int)(gid / Nq);
+    double acc[kMaxRank];
 #pragma unroll
-  for (int b = 0; b < kMaxRank; ++b) acc[b] = 0.0;
-  const int64_t base = (int64_t)i * q.stride_token + (int64_t)h * q.stride_head;
-  for (int k = 0; k < kHeadDim; ++k) {
-    float qv;
-    if constexpr (QF32) qv = reinterpret_cast<const float*>(q.ptr)[base + k];
-    else qv = bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(q.ptr)[base + k]);
+    for (int b = 0; b < kMaxRank; ++b) acc[b] = 0.0;
+    const int64_t base = (int64_t)i * q.stride_token + (int64_t)h * q.stride_head;
+    for (int k = 0; k < kHeadDim; ++k) {
+      float qv;
+      if constexpr (QF32) qv = reinterpret_cast<const float*>(q.ptr)[base + k];
+      else qv = bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(q.ptr)[base + k]);
 #pragma unroll
-    for (int b = 0; b < kMaxRank; ++b)
-      if (b < r) acc[b] += (double)qv * (double)U[((int64_t)h * kHeadDim + k) * r + b];
+      for (int b = 0; b < kMaxRank; ++b)
+        if (b < r) acc[b] += (double)qv * (double)U[((int64_t)h * kHeadDim + k) * r + b];
+    }
+#pragma unroll
+    for (int b = 0; b < kMaxRank; ++b) {
+      const float v = b < r ? (float)acc[b] : 0.0f;
+      qu[gid * kMaxRank + b] = v;
+      mx = fmaxf(mx, fabsf(v));
+    }
   }
 #pragma unroll
-  for (int b = 0; b < kMaxRank; ++b) qu[gid * kMaxRank + b] = b < r ? (float)acc[b] : 0.0f;
+  for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+  if ((threadIdx.x & 63) == 0) atomicMax(range + kRgQU, __float_as_uint(mx));
 }
 
 // TileRec of every tile: the chunk holding it is the last one whose first tile is <= j.
@@ -920,16 +977,20 @@ __global__ __launch_bounds__(256) void k_tile_table(const ChunkRec* __restrict__
   tiles[j] = t;
 }
 
-// Thread: 8 channels of one centroid row; blockIdx.y: 0 keys, 1 values.
-__global__ __launch_bounds__(256) void k_centroids_f16(const ChunkRec* __restrict__ recs, int n_chunks, int H, int kC,
-                                                       int vC, uint16_t* __restrict__ k16, uint16_t* __restrict__ v16) {
+// Thread: 8 channels of one centroid row; blockIdx.y: 0 keys, 1 values.  The
+// rows are scaled by the tensor's range exponent (exact) and rounded to fp16.
+__global__ __launch_bounds__(256) void k_centroids_f16(const ChunkRec* __restrict__ recs, int n_chunks, LayoutParams kp,
+                                                       LayoutParams vp, const uint32_t* __restrict__ range,
+                                                       uint16_t* __restrict__ k16, uint16_t* __restrict__ v16) {
   const bool v = blockIdx.y == 1;
   uint16_t* dst = v ? v16 : k16;
-  const int C = v ? vC : kC;
+  const int C = v ? vp.C : kp.C, H = kp.H;
   if (!dst) return;
   const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t per_chunk = (int64_t)H * C * (kHeadDim / 8);
   if (gid >= per_chunk * n_chunks) return;
+  const RangeExps rx = range_exps(range, kp, vp, kp.psac_rank > 0);
+  const float sc = pow2(-(v ? rx.ev : rx.ek));
   const int chunk = (int)(gid / per_chunk);
   const int64_t e = (gid % per_chunk) * 8;      // element within the chunk's [H][C][128] table
   const uint16_t* src = reinterpret_cast<const uint16_t*>(v ? recs[chunk].vcent : recs[chunk].kcent);
@@ -939,31 +1000,120 @@ __global__ __launch_bounds__(256) void k_centroids_f16(const ChunkRec* __restric
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     f16x2 r;
-    r[0] = (_Float16)__builtin_amdgcn_fmed3f(__uint_as_float(w4[k] << 16), -kCentF16Max, kCentF16Max);
-    r[1] = (_Float16)__builtin_amdgcn_fmed3f(__uint_as_float(w4[k] & 0xFFFF0000u), -kCentF16Max, kCentF16Max);
+    r[0] = (_Float16)__builtin_amdgcn_fmed3f(__uint_as_float(w4[k] << 16) * sc, -kF16Max, kF16Max);
+    r[1] = (_Float16)__builtin_amdgcn_fmed3f(__uint_as_float(w4[k] & 0xFFFF0000u) * sc, -kF16Max, kF16Max);
     o4[k] = __builtin_bit_cast(uint32_t, r);
   }
   *reinterpret_cast<uint4*>(dst + chunk * per_chunk * 8 + e) = make_uint4(o4[0], o4[1], o4[2], o4[3]);
 }
 
-__global__ void k_upload(ChunkBatch b, ChunkRec* __restrict__ dst) {
+// Largest bf16 magnitude (as float32 bits) of n values at p: this thread's
+// share of a grid-stride pass over uint4 words, then the scalar tail.
+__device__ __forceinline__ uint32_t bf16_absmax(const uint16_t* p, int64_t n, int64_t start, int64_t step) {
+  uint32_t m = 0;
+  const int64_t nv = n / 8;
+  const uint4* p4 = reinterpret_cast<const uint4*>(p);
+  for (int64_t i = start; i < nv; i += step) {
+    const uint4 w = p4[i];
+    const uint32_t w4[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) m = max(m, max(w4[k] & 0x7FFFu, (w4[k] >> 16) & 0x7FFFu));
+  }
+  for (int64_t i = nv * 8 + start; i < n; i += step) m = max(m, (uint32_t)p[i] & 0x7FFFu);
+  return m << 16;
+}
+
+// Range scan.  blockIdx.y = 2 chunk + tensor for the chunks' stored scales,
+// centroids (every stage) and PSAC coefficients; blockIdx.y = 2 n_chunks for
+// the queries.  Each block reduces its share and adds it with one atomic max
+// per slot.
+__global__ __launch_bounds__(256) void k_range_scan(const ChunkRec* __restrict__ recs, int n_chunks, LayoutParams kp,
+                                                    LayoutParams vp, TensorView q, int Nq,
+                                                    uint32_t* __restrict__ range) {
+  __shared__ uint32_t red[3][4];
+  const int64_t start = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t step = (int64_t)gridDim.x * blockDim.x;
+  uint32_t m[3] = {0u, 0u, 0u};                  // scale, centroid, coefficient (or query)
+  const int y = blockIdx.y;
+  if (y < 2 * n_chunks) {
+    const bool v = y & 1;
+    const ChunkRec& c = recs[y >> 1];
+    const LayoutParams& p = v ? vp : kp;
+    const ChunkDecode d = make_decode(p, c.n, v ? c.vbase : c.kbase);
+    for (int l = 0; l < d.n_stages; ++l) {
+      m[0] = max(m[0], bf16_absmax(reinterpret_cast<const uint16_t*>(d.base + d.off_scales + d.stage_scales * l),
+                                   (int64_t)d.H * d.N * d.groups, start, step));
+      m[1] = max(m[1], bf16_absmax(reinterpret_cast<const uint16_t*>(d.base + d.off_centroids + d.stage_centroids * l),
+                                   (int64_t)d.H * d.C * kHeadDim, start, step));
+    }
+    if (d.psac_rank > 0)
+      m[2] = bf16_absmax(reinterpret_cast<const uint16_t*>(d.base + d.off_psac), (int64_t)d.H * d.N * d.psac_rank,
+                         start, step);
+  } else {
+    // queries: rows of 128 values, 16 (bf16) or 32 (f32) uint4 words each
+    const int per_row = q.dtype == 0 ? 32 : 16;
+    const int64_t rows = (int64_t)Nq * kp.H;
+    for (int64_t i = start; i < rows * per_row; i += step) {
+      const int64_t row = i / per_row;
+      const int64_t off = (row / kp.H) * q.stride_token + (row % kp.H) * q.stride_head;
+      if (q.dtype == 0) {
+        const uint4 w = reinterpret_cast<const uint4*>(reinterpret_cast<const float*>(q.ptr) + off)[i % per_row];
+        m[2] = max(m[2], max(max(w.x & 0x7FFFFFFFu, w.y & 0x7FFFFFFFu), max(w.z & 0x7FFFFFFFu, w.w & 0x7FFFFFFFu)));
+      } else {
+        const uint4 w = reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(q.ptr) + off)[i % per_row];
+        const uint32_t w4[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) m[2] = max(m[2], max(w4[k] & 0x7FFFu, (w4[k] >> 16) & 0x7FFFu) << 16);
+      }
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < 3; ++k)
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) m[k] = max(m[k], (uint32_t)__shfl_xor((int)m[k], off));
+  const int wave = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0)
+#pragma unroll
+    for (int k = 0; k < 3; ++k) red[k][wave] = m[k];
+  __syncthreads();
+  if (threadIdx.x < 3) {
+    const int k = threadIdx.x;
+    const uint32_t r = max(max(red[k][0], red[k][1]), max(red[k][2], red[k][3]));
+    int slot;
+    if (y < 2 * n_chunks) slot = k == 2 ? kRgCoef : ((y & 1) ? (k == 0 ? kRgVScale : kRgVCent) : (k == 0 ? kRgKScale : kRgKCent));
+    else slot = k == 2 ? kRgQ : -1;
+    if (slot >= 0 && r != 0u) atomicMax(range + slot, r);
+  }
+}
+
+__global__ void k_upload(ChunkBatch b, ChunkRec* __restrict__ dst, uint32_t* __restrict__ range) {
   const int i = threadIdx.x;
   if (i < b.count) dst[b.first + i] = b.rec[i];
+  if (b.first == 0 && i < kRangeWords) range[i] = 0u;
 }
 
 }  // namespace
 
-hipError_t launch_upload_chunks(const ChunkBatch& b, ChunkRec* dst, hipStream_t s) {
-  hipLaunchKernelGGL(k_upload, dim3(1), dim3(kChunkBatch), 0, s, b, dst);
+hipError_t launch_upload_chunks(const ChunkBatch& b, ChunkRec* dst, uint32_t* range, hipStream_t s) {
+  static_assert(kRangeWords <= kChunkBatch, "the upload's threads clear the range record");
+  hipLaunchKernelGGL(k_upload, dim3(1), dim3(kChunkBatch), 0, s, b, dst, range);
   return hipGetLastError();
 }
 
-hipError_t launch_centroids_f16(const ChunkRec* recs, int n_chunks, int H, int kC, int vC, uint16_t* k16,
-                                uint16_t* v16, hipStream_t s) {
+hipError_t launch_range_scan(const ChunkRec* recs, int n_chunks, const LayoutParams& kp, const LayoutParams& vp,
+                             const TensorView& q, int Nq, uint32_t* range, hipStream_t s) {
+  const int ys = 2 * n_chunks + 1;
+  const int bx = std::max(1, std::min(64, 2048 / ys));
+  hipLaunchKernelGGL(k_range_scan, dim3((unsigned)bx, (unsigned)ys), dim3(256), 0, s, recs, n_chunks, kp, vp, q, Nq, range);
+  return hipGetLastError();
+}
+
+hipError_t launch_centroids_f16(const ChunkRec* recs, int n_chunks, const LayoutParams& kp, const LayoutParams& vp,
+                                const uint32_t* range, uint16_t* k16, uint16_t* v16, hipStream_t s) {
   if (!k16 && !v16) return hipSuccess;
-  const int64_t per = (int64_t)H * std::max(k16 ? kC : 0, v16 ? vC : 0) * (kHeadDim / 8) * n_chunks;
-  hipLaunchKernelGGL(k_centroids_f16, dim3((unsigned)((per + 255) / 256), 2), dim3(256), 0, s, recs, n_chunks, H, kC, vC,
-                     k16, v16);
+  const int64_t per = (int64_t)kp.H * std::max(k16 ? kp.C : 0, v16 ? vp.C : 0) * (kHeadDim / 8) * n_chunks;
+  hipLaunchKernelGGL(k_centroids_f16, dim3((unsigned)((per + 255) / 256), 2), dim3(256), 0, s, recs, n_chunks, kp, vp,
+                     range, k16, v16);
   return hipGetLastError();
 }
 
@@ -990,9 +1140,11 @@ hipError_t launch_attend(const AttendArgs& a, hipStream_t s) {
   if (a.psac_rank > 0) {
     const int64_t n = (int64_t)a.H * a.Nq;
     if (a.q.dtype == 0)
-      hipLaunchKernelGGL(k_qu<true>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a.q, a.H, a.Nq, a.psac_rank, a.U, a.qu);
+      hipLaunchKernelGGL(k_qu<true>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a.q, a.H, a.Nq, a.psac_rank, a.U, a.qu,
+                         a.range);
     else
-      hipLaunchKernelGGL(k_qu<false>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a.q, a.H, a.Nq, a.psac_rank, a.U, a.qu);
+      hipLaunchKernelGGL(k_qu<false>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a.q, a.H, a.Nq, a.psac_rank, a.U, a.qu,
+                         a.range);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -148,13 +148,25 @@ struct ChunkBatch {
   int32_t first, count;
   ChunkRec rec[kChunkBatch];
 };
-hipError_t launch_upload_chunks(const ChunkBatch& b, ChunkRec* dst, hipStream_t s);
+// Uploads one batch of chunk records; the first batch (first == 0) also clears
+// the range record.
+hipError_t launch_upload_chunks(const ChunkBatch& b, ChunkRec* dst, uint32_t* range, hipStream_t s);
+
+// Range record of one attention call (device, kRangeWords words): the largest
+// magnitudes of the operands that enter the fp16 MFMAs, as float32 bit patterns
+// (non-negative floats order like their bits, so they combine by integer max).
+enum RangeSlot { kRgKScale = 0, kRgKCent, kRgVScale, kRgVCent, kRgQ, kRgCoef, kRgQU, kRangeWords };
+// Fills every slot but kRgQU (k_qu adds that one) from the chunks' stored scales,
+// centroids and PSAC coefficients and from the queries.
+hipError_t launch_range_scan(const ChunkRec* recs, int n_chunks, const LayoutParams& kp, const LayoutParams& vp,
+                             const TensorView& q, int Nq, uint32_t* range, hipStream_t s);
 // TileRec of every tile from the uploaded chunk records.
-// fp16 copies of the chunks' bf16 centroid tables ([chunk][H][C][128], round to
-// nearest even, beyond the fp16 range -> +-inf) for the tensors decoded by the
-// attention fast path; k16 / v16 may be NULL (tensor not on the fast path).
-hipError_t launch_centroids_f16(const ChunkRec* recs, int n_chunks, int H, int kC, int vC, uint16_t* k16,
-                                uint16_t* v16, hipStream_t s);
+// fp16 copies of the chunks' bf16 centroid tables ([chunk][H][C][128]), scaled
+// by the tensor's range exponent (2^-e, exact) and rounded to nearest even, for
+// the tensors decoded by the attention fast path; k16 / v16 may be NULL (tensor
+// not on the fast path).
+hipError_t launch_centroids_f16(const ChunkRec* recs, int n_chunks, const LayoutParams& kp, const LayoutParams& vp,
+                                const uint32_t* range, uint16_t* k16, uint16_t* v16, hipStream_t s);
 // Tile records; the fast-path centroid pointers go to k16 / v16 when given.
 hipError_t launch_tile_table(const ChunkRec* recs, int n_chunks, int n_tiles, TokenBytes tb, int H, int kC, int vC,
                              const uint16_t* k16, const uint16_t* v16, TileRec* tiles, hipStream_t s);
@@ -178,6 +190,7 @@ struct AttendArgs {
   float* out;                    // [Nq][H][128] via strides
   int64_t out_stride_token, out_stride_head;
   float* logits;                 // [H][Nq][Nk] or null
+  uint32_t* range;               // range record (kRangeWords words, see RangeSlot)
   bool k_uniform_int2_1stage;    // fast-path selectors: one uniform INT2 stage,
   bool v_uniform_int2_1stage;    // groups of a multiple of 32 channels
 };

@@ -169,7 +169,7 @@ QuantWs quant_ws(const qkv_config* c, int64_t n) {
 constexpr int kTileKeys = 64;
 
 struct AttendWs {
-  uint64_t chunks, tiles, qu, part_o, part_ml, k16, v16, bytes;
+  uint64_t chunks, tiles, qu, part_o, part_ml, k16, v16, range, bytes;
 };
 
 // rows = n_split * nq: one partial (o, m, l) row per split and query (none when n_split == 1);
@@ -184,6 +184,7 @@ AttendWs attend_ws(int H, int64_t nq, int n_chunks, int64_t n_tiles, int64_t spl
   w.part_ml = off; off += align256((uint64_t)split_rows * H * 2 * 4);
   w.k16 = off;     off += align256((uint64_t)n_chunks * H * kC16 * kHeadDim * 2);
   w.v16 = off;     off += align256((uint64_t)n_chunks * H * vC16 * kHeadDim * 2);
+  w.range = off;   off += 256;
   w.bytes = off;
   return w;
 }
@@ -527,18 +528,22 @@ int qkv_attend(const qkv_config* k_cfg, const qkv_config* v_cfg, const qkv_tenso
 
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   ChunkRec* drecs = reinterpret_cast<ChunkRec*>(at(workspace, ws.chunks));
+  uint32_t* range = reinterpret_cast<uint32_t*>(at(workspace, ws.range));
   for (int first = 0; first < n_chunks; first += kChunkBatch) {
     ChunkBatch b;
     std::memset(&b, 0, sizeof b);
     b.first = first;
     b.count = std::min(kChunkBatch, n_chunks - first);
     for (int i = 0; i < b.count; ++i) b.rec[i] = recs[first + i];
-    QKV_HIP(launch_upload_chunks(b, drecs, s));
+    QKV_HIP(launch_upload_chunks(b, drecs, range, s));
   }
+  // operand range of the fp16 MFMAs: largest stored scale, centroid, PSAC
+  // coefficient and query (the kernels below derive their power-of-two scaling from it)
+  QKV_HIP(launch_range_scan(drecs, n_chunks, params_of(k_cfg), params_of(v_cfg), view_of(q), (int)Nq, range, s));
   TileRec* dtiles = reinterpret_cast<TileRec*>(at(workspace, ws.tiles));
   uint16_t* k16 = kfast ? reinterpret_cast<uint16_t*>(at(workspace, ws.k16)) : nullptr;
   uint16_t* v16 = vfast ? reinterpret_cast<uint16_t*>(at(workspace, ws.v16)) : nullptr;
-  QKV_HIP(launch_centroids_f16(drecs, n_chunks, H, k_cfg->n_clusters, v_cfg->n_clusters, k16, v16, s));
+  QKV_HIP(launch_centroids_f16(drecs, n_chunks, params_of(k_cfg), params_of(v_cfg), range, k16, v16, s));
   {
     const ChunkDecode dk = make_decode(params_of(k_cfg), 1, nullptr), dv = make_decode(params_of(v_cfg), 1, nullptr);
     const TokenBytes tb{dk.words * 4, dv.words * 4, dk.groups * 2, dv.groups * 2, k_cfg->psac_rank * 2};
@@ -569,6 +574,7 @@ int qkv_attend(const qkv_config* k_cfg, const qkv_config* v_cfg, const qkv_tenso
   a.out_stride_token = out->stride_token;
   a.out_stride_head = out->stride_head;
   a.logits = logits_debug;
+  a.range = range;
   a.k_uniform_int2_1stage = kfast;
   a.v_uniform_int2_1stage = vfast;
   QKV_HIP(launch_attend(a, s));
@@ -633,9 +639,11 @@ int qkv_psac_fit(const qkv_tensor* q_hist, int32_t n_heads, int32_t rank, int32_
     for (int k : top) hperm[(size_t)h * kHeadDim + p++] = (uint8_t)k;
     for (int k : rest) hperm[(size_t)h * kHeadDim + p++] = (uint8_t)k;
   }
-  if (w_out) QKV_HIP(hipMemcpy(w_out, hw.data(), hw.size() * 4, hipMemcpyHostToDevice));
-  if (rank > 0) QKV_HIP(hipMemcpy(U_out, hU.data(), (size_t)H * kHeadDim * rank * 4, hipMemcpyHostToDevice));
-  if (perm_out && n_int4 > 0) QKV_HIP(hipMemcpy(perm_out, hperm.data(), hperm.size(), hipMemcpyHostToDevice));
+  // outputs on the caller's stream, complete (host buffers released) before the return
+  if (w_out) QKV_HIP(hipMemcpyAsync(w_out, hw.data(), hw.size() * 4, hipMemcpyHostToDevice, s));
+  if (rank > 0) QKV_HIP(hipMemcpyAsync(U_out, hU.data(), (size_t)H * kHeadDim * rank * 4, hipMemcpyHostToDevice, s));
+  if (perm_out && n_int4 > 0) QKV_HIP(hipMemcpyAsync(perm_out, hperm.data(), hperm.size(), hipMemcpyHostToDevice, s));
+  QKV_HIP(hipStreamSynchronize(s));
   if (energy_out) std::memcpy(energy_out, energy.data(), H * sizeof(float));
   return ok();
 }
