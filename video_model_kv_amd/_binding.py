@@ -89,6 +89,14 @@ def lib():
     if _lib is None:
         if not os.path.exists(LIB_PATH):
             raise RuntimeError(f"libqkv.so is not built ({LIB_PATH}); run python -m video_model_kv_amd.build")
+        # torch ships its own HIP runtime; loading it first makes libqkv bind to
+        # that same runtime (one device context per process), where loading
+        # libqkv first would map a second HIP/HSA runtime from the ROCm install
+        # that then sees no device.
+        try:
+            import torch  # noqa: F401
+        except ImportError:
+            pass
         L = ct.CDLL(LIB_PATH)
         vp, i32, i64, sz = ct.c_void_p, ct.c_int32, ct.c_int64, ct.c_size_t
         P = ct.POINTER
