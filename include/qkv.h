@@ -207,6 +207,22 @@ int qkv_quantize_chunks(int32_t n, const qkv_config* const* cfgs, const qkv_tens
 int qkv_quantize_chunks_workspace_bytes(const qkv_config* cfg, int64_t n_tokens, int32_t n,
                                         size_t* out);
 
+/*
+ * qkv_quantize_chunk without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  The k-means and staging buffers live in a
+ * scratch array the library holds on each device (32 MiB, kept until the
+ * process ends; looked up on the first call on a device).  Writes the same
+ * packed chunk as qkv_quantize_chunk(cfg, x, side, packed, ...).  Calls no
+ * allocating routine.  Errors: QKV_EWORKSPACE when the chunk needs more than
+ * the scratch array holds (qkv_workspace_bytes(cfg, N, 0, 0) > 32 MiB: e.g.
+ * more than one stage at 32 heads x 6,240 tokens), else as qkv_quantize_chunk.
+ * All calls on one device share its scratch array: calls that overlap in time
+ * on one device (different streams or threads) race on it and must not.
+ */
+int qkv_quantize_chunk_noalloc(const qkv_config* cfg, const qkv_tensor* x, const qkv_side* side,
+                               void* packed, void* stream);
+
 /* Dequantize a packed chunk: out [N][H][d], f32 or bf16 (bf16 = nearest-even
    rounding of the f32 sum).  ([QVG] "Method / Overall framework".) */
 int qkv_dequantize(const qkv_config* cfg, int64_t n_tokens, const void* packed,

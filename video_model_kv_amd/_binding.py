@@ -23,7 +23,7 @@ EXPORTED = [
     "qkv_version", "qkv_last_error", "qkv_chunk_layout", "qkv_workspace_bytes",
     "qkv_quantize_chunk", "qkv_dequantize", "qkv_attend", "qkv_psac_fit",
     "qkv_kmeans_assign", "qkv_kmeans_update", "qkv_quant_pack",
-    "qkv_quantize_chunks", "qkv_quantize_chunks_workspace_bytes",
+    "qkv_quantize_chunks", "qkv_quantize_chunks_workspace_bytes", "qkv_quantize_chunk_noalloc",
 ]
 
 
@@ -114,6 +114,7 @@ def lib():
         L.qkv_quant_pack.argtypes = [P(qkv_config), P(qkv_tensor), vp, vp, vp, vp, i32, vp, vp]
         L.qkv_quantize_chunks.argtypes = [i32, P(P(qkv_config)), P(P(qkv_tensor)), P(P(qkv_side)), P(vp), vp, sz, vp]
         L.qkv_quantize_chunks_workspace_bytes.argtypes = [P(qkv_config), i64, i32, P(sz)]
+        L.qkv_quantize_chunk_noalloc.argtypes = [P(qkv_config), P(qkv_tensor), P(qkv_side), vp, vp]
         for name in EXPORTED[2:]:
             getattr(L, name).restype = ct.c_int
         _lib = L
@@ -174,6 +175,12 @@ def qkv_quantize_chunk(cfg: Config, x, packed, workspace, w=None, perm=None, U=N
     _check(lib().qkv_quantize_chunk(ct.byref(cfg.c()), ct.byref(tensor_desc(x)), ct.byref(side),
                                     _ptr(packed), _ptr(workspace), workspace.numel() * workspace.element_size(),
                                     _stream(stream)))
+
+
+def qkv_quantize_chunk_noalloc(cfg: Config, x, packed, w=None, perm=None, U=None, stream=None):
+    side = qkv_side(_ptr(w), _ptr(perm), _ptr(U))
+    _check(lib().qkv_quantize_chunk_noalloc(ct.byref(cfg.c()), ct.byref(tensor_desc(x)), ct.byref(side),
+                                            _ptr(packed), _stream(stream)))
 
 
 def qkv_dequantize(cfg: Config, n_tokens: int, packed, out, stream=None):

@@ -65,6 +65,12 @@ hipError_t launch_kmeans_group(const KmBatch& b, hipStream_t s);
 hipError_t launch_centroid_bf16(const KmBatch& b, hipStream_t s);
 hipError_t launch_fill_zero_u32(void* p, size_t n_words, hipStream_t s);
 
+// ---- library-held scratch (scratch.hip) ----
+// Bytes of the per-device scratch array behind qkv_quantize_chunk_noalloc.
+constexpr uint64_t kScratchBytes = 32ull << 20;
+// Device address of this device's scratch array (looked up once per device).
+hipError_t scratch_of_current_device(void** out);
+
 // ---- quantize / dequantize (quant.hip) ----
 struct PackArgs {
   TensorView y;          // stage input

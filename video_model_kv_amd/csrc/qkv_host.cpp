@@ -442,6 +442,23 @@ int qkv_quantize_chunks(int32_t n, const qkv_config* const* cfgs, const qkv_tens
   return quantize_batch(n, cfgs, xs, sides, packed, workspace, workspace_bytes, stream, "qkv_quantize_chunks");
 }
 
+int qkv_quantize_chunk_noalloc(const qkv_config* cfg, const qkv_tensor* x, const qkv_side* side, void* packed,
+                               void* stream) {
+  const char* fn = "qkv_quantize_chunk_noalloc";
+  QKV_TRY(check_config(cfg, fn));
+  QKV_TRY(check_tensor(x, cfg->n_heads, fn));
+  if (x->n_tokens < cfg->n_clusters)
+    return fail(QKV_EINVAL, "%s: n_tokens %lld < n_clusters %d", fn, (long long)x->n_tokens, cfg->n_clusters);
+  const uint64_t need = align256(quant_ws(cfg, x->n_tokens).bytes);
+  if (need > kScratchBytes)
+    return fail(QKV_EWORKSPACE, "%s: this chunk needs %llu bytes of scratch, the library holds %llu per device "
+                "(use qkv_quantize_chunk with a workspace)", fn, (unsigned long long)need,
+                (unsigned long long)kScratchBytes);
+  void* scratch = nullptr;
+  QKV_HIP(scratch_of_current_device(&scratch));
+  return quantize_batch(1, &cfg, &x, &side, &packed, scratch, (size_t)kScratchBytes, stream, fn);
+}
+
 int qkv_quantize_chunks_workspace_bytes(const qkv_config* cfg, int64_t n_tokens, int32_t n, size_t* out) {
   QKV_TRY(check_config(cfg, "qkv_quantize_chunks_workspace_bytes"));
   if (!out) return fail(QKV_EINVAL, "qkv_quantize_chunks_workspace_bytes: out is NULL");
