@@ -301,6 +301,27 @@ int qkv_quant_pack(const qkv_config* cfg, const qkv_tensor* y, const uint8_t* la
                    const float* centroids, const uint8_t* perm, void* packed, int32_t stage,
                    float* y_next, void* stream);
 
+/* ---- Kernel timing, for measurement tools ---- */
+
+/* Per-kernel totals returned by qkv_timing_read. */
+typedef struct {
+  char name[32];        /* kernel name, e.g. "k_assign", NUL-terminated */
+  int64_t launches;
+  double total_ms;      /* sum of the event-measured durations */
+} qkv_kernel_time;
+
+/* on = 1: from now on every kernel launch of the library (on any thread) is
+   bracketed by HIP events on its stream, and the record starts empty; on = 0:
+   stop recording.  The events add a few microseconds between launches; timed
+   runs that report throughput leave this off.  Host only; always QKV_OK. */
+int qkv_timing_enable(int32_t on);
+
+/* Waits for every recorded launch and writes per-kernel totals (sorted by
+   name) to out[0 .. min(n, max_kernels)), n = the number of distinct kernels
+   (*n_out).  Errors: QKV_EINVAL for a NULL n_out (or out with max_kernels >
+   0), QKV_EDEVICE when an event cannot be read. */
+int qkv_timing_read(int32_t max_kernels, qkv_kernel_time* out, int32_t* n_out);
+
 #ifdef __cplusplus
 }
 #endif

@@ -188,3 +188,12 @@ def test_psac_fit_validation_paths():
     assert lib.qkv_psac_fit(ct.byref(q), 2, 8, 0, None, None, None, f(), FAKE, 1 << 40, None) == B.QKV_EINVAL
     assert lib.qkv_psac_fit(ct.byref(q), 0, 8, 0, FAKE, None, None, f(), FAKE, 1 << 40, None) == B.QKV_EINVAL
     assert lib.qkv_psac_fit(ct.byref(q), 2, 8, 0, FAKE, None, None, f(), FAKE, 64, None) == B.QKV_EWORKSPACE
+
+
+def test_kernel_timing_switch_without_a_gpu():
+    """The timing record is host state: switching it on and reading an empty
+    record needs no device; a NULL count pointer is rejected."""
+    B.qkv_timing_enable(True)
+    assert B.qkv_timing_read() == {}
+    B.qkv_timing_enable(False)
+    assert B.lib().qkv_timing_read(0, None, None) == B.QKV_EINVAL

@@ -24,6 +24,7 @@ EXPORTED = [
     "qkv_quantize_chunk", "qkv_dequantize", "qkv_attend", "qkv_psac_fit",
     "qkv_kmeans_assign", "qkv_kmeans_update", "qkv_quant_pack",
     "qkv_quantize_chunks", "qkv_quantize_chunks_workspace_bytes", "qkv_quantize_chunk_noalloc",
+    "qkv_timing_enable", "qkv_timing_read",
 ]
 
 
@@ -46,6 +47,10 @@ class qkv_tensor(ct.Structure):
 
 class qkv_side(ct.Structure):
     _fields_ = [("w", ct.c_void_p), ("perm", ct.c_void_p), ("U", ct.c_void_p)]
+
+
+class qkv_kernel_time(ct.Structure):
+    _fields_ = [("name", ct.c_char * 32), ("launches", ct.c_int64), ("total_ms", ct.c_double)]
 
 
 class qkv_layout(ct.Structure):
@@ -115,6 +120,8 @@ def lib():
         L.qkv_quantize_chunks.argtypes = [i32, P(P(qkv_config)), P(P(qkv_tensor)), P(P(qkv_side)), P(vp), vp, sz, vp]
         L.qkv_quantize_chunks_workspace_bytes.argtypes = [P(qkv_config), i64, i32, P(sz)]
         L.qkv_quantize_chunk_noalloc.argtypes = [P(qkv_config), P(qkv_tensor), P(qkv_side), vp, vp]
+        L.qkv_timing_enable.argtypes = [i32]
+        L.qkv_timing_read.argtypes = [i32, P(qkv_kernel_time), P(i32)]
         for name in EXPORTED[2:]:
             getattr(L, name).restype = ct.c_int
         _lib = L
@@ -201,13 +208,14 @@ def qkv_attend(k_cfg: Config, v_cfg: Config, q, k_chunks, v_chunks, chunk_tokens
 
 
 def qkv_psac_fit(q_hist, n_heads: int, rank: int, n_int4: int, workspace, U_out=None, w_out=None,
-                 perm_out=None, stream=None):
-    """Returns the per-head energy fractions (host floats)."""
-    energy = (ct.c_float * n_heads)()
+                 perm_out=None, stream=None, energy: bool = True):
+    """Returns the per-head energy fractions (host floats), or None with energy=False
+    (then no eigensolver runs when rank == 0)."""
+    en = (ct.c_float * n_heads)() if energy else None
     _check(lib().qkv_psac_fit(ct.byref(tensor_desc(q_hist)), n_heads, rank, n_int4, _ptr(U_out), _ptr(w_out),
-                              _ptr(perm_out), energy, _ptr(workspace),
+                              _ptr(perm_out), en, _ptr(workspace),
                               workspace.numel() * workspace.element_size(), _stream(stream)))
-    return list(energy)
+    return list(en) if energy else None
 
 
 def qkv_quantize_chunks_workspace_bytes(cfg: Config, n_tokens: int, n: int) -> int:
@@ -247,3 +255,16 @@ def qkv_quant_pack(cfg: Config, y, labels, centroids, packed, stage: int = 0, pe
                    stream=None):
     _check(lib().qkv_quant_pack(ct.byref(cfg.c()), ct.byref(tensor_desc(y)), _ptr(labels), _ptr(centroids),
                                 _ptr(perm), _ptr(packed), stage, _ptr(y_next), _stream(stream)))
+
+
+def qkv_timing_enable(on: bool):
+    _check(lib().qkv_timing_enable(1 if on else 0))
+
+
+def qkv_timing_read() -> dict:
+    """{kernel name: (launches, total ms)} of the launches recorded since qkv_timing_enable(True)."""
+    n = ct.c_int32()
+    _check(lib().qkv_timing_read(0, None, ct.byref(n)))
+    buf = (qkv_kernel_time * max(1, n.value))()
+    _check(lib().qkv_timing_read(n.value, buf, ct.byref(n)))
+    return {buf[i].name.decode(): (int(buf[i].launches), float(buf[i].total_ms)) for i in range(n.value)}

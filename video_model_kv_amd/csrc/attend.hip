@@ -32,6 +32,7 @@
 
 #include "common.h"
 #include "kernels.h"
+#include "timing.h"
 
 namespace qkv {
 
@@ -1095,6 +1096,7 @@ __global__ void k_upload(ChunkBatch b, ChunkRec* __restrict__ dst, uint32_t* __r
 }  // namespace
 
 hipError_t launch_upload_chunks(const ChunkBatch& b, ChunkRec* dst, uint32_t* range, hipStream_t s) {
+  TimedLaunch tl_("k_upload", s);
   static_assert(kRangeWords <= kChunkBatch, "the upload's threads clear the range record");
   hipLaunchKernelGGL(k_upload, dim3(1), dim3(kChunkBatch), 0, s, b, dst, range);
   return hipGetLastError();
@@ -1102,6 +1104,7 @@ hipError_t launch_upload_chunks(const ChunkBatch& b, ChunkRec* dst, uint32_t* ra
 
 hipError_t launch_range_scan(const ChunkRec* recs, int n_chunks, const LayoutParams& kp, const LayoutParams& vp,
                              const TensorView& q, int Nq, uint32_t* range, hipStream_t s) {
+  TimedLaunch tl_("k_range_scan", s);
   const int ys = 2 * n_chunks + 1;
   const int bx = std::max(1, std::min(64, 2048 / ys));
   hipLaunchKernelGGL(k_range_scan, dim3((unsigned)bx, (unsigned)ys), dim3(256), 0, s, recs, n_chunks, kp, vp, q, Nq, range);
@@ -1110,6 +1113,7 @@ hipError_t launch_range_scan(const ChunkRec* recs, int n_chunks, const LayoutPar
 
 hipError_t launch_centroids_f16(const ChunkRec* recs, int n_chunks, const LayoutParams& kp, const LayoutParams& vp,
                                 const uint32_t* range, uint16_t* k16, uint16_t* v16, hipStream_t s) {
+  TimedLaunch tl_("k_centroids_f16", s);
   if (!k16 && !v16) return hipSuccess;
   const int64_t per = (int64_t)kp.H * std::max(k16 ? kp.C : 0, v16 ? vp.C : 0) * (kHeadDim / 8) * n_chunks;
   hipLaunchKernelGGL(k_centroids_f16, dim3((unsigned)((per + 255) / 256), 2), dim3(256), 0, s, recs, n_chunks, kp, vp,
@@ -1119,6 +1123,7 @@ hipError_t launch_centroids_f16(const ChunkRec* recs, int n_chunks, const Layout
 
 hipError_t launch_tile_table(const ChunkRec* recs, int n_chunks, int n_tiles, TokenBytes tb, int H, int kC, int vC,
                              const uint16_t* k16, const uint16_t* v16, TileRec* tiles, hipStream_t s) {
+  TimedLaunch tl_("k_tile_table", s);
   if (n_tiles <= 0) return hipSuccess;
   hipLaunchKernelGGL(k_tile_table, dim3((unsigned)((n_tiles + 255) / 256)), dim3(256), 0, s, recs, n_chunks, n_tiles, tb,
                      H, kC, vC, k16, v16, tiles);
@@ -1138,6 +1143,7 @@ void launch_attend_variant(int flags, const AttendArgs& a, dim3 grid, hipStream_
 
 hipError_t launch_attend(const AttendArgs& a, hipStream_t s) {
   if (a.psac_rank > 0) {
+    TimedLaunch tl_("k_qu", s);
     const int64_t n = (int64_t)a.H * a.Nq;
     if (a.q.dtype == 0)
       hipLaunchKernelGGL(k_qu<true>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a.q, a.H, a.Nq, a.psac_rank, a.U, a.qu,
@@ -1152,10 +1158,14 @@ hipError_t launch_attend(const AttendArgs& a, hipStream_t s) {
   const dim3 grid((unsigned)(q_tiles * a.n_split * a.H));
   const int flags = (a.q.dtype == 0 ? 1 : 0) | (a.k_uniform_int2_1stage ? 2 : 0) | (a.v_uniform_int2_1stage ? 4 : 0) |
                     (a.logits ? 8 : 0) | (a.psac_rank > 0 ? 16 : 0);
-  launch_attend_variant(flags, a, grid, s, std::make_integer_sequence<int, 32>{});
+  {
+    TimedLaunch tl_("k_attend", s);
+    launch_attend_variant(flags, a, grid, s, std::make_integer_sequence<int, 32>{});
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.n_split == 1) return e;
   const int64_t total = (int64_t)a.H * a.Nq * (kHeadDim / 4);
+  TimedLaunch tl_("k_merge", s);
   hipLaunchKernelGGL(k_merge, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, a);
   return hipGetLastError();
 }

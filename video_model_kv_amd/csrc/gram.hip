@@ -5,6 +5,7 @@
 // exact in float64 and every partial sum is accumulated in a fixed order.
 #include "common.h"
 #include "kernels.h"
+#include "timing.h"
 
 namespace qkv {
 
@@ -61,6 +62,7 @@ __global__ void k_gram_reduce(int64_t per, int n_split, const double* __restrict
 }  // namespace
 
 hipError_t launch_gram(const TensorView& q, int H, double* partial, int n_split, double* m, hipStream_t s) {
+  TimedLaunch tl_("k_gram", s);
   const dim3 grid(n_split, H);
   if (q.dtype == 0) hipLaunchKernelGGL(k_gram_partial<true>, grid, dim3(256), 0, s, q, n_split, partial);
   else hipLaunchKernelGGL(k_gram_partial<false>, grid, dim3(256), 0, s, q, n_split, partial);

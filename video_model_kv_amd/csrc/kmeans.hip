@@ -23,6 +23,7 @@
 
 #include "common.h"
 #include "kernels.h"
+#include "timing.h"
 
 namespace qkv {
 
@@ -919,6 +920,7 @@ __global__ void k_fill_zero(uint32_t* __restrict__ p, int64_t n) {
 }  // namespace
 
 hipError_t launch_kmeans_init(const KmBatch& b, hipStream_t s) {
+  TimedLaunch tl_("k_init", s);
   const dim3 grid((b.C + 7) / 8, b.H, b.n);
   if (b.dtype == 0) hipLaunchKernelGGL(k_init<true>, grid, dim3(256), 0, s, b);
   else hipLaunchKernelGGL(k_init<false>, grid, dim3(256), 0, s, b);
@@ -926,11 +928,13 @@ hipError_t launch_kmeans_init(const KmBatch& b, hipStream_t s) {
 }
 
 hipError_t launch_centroid_prep(const KmBatch& b, hipStream_t s) {
+  TimedLaunch tl_("k_prep", s);
   hipLaunchKernelGGL(k_prep, dim3(b.H * b.C, b.n), dim3(64), 0, s, b);
   return hipGetLastError();
 }
 
 hipError_t launch_kmeans_assign(const KmBatch& b, hipStream_t s) {
+  TimedLaunch tl_("k_assign", s);
   if (b.C > kAsgMaxC) return hipErrorInvalidValue;
   // Workgroups per head G: each workgroup pays a fixed cost (plane load,
   // first tokens, close calls; about kAsgUnitCost sub-blocks' worth) and the
@@ -954,6 +958,7 @@ hipError_t launch_kmeans_assign(const KmBatch& b, hipStream_t s) {
 }
 
 hipError_t launch_kmeans_update(const KmBatch& b, bool refresh, hipStream_t s) {
+  TimedLaunch tl_("k_update", s);
   const bool grouped = b.it[0].grp_off != nullptr && b.N <= kUpdWindow;   // set for all problems or none
   // 32 clusters per workgroup when the launch holds enough work to fill the
   // chip with the fewer, longer workgroups (measured: 7 % faster at 12
@@ -976,18 +981,21 @@ hipError_t launch_kmeans_update(const KmBatch& b, bool refresh, hipStream_t s) {
 }
 
 hipError_t launch_kmeans_group(const KmBatch& b, hipStream_t s) {
+  TimedLaunch tl_("k_group", s);
   if (b.N > kUpdWindow || b.C > 256) return hipErrorInvalidValue;
   hipLaunchKernelGGL(k_group, dim3(b.H, b.n), dim3(256), 0, s, b);
   return hipGetLastError();
 }
 
 hipError_t launch_centroid_bf16(const KmBatch& b, hipStream_t s) {
+  TimedLaunch tl_("k_centroid_bf16", s);
   const int64_t n = (int64_t)b.H * b.C * kHeadDim;
   hipLaunchKernelGGL(k_centroid_bf16, dim3((unsigned)((n + 255) / 256), b.n), dim3(256), 0, s, b);
   return hipGetLastError();
 }
 
 hipError_t launch_fill_zero_u32(void* p, size_t n_words, hipStream_t s) {
+  TimedLaunch tl_("k_fill_zero", s);
   if (n_words == 0) return hipSuccess;
   hipLaunchKernelGGL(k_fill_zero, dim3((unsigned)((n_words + 255) / 256)), dim3(256), 0, s,
                      reinterpret_cast<uint32_t*>(p), (int64_t)n_words);

@@ -15,6 +15,7 @@
 //   y_hat = fp32(S * q + C) (S * q is exact);  y_next = fp32(y - y_hat).
 #include "common.h"
 #include "kernels.h"
+#include "timing.h"
 
 namespace qkv {
 
@@ -392,6 +393,123 @@ __global__ __launch_bounds__(256) void k_quant_pack_tile(PackBatch pb, int tiles
   }
 }
 
+// Mixed layout (a per-head channel order perm: the 4-bit class first, then the
+// 2-bit class, each cut into runs of `group`), same tiles as the uniform
+// kernel, in three phases:
+//   (1) the residuals of the tile's rows in channel order, loaded and formed as
+//       in the uniform kernel, into LDS;
+//   (2) one thread per (row, group) reads its group's residuals in storage
+//       order through perm, takes the group scale and packs the group's words
+//       (groups never share a word: a class starts on a word boundary and
+//       `group` is a multiple of 16; positions past a class's end stay zero);
+//   (3) codes and scales leave per head as contiguous runs.
+// Stages that also need the fp32 residual (y_next) take k_quant_pack.
+constexpr int kMixMaxWords = 17;     // 4-bit words + 2-bit words of a row (n_int4 = 127)
+constexpr int kMixMaxGroups = 9;     // ceil(n_int4 / 16) + ceil((128 - n_int4) / 16)
+
+template <bool F32>
+__global__ __launch_bounds__(256) void k_quant_pack_tile_mixed(PackArgs a) {
+  __shared__ __attribute__((aligned(16))) float s_r[kTileRows][kHeadDim + 4];
+  __shared__ uint8_t s_perm[kTileHeads][kHeadDim];
+  __shared__ uint32_t s_codes[kTileRows * kMixMaxWords];
+  __shared__ uint16_t s_scales[kTileRows * kMixMaxGroups];
+  __shared__ float s_rtab[128];                   // fp32(1 / (1 + k / 128))
+  const int tid = threadIdx.x;
+  if (tid < 128) s_rtab[tid] = 1.0f / (1.0f + (float)tid * 0.0078125f);
+  const int tile = (int)xcd_remap(blockIdx.x, gridDim.x);
+  const TileGeom tg = tile_geom(a.H, a.N);
+  const int ntb = (a.N + tg.T - 1) / tg.T;
+  const int i0 = (tile % ntb) * tg.T, h0 = (tile / ntb) * tg.HB;
+  const int rows = tg.T * tg.HB;
+  const int tmax = a.N - 1 - i0, hmax = a.H - 1 - h0;
+  for (int i = tid; i < kTileHeads * kHeadDim; i += 256) {
+    const int hh = i >> 7, k = i & (kHeadDim - 1);
+    s_perm[hh][k] = a.perm[(int64_t)(h0 + min(hh, hmax)) * kHeadDim + k] & (kHeadDim - 1);
+  }
+  // (1) residuals; rows outside the tile read a clamped valid row
+  const int part = tid & 15, k0 = part * 8;
+  constexpr int kIt = kTileRows * 16 / 256;
+  const uint32_t ST = (uint32_t)a.y.stride_token, SH = (uint32_t)a.y.stride_head, NN = (uint32_t)a.N;
+  const int64_t y_base = (int64_t)i0 * a.y.stride_token + (int64_t)h0 * a.y.stride_head + k0;
+  const uint8_t* lab_base = a.labels + (int64_t)h0 * a.N + i0;
+  const uint16_t* cent_base = a.centroids + (int64_t)h0 * a.C * kHeadDim + k0;
+#pragma unroll
+  for (int x = 0; x < kIt; ++x) {
+    const int lr = x * 16 + (tid >> 4);
+    const int t = lr / tg.HB, hh = lr - t * tg.HB;
+    const int tc = min(t, tmax), hc = min(hh, hmax);
+    const int lab = min((int)lab_base[__umul24((uint32_t)hc, NN) + (uint32_t)tc], a.C - 1);
+    const uint32_t yo = __umul24((uint32_t)tc, ST) + __umul24((uint32_t)hc, SH);
+    float yv[8], cv[8];
+    if constexpr (F32) {
+      const float* p = reinterpret_cast<const float*>(a.y.ptr) + y_base + yo;
+      const float4 p0 = *reinterpret_cast<const float4*>(p);
+      const float4 p1 = *reinterpret_cast<const float4*>(p + 4);
+      yv[0] = p0.x; yv[1] = p0.y; yv[2] = p0.z; yv[3] = p0.w; yv[4] = p1.x; yv[5] = p1.y; yv[6] = p1.z; yv[7] = p1.w;
+    } else {
+      const uint4 p = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(a.y.ptr) + y_base + yo);
+      const uint32_t w4[4] = {p.x, p.y, p.z, p.w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) yv[e] = bf16_bits_to_f32((w4[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
+    }
+    const uint4 c = *reinterpret_cast<const uint4*>(cent_base + (__umul24((uint32_t)hc, (uint32_t)a.C) + (uint32_t)lab) * kHeadDim);
+    const uint32_t c4[4] = {c.x, c.y, c.z, c.w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) cv[e] = bf16_bits_to_f32((c4[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
+    float* dst = &s_r[lr][k0];
+    *reinterpret_cast<float4*>(dst) = make_float4(yv[0] - cv[0], yv[1] - cv[1], yv[2] - cv[2], yv[3] - cv[3]);
+    *reinterpret_cast<float4*>(dst + 4) = make_float4(yv[4] - cv[4], yv[5] - cv[5], yv[6] - cv[6], yv[7] - cv[7]);
+  }
+  __syncthreads();
+  // (2) one (row, group) per thread
+  const int NG = a.groups, W = a.words;
+  for (int idx = tid; idx < rows * NG; idx += 256) {
+    const int lr = idx / NG, g = idx - lr * NG;
+    const uint8_t* pr = s_perm[lr % tg.HB];
+    const float* rr = s_r[lr];
+    const GroupInfo gi = group_info(g, a.bits, a.group, a.n_int4, a.int4_words);
+    float amax = 0.0f;
+    for (int e = 0; e < gi.len; ++e) amax = fmaxf(amax, fabsf(rr[pr[gi.start + e]]));
+    const float qmax = (float)((1 << (gi.bits - 1)) - 1);
+    const uint32_t sbits = f32_to_bf16_bits(amax / qmax);
+    const float S = bf16_bits_to_f32(sbits);
+    s_scales[lr * NG + g] = (uint16_t)sbits;
+    const int per = 32 / gi.bits;
+    uint32_t* wout = &s_codes[lr * W + gi.word0 + gi.pos0 / per];
+    for (int e0 = 0; e0 < gi.len; e0 += 8) {
+      float r8[8];
+      const int n = min(8, gi.len - e0);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) r8[e] = e < n ? rr[pr[gi.start + e0 + e]] : 0.0f;
+      if (gi.bits == 4) {
+        uint32_t w = pack8_codes<4>(r8, S, sbits, s_rtab);
+        if (n < 8) w &= (1u << (4 * n)) - 1u;
+        wout[e0 >> 3] = w;
+      } else {
+        uint32_t w = pack8_codes<2>(r8, S, sbits, s_rtab);
+        if (n < 8) w &= (1u << (2 * n)) - 1u;
+        if ((e0 & 8) == 0) wout[e0 >> 4] = w;                 // low half; the high half may follow
+        else wout[e0 >> 4] |= w << 16;
+      }
+    }
+  }
+  __syncthreads();
+  // (3) write-out: per head, the tile's T rows are contiguous in [H][N] order
+  const int tv = min(tg.T, a.N - i0);
+  for (int idx = tid; idx < tg.HB * tg.T * W; idx += 256) {
+    const int hh = idx / (tg.T * W), rem = idx - hh * (tg.T * W);
+    const int t = rem / W, w = rem - t * W;
+    if (hh <= hmax && t < tv)
+      a.codes[((int64_t)(h0 + hh) * a.N + i0 + t) * W + w] = s_codes[(t * tg.HB + hh) * W + w];
+  }
+  for (int idx = tid; idx < tg.HB * tg.T * NG; idx += 256) {
+    const int hh = idx / (tg.T * NG), rem = idx - hh * (tg.T * NG);
+    const int t = rem / NG, g = rem - t * NG;
+    if (hh <= hmax && t < tv)
+      a.scales[((int64_t)(h0 + hh) * a.N + i0 + t) * NG + g] = s_scales[(t * tg.HB + hh) * NG + g];
+  }
+}
+
 __device__ __forceinline__ const uint8_t* stage_ptr(const ChunkDecode& d, uint64_t off, uint64_t stride, int l) {
   return d.base + off + stride * (uint64_t)l;
 }
@@ -493,6 +611,7 @@ __global__ __launch_bounds__(256) void k_psac_encode(ChunkDecode d, TensorView x
 }  // namespace
 
 hipError_t launch_quant_pack_generic(const PackArgs& a, hipStream_t s) {
+  TimedLaunch tl_("k_quant_pack", s);
   const bool f32 = a.y.dtype == 0;
   const int64_t total = (int64_t)a.H * a.N * a.groups;
   const dim3 grid((unsigned)((total + 255) / 256)), block(256);
@@ -516,6 +635,17 @@ hipError_t launch_quant_pack(const PackArgs& a, hipStream_t s) {
     pb.n = 1;
     pb.a[0] = a;
     return launch_quant_pack_batch(pb, s);
+  }
+  // the mixed tile kernel: no fp32 residual output, 24-bit in-tile offsets
+  const bool tile_ok = a.perm && !a.y_next && a.words <= kMixMaxWords && a.groups <= kMixMaxGroups &&
+                       a.y.stride_token < (1 << 23) && a.y.stride_head < (1 << 23) && a.N < (1 << 23) &&
+                       (int64_t)a.H * a.C < (1 << 23);
+  if (tile_ok) {
+    TimedLaunch tl_("k_quant_pack_tile_mixed", s);
+    const dim3 grid((unsigned)tile_geom(a.H, a.N).tiles), block(256);
+    if (a.y.dtype == 0) hipLaunchKernelGGL(k_quant_pack_tile_mixed<true>, grid, block, 0, s, a);
+    else hipLaunchKernelGGL(k_quant_pack_tile_mixed<false>, grid, block, 0, s, a);
+    return hipGetLastError();
   }
   return launch_quant_pack_generic(a, s);
 }
@@ -544,6 +674,7 @@ hipError_t launch_quant_pack_batch(const PackBatch& b, hipStream_t s) {
   const bool f32 = a.y.dtype == 0;
   const int tiles = tile_geom(a.H, a.N).tiles;
   const dim3 grid((unsigned)(tiles * b.n)), block(256);
+  TimedLaunch tl_("k_quant_pack_tile", s);
 #define QKV_QF(GV, BV)                                                                              \
   if (a.group == GV && a.bits == BV) {                                                              \
     if (f32) hipLaunchKernelGGL((k_quant_pack_tile<GV, BV, true>), grid, block, 0, s, b, tiles);     \
@@ -558,6 +689,7 @@ hipError_t launch_quant_pack_batch(const PackBatch& b, hipStream_t s) {
 
 hipError_t launch_dequantize(const ChunkDecode& d, void* out, int out_dtype, int64_t stride_token,
                              int64_t stride_head, hipStream_t s) {
+  TimedLaunch tl_("k_dequant", s);
   const dim3 grid((unsigned)((d.N + 31) / 32), (unsigned)d.H);
   hipLaunchKernelGGL(k_dequant, grid, dim3(256), 0, s, d, out, out_dtype, stride_token, stride_head);
   return hipGetLastError();
@@ -565,6 +697,7 @@ hipError_t launch_dequantize(const ChunkDecode& d, void* out, int out_dtype, int
 
 hipError_t launch_psac_encode(const ChunkDecode& d, const TensorView& x, const float* U, uint16_t* coef_out,
                               hipStream_t s) {
+  TimedLaunch tl_("k_psac_encode", s);
   const dim3 grid((unsigned)((d.N + 255) / 256), (unsigned)d.H);
   if (x.dtype == 0) hipLaunchKernelGGL(k_psac_encode<true>, grid, dim3(256), 0, s, d, x, U, coef_out);
   else hipLaunchKernelGGL(k_psac_encode<false>, grid, dim3(256), 0, s, d, x, U, coef_out);
@@ -572,6 +705,7 @@ hipError_t launch_psac_encode(const ChunkDecode& d, const TensorView& x, const f
 }
 
 hipError_t launch_copy_perm(const uint8_t* perm, uint8_t* dst, int H, hipStream_t s) {
+  TimedLaunch tl_("copy_perm", s);
   return hipMemcpyAsync(dst, perm, (size_t)H * kHeadDim, hipMemcpyDeviceToDevice, s);
 }
 
