@@ -260,8 +260,35 @@ typedef const __attribute__((address_space(4))) AttendArgs* cargs_ptr;
 typedef const __attribute__((address_space(4))) uint32_t* crange_ptr;
 
 
-template <bool QF32, bool KFAST, bool VFAST, bool LOGITS, bool PSAC>
+// Mixed INT4/INT2 keys on the fast path ("mix4"): a pre-pass (k_repack_mix)
+// rewrites each key's codes as 128 nibbles u' = q + 8 in the per-call item
+// order of MixOrder (whole 8-position items of one scale group, the groups'
+// remainders packed into the last items, each item split at most once, on a
+// pair boundary), with the two codes of a pair at nibble slots j and j + 4 of
+// the item's word.  Decoded keys then sit in LDS in that order; the queries are
+// loaded in the same order (through the chunk's channel permutation), so the
+// dot products are unchanged.
+__device__ __forceinline__ void decode_mix4(uint32_t w, float slo, float shi, int jb, const uint32_t* cw,
+                                            uint32_t* out) {
+  const _Float16 lo = (_Float16)slo, hi = (_Float16)shi;
+  const f16x2 slo2 = {lo, lo}, shi2 = {hi, hi};
+  const f16x2 off = {(_Float16)1032.0f, (_Float16)1032.0f};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const f16x2 q = __builtin_bit_cast(f16x2, ((w >> (4 * j)) & 0x000F000Fu) | 0x64006400u) - off;
+    const f16x2 s2 = j < jb ? slo2 : shi2;
+    out[j] = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(s2, q, __builtin_bit_cast(f16x2, cw[j])));
+  }
+}
+
+// KM: key decode mode -- 0 generic (every layout), 1 one uniform INT2 stage,
+// 2 one mixed INT4/INT2 stage through the mix4 pre-pass.
+template <bool QF32, int KM, bool VFAST, bool LOGITS, bool PSAC>
 __global__ __launch_bounds__(kThreads) void k_attend(AttendArgs a) {
+  constexpr bool KFAST = KM != 0;                // keys through the copy ring and the LDS staging
+  static_assert(KM != 2 || (!QF32 && !PSAC), "mix4 keys: bf16 queries, no PSAC term");
+  constexpr int kKW = KM == 2 ? 16 : 8;          // K code words per key in the ring
+  constexpr int kKGm = KM == 2 ? kMix4MaxGroups : 4;   // K scale groups per key (at most)
   // Separate LDS objects: the compiler waits for outstanding asynchronous
   // copies before an LDS read only when the read may touch a copy target, so
   // the MFMA operands (K, Vt, Kp) live apart from the copy targets (ring and
@@ -271,8 +298,11 @@ __global__ __launch_bounds__(kThreads) void k_attend(AttendArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t sKp[2][kKTile][16];             // fp16 [coef | coef]
   __shared__ __attribute__((aligned(16))) uint16_t sCentK[2][kKTile * kHeadDim];   // gathered K centroid rows
   __shared__ __attribute__((aligned(16))) uint16_t sCentV[2][kKTile * kHeadDim];   // gathered V centroid rows
-  __shared__ __attribute__((aligned(16))) uint32_t sRc[kRing][2][kKTile * 8];      // [slot][K/V] code words
-  __shared__ __attribute__((aligned(16))) uint16_t sRs[kRing][2][kKTile * 4 + 8];  // [slot][K/V] scales (+ lead)
+  __shared__ __attribute__((aligned(16))) uint32_t sRcK[kRing][kKTile * kKW];      // [slot] K code words
+  __shared__ __attribute__((aligned(16))) uint32_t sRcV[kRing][kKTile * 8];        // [slot] V code words
+  __shared__ __attribute__((aligned(16))) uint16_t sRsK[kRing][kKTile * kKGm + 8]; // [slot] K scales (+ lead)
+  __shared__ __attribute__((aligned(16))) uint16_t sRsV[kRing][kKTile * 4 + 8];    // [slot] V scales (+ lead)
+  __shared__ uint8_t sRho[KM == 2 ? kHeadDim : 1];                                 // mix4 item order
   __shared__ __attribute__((aligned(16))) uint8_t sRl[kRing][2][kKTile + 16];      // [slot][K/V] labels (+ lead)
   __shared__ ChannelCode sTabK[kHeadDim], sTabV[kHeadDim];                         // generic decode tables
   __shared__ __attribute__((aligned(16))) uint32_t sMeta[kMetaSlots][sizeof(TileRec) / 4];   // tile records
@@ -299,12 +329,20 @@ __global__ __launch_bounds__(kThreads) void k_attend(AttendArgs a) {
   // operand scaling of this call (scalar loads of the range record)
   const RangeExps rx = range_exps((crange_ptr)a.range, a.kp, a.vp, PSAC);
   const float qsc = pow2(-rx.eq), ksc = pow2(-rx.ek), vsc = pow2(-rx.ev);
+  uint32_t mdesc = 0;                            // mix4: this thread's item (first group, last group, split pair)
+  if constexpr (KM == 2) {
+    const int it = tid & 15;
+    mdesc = (uint32_t)a.mixp->glo[it] | ((uint32_t)a.mixp->ghi[it] << 8) | ((uint32_t)a.mixp->jb[it] << 16);
+  }
 
   // ---- Q fragments in fp16 (B operand: column = query, k = channel) ----
   f16x8 qh[8];
   f16x8 ql[QF32 ? 8 : 1];
   f16x8 qpsac;
-  {
+  if constexpr (KM == 2) {
+#pragma unroll
+    for (int s = 0; s < 8; ++s) qh[s] = f16x8{};   // loaded in item order with the first tile's chunk
+  } else {
     const int64_t base = (int64_t)(qok ? qrow : 0) * a.q.stride_token + (int64_t)h * a.q.stride_head;
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
@@ -346,6 +384,10 @@ __global__ __launch_bounds__(kThreads) void k_attend(AttendArgs a) {
       const _Float16 hv = (_Float16)v;
       qpsac[e] = half == 0 ? hv : (_Float16)(v - (float)hv);
     }
+  }
+  if constexpr (KM == 2) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) qpsac[e] = (_Float16)0.0f;
   }
 
   f32x16 o[4];
@@ -403,6 +445,8 @@ __global__ __launch_bounds__(kThreads) void k_attend(AttendArgs a) {
   };
   const int kG = kHeadDim / a.kp.group, vG = kHeadDim / a.vp.group;   // scale groups per token (fast paths)
   const int kGs = __builtin_ctz(kG), vGs = __builtin_ctz(vG);
+  const int kGn = KM == 2 ? make_decode(a.kp, 1, nullptr).groups : kG;  // K scales per key in the ring
+  constexpr int kKBpk = KM == 2 ? 64 : 32;       // K code bytes per key in the ring
   const int kC = a.kp.C, vC = a.vp.C;
 
   // Tile records travel into an LDS ring (sMeta, kMetaSlots tiles) by
@@ -413,10 +457,11 @@ __global__ __launch_bounds__(kThreads) void k_attend(AttendArgs a) {
   // not start on a 4-byte boundary: they are copied from the boundary below
   // and sit `lead` bytes into their LDS slot.
   constexpr int kRecWords = (int)(sizeof(TileRec) / 4);
-  constexpr int kFSrc = 0, kFCent = 12, kFPsac = 16, kFN = 18, kFNvalid = 19, kFKstart = 20;
+  constexpr int kFSrc = 0, kFCent = 12, kFPsac = 16, kFN = 18, kFNvalid = 19, kFKstart = 20, kFChunk = 22;
   static_assert(offsetof(TileRec, cent) == 4 * kFCent && offsetof(TileRec, kpsac) == 4 * kFPsac &&
                 offsetof(TileRec, n) == 4 * kFN && offsetof(TileRec, nvalid) == 4 * kFNvalid &&
-                offsetof(TileRec, kstart) == 4 * kFKstart, "TileRec field offsets");
+                offsetof(TileRec, kstart) == 4 * kFKstart && offsetof(TileRec, chunk) == 4 * kFChunk,
+                "TileRec field offsets");
   auto meta_copy = [&](int j) __attribute__((always_inline)) {   // wave 0 only
     const int lane = xtid & 63;
     if (lane < kRecWords)
@@ -430,16 +475,16 @@ __global__ __launch_bounds__(kThreads) void k_attend(AttendArgs a) {
   };
   auto lead_of = [](uint32_t addr_lo) __attribute__((always_inline)) -> int { return (int)(addr_lo & 3); };
   // raw copy role of this wave: tensor rv, part rpart (code words by parts
-  // 0 and 1, scales by part 2, labels by part 3); rshift = log2 bytes per token
+  // 0 and 1, scales by part 2, labels by part 3); bpk = bytes per key
   struct RawRole {
-    int rv, rpart, rsel, rshift;
+    int rv, rpart, rsel, bpk;
   };
   auto raw_role = [&]() __attribute__((always_inline)) -> RawRole {
     RawRole q;
     q.rv = xwave >> 2;
     q.rpart = xwave & 3;
     q.rsel = q.rpart < 2 ? 0 : q.rpart - 1;
-    q.rshift = q.rsel == 0 ? 5 : q.rsel == 1 ? (q.rv ? vGs : kGs) + 1 : 0;
+    q.bpk = q.rsel == 0 ? (q.rv ? 32 : kKBpk) : q.rsel == 1 ? 2 * (q.rv ? vG : kGn) : 1;
     return q;
   };
   struct RawView {                               // tile i+3: this wave's run
@@ -457,7 +502,7 @@ __global__ __launch_bounds__(kThreads) void k_attend(AttendArgs a) {
     const RawRole q = raw_role();
     RawView w;
     const int64_t hrow = (int64_t)h * (int)m32(j, kFN);
-    w.src = m64(j, kFSrc + (q.rv * 3 + q.rsel) * 2) + (hrow << q.rshift) + (q.rpart == 1 ? 1024 : 0);
+    w.src = m64(j, kFSrc + (q.rv * 3 + q.rsel) * 2) + hrow * q.bpk + (q.rpart == 1 ? 32 * q.bpk : 0);
     w.nvalid = live ? (int)m32(j, kFNvalid) : 0;
     return w;
   };
@@ -474,7 +519,7 @@ __global__ __launch_bounds__(kThreads) void k_attend(AttendArgs a) {
   auto decode_view = [&](int j, bool live) __attribute__((always_inline)) -> DecodeView {
     DecodeView w;
     const uint32_t hrow = (uint32_t)h * m32(j, kFN);
-    w.lead[0] = lead_of(m32(j, kFSrc + 2) + (hrow << (kGs + 1))) >> 1;   // src[0][1]: K scales
+    w.lead[0] = lead_of(m32(j, kFSrc + 2) + hrow * (uint32_t)(2 * kGn)) >> 1;   // src[0][1]: K scales
     w.lead[1] = lead_of(m32(j, kFSrc + 8) + (hrow << (vGs + 1))) >> 1;   // src[1][1]: V scales
     w.nvalid = live ? (int)m32(j, kFNvalid) : 0;
     return w;
@@ -486,20 +531,26 @@ __global__ __launch_bounds__(kThreads) void k_attend(AttendArgs a) {
   auto raw_copy = [&](const RawView& R, int r) __attribute__((always_inline)) {
     const int lane = xtid & 63;
     const RawRole q = raw_role();
-    const int rv = q.rv, rpart = q.rpart, rsel = q.rsel, rshift = q.rshift;
+    const int rv = q.rv, rpart = q.rpart, rsel = q.rsel, bpk = q.bpk;
     if ((rv == 0 && !KFAST) || (rv == 1 && !VFAST)) return;
-    if (rsel == 0) {                             // code words: 32 bytes per key
-      const int key = rpart * 32 + (lane >> 1);
-      if (key < R.nvalid) dma<16>(R.src + lane * 16, &sRc[r][rv][rpart * 256]);
+    if (rsel == 0) {                             // code words of 32 keys: 32 (or 64 for mix4 keys) bytes each
+      uint32_t* dst = rv ? &sRcV[r][rpart * 256] : &sRcK[r][rpart * 32 * kKW];   // 32 keys per part
+#pragma unroll
+      for (int x = 0; x < kKBpk / 32; ++x) {
+        if (x * 32 < bpk) {                      // wave-uniform: V keys take one pass
+          const int key = rpart * 32 + (x * 1024 + lane * 16) / bpk;
+          if (key < R.nvalid) dma<16>(R.src + x * 1024 + lane * 16, dst + x * 256);
+        }
+      }
     } else {                                     // scales (2G bytes per key) or labels (1 byte per key)
       const int lead = lead_of((uint32_t)reinterpret_cast<uintptr_t>(R.src));
       const uint8_t* base = R.src - lead;
-      const int words = (lead + (R.nvalid << rshift) + 3) >> 2;
+      const int words = (lead + R.nvalid * bpk + 3) >> 2;
 #pragma unroll
-      for (int x = 0; x < 3; ++x) {              // at most 3 + 512 bytes: 129 words
+      for (int x = 0; x < 3; ++x) {              // at most 3 + 640 bytes: 161 words
         const int wd = x * 64 + lane;
         if (x * 64 < words && wd < words) {
-          if (rsel == 1) dma<4>(base + wd * 4, &sRs[r][rv][x * 128]);
+          if (rsel == 1) dma<4>(base + wd * 4, rv ? &sRsV[r][x * 128] : &sRsK[r][x * 128]);
           else dma<4>(base + wd * 4, &sRl[r][rv][x * 256]);
         }
       }
@@ -539,16 +590,24 @@ __global__ __launch_bounds__(kThreads) void k_attend(AttendArgs a) {
       const int key = item >> 4, k0 = (item & 15) * 8;
       const bool ok = key < nvalid;
       uint32_t o4[4];
-      if constexpr (KFAST) {
-        const uint32_t w = sRc[r][0][key * 8 + (k0 >> 4)];
-        const uint32_t sb = sRs[r][0][klead + (key << kGs) + ((k0 << kGs) >> 7)];   // groups: powers of two
+      // keys past nvalid decode stale LDS contents (zero at the start, then
+      // earlier tiles' values): finite, and their scores are masked (probability 0)
+      if constexpr (KM == 1) {
+        const uint32_t w = sRcK[r][key * 8 + (k0 >> 4)];
+        const uint32_t sb = sRsK[r][klead + (key << kGs) + ((k0 << kGs) >> 7)];   // groups: powers of two
         const uint4 cr = *reinterpret_cast<const uint4*>(&sCentK[g][key * kHeadDim + k0]);
-        // keys past nvalid decode stale LDS contents (zero at the start,
-        // then earlier tiles' values): finite, and their scores are masked
-        // (probability 0)
         const uint32_t code16 = (w >> (16 * ((k0 >> 3) & 1))) & 0xFFFFu;
         const uint32_t cw[4] = {cr.x, cr.y, cr.z, cr.w};
         decode_pairs_f16<4>(code16 | (code16 << 14), bf16_bits_to_f32(sb) * ksc, cw, o4);
+      } else if constexpr (KM == 2) {
+        // item k0 / 8 (= tid % 16) of the mix4 order: one code word, the scales
+        // of its (at most two) groups, centroid values already in item order
+        const uint32_t w = sRcK[r][key * 16 + (k0 >> 3)];
+        const int srow = klead + key * kGn;
+        const uint32_t slo = sRsK[r][srow + (int)(mdesc & 0xFFu)], shi = sRsK[r][srow + (int)((mdesc >> 8) & 0xFFu)];
+        const uint4 cr = *reinterpret_cast<const uint4*>(&sCentK[g][key * kHeadDim + k0]);
+        const uint32_t cw[4] = {cr.x, cr.y, cr.z, cr.w};
+        decode_mix4(w, bf16_bits_to_f32(slo) * ksc, bf16_bits_to_f32(shi) * ksc, (int)(mdesc >> 16), cw, o4);
       } else {
         float v[8];
         if (ok && a.kp.n_int4 == 0) decode_uniform<8>(geom(tiles[j].chunk, false), h, tiles[j].token0 + key, k0, v);
@@ -572,8 +631,8 @@ __global__ __launch_bounds__(kThreads) void k_attend(AttendArgs a) {
         const int key = 2 * kp + y;
         const bool ok = key < nvalid;
         if constexpr (VFAST) {
-          const uint32_t w = sRc[r][1][key * 8 + (k0 >> 4)];
-          const uint32_t sb = sRs[r][1][vlead + (key << vGs) + ((k0 << vGs) >> 7)];
+          const uint32_t w = sRcV[r][key * 8 + (k0 >> 4)];
+          const uint32_t sb = sRsV[r][vlead + (key << vGs) + ((k0 << vGs) >> 7)];
           const uint2 cr = *reinterpret_cast<const uint2*>(&sCentV[g][key * kHeadDim + k0]);
           const uint32_t code8 = (w >> (2 * (k0 & 15))) & 0xFFu;   // keys past nvalid: finite, weight 0
           const uint32_t cw[2] = {cr.x, cr.y};
@@ -612,10 +671,37 @@ __global__ __launch_bounds__(kThreads) void k_attend(AttendArgs a) {
       *reinterpret_cast<uint4*>(&sKp[b][tid][8]) = make_uint4(f16w[0], f16w[1], f16w[2], f16w[3]);
     }
   };
+  // mix4 keys: the queries in the item order of chunk ch's channel permutation
+  // (reloaded by each wave when the chunk of its compute tile changes)
+  int q_chunk = -1;
+  auto load_q_mix = [&](int ch) __attribute__((always_inline)) {
+    const int lane = xtid & 63, half = lane >> 5;
+    const ChunkDecode d = make_decode(a.kp, recs[ch].n, recs[ch].kbase);
+    const uint8_t* prow = d.base + d.off_perm + (int64_t)h * kHeadDim;
+    const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q.ptr) + (int64_t)(qok ? qrow : 0) * a.q.stride_token +
+                         (int64_t)h * a.q.stride_head;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      f16x8 hv;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int k = prow[sRho[s * 16 + half * 8 + e]] & (kHeadDim - 1);
+        const float v = qok ? bf16_bits_to_f32(qp[k]) : 0.0f;
+        hv[e] = (_Float16)__builtin_amdgcn_fmed3f(v * qsc, -kF16Max, kF16Max);
+      }
+      qh[s] = hv;
+    }
+  };
   // (4) this wave's 32 queries against tile j in LDS buffer b
-  auto compute_tile = [&](int nvalid, int kstart, int b) __attribute__((always_inline)) {
+  auto compute_tile = [&](int nvalid, int kstart, int b, int chunk) __attribute__((always_inline)) {
     const int lane = xtid & 63, col = lane & 31, half = lane >> 5;
     if (!wave_active) return;
+    if constexpr (KM == 2) {
+      if (chunk != q_chunk) {                   // wave-uniform
+        load_q_mix(chunk);
+        q_chunk = chunk;
+      }
+    }
     if (a.causal && !LOGITS && kstart > wq_last) return;        // wholly above the diagonal
     const bool need_mask = nvalid < kKTile || (a.causal && kstart + kKTile - 1 > wq_first);
     // S^T = K_hat Q^T, both 32-key halves interleaved (fp16 operands, fp32 accumulation)
@@ -752,8 +838,13 @@ __global__ __launch_bounds__(kThreads) void k_attend(AttendArgs a) {
       ck[i] = make_uint4(0u, 0u, 0u, 0u);
       cv[i] = make_uint4(0u, 0u, 0u, 0u);
     }
-    uint32_t* rs = reinterpret_cast<uint32_t*>(&sRs[0][0][0]);
-    for (int i = tid; i < (int)(sizeof(sRs) / 4); i += kThreads) rs[i] = 0u;
+    uint32_t* rsk = reinterpret_cast<uint32_t*>(&sRsK[0][0]);
+    for (int i = tid; i < (int)(sizeof(sRsK) / 4); i += kThreads) rsk[i] = 0u;
+    uint32_t* rsv = reinterpret_cast<uint32_t*>(&sRsV[0][0]);
+    for (int i = tid; i < (int)(sizeof(sRsV) / 4); i += kThreads) rsv[i] = 0u;
+  }
+  if constexpr (KM == 2) {
+    if (tid < kHeadDim) sRho[tid] = a.mixp->rho[tid];
   }
   const int r0 = t_begin % kRing;
   if (xwave == 0) {
@@ -794,18 +885,18 @@ __global__ __launch_bounds__(kThreads) void k_attend(AttendArgs a) {
     const uint32_t* M2 = sMeta[j2 % kMetaSlots];
     const uint32_t* M3 = sMeta[j3 % kMetaSlots];
     const int fs = kFSrc + (q.rv * 3 + q.rsel) * 2;
-    uint32_t w[18] = {M0[kFNvalid], M0[kFKstart],
+    uint32_t w[19] = {M0[kFNvalid], M0[kFKstart],
                       M1[kFNvalid], M1[kFN], M1[kFSrc + 2], M1[kFSrc + 8],
                       M2[kFNvalid], M2[kFN], M2[kFCent], M2[kFCent + 1], M2[kFCent + 2], M2[kFCent + 3],
                       M2[kFSrc + 4], M2[kFSrc + 10],
-                      M3[kFNvalid], M3[kFN], M3[fs], M3[fs + 1]};
+                      M3[kFNvalid], M3[kFN], M3[fs], M3[fs + 1], KM == 2 ? M0[kFChunk] : 0u};
 #pragma unroll
-    for (int k = 0; k < 18; ++k) w[k] = (uint32_t)__builtin_amdgcn_readfirstlane((int)w[k]);
-    const int nv0 = (int)w[0], ks0 = (int)w[1];
+    for (int k = 0; k < 19; ++k) w[k] = (uint32_t)__builtin_amdgcn_readfirstlane((int)w[k]);
+    const int nv0 = (int)w[0], ks0 = (int)w[1], ch0 = (int)w[18];
     DecodeView DV;
     {
       const uint32_t hrow = (uint32_t)h * w[3];
-      DV.lead[0] = lead_of(w[4] + (hrow << (kGs + 1))) >> 1;     // K scales
+      DV.lead[0] = lead_of(w[4] + hrow * (uint32_t)(2 * kGn)) >> 1;   // K scales
       DV.lead[1] = lead_of(w[5] + (hrow << (vGs + 1))) >> 1;     // V scales
       DV.nvalid = has1 ? (int)w[2] : 0;
     }
@@ -821,7 +912,7 @@ __global__ __launch_bounds__(kThreads) void k_attend(AttendArgs a) {
     RawView RV;
     {
       const int64_t hrow = (int64_t)h * (int)w[15];
-      RV.src = reinterpret_cast<const uint8_t*>(((uint64_t)w[17] << 32) | w[16]) + (hrow << q.rshift) + (q.rpart == 1 ? 1024 : 0);
+      RV.src = reinterpret_cast<const uint8_t*>(((uint64_t)w[17] << 32) | w[16]) + hrow * q.bpk + (q.rpart == 1 ? 32 * q.bpk : 0);
       RV.nvalid = has3 ? (int)w[14] : 0;
     }
     if (has1) tables_for(j1);
@@ -837,7 +928,7 @@ __global__ __launch_bounds__(kThreads) void k_attend(AttendArgs a) {
     for (int ph = 0; ph < 2; ++ph) {
       if (ph == grp) {
         if (grp == 0) issue();
-        compute_tile(nv0, ks0, ti & 1);                                     // (4) tile i
+        compute_tile(nv0, ks0, ti & 1, ch0);                                // (4) tile i
       } else {
         if (has1) decode_tile(DV, j1, r1, (ti + 1) & 1, (ti + 1) & 1);      // (3) tile i+1
         if (grp == 1) issue();
@@ -960,7 +1051,7 @@ __global__ __launch_bounds__(256) void k_tile_table(const ChunkRec* __restrict__
   const ChunkRec& c = recs[lo];
   const int token0 = (j - c.tile_start) * kKTile;
   TileRec t;
-  t.src[0][0] = c.kcodes + (int64_t)token0 * tb.kcodes;
+  t.src[0][0] = (c.krep ? c.krep : c.kcodes) + (int64_t)token0 * tb.kcodes;
   t.src[1][0] = c.vcodes + (int64_t)token0 * tb.vcodes;
   t.src[0][1] = c.kscales + (int64_t)token0 * tb.kscales;
   t.src[1][1] = c.vscales + (int64_t)token0 * tb.vscales;
@@ -982,6 +1073,7 @@ __global__ __launch_bounds__(256) void k_tile_table(const ChunkRec* __restrict__
 // rows are scaled by the tensor's range exponent (exact) and rounded to fp16.
 __global__ __launch_bounds__(256) void k_centroids_f16(const ChunkRec* __restrict__ recs, int n_chunks, LayoutParams kp,
                                                        LayoutParams vp, const uint32_t* __restrict__ range,
+                                                       const MixOrder* __restrict__ kmix,
                                                        uint16_t* __restrict__ k16, uint16_t* __restrict__ v16) {
   const bool v = blockIdx.y == 1;
   uint16_t* dst = v ? v16 : k16;
@@ -995,8 +1087,23 @@ __global__ __launch_bounds__(256) void k_centroids_f16(const ChunkRec* __restric
   const int chunk = (int)(gid / per_chunk);
   const int64_t e = (gid % per_chunk) * 8;      // element within the chunk's [H][C][128] table
   const uint16_t* src = reinterpret_cast<const uint16_t*>(v ? recs[chunk].vcent : recs[chunk].kcent);
-  const uint4 w = *reinterpret_cast<const uint4*>(src + e);
-  const uint32_t w4[4] = {w.x, w.y, w.z, w.w};
+  uint32_t w4[4];
+  if (!v && kmix) {
+    // mix4 keys: the row in item order, through the chunk's channel permutation
+    const ChunkDecode d = make_decode(kp, recs[chunk].n, recs[chunk].kbase);
+    const int64_t row = e >> 7;                                    // h * C + j
+    const uint8_t* prow = d.base + d.off_perm + (row / C) * kHeadDim;
+    const int r0 = (int)(e & (kHeadDim - 1));
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t lo = src[row * kHeadDim + (prow[kmix->rho[r0 + 2 * k]] & (kHeadDim - 1))];
+      const uint32_t hi = src[row * kHeadDim + (prow[kmix->rho[r0 + 2 * k + 1]] & (kHeadDim - 1))];
+      w4[k] = lo | (hi << 16);
+    }
+  } else {
+    const uint4 w = *reinterpret_cast<const uint4*>(src + e);
+    w4[0] = w.x; w4[1] = w.y; w4[2] = w.z; w4[3] = w.w;
+  }
   uint32_t o4[4];
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
@@ -1087,20 +1194,72 @@ __global__ __launch_bounds__(256) void k_range_scan(const ChunkRec* __restrict__
   }
 }
 
-__global__ void k_upload(ChunkBatch b, ChunkRec* __restrict__ dst, uint32_t* __restrict__ range) {
+__global__ void k_upload(ChunkBatch b, ChunkRec* __restrict__ dst, uint32_t* __restrict__ range, MixOrder mix,
+                         MixOrder* __restrict__ mix_dst) {
   const int i = threadIdx.x;
   if (i < b.count) dst[b.first + i] = b.rec[i];
   if (b.first == 0 && i < kRangeWords) range[i] = 0u;
+  if (b.first == 0 && mix_dst && i == 0) *mix_dst = mix;
+}
+
+// mix4 codes: a block takes 16 consecutive (head, token) rows of chunk
+// blockIdx.y, their code words staged in LDS by contiguous loads; thread =
+// (row, item) writes the item's word: u' = q + 8 of position 2j at nibble slot
+// j and of position 2j + 1 at slot j + 4.
+constexpr int kRepackRows = 16;
+constexpr int kRepackMaxWords = 17;   // 4-bit words + 2-bit words of a mixed row (n_int4 = 127)
+__global__ __launch_bounds__(256) void k_repack_mix(const ChunkRec* __restrict__ recs, LayoutParams kp,
+                                                    const MixOrder* __restrict__ mix) {
+  __shared__ uint8_t rho[kHeadDim];
+  __shared__ uint32_t sw[kRepackRows][kRepackMaxWords + 1];
+  const ChunkRec& c = recs[blockIdx.y];
+  const int64_t rows = (int64_t)kp.H * c.n;
+  const int64_t r0 = (int64_t)blockIdx.x * kRepackRows;
+  if (r0 >= rows) return;                        // the whole block
+  const ChunkDecode d = make_decode(kp, c.n, c.kbase);
+  const int W = min(d.words, kRepackMaxWords), n4 = d.n_int4, w4 = d.int4_words;
+  const int nrows = (int)min<int64_t>(kRepackRows, rows - r0);
+  const uint32_t* src = reinterpret_cast<const uint32_t*>(d.base + d.off_codes) + r0 * d.words;
+  for (int i = threadIdx.x; i < nrows * W; i += blockDim.x) sw[i / W][i % W] = src[(i / W) * d.words + i % W];
+  if (threadIdx.x < kHeadDim) rho[threadIdx.x] = mix->rho[threadIdx.x];
+  __syncthreads();
+  const int tr = threadIdx.x >> 4, it = threadIdx.x & 15;
+  if (tr >= nrows) return;
+  uint32_t acc = 0;
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    const int p = rho[it * 8 + t];
+    uint32_t u;
+    if (p < n4) {
+      u = (sw[tr][min(p >> 3, W - 1)] >> (4 * (p & 7))) & 15u;
+    } else {
+      const int pb = p - n4;
+      u = ((sw[tr][min(w4 + (pb >> 4), W - 1)] >> (2 * (pb & 15))) & 3u) + 6u;
+    }
+    acc |= u << (4 * ((t >> 1) + 4 * (t & 1)));
+  }
+  reinterpret_cast<uint32_t*>(const_cast<uint8_t*>(c.krep))[(r0 + tr) * 16 + it] = acc;
 }
 
 }  // namespace
 
-hipError_t launch_upload_chunks(const ChunkBatch& b, ChunkRec* dst, uint32_t* range, hipStream_t s) {
+hipError_t launch_upload_chunks(const ChunkBatch& b, ChunkRec* dst, uint32_t* range, const MixOrder& mix,
+                                MixOrder* mix_dst, hipStream_t s) {
   TimedLaunch tl_("k_upload", s);
   static_assert(kRangeWords <= kChunkBatch, "the upload's threads clear the range record");
-  hipLaunchKernelGGL(k_upload, dim3(1), dim3(kChunkBatch), 0, s, b, dst, range);
+  hipLaunchKernelGGL(k_upload, dim3(1), dim3(kChunkBatch), 0, s, b, dst, range, mix, mix_dst);
   return hipGetLastError();
 }
+
+hipError_t launch_repack_mix(const ChunkRec* recs, int n_chunks, int max_tokens, const LayoutParams& kp,
+                             const MixOrder* mix, hipStream_t s) {
+  TimedLaunch tl_("k_repack_mix", s);
+  const int64_t per = (int64_t)kp.H * max_tokens;
+  hipLaunchKernelGGL(k_repack_mix, dim3((unsigned)((per + kRepackRows - 1) / kRepackRows), (unsigned)n_chunks), dim3(256),
+                     0, s, recs, kp, mix);
+  return hipGetLastError();
+}
+
 
 hipError_t launch_range_scan(const ChunkRec* recs, int n_chunks, const LayoutParams& kp, const LayoutParams& vp,
                              const TensorView& q, int Nq, uint32_t* range, hipStream_t s) {
@@ -1112,12 +1271,13 @@ hipError_t launch_range_scan(const ChunkRec* recs, int n_chunks, const LayoutPar
 }
 
 hipError_t launch_centroids_f16(const ChunkRec* recs, int n_chunks, const LayoutParams& kp, const LayoutParams& vp,
-                                const uint32_t* range, uint16_t* k16, uint16_t* v16, hipStream_t s) {
+                                const uint32_t* range, const MixOrder* kmix, uint16_t* k16, uint16_t* v16,
+                                hipStream_t s) {
   TimedLaunch tl_("k_centroids_f16", s);
   if (!k16 && !v16) return hipSuccess;
   const int64_t per = (int64_t)kp.H * std::max(k16 ? kp.C : 0, v16 ? vp.C : 0) * (kHeadDim / 8) * n_chunks;
   hipLaunchKernelGGL(k_centroids_f16, dim3((unsigned)((per + 255) / 256), 2), dim3(256), 0, s, recs, n_chunks, kp, vp,
-                     range, k16, v16);
+                     range, kmix, k16, v16);
   return hipGetLastError();
 }
 
@@ -1132,14 +1292,17 @@ hipError_t launch_tile_table(const ChunkRec* recs, int n_chunks, int n_tiles, To
 
 template <int F>
 void launch_attend_flags(const AttendArgs& a, dim3 grid, hipStream_t s) {
-  hipLaunchKernelGGL((k_attend<(F & 1) != 0, (F & 2) != 0, (F & 4) != 0, (F & 8) != 0, (F & 16) != 0>), grid,
+  constexpr int KM = (F & 32) ? 2 : (F & 2) ? 1 : 0;
+  hipLaunchKernelGGL((k_attend<(F & 1) != 0, KM, (F & 4) != 0, (F & 8) != 0, (F & 16) != 0>), grid,
                      dim3(kThreads), 0, s, a);
 }
-// flags: 1 fp32 queries, 2 K fast path, 4 V fast path, 8 debug logits, 16 PSAC
+// flags: 1 fp32 queries, 2 K INT2 fast path, 4 V fast path, 8 debug logits,
+// 16 PSAC, 32 K mix4 path (only with bf16 queries and no PSAC)
 template <int... F>
 void launch_attend_variant(int flags, const AttendArgs& a, dim3 grid, hipStream_t s, std::integer_sequence<int, F...>) {
   ((flags == F ? launch_attend_flags<F>(a, grid, s) : void()), ...);
 }
+
 
 hipError_t launch_attend(const AttendArgs& a, hipStream_t s) {
   if (a.psac_rank > 0) {
@@ -1156,11 +1319,13 @@ hipError_t launch_attend(const AttendArgs& a, hipStream_t s) {
   }
   const int q_tiles = (a.Nq + kBM - 1) / kBM;
   const dim3 grid((unsigned)(q_tiles * a.n_split * a.H));
-  const int flags = (a.q.dtype == 0 ? 1 : 0) | (a.k_uniform_int2_1stage ? 2 : 0) | (a.v_uniform_int2_1stage ? 4 : 0) |
+  const int flags = (a.q.dtype == 0 ? 1 : 0) | (a.k_mode == 1 ? 2 : 0) | (a.k_mode == 2 ? 32 : 0) |
+                    (a.v_uniform_int2_1stage ? 4 : 0) |
                     (a.logits ? 8 : 0) | (a.psac_rank > 0 ? 16 : 0);
   {
     TimedLaunch tl_("k_attend", s);
-    launch_attend_variant(flags, a, grid, s, std::make_integer_sequence<int, 32>{});
+    if (flags & 32) launch_attend_variant(flags, a, grid, s, std::integer_sequence<int, 32, 36, 40, 44>{});
+    else launch_attend_variant(flags, a, grid, s, std::make_integer_sequence<int, 32>{});
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.n_split == 1) return e;

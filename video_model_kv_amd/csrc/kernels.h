@@ -124,6 +124,7 @@ struct ChunkRec {
   const uint8_t* vscales;
   const uint8_t* vlabels;
   const uint8_t* vcent;
+  const uint8_t* krep;   // mix4 codes of the chunk's keys (64 bytes per token-head, workspace), or null
   int64_t token_start;   // global index of the chunk's first token
   int32_t n;             // tokens in the chunk
   int32_t tile_start;    // global index of the chunk's first 64-key tile
@@ -150,13 +151,32 @@ struct TokenBytes {
   int32_t kcodes, vcodes, kscales, vscales, kpsac;
 };
 
+// Item order of mixed INT4/INT2 keys on the attention fast path ("mix4"):
+// 16 items of 8 positions, each item within one scale group except for at
+// most one split on a pair boundary.  rho[r] is the storage position of item
+// position r; item i covers groups glo[i] (pairs < jb[i]) and ghi[i] (the
+// rest; jb = 4 when glo == ghi).
+constexpr int kMix4MaxGroups = 5;
+struct MixOrder {
+  uint8_t rho[128];
+  uint8_t glo[16], ghi[16], jb[16];
+};
+// The mix4 order of a mixed layout, or false when its groups cannot be laid
+// out so (odd class sizes, more than two groups in an item, more than
+// kMix4MaxGroups groups per token).
+bool mix4_order(const LayoutParams& p, MixOrder* m);
+
 struct ChunkBatch {
   int32_t first, count;
   ChunkRec rec[kChunkBatch];
 };
 // Uploads one batch of chunk records; the first batch (first == 0) also clears
 // the range record.
-hipError_t launch_upload_chunks(const ChunkBatch& b, ChunkRec* dst, uint32_t* range, hipStream_t s);
+hipError_t launch_upload_chunks(const ChunkBatch& b, ChunkRec* dst, uint32_t* range, const MixOrder& mix,
+                                MixOrder* mix_dst, hipStream_t s);
+// mix4 codes of every chunk's keys (ChunkRec::krep) from their packed codes.
+hipError_t launch_repack_mix(const ChunkRec* recs, int n_chunks, int max_tokens, const LayoutParams& kp,
+                             const MixOrder* mix, hipStream_t s);
 
 // Range record of one attention call (device, kRangeWords words): the largest
 // magnitudes of the operands that enter the fp16 MFMAs, as float32 bit patterns
@@ -172,7 +192,8 @@ hipError_t launch_range_scan(const ChunkRec* recs, int n_chunks, const LayoutPar
 // the tensors decoded by the attention fast path; k16 / v16 may be NULL (tensor
 // not on the fast path).
 hipError_t launch_centroids_f16(const ChunkRec* recs, int n_chunks, const LayoutParams& kp, const LayoutParams& vp,
-                                const uint32_t* range, uint16_t* k16, uint16_t* v16, hipStream_t s);
+                                const uint32_t* range, const MixOrder* kmix, uint16_t* k16, uint16_t* v16,
+                                hipStream_t s);
 // Tile records; the fast-path centroid pointers go to k16 / v16 when given.
 hipError_t launch_tile_table(const ChunkRec* recs, int n_chunks, int n_tiles, TokenBytes tb, int H, int kC, int vC,
                              const uint16_t* k16, const uint16_t* v16, TileRec* tiles, hipStream_t s);
@@ -197,8 +218,10 @@ struct AttendArgs {
   int64_t out_stride_token, out_stride_head;
   float* logits;                 // [H][Nq][Nk] or null
   uint32_t* range;               // range record (kRangeWords words, see RangeSlot)
-  bool k_uniform_int2_1stage;    // fast-path selectors: one uniform INT2 stage,
-  bool v_uniform_int2_1stage;    // groups of a multiple of 32 channels
+  const MixOrder* mixp;          // device copy of the mix4 order (k_mode 2)
+  int k_mode;                    // key decode: 0 generic, 1 one uniform INT2 stage (groups of a
+                                 // multiple of 32 channels), 2 one mixed INT4/INT2 stage via mix4
+  bool v_uniform_int2_1stage;    // value decode: one uniform INT2 stage, groups of a multiple of 32
 };
 hipError_t launch_attend(const AttendArgs& a, hipStream_t s);
 

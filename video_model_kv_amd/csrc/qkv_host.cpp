@@ -25,6 +25,40 @@ void jacobi_eigh(int n, double* a, double* evals, double* evecs);
 
 using namespace qkv;
 
+namespace qkv {
+
+bool mix4_order(const LayoutParams& p, MixOrder* m) {
+  const int n4 = p.n_int4, g = p.group;
+  if (n4 <= 0 || (n4 & 1) || (g & 1) || p.bits != 2) return false;
+  // groups in storage order: the 4-bit class, then the 2-bit class, runs of g
+  int start[kHeadDim], len[kHeadDim], ng = 0;
+  for (int a = 0; a < n4; a += g) { start[ng] = a; len[ng] = std::min(g, n4 - a); ++ng; }
+  for (int a = 0; a < kHeadDim - n4; a += g) { start[ng] = n4 + a; len[ng] = std::min(g, kHeadDim - n4 - a); ++ng; }
+  if (ng > kMix4MaxGroups) return false;
+  int pos = 0, grp[kHeadDim];
+  for (int k = 0; k < ng; ++k)                   // whole 8-position items of each group
+    for (int b = 0; b + 8 <= len[k]; b += 8)
+      for (int t = 0; t < 8; ++t) { m->rho[pos] = (uint8_t)(start[k] + b + t); grp[pos++] = k; }
+  for (int k = 0; k < ng; ++k)                   // then the groups' remainders, in group order
+    for (int t = len[k] / 8 * 8; t < len[k]; ++t) { m->rho[pos] = (uint8_t)(start[k] + t); grp[pos++] = k; }
+  if (pos != kHeadDim) return false;
+  for (int it = 0; it < 16; ++it) {
+    const int* gi = grp + it * 8;
+    int jb = 4;
+    for (int t = 1; t < 8; ++t) {
+      if (gi[t] == gi[t - 1]) continue;
+      if (jb != 4 || (t & 1)) return false;      // a second split, or a split inside a pair
+      jb = t / 2;
+    }
+    m->glo[it] = (uint8_t)gi[0];
+    m->ghi[it] = (uint8_t)gi[7];
+    m->jb[it] = (uint8_t)jb;
+  }
+  return true;
+}
+
+}  // namespace qkv
+
 namespace {
 
 thread_local std::string g_err;
@@ -169,12 +203,14 @@ QuantWs quant_ws(const qkv_config* c, int64_t n) {
 constexpr int kTileKeys = 64;
 
 struct AttendWs {
-  uint64_t chunks, tiles, qu, part_o, part_ml, k16, v16, range, bytes;
+  uint64_t chunks, tiles, qu, part_o, part_ml, k16, v16, range, mix, krep, bytes;
 };
 
 // rows = n_split * nq: one partial (o, m, l) row per split and query (none when n_split == 1);
 // kC16 / vC16: clusters of the key / value tables copied to fp16 for the fast decode (0: none)
-AttendWs attend_ws(int H, int64_t nq, int n_chunks, int64_t n_tiles, int64_t split_rows, int kC16, int vC16) {
+// krep_bytes: mix4 codes of the keys (64 bytes per token-head), 0 when the keys take another path
+AttendWs attend_ws(int H, int64_t nq, int n_chunks, int64_t n_tiles, int64_t split_rows, int kC16, int vC16,
+                   uint64_t krep_bytes) {
   AttendWs w;
   uint64_t off = 0;
   w.chunks = off;  off += align256((uint64_t)n_chunks * sizeof(ChunkRec));
@@ -185,6 +221,8 @@ AttendWs attend_ws(int H, int64_t nq, int n_chunks, int64_t n_tiles, int64_t spl
   w.k16 = off;     off += align256((uint64_t)n_chunks * H * kC16 * kHeadDim * 2);
   w.v16 = off;     off += align256((uint64_t)n_chunks * H * vC16 * kHeadDim * 2);
   w.range = off;   off += 256;
+  w.mix = off;     off += align256(sizeof(MixOrder));
+  w.krep = off;    off += align256(krep_bytes);
   w.bytes = off;
   return w;
 }
@@ -423,8 +461,12 @@ int qkv_workspace_bytes(const qkv_config* cfg, int64_t max_chunk_tokens, int64_t
   uint64_t need = 0;
   if (max_chunk_tokens > 0) need = std::max(need, quant_ws(cfg, max_chunk_tokens).bytes);
   if (n_query > 0 && n_chunks > 0) {
+    // mixed keys may take the mix4 path: room for their repacked codes
+    const uint64_t krep = cfg->n_int4_channels > 0
+                              ? (uint64_t)n_chunks * cfg->n_heads * (uint64_t)std::max<int64_t>(max_chunk_tokens, 1) * 64
+                              : 0;
     need = std::max(need, attend_ws(cfg->n_heads, n_query, n_chunks, max_tiles(std::max<int64_t>(max_chunk_tokens, 1), n_chunks),
-                                    max_split_rows(cfg->n_heads, n_query), kMaxClusters, kMaxClusters).bytes);
+                                    max_split_rows(cfg->n_heads, n_query), kMaxClusters, kMaxClusters, krep).bytes);
   }
   if (n_query > 0) need = std::max(need, psac_ws(cfg->n_heads));
   *out = (size_t)need;
@@ -539,9 +581,22 @@ int qkv_attend(const qkv_config* k_cfg, const qkv_config* v_cfg, const qkv_tenso
     return c->n_stages == 1 && c->n_int4_channels == 0 && c->bits == 2 && c->group % 32 == 0;
   };
   const bool kfast = fast(k_cfg), vfast = fast(v_cfg);
-  const int kC16 = kfast ? k_cfg->n_clusters : 0, vC16 = vfast ? v_cfg->n_clusters : 0;
-  const AttendWs ws = attend_ws(H, Nq, n_chunks, n_tiles, ns > 1 ? (int64_t)ns * Nq : 0, kC16, vC16);
+  // mixed INT4/INT2 keys of one stage: the mix4 path when their groups allow it
+  MixOrder mix{};
+  const bool kmix = !kfast && k_cfg->n_stages == 1 && k_cfg->n_int4_channels > 0 && k_cfg->psac_rank == 0 &&
+                    q->dtype == QKV_BF16 && mix4_order(params_of(k_cfg), &mix);
+  const int kmode = kfast ? 1 : kmix ? 2 : 0;
+  const int kC16 = kmode ? k_cfg->n_clusters : 0, vC16 = vfast ? v_cfg->n_clusters : 0;
+  const AttendWs ws = attend_ws(H, Nq, n_chunks, n_tiles, ns > 1 ? (int64_t)ns * Nq : 0, kC16, vC16,
+                                kmix ? (uint64_t)H * Nk * 64 : 0);
   QKV_TRY(check_ws(workspace, workspace_bytes, ws.bytes, fn));
+  if (kmix) {
+    uint64_t off = 0;
+    for (int i = 0; i < n_chunks; ++i) {
+      recs[i].krep = at(workspace, ws.krep + off);
+      off += (uint64_t)H * recs[i].n * 64;
+    }
+  }
 
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   ChunkRec* drecs = reinterpret_cast<ChunkRec*>(at(workspace, ws.chunks));
@@ -552,18 +607,23 @@ int qkv_attend(const qkv_config* k_cfg, const qkv_config* v_cfg, const qkv_tenso
     b.first = first;
     b.count = std::min(kChunkBatch, n_chunks - first);
     for (int i = 0; i < b.count; ++i) b.rec[i] = recs[first + i];
-    QKV_HIP(launch_upload_chunks(b, drecs, range, s));
+    QKV_HIP(launch_upload_chunks(b, drecs, range, mix, kmix ? reinterpret_cast<MixOrder*>(at(workspace, ws.mix)) : nullptr,
+                                 s));
   }
+  const MixOrder* dmix = kmix ? reinterpret_cast<const MixOrder*>(at(workspace, ws.mix)) : nullptr;
+  int64_t max_n = 0;
+  for (int i = 0; i < n_chunks; ++i) max_n = std::max<int64_t>(max_n, recs[i].n);
+  if (kmix) QKV_HIP(launch_repack_mix(drecs, n_chunks, (int)max_n, params_of(k_cfg), dmix, s));
   // operand range of the fp16 MFMAs: largest stored scale, centroid, PSAC
   // coefficient and query (the kernels below derive their power-of-two scaling from it)
   QKV_HIP(launch_range_scan(drecs, n_chunks, params_of(k_cfg), params_of(v_cfg), view_of(q), (int)Nq, range, s));
   TileRec* dtiles = reinterpret_cast<TileRec*>(at(workspace, ws.tiles));
-  uint16_t* k16 = kfast ? reinterpret_cast<uint16_t*>(at(workspace, ws.k16)) : nullptr;
+  uint16_t* k16 = kmode ? reinterpret_cast<uint16_t*>(at(workspace, ws.k16)) : nullptr;
   uint16_t* v16 = vfast ? reinterpret_cast<uint16_t*>(at(workspace, ws.v16)) : nullptr;
-  QKV_HIP(launch_centroids_f16(drecs, n_chunks, params_of(k_cfg), params_of(v_cfg), range, k16, v16, s));
+  QKV_HIP(launch_centroids_f16(drecs, n_chunks, params_of(k_cfg), params_of(v_cfg), range, dmix, k16, v16, s));
   {
     const ChunkDecode dk = make_decode(params_of(k_cfg), 1, nullptr), dv = make_decode(params_of(v_cfg), 1, nullptr);
-    const TokenBytes tb{dk.words * 4, dv.words * 4, dk.groups * 2, dv.groups * 2, k_cfg->psac_rank * 2};
+    const TokenBytes tb{kmix ? 64 : dk.words * 4, dv.words * 4, dk.groups * 2, dv.groups * 2, k_cfg->psac_rank * 2};
     QKV_HIP(launch_tile_table(drecs, n_chunks, (int)n_tiles, tb, H, k_cfg->n_clusters, v_cfg->n_clusters, k16, v16,
                               dtiles, s));
   }
@@ -592,7 +652,8 @@ int qkv_attend(const qkv_config* k_cfg, const qkv_config* v_cfg, const qkv_tenso
   a.out_stride_head = out->stride_head;
   a.logits = logits_debug;
   a.range = range;
-  a.k_uniform_int2_1stage = kfast;
+  a.k_mode = kmode;
+  a.mixp = dmix;
   a.v_uniform_int2_1stage = vfast;
   QKV_HIP(launch_attend(a, s));
   return ok();
