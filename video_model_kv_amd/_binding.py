@@ -13,7 +13,9 @@ import os
 from dataclasses import dataclass
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libqkv.so")
+# QKV_LIB_PATH selects another build of the library (the sanitizer tests load a
+# host-only instrumented build this way)
+LIB_PATH = os.environ.get("QKV_LIB_PATH") or os.path.join(HERE, "libqkv.so")
 
 QKV_OK, QKV_EINVAL, QKV_EUNSUPPORTED, QKV_EDEVICE, QKV_EWORKSPACE = 0, 1, 2, 3, 4
 QKV_F32, QKV_BF16 = 0, 1
