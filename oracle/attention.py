@@ -12,9 +12,20 @@ Readings taken: the correction is added before the softmax scale; the scale is
 queries are the cached tokens themselves.  Everything is float64: logits,
 softmax and the probability-weighted sum of the float32 V_hat values.
 
+Autoregressive chunk step (QVG notes, "Research background": chunk-by-chunk
+generation with causal attention over a resident KV cache; "Method / Overall
+framework": the cache is written chunk by chunk; 2-bit trap explainer, opening:
+every new frame attends to all cached frames).  Readings taken: the queries of
+a step are the new chunk's own tokens; they see every cached (quantized) key and
+the new chunk's own keys, unquantized, of frames up to their own frame
+(frame-block causal); the PSAC term applies to cached keys only (fresh keys
+carry no quantization error).
+
 Pins (tests/test_oracle_attention.py): equality with
 torch.nn.functional.scaled_dot_product_attention in float64 on the CPU, and a
-pure-Python loop on tiny shapes.
+pure-Python loop on tiny shapes; for the chunk step, the one-frame and
+one-token special cases (full and token-causal attention) and a Python loop
+over the visibility rule.
 """
 from __future__ import annotations
 
@@ -60,3 +71,39 @@ def attend(q, k_hat, v_hat, coef=None, u=None, scale=None, causal=False, heads=N
                              None if coef is None else coef[:, h],
                              None if u is None else u[h], scale, causal)
     return out
+
+
+def fresh_visible(nq: int, n_cache: int, n_fresh: int, frame_tokens: int) -> np.ndarray:
+    """Visibility [nq, n_cache + n_fresh] of one autoregressive chunk step: query i
+    (token i of the new chunk) sees every cached key and fresh key j iff
+    j // frame_tokens <= i // frame_tokens."""
+    qf = np.arange(nq) // frame_tokens
+    kf = np.arange(n_fresh) // frame_tokens
+    fresh = kf[None, :] <= qf[:, None]
+    return np.concatenate([np.ones((nq, n_cache), bool), fresh], axis=1)
+
+
+def logits_fresh(q, k_hat_cache, k_fresh, frame_tokens: int, coef=None, u=None, scale=None):
+    """s [Nq, Nc + Nf] of a chunk step (float64), -inf where not visible; the PSAC
+    term (coef [Nc, r]) is added for the cached keys only."""
+    k_all = np.concatenate([np.asarray(k_hat_cache, np.float32).reshape(-1, np.asarray(k_fresh).shape[1]),
+                            np.asarray(k_fresh, np.float32)])
+    nc = k_all.shape[0] - np.asarray(k_fresh).shape[0]
+    c_all = None
+    if coef is not None and u is not None and np.asarray(u).shape[-1] > 0:
+        c_all = np.concatenate([np.asarray(coef, np.float64).reshape(nc, -1),
+                                np.zeros((k_all.shape[0] - nc, np.asarray(u).shape[-1]))])
+    s = logits(q, k_all, c_all, u if c_all is not None else None, scale)
+    vis = fresh_visible(s.shape[0], nc, k_all.shape[0] - nc, frame_tokens)
+    return np.where(vis, s, -np.inf)
+
+
+def attend_fresh(q, k_hat_cache, v_hat_cache, k_fresh, v_fresh, frame_tokens: int, coef=None, u=None, scale=None):
+    """O [Nq, d] of one autoregressive chunk step for one head (float64)."""
+    s = logits_fresh(q, k_hat_cache, k_fresh, frame_tokens, coef, u, scale)
+    m = s.max(axis=1, keepdims=True)
+    p = np.exp(s - m)
+    p = p / p.sum(axis=1, keepdims=True)
+    d = np.asarray(v_fresh).shape[1]
+    v_all = np.concatenate([np.asarray(v_hat_cache, np.float32).reshape(-1, d), np.asarray(v_fresh, np.float32)])
+    return p @ v_all.astype(np.float64)

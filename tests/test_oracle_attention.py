@@ -61,3 +61,49 @@ def test_psac_full_rank_recovers_exact_logits():
     assert np.allclose(s_corr, s_true, rtol=0, atol=1e-12)
     # rank 0: no correction
     assert np.array_equal(attention.logits(q, k_hat, coef[:, :0], u[:, :0]), attention.logits(q, k_hat))
+
+
+def test_chunk_step_special_cases():
+    """One frame per chunk: the fresh keys are all visible (full attention over
+    cache + chunk); one token per frame and no cache: token-causal attention."""
+    rng = np.random.default_rng(3)
+    d, nc, nf = 16, 11, 9
+    q = rng.standard_normal((nf, d)).astype(np.float32)
+    kc, vc = rng.standard_normal((nc, d)).astype(np.float32), rng.standard_normal((nc, d)).astype(np.float32)
+    kf, vf = rng.standard_normal((nf, d)).astype(np.float32), rng.standard_normal((nf, d)).astype(np.float32)
+    full = attention.attend_head(q, np.concatenate([kc, kf]), np.concatenate([vc, vf]))
+    assert np.allclose(attention.attend_fresh(q, kc, vc, kf, vf, frame_tokens=nf), full, rtol=1e-13, atol=1e-13)
+    empty = np.zeros((0, d), np.float32)
+    causal = attention.attend_head(q, kf, vf, causal=True)
+    assert np.allclose(attention.attend_fresh(q, empty, empty, kf, vf, frame_tokens=1), causal, rtol=1e-13, atol=1e-13)
+
+
+def test_chunk_step_python_loop_with_psac():
+    """Visibility by a Python loop: cached keys always, fresh key j iff its frame
+    j // F is at most the query's frame i // F; the PSAC term on cached keys only."""
+    rng = np.random.default_rng(4)
+    d, r, nc, nf, F = 4, 2, 3, 6, 2
+    q = rng.standard_normal((nf, d)).astype(np.float32)
+    kc, vc = rng.standard_normal((nc, d)).astype(np.float32), rng.standard_normal((nc, d)).astype(np.float32)
+    kf, vf = rng.standard_normal((nf, d)).astype(np.float32), rng.standard_normal((nf, d)).astype(np.float32)
+    u = np.linalg.qr(rng.standard_normal((d, r)))[0]
+    coef = rng.standard_normal((nc, r)).astype(np.float32)
+    o = attention.attend_fresh(q, kc, vc, kf, vf, F, coef, u, scale=0.5)
+    keys = [(kc[j], vc[j], coef[j], None) for j in range(nc)] + [(kf[j], vf[j], None, j) for j in range(nf)]
+    for i in range(nf):
+        s, vals = [], []
+        for k, v, c, jf in keys:
+            if jf is not None and jf // F > i // F:
+                continue
+            dot = sum(float(q[i, a]) * float(k[a]) for a in range(d))
+            if c is not None:
+                qu = [sum(float(q[i, a]) * u[a, b] for a in range(d)) for b in range(r)]
+                dot += sum(qu[b] * float(c[b]) for b in range(r))
+            s.append(0.5 * dot)
+            vals.append(v)
+        m = max(s)
+        p = [math.exp(x - m) for x in s]
+        z = sum(p)
+        for a in range(d):
+            ref = sum(p[j] / z * float(vals[j][a]) for j in range(len(s)))
+            assert o[i, a] == pytest.approx(ref, rel=1e-12, abs=1e-14)
