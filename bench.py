@@ -12,7 +12,10 @@ Default workload: the one-minute cache -- 288 latent frames of 1,560 tokens in
 72 chunks of 6,240 (449,280 tokens), 32 heads, d = 128, bf16; keys INT4 on the
 26 most query-sensitive channels and INT2 on the rest, values INT2, C = 256,
 groups of 32.  The 5 s, progressive and QuantWM caches are timed after it
-(fewer steps) and reported under "workloads".
+(fewer steps) and reported under "workloads".  Beside the step, "ar_rollout"
+times one autoregressive rollout over the same 72 chunks: per chunk, its 6,240
+queries attend over the packed cache plus its own bf16 keys (frame-block
+causal), then the chunk is quantized and appended (chunks/s).
 
 Prints one JSON line.  `value` is KV tokens per second through the whole step
 (tokens quantized into the cache and attended, inputs resident in HBM).  Extra
@@ -48,6 +51,7 @@ def parse():
     p.add_argument("--workload", type=int, default=5, help="headline workload id (2: 5 s cache, 3, 4, 5: one minute)")
     p.add_argument("--extra", default="2,3,4", help="workload ids timed after the headline ('' for none)")
     p.add_argument("--batch", type=int, default=12, help="problems per qkv_quantize_chunks call (1-16)")
+    p.add_argument("--no-ar", action="store_true", help="skip the autoregressive rollout of the headline workload")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--kernel-reps", type=int, default=5)
     p.add_argument("--copy-calibration", action="store_true",
@@ -112,6 +116,7 @@ class Run:
 
         for c, kb, vb in generated_chunks(cid, wl.n_chunks):
             xk[c], xv[c] = to_dev(kb), to_dev(vb)
+        self.xk, self.xv = xk, xv
         self.q = torch.from_numpy(synth.queries(wl)).to(torch.bfloat16).to(dev)
         self.stats = wl.qsac or wl.psac_rank > 0 or wl.n_int4 > 0
         self.side = (None, None, None)
@@ -199,6 +204,79 @@ class Run:
                         pack_tile += b
         return {"k_attend": ("mfma", att), "k_assign": ("mfma", assign), "k_update": ("hbm", upd),
                 "k_quant_pack_tile": ("hbm", pack_tile), "k_quant_pack": ("hbm", pack_generic)}
+
+
+def _gen_queries(args):
+    """Queries of chunk c's own tokens as bf16 bit patterns (worker process)."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+    from video_model_kv_amd import synth
+    cid, c = args
+    with threadpool_limits(limits=1):
+        q = synth.chunk_queries(synth.workload(cid), c)
+    return c, (q.view(np.uint32) >> 16).astype(np.uint16)
+
+
+def ar_rollout(run: Run) -> dict:
+    """One autoregressive rollout over every chunk of the workload: per chunk, the
+    chunk's queries attend over the packed cache plus the chunk's own bf16 keys
+    and values (frame-block causal), then K and V of the chunk are quantized (one
+    qkv_quantize_chunks call) and appended.  Times the whole rollout, and its
+    attention and write parts, with events on the launch stream."""
+    import multiprocessing as mp
+    from concurrent.futures import ProcessPoolExecutor
+
+    import numpy as np
+    qk, torch, wl = run.qk, run.torch, run.wl
+    dev = torch.device("cuda")
+    qs = [None] * wl.n_chunks
+    workers = max(1, min(16, host_cores(), wl.n_chunks))
+    with ProcessPoolExecutor(max_workers=workers, mp_context=mp.get_context("spawn")) as ex:
+        for c, bits in ex.map(_gen_queries, [(wl.cid, c) for c in range(wl.n_chunks)]):
+            qs[c] = torch.from_numpy(bits.view(np.int16)).to(dev).view(torch.bfloat16)
+    n_max = max(run.ntok)
+    ws = torch.empty(qk.qkv_workspace_bytes(run.kcfg, n_max, n_max, wl.n_chunks), dtype=torch.uint8, device=dev)
+    qws = torch.empty(qk.qkv_quantize_chunks_workspace_bytes(run.kcfg, n_max, 2), dtype=torch.uint8, device=dev)
+    out = torch.empty((n_max, wl.n_heads, 128), dtype=torch.float32, device=dev)
+    run.fit()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+           torch.cuda.Event(enable_timing=True)) for _ in range(wl.n_chunks)]
+
+    def rollout(n, record):
+        for c in range(n):
+            nf = run.ntok[c]
+            if record:
+                ev[c][0].record()
+            qk.qkv_attend_fresh(run.kcfg, run.vcfg, qs[c], run.kp[:c], run.vp[:c], run.ntok[:c], run.xk[c], run.xv[c],
+                                wl.tokens_per_frame, out[:nf], ws, U=run.side[2])
+            if record:
+                ev[c][1].record()
+            qk.qkv_quantize_chunks([run.kcfg, run.vcfg], [run.xk[c], run.xv[c]], [run.kp[c], run.vp[c]], qws,
+                                   sides=[run.side, None])
+            if record:
+                ev[c][2].record()
+
+    rollout(2, False)                            # warm-up
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    rollout(wl.n_chunks, True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    total = ev[0][0].elapsed_time(ev[-1][2]) * 1e-3
+    att = sum(e[0].elapsed_time(e[1]) for e in ev) * 1e-3
+    wr = sum(e[1].elapsed_time(e[2]) for e in ev) * 1e-3
+    d, H = 128, wl.n_heads
+    flops = 0.0
+    for c in range(wl.n_chunks):            # visible pairs: all cached keys, fresh keys of frames <= own frame
+        nf, nc, F = run.ntok[c], sum(run.ntok[:c]), wl.tokens_per_frame
+        fresh_pairs = sum(min(nf, (f + 1) * F) * min(F, nf - f * F) for f in range(-(-nf // F)))
+        flops += 4.0 * d * H * (nf * nc + fresh_pairs)
+    log(f"AR rollout: {wl.n_chunks} chunks in {total:.3f} s ({wl.n_chunks / total:.2f} chunks/s); "
+        f"attention {att:.3f} s ({flops / att / 1e12:.0f} TFLOP/s), write path {wr:.3f} s")
+    return {"chunks": wl.n_chunks, "seconds": total, "wall_seconds": wall, "chunks_per_s": wl.n_chunks / total,
+            "kv_tokens_per_s": run.nk / total, "attend_s": att, "attend_tflops": flops / att / 1e12,
+            "attend_flops": flops, "write_s": wr, "write_ms_per_chunk": wr / wl.n_chunks * 1e3,
+            "queries_per_step": "the chunk's own tokens", "mask": "frame-block causal over the fresh chunk"}
 
 
 def time_steps(run: Run, steps: int, warmup: int):
@@ -409,6 +487,12 @@ def main():
         "quantize_batches_per_step": len(run.batches), "problems_per_batch": a.batch,
         "kernels": prof,
     }
+    ar = None
+    if not a.no_ar:
+        try:
+            ar = ar_rollout(run)
+        except Exception as e:  # reported, never fatal to the headline measurement
+            log(f"AR rollout failed: {e}")
     cfgd = {"workload": wl.name, "heads": wl.n_heads, "head_dim": 128, "chunks": wl.n_chunks,
             "chunk_tokens": wl.chunk_tokens, "cache_tokens": run.nk, "clusters": wl.n_clusters,
             "kmeans_iters": wl.kmeans_iters, "stages": wl.n_stages, "bits": wl.bits, "group": wl.group,
@@ -449,7 +533,7 @@ def main():
                          "attention on fp16 MFMA with fp32 accumulation and softmax"),
         "data": "synthetic", "config": cfgd,
         "roofline": {k: v for k, v in dominant.items()},
-        "rooflines": roofs, "components": comp, "workloads": extras, "cpu_baseline": cpu,
+        "rooflines": roofs, "components": comp, "ar_rollout": ar, "workloads": extras, "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)
 

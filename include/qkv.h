@@ -257,6 +257,27 @@ int qkv_attend(const qkv_config* k_cfg, const qkv_config* v_cfg, const qkv_tenso
                float* logits_debug, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * One step of autoregressive chunk-by-chunk generation ([QVG] "Research
+ * background": causal attention over a resident KV-cache, chunk by chunk; [TRAP]
+ * opening: every new frame attends to all cached frames): the queries q
+ * [Nf][H][d] (bf16) of a new chunk attend over the n_chunks packed chunks of the
+ * cache (as qkv_attend; n_chunks may be 0) followed by the chunk's own keys and
+ * values k_fresh, v_fresh [Nf][H][d] (bf16 or f32, unquantized), with a
+ * frame-block causal mask: query i sees every cached key and fresh key j iff
+ * j / frame_tokens <= i / frame_tokens.  The PSAC term applies to the cached
+ * keys only.  Same outputs, softmax_scale, U, logits_debug ([H][Nf][Nk + Nf])
+ * and errors as qkv_attend; the workspace of qkv_workspace_bytes(k_cfg,
+ * max_chunk_tokens, Nf, n_chunks) covers a fresh chunk of at most
+ * max_chunk_tokens tokens.  QKV_EUNSUPPORTED for f32 queries.  The caller then
+ * quantizes the chunk (qkv_quantize_chunk(s)) and appends it to the cache.
+ */
+int qkv_attend_fresh(const qkv_config* k_cfg, const qkv_config* v_cfg, const qkv_tensor* q,
+                     const void* const* k_chunks, const void* const* v_chunks, const int64_t* chunk_tokens,
+                     int32_t n_chunks, const qkv_tensor* k_fresh, const qkv_tensor* v_fresh,
+                     int32_t frame_tokens, const float* U, float softmax_scale, const qkv_tensor* out,
+                     float* logits_debug, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Statistics of history queries q_hist [n][n_heads][d] (bf16 or f32) for QSAC and
  * PSAC ([QWM] "QuantWM", both techniques; [TRAP] section five for the
  * ranking):  M_h = sum_n q q^T (float64 on the device);

@@ -73,34 +73,37 @@ def attend(q, k_hat, v_hat, coef=None, u=None, scale=None, causal=False, heads=N
     return out
 
 
-def fresh_visible(nq: int, n_cache: int, n_fresh: int, frame_tokens: int) -> np.ndarray:
+def fresh_visible(nq: int, n_cache: int, n_fresh: int, frame_tokens: int, q_index=None) -> np.ndarray:
     """Visibility [nq, n_cache + n_fresh] of one autoregressive chunk step: query i
-    (token i of the new chunk) sees every cached key and fresh key j iff
-    j // frame_tokens <= i // frame_tokens."""
-    qf = np.arange(nq) // frame_tokens
+    (token q_index[i] of the new chunk; default i) sees every cached key and fresh
+    key j iff j // frame_tokens <= q_index[i] // frame_tokens."""
+    qi = np.arange(nq) if q_index is None else np.asarray(q_index)
+    qf = qi // frame_tokens
     kf = np.arange(n_fresh) // frame_tokens
     fresh = kf[None, :] <= qf[:, None]
     return np.concatenate([np.ones((nq, n_cache), bool), fresh], axis=1)
 
 
-def logits_fresh(q, k_hat_cache, k_fresh, frame_tokens: int, coef=None, u=None, scale=None):
+def logits_fresh(q, k_hat_cache, k_fresh, frame_tokens: int, coef=None, u=None, scale=None, q_index=None):
     """s [Nq, Nc + Nf] of a chunk step (float64), -inf where not visible; the PSAC
-    term (coef [Nc, r]) is added for the cached keys only."""
+    term (coef [Nc, r]) is added for the cached keys only.  q_index: the chunk
+    token of each query row (a subset of the chunk's queries), default 0..Nq-1."""
     k_all = np.concatenate([np.asarray(k_hat_cache, np.float32).reshape(-1, np.asarray(k_fresh).shape[1]),
                             np.asarray(k_fresh, np.float32)])
     nc = k_all.shape[0] - np.asarray(k_fresh).shape[0]
     c_all = None
     if coef is not None and u is not None and np.asarray(u).shape[-1] > 0:
-        c_all = np.concatenate([np.asarray(coef, np.float64).reshape(nc, -1),
-                                np.zeros((k_all.shape[0] - nc, np.asarray(u).shape[-1]))])
+        r = np.asarray(u).shape[-1]
+        c_all = np.concatenate([np.asarray(coef, np.float64).reshape(nc, r), np.zeros((k_all.shape[0] - nc, r))])
     s = logits(q, k_all, c_all, u if c_all is not None else None, scale)
-    vis = fresh_visible(s.shape[0], nc, k_all.shape[0] - nc, frame_tokens)
+    vis = fresh_visible(s.shape[0], nc, k_all.shape[0] - nc, frame_tokens, q_index)
     return np.where(vis, s, -np.inf)
 
 
-def attend_fresh(q, k_hat_cache, v_hat_cache, k_fresh, v_fresh, frame_tokens: int, coef=None, u=None, scale=None):
+def attend_fresh(q, k_hat_cache, v_hat_cache, k_fresh, v_fresh, frame_tokens: int, coef=None, u=None, scale=None,
+                 q_index=None):
     """O [Nq, d] of one autoregressive chunk step for one head (float64)."""
-    s = logits_fresh(q, k_hat_cache, k_fresh, frame_tokens, coef, u, scale)
+    s = logits_fresh(q, k_hat_cache, k_fresh, frame_tokens, coef, u, scale, q_index)
     m = s.max(axis=1, keepdims=True)
     p = np.exp(s - m)
     p = p / p.sum(axis=1, keepdims=True)

@@ -27,11 +27,11 @@ QKV_STUB(hipError_t launch_gram(const TensorView&, int, double*, int, double*, h
 QKV_STUB(hipError_t launch_upload_chunks(const ChunkBatch&, ChunkRec*, uint32_t*, const MixOrder&, MixOrder*, hipStream_t))
 QKV_STUB(hipError_t launch_repack_mix(const ChunkRec*, int, int, const LayoutParams&, const MixOrder*, hipStream_t))
 QKV_STUB(hipError_t launch_range_scan(const ChunkRec*, int, const LayoutParams&, const LayoutParams&, const TensorView&,
-                                      int, uint32_t*, hipStream_t))
+                                      int, const TensorView&, const TensorView&, int, uint32_t*, hipStream_t))
 QKV_STUB(hipError_t launch_centroids_f16(const ChunkRec*, int, const LayoutParams&, const LayoutParams&, const uint32_t*,
                                          const MixOrder*, uint16_t*, uint16_t*, hipStream_t))
-QKV_STUB(hipError_t launch_tile_table(const ChunkRec*, int, int, TokenBytes, int, int, int, const uint16_t*,
-                                      const uint16_t*, TileRec*, hipStream_t))
+QKV_STUB(hipError_t launch_tile_table(const ChunkRec*, int, int, int, int, int64_t, TokenBytes, int, int, int,
+                                      const uint16_t*, const uint16_t*, TileRec*, hipStream_t))
 QKV_STUB(hipError_t launch_attend(const AttendArgs&, hipStream_t))
 QKV_STUB(hipError_t scratch_of_current_device(void**))
 

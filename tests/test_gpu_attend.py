@@ -221,7 +221,10 @@ def test_long_horizon_full_cache_sampled_queries():
     rest, values INT2, C = 256; 1,560 queries attend over the whole packed cache.
     The oracle quantizes heads 0 and 23 of every chunk itself (the packed bytes of
     both are compared bit for bit) and attends 65 sampled queries (every 24th) in
-    float64; logits of the first 64 queries are checked through the debug path."""
+    float64; logits of the first 64 queries are checked through the debug path.
+    Then one autoregressive step at full size: the last chunk's queries over the 71
+    packed chunks before it and its own unquantized keys (frame-block causal),
+    65 sampled queries on the same heads."""
     wl = synth.workload(5)
     H, heads, n = wl.n_heads, [0, 23], wl.n_chunks
     t = G.torch()
@@ -234,12 +237,15 @@ def test_long_horizon_full_cache_sampled_queries():
     wsv = G.workspace(vcfg, max(ntok))
     kch, vch, xk0, xv0 = [None] * n, [None] * n, [None] * n, [None] * n
     G.log(f"long-horizon: generating and quantizing {n} chunks x 2 tensors")
+    last = None
     for c, out in G.generated_chunks(5, n, heads):
         (kb, xk0[c]), (vb, xv0[c]) = out["K"], out["V"]
         kd = t.from_numpy(kb.view(np.int16)).to(G.dev()).view(t.bfloat16)
         vd = t.from_numpy(vb.view(np.int16)).to(G.dev()).view(t.bfloat16)
         kch[c] = G.quantize(kcfg, kd, perm=pd, ws=ws)
         vch[c] = G.quantize(vcfg, vd, ws=wsv)
+        if c == n - 1:
+            last = (kd, vd)                      # the fresh chunk of the autoregressive step below
         del kd, vd
     q = synth.queries(wl)
     qd = G.to_dev(q, wl.dtype)
@@ -283,3 +289,22 @@ def test_long_horizon_full_cache_sampled_queries():
               f"on {len(sample)} sampled queries over {k_hat.shape[0]} keys")
         assert e_log <= LOGIT_TOL, f"long-horizon h{h}: logits rel-L2 {e_log}"
         assert e_out <= OUT_TOL, f"long-horizon h{h}: output rel-L2 {e_out}"
+    # one autoregressive step at full size: the last chunk's 6,240 queries over the 71
+    # packed chunks before it plus its own bf16 keys and values (frame-block causal)
+    c = n - 1
+    qf = synth.chunk_queries(wl, c)
+    qfd = G.to_dev(qf, "bf16")
+    ws_f = G.workspace(kcfg, max(ntok), ntok[c], c)
+    out_f = t.empty((ntok[c], H, 128), dtype=t.float32, device=G.dev())
+    G.log(f"long-horizon AR step: {c} cached chunks + a fresh chunk of {ntok[c]} tokens")
+    qk.qkv_attend_fresh(kcfg, vcfg, qfd, kch[:c], vch[:c], ntok[:c], last[0], last[1], wl.tokens_per_frame, out_f, ws_f)
+    of = out_f.cpu().numpy()
+    sample = np.arange(0, ntok[c], 96)
+    for hi, h in enumerate(heads):
+        k_hat = np.concatenate([job(cc, hi, 0).x_hat for cc in range(c)])
+        v_hat = np.concatenate([job(cc, hi, 1).x_hat for cc in range(c)])
+        ref = oa.attend_fresh(qf[sample, h], k_hat, v_hat, xk0[c][:, hi], xv0[c][:, hi], wl.tokens_per_frame,
+                              q_index=sample)
+        e = G.rel_l2(of[sample, h], ref)
+        G.log(f"long-horizon AR step h{h}: output rel-L2 {e:.3g} on {len(sample)} sampled queries (tol {OUT_TOL})")
+        assert e <= OUT_TOL, f"long-horizon AR step h{h}: output rel-L2 {e}"

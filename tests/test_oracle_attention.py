@@ -107,3 +107,32 @@ def test_chunk_step_python_loop_with_psac():
         for a in range(d):
             ref = sum(p[j] / z * float(vals[j][a]) for j in range(len(s)))
             assert o[i, a] == pytest.approx(ref, rel=1e-12, abs=1e-14)
+
+
+def test_chunk_step_query_subset():
+    """Rows for a subset of the chunk's queries (q_index) equal those rows of the
+    whole step."""
+    rng = np.random.default_rng(5)
+    d, nc, nf, F = 8, 5, 12, 4
+    q = rng.standard_normal((nf, d)).astype(np.float32)
+    kc, vc = rng.standard_normal((nc, d)).astype(np.float32), rng.standard_normal((nc, d)).astype(np.float32)
+    kf, vf = rng.standard_normal((nf, d)).astype(np.float32), rng.standard_normal((nf, d)).astype(np.float32)
+    full = attention.attend_fresh(q, kc, vc, kf, vf, F)
+    idx = np.array([0, 3, 4, 11])
+    sub = attention.attend_fresh(q[idx], kc, vc, kf, vf, F, q_index=idx)
+    assert np.array_equal(sub, full[idx])
+
+
+def test_chunk_step_empty_cache_with_psac():
+    """First step of a rollout: no cached keys, so the PSAC term (which belongs to
+    cached keys only) has nothing to act on; one token per frame makes the step
+    token-causal attention over the fresh keys."""
+    rng = np.random.default_rng(6)
+    d, r, nf = 8, 3, 7
+    q = rng.standard_normal((nf, d)).astype(np.float32)
+    kf, vf = rng.standard_normal((nf, d)).astype(np.float32), rng.standard_normal((nf, d)).astype(np.float32)
+    u = np.linalg.qr(rng.standard_normal((d, r)))[0]
+    empty = np.zeros((0, d), np.float32)
+    o = attention.attend_fresh(q, empty, empty, kf, vf, 1, np.zeros((0, r), np.float32), u)
+    causal = attention.attend_head(q, kf, vf, causal=True)
+    assert np.allclose(o, causal, rtol=1e-13, atol=1e-13)

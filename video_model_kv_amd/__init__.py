@@ -7,7 +7,7 @@ chunk into typed views (``packed``), and the seeded synthetic inputs
 (``synth``).
 """
 from ._binding import (  # noqa: F401
-    Config, QkvError, qkv_attend, qkv_chunk_layout, qkv_dequantize, qkv_kmeans_assign,
+    Config, QkvError, qkv_attend, qkv_attend_fresh, qkv_chunk_layout, qkv_dequantize, qkv_kmeans_assign,
     qkv_kmeans_update, qkv_last_error, qkv_psac_fit, qkv_quant_pack, qkv_quantize_chunk, qkv_quantize_chunk_noalloc, qkv_quantize_chunks,
     qkv_quantize_chunks_workspace_bytes, qkv_timing_enable, qkv_timing_read, qkv_version, qkv_workspace_bytes, lib, tensor_desc, QKV_FLAG_RTN,
 )

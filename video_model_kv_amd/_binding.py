@@ -26,7 +26,7 @@ EXPORTED = [
     "qkv_quantize_chunk", "qkv_dequantize", "qkv_attend", "qkv_psac_fit",
     "qkv_kmeans_assign", "qkv_kmeans_update", "qkv_quant_pack",
     "qkv_quantize_chunks", "qkv_quantize_chunks_workspace_bytes", "qkv_quantize_chunk_noalloc",
-    "qkv_timing_enable", "qkv_timing_read",
+    "qkv_timing_enable", "qkv_timing_read", "qkv_attend_fresh",
 ]
 
 
@@ -122,6 +122,8 @@ def lib():
         L.qkv_quantize_chunks.argtypes = [i32, P(P(qkv_config)), P(P(qkv_tensor)), P(P(qkv_side)), P(vp), vp, sz, vp]
         L.qkv_quantize_chunks_workspace_bytes.argtypes = [P(qkv_config), i64, i32, P(sz)]
         L.qkv_quantize_chunk_noalloc.argtypes = [P(qkv_config), P(qkv_tensor), P(qkv_side), vp, vp]
+        L.qkv_attend_fresh.argtypes = [P(qkv_config), P(qkv_config), P(qkv_tensor), P(vp), P(vp), P(i64), i32,
+                                       P(qkv_tensor), P(qkv_tensor), i32, vp, ct.c_float, P(qkv_tensor), vp, vp, sz, vp]
         L.qkv_timing_enable.argtypes = [i32]
         L.qkv_timing_read.argtypes = [i32, P(qkv_kernel_time), P(i32)]
         for name in EXPORTED[2:]:
@@ -207,6 +209,19 @@ def qkv_attend(k_cfg: Config, v_cfg: Config, q, k_chunks, v_chunks, chunk_tokens
                             _ptr(U), 1 if causal else 0, float(softmax_scale), ct.byref(tensor_desc(out)),
                             _ptr(logits), _ptr(workspace), workspace.numel() * workspace.element_size(),
                             _stream(stream)))
+
+
+def qkv_attend_fresh(k_cfg: Config, v_cfg: Config, q, k_chunks, v_chunks, chunk_tokens, k_fresh, v_fresh,
+                     frame_tokens: int, out, workspace, U=None, softmax_scale: float = 0.0, logits=None, stream=None):
+    n = len(k_chunks)
+    m = max(n, 1)
+    kp = (ct.c_void_p * m)(*[c.data_ptr() for c in k_chunks])
+    vp_ = (ct.c_void_p * m)(*[c.data_ptr() for c in v_chunks])
+    nt = (ct.c_int64 * m)(*[int(x) for x in chunk_tokens])
+    _check(lib().qkv_attend_fresh(ct.byref(k_cfg.c()), ct.byref(v_cfg.c()), ct.byref(tensor_desc(q)), kp, vp_, nt, n,
+                                  ct.byref(tensor_desc(k_fresh)), ct.byref(tensor_desc(v_fresh)), int(frame_tokens),
+                                  _ptr(U), float(softmax_scale), ct.byref(tensor_desc(out)), _ptr(logits),
+                                  _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
 
 
 def qkv_psac_fit(q_hist, n_heads: int, rank: int, n_int4: int, workspace, U_out=None, w_out=None,

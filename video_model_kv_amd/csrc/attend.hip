@@ -27,6 +27,7 @@
 // k-step: [coef | coef] against [hi(qU) | lo(qU)].  Splits are merged with the
 // usual log-sum-exp rescaling.
 #include <algorithm>
+#include <climits>
 #include <cstddef>
 #include <utility>
 
@@ -193,6 +194,8 @@ __device__ __forceinline__ RangeExps range_exps(P rg, const LayoutParams& kp, co
   e.ek = range_exp(code_bound(kp, __uint_as_float(rg[kRgKScale]), __uint_as_float(rg[kRgKCent])));
   e.ev = range_exp(code_bound(vp, __uint_as_float(rg[kRgVScale]), __uint_as_float(rg[kRgVCent])));
   e.eq = range_exp(__uint_as_float(rg[kRgQ]));
+  e.ek = max(e.ek, range_exp(__uint_as_float(rg[kRgKFresh])));   // a fresh chunk's keys and values enter as they are
+  e.ev = max(e.ev, range_exp(__uint_as_float(rg[kRgVFresh])));
   if (psac) {
     e.ek = max(e.ek, range_exp(__uint_as_float(rg[kRgCoef])));
     e.eq = max(e.eq, range_exp(__uint_as_float(rg[kRgQU])));
@@ -281,11 +284,39 @@ __device__ __forceinline__ void decode_mix4(uint32_t w, float slo, float shi, in
   }
 }
 
+// NCH values of a fresh-chunk row (token tok, head h, channels k0 ..), as float.
+template <int NCH>
+__device__ __forceinline__ void fresh_row(const TensorView& t, int tok, int h, int k0, float* v) {
+  const int64_t off = (int64_t)tok * t.stride_token + (int64_t)h * t.stride_head + k0;
+  if (t.dtype == 0) {
+    const float* p = reinterpret_cast<const float*>(t.ptr) + off;
+#pragma unroll
+    for (int e = 0; e < NCH; e += 4) {
+      const float4 x = *reinterpret_cast<const float4*>(p + e);
+      v[e] = x.x; v[e + 1] = x.y; v[e + 2] = x.z; v[e + 3] = x.w;
+    }
+  } else {
+    const uint16_t* p = reinterpret_cast<const uint16_t*>(t.ptr) + off;
+    uint32_t w[NCH / 2];
+    if constexpr (NCH == 8) {
+      const uint4 x = *reinterpret_cast<const uint4*>(p);
+      w[0] = x.x; w[1] = x.y; w[2] = x.z; w[3] = x.w;
+    } else {
+      const uint2 x = *reinterpret_cast<const uint2*>(p);
+      w[0] = x.x; w[1] = x.y;
+    }
+#pragma unroll
+    for (int e = 0; e < NCH; ++e) v[e] = bf16_bits_to_f32((w[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
+  }
+}
+
 // KM: key decode mode -- 0 generic (every layout), 1 one uniform INT2 stage,
 // 2 one mixed INT4/INT2 stage through the mix4 pre-pass.
-template <bool QF32, int KM, bool VFAST, bool LOGITS, bool PSAC>
+// FRESH: the keys end with a fresh chunk (unquantized rows, frame-block mask).
+template <bool QF32, int KM, bool VFAST, bool LOGITS, bool PSAC, bool FRESH>
 __global__ __launch_bounds__(kThreads) void k_attend(AttendArgs a) {
   constexpr bool KFAST = KM != 0;                // keys through the copy ring and the LDS staging
+  static_assert(!FRESH || !QF32, "fresh chunks: bf16 queries");
   static_assert(KM != 2 || (!QF32 && !PSAC), "mix4 keys: bf16 queries, no PSAC term");
   constexpr int kKW = KM == 2 ? 16 : 8;          // K code words per key in the ring
   constexpr int kKGm = KM == 2 ? kMix4MaxGroups : 4;   // K scale groups per key (at most)
@@ -325,6 +356,12 @@ __global__ __launch_bounds__(kThreads) void k_attend(AttendArgs a) {
   const bool wave_active = wq_first < a.Nq;
   const int qrow = wq_first + col;             // this lane's query
   const bool qok = qrow < a.Nq;
+  // visibility (causal modes): key j is visible to query i iff j < vis_end(i)
+  // (token-causal: i + 1; with a fresh chunk: mask_base + (i / F + 1) F)
+  auto vis_end = [&](int i) __attribute__((always_inline)) -> int {
+    if constexpr (FRESH) return a.mask_base + (i / a.mask_F + 1) * a.mask_F;
+    return i + 1;
+  };
 
   // operand scaling of this call (scalar loads of the range record)
   const RangeExps rx = range_exps((crange_ptr)a.range, a.kp, a.vp, PSAC);
@@ -408,7 +445,7 @@ __global__ __launch_bounds__(kThreads) void k_attend(AttendArgs a) {
 
   // causal: drop trailing tiles wholly above the diagonal (unless debug logits are requested)
   if (a.causal && !LOGITS) {
-    while (t_end > t_begin && tiles[t_end - 1].kstart > q_last) --t_end;
+    while (t_end > t_begin && tiles[t_end - 1].kstart >= vis_end(q_last)) --t_end;
   }
   if (t_begin >= t_end) {
     // nothing visible in this split: write an empty partial
@@ -497,6 +534,7 @@ __global__ __launch_bounds__(kThreads) void k_attend(AttendArgs a) {
   };
   struct DecodeView {                            // tile i+1
     int lead[2], nvalid;                         // lead in scales (2 bytes)
+    int fresh, ftok0;                            // a fresh-chunk tile and its first token there
   };
   auto raw_view = [&](int j, bool live) __attribute__((always_inline)) -> RawView {
     const RawRole q = raw_role();
@@ -522,6 +560,8 @@ __global__ __launch_bounds__(kThreads) void k_attend(AttendArgs a) {
     w.lead[0] = lead_of(m32(j, kFSrc + 2) + hrow * (uint32_t)(2 * kGn)) >> 1;   // src[0][1]: K scales
     w.lead[1] = lead_of(m32(j, kFSrc + 8) + (hrow << (vGs + 1))) >> 1;   // src[1][1]: V scales
     w.nvalid = live ? (int)m32(j, kFNvalid) : 0;
+    w.fresh = FRESH && j >= a.n_cache_tiles;
+    w.ftok0 = FRESH ? (j - a.n_cache_tiles) * kKTile : 0;
     return w;
   };
 
@@ -592,7 +632,12 @@ __global__ __launch_bounds__(kThreads) void k_attend(AttendArgs a) {
       uint32_t o4[4];
       // keys past nvalid decode stale LDS contents (zero at the start, then
       // earlier tiles' values): finite, and their scores are masked (probability 0)
-      if constexpr (KM == 1) {
+      if (FRESH && D.fresh) {                    // a fresh-chunk tile: the keys as given, scaled
+        float v[8];
+        fresh_row<8>(a.kf, D.ftok0 + min(key, nvalid - 1), h, k0, v);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o4[e] = pack_f16x2(v[2 * e] * ksc, v[2 * e + 1] * ksc);
+      } else if constexpr (KM == 1) {
         const uint32_t w = sRcK[r][key * 8 + (k0 >> 4)];
         const uint32_t sb = sRsK[r][klead + (key << kGs) + ((k0 << kGs) >> 7)];   // groups: powers of two
         const uint4 cr = *reinterpret_cast<const uint4*>(&sCentK[g][key * kHeadDim + k0]);
@@ -630,7 +675,12 @@ __global__ __launch_bounds__(kThreads) void k_attend(AttendArgs a) {
       for (int y = 0; y < 2; ++y) {
         const int key = 2 * kp + y;
         const bool ok = key < nvalid;
-        if constexpr (VFAST) {
+        if (FRESH && D.fresh) {
+          float v[4];
+          fresh_row<4>(a.vf, D.ftok0 + min(key, nvalid - 1), h, k0, v);
+          pr[y][0] = pack_f16x2(v[0] * vsc, v[1] * vsc);
+          pr[y][1] = pack_f16x2(v[2] * vsc, v[3] * vsc);
+        } else if constexpr (VFAST) {
           const uint32_t w = sRcV[r][key * 8 + (k0 >> 4)];
           const uint32_t sb = sRsV[r][vlead + (key << vGs) + ((k0 << vGs) >> 7)];
           const uint2 cr = *reinterpret_cast<const uint2*>(&sCentV[g][key * kHeadDim + k0]);
@@ -658,7 +708,7 @@ __global__ __launch_bounds__(kThreads) void k_attend(AttendArgs a) {
     }
     if (PSAC && tid < kKTile) {
       uint32_t f16w[4] = {0u, 0u, 0u, 0u};
-      if (tid < nvalid) {
+      if (tid < nvalid && !(FRESH && D.fresh)) { // fresh keys carry no correction
         const int rank = a.psac_rank;
         const uint16_t* cpp = reinterpret_cast<const uint16_t*>(m64(j, kFPsac)) + ((int64_t)h * (int)m32(j, kFN) + tid) * rank;
         float f[8];
@@ -676,8 +726,12 @@ __global__ __launch_bounds__(kThreads) void k_attend(AttendArgs a) {
   int q_chunk = -1;
   auto load_q_mix = [&](int ch) __attribute__((always_inline)) {
     const int lane = xtid & 63, half = lane >> 5;
-    const ChunkDecode d = make_decode(a.kp, recs[ch].n, recs[ch].kbase);
-    const uint8_t* prow = d.base + d.off_perm + (int64_t)h * kHeadDim;
+    // the fresh chunk's tiles (ch == n_chunks) hold keys in channel order
+    const uint8_t* prow = nullptr;
+    if (!FRESH || ch < a.n_chunks) {
+      const ChunkDecode d = make_decode(a.kp, recs[ch].n, recs[ch].kbase);
+      prow = d.base + d.off_perm + (int64_t)h * kHeadDim;
+    }
     const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q.ptr) + (int64_t)(qok ? qrow : 0) * a.q.stride_token +
                          (int64_t)h * a.q.stride_head;
 #pragma unroll
@@ -685,7 +739,10 @@ __global__ __launch_bounds__(kThreads) void k_attend(AttendArgs a) {
       f16x8 hv;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const int k = prow[sRho[s * 16 + half * 8 + e]] & (kHeadDim - 1);
+        const int P = s * 16 + half * 8 + e;
+        int k;
+        if constexpr (FRESH) k = prow ? prow[sRho[P]] & (kHeadDim - 1) : P;
+        else k = prow[sRho[P]] & (kHeadDim - 1);
         const float v = qok ? bf16_bits_to_f32(qp[k]) : 0.0f;
         hv[e] = (_Float16)__builtin_amdgcn_fmed3f(v * qsc, -kF16Max, kF16Max);
       }
@@ -702,8 +759,8 @@ __global__ __launch_bounds__(kThreads) void k_attend(AttendArgs a) {
         q_chunk = chunk;
       }
     }
-    if (a.causal && !LOGITS && kstart > wq_last) return;        // wholly above the diagonal
-    const bool need_mask = nvalid < kKTile || (a.causal && kstart + kKTile - 1 > wq_first);
+    if (a.causal && !LOGITS && kstart >= vis_end(wq_last)) return;     // wholly invisible to this wave
+    const bool need_mask = nvalid < kKTile || (a.causal && kstart + kKTile > vis_end(wq_first));
     // S^T = K_hat Q^T, both 32-key halves interleaved (fp16 operands, fp32 accumulation)
     f32x16 acc[2] = {f32x16{}, f32x16{}};
     // K fragments of step s + 1 are read from LDS while step s multiplies
@@ -746,10 +803,10 @@ __global__ __launch_bounds__(kThreads) void k_attend(AttendArgs a) {
       for (int r = 0; r < 16; ++r) sv[kb * 16 + r] = acc[kb][r];
     if (need_mask || LOGITS) {
       // key kl of element i is kc(i) + half*4; it is visible iff kl < nvalid and
-      // (causal) kstart + kl <= qrow, i.e. iff kc(i) < lim.  The select is done
-      // with integer bit operations, not per-element compare masks.
+      // (causal modes) kstart + kl < vis_end(qrow), i.e. iff kc(i) < lim.  The
+      // select is done with integer bit operations, not per-element compare masks.
       int lim = nvalid;
-      if (a.causal) lim = min(lim, qrow - kstart + 1);
+      if (a.causal) lim = min(lim, vis_end(qrow) - kstart);
       lim -= half * 4;
 #pragma unroll
       for (int i = 0; i < 32; ++i) {
@@ -815,6 +872,7 @@ __global__ __launch_bounds__(kThreads) void k_attend(AttendArgs a) {
   int gen_chunk = -1;
   auto tables_for = [&](int j) __attribute__((always_inline)) {
     if constexpr (!KFAST || !VFAST) {
+      if (FRESH && j >= a.n_cache_tiles) return; // fresh-chunk tiles need no tables
       const int chunk = tiles[j].chunk;
       if (chunk != gen_chunk) {
         __syncthreads();
@@ -854,11 +912,13 @@ __global__ __launch_bounds__(kThreads) void k_attend(AttendArgs a) {
   wait_dma();
   __syncthreads();
 #pragma unroll 1
-  for (int k = 0; k < 3 && t_begin + k < t_end; ++k) raw_copy(raw_view(t_begin + k, true), (r0 + k) % kRing);
+  for (int k = 0; k < 3 && t_begin + k < t_end; ++k)
+    if (!FRESH || t_begin + k < a.n_cache_tiles) raw_copy(raw_view(t_begin + k, true), (r0 + k) % kRing);
   wait_dma();
   __syncthreads();
-  cent_gather(gather_view(t_begin, true), r0, t_begin & 1);
-  if (t_begin + 1 < t_end) cent_gather(gather_view(t_begin + 1, true), (r0 + 1) % kRing, (t_begin + 1) & 1);
+  if (!FRESH || t_begin < a.n_cache_tiles) cent_gather(gather_view(t_begin, true), r0, t_begin & 1);
+  if (t_begin + 1 < t_end && (!FRESH || t_begin + 1 < a.n_cache_tiles))
+    cent_gather(gather_view(t_begin + 1, true), (r0 + 1) % kRing, (t_begin + 1) & 1);
   wait_dma();
   __syncthreads();
   tables_for(t_begin);
@@ -899,6 +959,8 @@ __global__ __launch_bounds__(kThreads) void k_attend(AttendArgs a) {
       DV.lead[0] = lead_of(w[4] + hrow * (uint32_t)(2 * kGn)) >> 1;   // K scales
       DV.lead[1] = lead_of(w[5] + (hrow << (vGs + 1))) >> 1;     // V scales
       DV.nvalid = has1 ? (int)w[2] : 0;
+      DV.fresh = FRESH && j1 >= a.n_cache_tiles;
+      DV.ftok0 = FRESH ? (j1 - a.n_cache_tiles) * kKTile : 0;
     }
     GatherView GV;
     {
@@ -920,8 +982,8 @@ __global__ __launch_bounds__(kThreads) void k_attend(AttendArgs a) {
     // after this wave's decode (its reads of the copy targets would otherwise
     // wait for them) and before its compute, which reads other LDS objects.
     auto issue = [&]() __attribute__((always_inline)) {
-      if (has2) cent_gather(GV, r2, ti & 1);
-      if (has3) raw_copy(RV, r3);
+      if (has2 && (!FRESH || j2 < a.n_cache_tiles)) cent_gather(GV, r2, ti & 1);
+      if (has3 && (!FRESH || j3 < a.n_cache_tiles)) raw_copy(RV, r3);
       if (xwave == 0 && ti + 5 < t_end) meta_copy(ti + 5);   // slot of tile i+5: read from step i+2 on
     };
 #pragma unroll 1
@@ -1039,10 +1101,22 @@ __global__ __launch_bounds__(256) void k_qu(TensorView q, int H, int Nq, int r, 
 
 // TileRec of every tile: the chunk holding it is the last one whose first tile is <= j.
 __global__ __launch_bounds__(256) void k_tile_table(const ChunkRec* __restrict__ recs, int n_chunks, int n_tiles,
+                                                    int n_cache_tiles, int n_fresh, int64_t fresh_start,
                                                     TokenBytes tb, int H, int kC, int vC, const uint16_t* k16,
                                                     const uint16_t* v16, TileRec* __restrict__ tiles) {
   const int j = blockIdx.x * blockDim.x + threadIdx.x;
   if (j >= n_tiles) return;
+  if (j >= n_cache_tiles) {                      // a tile of the fresh chunk: geometry only
+    TileRec t{};
+    const int token0 = (j - n_cache_tiles) * kKTile;
+    t.n = n_fresh;
+    t.nvalid = min(kKTile, n_fresh - token0);
+    t.kstart = (int)fresh_start + token0;
+    t.token0 = token0;
+    t.chunk = n_chunks;
+    tiles[j] = t;
+    return;
+  }
   int lo = 0, hi = n_chunks - 1;
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
@@ -1131,13 +1205,34 @@ __device__ __forceinline__ uint32_t bf16_absmax(const uint16_t* p, int64_t n, in
   return m << 16;
 }
 
+// Largest |x| (float32 bits) of a strided [rows / H][H][128] tensor: this
+// thread's share of a grid-stride pass over its uint4 words.
+__device__ __forceinline__ uint32_t tensor_absmax(const TensorView& t, int H, int64_t rows, int64_t start, int64_t step) {
+  uint32_t m = 0;
+  const int per_row = t.dtype == 0 ? 32 : 16;    // uint4 words per row of 128 values
+  for (int64_t i = start; i < rows * per_row; i += step) {
+    const int64_t row = i / per_row;
+    const int64_t off = (row / H) * t.stride_token + (row % H) * t.stride_head;
+    if (t.dtype == 0) {
+      const uint4 w = reinterpret_cast<const uint4*>(reinterpret_cast<const float*>(t.ptr) + off)[i % per_row];
+      m = max(m, max(max(w.x & 0x7FFFFFFFu, w.y & 0x7FFFFFFFu), max(w.z & 0x7FFFFFFFu, w.w & 0x7FFFFFFFu)));
+    } else {
+      const uint4 w = reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(t.ptr) + off)[i % per_row];
+      const uint32_t w4[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) m = max(m, max(w4[k] & 0x7FFFu, (w4[k] >> 16) & 0x7FFFu) << 16);
+    }
+  }
+  return m;
+}
+
 // Range scan.  blockIdx.y = 2 chunk + tensor for the chunks' stored scales,
-// centroids (every stage) and PSAC coefficients; blockIdx.y = 2 n_chunks for
-// the queries.  Each block reduces its share and adds it with one atomic max
-// per slot.
+// centroids (every stage) and PSAC coefficients; blockIdx.y = 2 n_chunks + 0,
+// 1, 2 for the queries, the fresh keys and the fresh values.  Each block reduces
+// its share and adds it with one atomic max per slot.
 __global__ __launch_bounds__(256) void k_range_scan(const ChunkRec* __restrict__ recs, int n_chunks, LayoutParams kp,
-                                                    LayoutParams vp, TensorView q, int Nq,
-                                                    uint32_t* __restrict__ range) {
+                                                    LayoutParams vp, TensorView q, int Nq, TensorView kf,
+                                                    TensorView vf, int n_fresh, uint32_t* __restrict__ range) {
   __shared__ uint32_t red[3][4];
   const int64_t start = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t step = (int64_t)gridDim.x * blockDim.x;
@@ -1157,23 +1252,10 @@ __global__ __launch_bounds__(256) void k_range_scan(const ChunkRec* __restrict__
     if (d.psac_rank > 0)
       m[2] = bf16_absmax(reinterpret_cast<const uint16_t*>(d.base + d.off_psac), (int64_t)d.H * d.N * d.psac_rank,
                          start, step);
-  } else {
-    // queries: rows of 128 values, 16 (bf16) or 32 (f32) uint4 words each
-    const int per_row = q.dtype == 0 ? 32 : 16;
-    const int64_t rows = (int64_t)Nq * kp.H;
-    for (int64_t i = start; i < rows * per_row; i += step) {
-      const int64_t row = i / per_row;
-      const int64_t off = (row / kp.H) * q.stride_token + (row % kp.H) * q.stride_head;
-      if (q.dtype == 0) {
-        const uint4 w = reinterpret_cast<const uint4*>(reinterpret_cast<const float*>(q.ptr) + off)[i % per_row];
-        m[2] = max(m[2], max(max(w.x & 0x7FFFFFFFu, w.y & 0x7FFFFFFFu), max(w.z & 0x7FFFFFFFu, w.w & 0x7FFFFFFFu)));
-      } else {
-        const uint4 w = reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(q.ptr) + off)[i % per_row];
-        const uint32_t w4[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-        for (int k = 0; k < 4; ++k) m[2] = max(m[2], max(w4[k] & 0x7FFFu, (w4[k] >> 16) & 0x7FFFu) << 16);
-      }
-    }
+  } else if (y == 2 * n_chunks) {
+    m[2] = tensor_absmax(q, kp.H, (int64_t)Nq * kp.H, start, step);
+  } else if (n_fresh > 0) {
+    m[2] = tensor_absmax(y == 2 * n_chunks + 1 ? kf : vf, kp.H, (int64_t)n_fresh * kp.H, start, step);
   }
 #pragma unroll
   for (int k = 0; k < 3; ++k)
@@ -1189,7 +1271,7 @@ __global__ __launch_bounds__(256) void k_range_scan(const ChunkRec* __restrict__
     const uint32_t r = max(max(red[k][0], red[k][1]), max(red[k][2], red[k][3]));
     int slot;
     if (y < 2 * n_chunks) slot = k == 2 ? kRgCoef : ((y & 1) ? (k == 0 ? kRgVScale : kRgVCent) : (k == 0 ? kRgKScale : kRgKCent));
-    else slot = k == 2 ? kRgQ : -1;
+    else slot = k != 2 ? -1 : y == 2 * n_chunks ? kRgQ : y == 2 * n_chunks + 1 ? kRgKFresh : kRgVFresh;
     if (slot >= 0 && r != 0u) atomicMax(range + slot, r);
   }
 }
@@ -1253,6 +1335,7 @@ hipError_t launch_upload_chunks(const ChunkBatch& b, ChunkRec* dst, uint32_t* ra
 
 hipError_t launch_repack_mix(const ChunkRec* recs, int n_chunks, int max_tokens, const LayoutParams& kp,
                              const MixOrder* mix, hipStream_t s) {
+  if (n_chunks <= 0 || max_tokens <= 0) return hipSuccess;
   TimedLaunch tl_("k_repack_mix", s);
   const int64_t per = (int64_t)kp.H * max_tokens;
   hipLaunchKernelGGL(k_repack_mix, dim3((unsigned)((per + kRepackRows - 1) / kRepackRows), (unsigned)n_chunks), dim3(256),
@@ -1262,11 +1345,13 @@ hipError_t launch_repack_mix(const ChunkRec* recs, int n_chunks, int max_tokens,
 
 
 hipError_t launch_range_scan(const ChunkRec* recs, int n_chunks, const LayoutParams& kp, const LayoutParams& vp,
-                             const TensorView& q, int Nq, uint32_t* range, hipStream_t s) {
+                             const TensorView& q, int Nq, const TensorView& kf, const TensorView& vf, int n_fresh,
+                             uint32_t* range, hipStream_t s) {
   TimedLaunch tl_("k_range_scan", s);
-  const int ys = 2 * n_chunks + 1;
+  const int ys = 2 * n_chunks + 3;
   const int bx = std::max(1, std::min(64, 2048 / ys));
-  hipLaunchKernelGGL(k_range_scan, dim3((unsigned)bx, (unsigned)ys), dim3(256), 0, s, recs, n_chunks, kp, vp, q, Nq, range);
+  hipLaunchKernelGGL(k_range_scan, dim3((unsigned)bx, (unsigned)ys), dim3(256), 0, s, recs, n_chunks, kp, vp, q, Nq, kf,
+                     vf, n_fresh, range);
   return hipGetLastError();
 }
 
@@ -1274,30 +1359,32 @@ hipError_t launch_centroids_f16(const ChunkRec* recs, int n_chunks, const Layout
                                 const uint32_t* range, const MixOrder* kmix, uint16_t* k16, uint16_t* v16,
                                 hipStream_t s) {
   TimedLaunch tl_("k_centroids_f16", s);
-  if (!k16 && !v16) return hipSuccess;
+  if ((!k16 && !v16) || n_chunks <= 0) return hipSuccess;
   const int64_t per = (int64_t)kp.H * std::max(k16 ? kp.C : 0, v16 ? vp.C : 0) * (kHeadDim / 8) * n_chunks;
   hipLaunchKernelGGL(k_centroids_f16, dim3((unsigned)((per + 255) / 256), 2), dim3(256), 0, s, recs, n_chunks, kp, vp,
                      range, kmix, k16, v16);
   return hipGetLastError();
 }
 
-hipError_t launch_tile_table(const ChunkRec* recs, int n_chunks, int n_tiles, TokenBytes tb, int H, int kC, int vC,
-                             const uint16_t* k16, const uint16_t* v16, TileRec* tiles, hipStream_t s) {
+hipError_t launch_tile_table(const ChunkRec* recs, int n_chunks, int n_tiles, int n_cache_tiles, int n_fresh,
+                             int64_t fresh_start, TokenBytes tb, int H, int kC, int vC, const uint16_t* k16,
+                             const uint16_t* v16, TileRec* tiles, hipStream_t s) {
   TimedLaunch tl_("k_tile_table", s);
   if (n_tiles <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k_tile_table, dim3((unsigned)((n_tiles + 255) / 256)), dim3(256), 0, s, recs, n_chunks, n_tiles, tb,
-                     H, kC, vC, k16, v16, tiles);
+  hipLaunchKernelGGL(k_tile_table, dim3((unsigned)((n_tiles + 255) / 256)), dim3(256), 0, s, recs, n_chunks, n_tiles,
+                     n_cache_tiles, n_fresh, fresh_start, tb, H, kC, vC, k16, v16, tiles);
   return hipGetLastError();
 }
 
 template <int F>
 void launch_attend_flags(const AttendArgs& a, dim3 grid, hipStream_t s) {
   constexpr int KM = (F & 32) ? 2 : (F & 2) ? 1 : 0;
-  hipLaunchKernelGGL((k_attend<(F & 1) != 0, KM, (F & 4) != 0, (F & 8) != 0, (F & 16) != 0>), grid,
+  hipLaunchKernelGGL((k_attend<(F & 1) != 0, KM, (F & 4) != 0, (F & 8) != 0, (F & 16) != 0, (F & 64) != 0>), grid,
                      dim3(kThreads), 0, s, a);
 }
 // flags: 1 fp32 queries, 2 K INT2 fast path, 4 V fast path, 8 debug logits,
-// 16 PSAC, 32 K mix4 path (only with bf16 queries and no PSAC)
+// 16 PSAC, 32 K mix4 path (only with bf16 queries and no PSAC), 64 a fresh
+// chunk (only with bf16 queries)
 template <int... F>
 void launch_attend_variant(int flags, const AttendArgs& a, dim3 grid, hipStream_t s, std::integer_sequence<int, F...>) {
   ((flags == F ? launch_attend_flags<F>(a, grid, s) : void()), ...);
@@ -1321,11 +1408,18 @@ hipError_t launch_attend(const AttendArgs& a, hipStream_t s) {
   const dim3 grid((unsigned)(q_tiles * a.n_split * a.H));
   const int flags = (a.q.dtype == 0 ? 1 : 0) | (a.k_mode == 1 ? 2 : 0) | (a.k_mode == 2 ? 32 : 0) |
                     (a.v_uniform_int2_1stage ? 4 : 0) |
-                    (a.logits ? 8 : 0) | (a.psac_rank > 0 ? 16 : 0);
+                    (a.logits ? 8 : 0) | (a.psac_rank > 0 ? 16 : 0) | (a.kf.ptr ? 64 : 0);
   {
     TimedLaunch tl_("k_attend", s);
-    if (flags & 32) launch_attend_variant(flags, a, grid, s, std::integer_sequence<int, 32, 36, 40, 44>{});
-    else launch_attend_variant(flags, a, grid, s, std::make_integer_sequence<int, 32>{});
+    if (flags & 64) {
+      launch_attend_variant(flags, a, grid, s,
+                            std::integer_sequence<int, 64, 68, 72, 76, 80, 84, 88, 92, 66, 70, 74, 78, 82, 86, 90, 94,
+                                                  96, 100, 104, 108>{});
+    } else if (flags & 32) {
+      launch_attend_variant(flags, a, grid, s, std::integer_sequence<int, 32, 36, 40, 44>{});
+    } else {
+      launch_attend_variant(flags, a, grid, s, std::make_integer_sequence<int, 32>{});
+    }
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.n_split == 1) return e;

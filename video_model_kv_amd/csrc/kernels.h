@@ -181,12 +181,13 @@ hipError_t launch_repack_mix(const ChunkRec* recs, int n_chunks, int max_tokens,
 // Range record of one attention call (device, kRangeWords words): the largest
 // magnitudes of the operands that enter the fp16 MFMAs, as float32 bit patterns
 // (non-negative floats order like their bits, so they combine by integer max).
-enum RangeSlot { kRgKScale = 0, kRgKCent, kRgVScale, kRgVCent, kRgQ, kRgCoef, kRgQU, kRangeWords };
+enum RangeSlot { kRgKScale = 0, kRgKCent, kRgVScale, kRgVCent, kRgQ, kRgCoef, kRgQU, kRgKFresh, kRgVFresh, kRangeWords };
 // Fills every slot but kRgQU (k_qu adds that one) from the chunks' stored scales,
-// centroids and PSAC coefficients and from the queries.
+// centroids and PSAC coefficients, from the queries and from the fresh keys and
+// values (n_fresh tokens; none when n_fresh == 0).
 hipError_t launch_range_scan(const ChunkRec* recs, int n_chunks, const LayoutParams& kp, const LayoutParams& vp,
-                             const TensorView& q, int Nq, uint32_t* range, hipStream_t s);
-// TileRec of every tile from the uploaded chunk records.
+                             const TensorView& q, int Nq, const TensorView& kf, const TensorView& vf, int n_fresh,
+                             uint32_t* range, hipStream_t s);
 // fp16 copies of the chunks' bf16 centroid tables ([chunk][H][C][128]), scaled
 // by the tensor's range exponent (2^-e, exact) and rounded to nearest even, for
 // the tensors decoded by the attention fast path; k16 / v16 may be NULL (tensor
@@ -195,8 +196,11 @@ hipError_t launch_centroids_f16(const ChunkRec* recs, int n_chunks, const Layout
                                 const uint32_t* range, const MixOrder* kmix, uint16_t* k16, uint16_t* v16,
                                 hipStream_t s);
 // Tile records; the fast-path centroid pointers go to k16 / v16 when given.
-hipError_t launch_tile_table(const ChunkRec* recs, int n_chunks, int n_tiles, TokenBytes tb, int H, int kC, int vC,
-                             const uint16_t* k16, const uint16_t* v16, TileRec* tiles, hipStream_t s);
+// Tiles n_cache_tiles .. n_tiles - 1 are the fresh chunk's (n_fresh tokens,
+// the first at global key index fresh_start): chunk = n_chunks, no packed data.
+hipError_t launch_tile_table(const ChunkRec* recs, int n_chunks, int n_tiles, int n_cache_tiles, int n_fresh,
+                             int64_t fresh_start, TokenBytes tb, int H, int kC, int vC, const uint16_t* k16,
+                             const uint16_t* v16, TileRec* tiles, hipStream_t s);
 
 struct AttendArgs {
   TensorView q;
@@ -209,7 +213,10 @@ struct AttendArgs {
   const float* U;                // [H][128][r] or null
   int psac_rank;
   float* qu;                     // workspace [H][Nq][8] f32
-  int causal;
+  int causal;                    // 1: key j visible to query i iff j < mask_base + (i / mask_F + 1) * mask_F
+  int mask_F, mask_base;         // (token-causal: 1 and 0; frame-block over a fresh chunk: frame tokens, cached keys)
+  TensorView kf, vf;             // the fresh chunk's keys and values ([Nf][H][128]; ptr null when none)
+  int n_cache_tiles;             // tiles of the packed chunks; tiles past them are the fresh chunk's
   float scale;
   int n_split;                   // split s covers tiles [n_tiles*s/n_split, n_tiles*(s+1)/n_split)
   float* part_o;                 // [n_split][H][Nq][128]

@@ -460,12 +460,13 @@ int qkv_workspace_bytes(const qkv_config* cfg, int64_t max_chunk_tokens, int64_t
     return fail(QKV_EINVAL, "qkv_workspace_bytes: negative size or n_chunks > %d", kMaxChunks);
   uint64_t need = 0;
   if (max_chunk_tokens > 0) need = std::max(need, quant_ws(cfg, max_chunk_tokens).bytes);
-  if (n_query > 0 && n_chunks > 0) {
+  if (n_query > 0) {
     // mixed keys may take the mix4 path: room for their repacked codes
     const uint64_t krep = cfg->n_int4_channels > 0
                               ? (uint64_t)n_chunks * cfg->n_heads * (uint64_t)std::max<int64_t>(max_chunk_tokens, 1) * 64
                               : 0;
-    need = std::max(need, attend_ws(cfg->n_heads, n_query, n_chunks, max_tiles(std::max<int64_t>(max_chunk_tokens, 1), n_chunks),
+    // tiles for one more chunk: the fresh chunk of qkv_attend_fresh
+    need = std::max(need, attend_ws(cfg->n_heads, n_query, n_chunks, max_tiles(std::max<int64_t>(max_chunk_tokens, 1), n_chunks + 1),
                                     max_split_rows(cfg->n_heads, n_query), kMaxClusters, kMaxClusters, krep).bytes);
   }
   if (n_query > 0) need = std::max(need, psac_ws(cfg->n_heads));
@@ -526,22 +527,43 @@ int qkv_dequantize(const qkv_config* cfg, int64_t n_tokens, const void* packed, 
   return ok();
 }
 
-int qkv_attend(const qkv_config* k_cfg, const qkv_config* v_cfg, const qkv_tensor* q, const void* const* k_chunks,
-               const void* const* v_chunks, const int64_t* chunk_tokens, int32_t n_chunks, const float* U,
-               int32_t causal, float softmax_scale, const qkv_tensor* out, float* logits_debug, void* workspace,
-               size_t workspace_bytes, void* stream) {
-  const char* fn = "qkv_attend";
-  QKV_TRY(check_config(k_cfg, "qkv_attend (k_cfg)"));
-  QKV_TRY(check_config(v_cfg, "qkv_attend (v_cfg)"));
+}  // extern "C"
+
+namespace {
+
+// qkv_attend and qkv_attend_fresh: kf/vf (may be NULL) is a fresh chunk whose
+// keys follow the packed chunks, seen by query i up to frame i / frame_tokens.
+int attend_impl(const char* fn, const qkv_config* k_cfg, const qkv_config* v_cfg, const qkv_tensor* q,
+                const void* const* k_chunks, const void* const* v_chunks, const int64_t* chunk_tokens,
+                int32_t n_chunks, const qkv_tensor* kf, const qkv_tensor* vf, int32_t frame_tokens, const float* U,
+                int32_t causal, float softmax_scale, const qkv_tensor* out, float* logits_debug, void* workspace,
+                size_t workspace_bytes, void* stream) {
+  QKV_TRY(check_config(k_cfg, fn));
+  QKV_TRY(check_config(v_cfg, fn));
   if (k_cfg->n_heads != v_cfg->n_heads) return fail(QKV_EINVAL, "%s: K and V head counts differ", fn);
   if (v_cfg->psac_rank != 0) return fail(QKV_EINVAL, "%s: PSAC applies to keys only (v_cfg->psac_rank != 0)", fn);
   const int H = k_cfg->n_heads;
-  QKV_TRY(check_tensor(q, H, "qkv_attend (q)"));
-  QKV_TRY(check_tensor(out, H, "qkv_attend (out)"));
+  QKV_TRY(check_tensor(q, H, fn));
+  QKV_TRY(check_tensor(out, H, fn));
   if (out->dtype != QKV_F32) return fail(QKV_EINVAL, "%s: out must be f32", fn);
   if (out->n_tokens != q->n_tokens) return fail(QKV_EINVAL, "%s: out and q token counts differ", fn);
-  if (n_chunks < 1 || n_chunks > kMaxChunks) return fail(QKV_EINVAL, "%s: n_chunks %d not in [1, %d]", fn, n_chunks, kMaxChunks);
-  if (!k_chunks || !v_chunks || !chunk_tokens) return fail(QKV_EINVAL, "%s: chunk arrays are NULL", fn);
+  const bool fresh = kf != nullptr;
+  if (n_chunks < (fresh ? 0 : 1) || n_chunks > kMaxChunks)
+    return fail(QKV_EINVAL, "%s: n_chunks %d not in [%d, %d]", fn, n_chunks, fresh ? 0 : 1, kMaxChunks);
+  if (n_chunks > 0 && (!k_chunks || !v_chunks || !chunk_tokens)) return fail(QKV_EINVAL, "%s: chunk arrays are NULL", fn);
+  int64_t n_fresh = 0;
+  if (fresh) {
+    QKV_TRY(check_tensor(kf, H, fn));
+    QKV_TRY(check_tensor(vf, H, fn));
+    n_fresh = kf->n_tokens;
+    if (vf->n_tokens != n_fresh) return fail(QKV_EINVAL, "%s: fresh keys and values hold different token counts", fn);
+    if (q->n_tokens != n_fresh)
+      return fail(QKV_EINVAL, "%s: the queries must be the fresh chunk's %lld tokens (got %lld)", fn, (long long)n_fresh,
+                  (long long)q->n_tokens);
+    if (frame_tokens < 1) return fail(QKV_EINVAL, "%s: frame_tokens %d must be >= 1", fn, frame_tokens);
+    if (q->dtype != QKV_BF16) return fail(QKV_EUNSUPPORTED, "%s: a fresh chunk needs bf16 queries", fn);
+    if (n_fresh > ((int64_t)1 << 24)) return fail(QKV_EINVAL, "%s: fresh chunk of %lld tokens", fn, (long long)n_fresh);
+  }
   if (k_cfg->psac_rank > 0 && !U) return fail(QKV_EINVAL, "%s: k_cfg->psac_rank > 0 needs U", fn);
   if (!std::isfinite(softmax_scale) || softmax_scale < 0.0f) return fail(QKV_EINVAL, "%s: softmax_scale must be >= 0", fn);
   const int64_t Nq = q->n_tokens;
@@ -572,8 +594,11 @@ int qkv_attend(const qkv_config* k_cfg, const qkv_config* v_cfg, const qkv_tenso
     Nk += n;
     n_tiles += (n + kTileKeys - 1) / kTileKeys;
   }
+  const int64_t Nk_cache = Nk, n_cache_tiles = n_tiles;
+  Nk += n_fresh;
+  n_tiles += (n_fresh + kTileKeys - 1) / kTileKeys;
   if (Nk > ((int64_t)1 << 31) - 1) return fail(QKV_EINVAL, "%s: the cache holds more than 2^31 tokens", fn);
-  if (causal && Nk != Nq) return fail(QKV_EINVAL, "%s: causal attention needs as many queries as cached keys", fn);
+  if (causal && !fresh && Nk != Nq) return fail(QKV_EINVAL, "%s: causal attention needs as many queries as cached keys", fn);
   // A workspace sized by qkv_workspace_bytes for at least these queries and
   // chunks always suffices: ns <= split_cap(H, Nq).
   const int ns = choose_splits(H, Nq, n_tiles);
@@ -610,13 +635,24 @@ int qkv_attend(const qkv_config* k_cfg, const qkv_config* v_cfg, const qkv_tenso
     QKV_HIP(launch_upload_chunks(b, drecs, range, mix, kmix ? reinterpret_cast<MixOrder*>(at(workspace, ws.mix)) : nullptr,
                                  s));
   }
+  if (n_chunks == 0) {                           // a fresh chunk alone: the upload still clears the range record
+    ChunkBatch b;
+    std::memset(&b, 0, sizeof b);
+    QKV_HIP(launch_upload_chunks(b, drecs, range, mix, nullptr, s));
+  }
   const MixOrder* dmix = kmix ? reinterpret_cast<const MixOrder*>(at(workspace, ws.mix)) : nullptr;
   int64_t max_n = 0;
   for (int i = 0; i < n_chunks; ++i) max_n = std::max<int64_t>(max_n, recs[i].n);
   if (kmix) QKV_HIP(launch_repack_mix(drecs, n_chunks, (int)max_n, params_of(k_cfg), dmix, s));
   // operand range of the fp16 MFMAs: largest stored scale, centroid, PSAC
   // coefficient and query (the kernels below derive their power-of-two scaling from it)
-  QKV_HIP(launch_range_scan(drecs, n_chunks, params_of(k_cfg), params_of(v_cfg), view_of(q), (int)Nq, range, s));
+  TensorView kfv{}, vfv{};
+  if (fresh) {
+    kfv = view_of(kf);
+    vfv = view_of(vf);
+  }
+  QKV_HIP(launch_range_scan(drecs, n_chunks, params_of(k_cfg), params_of(v_cfg), view_of(q), (int)Nq, kfv, vfv,
+                            (int)n_fresh, range, s));
   TileRec* dtiles = reinterpret_cast<TileRec*>(at(workspace, ws.tiles));
   uint16_t* k16 = kmode ? reinterpret_cast<uint16_t*>(at(workspace, ws.k16)) : nullptr;
   uint16_t* v16 = vfast ? reinterpret_cast<uint16_t*>(at(workspace, ws.v16)) : nullptr;
@@ -624,8 +660,8 @@ int qkv_attend(const qkv_config* k_cfg, const qkv_config* v_cfg, const qkv_tenso
   {
     const ChunkDecode dk = make_decode(params_of(k_cfg), 1, nullptr), dv = make_decode(params_of(v_cfg), 1, nullptr);
     const TokenBytes tb{kmix ? 64 : dk.words * 4, dv.words * 4, dk.groups * 2, dv.groups * 2, k_cfg->psac_rank * 2};
-    QKV_HIP(launch_tile_table(drecs, n_chunks, (int)n_tiles, tb, H, k_cfg->n_clusters, v_cfg->n_clusters, k16, v16,
-                              dtiles, s));
+    QKV_HIP(launch_tile_table(drecs, n_chunks, (int)n_tiles, (int)n_cache_tiles, (int)n_fresh, Nk_cache, tb, H,
+                              k_cfg->n_clusters, v_cfg->n_clusters, k16, v16, dtiles, s));
   }
 
   AttendArgs a;
@@ -642,7 +678,12 @@ int qkv_attend(const qkv_config* k_cfg, const qkv_config* v_cfg, const qkv_tenso
   a.U = U;
   a.psac_rank = k_cfg->psac_rank;
   a.qu = reinterpret_cast<float*>(at(workspace, ws.qu));
-  a.causal = causal ? 1 : 0;
+  a.causal = (causal || fresh) ? 1 : 0;
+  a.mask_F = fresh ? frame_tokens : 1;           // token-causal: key j visible to query i iff j < i + 1
+  a.mask_base = fresh ? (int)Nk_cache : 0;
+  a.kf = kfv;
+  a.vf = vfv;
+  a.n_cache_tiles = (int)n_cache_tiles;
   a.scale = softmax_scale > 0.0f ? softmax_scale : 1.0f / std::sqrt((float)kHeadDim);
   a.n_split = ns;
   a.part_o = reinterpret_cast<float*>(at(workspace, ws.part_o));
@@ -657,6 +698,28 @@ int qkv_attend(const qkv_config* k_cfg, const qkv_config* v_cfg, const qkv_tenso
   a.v_uniform_int2_1stage = vfast;
   QKV_HIP(launch_attend(a, s));
   return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int qkv_attend(const qkv_config* k_cfg, const qkv_config* v_cfg, const qkv_tensor* q, const void* const* k_chunks,
+               const void* const* v_chunks, const int64_t* chunk_tokens, int32_t n_chunks, const float* U,
+               int32_t causal, float softmax_scale, const qkv_tensor* out, float* logits_debug, void* workspace,
+               size_t workspace_bytes, void* stream) {
+  return attend_impl("qkv_attend", k_cfg, v_cfg, q, k_chunks, v_chunks, chunk_tokens, n_chunks, nullptr, nullptr, 0, U,
+                     causal, softmax_scale, out, logits_debug, workspace, workspace_bytes, stream);
+}
+
+int qkv_attend_fresh(const qkv_config* k_cfg, const qkv_config* v_cfg, const qkv_tensor* q,
+                     const void* const* k_chunks, const void* const* v_chunks, const int64_t* chunk_tokens,
+                     int32_t n_chunks, const qkv_tensor* k_fresh, const qkv_tensor* v_fresh, int32_t frame_tokens,
+                     const float* U, float softmax_scale, const qkv_tensor* out, float* logits_debug,
+                     void* workspace, size_t workspace_bytes, void* stream) {
+  if (!k_fresh || !v_fresh) return fail(QKV_EINVAL, "qkv_attend_fresh: k_fresh or v_fresh is NULL");
+  return attend_impl("qkv_attend_fresh", k_cfg, v_cfg, q, k_chunks, v_chunks, chunk_tokens, n_chunks, k_fresh, v_fresh,
+                     frame_tokens, U, 1, softmax_scale, out, logits_debug, workspace, workspace_bytes, stream);
 }
 
 int qkv_psac_fit(const qkv_tensor* q_hist, int32_t n_heads, int32_t rank, int32_t n_int4, float* U_out, float* w_out, uint8_t* perm_out,

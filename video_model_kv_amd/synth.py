@@ -234,6 +234,23 @@ def queries(wl: Workload, heads=None, n: int | None = None) -> np.ndarray:
     return round_to(np.stack(cols, 1), wl.dtype)
 
 
+def chunk_queries(wl: Workload, c: int, heads=None) -> np.ndarray:
+    """Queries of chunk c's own tokens float32 [N_c, H, d] (bf16 values) for one
+    autoregressive step: the workload's query process with a stream per chunk."""
+    heads = range(wl.n_heads) if heads is None else heads
+    t0, t1 = wl.chunk_range(c)
+    cols = []
+    for h in heads:
+        if wl.cid in (4, 5):
+            b = _orthogonal(wl, h)
+            a = _rng(wl.seed, h, TENSOR["Q"], ROLE["query"], c + 1).standard_normal((t1 - t0, wl.head_dim))
+            a[:, :8] *= np.sqrt(20.0)
+            cols.append(a @ b.T)
+        else:
+            cols.append(_rng(wl.seed, h, TENSOR["Q"], ROLE["query"], c + 1).standard_normal((t1 - t0, wl.head_dim)))
+    return round_to(np.stack(cols, 1), "bf16")
+
+
 def history_queries(wl: Workload, heads=None) -> np.ndarray:
     """History queries float32 [n_hist, H, d] (bf16 values) for QSAC/PSAC statistics."""
     heads = range(wl.n_heads) if heads is None else heads
