@@ -14,10 +14,13 @@
 // fp32(-2*w*c) is split into bf16 hi + lo (16
 // significant bits), bf16 tokens are exact operands, fp32 tokens are split
 // into hi + lo too (three products: hh, lh, hl); products are exact and the
-// sums are fp32.  The error of D' stays below ~1e-6 of ||y||_w^2 + ||c||_w^2;
-// every token whose two best screened values are closer than 2e-5 of that
-// scale is re-decided from float64 distances accumulated in channel order, so
-// the labels are those of the float64 definition (ties to the lowest index).
+// sums are fp32.  screen_threshold() bounds the screening error rigorously
+// (the derivation is beside it); every token whose two best screened values
+// are not farther apart than that bound is a close call.  At the end of the
+// kernel a second screened sweep over the close calls lists the centroids
+// within the bound of the best, and those are compared in the definition's
+// own float64 arithmetic (channel order, each operation rounded once).  So
+// the labels are those of the float64 definition, ties to the lowest index.
 #include <algorithm>
 #include <type_traits>
 
@@ -58,6 +61,37 @@ __global__ __launch_bounds__(256) void k_init(KmBatch b) {
     const int k = (threadIdx.x & 31) * 4 + e;
     c[((int64_t)h * C + j) * kHeadDim + k] = load1<F32>(y, (int64_t)j * step, h, k);
   }
+}
+
+// Screening bound of the assign.  For a token y and centroid c (weights
+// w >= 0; ||.|| the w-weighted norm) the screened value is s = cn + the fp32
+// MFMA sum of y times the bf16 pieces of fp32(-2 w c), cn = fp32(||c||^2).
+// Its error against ||c||^2 - 2<y, c> is at most kT * 2||y|| ||c|| +
+// kC * ||c||^2 (u = 2^-24; every fp32 addition inside the MFMAs taken as
+// rounded within 2u, in any order, so n summed terms add (n-1) 2u / (1 -
+// (n-1) 2u) of their magnitudes; Cauchy-Schwarz bounds sum |2 w y c| by
+// 2||y|| ||c||):
+//   bf16 tokens: the hi + lo pieces hold fp32(-2wc) to 2^-16, its rounding
+//     adds u, and the 257 accumulated terms add 3.06e-5 of cn + 1.008 T:
+//     kT = 4.7e-5, kC = 3.1e-5;
+//   fp32 tokens: the token's own split and the dropped lo*lo product add
+//     2 * 2^-16, and the 385 terms add 4.58e-5: kT = 9.3e-5, kC = 4.6e-5.
+// Let b be the screened winner, D the exact distances.  A centroid j with
+// D_j <= D_b has ||c_j|| <= ||y|| + sqrt(D_b) =: R (triangle inequality), as
+// has c_b, so e_b + e_j <= 4 kT ||y|| R + 2 kC R^2 = thr, and s_j <= s_b + thr.
+// Hence when every other screened value exceeds s_b + thr, b is the unique
+// minimiser of the exact distances -- and of the float64 ones of the
+// definition, whose ~1e-14 relative rounding the 2^-10 margin covers.
+// D_b <= s_b + ||y||^2 + e_b and e_b <= (kT + kC)(||y||^2 + cn_b) give R;
+// ||y||^2 (fp32 sums) carries a 2^-12 margin, and 2^-100 (1 + ||y||) covers
+// products below fp32's normal range.
+template <bool F32>
+__device__ __forceinline__ float screen_threshold(float yn, float s_b, float cn_b) {
+  constexpr float kT = F32 ? 9.3e-5f : 4.7e-5f, kC = F32 ? 4.6e-5f : 3.1e-5f;
+  const float ynu = yn * (1.0f + 0x1p-12f);
+  const float db = (fmaxf(s_b + ynu, 0.0f) + (kT + kC) * (ynu + cn_b)) * (1.0f + 0x1p-12f);
+  const float ry = sqrtf(ynu), r = ry + sqrtf(db);
+  return (4.0f * kT * ry * r + 2.0f * kC * r * r) * (1.0f + 0x1p-10f) + 0x1p-100f * (1.0f + ry);
 }
 
 // One wave per centroid: hi/lo planes of fp32(w*c) and the weighted norm.
@@ -103,6 +137,8 @@ constexpr int kAsgWaves = 8;
 constexpr int kAsgThreads = kAsgWaves * 64;
 constexpr int kAsgMaxC = 256;
 constexpr int kAsgList = 1024;        // LDS close-call list; beyond it a wave re-decides on the spot
+constexpr int kCand = 16;             // candidates listed per close call; more: decided over all centroids
+constexpr int kRsw = kAsgWaves * 32;  // close calls per round of the second sweep
 constexpr int kAsgCUs = 256;
 constexpr int kAsgUnitCost = 25;
 
@@ -122,9 +158,10 @@ __global__ __launch_bounds__(kAsgThreads) void k_assign(KmBatch b, int G) {
   __shared__ __attribute__((aligned(16))) float sW[kHeadDim];
   __shared__ int sAmb[kAsgList];
   __shared__ int sAmbN, sNext;
-  __shared__ double sWY[4][kHeadDim];
-  __shared__ double sRv[kAsgWaves][4];
-  __shared__ int sRj[kAsgWaves][4];
+  __shared__ float sAmbM[kAsgList], sAmbT[kAsgList];   // screened best and bound of each close call
+  __shared__ uint8_t sCand[kRsw][kCand];
+  __shared__ int sCandN[kRsw], sOvf[kRsw];
+  __shared__ int sOvfN;
   const uint32_t logical = xcd_remap(blockIdx.x, (uint32_t)(G * n_heads));
   const int h = logical / G, g = logical % G;
   const int N = (int)y.n_tokens;
@@ -199,6 +236,54 @@ __global__ __launch_bounds__(kAsgThreads) void k_assign(KmBatch b, int G) {
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
   }
+
+  // One wave decides token tok over all centroids, lanes over centroids, in
+  // the definition's arithmetic: the sum over channels, in order, of
+  // w_k (y_k - c_k)^2, each float64 operation rounded once; the lowest wins,
+  // ties to the lowest index.  Called wave-uniformly.
+  auto decide_all = [&](int tok) __attribute__((always_inline)) {
+    const int64_t off = (int64_t)tok * y.stride_token + (int64_t)h * y.stride_head + lane * 2;
+    float ya, yb;
+    if constexpr (F32) {
+      const float2 v = *reinterpret_cast<const float2*>(reinterpret_cast<const float*>(y.ptr) + off);
+      ya = v.x;
+      yb = v.y;
+    } else {
+      const uint32_t v = *reinterpret_cast<const uint32_t*>(y16 + off);
+      ya = bf16_bits_to_f32(v & 0xFFFFu);
+      yb = bf16_bits_to_f32(v >> 16);
+    }
+    double best = INFINITY;
+    int bj = 0;
+    for (int q = 0; q < kAsgMaxC / 64; ++q) {
+      const int j = q * 64 + lane;
+      const float* cr = cent + ((int64_t)h * C + min(j, C - 1)) * kHeadDim;
+      double dist = 0.0;
+#pragma unroll 8
+      for (int k = 0; k < kHeadDim; k += 2) {
+        const float yk0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, ya), k >> 1));
+        const float yk1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, yb), k >> 1));
+        const float2 cv = *reinterpret_cast<const float2*>(cr + k);
+        const double d0 = (double)yk0 - (double)cv.x, d1 = (double)yk1 - (double)cv.y;
+        dist += (double)sW[k] * (d0 * d0);
+        dist += (double)sW[k + 1] * (d1 * d1);
+      }
+      if (j < C && dist < best) {
+        best = dist;
+        bj = j;
+      }
+    }
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const double ov = __shfl_xor(best, o);
+      const int oj = __shfl_xor(bj, o);
+      if (ov < best || (ov == best && oj < bj)) {
+        best = ov;
+        bj = oj;
+      }
+    }
+    if (lane == 0) labels[(int64_t)h * N + tok] = (uint8_t)bj;
+  };
 
   for (int it = wave; it < nitems;) {
     const int sb = sb0 + kPer * it, nt = it < npair ? 2 : 1;
@@ -354,8 +439,8 @@ __global__ __launch_bounds__(kAsgThreads) void k_assign(KmBatch b, int G) {
 #pragma unroll
       for (int t = 0; t < NT; ++t) bidx[t] = rel[t] + Cp - 32 + half * 4;
       // Close calls -- the two best screened values within the screening
-      // error bound (generously 2e-5 of ||y||_w^2 + ||c||_w^2) -- are listed
-      // for the float64 re-decision at the end.
+      // error bound (screen_threshold) -- are listed for the float64
+      // re-decision at the end.
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
         const float o1 = __shfl_xor(b1[t], 32), o2 = __shfl_xor(b2[t], 32);
@@ -369,11 +454,16 @@ __global__ __launch_bounds__(kAsgThreads) void k_assign(KmBatch b, int G) {
         const int tok = tok0 + t * 32 + col;
         if (half == 0 && tok < N) {
           labels[(int64_t)h * N + tok] = (uint8_t)bidx[t];
-          const float thr = 2e-5f * (yn + sCn[bidx[t]]);
+          const float thr = screen_threshold<F32>(yn, b1[t], sCn[bidx[t]]);
           if (!(second - b1[t] > thr)) {
             const int slot = atomicAdd(&sAmbN, 1);
-            if (slot < kAsgList) sAmb[slot] = tok;
-            else spill = tok + 1;
+            if (slot < kAsgList) {
+              sAmb[slot] = tok;
+              sAmbM[slot] = b1[t];
+              sAmbT[slot] = thr;
+            } else {
+              spill = tok + 1;
+            }
           }
         }
       }
@@ -384,137 +474,168 @@ __global__ __launch_bounds__(kAsgThreads) void k_assign(KmBatch b, int G) {
       if (nt == 2) sweep(std::integral_constant<int, 2>{});
       else sweep(std::integral_constant<int, 1>{});
     }
-    // the list is full (a pathological input): this wave re-decides its
-    // overflowing close calls one at a time, lanes over centroids
+    // the list is full (a pathological input): this wave decides its
+    // overflowing close calls one at a time over all centroids
     for (uint64_t m = __ballot(spill != 0); m; m &= m - 1) {
       const int src = __builtin_ctzll(m);
-      const int tok = __builtin_amdgcn_readlane(spill, src) - 1;
-      const int64_t off = (int64_t)tok * y.stride_token + (int64_t)h * y.stride_head + lane * 2;
-      float ya, yb;
-      if constexpr (F32) {
-        const float2 v = *reinterpret_cast<const float2*>(reinterpret_cast<const float*>(y.ptr) + off);
-        ya = v.x;
-        yb = v.y;
-      } else {
-        const uint32_t v = *reinterpret_cast<const uint32_t*>(y16 + off);
-        ya = bf16_bits_to_f32(v & 0xFFFFu);
-        yb = bf16_bits_to_f32(v >> 16);
-      }
-      double best = INFINITY;
-      int bj = 0;
-      for (int q = 0; q < kAsgMaxC / 64; ++q) {
-        const int j = q * 64 + lane;
-        const float* cr = cent + ((int64_t)h * C + min(j, C - 1)) * kHeadDim;
-        double dist = 0.0;
-#pragma unroll 8
-        for (int k = 0; k < kHeadDim; k += 2) {
-          const float yk0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, ya), k >> 1));
-          const float yk1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, yb), k >> 1));
-          const float2 cv = *reinterpret_cast<const float2*>(cr + k);
-          const double d0 = (double)yk0 - (double)cv.x, d1 = (double)yk1 - (double)cv.y;
-          dist += (double)sW[k] * (d0 * d0);
-          dist += (double)sW[k + 1] * (d1 * d1);
-        }
-        if (j < C && dist < best) {
-          best = dist;
-          bj = j;
-        }
-      }
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const double ov = __shfl_xor(best, o);
-        const int oj = __shfl_xor(bj, o);
-        if (ov < best || (ov == best && oj < bj)) {
-          best = ov;
-          bj = oj;
-        }
-      }
-      if (lane == 0) labels[(int64_t)h * N + tok] = (uint8_t)bj;
+      decide_all(__builtin_amdgcn_readlane(spill, src) - 1);
     }
     it = next;
   }
 
-  // Close calls re-decided in float64, four tokens at a time: the distances
-  // differ from sum_j w_k c_jk^2 - 2 sum_k (w_k y_k) c_jk by the token's own
-  // norm, which does not move the argmin.  Thread t holds half (t & 1) of
-  // centroid row t >> 1 (fp32) and accumulates its 64 channels of both sums
-  // (products of fp32 values are exact in float64); the halves are joined,
-  // then the lowest value wins, ties to the lowest index.
+  // Close calls.  A second screened sweep over them (32 per wave, the same
+  // MFMAs) lists every centroid j with s_j - s_b <= thr: by the bound of
+  // screen_threshold these include every centroid whose exact distance is not
+  // above the winner's, so the float64 minimiser of the definition is among
+  // them.  The candidates are evaluated in the definition's arithmetic (the
+  // sum over channels, in order, of w_k (y_k - c_k)^2, each float64 operation
+  // rounded once) and the lowest wins, ties to the lowest index.  A token with
+  // more than kCand candidates is decided over all centroids by one wave.
   __syncthreads();
   const int n_amb = min(sAmbN, kAsgList);
-  if (n_amb > 0) {
-    if (tid == 0 && amb_count) atomicAdd(amb_count, n_amb);   // statistics only
-    const int j = tid >> 1, hk = (tid & 1) * 64;
-    const float* cr = cent + ((int64_t)h * C + min(j, C - 1)) * kHeadDim + hk;
-    for (int e0 = 0; e0 < n_amb; e0 += 4) {
-      {
-        const int q = tid >> 7, k = tid & 127;                // 4 tokens x 128 channels: w_k y_k
-        const int tok = sAmb[min(e0 + q, n_amb - 1)];
-        const int64_t off = (int64_t)tok * y.stride_token + (int64_t)h * y.stride_head + k;
-        const float yv = F32 ? reinterpret_cast<const float*>(y.ptr)[off] : bf16_bits_to_f32(y16[off]);
-        sWY[q][k] = (double)sW[k] * (double)yv;
+  if (n_amb > 0 && tid == 0 && amb_count) atomicAdd(amb_count, n_amb);   // statistics only
+  for (int e0 = 0; e0 < n_amb; e0 += kRsw) {
+    const int nloc = min(kRsw, n_amb - e0);
+    if (tid < kRsw) sCandN[tid] = 0;
+    if (tid == 0) sOvfN = 0;
+    __syncthreads();
+    if (wave * 32 < nloc) {                                  // wave-uniform
+      const int loc = wave * 32 + col;
+      const bool live = loc < nloc;
+      const int slot = e0 + min(loc, nloc - 1);
+      const int tok = sAmb[slot];
+      const float m1 = sAmbM[slot], thr = sAmbT[slot];
+      const int64_t base = (int64_t)tok * y.stride_token + hoff;
+      bf16x8 rh[8], rl[F32 ? 8 : 1];
+      if constexpr (F32) {
+        const float* p = reinterpret_cast<const float*>(y.ptr) + base;
+#pragma unroll
+        for (int sI = 0; sI < 8; ++sI) {
+          const float4 a = *reinterpret_cast<const float4*>(p + sI * 16);
+          const float4 b = *reinterpret_cast<const float4*>(p + sI * 16 + 4);
+          const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+          u16x8 hi, lo;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const uint32_t hb = f32_to_bf16_bits(v[e]);
+            hi[e] = (uint16_t)hb;
+            lo[e] = (uint16_t)f32_to_bf16_bits(v[e] - bf16_bits_to_f32(hb));
+          }
+          rh[sI] = __builtin_bit_cast(bf16x8, hi);
+          rl[sI] = __builtin_bit_cast(bf16x8, lo);
+        }
+      } else {
+#pragma unroll
+        for (int sI = 0; sI < 8; ++sI) rh[sI] = as_bf16x8(*reinterpret_cast<const uint4*>(y16 + base + sI * 16));
       }
-      __syncthreads();
-      // the row half streams in four groups of 16 channels, the next group's
-      // loads in flight during the current group's arithmetic
-      double d[4] = {0.0, 0.0, 0.0, 0.0}, cc = 0.0;
-      float4 cur[4], nxt[4];
+      for (int cb = 0; cb < Cp; cb += 32) {
+        f32x16 acc;
 #pragma unroll
-      for (int x = 0; x < 4; ++x) cur[x] = *reinterpret_cast<const float4*>(cr + 4 * x);
-#pragma unroll 1
-      for (int g = 0; g < 4; ++g) {
-        if (g < 3) {
-#pragma unroll
-          for (int x = 0; x < 4; ++x) nxt[x] = *reinterpret_cast<const float4*>(cr + 16 * (g + 1) + 4 * x);
+        for (int q = 0; q < 4; ++q) {
+          const float4 c4 = *reinterpret_cast<const float4*>(&sCn[cb + q * 8 + half * 4]);
+          acc[4 * q] = c4.x;
+          acc[4 * q + 1] = c4.y;
+          acc[4 * q + 2] = c4.z;
+          acc[4 * q + 3] = c4.w;
         }
 #pragma unroll
-        for (int x = 0; x < 4; ++x) {
-          const float cv[4] = {cur[x].x, cur[x].y, cur[x].z, cur[x].w};
+        for (int sI = 0; sI < 8; ++sI) {
+          const bf16x8 ahi = as_bf16x8(*reinterpret_cast<const uint4*>(&sP[0][cb + col][sI * 16 + half * 8]));
+          const bf16x8 alo = as_bf16x8(*reinterpret_cast<const uint4*>(&sP[1][cb + col][sI * 16 + half * 8]));
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahi, rh[sI], acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(alo, rh[sI], acc, 0, 0, 0);
+          if constexpr (F32) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahi, rl[F32 ? sI : 0], acc, 0, 0, 0);
+        }
 #pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            const int k = hk + 16 * g + 4 * x + u;
-            const double c64 = (double)cv[u];
-            cc = __builtin_fma((double)sW[k], c64 * c64, cc);
-#pragma unroll
-            for (int q = 0; q < 4; ++q) d[q] = __builtin_fma(sWY[q][k], c64, d[q]);
+        for (int r = 0; r < 16; ++r) {
+          const int j = cb + (r >> 2) * 8 + half * 4 + (r & 3);
+          if (live && j < C && acc[r] - m1 <= thr) {
+            const int n = atomicAdd(&sCandN[loc], 1);
+            if (n < kCand) sCand[loc][n] = (uint8_t)j;
           }
         }
-#pragma unroll
-        for (int x = 0; x < 4; ++x) cur[x] = nxt[x];
       }
-      cc += __shfl_xor(cc, 1);
+    }
+    __syncthreads();
+    {
+      // thread pair (loc, sub) evaluates candidates sub, sub + 2, ... of close call loc
+      const int loc = tid >> 1, sub = tid & 1;
+      if (loc < nloc) {
+        const int cnt = sCandN[loc];
+        const int tok = sAmb[e0 + loc];
+        if (cnt > kCand || cnt == 0) {                       // none: a NaN bound
+          if (sub == 0) sOvf[atomicAdd(&sOvfN, 1)] = tok;
+        } else {
+          constexpr int kMine = kCand / 2;
+          const int my = (cnt - sub + 1) >> 1;
+          double dist[kMine];
+          int jj[kMine];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        double v = cc - 2.0 * (d[q] + __shfl_xor(d[q], 1));
-        int bj = j;
-        if (j >= C) v = INFINITY;
+          for (int n = 0; n < kMine; ++n) {
+            dist[n] = 0.0;
+            jj[n] = n < my ? (int)sCand[loc][sub + 2 * n] : 0;
+          }
+          const int64_t base = (int64_t)tok * y.stride_token + (int64_t)h * y.stride_head;
+#pragma unroll 1
+          for (int g = 0; g < kHeadDim / 16; ++g) {
+            float yv[16];
+            if constexpr (F32) {
+              const float* p = reinterpret_cast<const float*>(y.ptr) + base + g * 16;
 #pragma unroll
-        for (int off = 2; off < 64; off <<= 1) {
-          const double ov = __shfl_xor(v, off);
-          const int oj = __shfl_xor(bj, off);
-          if (ov < v || (ov == v && oj < bj)) {
-            v = ov;
+              for (int x = 0; x < 4; ++x) {
+                const float4 v = *reinterpret_cast<const float4*>(p + 4 * x);
+                yv[4 * x] = v.x;
+                yv[4 * x + 1] = v.y;
+                yv[4 * x + 2] = v.z;
+                yv[4 * x + 3] = v.w;
+              }
+            } else {
+#pragma unroll
+              for (int e = 0; e < 16; ++e) yv[e] = bf16_bits_to_f32(y16[base + g * 16 + e]);
+            }
+#pragma unroll
+            for (int n = 0; n < kMine; ++n) {
+              if (n < my) {
+                const float* cr = cent + ((int64_t)h * C + jj[n]) * kHeadDim + g * 16;
+                float cv[16];
+#pragma unroll
+                for (int x = 0; x < 4; ++x) {
+                  const float4 v = *reinterpret_cast<const float4*>(cr + 4 * x);
+                  cv[4 * x] = v.x;
+                  cv[4 * x + 1] = v.y;
+                  cv[4 * x + 2] = v.z;
+                  cv[4 * x + 3] = v.w;
+                }
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                  const double df = (double)yv[e] - (double)cv[e];
+                  const double sq = df * df;
+                  dist[n] = dist[n] + (double)sW[g * 16 + e] * sq;
+                }
+              }
+            }
+          }
+          double best = INFINITY;
+          int bj = 0x7fffffff;
+#pragma unroll
+          for (int n = 0; n < kMine; ++n)
+            if (n < my && (dist[n] < best || (dist[n] == best && jj[n] < bj))) {
+              best = dist[n];
+              bj = jj[n];
+            }
+          const double ob = __shfl_xor(best, 1);
+          const int oj = __shfl_xor(bj, 1);
+          if (ob < best || (ob == best && oj < bj)) {
+            best = ob;
             bj = oj;
           }
-        }
-        if (lane == 0) {
-          sRv[wave][q] = v;
-          sRj[wave][q] = bj;
+          if (sub == 0) labels[(int64_t)h * N + tok] = (uint8_t)bj;
         }
       }
-      __syncthreads();
-      if (tid < 4 && e0 + tid < n_amb) {
-        double v = sRv[0][tid];
-        int bj = sRj[0][tid];
-        for (int x = 1; x < kAsgWaves; ++x)
-          if (sRv[x][tid] < v || (sRv[x][tid] == v && sRj[x][tid] < bj)) {
-            v = sRv[x][tid];
-            bj = sRj[x][tid];
-          }
-        labels[(int64_t)h * N + sAmb[e0 + tid]] = (uint8_t)bj;
-      }
-      __syncthreads();
     }
+    __syncthreads();
+    for (int o = wave; o < sOvfN; o += kAsgWaves) decide_all(sOvf[o]);   // block-uniform bound
+    __syncthreads();
   }
 }
 
