@@ -11,6 +11,9 @@ framework" and the two designs under "Key designs":
   5. progressive residual stages ("Progressive Residual Quantization"): the
      next stage's input is Y_{l+1} = fp32(Y_l - Yhat_l) and each stage runs its
      own k-means; X_hat = Yhat_1 + Yhat_2 + ... summed in float32 in stage order;
+  1a. with ``qsac_range`` the k-means weights of each stage are QSAC's weights
+     times the squared range of each channel of that stage's input
+     (oracle.psac.qsac_range_weights; QuantWM summary, first technique);
   6. PSAC encode (QuantWM summary, "QuantWM", second technique), keys only:
      e = fp32(K - K_hat) after all stages, coef = bf16(U^T e).
 A test-only switch ``rtn`` replaces steps 1-2 by zero centroids (plain
@@ -29,7 +32,7 @@ import numpy as np
 
 from . import kmeans as km
 from .numerics import bf16_rne
-from .psac import psac_coefficients
+from .psac import psac_coefficients, qsac_range_weights
 from .quant import channel_layout, quantize_groups, dequantize
 
 
@@ -55,8 +58,13 @@ class ProblemResult:
 
 def quantize_problem(x, n_clusters: int, bits: int, group: int, n_stages: int = 1,
                      iters: int = 10, w=None, n_int4: int = 0, perm=None, u=None,
-                     rtn: bool = False, track_objective: bool = False) -> ProblemResult:
-    """Quantize one (head, tensor) problem: x is float32 [N, d] (bf16 values allowed)."""
+                     rtn: bool = False, track_objective: bool = False,
+                     qsac_range: bool = False) -> ProblemResult:
+    """Quantize one (head, tensor) problem: x is float32 [N, d] (bf16 values allowed).
+    ``qsac_range`` (needs ``w``): each stage's k-means weights get the stage
+    input's squared channel ranges as a second factor."""
+    if qsac_range and w is None:
+        raise ValueError("qsac_range needs the QSAC weights w")
     x = np.asarray(x, dtype=np.float32)
     if not np.all(np.isfinite(x)):
         raise ValueError("non-finite input")
@@ -71,7 +79,8 @@ def quantize_problem(x, n_clusters: int, bits: int, group: int, n_stages: int = 
             cent = np.zeros((n_clusters, d), np.float32)
             trace = None
         else:
-            trace = km.kmeans(y, n_clusters, iters, w, track_objective=track_objective)
+            w_stage = qsac_range_weights(y, w) if qsac_range else w
+            trace = km.kmeans(y, n_clusters, iters, w_stage, track_objective=track_objective)
             labels, cent = trace.labels, trace.centroids
         c_bf = bf16_rne(cent)
         rows = c_bf[labels]
@@ -90,7 +99,7 @@ def quantize_problem(x, n_clusters: int, bits: int, group: int, n_stages: int = 
 
 def quantize_chunk(x, n_clusters: int, bits: int, group: int, n_stages: int = 1,
                    iters: int = 10, w=None, n_int4: int = 0, perm=None, u=None,
-                   rtn: bool = False, heads=None) -> dict:
+                   rtn: bool = False, heads=None, qsac_range: bool = False) -> dict:
     """All heads (or the listed ``heads``) of one chunk x [N, H, d].
 
     ``w`` [H, d], ``perm`` [H, d] and ``u`` [H, d, r] are per-head side inputs
@@ -103,7 +112,7 @@ def quantize_chunk(x, n_clusters: int, bits: int, group: int, n_stages: int = 1,
         out[h] = quantize_problem(
             x[:, h, :], n_clusters, bits, group, n_stages, iters,
             None if w is None else w[h], n_int4,
-            None if perm is None else perm[h], None if u is None else u[h], rtn)
+            None if perm is None else perm[h], None if u is None else u[h], rtn, qsac_range=qsac_range)
     return out
 
 

@@ -10,13 +10,23 @@ channel-sensitivity ranking (oracle; test infrastructure only).
   the trace.  The key residual error e is projected onto U and the r
   coefficients are stored (bf16 here; the page says only that they are
   stored quantized); attention adds (q U) . coef back to the logit.
+* QSAC's second factor (same section, first technique: besides the channels'
+  query activity, the clustering weighs the dynamic range of the residual being
+  quantized, and combines both).  Reading: the weight of channel k for the
+  k-means of one stage is w_k * rho_k^2, rho_k the range (max - min over the
+  chunk's tokens) of channel k of that stage's input -- the data at stage 1,
+  the previous stages' residual after -- since a channel's range sets its
+  group's quantization step.  In float32: rho = fl(max - min),
+  w_eff = fl(w * fl(rho * rho)).
 * Sensitivity ranking for mixed precision (2-bit trap explainer, section five;
   practitioner blog, section 3.2): the channels with the largest query energy
   w_k get 4 bits; ties go to the lower channel index.
 
 Pins (tests/test_oracle_psac.py): eigenvalues against a 2x2 closed form and
 numpy.linalg.eigh, the Ky Fan bound by random r-frames for d <= 6, projector
-idempotence, full-rank exactness of the corrected logits.
+idempotence, full-rank exactness of the corrected logits; the range weights by
+a hand-worked chunk, and weighted k-means with them equal to plain k-means on
+the chunk with each channel scaled by its range (powers of two, exact).
 """
 from __future__ import annotations
 
@@ -37,6 +47,14 @@ def qsac_weights(q: np.ndarray) -> np.ndarray:
     n, d = q64.shape
     sums = np.array([math.fsum((q64[:, k] * q64[:, k]).tolist()) for k in range(d)])
     return (sums / float(n)).astype(np.float32)
+
+
+def qsac_range_weights(y: np.ndarray, w: np.ndarray) -> np.ndarray:
+    """QSAC weights with the residual-range factor for one stage's input y
+    [N, d]: fl32(w_k * fl32(rho_k^2)), rho_k = fl32(max_i y_ik - min_i y_ik)."""
+    y = np.asarray(y, dtype=np.float32)
+    rho = (y.max(axis=0) - y.min(axis=0)).astype(np.float32)
+    return (np.asarray(w, np.float32) * (rho * rho).astype(np.float32)).astype(np.float32)
 
 
 def principal_subspace(m: np.ndarray, rank: int):

@@ -72,3 +72,42 @@ def test_synthetic_query_energy_closed_form():
     for h in range(2):
         _, _, e = psac.principal_subspace(psac.query_gram(hq[:, h]), 8)
         assert e == pytest.approx(160.0 / 280.0, abs=0.02)
+
+
+def test_qsac_range_weights_by_hand():
+    """Hand-worked chunk: channel ranges 4 - (-2) = 6 and 2 - (-3) = 5, squared
+    36 and 25, times the query weights 0.5 and 2."""
+    y = np.array([[1.0, -3.0], [4.0, 0.5], [-2.0, 2.0]], np.float32)
+    w = np.array([0.5, 2.0], np.float32)
+    assert np.array_equal(psac.qsac_range_weights(y, w), np.array([18.0, 50.0], np.float32))
+
+
+def _ranged_chunk(rng, n, exps):
+    """Channel k takes values 2^e_k * (u - 1/4), u on a 1/8 grid in [0, 1] with
+    both ends present: range exactly 2^e_k, and max |y| (3/4 of it) differs."""
+    u = rng.integers(0, 9, (n, len(exps))) / 8.0
+    u[0], u[1] = 0.0, 1.0
+    return ((u - 0.25) * (2.0 ** np.asarray(exps, np.float64))).astype(np.float32)
+
+
+def test_qsac_range_kmeans_equals_plain_kmeans_on_range_scaled_channels():
+    """With unit query weights the range factor weighs channel k by rho_k^2, so
+    the weighted distance equals the plain distance of the chunk with channel k
+    scaled by rho_k.  Ranges that are powers of two make both exact: labels and
+    (scaled) centroids must agree bit for bit, through the whole pipeline too."""
+    from oracle import kmeans as km
+    from oracle import pipeline as pl
+    rng = np.random.default_rng(41)
+    exps = [-3, 0, 2, 5, 1, -1, 4, 3]
+    y = _ranged_chunk(rng, 96, exps)
+    rho = (2.0 ** np.asarray(exps, np.float64)).astype(np.float32)
+    w_eff = psac.qsac_range_weights(y, np.ones(8, np.float32))
+    assert np.array_equal(w_eff, rho * rho)
+    a = km.kmeans(y, 6, 10, w_eff)
+    b = km.kmeans((y * rho).astype(np.float32), 6, 10, None)
+    assert np.array_equal(a.labels, b.labels)
+    assert np.array_equal((a.centroids * rho).astype(np.float32), b.centroids)
+    res = pl.quantize_problem(y, 6, 2, 4, 1, 10, w=np.ones(8, np.float32), qsac_range=True)
+    assert np.array_equal(res.stages[0].labels, b.labels)
+    plain = pl.quantize_problem(y, 6, 2, 4, 1, 10, w=np.ones(8, np.float32))
+    assert not np.array_equal(plain.stages[0].labels, b.labels), "the factor should change this clustering"
