@@ -76,22 +76,26 @@ __global__ __launch_bounds__(256) void k_init(KmBatch b) {
 //     kT = 4.7e-5, kC = 3.1e-5;
 //   fp32 tokens: the token's own split and the dropped lo*lo product add
 //     2 * 2^-16, and the 385 terms add 4.58e-5: kT = 9.3e-5, kC = 4.6e-5.
-// Let b be the screened winner, D the exact distances.  A centroid j with
-// D_j <= D_b has ||c_j|| <= ||y|| + sqrt(D_b) =: R (triangle inequality), as
-// has c_b, so e_b + e_j <= 4 kT ||y|| R + 2 kC R^2 = thr, and s_j <= s_b + thr.
-// Hence when every other screened value exceeds s_b + thr, b is the unique
-// minimiser of the exact distances -- and of the float64 ones of the
-// definition, whose ~1e-14 relative rounding the 2^-10 margin covers.
-// D_b <= s_b + ||y||^2 + e_b and e_b <= (kT + kC)(||y||^2 + cn_b) give R;
-// ||y||^2 (fp32 sums) carries a 2^-12 margin, and 2^-100 (1 + ||y||) covers
-// products below fp32's normal range.
+// Let b be the screened winner and D the exact distances.  e_b is bounded
+// with c_b's own norm.  A centroid j with D_j <= D_b has ||c_j|| <= ||y|| +
+// sqrt(D_b) (triangle inequality) and ||c_j|| <= the head's largest centroid
+// norm; with r the smaller of the two, e_j <= kT 2||y|| r + kC r^2.  So s_j <=
+// s_b + e_b + e_j <= s_b + thr, and when every other screened value exceeds
+// s_b + thr, b is the unique minimiser of the exact distances -- and of the
+// float64 ones of the definition, whose ~1e-14 relative rounding the 2^-40
+// term covers.  D_b <= s_b + ||y||^2 + e_b; ||y||^2 (fp32 sums) carries a
+// 2^-12 margin, cn and the largest norm 2^-20, the evaluation of thr 2^-10,
+// and 2^-100 (1 + ||y||) covers products below fp32's normal range.
 template <bool F32>
-__device__ __forceinline__ float screen_threshold(float yn, float s_b, float cn_b) {
+__device__ __forceinline__ float screen_threshold(float yn, float s_b, float cn_b, float cmax2) {
   constexpr float kT = F32 ? 9.3e-5f : 4.7e-5f, kC = F32 ? 4.6e-5f : 3.1e-5f;
-  const float ynu = yn * (1.0f + 0x1p-12f);
-  const float db = (fmaxf(s_b + ynu, 0.0f) + (kT + kC) * (ynu + cn_b)) * (1.0f + 0x1p-12f);
-  const float ry = sqrtf(ynu), r = ry + sqrtf(db);
-  return (4.0f * kT * ry * r + 2.0f * kC * r * r) * (1.0f + 0x1p-10f) + 0x1p-100f * (1.0f + ry);
+  const float ynu = yn * (1.0f + 0x1p-12f), ry = sqrtf(ynu);
+  const float cb = cn_b * (1.0f + 0x1p-20f);
+  const float eb = 2.0f * kT * ry * sqrtf(cb) + kC * cb;
+  const float db = (fmaxf(s_b + ynu, 0.0f) + eb) * (1.0f + 0x1p-12f);
+  const float r = fminf(ry + sqrtf(db), sqrtf(cmax2 * (1.0f + 0x1p-20f)));
+  const float ej = 2.0f * kT * ry * r + kC * r * r;
+  return (eb + ej) * (1.0f + 0x1p-10f) + 0x1p-40f * (ynu + db) + 0x1p-100f * (1.0f + ry);
 }
 
 // One wave per centroid: hi/lo planes of fp32(w*c) and the weighted norm.
@@ -136,7 +140,7 @@ __global__ __launch_bounds__(64) void k_prep(KmBatch b) {
 constexpr int kAsgWaves = 8;
 constexpr int kAsgThreads = kAsgWaves * 64;
 constexpr int kAsgMaxC = 256;
-constexpr int kAsgList = 1024;        // LDS close-call list; beyond it a wave re-decides on the spot
+constexpr int kAsgList = 3072;        // LDS close-call list; beyond it a wave re-decides on the spot
 constexpr int kCand = 16;             // candidates listed per close call; more: decided over all centroids
 constexpr int kRsw = kAsgWaves * 32;  // close calls per round of the second sweep
 constexpr int kAsgCUs = 256;
@@ -158,7 +162,6 @@ __global__ __launch_bounds__(kAsgThreads) void k_assign(KmBatch b, int G) {
   __shared__ __attribute__((aligned(16))) float sW[kHeadDim];
   __shared__ int sAmb[kAsgList];
   __shared__ int sAmbN, sNext;
-  __shared__ float sAmbM[kAsgList], sAmbT[kAsgList];   // screened best and bound of each close call
   __shared__ uint8_t sCand[kRsw][kCand];
   __shared__ int sCandN[kRsw], sOvf[kRsw];
   __shared__ int sOvfN;
@@ -236,6 +239,13 @@ __global__ __launch_bounds__(kAsgThreads) void k_assign(KmBatch b, int G) {
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
   }
+
+  // largest centroid norm of the head (wave-uniform; rows past C hold +inf)
+  float cmax2 = 0.0f;
+  for (int j = lane; j < C; j += 64) cmax2 = fmaxf(cmax2, sCn[j]);
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) cmax2 = fmaxf(cmax2, __shfl_xor(cmax2, o));
+  cmax2 = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, cmax2)));
 
   // One wave decides token tok over all centroids, lanes over centroids, in
   // the definition's arithmetic: the sum over channels, in order, of
@@ -454,16 +464,10 @@ __global__ __launch_bounds__(kAsgThreads) void k_assign(KmBatch b, int G) {
         const int tok = tok0 + t * 32 + col;
         if (half == 0 && tok < N) {
           labels[(int64_t)h * N + tok] = (uint8_t)bidx[t];
-          const float thr = screen_threshold<F32>(yn, b1[t], sCn[bidx[t]]);
-          if (!(second - b1[t] > thr)) {
+          if (!(second - b1[t] > screen_threshold<F32>(yn, b1[t], sCn[bidx[t]], cmax2))) {
             const int slot = atomicAdd(&sAmbN, 1);
-            if (slot < kAsgList) {
-              sAmb[slot] = tok;
-              sAmbM[slot] = b1[t];
-              sAmbT[slot] = thr;
-            } else {
-              spill = tok + 1;
-            }
+            if (slot < kAsgList) sAmb[slot] = tok;
+            else spill = tok + 1;
           }
         }
       }
@@ -502,11 +506,10 @@ __global__ __launch_bounds__(kAsgThreads) void k_assign(KmBatch b, int G) {
     if (wave * 32 < nloc) {                                  // wave-uniform
       const int loc = wave * 32 + col;
       const bool live = loc < nloc;
-      const int slot = e0 + min(loc, nloc - 1);
-      const int tok = sAmb[slot];
-      const float m1 = sAmbM[slot], thr = sAmbT[slot];
+      const int tok = sAmb[e0 + min(loc, nloc - 1)];
       const int64_t base = (int64_t)tok * y.stride_token + hoff;
       bf16x8 rh[8], rl[F32 ? 8 : 1];
+      float yn = 0.0f;                                       // sum_k w_k y_k^2 (fp32; sets the bound only)
       if constexpr (F32) {
         const float* p = reinterpret_cast<const float*>(y.ptr) + base;
 #pragma unroll
@@ -520,15 +523,27 @@ __global__ __launch_bounds__(kAsgThreads) void k_assign(KmBatch b, int G) {
             const uint32_t hb = f32_to_bf16_bits(v[e]);
             hi[e] = (uint16_t)hb;
             lo[e] = (uint16_t)f32_to_bf16_bits(v[e] - bf16_bits_to_f32(hb));
+            yn += sW[sI * 16 + half * 8 + e] * (v[e] * v[e]);
           }
           rh[sI] = __builtin_bit_cast(bf16x8, hi);
           rl[sI] = __builtin_bit_cast(bf16x8, lo);
         }
       } else {
 #pragma unroll
-        for (int sI = 0; sI < 8; ++sI) rh[sI] = as_bf16x8(*reinterpret_cast<const uint4*>(y16 + base + sI * 16));
+        for (int sI = 0; sI < 8; ++sI) {
+          const uint4 raw4 = *reinterpret_cast<const uint4*>(y16 + base + sI * 16);
+          rh[sI] = as_bf16x8(raw4);
+          const uint32_t r4[4] = {raw4.x, raw4.y, raw4.z, raw4.w};
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float v = bf16_bits_to_f32((r4[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
+            yn += sW[sI * 16 + half * 8 + e] * (v * v);
+          }
+        }
       }
-      for (int cb = 0; cb < Cp; cb += 32) {
+      yn += __shfl_xor(yn, 32);
+      // screened values of block cb (the same MFMAs as the sweep)
+      auto block = [&](int cb) __attribute__((always_inline)) -> f32x16 {
         f32x16 acc;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -546,6 +561,34 @@ __global__ __launch_bounds__(kAsgThreads) void k_assign(KmBatch b, int G) {
           acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(alo, rh[sI], acc, 0, 0, 0);
           if constexpr (F32) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahi, rl[F32 ? sI : 0], acc, 0, 0, 0);
         }
+        return acc;
+      };
+      // pass 1: the screened winner (value, lowest index) and its bound
+      float m1 = INFINITY;
+      int b1j = 0;
+      for (int cb = 0; cb < Cp; cb += 32) {
+        const f32x16 acc = block(cb);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int j = cb + (r >> 2) * 8 + half * 4 + (r & 3);
+          if (acc[r] < m1) {                                 // rows rise with r and cb: ties keep the lowest
+            m1 = acc[r];
+            b1j = j;
+          }
+        }
+      }
+      {
+        const float om = __shfl_xor(m1, 32);
+        const int oj = __shfl_xor(b1j, 32);
+        if (om < m1 || (om == m1 && oj < b1j)) {
+          m1 = om;
+          b1j = oj;
+        }
+      }
+      const float thr = screen_threshold<F32>(yn, m1, sCn[min(b1j, C - 1)], cmax2);
+      // pass 2: every centroid within the bound of the winner
+      for (int cb = 0; cb < Cp; cb += 32) {
+        const f32x16 acc = block(cb);
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int j = cb + (r >> 2) * 8 + half * 4 + (r & 3);
