@@ -49,7 +49,8 @@ def parse():
     p.add_argument("--steps", type=int, default=10)
     p.add_argument("--warmup", type=int, default=2)
     p.add_argument("--workload", type=int, default=5, help="headline workload id (2: 5 s cache, 3, 4, 5: one minute)")
-    p.add_argument("--extra", default="2,3,4", help="workload ids timed after the headline ('' for none)")
+    p.add_argument("--extra", default="2,3,4,6",
+                   help="workload ids timed after the headline ('' for none; 6: QuantWM with QSAC's range factor)")
     p.add_argument("--batch", type=int, default=12, help="problems per qkv_quantize_chunks call (1-16)")
     p.add_argument("--no-ar", action="store_true", help="skip the autoregressive rollout of the headline workload")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -157,7 +158,7 @@ class Run:
                               n_stages=wl.n_stages, kmeans_iters=wl.kmeans_iters,
                               n_int4_channels=wl.n_int4 if mixed else 0,
                               psac_rank=wl.psac_rank if tensor == "K" else 0,
-                              use_qsac=1 if (wl.qsac and tensor == "K") else 0)
+                              use_qsac=(2 if wl.qsac_range else 1) if (wl.qsac and tensor == "K") else 0)
 
     def fit(self):
         if self.stats:
@@ -496,7 +497,7 @@ def main():
     cfgd = {"workload": wl.name, "heads": wl.n_heads, "head_dim": 128, "chunks": wl.n_chunks,
             "chunk_tokens": wl.chunk_tokens, "cache_tokens": run.nk, "clusters": wl.n_clusters,
             "kmeans_iters": wl.kmeans_iters, "stages": wl.n_stages, "bits": wl.bits, "group": wl.group,
-            "int4_channels": wl.n_int4, "psac_rank": wl.psac_rank, "qsac": wl.qsac,
+            "int4_channels": wl.n_int4, "psac_rank": wl.psac_rank, "qsac": wl.qsac, "qsac_range": wl.qsac_range,
             "n_query": wl.n_query, "parallelism": "single-gpu"}
     del run
     torch.cuda.empty_cache()
@@ -508,12 +509,16 @@ def main():
         r = Run(cid, a.batch)
         ms, _ = time_steps(r, max(3, a.steps // 2), 1)
         ta = timed_call(r, r.attend, a.kernel_reps)
+        tq = timed_call(r, r.quantize_all, max(2, a.kernel_reps // 2))
+        tf = timed_call(r, r.fit, max(2, a.kernel_reps // 2)) if r.stats else 0.0
         w = r.work_per_step()
         extras[r.wl.name] = {"ms_per_step": ms, "value": r.nk / (ms * 1e-3), "unit": "KV tokens/s",
                              "attend_ms": ta, "attend_tflops": w["k_attend"][1] / (ta * 1e-3) / 1e12,
+                             "quantize_ms": tq, "fit_ms": tf,
                              "cache_tokens": r.nk, "stages": r.wl.n_stages, "psac_rank": r.wl.psac_rank,
-                             "qsac": r.wl.qsac}
-        log(f"extra workload {r.wl.name}: {ms:.3f} ms/step, attend {ta:.3f} ms")
+                             "qsac": r.wl.qsac, "qsac_range": r.wl.qsac_range}
+        log(f"extra workload {r.wl.name}: {ms:.3f} ms/step; quantize {tq:.3f} ms, attend {ta:.3f} ms, "
+            f"query statistics {tf:.3f} ms")
         del r
         torch.cuda.empty_cache()
 

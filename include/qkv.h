@@ -80,7 +80,13 @@ typedef enum { QKV_F32 = 0, QKV_BF16 = 1 } qkv_dtype;
  *   psac_rank        r in [0, 8]: PSAC coefficients per key token ([QWM]
  *                    "QuantWM", second technique).  0 = off.
  *   use_qsac         1 = weight k-means distances per channel by w ([QWM]
- *                    "QuantWM", first technique).
+ *                    "QuantWM", first technique: the channels' query
+ *                    activity).  2 = also weigh the dynamic range of the
+ *                    residual being quantized (same technique): the weights
+ *                    of each stage's k-means are fl32(w_k * fl32(rho_k^2)),
+ *                    rho_k = fl32(max - min) of channel k over the chunk's
+ *                    tokens of that stage's input (the data, then the
+ *                    residual of the previous stages).  0 = off.
  *   flags            QKV_FLAG_*.
  */
 typedef struct {
@@ -114,7 +120,7 @@ typedef struct {
 /*
  * Per-head side inputs of the quantizer (device pointers; NULL when the
  * feature is off):
- *   w     float [H][d]      QSAC channel weights (required when use_qsac).
+ *   w     float [H][d]      QSAC channel weights (required when use_qsac > 0).
  *   perm  uint8 [H][d]      channel order, sensitive (4-bit) class first, each
  *                           class listed in the order its channels are packed
  *                           (required when n_int4_channels > 0).

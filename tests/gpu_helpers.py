@@ -66,7 +66,7 @@ def config_of(wl, tensor: str, n_heads=None, rtn=False) -> qk.Config:
                      n_stages=wl.n_stages, kmeans_iters=wl.kmeans_iters,
                      n_int4_channels=wl.n_int4 if mixed else 0,
                      psac_rank=wl.psac_rank if tensor == "K" else 0,
-                     use_qsac=1 if (wl.qsac and tensor == "K") else 0,
+                     use_qsac=(2 if wl.qsac_range else 1) if (wl.qsac and tensor == "K") else 0,
                      flags=qk.QKV_FLAG_RTN if rtn else 0)
 
 

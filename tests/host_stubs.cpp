@@ -16,6 +16,7 @@ QKV_STUB(hipError_t launch_centroid_prep(const KmBatch&, hipStream_t))
 QKV_STUB(hipError_t launch_kmeans_assign(const KmBatch&, hipStream_t))
 QKV_STUB(hipError_t launch_kmeans_update(const KmBatch&, bool, hipStream_t))
 QKV_STUB(hipError_t launch_kmeans_group(const KmBatch&, hipStream_t))
+QKV_STUB(hipError_t launch_qsac_range(const RangeBatch&, hipStream_t))
 QKV_STUB(hipError_t launch_centroid_bf16(const KmBatch&, hipStream_t))
 QKV_STUB(hipError_t launch_fill_zero_u32(void*, size_t, hipStream_t))
 QKV_STUB(hipError_t launch_quant_pack(const PackArgs&, hipStream_t))

@@ -302,6 +302,8 @@ FREE = [
     ("progressive-K", 3, dict(n_heads=2, n_clusters=64), "K", 1500, False),
     ("quantwm-K", 4, dict(n_heads=2, n_clusters=64), "K", 1300, False),
     ("mixed-K", 5, dict(n_heads=2, n_clusters=64), "K", 1500, False),
+    ("quantwm-range-K", 6, dict(n_heads=2, n_clusters=64), "K", 1300, False),
+    ("quantwm-range-K-2-stages", 6, dict(n_heads=2, n_clusters=64, n_stages=2), "K", 1300, False),
 ]
 
 
@@ -339,7 +341,8 @@ def test_quantize_chunk_free_running(case):
     jobs = [(x[:, h], dict(n_clusters=wl.n_clusters, bits=wl.bits, group=wl.group, n_stages=wl.n_stages,
                            iters=wl.kmeans_iters, w=None if w is None else w[h], n_int4=cfg.n_int4_channels,
                            perm=None if perm is None else perm[h],
-                           u=None if u is None else u[h].astype(np.float64), rtn=rtn))
+                           u=None if u is None else u[h].astype(np.float64), rtn=rtn,
+                           qsac_range=wl.qsac_range and tensor == "K"))
             for h in range(wl.n_heads)]
     res = dict(enumerate(G.oracle_problems(jobs)))
     near = G.compare_chunk(name, wl, tensor, x, packed, cfg, res, range(wl.n_heads))
@@ -409,6 +412,27 @@ def test_full_chunk_bench_shape_sampled_heads():
         res = dict(zip(heads, G.oracle_problems(jobs)))
         near = G.compare_chunk(f"bench-{tensor}", wl, tensor, x, packed, cfg, res, heads)
         G.log(f"bench-shape chunk {tensor}: bit-exact on heads {heads}; near-ties {near}")
+
+
+def test_full_chunk_qsac_range_sampled_heads():
+    """QSAC with the residual-range factor on the QuantWM cache's whole first
+    key chunk (32 heads x 6,240 tokens, C = 256, PSAC r = 8): the per-stage
+    range weights come from the device; the oracle recomputes heads 3 and 29
+    (weights, k-means, codes, PSAC coefficients) bit for bit."""
+    wl = synth.workload(6)
+    x = synth.kv_chunk(wl, "K", 0)
+    w, u, _ = _side(wl, "K")
+    cfg = G.config_of(wl, "K")
+    assert cfg.use_qsac == 2
+    heads = [3, 29]
+    G.log(f"qsac-range chunk: N={x.shape[0]} H={wl.n_heads}; oracle heads {heads}")
+    packed = G.quantize(cfg, G.to_dev(x, "bf16"), w=G.to_dev(w), u=G.to_dev(u))
+    G.torch().cuda.synchronize()
+    jobs = [(x[:, h], dict(n_clusters=wl.n_clusters, bits=2, group=32, iters=10, w=w[h],
+                           u=u[h].astype(np.float64), qsac_range=True)) for h in heads]
+    res = dict(zip(heads, G.oracle_problems(jobs)))
+    near = G.compare_chunk("qsac-range", wl, "K", x, packed, cfg, res, heads)
+    G.log(f"qsac-range chunk: bit-exact on heads {heads}; near-ties {near}")
 
 
 def test_psac_fit_matches_oracle():

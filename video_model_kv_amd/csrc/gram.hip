@@ -59,7 +59,88 @@ __global__ void k_gram_reduce(int64_t per, int n_split, const double* __restrict
   m[i] = s;
 }
 
+// QSAC's second factor (QuantWM summary, "QuantWM", first technique: the
+// clustering also weighs the dynamic range of the residual being quantized).
+// Block (head, split) of problem blockIdx.y: each lane keeps the running minimum
+// and maximum of two channels over the split's tokens (waves stride by 4
+// tokens); the four waves are joined in LDS.  Minima and maxima are exact, so
+// the split order is immaterial.
+template <bool F32>
+__global__ __launch_bounds__(256) void k_range_partial(RangeBatch b) {
+  const int p = blockIdx.y;
+  const int h = blockIdx.x / kRangeSplits, sp = blockIdx.x % kRangeSplits;
+  const int64_t t0 = b.N * sp / kRangeSplits, t1 = b.N * (sp + 1) / kRangeSplits;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  float mn0 = INFINITY, mn1 = INFINITY, mx0 = -INFINITY, mx1 = -INFINITY;
+  const int64_t hoff = (int64_t)h * b.stride_head[p] + lane * 2;
+#pragma unroll 4
+  for (int64_t t = t0 + wave; t < t1; t += 4) {
+    const int64_t off = t * b.stride_token[p] + hoff;
+    float a, c;
+    if constexpr (F32) {
+      const float2 v = *reinterpret_cast<const float2*>(reinterpret_cast<const float*>(b.y[p]) + off);
+      a = v.x;
+      c = v.y;
+    } else {
+      const uint32_t v = *reinterpret_cast<const uint32_t*>(reinterpret_cast<const uint16_t*>(b.y[p]) + off);
+      a = bf16_bits_to_f32(v & 0xFFFFu);
+      c = bf16_bits_to_f32(v >> 16);
+    }
+    mn0 = fminf(mn0, a);
+    mx0 = fmaxf(mx0, a);
+    mn1 = fminf(mn1, c);
+    mx1 = fmaxf(mx1, c);
+  }
+  __shared__ float sm[4][4][64];
+  sm[wave][0][lane] = mn0;
+  sm[wave][1][lane] = mn1;
+  sm[wave][2][lane] = mx0;
+  sm[wave][3][lane] = mx1;
+  __syncthreads();
+  if (wave == 0) {
+    for (int x = 1; x < 4; ++x) {
+      mn0 = fminf(mn0, sm[x][0][lane]);
+      mn1 = fminf(mn1, sm[x][1][lane]);
+      mx0 = fmaxf(mx0, sm[x][2][lane]);
+      mx1 = fmaxf(mx1, sm[x][3][lane]);
+    }
+    float* out = b.part[p] + ((int64_t)h * kRangeSplits + sp) * 2 * kHeadDim;
+    *reinterpret_cast<float2*>(out + lane * 2) = make_float2(mn0, mn1);
+    *reinterpret_cast<float2*>(out + kHeadDim + lane * 2) = make_float2(mx0, mx1);
+  }
+}
+
+// Block (head) of problem blockIdx.y, thread = channel: the range over the
+// splits and the combined weight, each float operation rounded once.
+__global__ __launch_bounds__(kHeadDim) void k_range_weights(RangeBatch b) {
+  const int p = blockIdx.y, h = blockIdx.x, k = threadIdx.x;
+  const float* part = b.part[p] + (int64_t)h * kRangeSplits * 2 * kHeadDim;
+  float mn = INFINITY, mx = -INFINITY;
+  for (int sp = 0; sp < kRangeSplits; ++sp) {
+    mn = fminf(mn, part[sp * 2 * kHeadDim + k]);
+    mx = fmaxf(mx, part[sp * 2 * kHeadDim + kHeadDim + k]);
+  }
+  const float rho = mx - mn;
+  const float rr = rho * rho;
+  b.w_out[p][h * kHeadDim + k] = b.wq[p][h * kHeadDim + k] * rr;
+}
+
 }  // namespace
+
+hipError_t launch_qsac_range(const RangeBatch& b, hipStream_t s) {
+  if (b.n <= 0) return hipSuccess;
+  {
+    TimedLaunch tl_("k_range_partial", s);
+    const dim3 grid((unsigned)(b.H * kRangeSplits), (unsigned)b.n);
+    if (b.dtype == 0) hipLaunchKernelGGL(k_range_partial<true>, grid, dim3(256), 0, s, b);
+    else hipLaunchKernelGGL(k_range_partial<false>, grid, dim3(256), 0, s, b);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  TimedLaunch tl_("k_range_weights", s);
+  hipLaunchKernelGGL(k_range_weights, dim3((unsigned)b.H, (unsigned)b.n), dim3(kHeadDim), 0, s, b);
+  return hipGetLastError();
+}
 
 hipError_t launch_gram(const TensorView& q, int H, double* partial, int n_split, double* m, hipStream_t s) {
   TimedLaunch tl_("k_gram", s);

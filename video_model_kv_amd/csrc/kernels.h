@@ -62,6 +62,21 @@ hipError_t launch_kmeans_update(const KmBatch& b, bool refresh, hipStream_t s);
 // at most kGroupMaxTokens tokens); the update then reads its clusters' members from there.
 constexpr int kGroupMaxTokens = 8192;
 hipError_t launch_kmeans_group(const KmBatch& b, hipStream_t s);
+// QSAC's residual-range factor (gram.hip): for every problem of the batch,
+// w_out[h][k] = fl32(wq[h][k] * fl32(rho * rho)), rho = fl32(max - min) of
+// channel k of head h over the problem's tokens.  part: [H][kRangeSplits][2][128]
+// f32 per problem (per-split minima and maxima).
+constexpr int kRangeSplits = 16;
+struct RangeBatch {
+  int n, dtype, H;
+  int64_t N;
+  const void* y[kKmMaxBatch];
+  int64_t stride_token[kKmMaxBatch], stride_head[kKmMaxBatch];
+  const float* wq[kKmMaxBatch];
+  float* w_out[kKmMaxBatch];
+  float* part[kKmMaxBatch];
+};
+hipError_t launch_qsac_range(const RangeBatch& b, hipStream_t s);
 hipError_t launch_centroid_bf16(const KmBatch& b, hipStream_t s);
 hipError_t launch_fill_zero_u32(void* p, size_t n_words, hipStream_t s);
 

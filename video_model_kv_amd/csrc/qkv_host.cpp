@@ -112,7 +112,7 @@ int check_config(const qkv_config* c, const char* what) {
     return fail(QKV_EINVAL, "%s: the mixed layout needs bits == 2 for the base class", what);
   if (c->psac_rank < 0 || c->psac_rank > kMaxRank)
     return fail(QKV_EINVAL, "%s: psac_rank %d not in [0, 8]", what, c->psac_rank);
-  if (c->use_qsac != 0 && c->use_qsac != 1) return fail(QKV_EINVAL, "%s: use_qsac must be 0 or 1", what);
+  if (c->use_qsac < 0 || c->use_qsac > 2) return fail(QKV_EINVAL, "%s: use_qsac must be 0, 1 or 2", what);
   if (c->flags & ~QKV_FLAG_RTN) return fail(QKV_EINVAL, "%s: unknown flags 0x%x", what, c->flags);
   return QKV_OK;
 }
@@ -181,7 +181,7 @@ TensorView view_of(const qkv_tensor* t) {
 
 // ---- workspace plans ----
 struct QuantWs {
-  uint64_t c, planes, cn, amb_count, grp_off, grp_list, ybuf0, ybuf1, bytes;
+  uint64_t c, planes, cn, amb_count, grp_off, grp_list, wq, rpart, ybuf0, ybuf1, bytes;
 };
 
 QuantWs quant_ws(const qkv_config* c, int64_t n) {
@@ -194,6 +194,8 @@ QuantWs quant_ws(const qkv_config* c, int64_t n) {
   w.amb_count = off; off += 256;
   w.grp_off = off; off += align256(H * (C + 1) * 4);
   w.grp_list = off; off += align256(H * (uint64_t)n * 2);
+  w.wq = off;      off += align256(H * kHeadDim * 4);                  // QSAC weights with the range factor
+  w.rpart = off;   off += align256(H * kRangeSplits * 2 * kHeadDim * 4);
   w.ybuf0 = off;   if (c->n_stages > 1) off += align256(H * (uint64_t)n * kHeadDim * 4);
   w.ybuf1 = off;   if (c->n_stages > 2) off += align256(H * (uint64_t)n * kHeadDim * 4);
   w.bytes = off;
@@ -378,6 +380,26 @@ int quantize_batch(int32_t n, const qkv_config* const* cfgs, const qkv_tensor* c
       it.cent_bf16 = reinterpret_cast<uint16_t*>(base + L[p].off_centroids + (uint64_t)l * L[p].stage_bytes_centroids);
     }
     b.dtype = y[0].dtype;
+    {
+      // QSAC with the range factor: this stage's weights from its input
+      RangeBatch rb{};
+      rb.dtype = y[0].dtype;
+      rb.H = H;
+      rb.N = N;
+      for (int p = 0; p < n; ++p) {
+        if (cfgs[p]->use_qsac != 2) continue;
+        uint8_t* wsp = at(workspace, per * p);
+        const int r = rb.n++;
+        rb.y[r] = y[p].ptr;
+        rb.stride_token[r] = y[p].stride_token;
+        rb.stride_head[r] = y[p].stride_head;
+        rb.wq[r] = sides[p]->w;
+        rb.w_out[r] = reinterpret_cast<float*>(wsp + ws.wq);
+        rb.part[r] = reinterpret_cast<float*>(wsp + ws.rpart);
+        b.it[p].w = rb.w_out[r];
+      }
+      if (rb.n > 0 && !(c0->flags & QKV_FLAG_RTN)) QKV_HIP(launch_qsac_range(rb, s));
+    }
     if (c0->flags & QKV_FLAG_RTN) {
       for (int p = 0; p < n; ++p) {
         QKV_HIP(launch_fill_zero_u32(b.it[p].labels, L[p].stage_bytes_labels / 4, s));

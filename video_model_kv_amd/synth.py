@@ -65,6 +65,7 @@ class Workload:
     n_query: int
     causal: bool
     qsac: bool = False
+    qsac_range: bool = False      # QSAC weights also take each stage's channel ranges (keys)
     psac_rank: int = 0
     n_int4: int = 0
     n_hist: int = 0
@@ -101,6 +102,8 @@ WORKLOADS = {
     5: Workload(5, "minute", 32, 128, "bf16", 288, 4, 256, 1, 2, 32, 1560, False,
                 n_int4=26, n_hist=4096),
 }
+# the QuantWM cache's data (same seed) with QSAC's residual-range factor
+WORKLOADS[6] = replace(WORKLOADS[4], name="quantwm-range", qsac_range=True)
 
 
 def workload(cid: int, **over) -> Workload:
