@@ -280,6 +280,76 @@ def ar_rollout(run: Run) -> dict:
             "queries_per_step": "the chunk's own tokens", "mask": "frame-block causal over the fresh chunk"}
 
 
+def temporal_codec(run: Run) -> dict:
+    """The practitioner blog's temporally stable codec over the same cache: K and
+    V streams of every chunk (4 frames of P positions x H heads) coded in frame
+    order with the state carried, then rebuilt to bf16.  Per chunk launch:
+    algorithmic bytes = the chunk's input + the state read and written + the
+    packed output (coding); packed input + the group's anchor + the bf16 output
+    (rebuilding)."""
+    qk, torch, wl = run.qk, run.torch, run.wl
+    dev = torch.device("cuda")
+    P, H, nf = wl.tokens_per_frame, wl.n_heads, wl.chunk_frames
+    cfg = qk.TConfig(n_heads=H, frame_tokens=P, bits=2, anchor_every=32, decay=0.8)
+    st_bytes = qk.qkv_temporal_state_bytes(cfg)
+    states = [torch.empty(st_bytes, dtype=torch.uint8, device=dev) for _ in range(2)]
+    packs, anchors = [], []
+    for c in range(wl.n_chunks):
+        nb, _ = qk.qkv_temporal_layout(cfg, c * nf, nf)
+        packs.append([torch.empty(nb, dtype=torch.uint8, device=dev) for _ in range(2)])
+    out = torch.empty((nf * P, H, 128), dtype=torch.bfloat16, device=dev)
+
+    def encode_all():
+        for c in range(wl.n_chunks):
+            for i, x in enumerate((run.xk[c], run.xv[c])):
+                qk.qkv_temporal_encode(cfg, x, c * nf, states[i], packs[c][i])
+
+    encode_all()                                   # warm-up (a whole stream: the state restarts at frame 0)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    encode_all()
+    e1.record()
+    torch.cuda.synchronize()
+    enc_ms = e0.elapsed_time(e1)
+    # anchors of each chunk's group for rebuilding: chunk c's group anchor is the
+    # first frame of chunk 8 * (c // 8) (anchor every 32 frames = 8 chunks)
+    def decode_all():
+        for c in range(wl.n_chunks):
+            a = 8 * (c // 8)
+            for i in range(2):
+                anchor = packs[a][i]                # the anchor frame's fp16 values lead that chunk's run
+                qk.qkv_temporal_decode(cfg, c * nf, nf, packs[c][i], anchor, out)
+
+    decode_all()
+    torch.cuda.synchronize()
+    e0.record()
+    decode_all()
+    e1.record()
+    torch.cuda.synchronize()
+    dec_ms = e0.elapsed_time(e1)
+    n_launch = 2 * wl.n_chunks
+    el = nf * P * H * 128                          # elements per chunk and tensor
+    coded = P * H * (32 + 4 * 7)                   # bytes per coded frame: codes + 4 x (lo, scale, outlier value, channel)
+    anchor_fr = P * H * 128 * 2
+    packed_bytes = sum(p[0].numel() for p in packs)
+    enc_bytes = n_launch * (el * 2 + 2 * P * H * 128 * 6) + 2 * sum(
+        anchor_fr if (c * nf + f) % 32 == 0 else coded for c in range(wl.n_chunks) for f in range(nf))
+    dec_bytes = n_launch * (P * H * 128 * 2 + el * 2) + 2 * sum(
+        anchor_fr if (c * nf + f) % 32 == 0 else coded for c in range(wl.n_chunks) for f in range(nf))
+    res = {"scheme": "practitioner blog: P99 outliers in fp16, per-block min/max INT2, fp16 anchor every 32 frames, "
+                     "0.8 error feedback",
+           "launches": n_launch, "encode_us_per_chunk": enc_ms * 1e3 / n_launch,
+           "decode_us_per_chunk": dec_ms * 1e3 / n_launch,
+           "encode_GBps": enc_bytes / (enc_ms * 1e-3) / 1e9, "decode_GBps": dec_bytes / (dec_ms * 1e-3) / 1e9,
+           "encode_frac_of_hbm": enc_bytes / (enc_ms * 1e-3) / 8e12, "decode_frac_of_hbm": dec_bytes / (dec_ms * 1e-3) / 8e12,
+           "compression_vs_bf16": (wl.n_chunks * el * 2) / packed_bytes}
+    log(f"temporal codec: encode {res['encode_us_per_chunk']:.1f} us/chunk ({res['encode_GBps']:.0f} GB/s), "
+        f"decode {res['decode_us_per_chunk']:.1f} us/chunk ({res['decode_GBps']:.0f} GB/s), "
+        f"{res['compression_vs_bf16']:.2f}x vs bf16")
+    return res
+
+
 def time_steps(run: Run, steps: int, warmup: int):
     torch = run.torch
     for _ in range(warmup):
@@ -488,6 +558,11 @@ def main():
         "quantize_batches_per_step": len(run.batches), "problems_per_batch": a.batch,
         "kernels": prof,
     }
+    tcodec = None
+    try:
+        tcodec = temporal_codec(run)
+    except Exception as e:  # reported, never fatal to the headline measurement
+        log(f"temporal codec failed: {e}")
     ar = None
     if not a.no_ar:
         try:
@@ -538,7 +613,7 @@ def main():
                          "attention on fp16 MFMA with fp32 accumulation and softmax"),
         "data": "synthetic", "config": cfgd,
         "roofline": {k: v for k, v in dominant.items()},
-        "rooflines": roofs, "components": comp, "ar_rollout": ar, "workloads": extras, "cpu_baseline": cpu,
+        "rooflines": roofs, "components": comp, "ar_rollout": ar, "temporal_codec": tcodec, "workloads": extras, "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)
 

@@ -328,6 +328,66 @@ int qkv_quant_pack(const qkv_config* cfg, const qkv_tensor* y, const uint8_t* la
                    const float* centroids, const uint8_t* perm, void* packed, int32_t stage,
                    float* y_next, void* stream);
 
+/* ---- Temporally stable 2-bit codec ([BLOG] sections 3.3-3.5) ---- */
+
+/*
+ * A second compression scheme, for comparison with the k-means quantizer: per
+ * 32-channel block of one token-head, the value of unique largest magnitude
+ * (the block's P99 outlier) is kept in fp16 and the others are coded with an
+ * fp16 zero point lo = fp16(min) and scale S = fp16((max - lo) / (2^b - 1)),
+ * q = clamp(rint((r - lo) / S), 0, 2^b - 1); frame f is an fp16 anchor iff
+ * f % anchor_every == 0, every other frame codes r = (kv + feedback) - anchor
+ * (its group's anchor as stored, position by position) and rebuilds kv_hat =
+ * anchor + (lo + q S); feedback = decay * (kv - kv_hat) carries to the same
+ * position of the next frame.  All arithmetic float32, each operation rounded
+ * once in that order; fp16 conversions to nearest even.  Inputs within the
+ * fp16 range.
+ *   n_heads       H in [1, 256] (head_dim 128).
+ *   frame_tokens  P >= 1: tokens (positions) per frame.
+ *   bits          2 or 4.
+ *   anchor_every  >= 1 frames per temporal group ([BLOG] 3.3: 32).
+ *   decay         error-feedback decay in [0, 1] ([BLOG] 3.5: 0.8).
+ */
+typedef struct {
+  int32_t n_heads;
+  int32_t frame_tokens;
+  int32_t bits;
+  int32_t anchor_every;
+  float decay;
+} qkv_tcfg;
+
+/* Bytes of one packed run of n_frames (1 to 64) frames starting at global frame
+   frame0 >= 0, and (frame_offsets non-NULL: n_frames entries) each frame's byte
+   offset in it.  An anchor frame holds fp16 values [P][H][128]; any other frame
+   holds, each section 256-byte aligned in this order: codes u32 [P][H][4 * bits]
+   (channel k of block j of a token-head in word j * bits + k / (32 / bits),
+   bits * (k % (32 / bits)) up), lo fp16 [P][H][4], scale fp16 [P][H][4],
+   outlier value fp16 [P][H][4] (0 when none), outlier channel within the block
+   u8 [P][H][4] (255 when none).  Host only. */
+int qkv_temporal_layout(const qkv_tcfg* cfg, int64_t frame0, int32_t n_frames, size_t* bytes,
+                        size_t* frame_offsets);
+
+/* Bytes of the state carried from one call to the next: feedback f32
+   [P][H][128], then (at offset 4 * P * H * 128) the current anchor fp16
+   [P][H][128].  Host only. */
+int qkv_temporal_state_bytes(const qkv_tcfg* cfg, size_t* bytes);
+
+/* Code frames frame0 .. frame0 + n_frames - 1 of x [n_frames * P][H][128] (bf16
+   or f32; frame by frame, each frame's P tokens in position order) into packed
+   (qkv_temporal_layout bytes, device), serially over frames.  state (device,
+   qkv_temporal_state_bytes): read unless frame0 is an anchor frame (the start
+   of a stream must be one), then replaced by the state after the last frame. */
+int qkv_temporal_encode(const qkv_tcfg* cfg, const qkv_tensor* x, int64_t frame0, void* state, void* packed,
+                        void* stream);
+
+/* Rebuild out [n_frames * P][H][128] (f32 or bf16, rounded to nearest even)
+   from a run packed by qkv_temporal_encode (same frame0 and n_frames).
+   anchor: fp16 [P][H][128] device, the anchor of frame0's group as stored (the
+   anchor section of the state before the run was coded, or that anchor frame's
+   packed values); unused, and may be NULL, when frame0 is an anchor frame. */
+int qkv_temporal_decode(const qkv_tcfg* cfg, int64_t frame0, int32_t n_frames, const void* packed,
+                        const void* anchor, const qkv_tensor* out, void* stream);
+
 /* ---- Kernel timing, for measurement tools ---- */
 
 /* Per-kernel totals returned by qkv_timing_read. */

@@ -17,6 +17,8 @@ QKV_STUB(hipError_t launch_kmeans_assign(const KmBatch&, hipStream_t))
 QKV_STUB(hipError_t launch_kmeans_update(const KmBatch&, bool, hipStream_t))
 QKV_STUB(hipError_t launch_kmeans_group(const KmBatch&, hipStream_t))
 QKV_STUB(hipError_t launch_qsac_range(const RangeBatch&, hipStream_t))
+QKV_STUB(hipError_t launch_temporal_encode(const TCodecArgs&, hipStream_t))
+QKV_STUB(hipError_t launch_temporal_decode(const TCodecArgs&, void*, int, int64_t, int64_t, hipStream_t))
 QKV_STUB(hipError_t launch_centroid_bf16(const KmBatch&, hipStream_t))
 QKV_STUB(hipError_t launch_fill_zero_u32(void*, size_t, hipStream_t))
 QKV_STUB(hipError_t launch_quant_pack(const PackArgs&, hipStream_t))

@@ -197,3 +197,29 @@ def test_kernel_timing_switch_without_a_gpu():
     assert B.qkv_timing_read() == {}
     B.qkv_timing_enable(False)
     assert B.lib().qkv_timing_read(0, None, None) == B.QKV_EINVAL
+
+
+def test_temporal_layout_arithmetic():
+    """Anchor frames hold fp16 values; the others codes, zero points, scales,
+    outlier values and channels, each section 256-byte aligned."""
+    def a256(x):
+        return (x + 255) // 256 * 256
+    cfg = B.TConfig(n_heads=3, frame_tokens=50, bits=2, anchor_every=4)
+    th = 150
+    coded = a256(th * 4 * 2 * 4) + 3 * a256(th * 4 * 2) + a256(th * 4)
+    anchor = a256(th * 128 * 2)
+    nb, offs = B.qkv_temporal_layout(cfg, 2, 5)            # frames 2, 3, [4 anchor], 5, 6
+    assert offs == [0, coded, 2 * coded, 2 * coded + anchor, 3 * coded + anchor]
+    assert nb == 4 * coded + anchor
+    assert B.qkv_temporal_state_bytes(cfg) == th * 128 * 6
+
+
+@pytest.mark.parametrize("kw,frame0,n", [
+    (dict(bits=3), 0, 4), (dict(decay=1.5), 0, 4), (dict(decay=-0.1), 0, 4), (dict(anchor_every=0), 0, 4),
+    (dict(n_heads=0), 0, 4), (dict(frame_tokens=0), 0, 4), ({}, -1, 4), ({}, 0, 0), ({}, 0, 65),
+])
+def test_temporal_invalid_arguments(kw, frame0, n):
+    cfg = B.TConfig(**dict(dict(n_heads=2, frame_tokens=8), **kw))
+    with pytest.raises(B.QkvError) as e:
+        B.qkv_temporal_layout(cfg, frame0, n)
+    assert e.value.status == B.QKV_EINVAL

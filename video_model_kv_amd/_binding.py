@@ -27,6 +27,7 @@ EXPORTED = [
     "qkv_kmeans_assign", "qkv_kmeans_update", "qkv_quant_pack",
     "qkv_quantize_chunks", "qkv_quantize_chunks_workspace_bytes", "qkv_quantize_chunk_noalloc",
     "qkv_timing_enable", "qkv_timing_read", "qkv_attend_fresh",
+    "qkv_temporal_layout", "qkv_temporal_state_bytes", "qkv_temporal_encode", "qkv_temporal_decode",
 ]
 
 
@@ -49,6 +50,11 @@ class qkv_tensor(ct.Structure):
 
 class qkv_side(ct.Structure):
     _fields_ = [("w", ct.c_void_p), ("perm", ct.c_void_p), ("U", ct.c_void_p)]
+
+
+class qkv_tcfg(ct.Structure):
+    _fields_ = [("n_heads", ct.c_int32), ("frame_tokens", ct.c_int32), ("bits", ct.c_int32),
+                ("anchor_every", ct.c_int32), ("decay", ct.c_float)]
 
 
 class qkv_kernel_time(ct.Structure):
@@ -85,6 +91,19 @@ class Config:
         return qkv_config(self.head_dim, self.n_heads, self.n_clusters, self.kmeans_iters,
                           self.n_stages, self.bits, self.group, self.n_int4_channels,
                           self.psac_rank, self.use_qsac, self.flags)
+
+
+@dataclass
+class TConfig:
+    """Python mirror of qkv_tcfg (the temporally stable codec; include/qkv.h)."""
+    n_heads: int
+    frame_tokens: int
+    bits: int = 2
+    anchor_every: int = 32
+    decay: float = 0.8
+
+    def c(self) -> qkv_tcfg:
+        return qkv_tcfg(self.n_heads, self.frame_tokens, self.bits, self.anchor_every, self.decay)
 
 
 _lib = None
@@ -124,6 +143,10 @@ def lib():
         L.qkv_quantize_chunk_noalloc.argtypes = [P(qkv_config), P(qkv_tensor), P(qkv_side), vp, vp]
         L.qkv_attend_fresh.argtypes = [P(qkv_config), P(qkv_config), P(qkv_tensor), P(vp), P(vp), P(i64), i32,
                                        P(qkv_tensor), P(qkv_tensor), i32, vp, ct.c_float, P(qkv_tensor), vp, vp, sz, vp]
+        L.qkv_temporal_layout.argtypes = [P(qkv_tcfg), i64, i32, P(sz), P(sz)]
+        L.qkv_temporal_state_bytes.argtypes = [P(qkv_tcfg), P(sz)]
+        L.qkv_temporal_encode.argtypes = [P(qkv_tcfg), P(qkv_tensor), i64, vp, vp, vp]
+        L.qkv_temporal_decode.argtypes = [P(qkv_tcfg), i64, i32, vp, vp, P(qkv_tensor), vp]
         L.qkv_timing_enable.argtypes = [i32]
         L.qkv_timing_read.argtypes = [i32, P(qkv_kernel_time), P(i32)]
         for name in EXPORTED[2:]:
@@ -285,3 +308,27 @@ def qkv_timing_read() -> dict:
     buf = (qkv_kernel_time * max(1, n.value))()
     _check(lib().qkv_timing_read(n.value, buf, ct.byref(n)))
     return {buf[i].name.decode(): (int(buf[i].launches), float(buf[i].total_ms)) for i in range(n.value)}
+
+
+def qkv_temporal_layout(cfg: TConfig, frame0: int, n_frames: int):
+    """(bytes, [frame byte offsets]) of a packed run of the temporally stable codec."""
+    nb = ct.c_size_t()
+    offs = (ct.c_size_t * max(1, n_frames))()
+    _check(lib().qkv_temporal_layout(ct.byref(cfg.c()), frame0, n_frames, ct.byref(nb), offs))
+    return nb.value, [offs[i] for i in range(n_frames)]
+
+
+def qkv_temporal_state_bytes(cfg: TConfig) -> int:
+    nb = ct.c_size_t()
+    _check(lib().qkv_temporal_state_bytes(ct.byref(cfg.c()), ct.byref(nb)))
+    return nb.value
+
+
+def qkv_temporal_encode(cfg: TConfig, x, frame0: int, state, packed, stream=None):
+    _check(lib().qkv_temporal_encode(ct.byref(cfg.c()), ct.byref(tensor_desc(x)), frame0, _ptr(state), _ptr(packed),
+                                     _stream(stream)))
+
+
+def qkv_temporal_decode(cfg: TConfig, frame0: int, n_frames: int, packed, anchor, out, stream=None):
+    _check(lib().qkv_temporal_decode(ct.byref(cfg.c()), frame0, n_frames, _ptr(packed), _ptr(anchor),
+                                     ct.byref(tensor_desc(out)), _stream(stream)))

@@ -77,6 +77,29 @@ struct RangeBatch {
   float* part[kKmMaxBatch];
 };
 hipError_t launch_qsac_range(const RangeBatch& b, hipStream_t s);
+
+// ---- temporally stable 2-bit codec (temporal.hip) ----
+// One call codes n_frames consecutive frames (global index frame0 + f) of P
+// positions x H heads; frame f's data starts at packed + frame_off[f]: fp16
+// values [P][H][128] for an anchor frame, else the sections at the sec_*
+// offsets (codes u32 [P][H][4 * bits], lo / scale / oval fp16 [P][H][4], oidx
+// u8 [P][H][4]).  State: fb f32 [P][H][128] and anchor fp16 [P][H][128].
+constexpr int kTMaxFrames = 64;
+struct TCodecArgs {
+  int H, P, bits, anchor_every, n_frames;
+  float decay;
+  int64_t frame0;
+  TensorView x;                  // encode input [n_frames * P][H][128]
+  float* fb;                     // encode: feedback state (read, then written)
+  uint16_t* anchor;              // encode: anchor state; decode: the anchor of frame0's group
+  uint8_t* packed;
+  uint64_t frame_off[kTMaxFrames];
+  int8_t anc_frame[kTMaxFrames];  // decode: the run's frame holding frame f's anchor, -1 = the caller's anchor
+  uint64_t sec_codes, sec_lo, sec_scale, sec_oval, sec_oidx;
+};
+hipError_t launch_temporal_encode(const TCodecArgs& a, hipStream_t s);
+hipError_t launch_temporal_decode(const TCodecArgs& a, void* out, int out_dtype, int64_t out_st, int64_t out_sh,
+                                  hipStream_t s);
 hipError_t launch_centroid_bf16(const KmBatch& b, hipStream_t s);
 hipError_t launch_fill_zero_u32(void* p, size_t n_words, hipStream_t s);
 

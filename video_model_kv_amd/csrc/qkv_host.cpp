@@ -919,3 +919,136 @@ int qkv_quant_pack(const qkv_config* cfg, const qkv_tensor* y, const uint8_t* la
 }
 
 }  // extern "C"
+
+namespace {
+
+int check_tcfg(const qkv_tcfg* c, const char* what) {
+  if (!c) return fail(QKV_EINVAL, "%s: cfg is NULL", what);
+  if (c->n_heads < 1 || c->n_heads > 256) return fail(QKV_EINVAL, "%s: n_heads %d not in [1, 256]", what, c->n_heads);
+  if (c->frame_tokens < 1 || c->frame_tokens > (1 << 24))
+    return fail(QKV_EINVAL, "%s: frame_tokens %d not in [1, 2^24]", what, c->frame_tokens);
+  if (c->bits != 2 && c->bits != 4) return fail(QKV_EINVAL, "%s: bits must be 2 or 4", what);
+  if (c->anchor_every < 1) return fail(QKV_EINVAL, "%s: anchor_every must be >= 1", what);
+  if (!(c->decay >= 0.0f && c->decay <= 1.0f)) return fail(QKV_EINVAL, "%s: decay must be in [0, 1]", what);
+  return QKV_OK;
+}
+
+struct TLayout {
+  uint64_t bytes;
+  uint64_t frame_off[kTMaxFrames];
+  uint64_t sec_codes, sec_lo, sec_scale, sec_oval, sec_oidx, coded_bytes, anchor_bytes;
+};
+
+TLayout temporal_layout(const qkv_tcfg* c, int64_t frame0, int n_frames) {
+  const uint64_t th = (uint64_t)c->frame_tokens * c->n_heads;
+  TLayout L;
+  L.sec_codes = 0;
+  L.sec_lo = align256(th * 4 * c->bits * 4);
+  L.sec_scale = L.sec_lo + align256(th * 4 * 2);
+  L.sec_oval = L.sec_scale + align256(th * 4 * 2);
+  L.sec_oidx = L.sec_oval + align256(th * 4 * 2);
+  L.coded_bytes = L.sec_oidx + align256(th * 4);
+  L.anchor_bytes = align256(th * kHeadDim * 2);
+  uint64_t off = 0;
+  for (int f = 0; f < n_frames; ++f) {
+    L.frame_off[f] = off;
+    off += (frame0 + f) % c->anchor_every == 0 ? L.anchor_bytes : L.coded_bytes;
+  }
+  L.bytes = off;
+  return L;
+}
+
+int check_trun(const qkv_tcfg* c, int64_t frame0, int32_t n_frames, const char* what) {
+  QKV_TRY(check_tcfg(c, what));
+  if (frame0 < 0) return fail(QKV_EINVAL, "%s: frame0 %lld < 0", what, (long long)frame0);
+  if (n_frames < 1 || n_frames > kTMaxFrames) return fail(QKV_EINVAL, "%s: n_frames %d not in [1, %d]", what, n_frames, kTMaxFrames);
+  return QKV_OK;
+}
+
+TCodecArgs tcodec_args(const qkv_tcfg* c, int64_t frame0, int32_t n_frames, const TLayout& L) {
+  TCodecArgs a{};
+  a.H = c->n_heads;
+  a.P = c->frame_tokens;
+  a.bits = c->bits;
+  a.anchor_every = c->anchor_every;
+  a.n_frames = n_frames;
+  a.decay = c->decay;
+  a.frame0 = frame0;
+  int fa = -1;
+  for (int f = 0; f < n_frames; ++f) {
+    a.frame_off[f] = L.frame_off[f];
+    if ((frame0 + f) % c->anchor_every == 0) fa = f;
+    a.anc_frame[f] = (int8_t)fa;
+  }
+  a.sec_codes = L.sec_codes;
+  a.sec_lo = L.sec_lo;
+  a.sec_scale = L.sec_scale;
+  a.sec_oval = L.sec_oval;
+  a.sec_oidx = L.sec_oidx;
+  return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+int qkv_temporal_layout(const qkv_tcfg* cfg, int64_t frame0, int32_t n_frames, size_t* bytes, size_t* frame_offsets) {
+  QKV_TRY(check_trun(cfg, frame0, n_frames, "qkv_temporal_layout"));
+  if (!bytes) return fail(QKV_EINVAL, "qkv_temporal_layout: bytes is NULL");
+  const TLayout L = temporal_layout(cfg, frame0, n_frames);
+  *bytes = (size_t)L.bytes;
+  if (frame_offsets)
+    for (int f = 0; f < n_frames; ++f) frame_offsets[f] = (size_t)L.frame_off[f];
+  return ok();
+}
+
+int qkv_temporal_state_bytes(const qkv_tcfg* cfg, size_t* bytes) {
+  QKV_TRY(check_tcfg(cfg, "qkv_temporal_state_bytes"));
+  if (!bytes) return fail(QKV_EINVAL, "qkv_temporal_state_bytes: bytes is NULL");
+  *bytes = (size_t)cfg->frame_tokens * cfg->n_heads * kHeadDim * 6;
+  return ok();
+}
+
+int qkv_temporal_encode(const qkv_tcfg* cfg, const qkv_tensor* x, int64_t frame0, void* state, void* packed,
+                        void* stream) {
+  const char* fn = "qkv_temporal_encode";
+  QKV_TRY(check_tcfg(cfg, fn));
+  QKV_TRY(check_tensor(x, cfg->n_heads, fn));
+  if (x->n_tokens % cfg->frame_tokens) return fail(QKV_EINVAL, "%s: n_tokens %lld is not a whole number of frames of %d tokens",
+                                                   fn, (long long)x->n_tokens, cfg->frame_tokens);
+  const int64_t nf = x->n_tokens / cfg->frame_tokens;
+  QKV_TRY(check_trun(cfg, frame0, (int32_t)std::min<int64_t>(nf, INT32_MAX), fn));
+  if (!state || !aligned16(state)) return fail(QKV_EINVAL, "%s: state is NULL or not 16-byte aligned", fn);
+  if (!packed || !aligned16(packed)) return fail(QKV_EINVAL, "%s: packed is NULL or not 16-byte aligned", fn);
+  const TLayout L = temporal_layout(cfg, frame0, (int)nf);
+  TCodecArgs a = tcodec_args(cfg, frame0, (int32_t)nf, L);
+  a.x = view_of(x);
+  a.fb = reinterpret_cast<float*>(state);
+  a.anchor = reinterpret_cast<uint16_t*>(reinterpret_cast<uint8_t*>(state) + (uint64_t)cfg->frame_tokens * cfg->n_heads * kHeadDim * 4);
+  a.packed = reinterpret_cast<uint8_t*>(packed);
+  QKV_HIP(launch_temporal_encode(a, reinterpret_cast<hipStream_t>(stream)));
+  return ok();
+}
+
+int qkv_temporal_decode(const qkv_tcfg* cfg, int64_t frame0, int32_t n_frames, const void* packed, const void* anchor,
+                        const qkv_tensor* out, void* stream) {
+  const char* fn = "qkv_temporal_decode";
+  QKV_TRY(check_trun(cfg, frame0, n_frames, fn));
+  QKV_TRY(check_tensor(out, cfg->n_heads, fn));
+  if (out->n_tokens != (int64_t)n_frames * cfg->frame_tokens)
+    return fail(QKV_EINVAL, "%s: out has %lld tokens, the run %lld", fn, (long long)out->n_tokens,
+                (long long)n_frames * cfg->frame_tokens);
+  if (!packed || !aligned16(packed)) return fail(QKV_EINVAL, "%s: packed is NULL or not 16-byte aligned", fn);
+  const bool need_anchor = frame0 % cfg->anchor_every != 0;
+  if (need_anchor && (!anchor || !aligned16(anchor)))
+    return fail(QKV_EINVAL, "%s: frame0 is not an anchor frame: the anchor of its group is required", fn);
+  const TLayout L = temporal_layout(cfg, frame0, n_frames);
+  TCodecArgs a = tcodec_args(cfg, frame0, n_frames, L);
+  a.packed = const_cast<uint8_t*>(reinterpret_cast<const uint8_t*>(packed));
+  a.anchor = const_cast<uint16_t*>(reinterpret_cast<const uint16_t*>(anchor));
+  QKV_HIP(launch_temporal_decode(a, out->ptr, out->dtype == QKV_F32 ? 0 : 1, out->stride_token, out->stride_head,
+                                 reinterpret_cast<hipStream_t>(stream)));
+  return ok();
+}
+
+}  // extern "C"
