@@ -350,6 +350,56 @@ def temporal_codec(run: Run) -> dict:
     return res
 
 
+def layer_batching(run: Run, n_layers: int = 8, n_chunks: int = 6) -> dict:
+    """Per-layer batching: layers stacked along the head axis run as one launch.
+    n_layers x n_chunks of the workload's bf16 chunks serve as the layers' caches
+    (layer l = chunks l * n_chunks ...), quantized INT2 (C = 256, groups of 32)
+    once per layer (32 heads) and once head-stacked (n_layers x 32 heads); the
+    attention of the same queries is timed both ways, for the whole query chunk
+    and for a small decode-sized one."""
+    qk, torch, wl = run.qk, run.torch, run.wl
+    dev = torch.device("cuda")
+    H = wl.n_heads
+    n_layers = min(n_layers, wl.n_chunks // n_chunks)
+    cfg_l = qk.Config(n_heads=H, n_clusters=256, bits=2, group=32)
+    cfg_s = qk.Config(n_heads=H * n_layers, n_clusters=256, bits=2, group=32)
+    ntok = [run.ntok[c] for c in range(n_chunks)]
+    n_max = max(ntok)
+    ws_l = torch.empty(qk.qkv_workspace_bytes(cfg_l, n_max, wl.n_query, n_chunks), dtype=torch.uint8, device=dev)
+    ws_s = torch.empty(qk.qkv_workspace_bytes(cfg_s, n_max, wl.n_query, n_chunks), dtype=torch.uint8, device=dev)
+
+    def packed(cfg, x, ws):
+        p = torch.empty(qk.qkv_chunk_layout(cfg, x.shape[0]).bytes, dtype=torch.uint8, device=dev)
+        qk.qkv_quantize_chunk(cfg, x, p, ws)
+        return p
+
+    kl = [[packed(cfg_l, run.xk[l * n_chunks + c], ws_l) for c in range(n_chunks)] for l in range(n_layers)]
+    vl = [[packed(cfg_l, run.xv[l * n_chunks + c], ws_l) for c in range(n_chunks)] for l in range(n_layers)]
+    ks, vs = [], []
+    for c in range(n_chunks):
+        for src, dst in ((run.xk, ks), (run.xv, vs)):
+            x = torch.cat([src[l * n_chunks + c] for l in range(n_layers)], dim=1)
+            dst.append(packed(cfg_s, x, ws_s))
+            del x
+    q_s = torch.cat([run.q] * n_layers, dim=1)
+    out_l = torch.empty((wl.n_query, H, 128), dtype=torch.float32, device=dev)
+    out_s = torch.empty((wl.n_query, H * n_layers, 128), dtype=torch.float32, device=dev)
+    res = {"layers": n_layers, "heads_per_layer": H, "chunks_per_layer": n_chunks, "keys_per_layer": sum(ntok)}
+    for nq in (wl.n_query, 64):
+        def per_layer():
+            for l in range(n_layers):
+                qk.qkv_attend(cfg_l, cfg_l, run.q[:nq], kl[l], vl[l], ntok, out_l[:nq], ws_l)
+
+        def stacked():
+            qk.qkv_attend(cfg_s, cfg_s, q_s[:nq], ks, vs, ntok, out_s[:nq], ws_s)
+
+        tl, ts = timed_call(run, per_layer, 5), timed_call(run, stacked, 5)
+        res[f"nq{nq}"] = {"per_layer_launches_ms": tl, "stacked_launch_ms": ts, "speedup": tl / ts}
+        log(f"layer batching ({n_layers} layers x {H} heads, {sum(ntok)} keys each), {nq} queries: "
+            f"{n_layers} launches {tl:.3f} ms, one stacked launch {ts:.3f} ms ({tl / ts:.2f}x)")
+    return res
+
+
 def time_steps(run: Run, steps: int, warmup: int):
     torch = run.torch
     for _ in range(warmup):
@@ -558,6 +608,11 @@ def main():
         "quantize_batches_per_step": len(run.batches), "problems_per_batch": a.batch,
         "kernels": prof,
     }
+    lbatch = None
+    try:
+        lbatch = layer_batching(run)
+    except Exception as e:  # reported, never fatal to the headline measurement
+        log(f"layer batching failed: {e}")
     tcodec = None
     try:
         tcodec = temporal_codec(run)
@@ -613,7 +668,7 @@ def main():
                          "attention on fp16 MFMA with fp32 accumulation and softmax"),
         "data": "synthetic", "config": cfgd,
         "roofline": {k: v for k, v in dominant.items()},
-        "rooflines": roofs, "components": comp, "ar_rollout": ar, "temporal_codec": tcodec, "workloads": extras, "cpu_baseline": cpu,
+        "rooflines": roofs, "components": comp, "ar_rollout": ar, "temporal_codec": tcodec, "layer_batching": lbatch, "workloads": extras, "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)
 

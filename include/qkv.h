@@ -59,7 +59,12 @@ typedef enum { QKV_F32 = 0, QKV_BF16 = 1 } qkv_dtype;
 /*
  * Quantizer configuration of one tensor (K or V) of one layer.
  *   head_dim         d; must be 128 (the only head size supported).
- *   n_heads          H >= 1.
+ *   n_heads          H in [1, 1024].  Every step is independent per head, so
+ *                    layers that share a configuration may be stacked along
+ *                    the head axis (H = layers x heads per layer, tensors
+ *                    [N][layers * heads][128]): one call then quantizes, and
+ *                    one qkv_attend launch attends, all of those layers, with
+ *                    each head's results those of its layer alone.
  *   n_clusters       C in [1, 256]: k-means groups per (chunk, head, stage)
  *                    ([QVG] "Semantic-Aware Smoothing").  Needs n_tokens >= C.
  *   kmeans_iters     Lloyd iterations per stage, >= 1 (the fixed protocol

@@ -308,3 +308,60 @@ def test_long_horizon_full_cache_sampled_queries():
         e = G.rel_l2(of[sample, h], ref)
         G.log(f"long-horizon AR step h{h}: output rel-L2 {e:.3g} on {len(sample)} sampled queries (tol {OUT_TOL})")
         assert e <= OUT_TOL, f"long-horizon AR step h{h}: output rel-L2 {e}"
+
+
+def test_layers_stacked_as_heads():
+    """Per-layer batching: every step of the path is independent per head, so L
+    layers that share a configuration stack along the head axis -- one quantize
+    call per chunk and one attention launch for all of them.  Here 4 layers of 4
+    heads (16 stacked heads) over two ragged chunks: each layer's heads in the
+    stacked packed chunks equal the layer quantized alone, byte for byte, and
+    each layer's outputs, from the stacked launch and from the layer's own
+    launch, match the oracle on sampled heads."""
+    t = G.torch()
+    L, Hl = 4, 4
+    wl = synth.workload(2, n_heads=L * Hl, n_clusters=64, frames=2)
+    bounds = [(0, 1400), (1400, 3120)]
+    nq = 200
+    cfg_s, cfg_l = G.config_of(wl, "K"), G.config_of(wl, "K", n_heads=Hl)
+    xs = {tensor: [synth.kv_tokens(wl, tensor, a, b) for a, b in bounds] for tensor in ("K", "V")}
+    ntok = [b - a for a, b in bounds]
+    ws_s = G.workspace(cfg_s, max(ntok), nq, len(bounds))
+    ws_l = G.workspace(cfg_l, max(ntok), nq, len(bounds))
+    packs_s = {tn: [] for tn in ("K", "V")}
+    packs_l = {tn: [[] for _ in range(L)] for tn in ("K", "V")}
+    for tensor in ("K", "V"):
+        for ci, x in enumerate(xs[tensor]):
+            xd = G.to_dev(x, "bf16")
+            packs_s[tensor].append(G.quantize(cfg_s, xd, ws=ws_s))
+            for l in range(L):
+                packs_l[tensor][l].append(G.quantize(cfg_l, xd[:, l * Hl:(l + 1) * Hl], ws=ws_l))
+            vs = G.host_views(packs_s[tensor][ci], cfg_s, ntok[ci])
+            for l in range(L):
+                vl = G.host_views(packs_l[tensor][l][ci], cfg_l, ntok[ci])
+                for key in ("labels", "codes", "scales", "centroids"):
+                    assert np.array_equal(vs[key][:, l * Hl:(l + 1) * Hl], vl[key]), \
+                        f"{tensor} chunk {ci} layer {l}: stacked {key} differ from the layer alone"
+    G.log(f"stacked layers: {L} layers x {Hl} heads quantized in one call per chunk = per-layer calls, byte for byte")
+    q = synth.queries(wl, n=nq)
+    qd = G.to_dev(q, "bf16")
+    out_s = t.empty((nq, L * Hl, 128), dtype=t.float32, device=G.dev())
+    qk.qkv_attend(cfg_s, cfg_s, qd, packs_s["K"], packs_s["V"], ntok, out_s, ws_s)
+    out_l = []
+    for l in range(L):
+        o = t.empty((nq, Hl, 128), dtype=t.float32, device=G.dev())
+        qk.qkv_attend(cfg_l, cfg_l, qd[:, l * Hl:(l + 1) * Hl], packs_l["K"][l], packs_l["V"][l], ntok, o, ws_l)
+        out_l.append(o.cpu().numpy())
+    os_ = out_s.cpu().numpy()
+    checked = [(0, 1), (1, 2), (3, 3)]               # (layer, head within the layer)
+    jobs = [(xs[tensor][ci][:, l * Hl + hl], dict(n_clusters=64, bits=2, group=32, iters=10))
+            for l, hl in checked for ci in range(len(bounds)) for tensor in ("K", "V")]
+    res = G.oracle_problems(jobs)
+    for i, (l, hl) in enumerate(checked):
+        r = res[i * 2 * len(bounds): (i + 1) * 2 * len(bounds)]
+        k_hat = np.concatenate([r[2 * ci].x_hat for ci in range(len(bounds))])
+        v_hat = np.concatenate([r[2 * ci + 1].x_hat for ci in range(len(bounds))])
+        ref = oa.attend_head(q[:, l * Hl + hl], k_hat, v_hat)
+        e_s, e_l = G.rel_l2(os_[:, l * Hl + hl], ref), G.rel_l2(out_l[l][:, hl], ref)
+        G.log(f"stacked layers: layer {l} head {hl}: rel-L2 stacked {e_s:.3g}, per-layer {e_l:.3g} (tol {OUT_TOL})")
+        assert e_s <= OUT_TOL and e_l <= OUT_TOL
