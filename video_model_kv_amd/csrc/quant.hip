@@ -396,10 +396,12 @@ __global__ __launch_bounds__(256) void k_quant_pack_tile(PackBatch pb, int tiles
 // Mixed layout (a per-head channel order perm: the 4-bit class first, then the
 // 2-bit class, each cut into runs of `group`), same tiles as the uniform
 // kernel, in three phases:
-//   (1) the residuals of the tile's rows in channel order, loaded and formed as
-//       in the uniform kernel, into LDS;
-//   (2) one thread per (row, group) reads its group's residuals in storage
-//       order through perm, takes the group scale and packs the group's words
+//   (1) the residuals of the tile's rows, loaded and formed as in the uniform
+//       kernel, into LDS in storage order (channel k at its position in perm,
+//       through the inverse order, which starts as the identity so that a perm
+//       that is not a permutation still writes inside the row);
+//   (2) one thread per (row, group) reads its group's residuals as one
+//       contiguous run, takes the group scale and packs the group's words
 //       (groups never share a word: a class starts on a word boundary and
 //       `group` is a multiple of 16; positions past a class's end stay zero);
 //   (3) codes and scales leave per head as contiguous runs.
@@ -410,7 +412,7 @@ constexpr int kMixMaxGroups = 9;     // ceil(n_int4 / 16) + ceil((128 - n_int4) 
 template <bool F32>
 __global__ __launch_bounds__(256) void k_quant_pack_tile_mixed(PackArgs a) {
   __shared__ __attribute__((aligned(16))) float s_r[kTileRows][kHeadDim + 4];
-  __shared__ uint8_t s_perm[kTileHeads][kHeadDim];
+  __shared__ uint8_t s_inv[kTileHeads][kHeadDim];     // storage position of each channel
   __shared__ uint32_t s_codes[kTileRows * kMixMaxWords];
   __shared__ uint16_t s_scales[kTileRows * kMixMaxGroups];
   __shared__ float s_rtab[128];                   // fp32(1 / (1 + k / 128))
@@ -422,10 +424,13 @@ __global__ __launch_bounds__(256) void k_quant_pack_tile_mixed(PackArgs a) {
   const int i0 = (tile % ntb) * tg.T, h0 = (tile / ntb) * tg.HB;
   const int rows = tg.T * tg.HB;
   const int tmax = a.N - 1 - i0, hmax = a.H - 1 - h0;
+  for (int i = tid; i < kTileHeads * kHeadDim; i += 256) s_inv[i >> 7][i & (kHeadDim - 1)] = (uint8_t)(i & (kHeadDim - 1));
+  __syncthreads();
   for (int i = tid; i < kTileHeads * kHeadDim; i += 256) {
-    const int hh = i >> 7, k = i & (kHeadDim - 1);
-    s_perm[hh][k] = a.perm[(int64_t)(h0 + min(hh, hmax)) * kHeadDim + k] & (kHeadDim - 1);
+    const int hh = i >> 7, p = i & (kHeadDim - 1);
+    s_inv[hh][a.perm[(int64_t)(h0 + min(hh, hmax)) * kHeadDim + p] & (kHeadDim - 1)] = (uint8_t)p;
   }
+  __syncthreads();
   // (1) residuals; rows outside the tile read a clamped valid row
   const int part = tid & 15, k0 = part * 8;
   constexpr int kIt = kTileRows * 16 / 256;
@@ -456,20 +461,19 @@ __global__ __launch_bounds__(256) void k_quant_pack_tile_mixed(PackArgs a) {
     const uint32_t c4[4] = {c.x, c.y, c.z, c.w};
 #pragma unroll
     for (int e = 0; e < 8; ++e) cv[e] = bf16_bits_to_f32((c4[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
-    float* dst = &s_r[lr][k0];
-    *reinterpret_cast<float4*>(dst) = make_float4(yv[0] - cv[0], yv[1] - cv[1], yv[2] - cv[2], yv[3] - cv[3]);
-    *reinterpret_cast<float4*>(dst + 4) = make_float4(yv[4] - cv[4], yv[5] - cv[5], yv[6] - cv[6], yv[7] - cv[7]);
+    const uint8_t* inv = s_inv[hh];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) s_r[lr][inv[k0 + e]] = yv[e] - cv[e];
   }
   __syncthreads();
   // (2) one (row, group) per thread
   const int NG = a.groups, W = a.words;
   for (int idx = tid; idx < rows * NG; idx += 256) {
     const int lr = idx / NG, g = idx - lr * NG;
-    const uint8_t* pr = s_perm[lr % tg.HB];
-    const float* rr = s_r[lr];
+    const float* rr = s_r[lr] + 0;
     const GroupInfo gi = group_info(g, a.bits, a.group, a.n_int4, a.int4_words);
     float amax = 0.0f;
-    for (int e = 0; e < gi.len; ++e) amax = fmaxf(amax, fabsf(rr[pr[gi.start + e]]));
+    for (int e = 0; e < gi.len; ++e) amax = fmaxf(amax, fabsf(rr[gi.start + e]));
     const float qmax = (float)((1 << (gi.bits - 1)) - 1);
     const uint32_t sbits = f32_to_bf16_bits(amax / qmax);
     const float S = bf16_bits_to_f32(sbits);
@@ -480,7 +484,7 @@ __global__ __launch_bounds__(256) void k_quant_pack_tile_mixed(PackArgs a) {
       float r8[8];
       const int n = min(8, gi.len - e0);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) r8[e] = e < n ? rr[pr[gi.start + e0 + e]] : 0.0f;
+      for (int e = 0; e < 8; ++e) r8[e] = e < n ? rr[gi.start + e0 + e] : 0.0f;
       if (gi.bits == 4) {
         uint32_t w = pack8_codes<4>(r8, S, sbits, s_rtab);
         if (n < 8) w &= (1u << (4 * n)) - 1u;
