@@ -51,7 +51,7 @@ def parse():
     p.add_argument("--workload", type=int, default=5, help="headline workload id (2: 5 s cache, 3, 4, 5: one minute)")
     p.add_argument("--extra", default="2,3,4,6",
                    help="workload ids timed after the headline ('' for none; 6: QuantWM with QSAC's range factor)")
-    p.add_argument("--batch", type=int, default=12, help="problems per qkv_quantize_chunks call (1-16)")
+    p.add_argument("--batch", type=int, default=16, help="problems per qkv_quantize_chunks call (1-16)")
     p.add_argument("--no-ar", action="store_true", help="skip the autoregressive rollout of the headline workload")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--kernel-reps", type=int, default=5)

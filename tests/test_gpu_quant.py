@@ -512,6 +512,34 @@ def test_quantize_batch_bench_shape_matches_single():
     _batch_vs_single(probs)
 
 
+def test_quantize_batch_headline_launch_matches_single():
+    """The headline bench's launch: K and V of eight chunks of the one-minute
+    cache (16 problems of 32 heads x 6,240 tokens, C = 256; keys in the mixed
+    INT4/INT2 layout) in one call -- one assign workgroup per head -- against
+    single calls, and one K and one V head of the first chunk against the
+    oracle."""
+    t = G.torch()
+    wl = synth.workload(5)
+    _, _, perm = _side(wl, "K")
+    pd = t.from_numpy(perm.astype(np.uint8)).to(G.dev())
+    probs, x0 = [], {}
+    for c in range(8):
+        for tensor in ("K", "V"):
+            x = synth.kv_chunk(wl, tensor, c)
+            if c == 0:
+                x0[tensor] = x
+            probs.append((G.config_of(wl, tensor), G.to_dev(x, "bf16"), (None, pd, None) if tensor == "K" else None))
+    G.log(f"headline batch: {len(probs)} problems of N={wl.chunk_tokens}, H={wl.n_heads}")
+    packs = _batch_vs_single(probs)
+    for i, (tensor, h) in enumerate((("K", 7), ("V", 26))):
+        kw = dict(n_clusters=wl.n_clusters, bits=2, group=32, iters=10)
+        if tensor == "K":
+            kw.update(n_int4=wl.n_int4, perm=perm[h])
+        res = G.oracle_problems([(x0[tensor][:, h], kw)])
+        near = G.compare_chunk(f"headline-{tensor}", wl, tensor, x0[tensor], packs[i], probs[i][0], {h: res[0]}, [h])
+        G.log(f"headline batch: chunk 0 {tensor} head {h} bit-exact against the oracle; near-ties {near}")
+
+
 def test_quantize_batch_all_ties_overflow_list():
     """Every token of a problem identical: all centroids tie, every token is a
     close call (more than the workgroup's LDS list holds, so the per-wave
