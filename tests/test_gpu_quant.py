@@ -31,6 +31,9 @@ SMALL = [
     ("field-K-ragged", 2, dict(n_heads=2, n_clusters=64), "K", 1500),
     ("field-V-ragged", 2, dict(n_heads=2, n_clusters=64), "V", 1500),
     ("qsac-K", 4, dict(n_heads=2, n_clusters=64), "K", 1300),
+    # three centroid blocks (the bf16 sweep pads to an even count) and an odd
+    # number of 32-token sub-blocks (the last item computes a spare one)
+    ("field-K-96-clusters-odd", 2, dict(n_heads=2, n_clusters=96), "K", 1100),
 ]
 
 

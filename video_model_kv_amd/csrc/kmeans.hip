@@ -134,9 +134,11 @@ __global__ __launch_bounds__(64) void k_prep(KmBatch b) {
 // Assign: one workgroup per (head, range of 32-token sub-blocks), eight waves.
 // The head's operand planes (2 x C rows of 128 bf16, ~136 KB padded) are
 // loaded into LDS once and stay resident; each wave then sweeps all centroid
-// blocks for 64 tokens at a time (32 for an odd last sub-block), with the next
-// tokens' loads in flight.  Close calls go to an LDS list, flushed to the
-// global queue with one atomic per workgroup.
+// blocks for 64 tokens at a time (fp32 tokens: 32).  bf16 sweeps are
+// software-pipelined: the MFMAs of centroid block k + 1 alternate with the
+// screening of block k, and the next item's tokens load into the operand
+// registers once the last block's MFMAs are issued.  Close calls go to an LDS
+// list and are re-decided at the end of the workgroup.
 constexpr int kAsgWaves = 8;
 constexpr int kAsgThreads = kAsgWaves * 64;
 constexpr int kAsgMaxC = 256;
@@ -179,19 +181,20 @@ __global__ __launch_bounds__(kAsgThreads) void k_assign(KmBatch b, int G) {
   const int nsb = sb1 - sb0;
   const int npair = F32 ? 0 : nsb >> 1, nitems = F32 ? nsb : npair + (nsb & 1);
   const int Cp = (C + 31) & ~31;                 // whole 32-row blocks; rows past C never win (norm +inf)
+  const int Cs = F32 ? Cp : (C + 63) & ~63;      // rows of the main sweep (bf16: an even block count)
   const uint16_t* y16 = reinterpret_cast<const uint16_t*>(y.ptr);
   const int64_t hoff = (int64_t)h * y.stride_head + half * 8;
 
-  // bf16 tokens of one item (nt sub-blocks; clamped rows past N are masked later)
+  // bf16 tokens of one item: always two sub-blocks, rows clamped to the
+  // head's last token (an odd last sub-block computes a spare one whose
+  // results are dropped)
   uint4 raw[2][8];
-  auto load_tokens = [&](int sb, int nt) __attribute__((always_inline)) {
+  auto load_tokens = [&](int sb) __attribute__((always_inline)) {
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-      if (t < nt) {                              // wave-uniform
-        const int64_t base = (int64_t)min(sb * 32 + t * 32 + col, N - 1) * y.stride_token + hoff;
+      const int64_t base = (int64_t)min(sb * 32 + t * 32 + col, N - 1) * y.stride_token + hoff;
 #pragma unroll
-        for (int s = 0; s < 8; ++s) raw[t][s] = *reinterpret_cast<const uint4*>(y16 + base + s * 16);
-      }
+      for (int s = 0; s < 8; ++s) raw[t][s] = *reinterpret_cast<const uint4*>(y16 + base + s * 16);
     }
   };
 
@@ -205,7 +208,7 @@ __global__ __launch_bounds__(kAsgThreads) void k_assign(KmBatch b, int G) {
       for (int q = 0; q < kAsgMaxC / 64; ++q) {
         const int j = q * 64 + lane;
         if (j < C) dma4(cn + h * C + j, &sCn[q * 64]);   // lane i lands at sCn[q*64 + i]
-        else if (j < Cp) sCn[j] = INFINITY;
+        else if (j < Cs) sCn[j] = INFINITY;
       }
     } else if (wave == 1) {
       if (w) {
@@ -220,10 +223,10 @@ __global__ __launch_bounds__(kAsgThreads) void k_assign(KmBatch b, int G) {
       sNext = kAsgWaves;
     }
     // planes: 1 KB of the padded image per wave instruction; pad pieces and
-    // rows in [C, Cp) take copies of valid pieces
+    // rows in [C, Cs) take copies of valid pieces
     const uint16_t* ph = planes + (int64_t)h * 2 * C * kHeadDim;
     constexpr int kPlaneBytes = kAsgMaxC * kPitch * 2;
-    const int nch = (Cp * kPitch * 2 + 1023) >> 10;          // 1 KB chunks per plane
+    const int nch = (Cs * kPitch * 2 + 1023) >> 10;          // 1 KB chunks per plane
     for (int k = wave; k < 2 * nch; k += kAsgWaves) {
       const int p = k >= nch ? 1 : 0;
       const int a = (k - p * nch) * 1024 + lane * 16;        // byte offset in the plane image
@@ -232,7 +235,7 @@ __global__ __launch_bounds__(kAsgThreads) void k_assign(KmBatch b, int G) {
             reinterpret_cast<char*>(&sP[0][0][0]) + p * kPlaneBytes + (k - p * nch) * 1024);
     }
     asm volatile("" ::: "memory");
-    if constexpr (!F32) load_tokens(sb0 + kPer * wave, 2);   // past the range: clamped, unused
+    if constexpr (!F32) load_tokens(sb0 + kPer * wave);      // past the range: clamped, unused
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(F32 ? 0 : 16));   // vmcnt counts in issue order
     __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
     asm volatile("" ::: "memory");
@@ -333,14 +336,6 @@ __global__ __launch_bounds__(kAsgThreads) void k_assign(KmBatch b, int G) {
         }
       }
     } else {
-      if (tok0 + 64 > N) {                       // the head's last item: rows past N are zero
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          const bool ok = tok0 + t * 32 + col < N;
-#pragma unroll
-          for (int s = 0; s < 8; ++s) raw[t][s] = ok ? raw[t][s] : make_uint4(0, 0, 0, 0);
-        }
-      }
 #pragma unroll
       for (int t = 0; t < 2; ++t)
 #pragma unroll
@@ -374,7 +369,6 @@ __global__ __launch_bounds__(kAsgThreads) void k_assign(KmBatch b, int G) {
             }
           }
       }
-      if (next < nitems) load_tokens(sb0 + kPer * next, next < npair ? 2 : 1);
     }
 
     int spill = 0;                               // 1 + token of a close call past the list
@@ -422,6 +416,41 @@ __global__ __launch_bounds__(kAsgThreads) void k_assign(KmBatch b, int G) {
           }
         }
       };
+      // The same MFMAs for bf16 tokens, with explicit LDS bases (each plane
+      // and the norms lie beyond the 16-bit offset field of one another, so
+      // each gets its own base) and the next k-slice's operands requested one
+      // slice ahead.
+      auto mma_p = [&](f32x16 (&acc)[NT], int cb) __attribute__((always_inline)) {
+        const uint4* ph = reinterpret_cast<const uint4*>(&sP[0][cb + col][half * 8]);
+        const uint4* pl = reinterpret_cast<const uint4*>(&sP[1][cb + col][half * 8]);
+        const float4* pn = reinterpret_cast<const float4*>(&sCn[cb + half * 4]);
+        uint4 ah = ph[0], al = pl[0];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float4 c4 = pn[2 * q];
+#pragma unroll
+          for (int t = 0; t < NT; ++t) {
+            acc[t][4 * q] = c4.x;
+            acc[t][4 * q + 1] = c4.y;
+            acc[t][4 * q + 2] = c4.z;
+            acc[t][4 * q + 3] = c4.w;
+          }
+        }
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+          uint4 nh = ah, nl = al;
+          if (s + 1 < 8) {
+            nh = ph[2 * (s + 1)];
+            nl = pl[2 * (s + 1)];
+          }
+#pragma unroll
+          for (int t = 0; t < NT; ++t) acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ah), yh[t][s], acc[t], 0, 0, 0);
+#pragma unroll
+          for (int t = 0; t < NT; ++t) acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(al), yh[t][s], acc[t], 0, 0, 0);
+          ah = nh;
+          al = nl;
+        }
+      };
       // rows increase with r within the lane, so strict '<' keeps the lowest
       // index among equal values
       auto top2 = [&](const f32x16 (&acc)[NT]) __attribute__((always_inline)) {
@@ -440,14 +469,94 @@ __global__ __launch_bounds__(kAsgThreads) void k_assign(KmBatch b, int G) {
           }
         }
       };
-      for (int cb = 0; cb < Cp; cb += 32) {
-        f32x16 acc[NT];
-        mma(acc, cb);
-        top2(acc);
+      // One screening step of top2: value v (token sub-block v % NT, element v / NT).
+      auto step = [&](const f32x16 (&acc)[NT], int v) __attribute__((always_inline)) {
+        const int t = v % NT, r = v / NT;
+        const int j = (r >> 2) * 8 + (r & 3);
+        const float x = acc[t][r];
+        const bool l = x < b1[t];
+        b2[t] = __builtin_amdgcn_fmed3f(b1[t], b2[t], x);
+        b1[t] = l ? x : b1[t];
+        rel[t] = l ? j : rel[t];
+      };
+      // The MFMAs of block cbn into an (from the norms), each followed by one
+      // screening step of ap, the previous block (same order of values as
+      // top2, so the same result); the scheduling barriers keep that order,
+      // so the matrix core runs while the wave screens.
+      auto stage = [&](f32x16 (&an)[NT], int cbn, const f32x16 (&ap)[NT]) __attribute__((always_inline)) {
+        const uint4* ph = reinterpret_cast<const uint4*>(&sP[0][cbn + col][half * 8]);
+        const uint4* pl = reinterpret_cast<const uint4*>(&sP[1][cbn + col][half * 8]);
+        const float4* pn = reinterpret_cast<const float4*>(&sCn[cbn + half * 4]);
+        uint4 ah = ph[0], al = pl[0];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float4 c4 = pn[2 * q];
+#pragma unroll
+          for (int t = 0; t < NT; ++t) {
+            an[t][4 * q] = c4.x;
+            an[t][4 * q + 1] = c4.y;
+            an[t][4 * q + 2] = c4.z;
+            an[t][4 * q + 3] = c4.w;
+          }
+        }
+#pragma unroll
+        for (int t = 0; t < NT; ++t) rel[t] -= 32;
+#pragma unroll
+        for (int v = 0; v < NT; ++v) step(ap, v);      // while the operands arrive
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+          uint4 nh = ah, nl = al;
+          if (s + 1 < 8) {
+            nh = ph[2 * (s + 1)];
+            nl = pl[2 * (s + 1)];
+          }
+#pragma unroll
+          for (int pln = 0; pln < 2; ++pln) {
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+              an[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(pln ? al : ah), yh[t][s], an[t], 0, 0, 0);
+              const int v = NT + (s * 2 + pln) * NT + t;
+              if (v < 16 * NT) step(ap, v);
+              __builtin_amdgcn_sched_barrier(0);
+            }
+          }
+          ah = nh;
+          al = nl;
+        }
+      };
+      if constexpr (F32) {
+        for (int cb = 0; cb < Cp; cb += 32) {
+          f32x16 acc[NT];
+          mma(acc, cb);
+          top2(acc);
+        }
+      } else {
+        // Software pipeline over the centroid blocks (stage): the MFMAs of
+        // block k + 1 alternate with the screening of block k, so the matrix
+        // core works while the wave screens.  After the last block's MFMAs
+        // the token registers are free: the next item's tokens load into
+        // them while the last block is screened.
+        // The block count is even (Cs = Cp rounded up to 64 rows; the extra
+        // rows hold copies of a valid row with norm +inf, so they never win
+        // and leave the second best alone).
+        f32x16 accA[NT], accB[NT];
+        const int nb = Cs >> 5;
+        mma_p(accA, 0);
+        for (int k = 0; k + 2 < nb; k += 2) {    // blocks k (in accA), k + 1, k + 2
+          stage(accB, (k + 1) * 32, accA);
+          stage(accA, (k + 2) * 32, accB);
+        }
+        stage(accB, (nb - 1) * 32, accA);
+        // the token registers are dead once the last block's MFMAs are issued
+        // (unconditional, so no branch splits the stage from the screening:
+        // past the last item a valid item is read again and not used)
+        load_tokens(sb0 + kPer * min(next, nitems - 1));
+        top2(accB);
       }
       int bidx[NT];
 #pragma unroll
-      for (int t = 0; t < NT; ++t) bidx[t] = rel[t] + Cp - 32 + half * 4;
+      for (int t = 0; t < NT; ++t) bidx[t] = rel[t] + Cs - 32 + half * 4;
       // Close calls -- the two best screened values within the screening
       // error bound (screen_threshold) -- are listed for the float64
       // re-decision at the end.
@@ -462,7 +571,7 @@ __global__ __launch_bounds__(kAsgThreads) void k_assign(KmBatch b, int G) {
         }
         const float yn = ynorm[t] + __shfl_xor(ynorm[t], 32);
         const int tok = tok0 + t * 32 + col;
-        if (half == 0 && tok < N) {
+        if (half == 0 && t < nt && tok < N) {
           labels[(int64_t)h * N + tok] = (uint8_t)bidx[t];
           if (!(second - b1[t] > screen_threshold<F32>(yn, b1[t], sCn[bidx[t]], cmax2))) {
             const int slot = atomicAdd(&sAmbN, 1);
@@ -472,12 +581,8 @@ __global__ __launch_bounds__(kAsgThreads) void k_assign(KmBatch b, int G) {
         }
       }
     };
-    if constexpr (F32) {
-      sweep(std::integral_constant<int, 1>{});
-    } else {
-      if (nt == 2) sweep(std::integral_constant<int, 2>{});
-      else sweep(std::integral_constant<int, 1>{});
-    }
+    if constexpr (F32) sweep(std::integral_constant<int, 1>{});
+    else sweep(std::integral_constant<int, 2>{});
     // the list is full (a pathological input): this wave decides its
     // overflowing close calls one at a time over all centroids
     for (uint64_t m = __ballot(spill != 0); m; m &= m - 1) {
