@@ -326,6 +326,31 @@ def _side(wl, tensor):
     return w, u, perm
 
 
+def test_incremental_updates_with_a_head_outside_the_certificate():
+    """Three heads of bf16 values through ten k-means iterations: heads 0 and 2
+    pass the head-wide exactness certificate and take the incremental updates
+    after the first; head 1 holds one magnitude of 2^-100 in channel 9 (its
+    range exceeds the certificate) and keeps the full update.  Every section of
+    the packed chunk and x_hat bit-exact against the oracle."""
+    wl = synth.workload(2, n_heads=3, n_clusters=64)
+    n = 1500
+    x = synth.kv_tokens(wl, "V", 0, n).copy()
+    x[700, 1, 9] = np.float32(2.0 ** -100)
+    cfg = G.config_of(wl, "V")
+    G.log(f"incremental updates: H=3 N={n} C=64, head 1 outside the certificate")
+    packed = G.quantize(cfg, G.to_dev(x, wl.dtype))
+    jobs = [(x[:, h], dict(n_clusters=wl.n_clusters, bits=wl.bits, group=wl.group, n_stages=wl.n_stages,
+                           iters=wl.kmeans_iters)) for h in range(wl.n_heads)]
+    res = dict(enumerate(G.oracle_problems(jobs)))
+    G.compare_chunk("incremental", wl, "V", x, packed, cfg, res, range(wl.n_heads))
+    t = G.torch()
+    out = t.empty((n, wl.n_heads, 128), dtype=t.float32, device=G.dev())
+    qk.qkv_dequantize(cfg, n, packed, out)
+    o = out.cpu().numpy()
+    for h in range(wl.n_heads):
+        assert np.array_equal(o[:, h].view(np.uint32), res[h].x_hat.view(np.uint32)), f"h{h}: x_hat"
+
+
 @pytest.mark.parametrize("case", FREE, ids=[c[0] for c in FREE])
 def test_quantize_chunk_free_running(case):
     name, cid, over, tensor, n, rtn = case

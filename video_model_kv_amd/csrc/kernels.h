@@ -41,11 +41,25 @@ struct KmItem {
   uint16_t* cent_bf16;           // bf16 centroids written by launch_centroid_bf16
   int* grp_off;                  // [H][C + 1] cluster offsets from launch_kmeans_group, or null
   uint16_t* grp_list;            // [H][N] tokens ordered by cluster (same producer)
+  // Incremental updates (bf16 tokens, grouped heads), or all null: the exact
+  // float64 cluster sums and member counts of the last update, the head's
+  // channel magnitude range (the certificate that every subset sum of its
+  // tokens is exact in float64), and the labels of the last two updates.
+  double* dsum;                  // [H][C][128]
+  int32_t* dcnt;                 // [H][C]
+  uint32_t* emag;                // [H][2][128]: max magnitude, 0xFFFF - (min nonzero magnitude - 1)
+  uint32_t* cert;                // [H]: 1 when the head passes the certificate (launch_kmeans_cert)
+  uint8_t* prev;                 // [2][H][N] labels at the previous updates (alternating)
 };
 constexpr int kKmMaxBatch = 16;
+// inc: 0 plain k-means; 1 the first iteration of an incremental stage (the
+// update also records dsum, dcnt, emag and the labels); 2 a later iteration
+// (heads that pass the certificate take launch_kmeans_update_delta, the
+// others the full update).  iter: the iteration index (0-based).
 struct KmBatch {
   int n, dtype, H, C;
   int64_t N;
+  int inc, iter;
   KmItem it[kKmMaxBatch];
 };
 hipError_t launch_kmeans_init(const KmBatch& b, hipStream_t s);
@@ -62,6 +76,13 @@ hipError_t launch_kmeans_update(const KmBatch& b, bool refresh, hipStream_t s);
 // at most kGroupMaxTokens tokens); the update then reads its clusters' members from there.
 constexpr int kGroupMaxTokens = 8192;
 hipError_t launch_kmeans_group(const KmBatch& b, hipStream_t s);
+// Incremental update (inc == 2): for every head that passes the certificate,
+// the tokens whose label changed since the previous update move between the
+// exact sums of their old and new clusters; the touched clusters' centroids
+// (and, with refresh, planes and norms) are rewritten.
+hipError_t launch_kmeans_update_delta(const KmBatch& b, bool refresh, hipStream_t s);
+// After the first update of an incremental stage: cert[h] from emag.
+hipError_t launch_kmeans_cert(const KmBatch& b, hipStream_t s);
 // QSAC's residual-range factor (gram.hip): for every problem of the batch,
 // w_out[h][k] = fl32(wq[h][k] * fl32(rho * rho)), rho = fl32(max - min) of
 // channel k of head h over the problem's tokens.  part: [H][kRangeSplits][2][128]

@@ -787,6 +787,68 @@ __global__ __launch_bounds__(kAsgThreads) void k_assign(KmBatch b, int G) {
   }
 }
 
+// The head-wide certificate of the incremental update, per channel over all
+// of the head's tokens (emag, recorded by the first update of the stage):
+// every nonzero bf16 magnitude is an integer multiple of 2^(emin - 134) and
+// below 2^(emax - 126) (biased exponents of the smallest nonzero and the
+// largest magnitude), so a signed sum of at most N of them is an integer
+// multiple of that unit below 2^(emax - emin + lg + 8) units, lg >= log2 N:
+// exact in float64 when emax - emin + lg <= 44 (the bound of the per-cluster
+// certificate, with N for the cluster size).  Every intermediate value of an
+// incremental update is such a sum (a set of distinct tokens), so the sums it
+// keeps are the exact sums.  Wave-uniform.
+__device__ __forceinline__ bool head_exact(const KmItem& it, int h, int N) {
+  const int lane = threadIdx.x & 63;
+  const int lg = 32 - __builtin_clz((unsigned)max(N, 1));
+  bool ok = true;
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int k = q * 64 + lane;
+    const uint32_t mx = it.emag[(int64_t)h * 2 * kHeadDim + k];
+    const uint32_t mn = 0xFFFFu - it.emag[((int64_t)h * 2 + 1) * kHeadDim + k];   // min nonzero magnitude - 1
+    const int emax = (int)(mx >> 7), emin = max((int)(((mn + 1u) >> 7) & 0xFFu), 1);
+    ok = ok && (mn == 0xFFFFu || (emax < 0xFF && emax - emin + lg <= 44));
+  }
+  return __ballot(!ok) == 0;
+}
+
+// Centroid j of head h from its exact sum (channels c4 .. c4 + 3 per lane of a
+// 32-lane group): c = fl32(sum / n); with refresh the operand planes (-2 w c,
+// bf16 hi + lo) and the weighted norm (float64 over the group's lanes, rounded
+// to float32).  Called by the whole lane group.
+__device__ __forceinline__ void centroid_from_sum(const KmItem& it, int h, int C, int j, int c4, const double* sv,
+                                                  int n, bool refresh) {
+  const int lane = threadIdx.x & 63;
+  const float* __restrict__ w = it.w;
+  float cv[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) cv[e] = (float)(sv[e] / (double)n);
+  *reinterpret_cast<float4*>(it.c + ((int64_t)h * C + j) * kHeadDim + c4) = make_float4(cv[0], cv[1], cv[2], cv[3]);
+  if (refresh) {
+    double nrm = 0.0;
+    uint32_t hw[2], lw[2];
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      hw[p] = lw[p] = 0u;
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int k = c4 + 2 * p + e;
+        const float wv = w ? w[h * kHeadDim + k] : 1.0f;
+        const float bb = -2.0f * (wv * cv[2 * p + e]);
+        const uint32_t hi = f32_to_bf16_bits(bb);
+        hw[p] |= hi << (16 * e);
+        lw[p] |= f32_to_bf16_bits(bb - bf16_bits_to_f32(hi)) << (16 * e);
+        nrm += (double)wv * ((double)cv[2 * p + e] * (double)cv[2 * p + e]);
+      }
+    }
+    *reinterpret_cast<uint2*>(it.planes + ((int64_t)h * 2 * C + j) * kHeadDim + c4) = make_uint2(hw[0], hw[1]);
+    *reinterpret_cast<uint2*>(it.planes + ((int64_t)h * 2 * C + C + j) * kHeadDim + c4) = make_uint2(lw[0], lw[1]);
+#pragma unroll
+    for (int off = 1; off < 32; off <<= 1) nrm += __shfl_xor(nrm, off);   // within the lane group
+    if ((lane & 31) == 0) it.cn[h * C + j] = (float)nrm;
+  }
+}
+
 // Centroid update fused with the grouping of tokens by label.  One workgroup
 // per (head, 8 consecutive clusters); wave w owns clusters 2w and 2w + 1 of
 // the group.  The head's labels are scanned in windows of kUpdWindow tokens:
@@ -822,7 +884,11 @@ __global__ __launch_bounds__(256) void k_group(KmBatch b) {
   __shared__ int s_c[256], s_o[257];
   __shared__ uint16_t s_l[kUpdWindow];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (b.inc == 2 && it.cert[h]) return;           // the incremental update takes this head
   const uint8_t* lab = it.labels + (int64_t)h * N;
+  // the first update of an incremental stage: these labels are the previous
+  // ones of the next update (alternate buffer 1)
+  uint8_t* rec = b.inc == 1 ? it.prev + ((int64_t)b.H + h) * N : nullptr;
   uint32_t kk[kUpdWindow / 256];                 // labels of tokens tid*32 .. tid*32 + 31
   {
     const int i0 = tid * 32;
@@ -831,6 +897,10 @@ __global__ __launch_bounds__(256) void k_group(KmBatch b) {
       const uint32_t* l4 = reinterpret_cast<const uint32_t*>(lab + i0);
 #pragma unroll
       for (int q = 0; q < 8; ++q) wv[q] = l4[q];
+      if (rec) {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) reinterpret_cast<uint32_t*>(rec + i0)[q] = wv[q];
+      }
 #pragma unroll
       for (int x = 0; x < 32; ++x) kk[x] = (wv[x >> 2] >> (8 * (x & 3))) & 0xFFu;
     } else {
@@ -839,6 +909,7 @@ __global__ __launch_bounds__(256) void k_group(KmBatch b) {
         const int i = i0 + x;
         const uint32_t l = lab[min(i, N - 1)];
         kk[x] = i < N ? l : 0xFFFFFFFFu;
+        if (rec && i < N) rec[i] = (uint8_t)l;
       }
     }
   }
@@ -899,12 +970,16 @@ __global__ __launch_bounds__(256, 4) void k_update(KmBatch b, int refresh) {
   __shared__ int s_cnt[kUpdClusters], s_off[kUpdClustersG + 1], s_cur[kUpdClusters];
   __shared__ uint16_t s_mem[kUpdWindow];
   __shared__ int s_wtot[4];
+  __shared__ uint32_t s_emag[2][kHeadDim];      // inc == 1: this workgroup's magnitude range per channel
   const int groups = (C + CPG - 1) / CPG;
   const uint32_t logical = xcd_remap(blockIdx.x, (uint32_t)(n_heads * groups));
   const int h = logical / groups, c0 = (logical % groups) * CPG;
   const int N = (int)y.n_tokens;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   if (blockIdx.x == 0 && tid == 0 && amb_count) *amb_count = 0;   // the close-call count of the next assign
+  if (b.inc == 2 && it.cert[h]) return;           // the incremental update takes this head
+  const bool record = GROUPED && !F32 && b.inc == 1;  // the first update of an incremental stage
+  if (record) s_emag[tid >> 7][tid & (kHeadDim - 1)] = 0u;   // 256 threads: both halves (synchronised below)
   const uint8_t* lab = labels + (int64_t)h * N;
   const int64_t hoff = (int64_t)h * y.stride_head + lane * 2;
   const bool plain = !F32 && N <= kUpdWindow;   // certified float64 sums
@@ -1111,40 +1186,30 @@ __global__ __launch_bounds__(256, 4) void k_update(KmBatch b, int refresh) {
       }
       const uint64_t bad = __ballot(!ok);
       const bool okc[2] = {(uint32_t)bad == 0u, (uint32_t)(bad >> 32) == 0u};
+      if (record) {                              // the head's magnitude range (both clusters of the wave)
+#pragma unroll
+        for (int p = 0; p < 2; ++p)
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            const int k = c4 + 2 * p + e;
+            if (mx[p][e]) atomicMax(&s_emag[0][k], (uint32_t)mx[p][e]);
+            if (mn[p][e] != 0xFFFF) atomicMax(&s_emag[1][k], 0xFFFFu - (uint32_t)mn[p][e]);
+          }
+      }
       // certified clusters: lane group 0 finishes the first, group 1 the second
       {
         const int cc = g;
         const int n = cc == 0 ? mb - ma : mc - mb;
         const int j = c0 + p * 2 + cc;
-        if (okc[cc] && n > 0 && j < C) {
-          float cv[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) cv[e] = (float)(sv[e] / (double)n);
-          *reinterpret_cast<float4*>(c + ((int64_t)h * C + j) * kHeadDim + c4) = make_float4(cv[0], cv[1], cv[2], cv[3]);
-          if (planes) {   // operand planes (-2 w c) and weighted norm for the next assign
-            double nrm = 0.0;
-            uint32_t hw[2], lw[2];
-#pragma unroll
-            for (int p = 0; p < 2; ++p) {
-              hw[p] = lw[p] = 0u;
-#pragma unroll
-              for (int e = 0; e < 2; ++e) {
-                const int k = c4 + 2 * p + e;
-                const float wv = w ? w[h * kHeadDim + k] : 1.0f;
-                const float bb = -2.0f * (wv * cv[2 * p + e]);
-                const uint32_t hi = f32_to_bf16_bits(bb);
-                hw[p] |= hi << (16 * e);
-                lw[p] |= f32_to_bf16_bits(bb - bf16_bits_to_f32(hi)) << (16 * e);
-                nrm += (double)wv * ((double)cv[2 * p + e] * (double)cv[2 * p + e]);
-              }
-            }
-            *reinterpret_cast<uint2*>(planes + ((int64_t)h * 2 * C + j) * kHeadDim + c4) = make_uint2(hw[0], hw[1]);
-            *reinterpret_cast<uint2*>(planes + ((int64_t)h * 2 * C + C + j) * kHeadDim + c4) = make_uint2(lw[0], lw[1]);
-#pragma unroll
-            for (int off = 1; off < 32; off <<= 1) nrm += __shfl_xor(nrm, off);   // within the lane group
-            if ((lane & 31) == 0) cn[h * C + j] = (float)nrm;
+        if (record && j < C) {                   // exact sums and counts for the incremental updates
+          if (okc[cc]) {
+            double2* ds = reinterpret_cast<double2*>(it.dsum + ((int64_t)h * C + j) * kHeadDim + c4);
+            ds[0] = make_double2(sv[0], sv[1]);
+            ds[1] = make_double2(sv[2], sv[3]);
           }
+          if ((lane & 31) == 0) it.dcnt[h * C + j] = n;
         }
+        if (okc[cc] && n > 0 && j < C) centroid_from_sum(it, h, C, j, c4, sv, n, planes != nullptr);
       }
 #pragma unroll
       for (int cc = 0; cc < 2; ++cc) {
@@ -1172,6 +1237,182 @@ __global__ __launch_bounds__(256, 4) void k_update(KmBatch b, int refresh) {
     __syncthreads();                           // the lists are rebuilt for the next window
   }
   if constexpr (!GROUPED) finish_pair(wave);
+  if (record) {                                  // this workgroup's clusters into the head's range
+    const uint32_t v = s_emag[tid >> 7][tid & (kHeadDim - 1)];
+    if (v) atomicMax(&it.emag[((int64_t)h * 2 + (tid >> 7)) * kHeadDim + (tid & (kHeadDim - 1))], v);
+  }
+}
+
+// Incremental update (the iterations after the first of a stage, bf16 heads
+// that pass head_exact): kDeltaSplit workgroups per (problem, head).  Each
+// scans the head's labels against those of the previous update, counts the
+// tokens that moved into and out of every cluster and lists them by cluster in
+// LDS (counting sort); the touched clusters, in index order, are dealt
+// round-robin to the workgroups and then to their eight 32-lane groups.  A
+// lane group (four channels per lane) adds its cluster's arriving rows to the
+// kept float64 sum and subtracts the leaving ones -- exact under the
+// certificate, so the order is free and the sum equals the full update's --
+// updates the member count and forms the centroid with centroid_from_sum; a
+// cluster left empty keeps its centroid.  The workgroup of split 0 also copies
+// the current labels into the other alternate buffer, where the next update
+// finds them as its previous labels.
+constexpr int kDeltaSplit = 4;
+
+__global__ __launch_bounds__(256) void k_update_delta(KmBatch b, int refresh) {
+  const KmItem& it = b.it[blockIdx.y];
+  const int C = b.C, N = (int)b.N, n_heads = b.H;
+  const uint32_t logical = xcd_remap(blockIdx.x, (uint32_t)(n_heads * kDeltaSplit));
+  const int h = logical / kDeltaSplit, r = logical % kDeltaSplit;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (!it.cert[h]) return;                       // the full update took this head
+  __shared__ int s_cnt[256], s_off[257], s_cur[256];
+  __shared__ uint16_t s_item[2 * kUpdWindow];    // token, | 0x8000 when it leaves the cluster
+  __shared__ uint8_t s_touch[256];
+  __shared__ int s_nt;
+  const uint8_t* cur = it.labels + (int64_t)h * N;
+  const uint8_t* prv = it.prev + ((int64_t)(b.iter & 1) * n_heads + h) * N;
+  uint8_t* nxt = it.prev + ((int64_t)((b.iter + 1) & 1) * n_heads + h) * N;
+  uint32_t kc[kUpdWindow / 256], kp[kUpdWindow / 256];   // labels of tokens tid*32 .. tid*32 + 31: now, before
+  {
+    const int i0 = tid * 32;
+    if ((N & 3) == 0 && i0 + 32 <= N) {
+      uint32_t wc[8], wp[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        wc[q] = reinterpret_cast<const uint32_t*>(cur + i0)[q];
+        wp[q] = reinterpret_cast<const uint32_t*>(prv + i0)[q];
+      }
+      if (r == 0) {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) reinterpret_cast<uint32_t*>(nxt + i0)[q] = wc[q];
+      }
+#pragma unroll
+      for (int x = 0; x < 32; ++x) {
+        kc[x] = (wc[x >> 2] >> (8 * (x & 3))) & 0xFFu;
+        kp[x] = (wp[x >> 2] >> (8 * (x & 3))) & 0xFFu;
+      }
+    } else {
+#pragma unroll
+      for (int x = 0; x < 32; ++x) {
+        const int i = i0 + x;
+        const uint32_t lc = cur[min(i, N - 1)], lp = prv[min(i, N - 1)];
+        kc[x] = i < N ? lc : 0u;                 // past the head: no move
+        kp[x] = i < N ? lp : 0u;
+        if (r == 0 && i < N) nxt[i] = (uint8_t)lc;
+      }
+    }
+  }
+  s_cnt[tid] = 0;
+  __syncthreads();
+#pragma unroll
+  for (int x = 0; x < 32; ++x)
+    if (kc[x] != kp[x]) {
+      atomicAdd(&s_cnt[kc[x]], 1);
+      atomicAdd(&s_cnt[kp[x]], 1);
+    }
+  __syncthreads();
+  if (wave == 0) {                               // exclusive prefix (four clusters per lane) and the touched list
+    int a[4], sum = 0, nz = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      a[e] = s_cnt[lane * 4 + e];
+      sum += a[e];
+      nz += a[e] > 0 ? 1 : 0;
+    }
+    int incl = sum, tincl = nz;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int t = __shfl_up(incl, o), tt = __shfl_up(tincl, o);
+      if (lane >= o) {
+        incl += t;
+        tincl += tt;
+      }
+    }
+    int ex = incl - sum, tp = tincl - nz;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      s_off[lane * 4 + e] = ex;
+      s_cur[lane * 4 + e] = ex;
+      ex += a[e];
+      if (a[e] > 0) s_touch[tp++] = (uint8_t)(lane * 4 + e);
+    }
+    if (lane == 63) {
+      s_off[256] = incl;
+      s_nt = tincl;
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int x = 0; x < 32; ++x)
+    if (kc[x] != kp[x]) {
+      const int tok = tid * 32 + x;
+      s_item[atomicAdd(&s_cur[kp[x]], 1)] = (uint16_t)(tok | 0x8000);
+      s_item[atomicAdd(&s_cur[kc[x]], 1)] = (uint16_t)tok;
+    }
+  __syncthreads();
+  const int nt = s_nt;
+  const int g = lane >> 5, c4 = (lane & 31) * 4;
+  const uint16_t* y16 = reinterpret_cast<const uint16_t*>(it.y);
+  const int64_t hoff4 = (int64_t)h * it.stride_head + c4;
+  // the wave's two lane groups take touched clusters base and base + kDeltaSplit
+  for (int base = r + kDeltaSplit * 2 * wave; base < nt; base += kDeltaSplit * 8) {
+    const int q = base + g * kDeltaSplit;
+    const bool live = q < nt;
+    const int j = live ? (int)s_touch[q] : 0;
+    const int i0 = live ? s_off[j] : 0, ni = live ? s_cnt[j] : 0;
+    const int nmax = max(ni, __shfl_xor(ni, 32));
+    double sv[4] = {0.0, 0.0, 0.0, 0.0};
+    const bool mine = live && j < C;
+    if (mine) {
+      const double2* ds = reinterpret_cast<const double2*>(it.dsum + ((int64_t)h * C + j) * kHeadDim + c4);
+      const double2 d0 = ds[0], d1 = ds[1];
+      sv[0] = d0.x;
+      sv[1] = d0.y;
+      sv[2] = d1.x;
+      sv[3] = d1.y;
+    }
+    int dn = 0;
+    for (int m = 0; m < nmax; m += kUpdRows) {
+      uint32_t itm[kUpdRows];
+      uint2 raw[kUpdRows];
+#pragma unroll
+      for (int q2 = 0; q2 < kUpdRows; ++q2) {
+        itm[q2] = s_item[i0 + min(m + q2, max(ni - 1, 0))];   // past the group's items: loaded, not added
+        raw[q2] = *reinterpret_cast<const uint2*>(y16 + (int64_t)(itm[q2] & 0x7FFFu) * it.stride_token + hoff4);
+      }
+#pragma unroll
+      for (int q2 = 0; q2 < kUpdRows; ++q2) {
+        if (m + q2 < ni) {
+          const bool out = (itm[q2] & 0x8000u) != 0;
+          const uint32_t w2[2] = {raw[q2].x, raw[q2].y};
+#pragma unroll
+          for (int p = 0; p < 2; ++p) {
+            const double v0 = (double)bf16_bits_to_f32(w2[p] & 0xFFFFu);
+            const double v1 = (double)bf16_bits_to_f32(w2[p] >> 16);
+            sv[2 * p] = out ? sv[2 * p] - v0 : sv[2 * p] + v0;
+            sv[2 * p + 1] = out ? sv[2 * p + 1] - v1 : sv[2 * p + 1] + v1;
+          }
+          dn += out ? -1 : 1;
+        }
+      }
+    }
+    if (mine) {
+      const int n = it.dcnt[h * C + j] + dn;
+      double2* ds = reinterpret_cast<double2*>(it.dsum + ((int64_t)h * C + j) * kHeadDim + c4);
+      ds[0] = make_double2(sv[0], sv[1]);
+      ds[1] = make_double2(sv[2], sv[3]);
+      if ((lane & 31) == 0) it.dcnt[h * C + j] = n;
+      if (n > 0) centroid_from_sum(it, h, C, j, c4, sv, n, refresh != 0);
+    }
+  }
+}
+
+// cert[h] = head_exact for every head of every problem (one wave per head).
+__global__ __launch_bounds__(64) void k_cert(KmBatch b) {
+  const KmItem& it = b.it[blockIdx.y];
+  const int h = blockIdx.x;
+  const bool ok = head_exact(it, h, (int)b.N);
+  if (threadIdx.x == 0) it.cert[h] = ok ? 1u : 0u;
 }
 
 __global__ void k_centroid_bf16(KmBatch b) {
@@ -1232,7 +1473,9 @@ hipError_t launch_kmeans_update(const KmBatch& b, bool refresh, hipStream_t s) {
   // 32 clusters per workgroup when the launch holds enough work to fill the
   // chip with the fewer, longer workgroups (measured: 7 % faster at 12
   // problems of 32 heads, 10 % slower at 2)
-  const bool wide = grouped && (int64_t)b.n * b.H * b.C >= 6 * 32 * 256;
+  // (incremental iterations: only the heads that fail the certificate remain,
+  // and shorter workgroups finish them sooner)
+  const bool wide = grouped && b.inc != 2 && (int64_t)b.n * b.H * b.C >= 6 * 32 * 256;
   const int cpg = wide ? kUpdClustersG : kUpdClusters;
   const dim3 grid((unsigned)(b.H * ((b.C + cpg - 1) / cpg)), b.n);
   const int r = refresh ? 1 : 0;
@@ -1246,6 +1489,21 @@ hipError_t launch_kmeans_update(const KmBatch& b, bool refresh, hipStream_t s) {
     if (b.dtype == 0) hipLaunchKernelGGL((k_update<true, false, kUpdClusters>), grid, dim3(256), 0, s, b, r);
     else hipLaunchKernelGGL((k_update<false, false, kUpdClusters>), grid, dim3(256), 0, s, b, r);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_kmeans_update_delta(const KmBatch& b, bool refresh, hipStream_t s) {
+  TimedLaunch tl_("k_update_delta", s);
+  if (b.inc != 2 || b.dtype != 1 || b.N > kUpdWindow || b.C > 256 || !b.it[0].dsum) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)(b.H * kDeltaSplit), b.n);
+  hipLaunchKernelGGL(k_update_delta, grid, dim3(256), 0, s, b, refresh ? 1 : 0);
+  return hipGetLastError();
+}
+
+hipError_t launch_kmeans_cert(const KmBatch& b, hipStream_t s) {
+  TimedLaunch tl_("k_cert", s);
+  if (b.inc != 1 || !b.it[0].cert) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_cert, dim3(b.H, b.n), dim3(64), 0, s, b);
   return hipGetLastError();
 }
 

@@ -181,7 +181,7 @@ TensorView view_of(const qkv_tensor* t) {
 
 // ---- workspace plans ----
 struct QuantWs {
-  uint64_t c, planes, cn, amb_count, grp_off, grp_list, wq, rpart, ybuf0, ybuf1, bytes;
+  uint64_t c, planes, cn, amb_count, grp_off, grp_list, wq, rpart, dsum, dcnt, emag, cert, prev, ybuf0, ybuf1, bytes;
 };
 
 QuantWs quant_ws(const qkv_config* c, int64_t n) {
@@ -196,6 +196,14 @@ QuantWs quant_ws(const qkv_config* c, int64_t n) {
   w.grp_list = off; off += align256(H * (uint64_t)n * 2);
   w.wq = off;      off += align256(H * kHeadDim * 4);                  // QSAC weights with the range factor
   w.rpart = off;   off += align256(H * kRangeSplits * 2 * kHeadDim * 4);
+  // incremental k-means updates (grouped heads): exact sums, counts, magnitude
+  // range, labels of the last two updates
+  const bool inc = n <= kGroupMaxTokens;
+  w.dsum = off;    if (inc) off += align256(H * C * kHeadDim * 8);
+  w.dcnt = off;    if (inc) off += align256(H * C * 4);
+  w.emag = off;    if (inc) off += align256(H * 2 * kHeadDim * 4);
+  w.cert = off;    if (inc) off += align256(H * 4);
+  w.prev = off;    if (inc) off += align256(2 * H * (uint64_t)n);
   w.ybuf0 = off;   if (c->n_stages > 1) off += align256(H * (uint64_t)n * kHeadDim * 4);
   w.ybuf1 = off;   if (c->n_stages > 2) off += align256(H * (uint64_t)n * kHeadDim * 4);
   w.bytes = off;
@@ -293,14 +301,27 @@ int check_ws(const void* ws, size_t have, uint64_t need, const char* what) {
 uint8_t* at(void* base, uint64_t off) { return reinterpret_cast<uint8_t*>(base) + off; }
 
 // Run the k-means protocol of one stage on every problem of the batch.
-int run_kmeans(const qkv_config* cfg, const KmBatch& b, hipStream_t s) {
+// With the incremental buffers set (bf16 tokens, grouped heads), the first
+// update of the stage also records the exact sums, counts, magnitude range and
+// labels; each later update takes the heads that pass the exactness
+// certificate incrementally (the moved tokens only) and the others in full.
+int run_kmeans(const qkv_config* cfg, const KmBatch& b0, hipStream_t s) {
+  KmBatch b = b0;
   const bool grouped = b.it[0].grp_off != nullptr;
+  const bool inc = grouped && b.dtype == 1 && b.it[0].dsum != nullptr && cfg->kmeans_iters > 1;
   QKV_HIP(launch_kmeans_init(b, s));
   QKV_HIP(launch_centroid_prep(b, s));
+  if (inc)
+    for (int p = 0; p < b.n; ++p) QKV_HIP(launch_fill_zero_u32(b.it[p].emag, (size_t)b.H * 2 * kHeadDim, s));
   for (int it = 0; it < cfg->kmeans_iters; ++it) {
+    const bool refresh = it + 1 < cfg->kmeans_iters;
+    b.inc = inc ? (it == 0 ? 1 : 2) : 0;
+    b.iter = it;
     QKV_HIP(launch_kmeans_assign(b, s));
     if (grouped) QKV_HIP(launch_kmeans_group(b, s));
-    QKV_HIP(launch_kmeans_update(b, it + 1 < cfg->kmeans_iters, s));
+    QKV_HIP(launch_kmeans_update(b, refresh, s));
+    if (b.inc == 1) QKV_HIP(launch_kmeans_cert(b, s));
+    if (b.inc == 2) QKV_HIP(launch_kmeans_update_delta(b, refresh, s));
   }
   return QKV_OK;
 }
@@ -366,6 +387,12 @@ int quantize_batch(int32_t n, const qkv_config* const* cfgs, const qkv_tensor* c
     const bool grouped = N <= kGroupMaxTokens;   // the update reads the tokens grouped by cluster
     it.grp_off = grouped ? reinterpret_cast<int*>(wsp + ws.grp_off) : nullptr;
     it.grp_list = grouped ? reinterpret_cast<uint16_t*>(wsp + ws.grp_list) : nullptr;
+    // incremental updates: enabled per stage below (bf16 stage inputs only)
+    it.dsum = grouped ? reinterpret_cast<double*>(wsp + ws.dsum) : nullptr;
+    it.dcnt = grouped ? reinterpret_cast<int32_t*>(wsp + ws.dcnt) : nullptr;
+    it.emag = grouped ? reinterpret_cast<uint32_t*>(wsp + ws.emag) : nullptr;
+    it.cert = grouped ? reinterpret_cast<uint32_t*>(wsp + ws.cert) : nullptr;
+    it.prev = grouped ? wsp + ws.prev : nullptr;
     if (cfgs[p]->n_int4_channels > 0)
       QKV_HIP(launch_copy_perm(side->perm, reinterpret_cast<uint8_t*>(packed[p]) + L[p].off_perm, H, s));
   }
