@@ -181,21 +181,22 @@ class Run:
         self.quantize_all()
         self.attend()
 
-    # algorithmic work per step of each hot kernel (flops for MFMA kernels, bytes for HBM kernels)
+    # algorithmic work per step of each hot kernel (flops for MFMA kernels, bytes for HBM kernels).
+    # The k-means update has no fixed figure: after the first iteration of a
+    # bf16 stage it reads only the rows of the tokens whose label changed
+    # (data-dependent); its measured HBM bytes are in the rocprofv3 summaries.
     def work_per_step(self) -> dict:
         wl, H, d = self.wl, self.wl.n_heads, 128
         C, iters, L = wl.n_clusters, wl.kmeans_iters, wl.n_stages
         elems = [n * H * d for n in self.ntok]
         att = 4.0 * wl.n_query * self.nk * d * H + 2.0 * wl.n_query * self.nk * wl.psac_rank * H
         assign = sum(2.0 * n * C * d * H for n in self.ntok) * 2 * iters * L
-        upd = 0.0
         pack_tile = pack_generic = 0.0
         for cfg in (self.kcfg, self.vcfg):
             lay = self.qk.qkv_chunk_layout(cfg, self.ntok[0])
             for l in range(L):
                 esz = 2 if l == 0 else 4
                 for n, e in zip(self.ntok, elems):
-                    upd += iters * (e * esz + n * H)          # Y rows + labels per iteration
                     b = e * esz + n * H + H * C * d * 2 + n * H * (4 * lay.words_per_token + 2 * lay.groups_per_token)
                     if l + 1 < L:
                         b += e * 4                            # the next stage's fp32 input
@@ -203,7 +204,7 @@ class Run:
                         pack_generic += b
                     else:
                         pack_tile += b
-        return {"k_attend": ("mfma", att), "k_assign": ("mfma", assign), "k_update": ("hbm", upd),
+        return {"k_attend": ("mfma", att), "k_assign": ("mfma", assign),
                 "k_quant_pack_tile": ("hbm", pack_tile), "k_quant_pack": ("hbm", pack_generic)}
 
 
@@ -465,7 +466,7 @@ def stored_traffic(profile_file: str, kernel: str, sources) -> dict | None:
 
 
 KERNEL_SOURCES = {
-    "k_attend": ["attend.hip"], "k_assign": ["kmeans.hip"], "k_update": ["kmeans.hip"],
+    "k_attend": ["attend.hip"], "k_assign": ["kmeans.hip"],
     "k_quant_pack_tile": ["quant.hip"], "k_quant_pack": ["quant.hip"],
 }
 

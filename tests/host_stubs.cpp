@@ -25,6 +25,7 @@ QKV_STUB(hipError_t launch_centroid_bf16(const KmBatch&, hipStream_t))
 QKV_STUB(hipError_t launch_fill_zero_u32(void*, size_t, hipStream_t))
 QKV_STUB(hipError_t launch_quant_pack(const PackArgs&, hipStream_t))
 QKV_STUB(hipError_t launch_quant_pack_batch(const PackBatch&, hipStream_t))
+QKV_STUB(hipError_t launch_quant_pack_mixed_batch(const PackBatch&, hipStream_t))
 QKV_STUB(hipError_t launch_dequantize(const ChunkDecode&, void*, int, int64_t, int64_t, hipStream_t))
 QKV_STUB(hipError_t launch_psac_encode(const ChunkDecode&, const TensorView&, const float*, uint16_t*, hipStream_t))
 QKV_STUB(hipError_t launch_copy_perm(const uint8_t*, uint8_t*, int, hipStream_t))
@@ -41,5 +42,6 @@ QKV_STUB(hipError_t launch_attend(const AttendArgs&, hipStream_t))
 QKV_STUB(hipError_t scratch_of_current_device(void**))
 
 bool quant_pack_batchable(const PackArgs&, const PackArgs&) { return false; }
+bool quant_pack_mixed_batchable(const PackArgs&, const PackArgs&) { return false; }
 
 }  // namespace qkv

@@ -142,6 +142,7 @@ struct PackArgs {
   uint16_t* scales;            // bf16 [H][N][groups]
   int words, groups;
   float* y_next;               // f32 [H][N][128] or null
+  uint8_t* perm_out;           // [H][128]: a copy of perm (the chunk's channel order section), or null
 };
 hipError_t launch_quant_pack(const PackArgs& a, hipStream_t s);
 // Several problems of the fast layout (no channel permutation) that share group,
@@ -152,6 +153,10 @@ struct PackBatch {
 };
 bool quant_pack_batchable(const PackArgs& a, const PackArgs& b0);
 hipError_t launch_quant_pack_batch(const PackBatch& b, hipStream_t s);
+// Several problems of the mixed layout (channel permutation, no fp32 residual
+// output) that share their geometry, in one launch.
+bool quant_pack_mixed_batchable(const PackArgs& a, const PackArgs& b0);
+hipError_t launch_quant_pack_mixed_batch(const PackBatch& b, hipStream_t s);
 
 hipError_t launch_dequantize(const ChunkDecode& d, void* out, int out_dtype, int64_t stride_token,
                              int64_t stride_head, hipStream_t s);

@@ -53,6 +53,8 @@ __global__ __launch_bounds__(256) void k_init(KmBatch b) {
   const int C = b.C;
   float* __restrict__ c = it.c;
   const int h = blockIdx.y;
+  // the head's magnitude range starts empty (the incremental updates' record)
+  if (blockIdx.x == 0 && it.emag) it.emag[(int64_t)h * 2 * kHeadDim + threadIdx.x] = 0u;   // 256 = 2 x 128 words
   const int j = blockIdx.x * 8 + (threadIdx.x >> 5);
   if (j >= C) return;
   const int64_t step = y.n_tokens / C;

@@ -309,10 +309,8 @@ int run_kmeans(const qkv_config* cfg, const KmBatch& b0, hipStream_t s) {
   KmBatch b = b0;
   const bool grouped = b.it[0].grp_off != nullptr;
   const bool inc = grouped && b.dtype == 1 && b.it[0].dsum != nullptr && cfg->kmeans_iters > 1;
-  QKV_HIP(launch_kmeans_init(b, s));
+  QKV_HIP(launch_kmeans_init(b, s));             // also clears emag
   QKV_HIP(launch_centroid_prep(b, s));
-  if (inc)
-    for (int p = 0; p < b.n; ++p) QKV_HIP(launch_fill_zero_u32(b.it[p].emag, (size_t)b.H * 2 * kHeadDim, s));
   for (int it = 0; it < cfg->kmeans_iters; ++it) {
     const bool refresh = it + 1 < cfg->kmeans_iters;
     b.inc = inc ? (it == 0 ? 1 : 2) : 0;
@@ -393,8 +391,6 @@ int quantize_batch(int32_t n, const qkv_config* const* cfgs, const qkv_tensor* c
     it.emag = grouped ? reinterpret_cast<uint32_t*>(wsp + ws.emag) : nullptr;
     it.cert = grouped ? reinterpret_cast<uint32_t*>(wsp + ws.cert) : nullptr;
     it.prev = grouped ? wsp + ws.prev : nullptr;
-    if (cfgs[p]->n_int4_channels > 0)
-      QKV_HIP(launch_copy_perm(side->perm, reinterpret_cast<uint8_t*>(packed[p]) + L[p].off_perm, H, s));
   }
   for (int l = 0; l < c0->n_stages; ++l) {
     for (int p = 0; p < n; ++p) {
@@ -437,13 +433,14 @@ int quantize_batch(int32_t n, const qkv_config* const* cfgs, const qkv_tensor* c
       QKV_HIP(launch_centroid_bf16(b, s));
     }
     const bool more = l + 1 < c0->n_stages;
-    PackBatch pb;
+    PackBatch pb, mb;                            // uniform-layout and mixed-layout problems
     pb.n = 0;
+    mb.n = 0;
     for (int p = 0; p < n; ++p) {
       const qkv_config* cfg = cfgs[p];
       uint8_t* base = reinterpret_cast<uint8_t*>(packed[p]);
       uint8_t* wsp = at(workspace, per * p);
-      PackArgs pa;
+      PackArgs pa{};
       pa.y = y[p];
       pa.H = H;
       pa.C = c0->n_clusters;
@@ -461,8 +458,12 @@ int quantize_batch(int32_t n, const qkv_config* const* cfgs, const qkv_tensor* c
       pa.groups = g[p].groups;
       float* ynext = more ? reinterpret_cast<float*>(wsp + ((l % 2 == 0) ? ws.ybuf0 : ws.ybuf1)) : nullptr;
       pa.y_next = ynext;
+      // the chunk's channel order section, written once (with the first stage)
+      pa.perm_out = l == 0 && cfg->n_int4_channels > 0 ? base + L[p].off_perm : nullptr;
       if (pb.n > 0 && quant_pack_batchable(pa, pb.a[0])) pb.a[pb.n++] = pa;   // joins the batched launch
       else if (pb.n == 0 && quant_pack_batchable(pa, pa)) pb.a[pb.n++] = pa;
+      else if (mb.n > 0 && quant_pack_mixed_batchable(pa, mb.a[0])) mb.a[mb.n++] = pa;
+      else if (mb.n == 0 && quant_pack_mixed_batchable(pa, pa)) mb.a[mb.n++] = pa;
       else QKV_HIP(launch_quant_pack(pa, s));
       if (more) {
         // y_next is laid out [H][N][128]: token stride 128, head stride N*128
@@ -473,6 +474,7 @@ int quantize_batch(int32_t n, const qkv_config* const* cfgs, const qkv_tensor* c
       }
     }
     if (pb.n > 0) QKV_HIP(launch_quant_pack_batch(pb, s));
+    if (mb.n > 0) QKV_HIP(launch_quant_pack_mixed_batch(mb, s));
   }
   for (int p = 0; p < n; ++p) {
     if (cfgs[p]->psac_rank > 0) {
@@ -924,7 +926,7 @@ int qkv_quant_pack(const qkv_config* cfg, const qkv_tensor* y, const uint8_t* la
   }
   const uint8_t* pm = cfg->n_int4_channels > 0 ? perm : nullptr;
   if (pm) QKV_HIP(launch_copy_perm(pm, base + L.off_perm, cfg->n_heads, s));
-  PackArgs pa;
+  PackArgs pa{};
   pa.y = view_of(y);
   pa.H = cfg->n_heads;
   pa.C = cfg->n_clusters;

@@ -410,7 +410,7 @@ constexpr int kMixMaxWords = 17;     // 4-bit words + 2-bit words of a row (n_in
 constexpr int kMixMaxGroups = 9;     // ceil(n_int4 / 16) + ceil((128 - n_int4) / 16)
 
 template <bool F32>
-__global__ __launch_bounds__(256) void k_quant_pack_tile_mixed(PackArgs a) {
+__global__ __launch_bounds__(256) void k_quant_pack_tile_mixed(PackBatch pb, int tiles) {
   __shared__ __attribute__((aligned(16))) float s_r[kTileRows][kHeadDim + 4];
   __shared__ uint8_t s_inv[kTileHeads][kHeadDim];     // storage position of each channel
   __shared__ uint32_t s_codes[kTileRows * kMixMaxWords];
@@ -418,7 +418,9 @@ __global__ __launch_bounds__(256) void k_quant_pack_tile_mixed(PackArgs a) {
   __shared__ float s_rtab[128];                   // fp32(1 / (1 + k / 128))
   const int tid = threadIdx.x;
   if (tid < 128) s_rtab[tid] = 1.0f / (1.0f + (float)tid * 0.0078125f);
-  const int tile = (int)xcd_remap(blockIdx.x, gridDim.x);
+  const uint32_t logical = xcd_remap(blockIdx.x, gridDim.x);   // consecutive tiles share an XCD (L2)
+  const PackArgs& a = pb.a[logical / tiles];
+  const int tile = (int)(logical % tiles);
   const TileGeom tg = tile_geom(a.H, a.N);
   const int ntb = (a.N + tg.T - 1) / tg.T;
   const int i0 = (tile % ntb) * tg.T, h0 = (tile / ntb) * tg.HB;
@@ -426,9 +428,13 @@ __global__ __launch_bounds__(256) void k_quant_pack_tile_mixed(PackArgs a) {
   const int tmax = a.N - 1 - i0, hmax = a.H - 1 - h0;
   for (int i = tid; i < kTileHeads * kHeadDim; i += 256) s_inv[i >> 7][i & (kHeadDim - 1)] = (uint8_t)(i & (kHeadDim - 1));
   __syncthreads();
+  // the first token block of each head block also copies its heads' perm rows
+  uint8_t* pout = i0 == 0 ? a.perm_out : nullptr;
   for (int i = tid; i < kTileHeads * kHeadDim; i += 256) {
     const int hh = i >> 7, p = i & (kHeadDim - 1);
-    s_inv[hh][a.perm[(int64_t)(h0 + min(hh, hmax)) * kHeadDim + p] & (kHeadDim - 1)] = (uint8_t)p;
+    const uint8_t v = a.perm[(int64_t)(h0 + min(hh, hmax)) * kHeadDim + p];
+    s_inv[hh][v & (kHeadDim - 1)] = (uint8_t)p;
+    if (pout && hh <= hmax) pout[(int64_t)(h0 + hh) * kHeadDim + p] = v;
   }
   __syncthreads();
   // (1) residuals; rows outside the tile read a clamped valid row
@@ -640,18 +646,39 @@ hipError_t launch_quant_pack(const PackArgs& a, hipStream_t s) {
     pb.a[0] = a;
     return launch_quant_pack_batch(pb, s);
   }
-  // the mixed tile kernel: no fp32 residual output, 24-bit in-tile offsets
+  if (quant_pack_mixed_batchable(a, a)) {
+    PackBatch pb;
+    pb.n = 1;
+    pb.a[0] = a;
+    return launch_quant_pack_mixed_batch(pb, s);
+  }
+  if (a.perm && a.perm_out) {
+    const hipError_t e = launch_copy_perm(a.perm, a.perm_out, a.H, s);
+    if (e != hipSuccess) return e;
+  }
+  return launch_quant_pack_generic(a, s);
+}
+
+// the mixed tile kernel: no fp32 residual output, 24-bit in-tile offsets
+bool quant_pack_mixed_batchable(const PackArgs& a, const PackArgs& b0) {
   const bool tile_ok = a.perm && !a.y_next && a.words <= kMixMaxWords && a.groups <= kMixMaxGroups &&
                        a.y.stride_token < (1 << 23) && a.y.stride_head < (1 << 23) && a.N < (1 << 23) &&
                        (int64_t)a.H * a.C < (1 << 23);
-  if (tile_ok) {
-    TimedLaunch tl_("k_quant_pack_tile_mixed", s);
-    const dim3 grid((unsigned)tile_geom(a.H, a.N).tiles), block(256);
-    if (a.y.dtype == 0) hipLaunchKernelGGL(k_quant_pack_tile_mixed<true>, grid, block, 0, s, a);
-    else hipLaunchKernelGGL(k_quant_pack_tile_mixed<false>, grid, block, 0, s, a);
-    return hipGetLastError();
-  }
-  return launch_quant_pack_generic(a, s);
+  return tile_ok && b0.perm && !b0.y_next && a.y.dtype == b0.y.dtype && a.H == b0.H && a.N == b0.N &&
+         a.C == b0.C && a.bits == b0.bits && a.group == b0.group && a.n_int4 == b0.n_int4 &&
+         a.int4_words == b0.int4_words && a.words == b0.words && a.groups == b0.groups;
+}
+
+hipError_t launch_quant_pack_mixed_batch(const PackBatch& b, hipStream_t s) {
+  const PackArgs& a = b.a[0];
+  for (int p = 0; p < b.n; ++p)
+    if (!quant_pack_mixed_batchable(b.a[p], a)) return hipErrorInvalidValue;
+  TimedLaunch tl_("k_quant_pack_tile_mixed", s);
+  const int tiles = tile_geom(a.H, a.N).tiles;
+  const dim3 grid((unsigned)(tiles * b.n)), block(256);
+  if (a.y.dtype == 0) hipLaunchKernelGGL(k_quant_pack_tile_mixed<true>, grid, block, 0, s, b, tiles);
+  else hipLaunchKernelGGL(k_quant_pack_tile_mixed<false>, grid, block, 0, s, b, tiles);
+  return hipGetLastError();
 }
 
 bool quant_pack_batchable(const PackArgs& a, const PackArgs& b0) {
