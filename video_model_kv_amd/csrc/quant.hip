@@ -427,44 +427,72 @@ __global__ __launch_bounds__(256) void k_quant_pack_tile_mixed(PackBatch pb, int
   const int rows = tg.T * tg.HB;
   const int tmax = a.N - 1 - i0, hmax = a.H - 1 - h0;
   for (int i = tid; i < kTileHeads * kHeadDim; i += 256) s_inv[i >> 7][i & (kHeadDim - 1)] = (uint8_t)(i & (kHeadDim - 1));
-  __syncthreads();
-  // the first token block of each head block also copies its heads' perm rows
-  uint8_t* pout = i0 == 0 ? a.perm_out : nullptr;
-  for (int i = tid; i < kTileHeads * kHeadDim; i += 256) {
-    const int hh = i >> 7, p = i & (kHeadDim - 1);
-    const uint8_t v = a.perm[(int64_t)(h0 + min(hh, hmax)) * kHeadDim + p];
-    s_inv[hh][v & (kHeadDim - 1)] = (uint8_t)p;
-    if (pout && hh <= hmax) pout[(int64_t)(h0 + hh) * kHeadDim + p] = v;
-  }
-  __syncthreads();
-  // (1) residuals; rows outside the tile read a clamped valid row
+  // (1) residuals; rows outside the tile read a clamped valid row.  Every
+  // global load the tile needs is issued before the first barrier -- the
+  // heads' perm rows, the labels, the input rows -- then the labelled
+  // centroid rows, so the latencies overlap.
+  static_assert(kTileHeads * kHeadDim == 2 * 256, "two perm entries per thread");
   const int part = tid & 15, k0 = part * 8;
   constexpr int kIt = kTileRows * 16 / 256;
   const uint32_t ST = (uint32_t)a.y.stride_token, SH = (uint32_t)a.y.stride_head, NN = (uint32_t)a.N;
   const int64_t y_base = (int64_t)i0 * a.y.stride_token + (int64_t)h0 * a.y.stride_head + k0;
   const uint8_t* lab_base = a.labels + (int64_t)h0 * a.N + i0;
   const uint16_t* cent_base = a.centroids + (int64_t)h0 * a.C * kHeadDim + k0;
+  uint32_t pv[2];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int i = tid + 256 * q, hh = i >> 7, p = i & (kHeadDim - 1);
+    pv[q] = a.perm[(int64_t)(h0 + min(hh, hmax)) * kHeadDim + p];
+  }
+  int lab[kIt], hcs[kIt];
+  uint32_t yw[kIt][F32 ? 8 : 4];
 #pragma unroll
   for (int x = 0; x < kIt; ++x) {
     const int lr = x * 16 + (tid >> 4);
     const int t = lr / tg.HB, hh = lr - t * tg.HB;
     const int tc = min(t, tmax), hc = min(hh, hmax);
-    const int lab = min((int)lab_base[__umul24((uint32_t)hc, NN) + (uint32_t)tc], a.C - 1);
+    hcs[x] = hc;
+    lab[x] = lab_base[__umul24((uint32_t)hc, NN) + (uint32_t)tc];
     const uint32_t yo = __umul24((uint32_t)tc, ST) + __umul24((uint32_t)hc, SH);
-    float yv[8], cv[8];
     if constexpr (F32) {
       const float* p = reinterpret_cast<const float*>(a.y.ptr) + y_base + yo;
-      const float4 p0 = *reinterpret_cast<const float4*>(p);
-      const float4 p1 = *reinterpret_cast<const float4*>(p + 4);
-      yv[0] = p0.x; yv[1] = p0.y; yv[2] = p0.z; yv[3] = p0.w; yv[4] = p1.x; yv[5] = p1.y; yv[6] = p1.z; yv[7] = p1.w;
+      const uint4 p0 = *reinterpret_cast<const uint4*>(p);
+      const uint4 p1 = *reinterpret_cast<const uint4*>(p + 4);
+      yw[x][0] = p0.x; yw[x][1] = p0.y; yw[x][2] = p0.z; yw[x][3] = p0.w;
+      yw[x][4] = p1.x; yw[x][5] = p1.y; yw[x][6] = p1.z; yw[x][7] = p1.w;
     } else {
       const uint4 p = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(a.y.ptr) + y_base + yo);
-      const uint32_t w4[4] = {p.x, p.y, p.z, p.w};
-#pragma unroll
-      for (int e = 0; e < 8; ++e) yv[e] = bf16_bits_to_f32((w4[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
+      yw[x][0] = p.x; yw[x][1] = p.y; yw[x][2] = p.z; yw[x][3] = p.w;
     }
-    const uint4 c = *reinterpret_cast<const uint4*>(cent_base + (__umul24((uint32_t)hc, (uint32_t)a.C) + (uint32_t)lab) * kHeadDim);
-    const uint32_t c4[4] = {c.x, c.y, c.z, c.w};
+  }
+  uint4 cw[kIt];
+#pragma unroll
+  for (int x = 0; x < kIt; ++x)
+    cw[x] = *reinterpret_cast<const uint4*>(cent_base + (__umul24((uint32_t)hcs[x], (uint32_t)a.C) +
+                                                         (uint32_t)min(lab[x], a.C - 1)) * kHeadDim);
+  __syncthreads();                                 // the identity order is in place
+  // the first token block of each head block also copies its heads' perm rows
+  uint8_t* pout = i0 == 0 ? a.perm_out : nullptr;
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int i = tid + 256 * q, hh = i >> 7, p = i & (kHeadDim - 1);
+    s_inv[hh][pv[q] & (kHeadDim - 1)] = (uint8_t)p;
+    if (pout && hh <= hmax) pout[(int64_t)(h0 + hh) * kHeadDim + p] = (uint8_t)pv[q];
+  }
+  __syncthreads();                                 // the storage order is complete
+#pragma unroll
+  for (int x = 0; x < kIt; ++x) {
+    const int lr = x * 16 + (tid >> 4);
+    const int hh = lr - (lr / tg.HB) * tg.HB;
+    float yv[8], cv[8];
+    if constexpr (F32) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) yv[e] = __uint_as_float(yw[x][e]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) yv[e] = bf16_bits_to_f32((yw[x][e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
+    }
+    const uint32_t c4[4] = {cw[x].x, cw[x].y, cw[x].z, cw[x].w};
 #pragma unroll
     for (int e = 0; e < 8; ++e) cv[e] = bf16_bits_to_f32((c4[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
     const uint8_t* inv = s_inv[hh];
