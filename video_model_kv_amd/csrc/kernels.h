@@ -41,6 +41,8 @@ struct KmItem {
   uint16_t* cent_bf16;           // bf16 centroids written by launch_centroid_bf16
   int* grp_off;                  // [H][C + 1] cluster offsets from launch_kmeans_group, or null
   uint16_t* grp_list;            // [H][N] tokens ordered by cluster (same producer)
+  float* ynorm;                  // [H][N] the assign's ||y||_w^2 of bf16 tokens, kept from the first
+                                 // iteration of a stage for the later ones (KmBatch::iter), or null
   // Incremental updates (bf16 tokens, grouped heads), or all null: the exact
   // float64 cluster sums and member counts of the last update, the head's
   // channel magnitude range (the certificate that every subset sum of its

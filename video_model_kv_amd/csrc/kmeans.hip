@@ -88,14 +88,16 @@ __global__ __launch_bounds__(256) void k_init(KmBatch b) {
 // term covers.  D_b <= s_b + ||y||^2 + e_b; ||y||^2 (fp32 sums) carries a
 // 2^-12 margin, cn and the largest norm 2^-20, the evaluation of thr 2^-10,
 // and 2^-100 (1 + ||y||) covers products below fp32's normal range.
+// scb = sqrtf(cn_b * (1 + 2^-20)) and rcm = sqrtf(cmax2 * (1 + 2^-20)) come
+// precomputed (per centroid and per head).
 template <bool F32>
-__device__ __forceinline__ float screen_threshold(float yn, float s_b, float cn_b, float cmax2) {
+__device__ __forceinline__ float screen_threshold(float yn, float s_b, float cn_b, float scb, float rcm) {
   constexpr float kT = F32 ? 9.3e-5f : 4.7e-5f, kC = F32 ? 4.6e-5f : 3.1e-5f;
   const float ynu = yn * (1.0f + 0x1p-12f), ry = sqrtf(ynu);
   const float cb = cn_b * (1.0f + 0x1p-20f);
-  const float eb = 2.0f * kT * ry * sqrtf(cb) + kC * cb;
+  const float eb = 2.0f * kT * ry * scb + kC * cb;
   const float db = (fmaxf(s_b + ynu, 0.0f) + eb) * (1.0f + 0x1p-12f);
-  const float r = fminf(ry + sqrtf(db), sqrtf(cmax2 * (1.0f + 0x1p-20f)));
+  const float r = fminf(ry + sqrtf(db), rcm);
   const float ej = 2.0f * kT * ry * r + kC * r * r;
   return (eb + ej) * (1.0f + 0x1p-10f) + 0x1p-40f * (ynu + db) + 0x1p-100f * (1.0f + ry);
 }
@@ -161,8 +163,10 @@ __global__ __launch_bounds__(kAsgThreads) void k_assign(KmBatch b, int G) {
   const float* __restrict__ cent = it.c;
   uint8_t* __restrict__ labels = it.labels;
   int* __restrict__ amb_count = it.amb_count;
+  float* const ynbuf = it.ynorm;
   __shared__ __attribute__((aligned(16))) uint16_t sP[2][kAsgMaxC][kPitch];
   __shared__ __attribute__((aligned(16))) float sCn[kAsgMaxC];
+  __shared__ float sCnS[kAsgMaxC];               // sqrtf(cn * (1 + 2^-20)), for the screening bound
   __shared__ __attribute__((aligned(16))) float sW[kHeadDim];
   __shared__ int sAmb[kAsgList];
   __shared__ int sAmbN, sNext;
@@ -251,6 +255,9 @@ __global__ __launch_bounds__(kAsgThreads) void k_assign(KmBatch b, int G) {
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) cmax2 = fmaxf(cmax2, __shfl_xor(cmax2, o));
   cmax2 = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, cmax2)));
+  const float rcm = sqrtf(cmax2 * (1.0f + 0x1p-20f));
+  if (tid < C) sCnS[tid] = sqrtf(sCn[tid] * (1.0f + 0x1p-20f));
+  __syncthreads();
 
   // One wave decides token tok over all centroids, lanes over centroids, in
   // the definition's arithmetic: the sum over channels, in order, of
@@ -312,6 +319,10 @@ __global__ __launch_bounds__(kAsgThreads) void k_assign(KmBatch b, int G) {
     bf16x8 yh[2][8];
     bf16x8 yl[2][F32 ? 8 : 1];
     float ynorm[2] = {0.0f, 0.0f};
+    // bf16 tokens after the first iteration: ||y||^2 from the first (it does
+    // not change within a stage)
+    const bool cached = !F32 && b.iter > 0 && ynbuf != nullptr;
+    float ync[2] = {0.0f, 0.0f};
     if constexpr (F32) {
 #pragma unroll
       for (int t = 0; t < kPer; ++t) {
@@ -342,7 +353,10 @@ __global__ __launch_bounds__(kAsgThreads) void k_assign(KmBatch b, int G) {
       for (int t = 0; t < 2; ++t)
 #pragma unroll
         for (int s = 0; s < 8; ++s) yh[t][s] = as_bf16x8(raw[t][s]);
-      if (w == nullptr) {                        // sum of squares by packed bf16 dot products
+      if (cached) {
+#pragma unroll
+        for (int t = 0; t < 2; ++t) ync[t] = ynbuf[(int64_t)h * N + min(tok0 + t * 32 + col, N - 1)];
+      } else if (w == nullptr) {                 // sum of squares by packed bf16 dot products
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
           float part[4] = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -571,11 +585,12 @@ __global__ __launch_bounds__(kAsgThreads) void k_assign(KmBatch b, int G) {
           b1[t] = o1;
           bidx[t] = oi;
         }
-        const float yn = ynorm[t] + __shfl_xor(ynorm[t], 32);
+        const float yn = cached ? ync[t] : ynorm[t] + __shfl_xor(ynorm[t], 32);
         const int tok = tok0 + t * 32 + col;
         if (half == 0 && t < nt && tok < N) {
           labels[(int64_t)h * N + tok] = (uint8_t)bidx[t];
-          if (!(second - b1[t] > screen_threshold<F32>(yn, b1[t], sCn[bidx[t]], cmax2))) {
+          if (!F32 && b.iter == 0 && ynbuf) ynbuf[(int64_t)h * N + tok] = yn;
+          if (!(second - b1[t] > screen_threshold<F32>(yn, b1[t], sCn[bidx[t]], sCnS[bidx[t]], rcm))) {
             const int slot = atomicAdd(&sAmbN, 1);
             if (slot < kAsgList) sAmb[slot] = tok;
             else spill = tok + 1;
@@ -692,7 +707,7 @@ __global__ __launch_bounds__(kAsgThreads) void k_assign(KmBatch b, int G) {
           b1j = oj;
         }
       }
-      const float thr = screen_threshold<F32>(yn, m1, sCn[min(b1j, C - 1)], cmax2);
+      const float thr = screen_threshold<F32>(yn, m1, sCn[min(b1j, C - 1)], sCnS[min(b1j, C - 1)], rcm);
       // pass 2: every centroid within the bound of the winner
       for (int cb = 0; cb < Cp; cb += 32) {
         const f32x16 acc = block(cb);

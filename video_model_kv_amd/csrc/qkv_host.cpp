@@ -181,7 +181,7 @@ TensorView view_of(const qkv_tensor* t) {
 
 // ---- workspace plans ----
 struct QuantWs {
-  uint64_t c, planes, cn, amb_count, grp_off, grp_list, wq, rpart, dsum, dcnt, emag, cert, prev, ybuf0, ybuf1, bytes;
+  uint64_t c, planes, cn, amb_count, grp_off, grp_list, ynorm, wq, rpart, dsum, dcnt, emag, cert, prev, ybuf0, ybuf1, bytes;
 };
 
 QuantWs quant_ws(const qkv_config* c, int64_t n) {
@@ -194,6 +194,7 @@ QuantWs quant_ws(const qkv_config* c, int64_t n) {
   w.amb_count = off; off += 256;
   w.grp_off = off; off += align256(H * (C + 1) * 4);
   w.grp_list = off; off += align256(H * (uint64_t)n * 2);
+  w.ynorm = off;   off += align256(H * (uint64_t)n * 4);                 // ||y||^2 kept across iterations
   w.wq = off;      off += align256(H * kHeadDim * 4);                  // QSAC weights with the range factor
   w.rpart = off;   off += align256(H * kRangeSplits * 2 * kHeadDim * 4);
   // incremental k-means updates (grouped heads): exact sums, counts, magnitude
@@ -385,6 +386,7 @@ int quantize_batch(int32_t n, const qkv_config* const* cfgs, const qkv_tensor* c
     const bool grouped = N <= kGroupMaxTokens;   // the update reads the tokens grouped by cluster
     it.grp_off = grouped ? reinterpret_cast<int*>(wsp + ws.grp_off) : nullptr;
     it.grp_list = grouped ? reinterpret_cast<uint16_t*>(wsp + ws.grp_list) : nullptr;
+    it.ynorm = reinterpret_cast<float*>(wsp + ws.ynorm);
     // incremental updates: enabled per stage below (bf16 stage inputs only)
     it.dsum = grouped ? reinterpret_cast<double*>(wsp + ws.dsum) : nullptr;
     it.dcnt = grouped ? reinterpret_cast<int32_t*>(wsp + ws.dcnt) : nullptr;
