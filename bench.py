@@ -53,6 +53,8 @@ def parse():
                    help="workload ids timed after the headline ('' for none; 6: QuantWM with QSAC's range factor)")
     p.add_argument("--batch", type=int, default=16, help="problems per qkv_quantize_chunks call (1-16)")
     p.add_argument("--no-ar", action="store_true", help="skip the autoregressive rollout of the headline workload")
+    p.add_argument("--headline-only", action="store_true",
+                   help="only the headline step and its kernel timing (no rollout, side measurements or extra workloads)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--kernel-reps", type=int, default=5)
     p.add_argument("--copy-calibration", action="store_true",
@@ -610,17 +612,18 @@ def main():
         "kernels": prof,
     }
     lbatch = None
-    try:
-        lbatch = layer_batching(run)
-    except Exception as e:  # reported, never fatal to the headline measurement
-        log(f"layer batching failed: {e}")
     tcodec = None
-    try:
-        tcodec = temporal_codec(run)
-    except Exception as e:  # reported, never fatal to the headline measurement
-        log(f"temporal codec failed: {e}")
+    if not a.headline_only:
+        try:
+            lbatch = layer_batching(run)
+        except Exception as e:  # reported, never fatal to the headline measurement
+            log(f"layer batching failed: {e}")
+        try:
+            tcodec = temporal_codec(run)
+        except Exception as e:  # reported, never fatal to the headline measurement
+            log(f"temporal codec failed: {e}")
     ar = None
-    if not a.no_ar:
+    if not a.no_ar and not a.headline_only:
         try:
             ar = ar_rollout(run)
         except Exception as e:  # reported, never fatal to the headline measurement
@@ -634,7 +637,7 @@ def main():
     torch.cuda.empty_cache()
 
     extras = {}
-    for cid in [int(x) for x in a.extra.split(",") if x.strip()]:
+    for cid in [] if a.headline_only else [int(x) for x in a.extra.split(",") if x.strip()]:
         if cid == a.workload:
             continue
         r = Run(cid, a.batch)
