@@ -333,7 +333,7 @@ __global__ __launch_bounds__(kThreads) void k_attend(AttendArgs a) {
   __shared__ __attribute__((aligned(16))) uint32_t sRcV[kRing][kKTile * 8];        // [slot] V code words
   __shared__ __attribute__((aligned(16))) uint16_t sRsK[kRing][kKTile * kKGm + 8]; // [slot] K scales (+ lead)
   __shared__ __attribute__((aligned(16))) uint16_t sRsV[kRing][kKTile * 4 + 8];    // [slot] V scales (+ lead)
-  __shared__ uint8_t sRho[KM == 2 ? kHeadDim : 1];                                 // mix4 item order
+  __shared__ __attribute__((aligned(8))) uint8_t sRho[KM == 2 ? kHeadDim : 8];    // mix4 item order
   __shared__ __attribute__((aligned(16))) uint8_t sRl[kRing][2][kKTile + 16];      // [slot][K/V] labels (+ lead)
   __shared__ ChannelCode sTabK[kHeadDim], sTabV[kHeadDim];                         // generic decode tables
   __shared__ __attribute__((aligned(16))) uint32_t sMeta[kMetaSlots][sizeof(TileRec) / 4];   // tile records
@@ -734,16 +734,28 @@ __global__ __launch_bounds__(kThreads) void k_attend(AttendArgs a) {
     }
     const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q.ptr) + (int64_t)(qok ? qrow : 0) * a.q.stride_token +
                          (int64_t)h * a.q.stride_head;
+    // per k-step: the eight item positions from LDS in one read, then eight
+    // independent order-byte loads, then eight independent query loads (the
+    // query row is clamped to a valid one, so no load is predicated): two
+    // memory round trips per k-step
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
+      const uint2 rr = *reinterpret_cast<const uint2*>(&sRho[s * 16 + half * 8]);
+      const uint32_t r2[2] = {rr.x, rr.y};
+      uint32_t k8[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t P = (r2[e >> 2] >> (8 * (e & 3))) & 0xFFu;
+        if constexpr (FRESH) k8[e] = prow ? prow[P] : (uint32_t)(s * 16 + half * 8 + e);
+        else k8[e] = prow[P];
+      }
+      uint32_t q8[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) q8[e] = qp[k8[e] & (kHeadDim - 1)];
       f16x8 hv;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const int P = s * 16 + half * 8 + e;
-        int k;
-        if constexpr (FRESH) k = prow ? prow[sRho[P]] & (kHeadDim - 1) : P;
-        else k = prow[sRho[P]] & (kHeadDim - 1);
-        const float v = qok ? bf16_bits_to_f32(qp[k]) : 0.0f;
+        const float v = qok ? bf16_bits_to_f32(q8[e]) : 0.0f;
         hv[e] = (_Float16)__builtin_amdgcn_fmed3f(v * qsc, -kF16Max, kF16Max);
       }
       qh[s] = hv;
