@@ -326,18 +326,22 @@ def _side(wl, tensor):
     return w, u, perm
 
 
-def test_incremental_updates_with_a_head_outside_the_certificate():
-    """Three heads of bf16 values through ten k-means iterations: heads 0 and 2
-    pass the head-wide exactness certificate and take the incremental updates
-    after the first; head 1 holds one magnitude of 2^-100 in channel 9 (its
-    range exceeds the certificate) and keeps the full update.  Every section of
-    the packed chunk and x_hat bit-exact against the oracle."""
+def test_incremental_updates_in_every_certificate_class():
+    """Three heads of bf16 values through ten k-means iterations, one per class
+    of the head-wide exactness certificate (max over channels of
+    emax - emin + ceil(log2 N), N = 1,500): head 0 (38) keeps float64 sums
+    incrementally from the second update on; head 2, with one magnitude of
+    2^-35 in channel 20, sits exactly at the fixed-point bound (55) and keeps
+    64-bit integer sums from the third; head 1, with 2^-100 in channel 9 (112),
+    takes the full update every iteration.  Every section of the packed chunk
+    and x_hat bit-exact against the oracle."""
     wl = synth.workload(2, n_heads=3, n_clusters=64)
     n = 1500
     x = synth.kv_tokens(wl, "V", 0, n).copy()
     x[700, 1, 9] = np.float32(2.0 ** -100)
+    x[900, 2, 20] = np.float32(2.0 ** -35)
     cfg = G.config_of(wl, "V")
-    G.log(f"incremental updates: H=3 N={n} C=64, head 1 outside the certificate")
+    G.log(f"incremental updates: H=3 N={n} C=64, one head per certificate class")
     packed = G.quantize(cfg, G.to_dev(x, wl.dtype))
     jobs = [(x[:, h], dict(n_clusters=wl.n_clusters, bits=wl.bits, group=wl.group, n_stages=wl.n_stages,
                            iters=wl.kmeans_iters)) for h in range(wl.n_heads)]

@@ -814,7 +814,7 @@ __global__ __launch_bounds__(kAsgThreads) void k_assign(KmBatch b, int G) {
 // certificate, with N for the cluster size).  Every intermediate value of an
 // incremental update is such a sum (a set of distinct tokens), so the sums it
 // keeps are the exact sums.  Wave-uniform.
-__device__ __forceinline__ bool head_exact(const KmItem& it, int h, int N) {
+__device__ __forceinline__ bool head_span_ok(const KmItem& it, int h, int N, int limit) {
   const int lane = threadIdx.x & 63;
   const int lg = 32 - __builtin_clz((unsigned)max(N, 1));
   bool ok = true;
@@ -824,9 +824,43 @@ __device__ __forceinline__ bool head_exact(const KmItem& it, int h, int N) {
     const uint32_t mx = it.emag[(int64_t)h * 2 * kHeadDim + k];
     const uint32_t mn = 0xFFFFu - it.emag[((int64_t)h * 2 + 1) * kHeadDim + k];   // min nonzero magnitude - 1
     const int emax = (int)(mx >> 7), emin = max((int)(((mn + 1u) >> 7) & 0xFFu), 1);
-    ok = ok && (mn == 0xFFFFu || (emax < 0xFF && emax - emin + lg <= 44));
+    ok = ok && (mn == 0xFFFFu || (emax < 0xFF && emax - emin + lg <= limit));
   }
   return __ballot(!ok) == 0;
+}
+
+// The head's classes: 1 when float64 sums are exact (the bound 44 above); 2
+// when 64-bit integer sums in units of 2^(emin - 134) are: a signed sum of at
+// most N values is then below 2^(emax - emin + 8 + lg) units, within int64
+// when emax - emin + lg <= 55; 0 otherwise (the full update every iteration).
+constexpr uint32_t kCertF64 = 1, kCertFix = 2;
+
+// Smallest nonzero biased exponent of channel k of head h (1 for subnormals
+// and for an all-zero channel), from the recorded range.
+__device__ __forceinline__ int chan_emin(const KmItem& it, int h, int k) {
+  const uint32_t mn = 0xFFFFu - it.emag[((int64_t)h * 2 + 1) * kHeadDim + k];
+  return max((int)(((mn + 1u) >> 7) & 0xFFu), 1);
+}
+// bf16 bits b as a signed integer number of units 2^(emin - 134) (exact: the
+// value's exponent is at least emin).
+__device__ __forceinline__ int64_t fix_of(uint32_t b, int emin) {
+  const uint32_t E = (b >> 7) & 0xFFu, f = b & 0x7Fu;
+  const int64_t m = (int64_t)(E ? (f | 0x80u) : f);
+  const int sh = max((E ? (int)E : 1) - emin, 0);
+  return (b & 0x8000u) ? -(m << sh) : (m << sh);
+}
+// The float64 rounding of the integer sum s units of 2^(emin - 134): both
+// 32-bit halves convert exactly, their sum rounds once, the scaling is exact.
+__device__ __forceinline__ double fix_to_f64(int64_t s, int emin) {
+  const double hi = (double)(int32_t)(s >> 32) * 4294967296.0, lo = (double)(uint32_t)(s & 0xFFFFFFFFll);
+  return ldexp(hi + lo, emin - 134);
+}
+// Whether the grouping and the full update take head h in iteration b.iter
+// of an incremental stage (inc == 2): the heads outside both classes always;
+// the fixed-point class in its first later iteration, which also records its
+// integer sums; never the float64 class.
+__device__ __forceinline__ bool full_update_takes(const KmBatch& b, uint32_t cert) {
+  return cert == 0 || (cert == kCertFix && b.iter == 1);
 }
 
 // Centroid j of head h from its exact sum (channels c4 .. c4 + 3 per lane of a
@@ -901,11 +935,14 @@ __global__ __launch_bounds__(256) void k_group(KmBatch b) {
   __shared__ int s_c[256], s_o[257];
   __shared__ uint16_t s_l[kUpdWindow];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  if (b.inc == 2 && it.cert[h]) return;           // the incremental update takes this head
+  const uint32_t cert = b.inc == 2 ? it.cert[h] : 0u;
+  if (b.inc == 2 && !full_update_takes(b, cert)) return;   // the incremental update takes this head
   const uint8_t* lab = it.labels + (int64_t)h * N;
-  // the first update of an incremental stage: these labels are the previous
-  // ones of the next update (alternate buffer 1)
-  uint8_t* rec = b.inc == 1 ? it.prev + ((int64_t)b.H + h) * N : nullptr;
+  // before a head's first incremental update (the stage's first update, or a
+  // fixed-point head's first full one after it) these labels are the previous
+  // ones of the next update (alternate buffer (iter + 1) & 1)
+  uint8_t* rec = b.inc == 1 || (b.inc == 2 && cert == kCertFix)
+                     ? it.prev + ((int64_t)((b.iter + 1) & 1) * b.H + h) * N : nullptr;
   uint32_t kk[kUpdWindow / 256];                 // labels of tokens tid*32 .. tid*32 + 31
   {
     const int i0 = tid * 32;
@@ -994,8 +1031,10 @@ __global__ __launch_bounds__(256, 4) void k_update(KmBatch b, int refresh) {
   const int N = (int)y.n_tokens;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   if (blockIdx.x == 0 && tid == 0 && amb_count) *amb_count = 0;   // the close-call count of the next assign
-  if (b.inc == 2 && it.cert[h]) return;           // the incremental update takes this head
+  const uint32_t cert = b.inc == 2 ? it.cert[h] : 0u;
+  if (b.inc == 2 && !full_update_takes(b, cert)) return;   // the incremental update takes this head
   const bool record = GROUPED && !F32 && b.inc == 1;  // the first update of an incremental stage
+  const bool record_fix = GROUPED && !F32 && b.inc == 2 && cert == kCertFix;   // integer sums, once
   if (record) s_emag[tid >> 7][tid & (kHeadDim - 1)] = 0u;   // 256 threads: both halves (synchronised below)
   const uint8_t* lab = labels + (int64_t)h * N;
   const int64_t hoff = (int64_t)h * y.stride_head + lane * 2;
@@ -1156,6 +1195,12 @@ __global__ __launch_bounds__(256, 4) void k_update(KmBatch b, int refresh) {
       const int mg0 = g == 0 ? ma : mb, ng = g == 0 ? mb - ma : mc - mb;
       const int nmax = max(mb - ma, mc - mb);
       double sv[4];
+      int64_t fv[4] = {0, 0, 0, 0};              // record_fix: integer sums in the head's units
+      int em[4] = {1, 1, 1, 1};
+      if (record_fix) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) em[e] = chan_emin(it, h, c4 + e);
+      }
       u16x2 mx[2], mn[2];                        // magnitudes: max, and min nonzero - 1
 #pragma unroll
       for (int e = 0; e < 4; ++e) sv[e] = 0.0;
@@ -1180,6 +1225,10 @@ __global__ __launch_bounds__(256, 4) void k_update(KmBatch b, int refresh) {
             for (int p = 0; p < 2; ++p) {
               sv[2 * p] += (double)bf16_bits_to_f32(w2[p] & 0xFFFFu);
               sv[2 * p + 1] += (double)bf16_bits_to_f32(w2[p] >> 16);
+              if (record_fix) {                  // workgroup-uniform
+                fv[2 * p] += fix_of(w2[p] & 0xFFFFu, em[2 * p]);
+                fv[2 * p + 1] += fix_of(w2[p] >> 16, em[2 * p + 1]);
+              }
               const u16x2 mag = __builtin_bit_cast(u16x2, w2[p] & 0x7FFF7FFFu);
               mx[p] = __builtin_elementwise_max(mx[p], mag);
               mn[p] = __builtin_elementwise_min(mn[p], mag - u16x2{1, 1});   // a zero wraps to 0xFFFF
@@ -1224,6 +1273,12 @@ __global__ __launch_bounds__(256, 4) void k_update(KmBatch b, int refresh) {
             ds[0] = make_double2(sv[0], sv[1]);
             ds[1] = make_double2(sv[2], sv[3]);
           }
+          if ((lane & 31) == 0) it.dcnt[h * C + j] = n;
+        }
+        if (record_fix && j < C) {               // the fixed-point head's integer sums (same storage)
+          longlong2* ds = reinterpret_cast<longlong2*>(it.dsum + ((int64_t)h * C + j) * kHeadDim + c4);
+          ds[0] = make_longlong2(fv[0], fv[1]);
+          ds[1] = make_longlong2(fv[2], fv[3]);
           if ((lane & 31) == 0) it.dcnt[h * C + j] = n;
         }
         if (okc[cc] && n > 0 && j < C) centroid_from_sum(it, h, C, j, c4, sv, n, planes != nullptr);
@@ -1281,7 +1336,9 @@ __global__ __launch_bounds__(256) void k_update_delta(KmBatch b, int refresh) {
   const uint32_t logical = xcd_remap(blockIdx.x, (uint32_t)(n_heads * kDeltaSplit));
   const int h = logical / kDeltaSplit, r = logical % kDeltaSplit;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  if (!it.cert[h]) return;                       // the full update took this head
+  const uint32_t cert = it.cert[h];
+  if (cert == 0 || (cert == kCertFix && b.iter < 2)) return;   // the full update took this head
+  const bool fixp = cert == kCertFix;            // integer sums in the head's units
   __shared__ int s_cnt[256], s_off[257], s_cur[256];
   __shared__ uint16_t s_item[2 * kUpdWindow];    // token, | 0x8000 when it leaves the cluster
   __shared__ uint8_t s_touch[256];
@@ -1369,6 +1426,11 @@ __global__ __launch_bounds__(256) void k_update_delta(KmBatch b, int refresh) {
   __syncthreads();
   const int nt = s_nt;
   const int g = lane >> 5, c4 = (lane & 31) * 4;
+  int em[4] = {1, 1, 1, 1};
+  if (fixp) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) em[e] = chan_emin(it, h, c4 + e);
+  }
   const uint16_t* y16 = reinterpret_cast<const uint16_t*>(it.y);
   const int64_t hoff4 = (int64_t)h * it.stride_head + c4;
   // the wave's two lane groups take touched clusters base and base + kDeltaSplit
@@ -1379,8 +1441,16 @@ __global__ __launch_bounds__(256) void k_update_delta(KmBatch b, int refresh) {
     const int i0 = live ? s_off[j] : 0, ni = live ? s_cnt[j] : 0;
     const int nmax = max(ni, __shfl_xor(ni, 32));
     double sv[4] = {0.0, 0.0, 0.0, 0.0};
+    int64_t fv[4] = {0, 0, 0, 0};
     const bool mine = live && j < C;
-    if (mine) {
+    if (mine && fixp) {
+      const longlong2* ds = reinterpret_cast<const longlong2*>(it.dsum + ((int64_t)h * C + j) * kHeadDim + c4);
+      const longlong2 d0 = ds[0], d1 = ds[1];
+      fv[0] = d0.x;
+      fv[1] = d0.y;
+      fv[2] = d1.x;
+      fv[3] = d1.y;
+    } else if (mine) {
       const double2* ds = reinterpret_cast<const double2*>(it.dsum + ((int64_t)h * C + j) * kHeadDim + c4);
       const double2 d0 = ds[0], d1 = ds[1];
       sv[0] = d0.x;
@@ -1404,10 +1474,16 @@ __global__ __launch_bounds__(256) void k_update_delta(KmBatch b, int refresh) {
           const uint32_t w2[2] = {raw[q2].x, raw[q2].y};
 #pragma unroll
           for (int p = 0; p < 2; ++p) {
-            const double v0 = (double)bf16_bits_to_f32(w2[p] & 0xFFFFu);
-            const double v1 = (double)bf16_bits_to_f32(w2[p] >> 16);
-            sv[2 * p] = out ? sv[2 * p] - v0 : sv[2 * p] + v0;
-            sv[2 * p + 1] = out ? sv[2 * p + 1] - v1 : sv[2 * p + 1] + v1;
+            if (fixp) {                          // workgroup-uniform
+              const int64_t f0 = fix_of(w2[p] & 0xFFFFu, em[2 * p]), f1 = fix_of(w2[p] >> 16, em[2 * p + 1]);
+              fv[2 * p] = out ? fv[2 * p] - f0 : fv[2 * p] + f0;
+              fv[2 * p + 1] = out ? fv[2 * p + 1] - f1 : fv[2 * p + 1] + f1;
+            } else {
+              const double v0 = (double)bf16_bits_to_f32(w2[p] & 0xFFFFu);
+              const double v1 = (double)bf16_bits_to_f32(w2[p] >> 16);
+              sv[2 * p] = out ? sv[2 * p] - v0 : sv[2 * p] + v0;
+              sv[2 * p + 1] = out ? sv[2 * p + 1] - v1 : sv[2 * p + 1] + v1;
+            }
           }
           dn += out ? -1 : 1;
         }
@@ -1415,21 +1491,29 @@ __global__ __launch_bounds__(256) void k_update_delta(KmBatch b, int refresh) {
     }
     if (mine) {
       const int n = it.dcnt[h * C + j] + dn;
-      double2* ds = reinterpret_cast<double2*>(it.dsum + ((int64_t)h * C + j) * kHeadDim + c4);
-      ds[0] = make_double2(sv[0], sv[1]);
-      ds[1] = make_double2(sv[2], sv[3]);
+      if (fixp) {
+        longlong2* ds = reinterpret_cast<longlong2*>(it.dsum + ((int64_t)h * C + j) * kHeadDim + c4);
+        ds[0] = make_longlong2(fv[0], fv[1]);
+        ds[1] = make_longlong2(fv[2], fv[3]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sv[e] = fix_to_f64(fv[e], em[e]);   // the exact sum, rounded once
+      } else {
+        double2* ds = reinterpret_cast<double2*>(it.dsum + ((int64_t)h * C + j) * kHeadDim + c4);
+        ds[0] = make_double2(sv[0], sv[1]);
+        ds[1] = make_double2(sv[2], sv[3]);
+      }
       if ((lane & 31) == 0) it.dcnt[h * C + j] = n;
       if (n > 0) centroid_from_sum(it, h, C, j, c4, sv, n, refresh != 0);
     }
   }
 }
 
-// cert[h] = head_exact for every head of every problem (one wave per head).
+// cert[h], the head's class, for every head of every problem (one wave per head).
 __global__ __launch_bounds__(64) void k_cert(KmBatch b) {
   const KmItem& it = b.it[blockIdx.y];
   const int h = blockIdx.x;
-  const bool ok = head_exact(it, h, (int)b.N);
-  if (threadIdx.x == 0) it.cert[h] = ok ? 1u : 0u;
+  const bool f64 = head_span_ok(it, h, (int)b.N, 44), fix = head_span_ok(it, h, (int)b.N, 55);
+  if (threadIdx.x == 0) it.cert[h] = f64 ? kCertF64 : fix ? kCertFix : 0u;
 }
 
 __global__ void k_centroid_bf16(KmBatch b) {
@@ -1490,9 +1574,11 @@ hipError_t launch_kmeans_update(const KmBatch& b, bool refresh, hipStream_t s) {
   // 32 clusters per workgroup when the launch holds enough work to fill the
   // chip with the fewer, longer workgroups (measured: 7 % faster at 12
   // problems of 32 heads, 10 % slower at 2)
-  // (incremental iterations: only the heads that fail the certificate remain,
-  // and shorter workgroups finish them sooner)
-  const bool wide = grouped && b.inc != 2 && (int64_t)b.n * b.H * b.C >= 6 * 32 * 256;
+  // Incremental iterations: in the first, the fixed-point heads' full update
+  // runs on the shorter 8-cluster workgroups; later only heads outside both
+  // certificate classes remain (usually none), and the 4x smaller grid of the
+  // wide variant costs less to dispatch when every workgroup just exits.
+  const bool wide = grouped && (b.inc != 2 || b.iter >= 2) && (int64_t)b.n * b.H * b.C >= 6 * 32 * 256;
   const int cpg = wide ? kUpdClustersG : kUpdClusters;
   const dim3 grid((unsigned)(b.H * ((b.C + cpg - 1) / cpg)), b.n);
   const int r = refresh ? 1 : 0;
