@@ -12,11 +12,10 @@ namespace qkv {
   sig { return hipErrorNotSupported; }
 
 QKV_STUB(hipError_t launch_kmeans_init(const KmBatch&, hipStream_t))
-QKV_STUB(hipError_t launch_centroid_prep(const KmBatch&, hipStream_t))
 QKV_STUB(hipError_t launch_kmeans_assign(const KmBatch&, hipStream_t))
-QKV_STUB(hipError_t launch_kmeans_update(const KmBatch&, bool, hipStream_t))
+QKV_STUB(hipError_t launch_kmeans_update(const KmBatch&, hipStream_t))
 QKV_STUB(hipError_t launch_kmeans_group(const KmBatch&, hipStream_t))
-QKV_STUB(hipError_t launch_kmeans_update_delta(const KmBatch&, bool, hipStream_t))
+QKV_STUB(hipError_t launch_kmeans_update_delta(const KmBatch&, hipStream_t))
 QKV_STUB(hipError_t launch_kmeans_cert(const KmBatch&, hipStream_t))
 QKV_STUB(hipError_t launch_qsac_range(const RangeBatch&, hipStream_t))
 QKV_STUB(hipError_t launch_temporal_encode(const TCodecArgs&, hipStream_t))

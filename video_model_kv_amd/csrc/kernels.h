@@ -23,9 +23,9 @@ struct ChannelCode {
 };
 
 // ---- k-means (kmeans.hip) ----
-// Centroids c: f32 [H][C][128].  planes: bf16 bits [H][2][C][128], the split
-// hi/lo of fp32(-2 w c) used as the MFMA operand of the distance GEMM.
-// cn: f32 [H][C], sum_k w_k c_k^2 (rounded from float64).
+// Centroids c: f32 [H][C][128].  The assign forms its MFMA operand, the split
+// hi/lo bf16 of fp32(-2 w c), and the weighted norms sum_k w_k c_k^2 (float64,
+// rounded to f32) from c in LDS.
 // Every launch covers a batch of independent problems (one per grid slice);
 // the problems of a batch share dtype, n_tokens, n_heads and n_clusters.
 struct KmItem {
@@ -33,8 +33,6 @@ struct KmItem {
   int64_t stride_token, stride_head;
   const float* w;                // QSAC weights [H][128], or null (all ones)
   float* c;
-  uint16_t* planes;
-  float* cn;
   uint8_t* labels;               // [H][N]
   int* amb_count;                // close calls of the last assign (statistics), or null
   int32_t* counts;               // member counts [H][C] from the update, or null
@@ -50,39 +48,37 @@ struct KmItem {
   double* dsum;                  // [H][C][128]
   int32_t* dcnt;                 // [H][C]
   uint32_t* emag;                // [H][2][128]: max magnitude, 0xFFFF - (min nonzero magnitude - 1)
-  uint32_t* cert;                // [H]: 1 when the head passes the certificate (launch_kmeans_cert)
+  uint32_t* cert;                // [H]: the head's class (1 float64 sums, 2 64-bit integer sums, 0 neither)
   uint8_t* prev;                 // [2][H][N] labels at the previous updates (alternating)
 };
 constexpr int kKmMaxBatch = 16;
 // inc: 0 plain k-means; 1 the first iteration of an incremental stage (the
 // update also records dsum, dcnt, emag and the labels); 2 a later iteration
-// (heads that pass the certificate take launch_kmeans_update_delta, the
-// others the full update).  iter: the iteration index (0-based).
+// (heads in a certificate class take launch_kmeans_update_delta, the others
+// the full update).  iter: the iteration index (0-based).
 struct KmBatch {
   int n, dtype, H, C;
   int64_t N;
   int inc, iter;
   KmItem it[kKmMaxBatch];
 };
+// Strided initial centroids; clears amb_count and emag.
 hipError_t launch_kmeans_init(const KmBatch& b, hipStream_t s);
-// planes + cn from c (and w); zeroes amb_count.
-hipError_t launch_centroid_prep(const KmBatch& b, hipStream_t s);
 // Assign = MFMA screening (labels) + float64 re-decision of the close calls,
 // in one kernel; adds the number of close calls to amb_count.
 hipError_t launch_kmeans_assign(const KmBatch& b, hipStream_t s);
-// Update = grouping of the tokens by label (in LDS) + exact per-cluster sums;
-// with refresh it also rewrites the operand planes / norms for the next
-// assign.  Zeroes amb_count.
-hipError_t launch_kmeans_update(const KmBatch& b, bool refresh, hipStream_t s);
+// Update = exact per-cluster sums over the member lists (or label windows) and
+// the means.  Zeroes amb_count.
+hipError_t launch_kmeans_update(const KmBatch& b, hipStream_t s);
 // Counting sort of each head's tokens by label into grp_off / grp_list (heads of
 // at most kGroupMaxTokens tokens); the update then reads its clusters' members from there.
 constexpr int kGroupMaxTokens = 8192;
 hipError_t launch_kmeans_group(const KmBatch& b, hipStream_t s);
-// Incremental update (inc == 2): for every head that passes the certificate,
-// the tokens whose label changed since the previous update move between the
-// exact sums of their old and new clusters; the touched clusters' centroids
-// (and, with refresh, planes and norms) are rewritten.
-hipError_t launch_kmeans_update_delta(const KmBatch& b, bool refresh, hipStream_t s);
+// Incremental update (inc == 2): for every head in a certificate class (from
+// its first incremental iteration on), the tokens whose label changed since
+// the previous update move between the exact sums of their old and new
+// clusters; the touched clusters' centroids are rewritten.
+hipError_t launch_kmeans_update_delta(const KmBatch& b, hipStream_t s);
 // After the first update of an incremental stage: cert[h] from emag.
 hipError_t launch_kmeans_cert(const KmBatch& b, hipStream_t s);
 // QSAC's residual-range factor (gram.hip): for every problem of the batch,

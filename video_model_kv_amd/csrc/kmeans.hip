@@ -55,6 +55,7 @@ __global__ __launch_bounds__(256) void k_init(KmBatch b) {
   const int h = blockIdx.y;
   // the head's magnitude range starts empty (the incremental updates' record)
   if (blockIdx.x == 0 && it.emag) it.emag[(int64_t)h * 2 * kHeadDim + threadIdx.x] = 0u;   // 256 = 2 x 128 words
+  if (blockIdx.x == 0 && h == 0 && threadIdx.x == 0 && it.amb_count) *it.amb_count = 0;   // the first assign's count
   const int j = blockIdx.x * 8 + (threadIdx.x >> 5);
   if (j >= C) return;
   const int64_t step = y.n_tokens / C;
@@ -102,42 +103,9 @@ __device__ __forceinline__ float screen_threshold(float yn, float s_b, float cn_
   return (eb + ej) * (1.0f + 0x1p-10f) + 0x1p-40f * (ynu + db) + 0x1p-100f * (1.0f + ry);
 }
 
-// One wave per centroid: hi/lo planes of fp32(w*c) and the weighted norm.
-__global__ __launch_bounds__(64) void k_prep(KmBatch b) {
-  const KmItem& it = b.it[blockIdx.y];
-  const int C = b.C;
-  const float* __restrict__ c = it.c;
-  const float* __restrict__ w = it.w;
-  uint16_t* __restrict__ planes = it.planes;
-  float* __restrict__ cn = it.cn;
-  int* __restrict__ amb_count = it.amb_count;
-  const int h = blockIdx.x / C, j = blockIdx.x % C;
-  const int lane = threadIdx.x;
-  if (blockIdx.x == 0 && lane == 0 && amb_count) *amb_count = 0;
-  const float* cr = c + ((int64_t)h * C + j) * kHeadDim;
-  double nrm = 0.0;
-  uint16_t* ph = planes + ((int64_t)h * 2 * C + j) * kHeadDim;
-  uint16_t* pl = planes + ((int64_t)h * 2 * C + C + j) * kHeadDim;
-#pragma unroll
-  for (int e = 0; e < 2; ++e) {
-    const int k = lane * 2 + e;
-    const float cv = cr[k];
-    const float wv = w ? w[h * kHeadDim + k] : 1.0f;
-    const float b = -2.0f * (wv * cv);           // exact doubling: the planes carry -2 w c
-    const uint32_t hi = f32_to_bf16_bits(b);
-    const uint32_t lo = f32_to_bf16_bits(b - bf16_bits_to_f32(hi));
-    ph[k] = (uint16_t)hi;
-    pl[k] = (uint16_t)lo;
-    nrm += (double)wv * ((double)cv * (double)cv);
-  }
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) nrm += __shfl_xor(nrm, off);
-  if (lane == 0) cn[h * C + j] = (float)nrm;
-}
-
 // Assign: one workgroup per (head, range of 32-token sub-blocks), eight waves.
 // The head's operand planes (2 x C rows of 128 bf16, ~136 KB padded) are
-// loaded into LDS once and stay resident; each wave then sweeps all centroid
+// formed in LDS from the centroids once and stay resident; each wave then sweeps all centroid
 // blocks for 64 tokens at a time (fp32 tokens: 32).  bf16 sweeps are
 // software-pipelined: the MFMAs of centroid block k + 1 alternate with the
 // screening of block k, and the next item's tokens load into the operand
@@ -157,8 +125,6 @@ __global__ __launch_bounds__(kAsgThreads) void k_assign(KmBatch b, int G) {
   const KmItem& it = b.it[blockIdx.y];
   const TensorView y = item_view(b, it);
   const int C = b.C, n_heads = b.H;
-  const uint16_t* __restrict__ planes = it.planes;
-  const float* __restrict__ cn = it.cn;
   const float* __restrict__ w = it.w;
   const float* __restrict__ cent = it.c;
   uint8_t* __restrict__ labels = it.labels;
@@ -205,18 +171,16 @@ __global__ __launch_bounds__(kAsgThreads) void k_assign(KmBatch b, int G) {
   };
 
   {
-    // Everything reaches LDS by asynchronous copies (norms, weights, the
-    // planes), then the first item's tokens are requested (always 16 loads);
-    // the barrier waits for all but those 16, so no wave waits for another
-    // wave's tokens.
-    if (wave == 0) {
-#pragma unroll
-      for (int q = 0; q < kAsgMaxC / 64; ++q) {
-        const int j = q * 64 + lane;
-        if (j < C) dma4(cn + h * C + j, &sCn[q * 64]);   // lane i lands at sCn[q*64 + i]
-        else if (j < Cs) sCn[j] = INFINITY;
-      }
-    } else if (wave == 1) {
+    // The head's operand planes and norms are formed here from the fp32
+    // centroids: thread t takes half a row (centroid t / 2, channels
+    // 64 (t % 2) .. + 63), writes bf16 hi and lo of fp32(-2 w c) into the LDS
+    // planes and sums w c^2 in float64 with its partner lane, rounded to fp32
+    // (the screening bound carries 2^-20 on the norms).  Rows in [C, Cs) have
+    // zero planes and norm +inf, so they never win.  The weights arrive in
+    // LDS by asynchronous copy for the rest of the kernel.  The first item's
+    // tokens are requested first, so their latency overlaps the centroids'.
+    if constexpr (!F32) load_tokens(sb0 + kPer * wave);      // past the range: clamped, unused
+    if (wave == 1) {
       if (w) {
         dma4(w + h * kHeadDim + lane, &sW[0]);        // lane i lands at sW[i]
         dma4(w + h * kHeadDim + 64 + lane, &sW[64]);
@@ -228,21 +192,44 @@ __global__ __launch_bounds__(kAsgThreads) void k_assign(KmBatch b, int G) {
       sAmbN = 0;
       sNext = kAsgWaves;
     }
-    // planes: 1 KB of the padded image per wave instruction; pad pieces and
-    // rows in [C, Cs) take copies of valid pieces
-    const uint16_t* ph = planes + (int64_t)h * 2 * C * kHeadDim;
-    constexpr int kPlaneBytes = kAsgMaxC * kPitch * 2;
-    const int nch = (Cs * kPitch * 2 + 1023) >> 10;          // 1 KB chunks per plane
-    for (int k = wave; k < 2 * nch; k += kAsgWaves) {
-      const int p = k >= nch ? 1 : 0;
-      const int a = (k - p * nch) * 1024 + lane * 16;        // byte offset in the plane image
-      const int row = min(a / (kPitch * 2), C - 1), piece = min((a % (kPitch * 2)) >> 4, 15);
-      dma16(ph + ((int64_t)(p * C + row) * kHeadDim + piece * 8),
-            reinterpret_cast<char*>(&sP[0][0][0]) + p * kPlaneBytes + (k - p * nch) * 1024);
+    {
+      const int j = tid >> 1, k0 = (tid & 1) * 64;
+      double nrm = 0.0;
+      if (j < C) {
+        const float4* cr = reinterpret_cast<const float4*>(cent + ((int64_t)h * C + j) * kHeadDim + k0);
+        const float4* wr = w ? reinterpret_cast<const float4*>(w + h * kHeadDim + k0) : nullptr;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {                      // 8 channels per step
+          const float4 ca = cr[2 * q], cb = cr[2 * q + 1];
+          const float4 wa = wr ? wr[2 * q] : make_float4(1.0f, 1.0f, 1.0f, 1.0f);
+          const float4 wb = wr ? wr[2 * q + 1] : make_float4(1.0f, 1.0f, 1.0f, 1.0f);
+          const float cv[8] = {ca.x, ca.y, ca.z, ca.w, cb.x, cb.y, cb.z, cb.w};
+          const float wv[8] = {wa.x, wa.y, wa.z, wa.w, wb.x, wb.y, wb.z, wb.w};
+          u16x8 hi8, lo8;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float bb = -2.0f * (wv[e] * cv[e]);      // exact doubling: the planes carry -2 w c
+            const uint32_t hb = f32_to_bf16_bits(bb);
+            hi8[e] = (uint16_t)hb;
+            lo8[e] = (uint16_t)f32_to_bf16_bits(bb - bf16_bits_to_f32(hb));
+            nrm += (double)wv[e] * ((double)cv[e] * (double)cv[e]);
+          }
+          *reinterpret_cast<u16x8*>(&sP[0][j][k0 + q * 8]) = hi8;
+          *reinterpret_cast<u16x8*>(&sP[1][j][k0 + q * 8]) = lo8;
+        }
+      } else if (j < Cs) {
+        const u16x8 z = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          *reinterpret_cast<u16x8*>(&sP[0][j][k0 + q * 8]) = z;
+          *reinterpret_cast<u16x8*>(&sP[1][j][k0 + q * 8]) = z;
+        }
+      }
+      nrm += __shfl_xor(nrm, 1);
+      if ((tid & 1) == 0 && j < Cs) sCn[j] = j < C ? (float)nrm : INFINITY;
     }
     asm volatile("" ::: "memory");
-    if constexpr (!F32) load_tokens(sb0 + kPer * wave);      // past the range: clamped, unused
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm(F32 ? 0 : 16));   // vmcnt counts in issue order
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));               // the weights' copies
     __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
@@ -863,41 +850,14 @@ __device__ __forceinline__ bool full_update_takes(const KmBatch& b, uint32_t cer
   return cert == 0 || (cert == kCertFix && b.iter == 1);
 }
 
-// Centroid j of head h from its exact sum (channels c4 .. c4 + 3 per lane of a
-// 32-lane group): c = fl32(sum / n); with refresh the operand planes (-2 w c,
-// bf16 hi + lo) and the weighted norm (float64 over the group's lanes, rounded
-// to float32).  Called by the whole lane group.
+// Centroid j of head h from its exact sum (channels c4 .. c4 + 3 per lane):
+// c = fl32(sum / n).  (The assign forms its operand planes and norms from c.)
 __device__ __forceinline__ void centroid_from_sum(const KmItem& it, int h, int C, int j, int c4, const double* sv,
-                                                  int n, bool refresh) {
-  const int lane = threadIdx.x & 63;
-  const float* __restrict__ w = it.w;
+                                                  int n) {
   float cv[4];
 #pragma unroll
   for (int e = 0; e < 4; ++e) cv[e] = (float)(sv[e] / (double)n);
   *reinterpret_cast<float4*>(it.c + ((int64_t)h * C + j) * kHeadDim + c4) = make_float4(cv[0], cv[1], cv[2], cv[3]);
-  if (refresh) {
-    double nrm = 0.0;
-    uint32_t hw[2], lw[2];
-#pragma unroll
-    for (int p = 0; p < 2; ++p) {
-      hw[p] = lw[p] = 0u;
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const int k = c4 + 2 * p + e;
-        const float wv = w ? w[h * kHeadDim + k] : 1.0f;
-        const float bb = -2.0f * (wv * cv[2 * p + e]);
-        const uint32_t hi = f32_to_bf16_bits(bb);
-        hw[p] |= hi << (16 * e);
-        lw[p] |= f32_to_bf16_bits(bb - bf16_bits_to_f32(hi)) << (16 * e);
-        nrm += (double)wv * ((double)cv[2 * p + e] * (double)cv[2 * p + e]);
-      }
-    }
-    *reinterpret_cast<uint2*>(it.planes + ((int64_t)h * 2 * C + j) * kHeadDim + c4) = make_uint2(hw[0], hw[1]);
-    *reinterpret_cast<uint2*>(it.planes + ((int64_t)h * 2 * C + C + j) * kHeadDim + c4) = make_uint2(lw[0], lw[1]);
-#pragma unroll
-    for (int off = 1; off < 32; off <<= 1) nrm += __shfl_xor(nrm, off);   // within the lane group
-    if ((lane & 31) == 0) it.cn[h * C + j] = (float)nrm;
-  }
 }
 
 // Centroid update fused with the grouping of tokens by label.  One workgroup
@@ -915,7 +875,7 @@ __device__ __forceinline__ void centroid_from_sum(const KmItem& it, int h, int C
 //    smallest nonzero magnitude, tracked with packed 16-bit min/max); a
 //    channel that fails it is summed again in double-double;
 //  - otherwise double-double throughout (exact up to ~2^-104 relative).
-// An empty cluster keeps its centroid (and its operand planes and norm).
+// An empty cluster keeps its centroid.
 constexpr int kUpdClusters = 8;
 constexpr int kUpdClustersG = 32;       // clusters per workgroup when the member lists come from k_group
 constexpr int kUpdWindow = 8192;          // token index << 3 fits 16 bits
@@ -1005,15 +965,13 @@ __global__ __launch_bounds__(256) void k_group(KmBatch b) {
 }
 
 template <bool F32, bool GROUPED, int CPG>
-__global__ __launch_bounds__(256, 4) void k_update(KmBatch b, int refresh) {
+__global__ __launch_bounds__(256, 4) void k_update(KmBatch b) {
   const KmItem& it = b.it[blockIdx.y];
   const TensorView y = item_view(b, it);
   const int C = b.C, n_heads = b.H;
   const uint8_t* __restrict__ labels = it.labels;
   float* __restrict__ c = it.c;
   const float* __restrict__ w = it.w;
-  uint16_t* __restrict__ planes = refresh ? it.planes : nullptr;
-  float* __restrict__ cn = it.cn;
   int32_t* __restrict__ counts = it.counts;
   int* __restrict__ amb_count = it.amb_count;
   // CPG clusters per workgroup: with k_group's member lists one prologue
@@ -1084,24 +1042,6 @@ __global__ __launch_bounds__(256, 4) void k_update(KmBatch b, int refresh) {
       if (n == 0 || !old_fin[cc]) continue;
       const float cv[2] = {(float)(acc[cc][0].hi / (double)n), (float)(acc[cc][1].hi / (double)n)};
       *reinterpret_cast<float2*>(c + ((int64_t)h * C + j) * kHeadDim + lane * 2) = make_float2(cv[0], cv[1]);
-      if (planes) {   // operand planes (-2 w c) and weighted norm for the next assign
-        double nrm = 0.0;
-        uint32_t hw = 0, lw = 0;
-  #pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          const float wv = w ? w[h * kHeadDim + lane * 2 + e] : 1.0f;
-          const float b = -2.0f * (wv * cv[e]);
-          const uint32_t hi = f32_to_bf16_bits(b);
-          hw |= hi << (16 * e);
-          lw |= f32_to_bf16_bits(b - bf16_bits_to_f32(hi)) << (16 * e);
-          nrm += (double)wv * ((double)cv[e] * (double)cv[e]);
-        }
-        *reinterpret_cast<uint32_t*>(planes + ((int64_t)h * 2 * C + j) * kHeadDim + lane * 2) = hw;
-        *reinterpret_cast<uint32_t*>(planes + ((int64_t)h * 2 * C + C + j) * kHeadDim + lane * 2) = lw;
-  #pragma unroll
-        for (int off = 32; off > 0; off >>= 1) nrm += __shfl_xor(nrm, off);
-        if (lane == 0) cn[h * C + j] = (float)nrm;
-      }
     }
   };
 
@@ -1281,7 +1221,7 @@ __global__ __launch_bounds__(256, 4) void k_update(KmBatch b, int refresh) {
           ds[1] = make_longlong2(fv[2], fv[3]);
           if ((lane & 31) == 0) it.dcnt[h * C + j] = n;
         }
-        if (okc[cc] && n > 0 && j < C) centroid_from_sum(it, h, C, j, c4, sv, n, planes != nullptr);
+        if (okc[cc] && n > 0 && j < C) centroid_from_sum(it, h, C, j, c4, sv, n);
       }
 #pragma unroll
       for (int cc = 0; cc < 2; ++cc) {
@@ -1330,7 +1270,7 @@ __global__ __launch_bounds__(256, 4) void k_update(KmBatch b, int refresh) {
 // finds them as its previous labels.
 constexpr int kDeltaSplit = 4;
 
-__global__ __launch_bounds__(256) void k_update_delta(KmBatch b, int refresh) {
+__global__ __launch_bounds__(256) void k_update_delta(KmBatch b) {
   const KmItem& it = b.it[blockIdx.y];
   const int C = b.C, N = (int)b.N, n_heads = b.H;
   const uint32_t logical = xcd_remap(blockIdx.x, (uint32_t)(n_heads * kDeltaSplit));
@@ -1503,7 +1443,7 @@ __global__ __launch_bounds__(256) void k_update_delta(KmBatch b, int refresh) {
         ds[1] = make_double2(sv[2], sv[3]);
       }
       if ((lane & 31) == 0) it.dcnt[h * C + j] = n;
-      if (n > 0) centroid_from_sum(it, h, C, j, c4, sv, n, refresh != 0);
+      if (n > 0) centroid_from_sum(it, h, C, j, c4, sv, n);
     }
   }
 }
@@ -1538,12 +1478,6 @@ hipError_t launch_kmeans_init(const KmBatch& b, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_centroid_prep(const KmBatch& b, hipStream_t s) {
-  TimedLaunch tl_("k_prep", s);
-  hipLaunchKernelGGL(k_prep, dim3(b.H * b.C, b.n), dim3(64), 0, s, b);
-  return hipGetLastError();
-}
-
 hipError_t launch_kmeans_assign(const KmBatch& b, hipStream_t s) {
   TimedLaunch tl_("k_assign", s);
   if (b.C > kAsgMaxC) return hipErrorInvalidValue;
@@ -1568,7 +1502,7 @@ hipError_t launch_kmeans_assign(const KmBatch& b, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_kmeans_update(const KmBatch& b, bool refresh, hipStream_t s) {
+hipError_t launch_kmeans_update(const KmBatch& b, hipStream_t s) {
   TimedLaunch tl_("k_update", s);
   const bool grouped = b.it[0].grp_off != nullptr && b.N <= kUpdWindow;   // set for all problems or none
   // 32 clusters per workgroup when the launch holds enough work to fill the
@@ -1581,25 +1515,24 @@ hipError_t launch_kmeans_update(const KmBatch& b, bool refresh, hipStream_t s) {
   const bool wide = grouped && (b.inc != 2 || b.iter >= 2) && (int64_t)b.n * b.H * b.C >= 6 * 32 * 256;
   const int cpg = wide ? kUpdClustersG : kUpdClusters;
   const dim3 grid((unsigned)(b.H * ((b.C + cpg - 1) / cpg)), b.n);
-  const int r = refresh ? 1 : 0;
   if (wide) {
-    if (b.dtype == 0) hipLaunchKernelGGL((k_update<true, true, kUpdClustersG>), grid, dim3(256), 0, s, b, r);
-    else hipLaunchKernelGGL((k_update<false, true, kUpdClustersG>), grid, dim3(256), 0, s, b, r);
+    if (b.dtype == 0) hipLaunchKernelGGL((k_update<true, true, kUpdClustersG>), grid, dim3(256), 0, s, b);
+    else hipLaunchKernelGGL((k_update<false, true, kUpdClustersG>), grid, dim3(256), 0, s, b);
   } else if (grouped) {
-    if (b.dtype == 0) hipLaunchKernelGGL((k_update<true, true, kUpdClusters>), grid, dim3(256), 0, s, b, r);
-    else hipLaunchKernelGGL((k_update<false, true, kUpdClusters>), grid, dim3(256), 0, s, b, r);
+    if (b.dtype == 0) hipLaunchKernelGGL((k_update<true, true, kUpdClusters>), grid, dim3(256), 0, s, b);
+    else hipLaunchKernelGGL((k_update<false, true, kUpdClusters>), grid, dim3(256), 0, s, b);
   } else {
-    if (b.dtype == 0) hipLaunchKernelGGL((k_update<true, false, kUpdClusters>), grid, dim3(256), 0, s, b, r);
-    else hipLaunchKernelGGL((k_update<false, false, kUpdClusters>), grid, dim3(256), 0, s, b, r);
+    if (b.dtype == 0) hipLaunchKernelGGL((k_update<true, false, kUpdClusters>), grid, dim3(256), 0, s, b);
+    else hipLaunchKernelGGL((k_update<false, false, kUpdClusters>), grid, dim3(256), 0, s, b);
   }
   return hipGetLastError();
 }
 
-hipError_t launch_kmeans_update_delta(const KmBatch& b, bool refresh, hipStream_t s) {
+hipError_t launch_kmeans_update_delta(const KmBatch& b, hipStream_t s) {
   TimedLaunch tl_("k_update_delta", s);
   if (b.inc != 2 || b.dtype != 1 || b.N > kUpdWindow || b.C > 256 || !b.it[0].dsum) return hipErrorInvalidValue;
   const dim3 grid((unsigned)(b.H * kDeltaSplit), b.n);
-  hipLaunchKernelGGL(k_update_delta, grid, dim3(256), 0, s, b, refresh ? 1 : 0);
+  hipLaunchKernelGGL(k_update_delta, grid, dim3(256), 0, s, b);
   return hipGetLastError();
 }
 

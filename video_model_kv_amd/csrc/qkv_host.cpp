@@ -181,7 +181,7 @@ TensorView view_of(const qkv_tensor* t) {
 
 // ---- workspace plans ----
 struct QuantWs {
-  uint64_t c, planes, cn, amb_count, grp_off, grp_list, ynorm, wq, rpart, dsum, dcnt, emag, cert, prev, ybuf0, ybuf1, bytes;
+  uint64_t c, amb_count, grp_off, grp_list, ynorm, wq, rpart, dsum, dcnt, emag, cert, prev, ybuf0, ybuf1, bytes;
 };
 
 QuantWs quant_ws(const qkv_config* c, int64_t n) {
@@ -189,8 +189,6 @@ QuantWs quant_ws(const qkv_config* c, int64_t n) {
   QuantWs w;
   uint64_t off = 0;
   w.c = off;       off += align256(H * C * kHeadDim * 4);
-  w.planes = off;  off += align256(H * 2 * C * kHeadDim * 2);
-  w.cn = off;      off += align256(H * C * 4);
   w.amb_count = off; off += 256;
   w.grp_off = off; off += align256(H * (C + 1) * 4);
   w.grp_list = off; off += align256(H * (uint64_t)n * 2);
@@ -310,17 +308,15 @@ int run_kmeans(const qkv_config* cfg, const KmBatch& b0, hipStream_t s) {
   KmBatch b = b0;
   const bool grouped = b.it[0].grp_off != nullptr;
   const bool inc = grouped && b.dtype == 1 && b.it[0].dsum != nullptr && cfg->kmeans_iters > 1;
-  QKV_HIP(launch_kmeans_init(b, s));             // also clears emag
-  QKV_HIP(launch_centroid_prep(b, s));
+  QKV_HIP(launch_kmeans_init(b, s));             // also clears emag and the close-call count
   for (int it = 0; it < cfg->kmeans_iters; ++it) {
-    const bool refresh = it + 1 < cfg->kmeans_iters;
     b.inc = inc ? (it == 0 ? 1 : 2) : 0;
     b.iter = it;
     QKV_HIP(launch_kmeans_assign(b, s));
     if (grouped) QKV_HIP(launch_kmeans_group(b, s));
-    QKV_HIP(launch_kmeans_update(b, refresh, s));
+    QKV_HIP(launch_kmeans_update(b, s));
     if (b.inc == 1) QKV_HIP(launch_kmeans_cert(b, s));
-    if (b.inc == 2) QKV_HIP(launch_kmeans_update_delta(b, refresh, s));
+    if (b.inc == 2) QKV_HIP(launch_kmeans_update_delta(b, s));
   }
   return QKV_OK;
 }
@@ -379,8 +375,6 @@ int quantize_batch(int32_t n, const qkv_config* const* cfgs, const qkv_tensor* c
     KmItem& it = b.it[p];
     it.w = cfgs[p]->use_qsac ? side->w : nullptr;
     it.c = reinterpret_cast<float*>(wsp + ws.c);
-    it.planes = reinterpret_cast<uint16_t*>(wsp + ws.planes);
-    it.cn = reinterpret_cast<float*>(wsp + ws.cn);
     it.amb_count = reinterpret_cast<int*>(wsp + ws.amb_count);
     it.counts = nullptr;
     const bool grouped = N <= kGroupMaxTokens;   // the update reads the tokens grouped by cluster
@@ -858,8 +852,6 @@ KmBatch single_batch(const qkv_config* cfg, const qkv_tensor* y, const float* w,
   it.stride_head = v.stride_head;
   it.w = w;
   it.c = centroids;
-  it.planes = reinterpret_cast<uint16_t*>(at(workspace, ws.planes));
-  it.cn = reinterpret_cast<float*>(at(workspace, ws.cn));
   it.labels = labels;
   it.amb_count = reinterpret_cast<int*>(at(workspace, ws.amb_count));
   it.counts = counts;
@@ -881,7 +873,7 @@ int qkv_kmeans_assign(const qkv_config* cfg, const qkv_tensor* y, const float* c
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   // the kernels only read the centroids here
   const KmBatch b = single_batch(cfg, y, w, const_cast<float*>(centroids), labels, nullptr, workspace, ws);
-  QKV_HIP(launch_centroid_prep(b, s));
+  QKV_HIP(launch_fill_zero_u32(b.it[0].amb_count, 1, s));   // the close-call count (statistics)
   QKV_HIP(launch_kmeans_assign(b, s));
   return ok();
 }
@@ -895,7 +887,7 @@ int qkv_kmeans_update(const qkv_config* cfg, const qkv_tensor* y, const uint8_t*
   const QuantWs ws = quant_ws(cfg, y->n_tokens);
   QKV_TRY(check_ws(workspace, workspace_bytes, ws.ybuf0, fn));
   const KmBatch b = single_batch(cfg, y, nullptr, centroids, const_cast<uint8_t*>(labels), counts, workspace, ws);
-  QKV_HIP(launch_kmeans_update(b, false, reinterpret_cast<hipStream_t>(stream)));
+  QKV_HIP(launch_kmeans_update(b, reinterpret_cast<hipStream_t>(stream)));
   return ok();
 }
 
