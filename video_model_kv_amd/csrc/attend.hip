@@ -1296,16 +1296,17 @@ __global__ void k_upload(ChunkBatch b, ChunkRec* __restrict__ dst, uint32_t* __r
   if (b.first == 0 && mix_dst && i == 0) *mix_dst = mix;
 }
 
-// mix4 codes: a block takes 16 consecutive (head, token) rows of chunk
-// blockIdx.y, their code words staged in LDS by contiguous loads; thread =
-// (row, item) writes the item's word: u' = q + 8 of position 2j at nibble slot
-// j and of position 2j + 1 at slot j + 4.
-constexpr int kRepackRows = 16;
+// mix4 codes: a block takes 256 consecutive (head, token) rows of chunk
+// blockIdx.y (one contiguous run of code words, staged in LDS); thread =
+// (row, item) writes the item's word, 16 rows per pass: u' = q + 8 of position
+// 2j at nibble slot j and of position 2j + 1 at slot j + 4.  (Sixteen rows per
+// block made the launch dispatch-bound: 900,000 blocks for the one-minute cache.)
+constexpr int kRepackRows = 256;        // token-heads per workgroup (16 per pass of the 256 threads)
 constexpr int kRepackMaxWords = 17;   // 4-bit words + 2-bit words of a mixed row (n_int4 = 127)
 __global__ __launch_bounds__(256) void k_repack_mix(const ChunkRec* __restrict__ recs, LayoutParams kp,
                                                     const MixOrder* __restrict__ mix) {
   __shared__ uint8_t rho[kHeadDim];
-  __shared__ uint32_t sw[kRepackRows][kRepackMaxWords + 1];
+  __shared__ uint32_t sw[kRepackRows * kRepackMaxWords];
   const ChunkRec& c = recs[blockIdx.y];
   const int64_t rows = (int64_t)kp.H * c.n;
   const int64_t r0 = (int64_t)blockIdx.x * kRepackRows;
@@ -1313,26 +1314,35 @@ __global__ __launch_bounds__(256) void k_repack_mix(const ChunkRec* __restrict__
   const ChunkDecode d = make_decode(kp, c.n, c.kbase);
   const int W = min(d.words, kRepackMaxWords), n4 = d.n_int4, w4 = d.int4_words;
   const int nrows = (int)min<int64_t>(kRepackRows, rows - r0);
+  // the block's rows are one contiguous run of nrows * words code words
   const uint32_t* src = reinterpret_cast<const uint32_t*>(d.base + d.off_codes) + r0 * d.words;
-  for (int i = threadIdx.x; i < nrows * W; i += blockDim.x) sw[i / W][i % W] = src[(i / W) * d.words + i % W];
+  if (W == d.words) {                            // always for a valid layout: one contiguous copy
+#pragma unroll 4
+    for (int i = threadIdx.x; i < nrows * W; i += blockDim.x) sw[i] = src[i];
+  } else {
+    for (int i = threadIdx.x; i < nrows * W; i += blockDim.x) sw[i] = src[(i / W) * d.words + i % W];
+  }
   if (threadIdx.x < kHeadDim) rho[threadIdx.x] = mix->rho[threadIdx.x];
   __syncthreads();
-  const int tr = threadIdx.x >> 4, it = threadIdx.x & 15;
-  if (tr >= nrows) return;
-  uint32_t acc = 0;
+  const int it = threadIdx.x & 15;
+  uint32_t* dst = reinterpret_cast<uint32_t*>(const_cast<uint8_t*>(c.krep)) + r0 * 16;
+  for (int tr = threadIdx.x >> 4; tr < nrows; tr += 16) {   // thread (row, 4-byte output word)
+    const uint32_t* rw = sw + tr * W;
+    uint32_t acc = 0;
 #pragma unroll
-  for (int t = 0; t < 8; ++t) {
-    const int p = rho[it * 8 + t];
-    uint32_t u;
-    if (p < n4) {
-      u = (sw[tr][min(p >> 3, W - 1)] >> (4 * (p & 7))) & 15u;
-    } else {
-      const int pb = p - n4;
-      u = ((sw[tr][min(w4 + (pb >> 4), W - 1)] >> (2 * (pb & 15))) & 3u) + 6u;
+    for (int t = 0; t < 8; ++t) {
+      const int p = rho[it * 8 + t];
+      uint32_t u;
+      if (p < n4) {
+        u = (rw[min(p >> 3, W - 1)] >> (4 * (p & 7))) & 15u;
+      } else {
+        const int pb = p - n4;
+        u = ((rw[min(w4 + (pb >> 4), W - 1)] >> (2 * (pb & 15))) & 3u) + 6u;
+      }
+      acc |= u << (4 * ((t >> 1) + 4 * (t & 1)));
     }
-    acc |= u << (4 * ((t >> 1) + 4 * (t & 1)));
+    dst[tr * 16 + it] = acc;
   }
-  reinterpret_cast<uint32_t*>(const_cast<uint8_t*>(c.krep))[(r0 + tr) * 16 + it] = acc;
 }
 
 }  // namespace
