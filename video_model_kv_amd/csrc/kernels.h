@@ -49,6 +49,7 @@ struct KmItem {
   int32_t* dcnt;                 // [H][C]
   uint32_t* emag;                // [H][2][128]: max magnitude, 0xFFFF - (min nonzero magnitude - 1)
   uint32_t* cert;                // [H]: the head's class (1 float64 sums, 2 64-bit integer sums, 0 neither)
+  uint32_t* hlist;               // [2 + 2H]: counts, then the heads of class 0 and of class 2 (k_cert)
   uint8_t* prev;                 // [2][H][N] labels at the previous updates (alternating)
 };
 constexpr int kKmMaxBatch = 16;

@@ -56,6 +56,7 @@ __global__ __launch_bounds__(256) void k_init(KmBatch b) {
   // the head's magnitude range starts empty (the incremental updates' record)
   if (blockIdx.x == 0 && it.emag) it.emag[(int64_t)h * 2 * kHeadDim + threadIdx.x] = 0u;   // 256 = 2 x 128 words
   if (blockIdx.x == 0 && h == 0 && threadIdx.x == 0 && it.amb_count) *it.amb_count = 0;   // the first assign's count
+  if (blockIdx.x == 0 && h == 0 && threadIdx.x < 2 && it.hlist) it.hlist[threadIdx.x] = 0u;   // k_cert's lists
   const int j = blockIdx.x * 8 + (threadIdx.x >> 5);
   if (j >= C) return;
   const int64_t step = y.n_tokens / C;
@@ -881,6 +882,8 @@ constexpr int kUpdClustersG = 32;       // clusters per workgroup when the membe
 constexpr int kUpdWindow = 8192;          // token index << 3 fits 16 bits
 static_assert(kUpdWindow == kGroupMaxTokens, "grouped heads fit one update window");
 constexpr int kUpdRows = 12;            // member-row loads in flight per lane group
+constexpr int kListGroupGrid = 256;     // workgroups of the list-driven grouping and update
+constexpr int kListUpdateGrid = 1024;
 
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
@@ -889,9 +892,9 @@ typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 // offsets [C + 1] and the token list ordered by cluster, so that the update's
 // workgroups (32 per head) read their clusters' members instead of each
 // scanning all labels.
-__global__ __launch_bounds__(256) void k_group(KmBatch b) {
-  const KmItem& it = b.it[blockIdx.y];
-  const int C = b.C, N = (int)b.N, h = blockIdx.x;
+__device__ __forceinline__ void group_head(const KmBatch& b, int pi, int h) {
+  const KmItem& it = b.it[pi];
+  const int C = b.C, N = (int)b.N;
   __shared__ int s_c[256], s_o[257];
   __shared__ uint16_t s_l[kUpdWindow];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -964,16 +967,54 @@ __global__ __launch_bounds__(256) void k_group(KmBatch b) {
   for (int e = tid; e < N; e += 256) it.grp_list[(int64_t)h * N + e] = s_l[e];
 }
 
+__global__ __launch_bounds__(256) void k_group(KmBatch b) { group_head(b, blockIdx.y, blockIdx.x); }
+
+// The heads that a later iteration's full update takes (inc == 2), from the
+// per-problem lists that k_cert writes: those outside both certificate
+// classes, and in iteration 1 the fixed-point heads as well.  The list
+// kernels' workgroups stride over these heads (or (head, cluster group)
+// items), problem after problem, so that iterations where no head needs the
+// full update (the usual case) dispatch a few hundred workgroups, not one per
+// head and cluster group.
+__device__ __forceinline__ int listed_heads(const KmBatch& b, const KmItem& it) {
+  return (int)it.hlist[0] + (b.iter == 1 ? (int)it.hlist[1] : 0);
+}
+__device__ __forceinline__ int listed_head(const KmBatch& b, const KmItem& it, int e) {
+  const int n0 = (int)it.hlist[0];
+  return (int)(e < n0 ? it.hlist[2 + e] : it.hlist[2 + b.H + (e - n0)]);
+}
+
+// Every problem's item count (listed heads x per_head) into s_n, fetched at once.
+__device__ __forceinline__ void listed_counts(const KmBatch& b, int per_head, int* s_n) {
+  if (threadIdx.x < b.n) s_n[threadIdx.x] = listed_heads(b, b.it[threadIdx.x]) * per_head;
+  __syncthreads();
+}
+
+__global__ __launch_bounds__(256) void k_group_list(KmBatch b) {
+  __shared__ int s_n[kKmMaxBatch];
+  listed_counts(b, 1, s_n);
+  int e = blockIdx.x;
+  for (int p = 0; p < b.n; ++p) {
+    const KmItem& it = b.it[p];
+    const int cnt = s_n[p];
+    for (; e < cnt; e += gridDim.x) {
+      group_head(b, p, listed_head(b, it, e));
+      __syncthreads();                           // the LDS lists are rebuilt for the next head
+    }
+    e -= cnt;
+  }
+}
+
+// clusters c0 .. c0 + CPG - 1 of head h of problem pi
 template <bool F32, bool GROUPED, int CPG>
-__global__ __launch_bounds__(256, 4) void k_update(KmBatch b) {
-  const KmItem& it = b.it[blockIdx.y];
+__device__ __forceinline__ void update_block(const KmBatch& b, int pi, int h, int c0) {
+  const KmItem& it = b.it[pi];
   const TensorView y = item_view(b, it);
-  const int C = b.C, n_heads = b.H;
+  const int C = b.C;
   const uint8_t* __restrict__ labels = it.labels;
   float* __restrict__ c = it.c;
   const float* __restrict__ w = it.w;
   int32_t* __restrict__ counts = it.counts;
-  int* __restrict__ amb_count = it.amb_count;
   // CPG clusters per workgroup: with k_group's member lists one prologue
   // (offsets, then the list) can serve up to 32 clusters, which the waves take
   // two at a time in CPG / 8 sub-rounds; the label-scanning variant keeps 8
@@ -983,12 +1024,8 @@ __global__ __launch_bounds__(256, 4) void k_update(KmBatch b) {
   __shared__ uint16_t s_mem[kUpdWindow];
   __shared__ int s_wtot[4];
   __shared__ uint32_t s_emag[2][kHeadDim];      // inc == 1: this workgroup's magnitude range per channel
-  const int groups = (C + CPG - 1) / CPG;
-  const uint32_t logical = xcd_remap(blockIdx.x, (uint32_t)(n_heads * groups));
-  const int h = logical / groups, c0 = (logical % groups) * CPG;
   const int N = (int)y.n_tokens;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  if (blockIdx.x == 0 && tid == 0 && amb_count) *amb_count = 0;   // the close-call count of the next assign
   const uint32_t cert = b.inc == 2 ? it.cert[h] : 0u;
   if (b.inc == 2 && !full_update_takes(b, cert)) return;   // the incremental update takes this head
   const bool record = GROUPED && !F32 && b.inc == 1;  // the first update of an incremental stage
@@ -1255,6 +1292,34 @@ __global__ __launch_bounds__(256, 4) void k_update(KmBatch b) {
   }
 }
 
+template <bool F32, bool GROUPED, int CPG>
+__global__ __launch_bounds__(256, 4) void k_update(KmBatch b) {
+  const int groups = (b.C + CPG - 1) / CPG;
+  const uint32_t logical = xcd_remap(blockIdx.x, (uint32_t)(b.H * groups));
+  const KmItem& it = b.it[blockIdx.y];
+  if (blockIdx.x == 0 && threadIdx.x == 0 && it.amb_count) *it.amb_count = 0;   // the next assign's close calls
+  update_block<F32, GROUPED, CPG>(b, blockIdx.y, logical / groups, (logical % groups) * CPG);
+}
+
+// The full update of the listed heads (bf16 tokens, grouped, inc == 2).
+template <int CPG>
+__global__ __launch_bounds__(256, 4) void k_update_list(KmBatch b) {
+  const int groups = (b.C + CPG - 1) / CPG;
+  if (blockIdx.x == 0 && threadIdx.x < b.n && b.it[threadIdx.x].amb_count) *b.it[threadIdx.x].amb_count = 0;
+  __shared__ int s_n[kKmMaxBatch];
+  listed_counts(b, groups, s_n);
+  int e = blockIdx.x;
+  for (int p = 0; p < b.n; ++p) {
+    const KmItem& it = b.it[p];
+    const int cnt = s_n[p];
+    for (; e < cnt; e += gridDim.x) {
+      update_block<false, true, CPG>(b, p, listed_head(b, it, e / groups), (e % groups) * CPG);
+      __syncthreads();                           // the LDS lists are rebuilt for the next item
+    }
+    e -= cnt;
+  }
+}
+
 // Incremental update (the iterations after the first of a stage, bf16 heads
 // that pass head_exact): kDeltaSplit workgroups per (problem, head).  Each
 // scans the head's labels against those of the previous update, counts the
@@ -1268,7 +1333,9 @@ __global__ __launch_bounds__(256, 4) void k_update(KmBatch b) {
 // cluster left empty keeps its centroid.  The workgroup of split 0 also copies
 // the current labels into the other alternate buffer, where the next update
 // finds them as its previous labels.
-constexpr int kDeltaSplit = 4;
+constexpr int kDeltaSplit = 2;
+constexpr int kDeltaSlots = 2;               // clusters per lane group in flight
+constexpr int kDeltaRows = 8;                 // member-row loads in flight per cluster
 
 __global__ __launch_bounds__(256) void k_update_delta(KmBatch b) {
   const KmItem& it = b.it[blockIdx.y];
@@ -1373,87 +1440,123 @@ __global__ __launch_bounds__(256) void k_update_delta(KmBatch b) {
   }
   const uint16_t* y16 = reinterpret_cast<const uint16_t*>(it.y);
   const int64_t hoff4 = (int64_t)h * it.stride_head + c4;
-  // the wave's two lane groups take touched clusters base and base + kDeltaSplit
-  for (int base = r + kDeltaSplit * 2 * wave; base < nt; base += kDeltaSplit * 8) {
-    const int q = base + g * kDeltaSplit;
-    const bool live = q < nt;
-    const int j = live ? (int)s_touch[q] : 0;
-    const int i0 = live ? s_off[j] : 0, ni = live ? s_cnt[j] : 0;
-    const int nmax = max(ni, __shfl_xor(ni, 32));
-    double sv[4] = {0.0, 0.0, 0.0, 0.0};
-    int64_t fv[4] = {0, 0, 0, 0};
-    const bool mine = live && j < C;
-    if (mine && fixp) {
-      const longlong2* ds = reinterpret_cast<const longlong2*>(it.dsum + ((int64_t)h * C + j) * kHeadDim + c4);
-      const longlong2 d0 = ds[0], d1 = ds[1];
-      fv[0] = d0.x;
-      fv[1] = d0.y;
-      fv[2] = d1.x;
-      fv[3] = d1.y;
-    } else if (mine) {
-      const double2* ds = reinterpret_cast<const double2*>(it.dsum + ((int64_t)h * C + j) * kHeadDim + c4);
-      const double2 d0 = ds[0], d1 = ds[1];
-      sv[0] = d0.x;
-      sv[1] = d0.y;
-      sv[2] = d1.x;
-      sv[3] = d1.y;
-    }
-    int dn = 0;
-    for (int m = 0; m < nmax; m += kUpdRows) {
-      uint32_t itm[kUpdRows];
-      uint2 raw[kUpdRows];
+  // Lane group lg = 2 * wave + g takes the touched clusters q = r + kDeltaSplit * (lg + 8 k),
+  // kDeltaSlots of them at a time, so that the loads of several clusters (their
+  // sums, counts and member rows) are in flight together.
+  const int lg = 2 * wave + g;
+  for (int base = r + kDeltaSplit * lg; base < nt; base += kDeltaSplit * 8 * kDeltaSlots) {
+    int jj[kDeltaSlots], i0[kDeltaSlots], ni[kDeltaSlots], n_old[kDeltaSlots], dn[kDeltaSlots];
+    bool mine[kDeltaSlots];
+    double sv[kDeltaSlots][4];
+    int64_t fv[kDeltaSlots][4];
+    int nmax = 0;
 #pragma unroll
-      for (int q2 = 0; q2 < kUpdRows; ++q2) {
-        itm[q2] = s_item[i0 + min(m + q2, max(ni - 1, 0))];   // past the group's items: loaded, not added
-        raw[q2] = *reinterpret_cast<const uint2*>(y16 + (int64_t)(itm[q2] & 0x7FFFu) * it.stride_token + hoff4);
+    for (int sl = 0; sl < kDeltaSlots; ++sl) {
+      const int q = base + sl * kDeltaSplit * 8;
+      const bool live = q < nt;
+      const int j = live ? (int)s_touch[q] : 0;
+      jj[sl] = j;
+      i0[sl] = live ? s_off[j] : 0;
+      ni[sl] = live ? s_cnt[j] : 0;
+      dn[sl] = 0;
+      nmax = max(nmax, ni[sl]);
+      mine[sl] = live && j < C;
+      n_old[sl] = mine[sl] ? it.dcnt[h * C + j] : 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        sv[sl][e] = 0.0;
+        fv[sl][e] = 0;
+      }
+      if (mine[sl] && fixp) {
+        const longlong2* ds = reinterpret_cast<const longlong2*>(it.dsum + ((int64_t)h * C + j) * kHeadDim + c4);
+        const longlong2 d0 = ds[0], d1 = ds[1];
+        fv[sl][0] = d0.x;
+        fv[sl][1] = d0.y;
+        fv[sl][2] = d1.x;
+        fv[sl][3] = d1.y;
+      } else if (mine[sl]) {
+        const double2* ds = reinterpret_cast<const double2*>(it.dsum + ((int64_t)h * C + j) * kHeadDim + c4);
+        const double2 d0 = ds[0], d1 = ds[1];
+        sv[sl][0] = d0.x;
+        sv[sl][1] = d0.y;
+        sv[sl][2] = d1.x;
+        sv[sl][3] = d1.y;
+      }
+    }
+    nmax = max(nmax, __shfl_xor(nmax, 32));
+    for (int m = 0; m < nmax; m += kDeltaRows) {
+      uint32_t itm[kDeltaSlots][kDeltaRows];
+      uint2 raw[kDeltaSlots][kDeltaRows];
+#pragma unroll
+      for (int sl = 0; sl < kDeltaSlots; ++sl) {
+#pragma unroll
+        for (int q2 = 0; q2 < kDeltaRows; ++q2) {   // past a cluster's items: loaded, not added
+          itm[sl][q2] = s_item[i0[sl] + min(m + q2, max(ni[sl] - 1, 0))];
+          raw[sl][q2] =
+              *reinterpret_cast<const uint2*>(y16 + (int64_t)(itm[sl][q2] & 0x7FFFu) * it.stride_token + hoff4);
+        }
       }
 #pragma unroll
-      for (int q2 = 0; q2 < kUpdRows; ++q2) {
-        if (m + q2 < ni) {
-          const bool out = (itm[q2] & 0x8000u) != 0;
-          const uint32_t w2[2] = {raw[q2].x, raw[q2].y};
+      for (int sl = 0; sl < kDeltaSlots; ++sl) {
 #pragma unroll
-          for (int p = 0; p < 2; ++p) {
-            if (fixp) {                          // workgroup-uniform
-              const int64_t f0 = fix_of(w2[p] & 0xFFFFu, em[2 * p]), f1 = fix_of(w2[p] >> 16, em[2 * p + 1]);
-              fv[2 * p] = out ? fv[2 * p] - f0 : fv[2 * p] + f0;
-              fv[2 * p + 1] = out ? fv[2 * p + 1] - f1 : fv[2 * p + 1] + f1;
-            } else {
-              const double v0 = (double)bf16_bits_to_f32(w2[p] & 0xFFFFu);
-              const double v1 = (double)bf16_bits_to_f32(w2[p] >> 16);
-              sv[2 * p] = out ? sv[2 * p] - v0 : sv[2 * p] + v0;
-              sv[2 * p + 1] = out ? sv[2 * p + 1] - v1 : sv[2 * p + 1] + v1;
+        for (int q2 = 0; q2 < kDeltaRows; ++q2) {
+          if (m + q2 < ni[sl]) {
+            const bool out = (itm[sl][q2] & 0x8000u) != 0;
+            const uint32_t w2[2] = {raw[sl][q2].x, raw[sl][q2].y};
+#pragma unroll
+            for (int p = 0; p < 2; ++p) {
+              if (fixp) {                        // workgroup-uniform
+                const int64_t f0 = fix_of(w2[p] & 0xFFFFu, em[2 * p]), f1 = fix_of(w2[p] >> 16, em[2 * p + 1]);
+                fv[sl][2 * p] = out ? fv[sl][2 * p] - f0 : fv[sl][2 * p] + f0;
+                fv[sl][2 * p + 1] = out ? fv[sl][2 * p + 1] - f1 : fv[sl][2 * p + 1] + f1;
+              } else {
+                const double v0 = (double)bf16_bits_to_f32(w2[p] & 0xFFFFu);
+                const double v1 = (double)bf16_bits_to_f32(w2[p] >> 16);
+                sv[sl][2 * p] = out ? sv[sl][2 * p] - v0 : sv[sl][2 * p] + v0;
+                sv[sl][2 * p + 1] = out ? sv[sl][2 * p + 1] - v1 : sv[sl][2 * p + 1] + v1;
+              }
             }
+            dn[sl] += out ? -1 : 1;
           }
-          dn += out ? -1 : 1;
         }
       }
     }
-    if (mine) {
-      const int n = it.dcnt[h * C + j] + dn;
+#pragma unroll
+    for (int sl = 0; sl < kDeltaSlots; ++sl) {
+      if (!mine[sl]) continue;
+      const int j = jj[sl], n = n_old[sl] + dn[sl];
       if (fixp) {
         longlong2* ds = reinterpret_cast<longlong2*>(it.dsum + ((int64_t)h * C + j) * kHeadDim + c4);
-        ds[0] = make_longlong2(fv[0], fv[1]);
-        ds[1] = make_longlong2(fv[2], fv[3]);
+        ds[0] = make_longlong2(fv[sl][0], fv[sl][1]);
+        ds[1] = make_longlong2(fv[sl][2], fv[sl][3]);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) sv[e] = fix_to_f64(fv[e], em[e]);   // the exact sum, rounded once
+        for (int e = 0; e < 4; ++e) sv[sl][e] = fix_to_f64(fv[sl][e], em[e]);   // the exact sum, rounded once
       } else {
         double2* ds = reinterpret_cast<double2*>(it.dsum + ((int64_t)h * C + j) * kHeadDim + c4);
-        ds[0] = make_double2(sv[0], sv[1]);
-        ds[1] = make_double2(sv[2], sv[3]);
+        ds[0] = make_double2(sv[sl][0], sv[sl][1]);
+        ds[1] = make_double2(sv[sl][2], sv[sl][3]);
       }
       if ((lane & 31) == 0) it.dcnt[h * C + j] = n;
-      if (n > 0) centroid_from_sum(it, h, C, j, c4, sv, n);
+      if (n > 0) centroid_from_sum(it, h, C, j, c4, sv[sl], n);
     }
   }
 }
 
-// cert[h], the head's class, for every head of every problem (one wave per head).
+// cert[h], the head's class, for every head of every problem (one wave per head);
+// the heads outside the float64 class are appended to the problem's hlist.
 __global__ __launch_bounds__(64) void k_cert(KmBatch b) {
   const KmItem& it = b.it[blockIdx.y];
   const int h = blockIdx.x;
   const bool f64 = head_span_ok(it, h, (int)b.N, 44), fix = head_span_ok(it, h, (int)b.N, 55);
-  if (threadIdx.x == 0) it.cert[h] = f64 ? kCertF64 : fix ? kCertFix : 0u;
+  if (threadIdx.x == 0) {
+    const uint32_t cl = f64 ? kCertF64 : fix ? kCertFix : 0u;
+    it.cert[h] = cl;
+    if (cl != kCertF64) {                        // the later full updates' head lists
+      const int k = cl == kCertFix ? 1 : 0;
+      const uint32_t slot = atomicAdd(&it.hlist[k], 1u);   // one entry per head: slot < H
+      it.hlist[2 + k * b.H + slot] = (uint32_t)h;
+    }
+  }
 }
 
 __global__ void k_centroid_bf16(KmBatch b) {
@@ -1508,11 +1611,19 @@ hipError_t launch_kmeans_update(const KmBatch& b, hipStream_t s) {
   // 32 clusters per workgroup when the launch holds enough work to fill the
   // chip with the fewer, longer workgroups (measured: 7 % faster at 12
   // problems of 32 heads, 10 % slower at 2)
-  // Incremental iterations: in the first, the fixed-point heads' full update
-  // runs on the shorter 8-cluster workgroups; later only heads outside both
-  // certificate classes remain (usually none), and the 4x smaller grid of the
-  // wide variant costs less to dispatch when every workgroup just exits.
-  const bool wide = grouped && (b.inc != 2 || b.iter >= 2) && (int64_t)b.n * b.H * b.C >= 6 * 32 * 256;
+  // Incremental iterations (inc == 2) take only the heads k_cert listed: in the
+  // first, the fixed-point heads on the shorter 8-cluster workgroups (few heads,
+  // more workgroups each); later the heads outside both classes, usually none.
+  if (b.inc == 2) {                              // the listed heads: fixed-point ones once, then the rest
+    if (!grouped || b.dtype != 1 || !b.it[0].hlist) return hipErrorInvalidValue;
+    const int cpg = b.iter == 1 ? kUpdClusters : kUpdClustersG;
+    const int64_t items = (int64_t)b.n * b.H * ((b.C + cpg - 1) / cpg);
+    const dim3 grid((unsigned)std::min<int64_t>(items, kListUpdateGrid));
+    if (b.iter == 1) hipLaunchKernelGGL(k_update_list<kUpdClusters>, grid, dim3(256), 0, s, b);
+    else hipLaunchKernelGGL(k_update_list<kUpdClustersG>, grid, dim3(256), 0, s, b);
+    return hipGetLastError();
+  }
+  const bool wide = grouped && (int64_t)b.n * b.H * b.C >= 6 * 32 * 256;
   const int cpg = wide ? kUpdClustersG : kUpdClusters;
   const dim3 grid((unsigned)(b.H * ((b.C + cpg - 1) / cpg)), b.n);
   if (wide) {
@@ -1546,6 +1657,12 @@ hipError_t launch_kmeans_cert(const KmBatch& b, hipStream_t s) {
 hipError_t launch_kmeans_group(const KmBatch& b, hipStream_t s) {
   TimedLaunch tl_("k_group", s);
   if (b.N > kUpdWindow || b.C > 256) return hipErrorInvalidValue;
+  if (b.inc == 2) {                              // the listed heads only
+    if (!b.it[0].hlist) return hipErrorInvalidValue;
+    const dim3 grid((unsigned)std::min<int64_t>((int64_t)b.n * b.H, kListGroupGrid));
+    hipLaunchKernelGGL(k_group_list, grid, dim3(256), 0, s, b);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(k_group, dim3(b.H, b.n), dim3(256), 0, s, b);
   return hipGetLastError();
 }

@@ -181,7 +181,7 @@ TensorView view_of(const qkv_tensor* t) {
 
 // ---- workspace plans ----
 struct QuantWs {
-  uint64_t c, amb_count, grp_off, grp_list, ynorm, wq, rpart, dsum, dcnt, emag, cert, prev, ybuf0, ybuf1, bytes;
+  uint64_t c, amb_count, grp_off, grp_list, ynorm, wq, rpart, dsum, dcnt, emag, cert, hlist, prev, ybuf0, ybuf1, bytes;
 };
 
 QuantWs quant_ws(const qkv_config* c, int64_t n) {
@@ -202,6 +202,7 @@ QuantWs quant_ws(const qkv_config* c, int64_t n) {
   w.dcnt = off;    if (inc) off += align256(H * C * 4);
   w.emag = off;    if (inc) off += align256(H * 2 * kHeadDim * 4);
   w.cert = off;    if (inc) off += align256(H * 4);
+  w.hlist = off;   if (inc) off += align256((2 + 2 * H) * 4);
   w.prev = off;    if (inc) off += align256(2 * H * (uint64_t)n);
   w.ybuf0 = off;   if (c->n_stages > 1) off += align256(H * (uint64_t)n * kHeadDim * 4);
   w.ybuf1 = off;   if (c->n_stages > 2) off += align256(H * (uint64_t)n * kHeadDim * 4);
@@ -386,6 +387,7 @@ int quantize_batch(int32_t n, const qkv_config* const* cfgs, const qkv_tensor* c
     it.dcnt = grouped ? reinterpret_cast<int32_t*>(wsp + ws.dcnt) : nullptr;
     it.emag = grouped ? reinterpret_cast<uint32_t*>(wsp + ws.emag) : nullptr;
     it.cert = grouped ? reinterpret_cast<uint32_t*>(wsp + ws.cert) : nullptr;
+    it.hlist = grouped ? reinterpret_cast<uint32_t*>(wsp + ws.hlist) : nullptr;
     it.prev = grouped ? wsp + ws.prev : nullptr;
   }
   for (int l = 0; l < c0->n_stages; ++l) {
