@@ -572,6 +572,34 @@ def test_quantize_batch_headline_launch_matches_single():
         G.log(f"headline batch: chunk 0 {tensor} head {h} bit-exact against the oracle; near-ties {near}")
 
 
+def test_quantize_batch_certificate_classes():
+    """Four problems in one call with heads of every exactness class spread over
+    them (a head with 2^-100 in one channel is outside both classes; head 2
+    with 2^-35 in channel 20 sits at the fixed-point bound), so that the later
+    iterations' full updates run from per-problem head lists across several
+    problems: bytes equal to single calls, and every head of every problem
+    bit-exact against the oracle."""
+    wl = synth.workload(2, n_heads=3, n_clusters=64)
+    n = 1500
+    base = synth.kv_tokens(wl, "V", 0, n)
+    plants = ([], [(700, 1, 9, -100)], [(700, 1, 9, -100), (900, 2, 20, -35)],
+              [(900, 2, 20, -35), (100, 0, 3, -100)])
+    xs = []
+    for pl in plants:
+        x = base.copy()
+        for i, h, k, e in pl:
+            x[i, h, k] = np.float32(2.0 ** e)
+        xs.append(x)
+    cfg = G.config_of(wl, "V")
+    G.log("batch of 4 problems, N=1500, H=3, C=64, heads of every certificate class")
+    packs = _batch_vs_single([(cfg, G.to_dev(x, wl.dtype), None) for x in xs])
+    kw = dict(n_clusters=wl.n_clusters, bits=wl.bits, group=wl.group, n_stages=wl.n_stages, iters=wl.kmeans_iters)
+    res = G.oracle_problems([(x[:, h], kw) for x in xs for h in range(wl.n_heads)])
+    for p, x in enumerate(xs):
+        G.compare_chunk(f"classes-{p}", wl, "V", x, packs[p], cfg,
+                        {h: res[p * wl.n_heads + h] for h in range(wl.n_heads)}, range(wl.n_heads))
+
+
 def test_quantize_batch_all_ties_overflow_list():
     """Every token of a problem identical: all centroids tie, every token is a
     close call (more than the workgroup's LDS list holds, so the per-wave
