@@ -29,6 +29,7 @@ QKV_STUB(hipError_t launch_dequantize(const ChunkDecode&, void*, int, int64_t, i
 QKV_STUB(hipError_t launch_psac_encode(const ChunkDecode&, const TensorView&, const float*, uint16_t*, hipStream_t))
 QKV_STUB(hipError_t launch_copy_perm(const uint8_t*, uint8_t*, int, hipStream_t))
 QKV_STUB(hipError_t launch_gram(const TensorView&, int, double*, int, double*, hipStream_t))
+QKV_STUB(hipError_t launch_gram_diag(const TensorView&, int, double*, int, double*, hipStream_t))
 QKV_STUB(hipError_t launch_upload_chunks(const ChunkBatch&, ChunkRec*, uint32_t*, const MixOrder&, MixOrder*, hipStream_t))
 QKV_STUB(hipError_t launch_repack_mix(const ChunkRec*, int, int, const LayoutParams&, const MixOrder*, hipStream_t))
 QKV_STUB(hipError_t launch_range_scan(const ChunkRec*, int, const LayoutParams&, const LayoutParams&, const TensorView&,

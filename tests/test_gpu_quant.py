@@ -492,6 +492,13 @@ def test_psac_fit_matches_oracle():
         worst = max(worst, dp)
         assert dp < 1e-4, f"head {h}: projector differs by {dp}"
     G.log(f"psac_fit: weights/perm exact, worst projector difference {worst:.3g}, energy[0] {energy[0]:.4f}")
+    # rank 0 without the energy fractions (the mixed layout's channel order, as the one-minute cache
+    # takes it): only the diagonal of M is formed, and weights and order are the same bits
+    w0 = t.empty((H, 128), dtype=t.float32, device=G.dev())
+    p0 = t.empty((H, 128), dtype=t.uint8, device=G.dev())
+    assert qk.qkv_psac_fit(G.to_dev(hist, "bf16"), H, 0, 26, ws, w_out=w0, perm_out=p0, energy=False) is None
+    assert np.array_equal(w0.cpu().numpy().view(np.uint32), wg.view(np.uint32)), "rank 0: weights"
+    assert np.array_equal(p0.cpu().numpy(), pg), "rank 0: channel order"
 
 
 def _batch_vs_single(problems):

@@ -51,6 +51,28 @@ __global__ __launch_bounds__(256) void k_gram_partial(TensorView q, int n_split,
   for (int c = 0; c < 64; ++c) out[c] = acc[c];
 }
 
+// The diagonal alone (QSAC's activity and the mixed layout's channel order
+// need no more): block (split, head), thread = channel, the split's rows in
+// the same order as k_gram_partial, so every value is the same as that
+// kernel's diagonal.
+template <bool F32>
+__global__ __launch_bounds__(kHeadDim) void k_gram_diag_partial(TensorView q, int n_split, double* __restrict__ partial) {
+  const int split = blockIdx.x, h = blockIdx.y, H = gridDim.y, k = threadIdx.x;
+  const int64_t n = q.n_tokens;
+  const int64_t rows_per = (n + n_split - 1) / n_split;
+  const int64_t r0 = split * rows_per, r1 = min(n, r0 + rows_per);
+  const int64_t off0 = (int64_t)h * q.stride_head + k;
+  double acc = 0.0;
+#pragma unroll 8
+  for (int64_t row = r0; row < r1; ++row) {
+    double v;
+    if constexpr (F32) v = (double)reinterpret_cast<const float*>(q.ptr)[row * q.stride_token + off0];
+    else v = (double)bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(q.ptr)[row * q.stride_token + off0]);
+    acc += v * v;
+  }
+  partial[((int64_t)split * H + h) * kHeadDim + k] = acc;
+}
+
 __global__ void k_gram_reduce(int64_t per, int n_split, const double* __restrict__ partial, double* __restrict__ m) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= per) return;
@@ -150,6 +172,18 @@ hipError_t launch_gram(const TensorView& q, int H, double* partial, int n_split,
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t per = (int64_t)H * kHeadDim * kHeadDim;
+  hipLaunchKernelGGL(k_gram_reduce, dim3((unsigned)((per + 255) / 256)), dim3(256), 0, s, per, n_split, partial, m);
+  return hipGetLastError();
+}
+
+hipError_t launch_gram_diag(const TensorView& q, int H, double* partial, int n_split, double* m, hipStream_t s) {
+  TimedLaunch tl_("k_gram_diag", s);
+  const dim3 grid(n_split, H);
+  if (q.dtype == 0) hipLaunchKernelGGL(k_gram_diag_partial<true>, grid, dim3(kHeadDim), 0, s, q, n_split, partial);
+  else hipLaunchKernelGGL(k_gram_diag_partial<false>, grid, dim3(kHeadDim), 0, s, q, n_split, partial);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t per = (int64_t)H * kHeadDim;
   hipLaunchKernelGGL(k_gram_reduce, dim3((unsigned)((per + 255) / 256)), dim3(256), 0, s, per, n_split, partial, m);
   return hipGetLastError();
 }

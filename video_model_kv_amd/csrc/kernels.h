@@ -166,6 +166,9 @@ hipError_t launch_copy_perm(const uint8_t* perm, uint8_t* dst, int H, hipStream_
 // ---- history-query statistics (gram.hip) ----
 hipError_t launch_gram(const TensorView& q, int H, double* partial, int n_split, double* m,
                        hipStream_t s);
+// Its diagonal only: m [H][128], the same values as launch_gram's diagonal.
+hipError_t launch_gram_diag(const TensorView& q, int H, double* partial, int n_split, double* m,
+                            hipStream_t s);
 
 // ---- attention (attend.hip) ----
 constexpr int kMaxChunks = 1024;

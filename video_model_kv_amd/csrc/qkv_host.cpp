@@ -785,8 +785,11 @@ int qkv_psac_fit(const qkv_tensor* q_hist, int32_t n_heads, int32_t rank, int32_
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   double* partial = reinterpret_cast<double*>(workspace);
   double* m = reinterpret_cast<double*>(at(workspace, align256((uint64_t)kGramSplit * H * kHeadDim * kHeadDim * 8)));
-  QKV_HIP(launch_gram(view_of(q_hist), H, partial, kGramSplit, m, s));
-  std::vector<double> hm((size_t)H * kHeadDim * kHeadDim);
+  // the eigendecomposition needs all of M; the activity and the channel order only its diagonal
+  const bool full = rank > 0 || energy_out;
+  std::vector<double> hm(full ? (size_t)H * kHeadDim * kHeadDim : (size_t)H * kHeadDim);
+  if (full) QKV_HIP(launch_gram(view_of(q_hist), H, partial, kGramSplit, m, s));
+  else QKV_HIP(launch_gram_diag(view_of(q_hist), H, partial, kGramSplit, m, s));
   QKV_HIP(hipMemcpyAsync(hm.data(), m, hm.size() * 8, hipMemcpyDeviceToHost, s));
   QKV_HIP(hipStreamSynchronize(s));
 
@@ -795,8 +798,10 @@ int qkv_psac_fit(const qkv_tensor* q_hist, int32_t n_heads, int32_t rank, int32_
   std::vector<uint8_t> hperm((size_t)H * kHeadDim);
   std::vector<float> energy(H);
   for (int h = 0; h < H; ++h)
-    for (int k = 0; k < kHeadDim; ++k) hw[(size_t)h * kHeadDim + k] = (float)(hm[((size_t)h * kHeadDim + k) * kHeadDim + k] / n);
-  if (rank > 0 || energy_out) {
+    for (int k = 0; k < kHeadDim; ++k)
+      hw[(size_t)h * kHeadDim + k] =
+          (float)(hm[full ? ((size_t)h * kHeadDim + k) * kHeadDim + k : (size_t)h * kHeadDim + k] / n);
+  if (full) {
     const unsigned nt = std::max(1u, std::min(16u, std::thread::hardware_concurrency()));
     std::vector<std::thread> pool;
     for (unsigned t = 0; t < nt; ++t) {
