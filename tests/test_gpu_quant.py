@@ -305,6 +305,9 @@ FREE = [
     ("progressive-K", 3, dict(n_heads=2, n_clusters=64), "K", 1500, False),
     ("quantwm-K", 4, dict(n_heads=2, n_clusters=64), "K", 1300, False),
     ("mixed-K", 5, dict(n_heads=2, n_clusters=64), "K", 1500, False),
+    # the mixed-layout tile kernel's other tile shapes: 3 x 21 (63 rows) and 1 x 64 (head, token) rows
+    ("mixed-K-3-heads", 5, dict(n_heads=3, n_clusters=64), "K", 1501, False),
+    ("mixed-K-1-head", 5, dict(n_heads=1, n_clusters=64), "K", 1300, False),
     ("quantwm-range-K", 6, dict(n_heads=2, n_clusters=64), "K", 1300, False),
     ("quantwm-range-K-2-stages", 6, dict(n_heads=2, n_clusters=64, n_stages=2), "K", 1300, False),
 ]

@@ -400,10 +400,13 @@ __global__ __launch_bounds__(256) void k_quant_pack_tile(PackBatch pb, int tiles
 //       kernel, into LDS in storage order (channel k at its position in perm,
 //       through the inverse order, which starts as the identity so that a perm
 //       that is not a permutation still writes inside the row);
-//   (2) one thread per (row, group) reads its group's residuals as one
-//       contiguous run, takes the group scale and packs the group's words
-//       (groups never share a word: a class starts on a word boundary and
-//       `group` is a multiple of 16; positions past a class's end stay zero);
+//   (2) wave w takes groups w, w + 4, ... of all 64 rows, one row per lane
+//       (so the group's width and bits are wave-uniform, and the rows' odd
+//       LDS pitch keeps the lanes' reads in distinct banks): it reads the
+//       group's residuals as one run, takes the group scale and packs the
+//       group's words (groups never share a word: a class starts on a word
+//       boundary and `group` is a multiple of 16; positions past a class's
+//       end stay zero), into LDS rows ordered (head, token);
 //   (3) codes and scales leave per head as contiguous runs.
 // Stages that also need the fp32 residual (y_next) take k_quant_pack.
 constexpr int kMixMaxWords = 17;     // 4-bit words + 2-bit words of a row (n_int4 = 127)
@@ -411,11 +414,12 @@ constexpr int kMixMaxGroups = 9;     // ceil(n_int4 / 16) + ceil((128 - n_int4) 
 
 template <bool F32>
 __global__ __launch_bounds__(256) void k_quant_pack_tile_mixed(PackBatch pb, int tiles) {
-  __shared__ __attribute__((aligned(16))) float s_r[kTileRows][kHeadDim + 4];
+  __shared__ float s_r[kTileRows][kHeadDim + 5];   // odd pitch: one row per lane in (2)
   __shared__ uint8_t s_inv[kTileHeads][kHeadDim];     // storage position of each channel
-  __shared__ uint32_t s_codes[kTileRows * kMixMaxWords];
+  __shared__ uint32_t s_codes[kTileRows * kMixMaxWords];   // rows in (head, token) order
   __shared__ uint16_t s_scales[kTileRows * kMixMaxGroups];
   __shared__ float s_rtab[128];                   // fp32(1 / (1 + k / 128))
+  __shared__ int4 s_grp[kMixMaxGroups];           // per group: start, len, bits, first word
   const int tid = threadIdx.x;
   if (tid < 128) s_rtab[tid] = 1.0f / (1.0f + (float)tid * 0.0078125f);
   const uint32_t logical = xcd_remap(blockIdx.x, gridDim.x);   // consecutive tiles share an XCD (L2)
@@ -424,9 +428,15 @@ __global__ __launch_bounds__(256) void k_quant_pack_tile_mixed(PackBatch pb, int
   const TileGeom tg = tile_geom(a.H, a.N);
   const int ntb = (a.N + tg.T - 1) / tg.T;
   const int i0 = (tile % ntb) * tg.T, h0 = (tile / ntb) * tg.HB;
-  const int rows = tg.T * tg.HB;
   const int tmax = a.N - 1 - i0, hmax = a.H - 1 - h0;
+  // row lr of the tile is (token lr / HB, head lr % HB); HB <= 4 and lr < 64, so
+  // (lr * hb_inv) >> 16 is the exact quotient
+  const uint32_t hb_inv = (65536u + (uint32_t)tg.HB - 1u) / (uint32_t)tg.HB;
   for (int i = tid; i < kTileHeads * kHeadDim; i += 256) s_inv[i >> 7][i & (kHeadDim - 1)] = (uint8_t)(i & (kHeadDim - 1));
+  if (tid < a.groups) {
+    const GroupInfo gi = group_info(tid, a.bits, a.group, a.n_int4, a.int4_words);
+    s_grp[tid] = make_int4(gi.start, gi.len, gi.bits, gi.word0 + gi.pos0 / (32 / gi.bits));
+  }
   // (1) residuals; rows outside the tile read a clamped valid row.  Every
   // global load the tile needs is issued before the first barrier -- the
   // heads' perm rows, the labels, the input rows -- then the labelled
@@ -449,7 +459,7 @@ __global__ __launch_bounds__(256) void k_quant_pack_tile_mixed(PackBatch pb, int
 #pragma unroll
   for (int x = 0; x < kIt; ++x) {
     const int lr = x * 16 + (tid >> 4);
-    const int t = lr / tg.HB, hh = lr - t * tg.HB;
+    const int t = (int)(((uint32_t)lr * hb_inv) >> 16), hh = lr - t * tg.HB;
     const int tc = min(t, tmax), hc = min(hh, hmax);
     hcs[x] = hc;
     lab[x] = lab_base[__umul24((uint32_t)hc, NN) + (uint32_t)tc];
@@ -483,7 +493,7 @@ __global__ __launch_bounds__(256) void k_quant_pack_tile_mixed(PackBatch pb, int
 #pragma unroll
   for (int x = 0; x < kIt; ++x) {
     const int lr = x * 16 + (tid >> 4);
-    const int hh = lr - (lr / tg.HB) * tg.HB;
+    const int hh = lr - (int)(((uint32_t)lr * hb_inv) >> 16) * tg.HB;
     float yv[8], cv[8];
     if constexpr (F32) {
 #pragma unroll
@@ -500,51 +510,59 @@ __global__ __launch_bounds__(256) void k_quant_pack_tile_mixed(PackBatch pb, int
     for (int e = 0; e < 8; ++e) s_r[lr][inv[k0 + e]] = yv[e] - cv[e];
   }
   __syncthreads();
-  // (2) one (row, group) per thread
+  // (2) wave w: groups w, w + 4, ... of every row, lane = row
   const int NG = a.groups, W = a.words;
-  for (int idx = tid; idx < rows * NG; idx += 256) {
-    const int lr = idx / NG, g = idx - lr * NG;
-    const float* rr = s_r[lr] + 0;
-    const GroupInfo gi = group_info(g, a.bits, a.group, a.n_int4, a.int4_words);
-    float amax = 0.0f;
-    for (int e = 0; e < gi.len; ++e) amax = fmaxf(amax, fabsf(rr[gi.start + e]));
-    const float qmax = (float)((1 << (gi.bits - 1)) - 1);
-    const uint32_t sbits = f32_to_bf16_bits(amax / qmax);
-    const float S = bf16_bits_to_f32(sbits);
-    s_scales[lr * NG + g] = (uint16_t)sbits;
-    const int per = 32 / gi.bits;
-    uint32_t* wout = &s_codes[lr * W + gi.word0 + gi.pos0 / per];
-    for (int e0 = 0; e0 < gi.len; e0 += 8) {
-      float r8[8];
-      const int n = min(8, gi.len - e0);
+  {
+    const int lr = tid & (kTileRows - 1), wave = tid >> 6;
+    const int t = (int)(((uint32_t)lr * hb_inv) >> 16), hh = lr - t * tg.HB;
+    const int orow = hh * tg.T + t;                // output row: (head, token) order
+    const float* rr = s_r[lr];
+    // t == T only for lane 63 when HB = 3 (63 rows): not a row of the tile
+    for (int g = t < tg.T ? wave : NG; g < NG; g += 4) {
+      const int4 gd = s_grp[g];
+      const int start = gd.x, len = gd.y, bits = gd.z;
+      float amax = 0.0f;
+      for (int e0 = 0; e0 < len; e0 += 8) {       // eight reads at a time (past the end: the last again)
+        float r8[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) r8[e] = e < n ? rr[gi.start + e0 + e] : 0.0f;
-      if (gi.bits == 4) {
-        uint32_t w = pack8_codes<4>(r8, S, sbits, s_rtab);
-        if (n < 8) w &= (1u << (4 * n)) - 1u;
-        wout[e0 >> 3] = w;
-      } else {
-        uint32_t w = pack8_codes<2>(r8, S, sbits, s_rtab);
-        if (n < 8) w &= (1u << (2 * n)) - 1u;
-        if ((e0 & 8) == 0) wout[e0 >> 4] = w;                 // low half; the high half may follow
-        else wout[e0 >> 4] |= w << 16;
+        for (int e = 0; e < 8; ++e) r8[e] = rr[start + min(e0 + e, len - 1)];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(r8[e]));
+      }
+      const float qmax = (float)((1 << (bits - 1)) - 1);
+      const uint32_t sbits = f32_to_bf16_bits(amax / qmax);
+      const float S = bf16_bits_to_f32(sbits);
+      s_scales[orow * NG + g] = (uint16_t)sbits;
+      uint32_t* wout = &s_codes[orow * W + gd.w];
+      for (int e0 = 0; e0 < len; e0 += 8) {
+        float r8[8];
+        const int n = min(8, len - e0);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) r8[e] = e < n ? rr[start + e0 + e] : 0.0f;
+        if (bits == 4) {
+          uint32_t w = pack8_codes<4>(r8, S, sbits, s_rtab);
+          if (n < 8) w &= (1u << (4 * n)) - 1u;
+          wout[e0 >> 3] = w;
+        } else {
+          uint32_t w = pack8_codes<2>(r8, S, sbits, s_rtab);
+          if (n < 8) w &= (1u << (2 * n)) - 1u;
+          if ((e0 & 8) == 0) wout[e0 >> 4] = w;                 // low half; the high half may follow
+          else wout[e0 >> 4] |= w << 16;
+        }
       }
     }
   }
   __syncthreads();
-  // (3) write-out: per head, the tile's T rows are contiguous in [H][N] order
+  // (3) write-out: per head, the tile's valid rows are one contiguous run of
+  // codes and one of scales, in LDS and in the packed layout alike
   const int tv = min(tg.T, a.N - i0);
-  for (int idx = tid; idx < tg.HB * tg.T * W; idx += 256) {
-    const int hh = idx / (tg.T * W), rem = idx - hh * (tg.T * W);
-    const int t = rem / W, w = rem - t * W;
-    if (hh <= hmax && t < tv)
-      a.codes[((int64_t)(h0 + hh) * a.N + i0 + t) * W + w] = s_codes[(t * tg.HB + hh) * W + w];
-  }
-  for (int idx = tid; idx < tg.HB * tg.T * NG; idx += 256) {
-    const int hh = idx / (tg.T * NG), rem = idx - hh * (tg.T * NG);
-    const int t = rem / NG, g = rem - t * NG;
-    if (hh <= hmax && t < tv)
-      a.scales[((int64_t)(h0 + hh) * a.N + i0 + t) * NG + g] = s_scales[(t * tg.HB + hh) * NG + g];
+  for (int hh = 0; hh < tg.HB && hh <= hmax; ++hh) {
+    uint32_t* cdst = a.codes + ((int64_t)(h0 + hh) * a.N + i0) * W;
+    const uint32_t* csrc = &s_codes[hh * tg.T * W];
+    for (int j = tid; j < tv * W; j += 256) cdst[j] = csrc[j];
+    uint16_t* sdst = a.scales + ((int64_t)(h0 + hh) * a.N + i0) * NG;
+    const uint16_t* ssrc = &s_scales[hh * tg.T * NG];
+    for (int j = tid; j < tv * NG; j += 256) sdst[j] = ssrc[j];
   }
 }
 
