@@ -1324,23 +1324,29 @@ __global__ __launch_bounds__(256) void k_repack_mix(const ChunkRec* __restrict__
   }
   if (threadIdx.x < kHeadDim) rho[threadIdx.x] = mix->rho[threadIdx.x];
   __syncthreads();
+  // this thread's output word `it` is the same for every row: its eight
+  // nibbles' source word, bit offset, width and offset (u' = q + 8: a 4-bit
+  // code as stored, a 2-bit code + 6) are fixed before the row loop
   const int it = threadIdx.x & 15;
+  int src_w[8];
+  uint32_t src_sh[8], src_bw[8], src_ad[8];
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    const int p = rho[it * 8 + t];
+    const int pb = p - n4;
+    const bool b4 = p < n4;
+    src_w[t] = b4 ? min(p >> 3, W - 1) : min(w4 + (pb >> 4), W - 1);
+    src_sh[t] = b4 ? 4u * (uint32_t)(p & 7) : 2u * (uint32_t)(pb & 15);
+    src_bw[t] = b4 ? 4u : 2u;
+    src_ad[t] = b4 ? 0u : 6u;
+  }
   uint32_t* dst = reinterpret_cast<uint32_t*>(const_cast<uint8_t*>(c.krep)) + r0 * 16;
   for (int tr = threadIdx.x >> 4; tr < nrows; tr += 16) {   // thread (row, 4-byte output word)
     const uint32_t* rw = sw + tr * W;
     uint32_t acc = 0;
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      const int p = rho[it * 8 + t];
-      uint32_t u;
-      if (p < n4) {
-        u = (rw[min(p >> 3, W - 1)] >> (4 * (p & 7))) & 15u;
-      } else {
-        const int pb = p - n4;
-        u = ((rw[min(w4 + (pb >> 4), W - 1)] >> (2 * (pb & 15))) & 3u) + 6u;
-      }
-      acc |= u << (4 * ((t >> 1) + 4 * (t & 1)));
-    }
+    for (int t = 0; t < 8; ++t)
+      acc |= (__builtin_amdgcn_ubfe(rw[src_w[t]], src_sh[t], src_bw[t]) + src_ad[t]) << (4 * ((t >> 1) + 4 * (t & 1)));
     dst[tr * 16 + it] = acc;
   }
 }
