@@ -820,6 +820,9 @@ __global__ __launch_bounds__(kThreads) void k_attend(AttendArgs a) {
       int lim = nvalid;
       if (a.causal) lim = min(lim, vis_end(qrow) - kstart);
       lim -= half * 4;
+      // opaque here, so the 32 differences below are formed only in masked
+      // tiles (hoisted, they cost 32 VALU and 31 VGPRs in every tile)
+      asm volatile("" : "+v"(lim));
 #pragma unroll
       for (int i = 0; i < 32; ++i) {
         const int kc = (i >> 4) * 32 + ((i & 15) >> 2) * 8 + (i & 3);
