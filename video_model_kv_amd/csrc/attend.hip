@@ -473,9 +473,10 @@ __global__ __launch_bounds__(kThreads) void k_attend(AttendArgs a) {
   // compute, so the two waves sharing a SIMD overlap MFMA and VALU work.
   //
   // Per-thread and per-wave indexes used inside the steps come from xtid and
-  // xwave, which are made opaque at every step so that the addresses derived
-  // from them are recomputed there instead of being held in registers across
-  // the whole loop.
+  // xwave, which are made opaque at every step (xtid only in the variants
+  // whose registers cannot hold the lane addresses) so that the addresses
+  // derived from them are recomputed there instead of being held in registers
+  // across the whole loop.
   int xtid = tid, xwave = wave;
   auto geom = [&](int cc, bool v) __attribute__((always_inline)) -> ChunkDecode {
     return make_decode(v ? a.vp : a.kp, recs[cc].n, v ? recs[cc].vbase : recs[cc].kbase);
@@ -945,7 +946,12 @@ __global__ __launch_bounds__(kThreads) void k_attend(AttendArgs a) {
   for (int ti = t_begin; ti < t_end; ++ti) {
     xtid = tid;
     xwave = wave;
-    asm volatile("" : "+v"(xtid), "+s"(xwave));
+    // the lean fast-decode variants keep their lane addresses in registers
+    // (101 instead of 204 VALU of per-step set-up, no spills); the others would
+    // spill them, so there the thread index is made opaque too
+    constexpr bool kLaneAddrKept = !QF32 && KM != 0 && VFAST && !LOGITS && !PSAC && !FRESH;
+    if constexpr (kLaneAddrKept) asm volatile("" : "+s"(xwave));
+    else asm volatile("" : "+v"(xtid), "+s"(xwave));
     const int r3 = ring;                         // (ti + 3) % 3
     const int r1 = ring + 1 == kRing ? 0 : ring + 1;
     const int r2 = r1 + 1 == kRing ? 0 : r1 + 1;
