@@ -434,8 +434,10 @@ __global__ __launch_bounds__(kThreads) void k_attend(AttendArgs a) {
   const float sfull = a.scale * pow2(rx.eq + rx.ek);   // logit = sfull * accumulator
   const float c2 = sfull * kLog2e;
 
-  const int t_begin = (int)(((int64_t)a.n_tiles * split) / a.n_split);
-  int t_end = (int)(((int64_t)a.n_tiles * (split + 1)) / a.n_split);
+  const int64_t t_span = a.n_tiles - a.tile_lo;
+  const int t_begin = a.tile_lo + (int)((t_span * split) / a.n_split);
+  int t_end = a.tile_lo + (int)((t_span * (split + 1)) / a.n_split);
+  const int prow_split = a.split_base + split;   // this split's partial row
 
   // Tile and chunk records are read-only here: scalar loads through the
   // constant address space keep them out of the vector-memory counter, which
@@ -449,13 +451,13 @@ __global__ __launch_bounds__(kThreads) void k_attend(AttendArgs a) {
   }
   if (t_begin >= t_end) {
     // nothing visible in this split: write an empty partial
-    if (qok && a.n_split > 1) {
+    if (qok && a.n_split_total > 1) {
       if (half == 0) {
-        float* ml = a.part_ml + (((int64_t)split * a.H + h) * a.Nq + qrow) * 2;
+        float* ml = a.part_ml + (((int64_t)prow_split * a.H + h) * a.Nq + qrow) * 2;
         ml[0] = -INFINITY;
         ml[1] = 0.0f;
       }
-      float* prow = a.part_o + (((int64_t)split * a.H + h) * a.Nq + qrow) * kHeadDim;
+      float* prow = a.part_o + (((int64_t)prow_split * a.H + h) * a.Nq + qrow) * kHeadDim;
       for (int d0 = half * 4; d0 < kHeadDim; d0 += 8)
         *reinterpret_cast<float4*>(prow + d0) = make_float4(0, 0, 0, 0);
     }
@@ -1029,7 +1031,7 @@ __global__ __launch_bounds__(kThreads) void k_attend(AttendArgs a) {
   asm volatile("" : "+s"(E));
   const float l_tot = l_run + __shfl_xor(l_run, 32);
   if (!qok) return;
-  if (E->n_split == 1) {
+  if (E->n_split_total == 1) {
     const float inv = l_tot > 0.0f ? pow2(rx.ev) / l_tot : 0.0f;
     float* orow = E->out + (int64_t)qrow * E->out_stride_token + (int64_t)h * E->out_stride_head;
 #pragma unroll
@@ -1041,7 +1043,8 @@ __global__ __launch_bounds__(kThreads) void k_attend(AttendArgs a) {
             make_float4(o[db][4 * g] * inv, o[db][4 * g + 1] * inv, o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv);
       }
   } else {
-    float* prow = E->part_o + (((int64_t)split * E->H + h) * E->Nq + qrow) * kHeadDim;
+    const int ps = E->split_base + split;
+    float* prow = E->part_o + (((int64_t)ps * E->H + h) * E->Nq + qrow) * kHeadDim;
 #pragma unroll
     for (int db = 0; db < 4; ++db)
 #pragma unroll
@@ -1050,7 +1053,7 @@ __global__ __launch_bounds__(kThreads) void k_attend(AttendArgs a) {
         *reinterpret_cast<float4*>(prow + d0) = make_float4(o[db][4 * g], o[db][4 * g + 1], o[db][4 * g + 2], o[db][4 * g + 3]);
       }
     if (half == 0) {
-      float* ml = E->part_ml + (((int64_t)split * E->H + h) * E->Nq + qrow) * 2;
+      float* ml = E->part_ml + (((int64_t)ps * E->H + h) * E->Nq + qrow) * 2;
       ml[0] = m_run;
       ml[1] = l_tot;
     }
@@ -1066,12 +1069,12 @@ __global__ __launch_bounds__(256) void k_merge(AttendArgs a) {
   const int64_t hq = gid / (kHeadDim / 4);
   const int qrow = (int)(hq % a.Nq), h = (int)(hq / a.Nq);
   float mmax = -INFINITY;
-  for (int s = 0; s < a.n_split; ++s)
+  for (int s = 0; s < a.n_split_total; ++s)
     mmax = fmaxf(mmax, a.part_ml[(((int64_t)s * a.H + h) * a.Nq + qrow) * 2]);
   float4 acc = make_float4(0, 0, 0, 0);
   float lsum = 0.0f;
   if (mmax != -INFINITY) {
-    for (int s = 0; s < a.n_split; ++s) {
+    for (int s = 0; s < a.n_split_total; ++s) {
       const int64_t r = ((int64_t)s * a.H + h) * a.Nq + qrow;
       const float ms = a.part_ml[r * 2];
       if (ms == -INFINITY) continue;
@@ -1429,6 +1432,9 @@ void launch_attend_variant(int flags, const AttendArgs& a, dim3 grid, hipStream_
 
 
 hipError_t launch_attend(const AttendArgs& a, hipStream_t s) {
+  if (a.n_split < 1 || a.tile_lo < 0 || a.tile_lo >= a.n_tiles || a.split_base < 0 ||
+      a.split_base + a.n_split > a.n_split_total || (a.n_split_total > 1 && (!a.part_o || !a.part_ml)))
+    return hipErrorInvalidValue;
   if (a.psac_rank > 0) {
     TimedLaunch tl_("k_qu", s);
     const int64_t n = (int64_t)a.H * a.Nq;
@@ -1459,7 +1465,8 @@ hipError_t launch_attend(const AttendArgs& a, hipStream_t s) {
     }
   }
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || a.n_split == 1) return e;
+  // the merge follows the launch that writes the last partial rows
+  if (e != hipSuccess || a.n_split_total == 1 || a.split_base + a.n_split < a.n_split_total) return e;
   const int64_t total = (int64_t)a.H * a.Nq * (kHeadDim / 4);
   TimedLaunch tl_("k_merge", s);
   hipLaunchKernelGGL(k_merge, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, a);

@@ -284,9 +284,11 @@ struct AttendArgs {
   TensorView kf, vf;             // the fresh chunk's keys and values ([Nf][H][128]; ptr null when none)
   int n_cache_tiles;             // tiles of the packed chunks; tiles past them are the fresh chunk's
   float scale;
-  int n_split;                   // split s covers tiles [n_tiles*s/n_split, n_tiles*(s+1)/n_split)
-  float* part_o;                 // [n_split][H][Nq][128]
-  float* part_ml;                // [n_split][H][Nq][2]
+  int n_split;                   // split s covers tiles [t0 + n*s/n_split, t0 + n*(s+1)/n_split), n = n_tiles - t0
+  int tile_lo;                   // t0: the first tile of this launch (0 unless a call takes two launches)
+  int split_base, n_split_total; // split s writes partial row split_base + s of n_split_total (1: the output)
+  float* part_o;                 // [n_split_total][H][Nq][128]
+  float* part_ml;                // [n_split_total][H][Nq][2]
   float* out;                    // [Nq][H][128] via strides
   int64_t out_stride_token, out_stride_head;
   float* logits;                 // [H][Nq][Nk] or null

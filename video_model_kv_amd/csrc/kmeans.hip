@@ -977,10 +977,10 @@ __global__ __launch_bounds__(256) void k_group(KmBatch b) { group_head(b, blockI
 // full update (the usual case) dispatch a few hundred workgroups, not one per
 // head and cluster group.
 __device__ __forceinline__ int listed_heads(const KmBatch& b, const KmItem& it) {
-  return (int)it.hlist[0] + (b.iter == 1 ? (int)it.hlist[1] : 0);
+  return (int)min(it.hlist[0], (uint32_t)b.H) + (b.iter == 1 ? (int)min(it.hlist[1], (uint32_t)b.H) : 0);
 }
 __device__ __forceinline__ int listed_head(const KmBatch& b, const KmItem& it, int e) {
-  const int n0 = (int)it.hlist[0];
+  const int n0 = (int)min(it.hlist[0], (uint32_t)b.H);
   return (int)(e < n0 ? it.hlist[2 + e] : it.hlist[2 + b.H + (e - n0)]);
 }
 
@@ -1554,7 +1554,7 @@ __global__ __launch_bounds__(64) void k_cert(KmBatch b) {
     if (cl != kCertF64) {                        // the later full updates' head lists
       const int k = cl == kCertFix ? 1 : 0;
       const uint32_t slot = atomicAdd(&it.hlist[k], 1u);   // one entry per head: slot < H
-      it.hlist[2 + k * b.H + slot] = (uint32_t)h;
+      if (slot < (uint32_t)b.H) it.hlist[2 + k * b.H + slot] = (uint32_t)h;
     }
   }
 }

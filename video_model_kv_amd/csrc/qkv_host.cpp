@@ -661,7 +661,17 @@ int attend_impl(const char* fn, const qkv_config* k_cfg, const qkv_config* v_cfg
                     q->dtype == QKV_BF16 && mix4_order(params_of(k_cfg), &mix);
   const int kmode = kfast ? 1 : kmix ? 2 : 0;
   const int kC16 = kmode ? k_cfg->n_clusters : 0, vC16 = vfast ? v_cfg->n_clusters : 0;
-  const AttendWs ws = attend_ws(H, Nq, n_chunks, n_tiles, ns > 1 ? (int64_t)ns * Nq : 0, kC16, vC16,
+  // A fresh chunk over packed chunks with the lean decode (fast K and V, bf16 queries, no PSAC, no
+  // logits): the cached tiles take the lean kernel variant in a launch of their own -- non-causal, as
+  // every cached key is visible to every query of the fresh chunk -- and the fresh chunk's tiles the
+  // fresh-chunk variant in a second one; the merge joins their partial rows (at most split_cap rows
+  // per query in all, as the workspace provides).
+  const int cap = split_cap(H, Nq);
+  const bool two = fresh && n_chunks > 0 && kmode != 0 && vfast && q->dtype == QKV_BF16 && k_cfg->psac_rank == 0 &&
+                   !logits_debug && cap >= 2;
+  const int ns_cache = two ? std::min(choose_splits(H, Nq, n_cache_tiles), cap - 1) : 0;
+  const int ns_total = two ? ns_cache + 1 : ns;
+  const AttendWs ws = attend_ws(H, Nq, n_chunks, n_tiles, ns_total > 1 ? (int64_t)ns_total * Nq : 0, kC16, vC16,
                                 kmix ? (uint64_t)H * Nk * 64 : 0);
   QKV_TRY(check_ws(workspace, workspace_bytes, ws.bytes, fn));
   if (kmix) {
@@ -735,6 +745,9 @@ int attend_impl(const char* fn, const qkv_config* k_cfg, const qkv_config* v_cfg
   a.n_cache_tiles = (int)n_cache_tiles;
   a.scale = softmax_scale > 0.0f ? softmax_scale : 1.0f / std::sqrt((float)kHeadDim);
   a.n_split = ns;
+  a.tile_lo = 0;
+  a.split_base = 0;
+  a.n_split_total = ns;
   a.part_o = reinterpret_cast<float*>(at(workspace, ws.part_o));
   a.part_ml = reinterpret_cast<float*>(at(workspace, ws.part_ml));
   a.out = reinterpret_cast<float*>(out->ptr);
@@ -745,6 +758,22 @@ int attend_impl(const char* fn, const qkv_config* k_cfg, const qkv_config* v_cfg
   a.k_mode = kmode;
   a.mixp = dmix;
   a.v_uniform_int2_1stage = vfast;
+  if (two) {
+    AttendArgs c = a;                            // the cached tiles
+    c.kf = TensorView{};
+    c.vf = TensorView{};
+    c.causal = 0;
+    c.mask_F = 1;
+    c.mask_base = 0;
+    c.n_tiles = (int)n_cache_tiles;
+    c.n_split = ns_cache;
+    c.n_split_total = ns_total;
+    QKV_HIP(launch_attend(c, s));
+    a.tile_lo = (int)n_cache_tiles;              // the fresh chunk's tiles, then the merge
+    a.n_split = 1;
+    a.split_base = ns_cache;
+    a.n_split_total = ns_total;
+  }
   QKV_HIP(launch_attend(a, s));
   return ok();
 }
