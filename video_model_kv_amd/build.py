@@ -17,8 +17,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libqkv.so")
-HIP_SOURCES = ["kmeans.hip", "quant.hip", "attend.hip", "gram.hip", "scratch.hip", "temporal.hip"]
-CPP_SOURCES = ["qkv_host.cpp", "jacobi.cpp", "timing.cpp"]
+HIP_SOURCES = ["kmeans.hip", "quant.hip", "attend.hip", "gram.hip", "eigh.hip", "scratch.hip", "temporal.hip"]
+CPP_SOURCES = ["qkv_host.cpp", "timing.cpp"]
 ARCH = os.environ.get("QKV_OFFLOAD_ARCH", "gfx950")
 
 HIP_FLAGS = [

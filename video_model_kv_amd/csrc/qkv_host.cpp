@@ -19,10 +19,6 @@
 
 #include "kernels.h"
 
-namespace qkv {
-void jacobi_eigh(int n, double* a, double* evals, double* evecs);
-}
-
 using namespace qkv;
 
 namespace qkv {
@@ -816,41 +812,28 @@ int qkv_psac_fit(const qkv_tensor* q_hist, int32_t n_heads, int32_t rank, int32_
   double* m = reinterpret_cast<double*>(at(workspace, align256((uint64_t)kGramSplit * H * kHeadDim * kHeadDim * 8)));
   // the eigendecomposition needs all of M; the activity and the channel order only its diagonal
   const bool full = rank > 0 || energy_out;
-  std::vector<double> hm(full ? (size_t)H * kHeadDim * kHeadDim : (size_t)H * kHeadDim);
-  if (full) QKV_HIP(launch_gram(view_of(q_hist), H, partial, kGramSplit, m, s));
-  else QKV_HIP(launch_gram_diag(view_of(q_hist), H, partial, kGramSplit, m, s));
-  QKV_HIP(hipMemcpyAsync(hm.data(), m, hm.size() * 8, hipMemcpyDeviceToHost, s));
+  std::vector<double> hd((size_t)H * kHeadDim);
+  std::vector<float> energy(H);
+  if (full) {
+    // the partials are consumed by the reduction: they hold the solver's V^T, M's diagonal and the energies
+    double* vt = partial;
+    double* dg = partial + (size_t)H * kHeadDim * kHeadDim;
+    float* en = reinterpret_cast<float*>(dg + (size_t)H * kHeadDim);
+    QKV_HIP(launch_gram(view_of(q_hist), H, partial, kGramSplit, m, s));
+    QKV_HIP(launch_eigh(m, H, vt, rank, rank > 0 ? U_out : nullptr, en, dg, s));
+    QKV_HIP(hipMemcpyAsync(hd.data(), dg, hd.size() * 8, hipMemcpyDeviceToHost, s));
+    QKV_HIP(hipMemcpyAsync(energy.data(), en, energy.size() * 4, hipMemcpyDeviceToHost, s));
+  } else {
+    QKV_HIP(launch_gram_diag(view_of(q_hist), H, partial, kGramSplit, m, s));
+    QKV_HIP(hipMemcpyAsync(hd.data(), m, hd.size() * 8, hipMemcpyDeviceToHost, s));
+  }
   QKV_HIP(hipStreamSynchronize(s));
 
   const double n = (double)q_hist->n_tokens;
-  std::vector<float> hw((size_t)H * kHeadDim), hU((size_t)H * kHeadDim * std::max(rank, 1));
+  std::vector<float> hw((size_t)H * kHeadDim);
   std::vector<uint8_t> hperm((size_t)H * kHeadDim);
-  std::vector<float> energy(H);
   for (int h = 0; h < H; ++h)
-    for (int k = 0; k < kHeadDim; ++k)
-      hw[(size_t)h * kHeadDim + k] =
-          (float)(hm[full ? ((size_t)h * kHeadDim + k) * kHeadDim + k : (size_t)h * kHeadDim + k] / n);
-  if (full) {
-    const unsigned nt = std::max(1u, std::min(16u, std::thread::hardware_concurrency()));
-    std::vector<std::thread> pool;
-    for (unsigned t = 0; t < nt; ++t) {
-      pool.emplace_back([&, t]() {
-        std::vector<double> a((size_t)kHeadDim * kHeadDim), ev(kHeadDim), vec((size_t)kHeadDim * kHeadDim);
-        for (int h = (int)t; h < H; h += (int)nt) {
-          std::memcpy(a.data(), hm.data() + (size_t)h * kHeadDim * kHeadDim, a.size() * 8);
-          jacobi_eigh(kHeadDim, a.data(), ev.data(), vec.data());
-          double tot = 0.0, top = 0.0;
-          for (int i = 0; i < kHeadDim; ++i) tot += ev[i];
-          for (int i = 0; i < rank; ++i) top += ev[i];
-          energy[h] = tot > 0.0 ? (float)(top / tot) : 0.0f;
-          for (int k = 0; k < kHeadDim; ++k)
-            for (int b = 0; b < rank; ++b)
-              hU[((size_t)h * kHeadDim + k) * rank + b] = (float)vec[(size_t)k * kHeadDim + b];
-        }
-      });
-    }
-    for (auto& th : pool) th.join();
-  }
+    for (int k = 0; k < kHeadDim; ++k) hw[(size_t)h * kHeadDim + k] = (float)(hd[(size_t)h * kHeadDim + k] / n);
   for (int h = 0; h < H; ++h) {
     std::vector<int> order(kHeadDim);
     for (int k = 0; k < kHeadDim; ++k) order[k] = k;
@@ -865,7 +848,6 @@ int qkv_psac_fit(const qkv_tensor* q_hist, int32_t n_heads, int32_t rank, int32_
   }
   // outputs on the caller's stream, complete (host buffers released) before the return
   if (w_out) QKV_HIP(hipMemcpyAsync(w_out, hw.data(), hw.size() * 4, hipMemcpyHostToDevice, s));
-  if (rank > 0) QKV_HIP(hipMemcpyAsync(U_out, hU.data(), (size_t)H * kHeadDim * rank * 4, hipMemcpyHostToDevice, s));
   if (perm_out && n_int4 > 0) QKV_HIP(hipMemcpyAsync(perm_out, hperm.data(), hperm.size(), hipMemcpyHostToDevice, s));
   QKV_HIP(hipStreamSynchronize(s));
   if (energy_out) std::memcpy(energy_out, energy.data(), H * sizeof(float));
