@@ -103,28 +103,36 @@ __global__ __launch_bounds__(kEighThreads) void k_eigh(const double* __restrict_
       }
       __syncthreads();
       // columns p, q of every row: lanes take different pairs, the waves rows r = wave + 4 j
-      {
+      {                                          // (the pairs are disjoint: eight rows' loads, then their stores)
         const int i = lane, p = rp[i], q = rq[i];
         const double c = rc[i], s = rs[i];
-        for (int r = wave; r < kN; r += kEighThreads / 64) {
-          const double ap = A[r][p], aq = A[r][q];
-          A[r][p] = c * ap - s * aq;
-          A[r][q] = s * ap + c * aq;
+        for (int r0 = wave; r0 < kN; r0 += 8 * (kEighThreads / 64)) {
+          double ap[8], aq[8];
+#pragma unroll
+          for (int u = 0; u < 8; ++u) {
+            ap[u] = A[r0 + u * (kEighThreads / 64)][p];
+            aq[u] = A[r0 + u * (kEighThreads / 64)][q];
+          }
+#pragma unroll
+          for (int u = 0; u < 8; ++u) {
+            A[r0 + u * (kEighThreads / 64)][p] = c * ap[u] - s * aq[u];
+            A[r0 + u * (kEighThreads / 64)][q] = s * ap[u] + c * aq[u];
+          }
         }
       }
       __syncthreads();
       // rows p, q of every column: of V^T by threads 0 .. 127 (thread = column, every
-      // pair, sixteen pairs' loads at a time), of A by threads 128 .. 255
+      // pair, 32 pairs' loads at a time), of A by threads 128 .. 255 (16 at a time)
       if (tid < kN) {
-        for (int i0 = 0; i0 < kPairs; i0 += 16) {
-          double vp[16], vq[16];
+        for (int i0 = 0; i0 < kPairs; i0 += 32) {
+          double vp[32], vq[32];
 #pragma unroll
-          for (int u = 0; u < 16; ++u) {
+          for (int u = 0; u < 32; ++u) {
             vp[u] = vh[rp[i0 + u] * kN + tid];
             vq[u] = vh[rq[i0 + u] * kN + tid];
           }
 #pragma unroll
-          for (int u = 0; u < 16; ++u) {
+          for (int u = 0; u < 32; ++u) {
             const double c = rc[i0 + u], s = rs[i0 + u];
             vh[rp[i0 + u] * kN + tid] = c * vp[u] - s * vq[u];
             vh[rq[i0 + u] * kN + tid] = s * vp[u] + c * vq[u];
@@ -132,12 +140,19 @@ __global__ __launch_bounds__(kEighThreads) void k_eigh(const double* __restrict_
         }
       } else {
         const int col = tid - kN;
-        for (int i = 0; i < kPairs; ++i) {
-          const int p = rp[i], q = rq[i];
-          const double c = rc[i], s = rs[i];
-          const double ap = A[p][col], aq = A[q][col];
-          A[p][col] = c * ap - s * aq;
-          A[q][col] = s * ap + c * aq;
+        for (int i0 = 0; i0 < kPairs; i0 += 16) {
+          double ap[16], aq[16];
+#pragma unroll
+          for (int u = 0; u < 16; ++u) {
+            ap[u] = A[rp[i0 + u]][col];
+            aq[u] = A[rq[i0 + u]][col];
+          }
+#pragma unroll
+          for (int u = 0; u < 16; ++u) {
+            const double c = rc[i0 + u], s = rs[i0 + u];
+            A[rp[i0 + u]][col] = c * ap[u] - s * aq[u];
+            A[rq[i0 + u]][col] = s * ap[u] + c * aq[u];
+          }
         }
       }
       __syncthreads();
