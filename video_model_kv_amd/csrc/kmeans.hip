@@ -1335,7 +1335,7 @@ __global__ __launch_bounds__(256, 4) void k_update_list(KmBatch b) {
 // finds them as its previous labels.
 constexpr int kDeltaSplit = 2;
 constexpr int kDeltaSlots = 2;               // clusters per lane group in flight
-constexpr int kDeltaRows = 8;                 // member-row loads in flight per cluster
+constexpr int kDeltaRows = 4;                 // member-row loads in flight per cluster
 
 __global__ __launch_bounds__(256) void k_update_delta(KmBatch b) {
   const KmItem& it = b.it[blockIdx.y];
