@@ -21,9 +21,10 @@ __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as
 
 // float -> bfloat16 bits, round to nearest, ties to even (finite inputs).
 __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return u >> 16;
+  // round to nearest even by the hardware conversion (v_cvt_pk_bf16_f32 on
+  // gfx950; fp32 subnormals are kept): for every finite f the same bits as
+  // adding 0x7FFF + the lowest kept bit and truncating
+  return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)f);
 }
 
 // double -> bfloat16 bits with a single round-to-nearest-even (normal range;
