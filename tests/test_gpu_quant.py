@@ -504,6 +504,44 @@ def test_psac_fit_matches_oracle():
     assert np.array_equal(p0.cpu().numpy(), pg), "rank 0: channel order"
 
 
+def test_psac_fit_degenerate_histories():
+    """The GPU eigensolver at its edges.  An all-zero history: M = 0, no sweep
+    runs, every weight is 0 and the energy fraction is 0 (the total is not
+    positive); U is still orthonormal.  A history whose channels are mutually
+    orthogonal (each query has one nonzero channel): M is diagonal, already
+    converged, so U's columns are the unit vectors of the eight largest
+    entries in descending order and the energy is their share of the trace."""
+    t = G.torch()
+    H, n, r = 2, 512, 8
+    cfg = G.config_of(synth.workload(4, n_heads=H), "K")
+    ws = G.workspace(cfg, 0, n, 0)
+    U = t.empty((H, 128, r), dtype=t.float32, device=G.dev())
+    w = t.empty((H, 128), dtype=t.float32, device=G.dev())
+    zero = np.zeros((n, H, 128), np.float32)
+    energy = qk.qkv_psac_fit(G.to_dev(zero, "bf16"), H, r, 0, ws, U_out=U, w_out=w)
+    Ug = U.cpu().numpy().astype(np.float64)
+    assert np.all(w.cpu().numpy() == 0.0) and all(e == 0.0 for e in energy)
+    for h in range(H):
+        assert np.allclose(Ug[h].T @ Ug[h], np.eye(r), atol=1e-6), f"zero history, head {h}: U not orthonormal"
+    # one nonzero channel per query: query i of head h has value a[h, i % 128] in channel i % 128
+    rng = np.random.default_rng(3)
+    amp = rng.choice(np.arange(1, 129), size=(H, 128), replace=True).astype(np.float32) / 16.0
+    x = np.zeros((n, H, 128), np.float32)
+    for i in range(n):
+        x[i, :, i % 128] = amp[:, i % 128]
+    energy = qk.qkv_psac_fit(G.to_dev(x, "bf16"), H, r, 0, ws, U_out=U, w_out=w)
+    Ug = U.cpu().numpy().astype(np.float64)
+    for h in range(H):
+        d = (x[:, h].astype(np.float64) ** 2).sum(axis=0)       # diag(M); the bf16 inputs are exact here
+        order = sorted(range(128), key=lambda k: (-d[k], k))[:r]
+        for b, k in enumerate(order):
+            col = Ug[h][:, b]
+            assert abs(abs(col[k]) - 1.0) < 1e-6 and np.abs(np.delete(col, k)).max() < 1e-6, (
+                f"diagonal history, head {h}: column {b} is not e_{k}")
+        assert abs(energy[h] - d[order].sum() / d.sum()) < 1e-6
+    G.log("psac_fit: zero and diagonal histories as defined")
+
+
 def _batch_vs_single(problems):
     """problems: list of (cfg, x_dev, (w, perm, u) device tensors or None).
     The batched write path must reproduce every single-problem call byte for byte."""
