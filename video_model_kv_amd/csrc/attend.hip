@@ -636,10 +636,17 @@ __global__ __launch_bounds__(kThreads) void k_attend(AttendArgs a) {
       // keys past nvalid decode stale LDS contents (zero at the start, then
       // earlier tiles' values): finite, and their scores are masked (probability 0)
       if (FRESH && D.fresh) {                    // a fresh-chunk tile: the keys as given, scaled
-        float v[8];
-        fresh_row<8>(a.kf, D.ftok0 + min(key, nvalid - 1), h, k0, v);
+        if (a.kf.dtype == 2) {                   // dense fp16 rows of a decoded cache, already scaled
+          const uint4 w = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(a.kf.ptr) +
+                                                          (int64_t)(D.ftok0 + min(key, nvalid - 1)) * a.kf.stride_token +
+                                                          (int64_t)h * a.kf.stride_head + k0);
+          o4[0] = w.x; o4[1] = w.y; o4[2] = w.z; o4[3] = w.w;
+        } else {
+          float v[8];
+          fresh_row<8>(a.kf, D.ftok0 + min(key, nvalid - 1), h, k0, v);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) o4[e] = pack_f16x2(v[2 * e] * ksc, v[2 * e + 1] * ksc);
+          for (int e = 0; e < 4; ++e) o4[e] = pack_f16x2(v[2 * e] * ksc, v[2 * e + 1] * ksc);
+        }
       } else if constexpr (KM == 1) {
         const uint32_t w = sRcK[r][key * 8 + (k0 >> 4)];
         const uint32_t sb = sRsK[r][klead + (key << kGs) + ((k0 << kGs) >> 7)];   // groups: powers of two
@@ -679,10 +686,18 @@ __global__ __launch_bounds__(kThreads) void k_attend(AttendArgs a) {
         const int key = 2 * kp + y;
         const bool ok = key < nvalid;
         if (FRESH && D.fresh) {
-          float v[4];
-          fresh_row<4>(a.vf, D.ftok0 + min(key, nvalid - 1), h, k0, v);
-          pr[y][0] = pack_f16x2(v[0] * vsc, v[1] * vsc);
-          pr[y][1] = pack_f16x2(v[2] * vsc, v[3] * vsc);
+          if (a.vf.dtype == 2) {                 // dense fp16 rows, already scaled
+            const uint2 w = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(a.vf.ptr) +
+                                                            (int64_t)(D.ftok0 + min(key, nvalid - 1)) * a.vf.stride_token +
+                                                            (int64_t)h * a.vf.stride_head + k0);
+            pr[y][0] = w.x;
+            pr[y][1] = w.y;
+          } else {
+            float v[4];
+            fresh_row<4>(a.vf, D.ftok0 + min(key, nvalid - 1), h, k0, v);
+            pr[y][0] = pack_f16x2(v[0] * vsc, v[1] * vsc);
+            pr[y][1] = pack_f16x2(v[2] * vsc, v[3] * vsc);
+          }
         } else if constexpr (VFAST) {
           const uint32_t w = sRcV[r][key * 8 + (k0 >> 4)];
           const uint32_t sb = sRsV[r][vlead + (key << vGs) + ((k0 << vGs) >> 7)];
@@ -1300,6 +1315,41 @@ __global__ __launch_bounds__(256) void k_range_scan(const ChunkRec* __restrict__
   }
 }
 
+// Caches that take the generic decode (several stages, INT4, groups that are
+// not multiples of 32): every (chunk, head) is decoded once per call into
+// dense fp16 rows [Nk][H][128] of K and of V, with the tile decode's own
+// arithmetic and operand scaling (decode_uniform or decode_generic, then
+// fp16(x * 2^-e)), so attending over them as fresh-chunk tiles gives the
+// attention of the generic decode.  Block (64-token block, head, chunk).
+__global__ __launch_bounds__(256) void k_dense_decode(const ChunkRec* __restrict__ recs, LayoutParams kp,
+                                                      LayoutParams vp, const uint32_t* __restrict__ range,
+                                                      uint16_t* __restrict__ dk, uint16_t* __restrict__ dv) {
+  __shared__ ChannelCode sTab[2][kHeadDim];
+  const ChunkRec& c = recs[blockIdx.z];
+  const int h = blockIdx.y, H = gridDim.y, t0 = blockIdx.x * 64;
+  if (t0 >= c.n) return;                         // the whole block
+  const RangeExps rx = range_exps((crange_ptr)range, kp, vp, false);
+  const float sc[2] = {pow2(-rx.ek), pow2(-rx.ev)};
+  const ChunkDecode dd[2] = {make_decode(kp, c.n, c.kbase), make_decode(vp, c.n, c.vbase)};
+  if (kp.n_int4 > 0) build_tab(dd[0], h, sTab[0]);
+  if (vp.n_int4 > 0) build_tab(dd[1], h, sTab[1]);
+  __syncthreads();
+  const int nt = min(64, c.n - t0);
+  for (int item = threadIdx.x; item < 2 * 64 * 16; item += blockDim.x) {   // (tensor, token, 8 channels)
+    const int v = item >= 64 * 16, r = item - v * 64 * 16;
+    const int key = r >> 4, k0 = (r & 15) * 8;
+    if (key >= nt) continue;
+    float x[8];
+    if ((v ? vp : kp).n_int4 == 0) decode_uniform<8>(dd[v], h, t0 + key, k0, x);
+    else decode_generic<8>(dd[v], sTab[v], h, t0 + key, k0, x);
+    uint32_t o4[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o4[e] = pack_f16x2(x[2 * e] * sc[v], x[2 * e + 1] * sc[v]);
+    uint16_t* dst = (v ? dv : dk) + ((int64_t)(c.token_start + t0 + key) * H + h) * kHeadDim + k0;
+    *reinterpret_cast<uint4*>(dst) = make_uint4(o4[0], o4[1], o4[2], o4[3]);
+  }
+}
+
 __global__ void k_upload(ChunkBatch b, ChunkRec* __restrict__ dst, uint32_t* __restrict__ range, MixOrder mix,
                          MixOrder* __restrict__ mix_dst) {
   const int i = threadIdx.x;
@@ -1392,6 +1442,16 @@ hipError_t launch_range_scan(const ChunkRec* recs, int n_chunks, const LayoutPar
   const int bx = std::max(1, std::min(64, 2048 / ys));
   hipLaunchKernelGGL(k_range_scan, dim3((unsigned)bx, (unsigned)ys), dim3(256), 0, s, recs, n_chunks, kp, vp, q, Nq, kf,
                      vf, n_fresh, range);
+  return hipGetLastError();
+}
+
+hipError_t launch_dense_decode(const ChunkRec* recs, int n_chunks, int max_n, int H, const LayoutParams& kp,
+                               const LayoutParams& vp, const uint32_t* range, uint16_t* dk, uint16_t* dv,
+                               hipStream_t s) {
+  TimedLaunch tl_("k_dense_decode", s);
+  if (n_chunks <= 0 || max_n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_dense_decode, dim3((unsigned)((max_n + 63) / 64), (unsigned)H, (unsigned)n_chunks), dim3(256), 0,
+                     s, recs, kp, vp, range, dk, dv);
   return hipGetLastError();
 }
 

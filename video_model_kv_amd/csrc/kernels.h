@@ -9,7 +9,8 @@
 
 namespace qkv {
 
-// A strided [n_tokens][n_heads][128] tensor (f32 or bf16; dtype 0 = f32, 1 = bf16).
+// A strided [n_tokens][n_heads][128] tensor (dtype 0 = f32, 1 = bf16; 2 = fp16 already scaled by the
+// call's operand range: the dense rows of a decoded cache, read by the attention only).
 struct TensorView {
   const void* ptr;
   int dtype;
@@ -263,6 +264,12 @@ hipError_t launch_range_scan(const ChunkRec* recs, int n_chunks, const LayoutPar
 // by the tensor's range exponent (2^-e, exact) and rounded to nearest even, for
 // the tensors decoded by the attention fast path; k16 / v16 may be NULL (tensor
 // not on the fast path).
+// Generic-layout caches decoded once into dense fp16 rows dk/dv [Nk][H][128]
+// (already scaled by the call's operand range; attended as fresh-chunk tiles
+// of dtype 2).
+hipError_t launch_dense_decode(const ChunkRec* recs, int n_chunks, int max_n, int H, const LayoutParams& kp,
+                               const LayoutParams& vp, const uint32_t* range, uint16_t* dk, uint16_t* dv,
+                               hipStream_t s);
 hipError_t launch_centroids_f16(const ChunkRec* recs, int n_chunks, const LayoutParams& kp, const LayoutParams& vp,
                                 const uint32_t* range, const MixOrder* kmix, uint16_t* k16, uint16_t* v16,
                                 hipStream_t s);

@@ -209,14 +209,15 @@ QuantWs quant_ws(const qkv_config* c, int64_t n) {
 constexpr int kTileKeys = 64;
 
 struct AttendWs {
-  uint64_t chunks, tiles, qu, part_o, part_ml, k16, v16, range, mix, krep, bytes;
+  uint64_t chunks, tiles, qu, part_o, part_ml, k16, v16, range, mix, krep, dense, bytes;
 };
 
 // rows = n_split * nq: one partial (o, m, l) row per split and query (none when n_split == 1);
 // kC16 / vC16: clusters of the key / value tables copied to fp16 for the fast decode (0: none)
 // krep_bytes: mix4 codes of the keys (64 bytes per token-head), 0 when the keys take another path
+// dense_bytes: the dense fp16 K and V rows of a cache on the generic decode (0: none)
 AttendWs attend_ws(int H, int64_t nq, int n_chunks, int64_t n_tiles, int64_t split_rows, int kC16, int vC16,
-                   uint64_t krep_bytes) {
+                   uint64_t krep_bytes, uint64_t dense_bytes = 0) {
   AttendWs w;
   uint64_t off = 0;
   w.chunks = off;  off += align256((uint64_t)n_chunks * sizeof(ChunkRec));
@@ -229,6 +230,7 @@ AttendWs attend_ws(int H, int64_t nq, int n_chunks, int64_t n_tiles, int64_t spl
   w.range = off;   off += 256;
   w.mix = off;     off += align256(sizeof(MixOrder));
   w.krep = off;    off += align256(krep_bytes);
+  w.dense = off;   off += align256(dense_bytes);
   w.bytes = off;
   return w;
 }
@@ -510,9 +512,15 @@ int qkv_workspace_bytes(const qkv_config* cfg, int64_t max_chunk_tokens, int64_t
     const uint64_t krep = cfg->n_int4_channels > 0
                               ? (uint64_t)n_chunks * cfg->n_heads * (uint64_t)std::max<int64_t>(max_chunk_tokens, 1) * 64
                               : 0;
+    // caches on the generic decode (several stages, INT4, groups not a multiple of 32): room for
+    // their dense fp16 K and V rows
+    const bool generic = cfg->n_stages > 1 || cfg->bits == 4 || cfg->group % 32 != 0;
+    const uint64_t dense = generic ? 2ull * n_chunks * (uint64_t)std::max<int64_t>(max_chunk_tokens, 1) *
+                                         cfg->n_heads * kHeadDim * 2
+                                   : 0;
     // tiles for one more chunk: the fresh chunk of qkv_attend_fresh
     need = std::max(need, attend_ws(cfg->n_heads, n_query, n_chunks, max_tiles(std::max<int64_t>(max_chunk_tokens, 1), n_chunks + 1),
-                                    max_split_rows(cfg->n_heads, n_query), kMaxClusters, kMaxClusters, krep).bytes);
+                                    max_split_rows(cfg->n_heads, n_query), kMaxClusters, kMaxClusters, krep, dense).bytes);
   }
   if (n_query > 0) need = std::max(need, psac_ws(cfg->n_heads));
   *out = (size_t)need;
@@ -665,12 +673,25 @@ int attend_impl(const char* fn, const qkv_config* k_cfg, const qkv_config* v_cfg
   const int cap = split_cap(H, Nq);
   const bool two = fresh && n_chunks > 0 && kmode != 0 && vfast && q->dtype == QKV_BF16 && k_cfg->psac_rank == 0 &&
                    !logits_debug && cap >= 2;
+  // A cache on the generic decode (bf16 queries, no PSAC), when the workspace has room:
+  // decoded once into dense fp16 rows (k_dense_decode, the tile decode's own arithmetic and scaling),
+  // then attended as the tiles of one fresh chunk, so the tile loop does no per-element decode.
+  const int64_t n_dtiles = (Nk + kTileKeys - 1) / kTileKeys;
+  bool dense = false;
+  if (!fresh && n_chunks > 0 && (kmode == 0 || !vfast) && q->dtype == QKV_BF16 && k_cfg->psac_rank == 0) {
+    const int nsd = choose_splits(H, Nq, n_dtiles);
+    dense = workspace_bytes >= attend_ws(H, Nq, n_chunks, std::max<int64_t>(n_tiles, n_dtiles), nsd > 1 ? (int64_t)nsd * Nq : 0,
+                                         0, 0, 0, 2ull * Nk * H * kHeadDim * 2).bytes;
+  }
   const int ns_cache = two ? std::min(choose_splits(H, Nq, n_cache_tiles), cap - 1) : 0;
   const int ns_total = two ? ns_cache + 1 : ns;
-  const AttendWs ws = attend_ws(H, Nq, n_chunks, n_tiles, ns_total > 1 ? (int64_t)ns_total * Nq : 0, kC16, vC16,
-                                kmix ? (uint64_t)H * Nk * 64 : 0);
+  const int ns_dense = dense ? choose_splits(H, Nq, n_dtiles) : 0;
+  const AttendWs ws = dense ? attend_ws(H, Nq, n_chunks, std::max<int64_t>(n_tiles, n_dtiles),
+                                        ns_dense > 1 ? (int64_t)ns_dense * Nq : 0, 0, 0, 0, 2ull * Nk * H * kHeadDim * 2)
+                            : attend_ws(H, Nq, n_chunks, n_tiles, ns_total > 1 ? (int64_t)ns_total * Nq : 0, kC16, vC16,
+                                        kmix ? (uint64_t)H * Nk * 64 : 0);
   QKV_TRY(check_ws(workspace, workspace_bytes, ws.bytes, fn));
-  if (kmix) {
+  if (kmix && !dense) {
     uint64_t off = 0;
     for (int i = 0; i < n_chunks; ++i) {
       recs[i].krep = at(workspace, ws.krep + off);
@@ -698,7 +719,7 @@ int attend_impl(const char* fn, const qkv_config* k_cfg, const qkv_config* v_cfg
   const MixOrder* dmix = kmix ? reinterpret_cast<const MixOrder*>(at(workspace, ws.mix)) : nullptr;
   int64_t max_n = 0;
   for (int i = 0; i < n_chunks; ++i) max_n = std::max<int64_t>(max_n, recs[i].n);
-  if (kmix) QKV_HIP(launch_repack_mix(drecs, n_chunks, (int)max_n, params_of(k_cfg), dmix, s));
+  if (kmix && !dense) QKV_HIP(launch_repack_mix(drecs, n_chunks, (int)max_n, params_of(k_cfg), dmix, s));
   // operand range of the fp16 MFMAs: largest stored scale, centroid, PSAC
   // coefficient and query (the kernels below derive their power-of-two scaling from it)
   TensorView kfv{}, vfv{};
@@ -709,6 +730,49 @@ int attend_impl(const char* fn, const qkv_config* k_cfg, const qkv_config* v_cfg
   QKV_HIP(launch_range_scan(drecs, n_chunks, params_of(k_cfg), params_of(v_cfg), view_of(q), (int)Nq, kfv, vfv,
                             (int)n_fresh, range, s));
   TileRec* dtiles = reinterpret_cast<TileRec*>(at(workspace, ws.tiles));
+  if (dense) {
+    uint16_t* dk = reinterpret_cast<uint16_t*>(at(workspace, ws.dense));
+    uint16_t* dv = dk + (size_t)Nk * H * kHeadDim;
+    QKV_HIP(launch_dense_decode(drecs, n_chunks, (int)max_n, H, params_of(k_cfg), params_of(v_cfg), range, dk, dv, s));
+    const TokenBytes tb{0, 0, 0, 0, 0};
+    QKV_HIP(launch_tile_table(drecs, 0, (int)n_dtiles, 0, (int)Nk, 0, tb, H, k_cfg->n_clusters, v_cfg->n_clusters, nullptr,
+                              nullptr, dtiles, s));
+    AttendArgs a{};
+    a.q = view_of(q);
+    a.H = H;
+    a.Nq = (int)Nq;
+    a.Nk = Nk;
+    a.n_chunks = 0;
+    a.n_tiles = (int)n_dtiles;
+    a.kp = params_of(k_cfg);
+    a.vp = params_of(v_cfg);
+    a.chunks = drecs;
+    a.tiles = dtiles;
+    a.qu = reinterpret_cast<float*>(at(workspace, ws.qu));
+    a.causal = causal ? 1 : 0;                   // token-causal: frames of one token from key 0
+    a.mask_F = causal ? 1 : (1 << 30);
+    a.mask_base = 0;
+    a.kf = TensorView{dk, 2, Nk, (int64_t)H * kHeadDim, kHeadDim};
+    a.vf = TensorView{dv, 2, Nk, (int64_t)H * kHeadDim, kHeadDim};
+    a.n_cache_tiles = 0;
+    a.scale = softmax_scale > 0.0f ? softmax_scale : 1.0f / std::sqrt((float)kHeadDim);
+    a.n_split = ns_dense;
+    a.tile_lo = 0;
+    a.split_base = 0;
+    a.n_split_total = ns_dense;
+    a.part_o = reinterpret_cast<float*>(at(workspace, ws.part_o));
+    a.part_ml = reinterpret_cast<float*>(at(workspace, ws.part_ml));
+    a.out = reinterpret_cast<float*>(out->ptr);
+    a.out_stride_token = out->stride_token;
+    a.out_stride_head = out->stride_head;
+    a.logits = logits_debug;                     // key index = the dense row = the cache's token index
+    a.range = range;
+    a.k_mode = 1;                                // the lean fresh-chunk variant: every tile is a dense one
+    a.mixp = nullptr;
+    a.v_uniform_int2_1stage = true;
+    QKV_HIP(launch_attend(a, s));
+    return ok();
+  }
   uint16_t* k16 = kmode ? reinterpret_cast<uint16_t*>(at(workspace, ws.k16)) : nullptr;
   uint16_t* v16 = vfast ? reinterpret_cast<uint16_t*>(at(workspace, ws.v16)) : nullptr;
   QKV_HIP(launch_centroids_f16(drecs, n_chunks, params_of(k_cfg), params_of(v_cfg), range, dmix, k16, v16, s));
