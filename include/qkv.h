@@ -182,7 +182,12 @@ int qkv_chunk_layout(const qkv_config* cfg, int64_t n_tokens, qkv_layout* out);
 /* Host only: bytes of device workspace that every entry point below needs for
    chunks of at most max_chunk_tokens tokens, attention over at most n_chunks
    chunks with n_query queries, and qkv_psac_fit with n_query history queries.
-   One workspace of this size serves every call with those bounds. */
+   One workspace of this size serves every call with those bounds.  For a
+   configuration on the generic decode (several stages, 4-bit codes, or groups
+   that are not a multiple of 32) it includes 512 bytes per cached token-head
+   for dense fp16 K and V rows, which qkv_attend decodes once per call and
+   attends over; given less, qkv_attend decodes inside its tile loop instead
+   (the same result up to summation order). */
 int qkv_workspace_bytes(const qkv_config* cfg, int64_t max_chunk_tokens, int64_t n_query,
                         int32_t n_chunks, size_t* out);
 
