@@ -122,6 +122,14 @@ def test_progressive_three_stages():
     _run("progressive", wl, [(0, 900), (900, 1700)], 200, [1])
 
 
+def test_progressive_causal_bf16_queries():
+    """Token-causal attention over a three-stage cache with bf16 queries: the
+    dense-decode path (every key row decoded once, then the tiles of one fresh
+    chunk) under the token-causal mask (frames of one token from key 0)."""
+    wl = synth.workload(3, n_heads=2, n_clusters=64)
+    _run("progressive-causal", wl, [(0, 700), (700, 1300)], 1300, [0], causal=True, logit_queries=96)
+
+
 def test_quantwm_psac():
     wl = synth.workload(4, n_heads=2, n_clusters=64)
     _run("quantwm", wl, [(0, 1200), (1200, 2400)], 260, [0, 1])
