@@ -30,7 +30,7 @@ QKV_STUB(hipError_t launch_psac_encode(const ChunkDecode&, const TensorView&, co
 QKV_STUB(hipError_t launch_copy_perm(const uint8_t*, uint8_t*, int, hipStream_t))
 QKV_STUB(hipError_t launch_gram(const TensorView&, int, double*, int, double*, hipStream_t))
 QKV_STUB(hipError_t launch_gram_diag(const TensorView&, int, double*, int, double*, hipStream_t))
-QKV_STUB(hipError_t launch_eigh(const double*, int, double*, int, float*, float*, double*, hipStream_t))
+QKV_STUB(hipError_t launch_eigh(const double*, int, void*, size_t, int, float*, float*, double*, hipStream_t))
 QKV_STUB(hipError_t launch_dense_decode(const ChunkRec*, int, int, int, const LayoutParams&, const LayoutParams&,
                                         const uint32_t*, uint16_t*, uint16_t*, hipStream_t))
 QKV_STUB(hipError_t launch_upload_chunks(const ChunkBatch&, ChunkRec*, uint32_t*, const MixOrder&, MixOrder*, hipStream_t))

@@ -9,14 +9,18 @@
 // rotation of a pair annihilates a_pq (tan 2 theta = 2 a_pq / (a_qq - a_pp),
 // t = tan theta the smaller root, c = 1 / sqrt(1 + t^2), s = t c); as the
 // pairs are disjoint their rotations commute, so A <- J^T A J is applied as
-// one pass over the pairs' columns and then one over their rows, and the
-// eigenvector matrix (kept transposed in global memory) as V^T <- J^T V^T,
-// each column of V^T updated by one fixed thread throughout (no thread reads
-// global memory that another thread of the block wrote).
+// one pass over the pairs' columns and then one over their rows.
 // Sweeps stop when the off-diagonal mass is at most 1e-30 of the total (or
-// after 60).  The eigenvalues are ranked in descending order (ties to the
-// lower index); the leading `rank` eigenvectors and the energy fraction of
-// their eigenvalues are written out.
+// after the sweeps the rotation record has room for, at most 60).  The
+// eigenvalues are ranked in descending order (ties to the lower index).
+// Eigenvectors: the eigenvector matrix is V = J_1 J_2 ... J_n, and only its
+// columns of the `rank` (at most 8) largest eigenvalues are wanted, so the
+// sweeps record every step's (c, s) and the columns are formed at the end as
+// J_1 (J_2 (... (J_n e_j))), the recorded steps applied backwards to unit
+// vectors in LDS.  Those columns, and the energy fraction of their
+// eigenvalues, are written out.
+#include <algorithm>
+
 #include "common.h"
 #include "kernels.h"
 #include "timing.h"
@@ -27,8 +31,10 @@ namespace {
 
 constexpr int kN = kHeadDim;         // 128
 constexpr int kPairs = kN / 2;       // 64
+constexpr int kSteps = kN - 1;       // 127 steps per sweep
 constexpr int kEighThreads = 256;
 constexpr int kEighMaxSweeps = 60;
+constexpr size_t kSweepRecordBytes = (size_t)kSteps * kPairs * 16;   // (c, s) per pair and step
 
 // Step k of the round-robin over 128 indices: index 0 stays, 1 .. 127 rotate.
 __device__ __forceinline__ void rr_pair(int k, int i, int& p, int& q) {
@@ -44,25 +50,25 @@ __device__ __forceinline__ void rr_pair(int k, int i, int& p, int& q) {
   q = max(a, b);
 }
 
-// Block h: m [H][128][128] (row-major, read), vt [H][128][128] scratch,
-// U [H][128][rank] (column b = eigenvector of the b-th largest eigenvalue),
-// energy [H] (sum of the rank largest eigenvalues over their total; 0 when
-// the total is not positive), diag [H][128] (M's own diagonal, as read).
-__global__ __launch_bounds__(kEighThreads) void k_eigh(const double* __restrict__ m, double* __restrict__ vt,
-                                                        int rank, float* __restrict__ U, float* __restrict__ energy,
-                                                        double* __restrict__ diag) {
+// Block h: m [H][128][128] (row-major, read), rot [H][max_sweeps][127][64] (c, s)
+// scratch, U [H][128][rank] (column b = eigenvector of the b-th largest
+// eigenvalue), energy [H] (sum of the rank largest eigenvalues over their total;
+// 0 when the total is not positive), diag [H][128] (M's own diagonal, as read).
+__global__ __launch_bounds__(kEighThreads) void k_eigh(const double* __restrict__ m, double2* __restrict__ rot,
+                                                        int max_sweeps, int rank, float* __restrict__ U,
+                                                        float* __restrict__ energy, double* __restrict__ diag) {
   __shared__ double A[kN][kN];
   __shared__ double rc[kPairs], rs[kPairs];
   __shared__ int rp[kPairs], rq[kPairs];
   __shared__ double red[kEighThreads / 64];
   __shared__ int rank_of[kN];
+  __shared__ int sel[kMaxRank];
+  __shared__ double X[kMaxRank][kN];
   const int h = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const double* mh = m + (int64_t)h * kN * kN;
-  double* vh = vt + (int64_t)h * kN * kN;
+  double2* rh = rot + (int64_t)h * max_sweeps * kSteps * kPairs;
   for (int i = tid; i < kN * kN; i += kEighThreads) A[i / kN][i % kN] = mh[i];
   if (tid < kN && diag) diag[(int64_t)h * kN + tid] = mh[tid * (kN + 1)];
-  if (tid < kN)                                  // thread c owns column c of V^T
-    for (int r = 0; r < kN; ++r) vh[r * kN + tid] = r == tid ? 1.0 : 0.0;
   __syncthreads();
   // sum over all elements (kind 0) or over the off-diagonal ones (kind 1), block-wide
   auto mass = [&](bool off_only) -> double {
@@ -80,11 +86,12 @@ __global__ __launch_bounds__(kEighThreads) void k_eigh(const double* __restrict_
     return t;
   };
   const double total = mass(false);
-  for (int sweep = 0; sweep < kEighMaxSweeps; ++sweep) {
+  int n_sweeps = 0;                              // block-uniform
+  for (; n_sweeps < max_sweeps; ++n_sweeps) {
     const double off = mass(true);               // block-uniform
     if (off <= 1e-30 * total || off == 0.0) break;
-    for (int k = 0; k < kN - 1; ++k) {
-      if (tid < kPairs) {                        // the step's rotations
+    for (int k = 0; k < kSteps; ++k) {
+      if (tid < kPairs) {                        // the step's rotations, recorded by the thread that forms them
         int p, q;
         rr_pair(k, tid, p, q);
         const double apq = 0.5 * (A[p][q] + A[q][p]);
@@ -100,6 +107,7 @@ __global__ __launch_bounds__(kEighThreads) void k_eigh(const double* __restrict_
         rq[tid] = q;
         rc[tid] = c;
         rs[tid] = s;
+        rh[((int64_t)n_sweeps * kSteps + k) * kPairs + tid] = make_double2(c, s);
       }
       __syncthreads();
       // columns p, q of every row: lanes take different pairs, the waves rows r = wave + 4 j
@@ -121,26 +129,11 @@ __global__ __launch_bounds__(kEighThreads) void k_eigh(const double* __restrict_
         }
       }
       __syncthreads();
-      // rows p, q of every column: of V^T by threads 0 .. 127 (thread = column, every
-      // pair, 32 pairs' loads at a time), of A by threads 128 .. 255 (16 at a time)
-      if (tid < kN) {
-        for (int i0 = 0; i0 < kPairs; i0 += 32) {
-          double vp[32], vq[32];
-#pragma unroll
-          for (int u = 0; u < 32; ++u) {
-            vp[u] = vh[rp[i0 + u] * kN + tid];
-            vq[u] = vh[rq[i0 + u] * kN + tid];
-          }
-#pragma unroll
-          for (int u = 0; u < 32; ++u) {
-            const double c = rc[i0 + u], s = rs[i0 + u];
-            vh[rp[i0 + u] * kN + tid] = c * vp[u] - s * vq[u];
-            vh[rq[i0 + u] * kN + tid] = s * vp[u] + c * vq[u];
-          }
-        }
-      } else {
-        const int col = tid - kN;
-        for (int i0 = 0; i0 < kPairs; i0 += 16) {
+      // rows p, q of every column: thread = column, the two halves of the block
+      // taking 32 pairs each (16 pairs' loads at a time)
+      {
+        const int col = tid & (kN - 1), i1 = (tid >> 7) * (kPairs / 2);
+        for (int i0 = i1; i0 < i1 + kPairs / 2; i0 += 16) {
           double ap[16], aq[16];
 #pragma unroll
           for (int u = 0; u < 16; ++u) {
@@ -167,16 +160,9 @@ __global__ __launch_bounds__(kEighThreads) void k_eigh(const double* __restrict_
       rk += (e > d || (e == d && j < tid)) ? 1 : 0;
     }
     rank_of[tid] = rk;
+    if (rk < rank) sel[rk] = tid;                // the ranks are a permutation of 0 .. 127
   }
   __syncthreads();
-  // U[h][k][b] = V[k][j] for the j of rank b < rank (V^T row j is eigenvector j),
-  // each thread reading its own column of V^T
-  if (tid < kN) {
-    for (int j = 0; j < kN; ++j) {
-      const int b = rank_of[j];
-      if (b < rank) U[((int64_t)h * kN + tid) * rank + b] = (float)vh[j * kN + tid];
-    }
-  }
   if (tid == 0 && energy) {
     double tot = 0.0, top = 0.0;
     for (int j = 0; j < kN; ++j) {
@@ -185,15 +171,72 @@ __global__ __launch_bounds__(kEighThreads) void k_eigh(const double* __restrict_
     }
     energy[h] = tot > 0.0 ? (float)(top / tot) : 0.0f;
   }
+  // U[h][k][b] = V[k][sel[b]]: wave 0 applies the recorded steps, last first, to the
+  // unit vectors e_sel[b]; lane i takes pair slot i of every step, whose (c, s) this
+  // same thread recorded, and the wave orders its LDS accesses between steps
+  if (wave == 0 && rank > 0) {
+#pragma unroll
+    for (int b = 0; b < kMaxRank; ++b)
+      if (b < rank) {
+        X[b][lane] = lane == sel[b] ? 1.0 : 0.0;
+        X[b][lane + kPairs] = lane + kPairs == sel[b] ? 1.0 : 0.0;
+      }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // the records are read kAhead steps at a time, the next batch in flight while
+    // the current one is applied
+    constexpr int kAhead = 8;
+    auto load_batch = [&](int st0, double2* dst) {
+#pragma unroll
+      for (int u = 0; u < kAhead; ++u)
+        dst[u] = st0 - u >= 0 ? rh[(int64_t)(st0 - u) * kPairs + lane] : make_double2(1.0, 0.0);
+    };
+    double2 cur[kAhead];
+    load_batch(n_sweeps * kSteps - 1, cur);
+    for (int st0 = n_sweeps * kSteps - 1; st0 >= 0; st0 -= kAhead) {
+      double2 nxt[kAhead];
+      load_batch(st0 - kAhead, nxt);
+#pragma unroll
+      for (int u = 0; u < kAhead; ++u) {
+        const int st = st0 - u;                  // wave-uniform
+        if (st < 0) break;
+        int p, q;
+        rr_pair(st % kSteps, lane, p, q);
+#pragma unroll
+        for (int b = 0; b < kMaxRank; ++b)
+          if (b < rank) {
+            const double xp = X[b][p], xq = X[b][q];
+            X[b][p] = cur[u].x * xp + cur[u].y * xq;     // x <- J x: J_pp = J_qq = c, J_pq = s, J_qp = -s
+            X[b][q] = cur[u].x * xq - cur[u].y * xp;
+          }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      }
+#pragma unroll
+      for (int u = 0; u < kAhead; ++u) cur[u] = nxt[u];
+    }
+#pragma unroll
+    for (int b = 0; b < kMaxRank; ++b)
+      if (b < rank) {
+        U[((int64_t)h * kN + lane) * rank + b] = (float)X[b][lane];
+        U[((int64_t)h * kN + lane + kPairs) * rank + b] = (float)X[b][lane + kPairs];
+      }
+  }
 }
 
 }  // namespace
 
-hipError_t launch_eigh(const double* m, int H, double* vt, int rank, float* U, float* energy, double* diag,
-                       hipStream_t s) {
-  if (H < 1 || rank < 0 || rank > kN || (rank > 0 && !U)) return hipErrorInvalidValue;
+hipError_t launch_eigh(const double* m, int H, void* rot, size_t rot_bytes, int rank, float* U, float* energy,
+                       double* diag, hipStream_t s) {
+  if (H < 1 || rank < 0 || rank > kMaxRank || (rank > 0 && !U) || !rot) return hipErrorInvalidValue;
+  const size_t room = rot_bytes / ((size_t)H * kSweepRecordBytes);
+  if (room < 1) return hipErrorInvalidValue;
+  const int max_sweeps = (int)std::min<size_t>(room, kEighMaxSweeps);
   TimedLaunch tl_("k_eigh", s);
-  hipLaunchKernelGGL(k_eigh, dim3((unsigned)H), dim3(kEighThreads), 0, s, m, vt, rank, U, energy, diag);
+  hipLaunchKernelGGL(k_eigh, dim3((unsigned)H), dim3(kEighThreads), 0, s, m, reinterpret_cast<double2*>(rot),
+                     max_sweeps, rank, U, energy, diag);
   return hipGetLastError();
 }
 

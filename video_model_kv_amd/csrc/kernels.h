@@ -167,12 +167,14 @@ hipError_t launch_copy_perm(const uint8_t* perm, uint8_t* dst, int H, hipStream_
 // ---- history-query statistics (gram.hip) ----
 hipError_t launch_gram(const TensorView& q, int H, double* partial, int n_split, double* m,
                        hipStream_t s);
+// Eigendecomposition of m [H][128][128] (eigh.hip): the rank (at most 8)
+// leading eigenvectors into U [H][128][rank], their energy fraction into
+// energy [H], m's diagonal into diag [H][128]; rot (rot_bytes, 16-byte
+// aligned) is scratch for the rotation record, whose room per head bounds the
+// sweeps (invalid value below one sweep's 130,048 bytes per head).
+hipError_t launch_eigh(const double* m, int H, void* rot, size_t rot_bytes, int rank, float* U, float* energy,
+                       double* diag, hipStream_t s);
 // Its diagonal only: m [H][128], the same values as launch_gram's diagonal.
-// Eigendecomposition of m [H][128][128] (eigh.hip): the rank leading
-// eigenvectors into U [H][128][rank], their energy fraction into energy [H],
-// m's diagonal into diag [H][128]; vt [H][128][128] is scratch.
-hipError_t launch_eigh(const double* m, int H, double* vt, int rank, float* U, float* energy, double* diag,
-                       hipStream_t s);
 hipError_t launch_gram_diag(const TensorView& q, int H, double* partial, int n_split, double* m,
                             hipStream_t s);
 

@@ -879,12 +879,14 @@ int qkv_psac_fit(const qkv_tensor* q_hist, int32_t n_heads, int32_t rank, int32_
   std::vector<double> hd((size_t)H * kHeadDim);
   std::vector<float> energy(H);
   if (full) {
-    // the partials are consumed by the reduction: they hold the solver's V^T, M's diagonal and the energies
-    double* vt = partial;
-    double* dg = partial + (size_t)H * kHeadDim * kHeadDim;
+    // the partials are consumed by the reduction: they then hold M's diagonal, the energies
+    // and the solver's rotation record (room for 16 sweeps per head)
+    double* dg = partial;
     float* en = reinterpret_cast<float*>(dg + (size_t)H * kHeadDim);
+    const uint64_t rot_off = align256((uint64_t)H * kHeadDim * 8 + (uint64_t)H * 4);
+    const uint64_t part_bytes = (uint64_t)kGramSplit * H * kHeadDim * kHeadDim * 8;
     QKV_HIP(launch_gram(view_of(q_hist), H, partial, kGramSplit, m, s));
-    QKV_HIP(launch_eigh(m, H, vt, rank, rank > 0 ? U_out : nullptr, en, dg, s));
+    QKV_HIP(launch_eigh(m, H, at(workspace, rot_off), part_bytes - rot_off, rank, rank > 0 ? U_out : nullptr, en, dg, s));
     QKV_HIP(hipMemcpyAsync(hd.data(), dg, hd.size() * 8, hipMemcpyDeviceToHost, s));
     QKV_HIP(hipMemcpyAsync(energy.data(), en, energy.size() * 4, hipMemcpyDeviceToHost, s));
   } else {
