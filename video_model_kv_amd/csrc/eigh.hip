@@ -8,8 +8,8 @@
 // indices into 64 disjoint pairs (p, q) and rotates every pair at once.  The
 // rotation of a pair annihilates a_pq (tan 2 theta = 2 a_pq / (a_qq - a_pp),
 // t = tan theta the smaller root, c = 1 / sqrt(1 + t^2), s = t c); as the
-// pairs are disjoint their rotations commute, so A <- J^T A J is applied as
-// one pass over the pairs' columns and then one over their rows.
+// pairs are disjoint their rotations commute, so A <- J^T A J is applied in
+// one pass over the 2 x 2 blocks that the pairs cut A into.
 // Sweeps stop when the off-diagonal mass is at most 1e-30 of the total (or
 // after the sweeps the rotation record has room for, at most 60).  The
 // eigenvalues are ranked in descending order (ties to the lower index).
@@ -32,7 +32,9 @@ namespace {
 constexpr int kN = kHeadDim;         // 128
 constexpr int kPairs = kN / 2;       // 64
 constexpr int kSteps = kN - 1;       // 127 steps per sweep
-constexpr int kEighThreads = 256;
+constexpr int kEighThreads = 1024;
+constexpr int kEighWaves = kEighThreads / 64;
+constexpr int kRowPairsPerWave = kPairs / kEighWaves;   // 4
 constexpr int kEighMaxSweeps = 60;
 constexpr size_t kSweepRecordBytes = (size_t)kSteps * kPairs * 16;   // (c, s) per pair and step
 
@@ -110,41 +112,35 @@ __global__ __launch_bounds__(kEighThreads) void k_eigh(const double* __restrict_
         rh[((int64_t)n_sweeps * kSteps + k) * kPairs + tid] = make_double2(c, s);
       }
       __syncthreads();
-      // columns p, q of every row: lanes take different pairs, the waves rows r = wave + 4 j
-      {                                          // (the pairs are disjoint: eight rows' loads, then their stores)
-        const int i = lane, p = rp[i], q = rq[i];
-        const double c = rc[i], s = rs[i];
-        for (int r0 = wave; r0 < kN; r0 += 8 * (kEighThreads / 64)) {
-          double ap[8], aq[8];
-#pragma unroll
-          for (int u = 0; u < 8; ++u) {
-            ap[u] = A[r0 + u * (kEighThreads / 64)][p];
-            aq[u] = A[r0 + u * (kEighThreads / 64)][q];
-          }
-#pragma unroll
-          for (int u = 0; u < 8; ++u) {
-            A[r0 + u * (kEighThreads / 64)][p] = c * ap[u] - s * aq[u];
-            A[r0 + u * (kEighThreads / 64)][q] = s * ap[u] + c * aq[u];
-          }
-        }
-      }
-      __syncthreads();
-      // rows p, q of every column: thread = column, the two halves of the block
-      // taking 32 pairs each (16 pairs' loads at a time)
+      // J^T A J over the 64 x 64 blocks of the pairs: block (i, j) holds rows p_i, q_i and
+      // columns p_j, q_j, which no other block touches, so each block is read once, its
+      // columns rotated by pair j and then its rows by pair i (the operations of a pass
+      // over the columns followed by one over the rows), and written once.  Lane = column
+      // pair j, each wave 4 row pairs, all their blocks' loads ahead of their stores.
       {
-        const int col = tid & (kN - 1), i1 = (tid >> 7) * (kPairs / 2);
-        for (int i0 = i1; i0 < i1 + kPairs / 2; i0 += 16) {
-          double ap[16], aq[16];
+        const int pj = rp[lane], qj = rq[lane];
+        const double cj = rc[lane], sj = rs[lane];
+        {
+          const int i0 = wave * kRowPairsPerWave;
+          double a[kRowPairsPerWave][4];
 #pragma unroll
-          for (int u = 0; u < 16; ++u) {
-            ap[u] = A[rp[i0 + u]][col];
-            aq[u] = A[rq[i0 + u]][col];
+          for (int u = 0; u < kRowPairsPerWave; ++u) {
+            const int pi = rp[i0 + u], qi = rq[i0 + u];
+            a[u][0] = A[pi][pj];
+            a[u][1] = A[pi][qj];
+            a[u][2] = A[qi][pj];
+            a[u][3] = A[qi][qj];
           }
 #pragma unroll
-          for (int u = 0; u < 16; ++u) {
-            const double c = rc[i0 + u], s = rs[i0 + u];
-            A[rp[i0 + u]][col] = c * ap[u] - s * aq[u];
-            A[rq[i0 + u]][col] = s * ap[u] + c * aq[u];
+          for (int u = 0; u < kRowPairsPerWave; ++u) {
+            const int pi = rp[i0 + u], qi = rq[i0 + u];
+            const double ci = rc[i0 + u], si = rs[i0 + u];
+            const double x0 = cj * a[u][0] - sj * a[u][1], x1 = sj * a[u][0] + cj * a[u][1];   // row p_i
+            const double y0 = cj * a[u][2] - sj * a[u][3], y1 = sj * a[u][2] + cj * a[u][3];   // row q_i
+            A[pi][pj] = ci * x0 - si * y0;
+            A[qi][pj] = si * x0 + ci * y0;
+            A[pi][qj] = ci * x1 - si * y1;
+            A[qi][qj] = si * x1 + ci * y1;
           }
         }
       }
