@@ -21,12 +21,16 @@ Prints one JSON line.  `value` is KV tokens per second through the whole step
 (tokens quantized into the cache and attended, inputs resident in HBM).  Extra
 fields: per-kernel durations of the step's launches (HIP events recorded by the
 library around each launch, in a pass of their own after the timed steps), the
-roofline of the step's dominant kernel and of the other hot kernels, and the CPU
-oracle's throughput on a bounded sample of the same workload.
+roofline of the step's dominant kernel and of the other hot kernels, the CPU
+oracle's throughput on a bounded sample of the same workload, and untimed quality
+diagnostics of each workload's cache ("quality": rebuild error against plain
+round-to-nearest, attention against the unquantized cache, PSAC's top-1 shift
+rate and energy).
 """
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import json
 import os
 import subprocess
@@ -432,6 +436,90 @@ def timed_call(run: Run, fn, reps: int) -> float:
     return e0.elapsed_time(e1) / reps
 
 
+def quality(run: Run, n_q: int = 128) -> dict:
+    """Quality diagnostics of a workload's packed cache, reported and not targets
+    (untimed; the cache of the run's last step):
+      - rel-L2 of the rebuilt K and V (all stages) against the bf16 input, and the
+        same for plain per-group round-to-nearest (centroids 0, QKV_FLAG_RTN), whose
+        ratio is the error reduction of the smoothing (Quant VideoGen notes,
+        "Experiments", against the RTN baseline);
+      - attention of the first n_q queries over the packed cache against float32
+        attention over the unquantized bf16 cache (rel-L2 of the outputs);
+      - with PSAC: the top-1 shift rate, the share of (head, query) whose
+        highest-logit key differs from that of the exact logits, with the fitted
+        U and with U = 0 (the same cache without the correction term), and the
+        energy fraction of the fitted subspace (QuantWM summary, second technique)."""
+    qk, torch = run.qk, run.torch
+    wl, H, d = run.wl, run.wl.n_heads, 128
+    run.step()
+    torch.cuda.synchronize()
+    res = {"queries": n_q, "stages": wl.n_stages}
+
+    def rebuild_err(cfg, xs, packs):
+        num = den = 0.0
+        for x, pk in zip(xs, packs):
+            xh = torch.empty(x.shape, dtype=torch.float32, device=x.device)
+            qk.qkv_dequantize(cfg, x.shape[0], pk, xh)
+            xf = x.float()
+            num += float(((xh - xf) ** 2).sum())
+            den += float((xf ** 2).sum())
+        return (num / den) ** 0.5
+
+    res["rel_l2_k"] = rebuild_err(run.kcfg, run.xk, run.kp)
+    res["rel_l2_v"] = rebuild_err(run.vcfg, run.xv, run.vp)
+    try:
+        rk, rv = (dataclasses.replace(c, flags=c.flags | qk.QKV_FLAG_RTN) for c in (run.kcfg, run.vcfg))
+        errs = []
+        for cfg, xs, side in ((rk, run.xk, run.side), (rv, run.xv, (None, None, None))):
+            packs = []
+            for x in xs:
+                pk = torch.empty(qk.qkv_chunk_layout(cfg, x.shape[0]).bytes, dtype=torch.uint8, device=x.device)
+                qk.qkv_quantize_chunk(cfg, x, pk, run.ws, w=side[0], perm=side[1], U=side[2])
+                packs.append(pk)
+            errs.append(rebuild_err(cfg, xs, packs))
+            del packs
+        res["rtn_rel_l2_k"], res["rtn_rel_l2_v"] = errs
+        res["error_reduction_vs_rtn_k"] = errs[0] / res["rel_l2_k"]
+        res["error_reduction_vs_rtn_v"] = errs[1] / res["rel_l2_v"]
+    except Exception as e:  # reported, never fatal to the measurement
+        res["rtn_error"] = str(e)
+    q = run.q[:n_q].contiguous()
+    out = torch.empty((n_q, H, d), dtype=torch.float32, device=q.device)
+    U = run.side[2]
+    nk = run.nk
+    logits = torch.empty((H, n_q, nk), dtype=torch.float32, device=q.device) if U is not None else None
+    qk.qkv_attend(run.kcfg, run.vcfg, q, run.kp, run.vp, run.ntok, out, run.ws, U=U, logits=logits)
+    torch.cuda.synchronize()
+    num = den = 0.0
+    shift = shift0 = 0
+    top_exact = []
+    for h in range(H):
+        kh = torch.cat([x[:, h] for x in run.xk]).float()
+        vh = torch.cat([x[:, h] for x in run.xv]).float()
+        qh = q[:, h].float()
+        s_exact = torch.matmul(qh, kh.t().contiguous())
+        o = torch.matmul(torch.softmax(s_exact / d ** 0.5, dim=1), vh)
+        num += float(((out[:, h] - o) ** 2).sum())
+        den += float((o ** 2).sum())
+        top_exact.append(s_exact.argmax(dim=1))
+        if logits is not None:
+            shift += int((logits[h].argmax(dim=1) != top_exact[-1]).sum())
+    res["attention_rel_l2_vs_bf16_cache"] = (num / den) ** 0.5
+    if U is not None:
+        qk.qkv_attend(run.kcfg, run.vcfg, q, run.kp, run.vp, run.ntok, out, run.ws, U=torch.zeros_like(U),
+                      logits=logits)
+        torch.cuda.synchronize()
+        for h in range(H):
+            shift0 += int((logits[h].argmax(dim=1) != top_exact[h]).sum())
+        res["top1_shift_rate_psac"] = shift / (H * n_q)
+        res["top1_shift_rate_no_psac"] = shift0 / (H * n_q)
+        energy = qk.qkv_psac_fit(run.hist, H, wl.psac_rank, wl.n_int4, run.ws_fit, U_out=U, w_out=run.w,
+                                 perm_out=run.perm if wl.n_int4 else None)
+        res["psac_energy_mean"] = sum(energy) / len(energy)
+        res["psac_energy_min"] = min(energy)
+    return res
+
+
 def kernel_profile(run: Run, steps: int) -> dict:
     """Per-kernel launches and average duration over `steps` steps, from the HIP
     events the library records around its own launches while timing is on."""
@@ -633,6 +721,12 @@ def main():
             "kmeans_iters": wl.kmeans_iters, "stages": wl.n_stages, "bits": wl.bits, "group": wl.group,
             "int4_channels": wl.n_int4, "psac_rank": wl.psac_rank, "qsac": wl.qsac, "qsac_range": wl.qsac_range,
             "n_query": wl.n_query, "parallelism": "single-gpu"}
+    qual = None
+    if not a.headline_only:
+        try:
+            qual = quality(run)
+        except Exception as e:  # reported, never fatal to the GPU measurement
+            log(f"quality diagnostics failed: {e}")
     del run
     torch.cuda.empty_cache()
 
@@ -651,6 +745,10 @@ def main():
                              "quantize_ms": tq, "fit_ms": tf,
                              "cache_tokens": r.nk, "stages": r.wl.n_stages, "psac_rank": r.wl.psac_rank,
                              "qsac": r.wl.qsac, "qsac_range": r.wl.qsac_range}
+        try:
+            extras[r.wl.name]["quality"] = quality(r)
+        except Exception as e:  # reported, never fatal to the GPU measurement
+            log(f"quality diagnostics of {r.wl.name} failed: {e}")
         log(f"extra workload {r.wl.name}: {ms:.3f} ms/step; quantize {tq:.3f} ms, attend {ta:.3f} ms, "
             f"query statistics {tf:.3f} ms")
         del r
@@ -672,7 +770,7 @@ def main():
                          "attention on fp16 MFMA with fp32 accumulation and softmax"),
         "data": "synthetic", "config": cfgd,
         "roofline": {k: v for k, v in dominant.items()},
-        "rooflines": roofs, "components": comp, "ar_rollout": ar, "temporal_codec": tcodec, "layer_batching": lbatch, "workloads": extras, "cpu_baseline": cpu,
+        "rooflines": roofs, "components": comp, "ar_rollout": ar, "temporal_codec": tcodec, "layer_batching": lbatch, "workloads": extras, "quality": qual, "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)
 
