@@ -439,10 +439,10 @@ def timed_call(run: Run, fn, reps: int) -> float:
 def quality(run: Run, n_q: int = 128) -> dict:
     """Quality diagnostics of a workload's packed cache, reported and not targets
     (untimed; the cache of the run's last step):
-      - rel-L2 of the rebuilt K and V (all stages) against the bf16 input, and the
-        same for plain per-group round-to-nearest (centroids 0, QKV_FLAG_RTN), whose
-        ratio is the error reduction of the smoothing (Quant VideoGen notes,
-        "Experiments", against the RTN baseline);
+      - rel-L2 of the rebuilt K and V (all stages, and after each stage) against the
+        bf16 input, and the same for plain per-group round-to-nearest (centroids 0,
+        QKV_FLAG_RTN), whose ratio is the error reduction of the smoothing (the QVG
+        notes' main table, "RTN" row);
       - attention of the first n_q queries over the packed cache against float32
         attention over the unquantized bf16 cache (rel-L2 of the outputs);
       - with PSAC: the top-1 shift rate, the share of (head, query) whose
@@ -467,6 +467,22 @@ def quality(run: Run, n_q: int = 128) -> dict:
 
     res["rel_l2_k"] = rebuild_err(run.kcfg, run.xk, run.kp)
     res["rel_l2_v"] = rebuild_err(run.vcfg, run.xv, run.vp)
+    if wl.n_stages > 1:
+        # stage l quantizes the residual of stages 1 .. l-1 only, so the error after s
+        # stages is the rebuild error of an s-stage quantization of the same input
+        by_stage = {"k": [], "v": []}
+        for s_ in range(1, wl.n_stages):
+            for key, cfg0, xs, side in (("k", run.kcfg, run.xk, run.side), ("v", run.vcfg, run.xv, (None, None, None))):
+                cfg = dataclasses.replace(cfg0, n_stages=s_)
+                packs = []
+                for x in xs:
+                    pk = torch.empty(qk.qkv_chunk_layout(cfg, x.shape[0]).bytes, dtype=torch.uint8, device=x.device)
+                    qk.qkv_quantize_chunk(cfg, x, pk, run.ws, w=side[0], perm=side[1], U=side[2])
+                    packs.append(pk)
+                by_stage[key].append(rebuild_err(cfg, xs, packs))
+                del packs
+        res["rel_l2_k_by_stage"] = by_stage["k"] + [res["rel_l2_k"]]
+        res["rel_l2_v_by_stage"] = by_stage["v"] + [res["rel_l2_v"]]
     try:
         rk, rv = (dataclasses.replace(c, flags=c.flags | qk.QKV_FLAG_RTN) for c in (run.kcfg, run.vcfg))
         errs = []
