@@ -25,7 +25,7 @@ roofline of the step's dominant kernel and of the other hot kernels, the CPU
 oracle's throughput on a bounded sample of the same workload, and untimed quality
 diagnostics of each workload's cache ("quality": rebuild error against plain
 round-to-nearest, attention against the unquantized cache, PSAC's top-1 shift
-rate and energy).
+rate and energy), and the pack kernel on one problem cold and warm ("hbm_cold").
 """
 from __future__ import annotations
 
@@ -536,6 +536,47 @@ def quality(run: Run, n_q: int = 128) -> dict:
     return res
 
 
+def hbm_cold(run: Run, reps: int = 10) -> dict:
+    """The uniform pack kernel (k_quant_pack_tile, through qkv_quant_pack) on one V
+    problem of chunk 0, cold and warm.  Cold: a 512 MB write before each rep evicts
+    the 256 MB MALL; the write also keeps the GPU busy while the call is enqueued,
+    so the events bracket the kernel alone.  Warm: reps back to back (the
+    problem's ~66 MB stay in the MALL).  The step launches the kernel for 8
+    problems at once; one problem is the unit the call takes."""
+    import statistics
+    qk, torch = run.qk, run.torch
+    H, d, C = run.wl.n_heads, 128, run.wl.n_clusters
+    cfg, x = run.vcfg, run.xv[0]
+    n = x.shape[0]
+    cent = x[::max(1, n // C)][:C].float().permute(1, 0, 2).contiguous()   # [H][C][d]
+    labels = torch.empty((H, n), dtype=torch.uint8, device=x.device)
+    qk.qkv_kmeans_assign(cfg, x, cent, labels, run.ws)
+    lay = qk.qkv_chunk_layout(cfg, n)
+    packed = torch.empty(lay.bytes, dtype=torch.uint8, device=x.device)
+    work = n * H * d * 2 + n * H + H * C * d * 2 + n * H * (4 * lay.words_per_token + 2 * lay.groups_per_token)
+    scratch = torch.empty(512 << 20, dtype=torch.uint8, device=x.device)
+
+    def pack():
+        qk.qkv_quant_pack(cfg, x, labels, cent, packed)
+
+    cold = []
+    for _ in range(reps + 1):
+        scratch.fill_(1)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        pack()
+        e1.record()
+        torch.cuda.synchronize()
+        cold.append(e0.elapsed_time(e1))
+    cold = cold[1:]
+    warm = timed_call(run, pack, reps)
+    del scratch
+    cm = statistics.median(cold)
+    return {"kernel": "k_quant_pack_tile", "problems_per_launch": 1, "algorithmic_bytes": work,
+            "cold_us_median": cm * 1e3, "cold_us_min": min(cold) * 1e3, "warm_us_mean": warm * 1e3,
+            "cold_GBps": work / (cm * 1e-3) / 1e9, "warm_GBps": work / (warm * 1e-3) / 1e9}
+
+
 def kernel_profile(run: Run, steps: int) -> dict:
     """Per-kernel launches and average duration over `steps` steps, from the HIP
     events the library records around its own launches while timing is on."""
@@ -737,12 +778,16 @@ def main():
             "kmeans_iters": wl.kmeans_iters, "stages": wl.n_stages, "bits": wl.bits, "group": wl.group,
             "int4_channels": wl.n_int4, "psac_rank": wl.psac_rank, "qsac": wl.qsac, "qsac_range": wl.qsac_range,
             "n_query": wl.n_query, "parallelism": "single-gpu"}
-    qual = None
+    qual = cold = None
     if not a.headline_only:
         try:
             qual = quality(run)
         except Exception as e:  # reported, never fatal to the GPU measurement
             log(f"quality diagnostics failed: {e}")
+        try:
+            cold = hbm_cold(run)
+        except Exception as e:  # reported, never fatal to the GPU measurement
+            log(f"cold pack timing failed: {e}")
     del run
     torch.cuda.empty_cache()
 
@@ -786,7 +831,7 @@ def main():
                          "attention on fp16 MFMA with fp32 accumulation and softmax"),
         "data": "synthetic", "config": cfgd,
         "roofline": {k: v for k, v in dominant.items()},
-        "rooflines": roofs, "components": comp, "ar_rollout": ar, "temporal_codec": tcodec, "layer_batching": lbatch, "workloads": extras, "quality": qual, "cpu_baseline": cpu,
+        "rooflines": roofs, "components": comp, "ar_rollout": ar, "temporal_codec": tcodec, "layer_batching": lbatch, "workloads": extras, "quality": qual, "hbm_cold": cold, "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)
 
