@@ -304,8 +304,13 @@ int qkv_attend_fresh(const qkv_config* k_cfg, const qkv_config* v_cfg, const qkv
  *           then the rest ascending (ties -> lower index); NULL or n_int4 == 0
  *           to skip;
  *   energy_out float [H] HOST: top-rank eigenvalue sum / trace (may be NULL).
- * The eigensolver (cyclic Jacobi, float64) runs on the host: this call
- * copies M to the host and synchronises `stream`.
+ * The eigensolver (parallel cyclic Jacobi, float64) runs on the device, one
+ * workgroup per head; it stops once the off-diagonal mass is at most 1e-30 of
+ * the total, or after 16 sweeps (the room the workspace gives its rotation
+ * record).  When rank == 0 and energy_out is NULL only M's diagonal is formed.
+ * The host orders the channels from M's diagonal: the call copies it (and the
+ * energies) to the host, synchronises `stream`, and returns with w_out and
+ * perm_out written.  workspace: qkv_workspace_bytes(cfg, 0, n, 0) bytes.
  */
 int qkv_psac_fit(const qkv_tensor* q_hist, int32_t n_heads, int32_t rank, int32_t n_int4,
                  float* U_out, float* w_out, uint8_t* perm_out, float* energy_out,
