@@ -542,6 +542,42 @@ def test_psac_fit_degenerate_histories():
     G.log("psac_fit: zero and diagonal histories as defined")
 
 
+def test_psac_fit_clustered_spectrum():
+    """The GPU eigensolver where single eigenvectors are ill-defined: per head, the
+    history's covariance has eight equal leading eigenvalues (100) in a random
+    orthogonal basis and the rest in [1, 10], so the sample Gram M has a leading
+    cluster of eight (within about 15 % of each other, some pairs within 0.2 %)
+    and a gap of about 7.5x after it.  The rank-8 subspace is then well defined: its projector must match LAPACK's on the same M (float64 of the bf16
+    queries), and the energy fraction must match."""
+    t = G.torch()
+    H, n, r = 4, 2048, 8
+    rng = np.random.default_rng(11)
+    x = np.empty((n, H, 128), np.float32)
+    for h in range(H):
+        q, _ = np.linalg.qr(rng.standard_normal((128, 128)))
+        lam = np.concatenate([np.full(r, 100.0), rng.uniform(1.0, 10.0, 128 - r)])
+        x[:, h] = (rng.standard_normal((n, 128)) * np.sqrt(lam)) @ q.T
+    x = synth.round_to(x.astype(np.float64), "bf16")
+    cfg = G.config_of(synth.workload(4, n_heads=H), "K")
+    ws = G.workspace(cfg, 0, n, 0)
+    U = t.empty((H, 128, r), dtype=t.float32, device=G.dev())
+    w = t.empty((H, 128), dtype=t.float32, device=G.dev())
+    energy = qk.qkv_psac_fit(G.to_dev(x, "bf16"), H, r, 0, ws, U_out=U, w_out=w)
+    Ug = U.cpu().numpy().astype(np.float64)
+    worst = 0.0
+    for h in range(H):
+        m = ops.query_gram(x[:, h])
+        uo, lam_o, eo = ops.principal_subspace(m, r)
+        ev = np.linalg.eigvalsh(m)[::-1]
+        assert ev[r - 1] > 5.0 * ev[r], f"head {h}: no gap after the leading cluster"
+        assert np.allclose(Ug[h].T @ Ug[h], np.eye(r), atol=1e-5), f"head {h}: U not orthonormal"
+        dp = np.linalg.norm(Ug[h] @ Ug[h].T - uo @ uo.T)
+        worst = max(worst, dp)
+        assert dp < 1e-4, f"head {h}: projector differs by {dp}"
+        assert abs(energy[h] - eo) < 1e-6, f"head {h}: energy {energy[h]} against {eo}"
+    G.log(f"psac_fit: clustered spectrum, worst projector difference {worst:.3g}")
+
+
 def _batch_vs_single(problems):
     """problems: list of (cfg, x_dev, (w, perm, u) device tensors or None).
     The batched write path must reproduce every single-problem call byte for byte."""
