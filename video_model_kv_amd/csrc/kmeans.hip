@@ -1559,11 +1559,21 @@ __global__ __launch_bounds__(64) void k_cert(KmBatch b) {
   }
 }
 
+// Eight values per thread (H * C * 128 is a multiple of 8; both tables are
+// 16-byte aligned): two 16-byte loads, one 16-byte store.
 __global__ void k_centroid_bf16(KmBatch b) {
   const KmItem& it = b.it[blockIdx.y];
-  const int64_t n = (int64_t)b.H * b.C * kHeadDim;
+  const int64_t n8 = (int64_t)b.H * b.C * (kHeadDim / 8);
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) it.cent_bf16[i] = (uint16_t)f32_to_bf16_bits(it.c[i]);
+  if (i >= n8) return;
+  const float4 a = reinterpret_cast<const float4*>(it.c)[2 * i];
+  const float4 c = reinterpret_cast<const float4*>(it.c)[2 * i + 1];
+  uint4 o;
+  o.x = f32_to_bf16_bits(a.x) | (f32_to_bf16_bits(a.y) << 16);
+  o.y = f32_to_bf16_bits(a.z) | (f32_to_bf16_bits(a.w) << 16);
+  o.z = f32_to_bf16_bits(c.x) | (f32_to_bf16_bits(c.y) << 16);
+  o.w = f32_to_bf16_bits(c.z) | (f32_to_bf16_bits(c.w) << 16);
+  reinterpret_cast<uint4*>(it.cent_bf16)[i] = o;
 }
 
 __global__ void k_fill_zero(uint32_t* __restrict__ p, int64_t n) {
@@ -1669,8 +1679,8 @@ hipError_t launch_kmeans_group(const KmBatch& b, hipStream_t s) {
 
 hipError_t launch_centroid_bf16(const KmBatch& b, hipStream_t s) {
   TimedLaunch tl_("k_centroid_bf16", s);
-  const int64_t n = (int64_t)b.H * b.C * kHeadDim;
-  hipLaunchKernelGGL(k_centroid_bf16, dim3((unsigned)((n + 255) / 256), b.n), dim3(256), 0, s, b);
+  const int64_t n8 = (int64_t)b.H * b.C * (kHeadDim / 8);
+  hipLaunchKernelGGL(k_centroid_bf16, dim3((unsigned)((n8 + 255) / 256), b.n), dim3(256), 0, s, b);
   return hipGetLastError();
 }
 
